@@ -16,7 +16,7 @@ QMAX = np.float32(127.0)           # symmetric INT8 range; -128 is never produce
 __all__ = [
     "INVALID", "AMAX_FLOOR", "QMAX", "row_bytes_for", "quantize_rows", "pack_rows",
     "store_int8", "dequantize_rows", "layer_norm", "slot_softmax", "pool_states",
-    "visible", "visible_pool_count", "index_scores", "topk_pools", "expand_selection",
+    "store_bf16", "visible", "visible_pool_count", "index_scores", "topk_pools", "expand_selection",
     "topk_to_mask", "sparse_mla", "masked_attention", "attention_unquantized",
 ]
 
@@ -118,6 +118,19 @@ def pool_states(k: np.ndarray, gate: np.ndarray, ln_w, ln_b, eps: float,
     a = slot_softmax(np.asarray(gate)[toks])                     # [P, kpool, Di]
     pools = (a * y).sum(axis=1)
     return (pools, a) if return_weights else pools
+
+
+def store_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bf16 (ties to even), returned as float64.
+
+    Pool states are held in bf16 (bf16 pool states with fp32 accumulation are
+    the precision the path is specified at; reading R19), so a pool is
+    computed in full precision and then rounded once to the 8-bit-significand
+    bf16 grid.  Computed directly from the float64 value (no intermediate
+    fp32 rounding)."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                           # x = m * 2**e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
 
 
 # ---------------------------------------------------------------------------

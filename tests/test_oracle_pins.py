@@ -170,6 +170,19 @@ def test_layer_norm_is_normalising_with_unit_affine():
     assert np.allclose((y ** 2).mean(axis=1), 1.0, atol=1e-12)
 
 
+def test_store_bf16_ties_to_even_and_library_agreement():
+    one = 1.0
+    assert O.store_bf16(np.array([one + 2.0 ** -8]))[0] == 1.0                 # tie -> even (mantissa 0)
+    assert O.store_bf16(np.array([one + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6  # tie -> even (mantissa 2)
+    assert O.store_bf16(np.array([one + 2.0 ** -8 + 2.0 ** -30]))[0] == 1.0 + 2.0 ** -7
+    assert O.store_bf16(np.array([-3.0, 0.0, 96.0]))[0:3].tolist() == [-3.0, 0.0, 96.0]
+    g = np.random.default_rng(14)
+    x = (g.standard_normal(20000) * 10.0 ** g.uniform(-3, 3, 20000)).astype(np.float32).astype(np.float64)
+    ref = torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.store_bf16(x), ref)
+    assert np.all(np.abs(O.store_bf16(x) - x) <= np.abs(x) * 2.0 ** -8)
+
+
 # ------------------------------------------------------------------ O3 scores
 
 def test_scores_single_head_unit_weight_is_relu_dot():
