@@ -1,0 +1,154 @@
+"""Device-side workload setup for tests, smoke() and bench.py.
+
+Uploads the seeded synthetic inputs of a dsa_synth.Workload, builds the INT8
+latent cache and the pool cache through the library, allocates the step's
+outputs and workspaces, and runs one decode/prefill step of the path:
+
+  store_int8 (the step's new tokens) -> index_pools (pools those tokens
+  complete) -> index_scores -> topk_select -> expand_selection -> sparse_mla
+
+This module only marshals data; every computation runs in libdsa's kernels.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import dsa_synth as syn
+import sparse_attention_store_amd as dsa
+
+
+def _bits_to_bf16(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(syn.bf16_bits(a).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def _f32(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+class DeviceWorkload:
+    """All device state of one workload (optionally R replicas of the caches)."""
+
+    def __init__(self, wl: syn.Workload, device="cuda", replicas: int = 1, score_stride: int | None = None,
+                 out_dtype=torch.float32, num_splits: int = 0, build: bool = True, gen_workers: int = 8,
+                 canary: int | None = None):
+        self.wl = wl
+        self.device = torch.device(device)
+        d = wl.dims
+        self.dims = dsa.Dims.of(d)
+        dev = self.device
+        self.num_splits = num_splits
+        self.gen_workers = gen_workers
+        self.seqs = dsa.Seqs(
+            first_valid=torch.tensor(wl.first_valid, dtype=torch.int32, device=dev),
+            row_base=torch.tensor(wl.row_base, dtype=torch.int64, device=dev),
+            tok_base=torch.tensor(wl.tok_base, dtype=torch.int64, device=dev),
+            pool_base=torch.tensor(wl.pool_base, dtype=torch.int64, device=dev))
+        self.q_seq = torch.tensor(wl.q_seq, dtype=torch.int32, device=dev)
+        self.q_pos = torch.tensor(wl.q_pos, dtype=torch.int32, device=dev)
+        T = wl.T
+        rows, toks, npools = wl.total_rows, wl.total_tokens, max(wl.total_pools, 1)
+        fill = canary if canary is not None else 0
+        self.caches = [torch.full((rows, d.row_bytes), fill, dtype=torch.int8, device=dev)
+                       for _ in range(replicas)]
+        self.pools = [torch.zeros((npools, d.idx_dim), dtype=torch.bfloat16, device=dev)
+                      for _ in range(replicas)]
+        self.k = torch.zeros((toks, d.idx_dim), dtype=torch.bfloat16, device=dev)
+        self.gate = torch.zeros((toks, d.idx_dim), dtype=torch.bfloat16, device=dev)
+        lw, lb = syn.gen_ln(wl)
+        self.ln_w, self.ln_b = _f32(lw, dev), _f32(lb, dev)
+        # Per-query inputs.
+        self.q_idx = _bits_to_bf16(syn.gen_qidx(wl, 0, T), dev)
+        self.w = _f32(syn.gen_w(wl, 0, T), dev)
+        qv = syn.gen_q(wl, 0, T)
+        self.q = _f32(qv, dev) if wl.fp32_mla else _bits_to_bf16(qv, dev)
+        # The step's new tokens: the query positions themselves.
+        lat = np.concatenate([syn.gen_latent(wl, int(b), int(x), int(x) + 1)
+                              for b, x in zip(wl.q_seq, wl.q_pos)], axis=0) if T else \
+            np.zeros((0, d.latent_dim), np.float32)
+        self.latent_q = _f32(lat, dev) if wl.fp32_mla else _bits_to_bf16(lat, dev)
+        self.slots_q = torch.tensor(wl.row_base[wl.q_seq] + wl.q_pos, dtype=torch.int64, device=dev)
+        # Pools the step's tokens complete: pool p ends at position f + kpool*p + kpool - 1.
+        pb, pe = [], []
+        for b in range(wl.B):
+            f = int(wl.first_valid[b])
+            ends = [(int(x) - f + 1) // d.kpool for x in wl.q_pos[wl.q_seq == b]
+                    if int(x) >= f and (int(x) - f + 1) % d.kpool == 0]
+            if ends:
+                pb.append(min(ends) - 1)
+                pe.append(max(ends))
+            else:
+                pb.append(0)
+                pe.append(0)
+        self.step_pool_begin = torch.tensor(pb, dtype=torch.int32, device=dev)
+        self.step_pool_end = torch.tensor(pe, dtype=torch.int32, device=dev)
+        self.step_max_pools = max([e - s for s, e in zip(pb, pe)] + [0])
+        # Outputs and workspaces.
+        self.stride = score_stride or max(256, -(-max(wl.max_n_vis, 1) // 256) * 256)
+        self.scores = torch.empty((T, self.stride), dtype=torch.float32, device=dev)
+        self.pool_ids = torch.empty((T, d.select_k), dtype=torch.int32, device=dev)
+        self.indices = torch.empty((T, d.out_width), dtype=torch.int32, device=dev)
+        self.out = torch.empty((T, d.mla_heads, d.latent_dim), dtype=out_dtype, device=dev)
+        self.lse = torch.empty((T, d.mla_heads), dtype=torch.float32, device=dev)
+        self.ws_topk = dsa.topk_workspace(self.dims, T, self.stride, device=dev)
+        n = dsa.sparse_mla_workspace_bytes(self.dims, T, num_splits)
+        self.ws_mla = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
+        if build:
+            self.build_caches()
+
+    # ------------------------------------------------------------------ setup
+    def build_caches(self):
+        """Store every position's INT8 row and build every complete pool (replica 0, then copies)."""
+        wl, d, dev = self.wl, self.wl.dims, self.device
+        cache, pools = self.caches[0], self.pools[0]
+        for b in range(wl.B):
+            n = int(wl.seq_len[b])
+            rb, tb = int(wl.row_base[b]), int(wl.tok_base[b])
+            for x0, lat in syn.gen_sequence_blocks(syn.gen_latent, wl, b, 0, n, workers=self.gen_workers):
+                lt = _f32(lat, dev) if wl.fp32_mla else _bits_to_bf16(lat, dev)
+                slots = torch.arange(rb + x0, rb + x0 + lat.shape[0], dtype=torch.int64, device=dev)
+                dsa.store_int8(self.dims, lt, slots, cache)
+            for x0, (k, g) in syn.gen_sequence_blocks(syn.gen_kgate, wl, b, 0, n, workers=self.gen_workers):
+                self.k[tb + x0: tb + x0 + k.shape[0]] = _bits_to_bf16(k, dev)
+                self.gate[tb + x0: tb + x0 + g.shape[0]] = _bits_to_bf16(g, dev)
+        ends = [wl.n_pools(b) for b in range(wl.B)]
+        if max(ends) > 0:
+            dsa.index_pools(self.dims, self.k, self.gate, self.ln_w, self.ln_b, self.seqs,
+                            torch.zeros(wl.B, dtype=torch.int32, device=dev),
+                            torch.tensor(ends, dtype=torch.int32, device=dev), max(ends), pools)
+        for r in range(1, len(self.caches)):
+            self.caches[r].copy_(cache)
+            self.pools[r].copy_(pools)
+        torch.cuda.synchronize()
+
+    # ------------------------------------------------------------------ the step
+    def step_store(self, r: int = 0):
+        dsa.store_int8(self.dims, self.latent_q, self.slots_q, self.caches[r])
+
+    def step_pools(self, r: int = 0):
+        if self.step_max_pools > 0:
+            dsa.index_pools(self.dims, self.k, self.gate, self.ln_w, self.ln_b, self.seqs,
+                            self.step_pool_begin, self.step_pool_end, self.step_max_pools, self.pools[r])
+
+    def step_scores(self, r: int = 0):
+        dsa.index_scores(self.dims, self.q_idx, self.w, self.pools[r], self.seqs, self.q_seq, self.q_pos,
+                         self.scores)
+
+    def step_topk(self):
+        dsa.topk_select(self.dims, self.scores, self.seqs, self.q_seq, self.q_pos, self.pool_ids, self.ws_topk)
+
+    def step_expand(self):
+        dsa.expand_selection(self.dims, self.pool_ids, self.seqs, self.q_seq, self.q_pos, self.indices)
+
+    def step_attention(self, r: int = 0):
+        dsa.sparse_mla(self.dims, self.q, self.caches[r], self.indices, self.wl.scale, self.out, self.lse,
+                       self.num_splits, self.ws_mla)
+
+    def step(self, r: int = 0):
+        """One pass of the whole path over replica r."""
+        self.step_store(r)
+        self.step_pools(r)
+        self.step_scores(r)
+        self.step_topk()
+        self.step_expand()
+        self.step_attention(r)

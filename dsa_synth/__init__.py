@@ -398,3 +398,76 @@ WORKLOADS = {
 
 def get(name: str) -> Workload:
     return WORKLOADS[name]()
+
+
+# ----------------------------------------------------------------------------
+# parallel block generation (large contexts)
+# ----------------------------------------------------------------------------
+
+def gen_sequence_blocks(fn, wl: Workload, b: int, x0: int, x1: int, workers: int = 8, step: int = 65536):
+    """Yield (x, arrays) chunks of fn(wl, b, x, x+step) over [x0, x1), generated by a thread pool.
+
+    numpy's Philox fills release the GIL, so blocks generate in parallel."""
+    import concurrent.futures as cf
+    starts = list(range(x0, x1, step))
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        futs = [ex.submit(fn, wl, b, s, min(s + step, x1)) for s in starts]
+        for s, fu in zip(starts, futs):
+            yield s, fu.result()
+
+
+# ----------------------------------------------------------------------------
+# synthetic score rows and index lists (inputs for stage-isolated tests)
+# ----------------------------------------------------------------------------
+
+def gen_score_rows(seed: int, T: int, stride: int, n_vis: np.ndarray, kind: str = "ties") -> np.ndarray:
+    """Float32 score rows [T, stride]; entries past n_vis[t] are -inf.
+
+    kind: "ties" (values on a coarse grid so many scores tie), "normal",
+    "equal" (all visible scores equal), "signed_zero" (+0/-0 and small
+    negatives)."""
+    out = np.full((T, stride), -np.inf, dtype=np.float32)
+    for t in range(T):
+        g = _rng(seed, "queries", t, 7)
+        n = int(n_vis[t])
+        if kind == "ties":
+            v = np.round(g.standard_normal(n) * 8.0) / 4.0 + 10.0
+        elif kind == "normal":
+            v = g.standard_normal(n) * 3.0 + 20.0
+        elif kind == "equal":
+            v = np.full(n, 1.5)
+        elif kind == "signed_zero":
+            v = np.where(g.random(n) < 0.5, 0.0, -0.0)
+            v = np.where(g.random(n) < 0.3, -np.round(g.random(n) * 4) / 4, v)
+        else:
+            raise ValueError(kind)
+        out[t, :n] = v.astype(np.float32)
+    return out
+
+
+def gen_index_lists(seed: int, T: int, width: int, candidates: np.ndarray, valid: np.ndarray,
+                    interior_gaps: bool = True) -> np.ndarray:
+    """int32 [T, width] lists of distinct rows drawn from `candidates`: valid[t] entries, -1 elsewhere.
+
+    With interior_gaps, the -1 entries are scattered among the valid ones (the
+    attention contract skips negative entries wherever they sit)."""
+    candidates = np.asarray(candidates, dtype=np.int64)
+    out = np.full((T, width), -1, dtype=np.int32)
+    for t in range(T):
+        g = _rng(seed, "queries", t, 9)
+        k = int(valid[t])
+        if k == 0:
+            continue
+        rows = np.sort(g.choice(candidates, size=k, replace=False)).astype(np.int32)
+        if interior_gaps and k < width:
+            slots = np.sort(g.choice(width, size=k, replace=False))
+            out[t, slots] = rows
+        else:
+            out[t, :k] = rows
+    return out
+
+
+def valid_rows(wl: Workload) -> np.ndarray:
+    """Cache rows of every non-padding position of the workload."""
+    return np.concatenate([np.arange(int(wl.first_valid[b]), int(wl.seq_len[b])) + int(wl.row_base[b])
+                           for b in range(wl.B)]).astype(np.int64)

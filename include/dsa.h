@@ -1,0 +1,223 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) DeepSeek-Sparse-Attention path used by
+ * GLM-5.3-Flash: kpool indexer (pools, scores, top-k, expansion) and sparse
+ * NoPE MLA over an INT8 latent cache.
+ *
+ * Page citations use these short names:
+ *   [Flash]   "GLM-5.3-Flash" (pypto-lib model staging page)
+ *   [Kernels] "GLM-5.3 Kernels" (store_int8 / sparse MLA kernel release)
+ *   [Ref]     "Module glm5next_dsa_ref" (DSA + kpool indexer CPU reference docs)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Pointers documented as "device" point to GPU memory on the device that is
+ *    current for the calling thread; "host" pointers are read before the call
+ *    returns.  The caller owns every buffer, including workspaces; the library
+ *    allocates nothing and keeps no per-call state (it caches device
+ *    properties only) and is safe to call from several host threads.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream), never synchronises, and returns a dsa_status.  Only host-visible
+ *    arguments are validated; on any error nothing is launched.  Device data
+ *    (slots, indices, positions, lengths) is trusted: out-of-range positive
+ *    indices and duplicate slots are outside the contract, as for the pages'
+ *    low-level API ([Kernels] Install: contract paragraph).
+ *  - Outputs are written, never read-modify-written, and every entry of every
+ *    output is written, so uninitialised destinations are safe ([Ref] Traps:
+ *    the sentinel and the fully written destination).
+ *  - bf16 buffers hold raw bf16 bit patterns (uint16_t).
+ *  - Position x of sequence b (0 <= x < its length) lives at cache row
+ *    row_base[b] + x and at indexer-state row tok_base[b] + x; positions below
+ *    first_valid[b] are left padding.  Pool p of sequence b lives at pool row
+ *    pool_base[b] + p and covers positions first_valid[b] + kpool*p + s,
+ *    s in [0, kpool) ([Ref] Traps: pools start at the first valid token).
+ *  - A query at position q_pos of sequence b sees positions first_valid[b]..
+ *    q_pos (itself included) and the n_vis = (q_pos - first_valid + 1) / kpool
+ *    pools whose slots all lie in that range (0 when q_pos < first_valid)
+ *    ([Ref] Functions: visible; Traps: a pool needs all of its slots).
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+typedef enum dsa_status {
+    DSA_OK = 0,
+    DSA_ERR_NULL = -1,        /* a required pointer is NULL */
+    DSA_ERR_DIMS = -2,        /* inconsistent or non-positive dims */
+    DSA_ERR_DTYPE = -3,       /* dtype code not accepted by this call */
+    DSA_ERR_ALIGN = -4,       /* pointer or leading dimension misaligned */
+    DSA_ERR_WIDTH = -5,       /* out_width < index_topk + kpool - 1 */
+    DSA_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required */
+    DSA_ERR_UNSUPPORTED = -7, /* valid dims this build has no kernel for */
+    DSA_ERR_HIP = -8,         /* a HIP runtime call or launch failed */
+    DSA_ERR_SIZE = -9         /* negative count or a stride smaller than needed */
+} dsa_status;
+
+typedef enum dsa_dtype {
+    DSA_F32 = 0,
+    DSA_BF16 = 1
+} dsa_dtype;
+
+/*
+ * Indexer + MLA geometry, read from the model config and never defaulted
+ * ([Ref] Structs: DsaDims).  GLM-5.3-Flash: idx_heads 32, idx_dim 128,
+ * kpool 4, index_topk 2048 ([Flash] checkpoint table), out_width 2176,
+ * latent_dim 512, row_bytes 528, mla_heads 16 per rank ([Kernels] Included).
+ * Required: all positive; index_topk % kpool == 0 (select_k = index_topk /
+ * kpool pools); out_width >= index_topk + kpool - 1; row_bytes ==
+ * round_up(latent_dim + 4, 16); ln_eps >= 0.
+ */
+typedef struct dsa_dims {
+    int32_t idx_heads;
+    int32_t idx_dim;
+    int32_t kpool;
+    int32_t index_topk;
+    int32_t out_width;
+    int32_t mla_heads;
+    int32_t latent_dim;
+    int32_t row_bytes;
+    float ln_eps;
+} dsa_dims;
+
+/* Per-sequence layout; every pointer is a device array of num_seqs entries. */
+typedef struct dsa_seqs {
+    const int32_t* first_valid;  /* left-padding length f_b (first valid position) */
+    const int64_t* row_base;     /* cache row of position 0 */
+    const int64_t* tok_base;     /* indexer-state (k, gate) row of position 0 */
+    const int64_t* pool_base;    /* pool row of pool 0 */
+} dsa_seqs;
+
+int dsa_abi_version(void);
+const char* dsa_status_string(int status);
+
+/*
+ * store_int8 -- [Kernels] Included: each latent row becomes one INT8 row of
+ * row_bytes bytes: latent_dim int8 codes, then the fp32 scale (little endian),
+ * then zero bytes up to row_bytes (512 + 4 + 12 = 528).  Per row:
+ *   amax = max|x|, s = fp32(max(amax, 1e-4) / 127) (IEEE division),
+ *   code = clamp(round_half_even(fp32(x / s)), -127, 127).
+ *   latent  device, [n, ld] of latent_dtype (DSA_BF16 or DSA_F32), rows of
+ *           latent_dim contiguous values; 16-byte aligned base and row pitch.
+ *   slots   device int64 [n]: destination cache row of each latent row;
+ *           negative = skip (padding).  Must be < cache_rows and distinct.
+ *   cache   device, [cache_rows, row_bytes] bytes, 16-byte aligned.
+ */
+int dsa_store_int8(const dsa_dims* dims, const void* latent, int latent_dtype,
+                   int64_t n, int64_t ld, const int64_t* slots,
+                   int8_t* cache, int64_t cache_rows, void* stream);
+
+/*
+ * index_pools -- [Ref] Traps and Functions (layer_norm, pool_states): for
+ * every pool p in [pool_begin[b], pool_end[b]) of every sequence b,
+ *   y_s = LayerNorm(k[t_s]) * ln_w + ln_b   (mean-subtracted, biased variance, ln_eps)
+ *   a_s[c] = softmax over the kpool slots s of gate[t_s][c]   (per channel)
+ *   pool[p][c] = sum_s a_s[c] * y_s[c], stored as bf16 (round to nearest even)
+ * with t_s = tok_base[b] + first_valid[b] + kpool*p + s.
+ *   k, gate     device [tokens, idx_dim] of kg_dtype (DSA_BF16 or DSA_F32)
+ *   ln_w, ln_b  device fp32 [idx_dim]
+ *   pool_begin, pool_end  device int32 [num_seqs]; the caller guarantees that
+ *               all kpool tokens of every listed pool exist.
+ *   max_pools   host: >= max_b (pool_end[b] - pool_begin[b]) (sizes the grid)
+ *   pools       device bf16 [*, idx_dim]
+ * Supported: kpool 4, idx_dim in {32, 128}.
+ */
+int dsa_index_pools(const dsa_dims* dims, const void* k, const void* gate, int kg_dtype,
+                    const float* ln_w, const float* ln_b, const dsa_seqs* seqs,
+                    int32_t num_seqs, const int32_t* pool_begin, const int32_t* pool_end,
+                    int32_t max_pools, uint16_t* pools, void* stream);
+
+/*
+ * index_scores -- [Ref] Functions (index_scores): matmul, ReLU, head-weighted
+ * sum.  For query t (sequence q_seq[t], position q_pos[t]) and pool p:
+ *   scores[t][p] = sum_h w[t][h] * max(0, q_idx[t][h] . pool[p])   for p < n_vis(t)
+ *   scores[t][p] = -inf                                            for n_vis(t) <= p < score_stride
+ * bf16 products, fp32 accumulation.
+ *   q_idx   device bf16 [T, idx_heads, idx_dim]; w device fp32 [T, idx_heads]
+ *   pools   device bf16; rows pool_base[b] + p must hold built pools for every
+ *           p < n_vis(t) of every query t of sequence b
+ *   q_seq, q_pos  device int32 [T]
+ *   scores  device fp32 [T, score_stride]; score_stride must be >= every
+ *           query's n_vis.
+ * Uses the MFMA kernel for idx_heads 32 x idx_dim 128, a vector kernel otherwise.
+ */
+int dsa_index_scores(const dsa_dims* dims, const uint16_t* q_idx, const float* w,
+                     const uint16_t* pools, const dsa_seqs* seqs, int32_t num_seqs,
+                     const int32_t* q_seq, const int32_t* q_pos, int32_t T,
+                     int32_t score_stride, float* scores, void* stream);
+
+/*
+ * topk_select -- [Ref] Functions (topk_pools); [Flash] Stream C
+ * (indexer_topk512): select K = min(select_k, n_vis(t)) pools per query by
+ * (score descending, pool id ascending; -0 equals +0), and write their ids
+ * in ascending order to pool_ids[t][0..K), then -1 up to select_k.  When
+ * n_vis <= select_k every visible pool is selected.  NaN scores are outside
+ * the contract.
+ *   scores    device fp32 [T, score_stride] (as written by dsa_index_scores)
+ *   pool_ids  device int32 [T, select_k]
+ *   workspace device, >= dsa_topk_workspace_bytes(dims, T, score_stride) bytes,
+ *             256-byte aligned.  It must be zero-filled before its first use;
+ *             every call that completes returns the counters and histograms it
+ *             uses to zero (the rest is scratch), so it can be reused without
+ *             clearing.  Calls sharing one workspace must not overlap.  May be
+ *             NULL when the size query returns 0.
+ */
+size_t dsa_topk_workspace_bytes(const dsa_dims* dims, int32_t T, int32_t score_stride);
+int dsa_topk_select(const dsa_dims* dims, const float* scores, int32_t score_stride,
+                    const dsa_seqs* seqs, int32_t num_seqs, const int32_t* q_seq,
+                    const int32_t* q_pos, int32_t T, int32_t* pool_ids,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * expand_selection -- [Ref] Functions (expand_selection) and Traps (the -1
+ * sentinel, fully written output): for each query, the selected pools (the
+ * leading non-negative entries of pool_ids[t], ascending) become their kpool
+ * cache rows row_base + first_valid + kpool*p + s, then the visible tail
+ * positions first_valid + kpool*n_vis .. q_pos follow (at most kpool - 1),
+ * then -1 fills the row up to out_width.
+ *   pool_ids  device int32 [T, select_k], front-packed
+ *   indices   device int32 [T, out_width]
+ */
+int dsa_expand_selection(const dsa_dims* dims, const int32_t* pool_ids, const dsa_seqs* seqs,
+                         int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos,
+                         int32_t T, int32_t* indices, void* stream);
+
+/*
+ * sparse_mla -- [Kernels] Included and Install (triton_mla_sparse_attention:
+ * fused INT8 dequant, one shared K/V latent, split-KV decode, bf16 products,
+ * fp32 softmax); [Ref] Functions (mla_masked_attention).  For query t, head h:
+ *   J = { j : indices[t][j] >= 0 },  K_j = V_j = code_j * scale_j (the stored row)
+ *   z_j = scale * q[t][h] . K_j,  out[t][h] = sum_j softmax_j(z) V_j,
+ *   lse[t][h] = log(sum_j exp(z_j)) (natural log).
+ * Negative entries are skipped wherever they sit; an empty J gives out = 0
+ * and lse = -inf.  Bitwise run-to-run deterministic for a fixed num_splits.
+ *   q        device [T, mla_heads, latent_dim] of q_dtype (DSA_BF16 or DSA_F32)
+ *   cache    device [cache_rows, row_bytes] (rows written by dsa_store_int8)
+ *   indices  device int32 [T, out_width]; valid entries < cache_rows
+ *   out      device [T, mla_heads, latent_dim] of out_dtype (DSA_F32 or DSA_BF16)
+ *   lse      device fp32 [T, mla_heads] or NULL
+ *   num_splits  0 = choose from T, heads and the device's CU count; otherwise
+ *            the number of list partitions per query (clamped to what the
+ *            list width allows).
+ *   workspace device, >= dsa_sparse_mla_workspace_bytes(dims, T, num_splits)
+ *            bytes, 256-byte aligned (NULL allowed when that size is 0).
+ * bf16 q with latent_dim 512 and mla_heads % 16 == 0 runs on MFMA; other
+ * shapes and fp32 q use an fp32 vector kernel.
+ */
+size_t dsa_sparse_mla_workspace_bytes(const dsa_dims* dims, int32_t T, int32_t num_splits);
+int dsa_sparse_mla(const dsa_dims* dims, const void* q, int q_dtype, const int8_t* cache,
+                   int64_t cache_rows, const int32_t* indices, int32_t T, float scale,
+                   void* out, int out_dtype, float* lse, int32_t num_splits,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

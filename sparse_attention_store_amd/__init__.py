@@ -1,0 +1,280 @@
+"""Python binding of libdsa, the gfx950 DSA decode/prefill path.
+
+Thin ctypes marshalling over the C ABI declared in include/dsa.h: each
+function checks tensor dtypes/devices/shapes, passes device pointers, the
+dims struct and the current HIP stream, and raises DsaError on a non-zero
+status.  Every step of the path runs in the library's HIP kernels; PyTorch
+only provides device memory and streams.  There is no fallback: if the
+shared library is missing, importing any entry point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+DSA_F32 = 0
+DSA_BF16 = 1
+
+
+class DsaError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    """Mirror of dsa_dims (indexer + MLA geometry)."""
+    _fields_ = [
+        ("idx_heads", ctypes.c_int32), ("idx_dim", ctypes.c_int32),
+        ("kpool", ctypes.c_int32), ("index_topk", ctypes.c_int32),
+        ("out_width", ctypes.c_int32), ("mla_heads", ctypes.c_int32),
+        ("latent_dim", ctypes.c_int32), ("row_bytes", ctypes.c_int32),
+        ("ln_eps", ctypes.c_float),
+    ]
+
+    @classmethod
+    def of(cls, d) -> "Dims":
+        """Build from any object with the same attribute names."""
+        return cls(int(d.idx_heads), int(d.idx_dim), int(d.kpool), int(d.index_topk),
+                   int(d.out_width), int(d.mla_heads), int(d.latent_dim), int(d.row_bytes),
+                   float(d.ln_eps))
+
+    @property
+    def select_k(self) -> int:
+        return self.index_topk // self.kpool
+
+
+class _Seqs(ctypes.Structure):
+    _fields_ = [("first_valid", ctypes.c_void_p), ("row_base", ctypes.c_void_p),
+                ("tok_base", ctypes.c_void_p), ("pool_base", ctypes.c_void_p)]
+
+
+@dataclass
+class Seqs:
+    """Per-sequence layout as device tensors (int32 first_valid, int64 bases)."""
+    first_valid: torch.Tensor
+    row_base: torch.Tensor
+    tok_base: torch.Tensor
+    pool_base: torch.Tensor
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.first_valid.shape[0])
+
+    def _c(self) -> _Seqs:
+        for name, t, dt in (("first_valid", self.first_valid, torch.int32),
+                            ("row_base", self.row_base, torch.int64),
+                            ("tok_base", self.tok_base, torch.int64),
+                            ("pool_base", self.pool_base, torch.int64)):
+            _check(t, dt, name)
+        return _Seqs(self.first_valid.data_ptr(), self.row_base.data_ptr(),
+                     self.tok_base.data_ptr(), self.pool_base.data_ptr())
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdsa.so once; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m sparse_attention_store_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+        DP, SP = ctypes.POINTER(Dims), ctypes.POINTER(_Seqs)
+        sig = {
+            "dsa_abi_version": (ctypes.c_int, []),
+            "dsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+            "dsa_store_int8": (ctypes.c_int, [DP, P, ctypes.c_int, I64, I64, P, P, I64, P]),
+            "dsa_index_pools": (ctypes.c_int, [DP, P, P, ctypes.c_int, P, P, SP, I32, P, P, I32, P, P]),
+            "dsa_index_scores": (ctypes.c_int, [DP, P, P, P, SP, I32, P, P, I32, I32, P, P]),
+            "dsa_topk_workspace_bytes": (SZ, [DP, I32, I32]),
+            "dsa_topk_select": (ctypes.c_int, [DP, P, I32, SP, I32, P, P, I32, P, P, SZ, P]),
+            "dsa_expand_selection": (ctypes.c_int, [DP, P, SP, I32, P, P, I32, P, P]),
+            "dsa_sparse_mla_workspace_bytes": (SZ, [DP, I32, I32]),
+            "dsa_sparse_mla": (ctypes.c_int, [DP, P, ctypes.c_int, P, I64, P, I32, F, P, ctypes.c_int, P, I32,
+                                              P, SZ, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(t: torch.Tensor, dtype, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _raise(fn: str, st: int):
+    if st != 0:
+        raise DsaError(fn, st, lib().dsa_status_string(st).decode())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DSA_F32
+    if t.dtype == torch.bfloat16:
+        return DSA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def abi_version() -> int:
+    return lib().dsa_abi_version()
+
+
+def status_string(status: int) -> str:
+    return lib().dsa_status_string(status).decode()
+
+
+def store_int8(dims: Dims, latent: torch.Tensor, slots: torch.Tensor, cache: torch.Tensor, stream=None):
+    """Quantise latent rows [n, D] (bf16/fp32) into INT8 rows of cache [rows, row_bytes] at slots."""
+    if latent.dim() != 2 or latent.stride(1) != 1:
+        raise ValueError("latent must be [n, D] with unit stride in D")
+    if latent.dtype not in (torch.bfloat16, torch.float32) or not latent.is_cuda:
+        raise TypeError("latent must be a bf16/fp32 device tensor")
+    _check(slots, torch.int64, "slots")
+    _check(cache, torch.int8, "cache")
+    if slots.numel() != latent.shape[0]:
+        raise ValueError("slots must have one entry per latent row")
+    _raise("dsa_store_int8", lib().dsa_store_int8(
+        ctypes.byref(dims), latent.data_ptr(), _dt(latent), latent.shape[0], latent.stride(0),
+        slots.data_ptr(), cache.data_ptr(), cache.shape[0], _stream(stream)))
+
+
+def index_pools(dims: Dims, k: torch.Tensor, gate: torch.Tensor, ln_w: torch.Tensor, ln_b: torch.Tensor,
+                seqs: Seqs, pool_begin: torch.Tensor, pool_end: torch.Tensor, max_pools: int,
+                pools: torch.Tensor, stream=None):
+    """Build pools [pool_begin[b], pool_end[b]) of each sequence into pools (bf16 [*, idx_dim])."""
+    if k.dtype != gate.dtype:
+        raise TypeError("k and gate must share a dtype")
+    for name, t in (("k", k), ("gate", gate)):
+        _check(t, k.dtype, name)
+    _check(ln_w, torch.float32, "ln_w")
+    _check(ln_b, torch.float32, "ln_b")
+    _check(pool_begin, torch.int32, "pool_begin")
+    _check(pool_end, torch.int32, "pool_end")
+    _check(pools, torch.bfloat16, "pools")
+    _raise("dsa_index_pools", lib().dsa_index_pools(
+        ctypes.byref(dims), k.data_ptr(), gate.data_ptr(), _dt(k), ln_w.data_ptr(), ln_b.data_ptr(),
+        ctypes.byref(seqs._c()), seqs.num_seqs, pool_begin.data_ptr(), pool_end.data_ptr(),
+        int(max_pools), pools.data_ptr(), _stream(stream)))
+
+
+def index_scores(dims: Dims, q_idx: torch.Tensor, w: torch.Tensor, pools: torch.Tensor, seqs: Seqs,
+                 q_seq: torch.Tensor, q_pos: torch.Tensor, scores: torch.Tensor, stream=None):
+    """scores [T, stride] (fp32) from q_idx [T, Hi, Di] (bf16), w [T, Hi] (fp32), pools (bf16)."""
+    _check(q_idx, torch.bfloat16, "q_idx")
+    _check(w, torch.float32, "w")
+    _check(pools, torch.bfloat16, "pools")
+    _check(q_seq, torch.int32, "q_seq")
+    _check(q_pos, torch.int32, "q_pos")
+    _check(scores, torch.float32, "scores")
+    T = q_pos.shape[0]
+    if scores.dim() != 2 or scores.shape[0] != T:
+        raise ValueError("scores must be [T, stride]")
+    _raise("dsa_index_scores", lib().dsa_index_scores(
+        ctypes.byref(dims), q_idx.data_ptr(), w.data_ptr(), pools.data_ptr(), ctypes.byref(seqs._c()),
+        seqs.num_seqs, q_seq.data_ptr(), q_pos.data_ptr(), T, scores.shape[1], scores.data_ptr(),
+        _stream(stream)))
+
+
+def topk_workspace_bytes(dims: Dims, T: int, score_stride: int) -> int:
+    return int(lib().dsa_topk_workspace_bytes(ctypes.byref(dims), int(T), int(score_stride)))
+
+
+def topk_workspace(dims: Dims, T: int, score_stride: int, device="cuda") -> torch.Tensor | None:
+    """A zero-filled workspace of the required size (None when no workspace is needed)."""
+    n = topk_workspace_bytes(dims, T, score_stride)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+
+def topk_select(dims: Dims, scores: torch.Tensor, seqs: Seqs, q_seq: torch.Tensor, q_pos: torch.Tensor,
+                pool_ids: torch.Tensor, workspace: torch.Tensor | None = None, stream=None):
+    """pool_ids [T, select_k] (int32): ascending selected pool ids, -1 padded."""
+    _check(scores, torch.float32, "scores")
+    _check(pool_ids, torch.int32, "pool_ids")
+    _check(q_seq, torch.int32, "q_seq")
+    _check(q_pos, torch.int32, "q_pos")
+    T = q_pos.shape[0]
+    ws_bytes = 0
+    if workspace is not None:
+        _check(workspace, workspace.dtype, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _raise("dsa_topk_select", lib().dsa_topk_select(
+        ctypes.byref(dims), scores.data_ptr(), scores.shape[1], ctypes.byref(seqs._c()), seqs.num_seqs,
+        q_seq.data_ptr(), q_pos.data_ptr(), T, pool_ids.data_ptr(), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
+def expand_selection(dims: Dims, pool_ids: torch.Tensor, seqs: Seqs, q_seq: torch.Tensor,
+                     q_pos: torch.Tensor, indices: torch.Tensor, stream=None):
+    """indices [T, out_width] (int32) from pool_ids [T, select_k]."""
+    _check(pool_ids, torch.int32, "pool_ids")
+    _check(indices, torch.int32, "indices")
+    _check(q_seq, torch.int32, "q_seq")
+    _check(q_pos, torch.int32, "q_pos")
+    _raise("dsa_expand_selection", lib().dsa_expand_selection(
+        ctypes.byref(dims), pool_ids.data_ptr(), ctypes.byref(seqs._c()), seqs.num_seqs,
+        q_seq.data_ptr(), q_pos.data_ptr(), q_pos.shape[0], indices.data_ptr(), _stream(stream)))
+
+
+def sparse_mla_workspace_bytes(dims: Dims, T: int, num_splits: int = 0) -> int:
+    return int(lib().dsa_sparse_mla_workspace_bytes(ctypes.byref(dims), int(T), int(num_splits)))
+
+
+def sparse_mla(dims: Dims, q: torch.Tensor, cache: torch.Tensor, indices: torch.Tensor, scale: float,
+               out: torch.Tensor, lse: torch.Tensor | None = None, num_splits: int = 0,
+               workspace: torch.Tensor | None = None, stream=None):
+    """out [T, H, D] = sparse NoPE MLA of q [T, H, D] over the INT8 rows listed in indices [T, W]."""
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q must be bf16 or fp32")
+    _check(q, q.dtype, "q")
+    _check(cache, torch.int8, "cache")
+    _check(indices, torch.int32, "indices")
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bf16 or fp32")
+    _check(out, out.dtype, "out")
+    if lse is not None:
+        _check(lse, torch.float32, "lse")
+    T = q.shape[0]
+    ws_bytes = 0
+    if workspace is not None:
+        _check(workspace, workspace.dtype, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _raise("dsa_sparse_mla", lib().dsa_sparse_mla(
+        ctypes.byref(dims), q.data_ptr(), _dt(q), cache.data_ptr(), cache.shape[0], indices.data_ptr(),
+        T, float(scale), out.data_ptr(), _dt(out), _ptr(lse), int(num_splits), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
+__all__ = [
+    "DSA_F32", "DSA_BF16", "DsaError", "Dims", "Seqs", "lib", "abi_version", "status_string",
+    "store_int8", "index_pools", "index_scores", "topk_workspace_bytes", "topk_workspace",
+    "topk_select", "expand_selection", "sparse_mla_workspace_bytes", "sparse_mla",
+]

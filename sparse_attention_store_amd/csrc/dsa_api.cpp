@@ -1,0 +1,220 @@
+// C ABI entry points: argument validation, dispatch, status codes.
+// Only host-visible arguments are checked; device contents are trusted.
+// Nothing here allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <vector>
+
+#include "dsa.h"
+#include "dsa_common.h"
+#include "dsa_launch.h"
+
+namespace dsa_host {
+
+DeviceInfo device_info() {
+    static std::mutex mu;
+    static std::vector<DeviceInfo> cache;
+    static std::vector<bool> have;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)cache.size() <= dev) {
+        cache.resize(dev + 1);
+        have.resize(dev + 1, false);
+    }
+    if (!have[dev]) {
+        DeviceInfo info{256, 160 * 1024};
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) == hipSuccess) {
+            info.cu_count = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+            if (prop.sharedMemPerBlock > 0) info.max_lds_per_block = prop.sharedMemPerBlock;
+        }
+        cache[dev] = info;
+        have[dev] = true;
+    }
+    return cache[dev];
+}
+
+}  // namespace dsa_host
+
+namespace {
+
+using dsa_host::cdiv;
+
+int check_dims(const dsa_dims* d) {
+    if (!d) return DSA_ERR_NULL;
+    if (d->idx_heads <= 0 || d->idx_dim <= 0 || d->kpool <= 0 || d->index_topk <= 0 ||
+        d->out_width <= 0 || d->mla_heads <= 0 || d->latent_dim <= 0 || d->row_bytes <= 0 ||
+        !(d->ln_eps >= 0.0f))
+        return DSA_ERR_DIMS;
+    if (d->index_topk % d->kpool != 0) return DSA_ERR_DIMS;
+    if (d->row_bytes != (int)(((d->latent_dim + 4 + 15) / 16) * 16)) return DSA_ERR_DIMS;
+    if (d->out_width < d->index_topk + d->kpool - 1) return DSA_ERR_WIDTH;
+    return DSA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int check_seqs(const dsa_seqs* s, int32_t num_seqs, bool need_row, bool need_tok, bool need_pool) {
+    if (!s) return DSA_ERR_NULL;
+    if (num_seqs <= 0) return DSA_ERR_SIZE;
+    if (!s->first_valid) return DSA_ERR_NULL;
+    if (need_row && !s->row_base) return DSA_ERR_NULL;
+    if (need_tok && !s->tok_base) return DSA_ERR_NULL;
+    if (need_pool && !s->pool_base) return DSA_ERR_NULL;
+    return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+const char* dsa_status_string(int status) {
+    switch (status) {
+        case DSA_OK: return "ok";
+        case DSA_ERR_NULL: return "a required pointer is NULL";
+        case DSA_ERR_DIMS: return "inconsistent or non-positive dims";
+        case DSA_ERR_DTYPE: return "dtype not accepted by this call";
+        case DSA_ERR_ALIGN: return "pointer or leading dimension misaligned";
+        case DSA_ERR_WIDTH: return "out_width < index_topk + kpool - 1";
+        case DSA_ERR_WORKSPACE: return "workspace missing or too small";
+        case DSA_ERR_UNSUPPORTED: return "dims not supported by this build";
+        case DSA_ERR_HIP: return "HIP runtime error";
+        case DSA_ERR_SIZE: return "negative count or stride too small";
+        default: return "unknown status";
+    }
+}
+
+int dsa_store_int8(const dsa_dims* dims, const void* latent, int latent_dtype, int64_t n,
+                   int64_t ld, const int64_t* slots, int8_t* cache, int64_t cache_rows,
+                   void* stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (n < 0 || cache_rows < 0) return DSA_ERR_SIZE;
+    if (latent_dtype != DSA_F32 && latent_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    const int D = dims->latent_dim;
+    if (D != 64 && D != 128 && D != 256 && D != 512) return DSA_ERR_UNSUPPORTED;
+    if (n == 0) return DSA_OK;
+    if (!latent || !slots || !cache) return DSA_ERR_NULL;
+    if (ld < D) return DSA_ERR_SIZE;
+    const size_t esz = latent_dtype == DSA_F32 ? 4 : 2;
+    if (!aligned(latent, 16) || (ld * esz) % 16 != 0 || !aligned(cache, 16)) return DSA_ERR_ALIGN;
+    return hip_status(dsa_host::launch_store_int8(*dims, latent, latent_dtype, n, ld, slots, cache,
+                                                  as_stream(stream)));
+}
+
+int dsa_index_pools(const dsa_dims* dims, const void* k, const void* gate, int kg_dtype,
+                    const float* ln_w, const float* ln_b, const dsa_seqs* seqs, int32_t num_seqs,
+                    const int32_t* pool_begin, const int32_t* pool_end, int32_t max_pools,
+                    uint16_t* pools, void* stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (kg_dtype != DSA_F32 && kg_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    if (dims->kpool != 4 || (dims->idx_dim != 128 && dims->idx_dim != 32)) return DSA_ERR_UNSUPPORTED;
+    if (max_pools < 0) return DSA_ERR_SIZE;
+    st = check_seqs(seqs, num_seqs, false, true, true);
+    if (st) return st;
+    if (num_seqs > 65535) return DSA_ERR_SIZE;
+    if (max_pools == 0) return DSA_OK;
+    if (!k || !gate || !ln_w || !ln_b || !pool_begin || !pool_end || !pools) return DSA_ERR_NULL;
+    if (!aligned(k, 4) || !aligned(gate, 4) || !aligned(pools, 4)) return DSA_ERR_ALIGN;
+    return hip_status(dsa_host::launch_index_pools(*dims, k, gate, kg_dtype, ln_w, ln_b, *seqs, num_seqs,
+                                                   pool_begin, pool_end, max_pools, pools,
+                                                   as_stream(stream)));
+}
+
+int dsa_index_scores(const dsa_dims* dims, const uint16_t* q_idx, const float* w,
+                     const uint16_t* pools, const dsa_seqs* seqs, int32_t num_seqs,
+                     const int32_t* q_seq, const int32_t* q_pos, int32_t T, int32_t score_stride,
+                     float* scores, void* stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (dims->kpool != 4) return DSA_ERR_UNSUPPORTED;
+    if (T < 0 || score_stride < 0) return DSA_ERR_SIZE;
+    st = check_seqs(seqs, num_seqs, false, false, true);
+    if (st) return st;
+    if (T == 0 || score_stride == 0) return DSA_OK;
+    if (T > 65535 * 64) return DSA_ERR_SIZE;
+    if (!q_idx || !w || !pools || !q_seq || !q_pos || !scores) return DSA_ERR_NULL;
+    if (!aligned(q_idx, 16) || !aligned(pools, 16) || !aligned(scores, 4)) return DSA_ERR_ALIGN;
+    return hip_status(dsa_host::launch_index_scores(*dims, q_idx, w, pools, *seqs, q_seq, q_pos, T,
+                                                    score_stride, scores, as_stream(stream)));
+}
+
+size_t dsa_topk_workspace_bytes(const dsa_dims* dims, int32_t T, int32_t score_stride) {
+    if (check_dims(dims) != DSA_OK) return 0;
+    return dsa_host::topk_workspace_bytes(*dims, T, score_stride);
+}
+
+int dsa_topk_select(const dsa_dims* dims, const float* scores, int32_t score_stride,
+                    const dsa_seqs* seqs, int32_t num_seqs, const int32_t* q_seq,
+                    const int32_t* q_pos, int32_t T, int32_t* pool_ids, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (dims->kpool != 4) return DSA_ERR_UNSUPPORTED;
+    if (T < 0 || score_stride < 0) return DSA_ERR_SIZE;
+    st = check_seqs(seqs, num_seqs, false, false, false);
+    if (st) return st;
+    if (T == 0) return DSA_OK;
+    if (T > 65535) return DSA_ERR_SIZE;
+    if (!scores || !q_seq || !q_pos || !pool_ids) return DSA_ERR_NULL;
+    const size_t need = dsa_host::topk_workspace_bytes(*dims, T, score_stride);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return DSA_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return DSA_ERR_ALIGN;
+    }
+    return hip_status(dsa_host::launch_topk(*dims, scores, score_stride, *seqs, q_seq, q_pos, T,
+                                            pool_ids, workspace, as_stream(stream)));
+}
+
+int dsa_expand_selection(const dsa_dims* dims, const int32_t* pool_ids, const dsa_seqs* seqs,
+                         int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos, int32_t T,
+                         int32_t* indices, void* stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (T < 0) return DSA_ERR_SIZE;
+    st = check_seqs(seqs, num_seqs, true, false, false);
+    if (st) return st;
+    if (T == 0) return DSA_OK;
+    if (!pool_ids || !q_seq || !q_pos || !indices) return DSA_ERR_NULL;
+    return hip_status(dsa_host::launch_expand(*dims, pool_ids, *seqs, q_seq, q_pos, T, indices,
+                                              as_stream(stream)));
+}
+
+size_t dsa_sparse_mla_workspace_bytes(const dsa_dims* dims, int32_t T, int32_t num_splits) {
+    if (check_dims(dims) != DSA_OK || T <= 0 || num_splits < 0) return 0;
+    return dsa_host::plan_sparse_mla(*dims, T, num_splits, DSA_BF16).ws_bytes;
+}
+
+int dsa_sparse_mla(const dsa_dims* dims, const void* q, int q_dtype, const int8_t* cache,
+                   int64_t cache_rows, const int32_t* indices, int32_t T, float scale, void* out,
+                   int out_dtype, float* lse, int32_t num_splits, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (q_dtype != DSA_F32 && q_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    if (out_dtype != DSA_F32 && out_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    if (T < 0 || cache_rows < 0 || num_splits < 0) return DSA_ERR_SIZE;
+    if (dims->latent_dim % 64 != 0 || dims->latent_dim > 1024) return DSA_ERR_UNSUPPORTED;
+    if (T == 0) return DSA_OK;
+    if (T > 65535) return DSA_ERR_SIZE;
+    if (!q || !cache || !indices || !out) return DSA_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(out, 16)) return DSA_ERR_ALIGN;
+    const dsa_host::MlaPlan plan = dsa_host::plan_sparse_mla(*dims, T, num_splits, q_dtype);
+    if (plan.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < plan.ws_bytes) return DSA_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return DSA_ERR_ALIGN;
+    }
+    return hip_status(dsa_host::launch_sparse_mla(*dims, plan, q, q_dtype, cache, indices, T, scale, out,
+                                                  out_dtype, lse, workspace, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,122 @@
+// Shared device helpers for the gfx950 DSA kernels (wave64, MFMA, LDS).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dsa.h"
+
+namespace dsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// Round to nearest even; inputs are finite.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ---------------------------------------------------------------- wave reductions
+// Butterfly reductions over the 64 lanes of a wave; every lane gets the result
+// and the combination order is fixed, so results are deterministic.
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// ---------------------------------------------------------------- ordering keys
+// Order-preserving map from fp32 to uint32 (larger float -> larger key),
+// with -0 mapped onto +0 so the two compare equal.
+
+__device__ __forceinline__ uint32_t f32_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------- MFMA
+// v_mfma_f32_16x16x32_bf16: lane l holds A row (l % 16) and B column (l % 16),
+// 8 k-values each for k-group (l / 16); D lane l holds column (l % 16), rows
+// 4 * (l / 16) + i for i = 0..3.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_f32_32x32x16_bf16: lane l holds A row (l % 32) and B column (l % 32),
+// 8 k-values each for k-group (l / 32); D lane l holds column (l % 32), rows
+// 8 * (r / 4) + 4 * (l / 32) + (r % 4) for r = 0..15.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- block scans
+
+// Exclusive prefix sum of one uint32 per thread over a block of NT threads.
+// `sh` must hold NT / 64 + 1 entries.  Returns the exclusive prefix; *total
+// receives the block total.  Contains __syncthreads().
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* sh, uint32_t* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        uint32_t y = __shfl_up(x, o, kWave);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) sh[wave] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t acc = 0;
+        for (int w = 0; w < NT / 64; ++w) {
+            uint32_t t = sh[w];
+            sh[w] = acc;
+            acc += t;
+        }
+        sh[NT / 64] = acc;
+    }
+    __syncthreads();
+    uint32_t r = sh[wave] + x - v;
+    *total = sh[NT / 64];
+    __syncthreads();
+    return r;
+}
+
+}  // namespace dsa
+
+// Host-side helpers shared by the launchers.
+namespace dsa_host {
+
+struct DeviceInfo {
+    int cu_count;
+    size_t max_lds_per_block;
+};
+
+// Cached per device; never allocates device memory.
+DeviceInfo device_info();
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace dsa_host

@@ -1,0 +1,49 @@
+// Internal launchers: each validates nothing (dsa_api.cpp does) and enqueues
+// its kernels on the given stream.  They return the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dsa.h"
+
+namespace dsa_host {
+
+hipError_t launch_store_int8(const dsa_dims& d, const void* latent, int dtype, int64_t n,
+                             int64_t ld, const int64_t* slots, int8_t* cache, hipStream_t s);
+
+hipError_t launch_index_pools(const dsa_dims& d, const void* k, const void* gate, int dtype,
+                              const float* ln_w, const float* ln_b, const dsa_seqs& seqs,
+                              int32_t num_seqs, const int32_t* pool_begin,
+                              const int32_t* pool_end, int32_t max_pools, uint16_t* pools,
+                              hipStream_t s);
+
+hipError_t launch_index_scores(const dsa_dims& d, const uint16_t* q_idx, const float* w,
+                               const uint16_t* pools, const dsa_seqs& seqs, const int32_t* q_seq,
+                               const int32_t* q_pos, int32_t T, int32_t stride, float* scores,
+                               hipStream_t s);
+
+size_t topk_workspace_bytes(const dsa_dims& d, int32_t T, int32_t stride);
+hipError_t launch_topk(const dsa_dims& d, const float* scores, int32_t stride, const dsa_seqs& seqs,
+                       const int32_t* q_seq, const int32_t* q_pos, int32_t T, int32_t* pool_ids,
+                       void* ws, hipStream_t s);
+
+hipError_t launch_expand(const dsa_dims& d, const int32_t* pool_ids, const dsa_seqs& seqs,
+                         const int32_t* q_seq, const int32_t* q_pos, int32_t T, int32_t* indices,
+                         hipStream_t s);
+
+struct MlaPlan {
+    bool mfma;          // MFMA kernel (bf16 q, latent 512, heads % 16 == 0)
+    int head_tiles;     // 16-head tiles per workgroup (MFMA path)
+    int head_groups;    // workgroups along the head axis
+    int chunks_per_split;
+    int splits;         // list partitions per query
+    size_t ws_bytes;    // partial results (0 when splits == 1)
+};
+MlaPlan plan_sparse_mla(const dsa_dims& d, int32_t T, int32_t num_splits, int q_dtype);
+hipError_t launch_sparse_mla(const dsa_dims& d, const MlaPlan& plan, const void* q, int q_dtype,
+                             const int8_t* cache, const int32_t* indices, int32_t T, float scale,
+                             void* out, int out_dtype, float* lse, void* ws, hipStream_t s);
+
+}  // namespace dsa_host

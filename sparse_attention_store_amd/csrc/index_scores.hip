@@ -1,0 +1,202 @@
+// index_scores: score[t][p] = sum_h w[t][h] * relu(q_idx[t][h] . pool[p])
+// ([Ref] Functions: index_scores -- matmul, ReLU, head-weighted sum).
+//
+// MFMA kernel (32 heads x 128): the contraction q_idx[t] (32 x 128) x
+// pool^T (128 x pools) maps onto v_mfma_f32_32x32x16_bf16 with the 32 heads
+// as M and 32 pools per N-tile.  Each wave keeps 64 pools (two N-tiles, 64
+// VGPRs) resident as the B operand and walks the queries of its workgroup;
+// query rows are staged through LDS (padded rows, conflict-free 16-byte
+// reads) with a register prefetch of the next batch.  The ReLU and the
+// head-weighted sum run on the accumulators: each lane holds 16 heads of one
+// pool, the other 16 sit in lane l ^ 32, so one shuffle completes the sum.
+// Decode launches one query per workgroup (pure pool streaming, HBM bound);
+// prefill launches many queries per workgroup so the resident pools are
+// reused (MFMA bound).
+#include "dsa_common.h"
+#include "dsa_launch.h"
+
+namespace dsa {
+
+constexpr int kHI = 32, kDI = 128, kQROW = kDI + 8;   // padded LDS row (bf16 elements)
+constexpr int kQBYTES = kHI * kDI * 2;                // 8 KB per query
+
+template <int WAVES, int QB>
+__global__ __launch_bounds__(WAVES * 64) void k_scores_mfma(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    const uint16_t* __restrict__ pools, const int32_t* __restrict__ first_valid,
+    const int64_t* __restrict__ pool_base, const int32_t* __restrict__ q_seq,
+    const int32_t* __restrict__ q_pos, int T, int q_per_block, int stride,
+    float* __restrict__ scores) {
+    constexpr int NT = WAVES * 64;
+    constexpr int CHUNKS = QB * kQBYTES / 16;              // 16-byte pieces per batch
+    constexpr int PER_T = (CHUNKS + NT - 1) / NT;
+    __shared__ uint16_t q_lds[QB][kHI * kQROW];
+    __shared__ float w_lds[QB][kHI];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, g = lane >> 5;
+    const int tile0 = blockIdx.x * (WAVES * 64);
+    const int p0 = tile0 + wave * 64;
+    const int t_begin = blockIdx.y * q_per_block;
+    const int t_end = min(T, t_begin + q_per_block);
+    if (t_begin >= t_end) return;
+
+    // Register prefetch of one batch of query rows + weights.
+    u32x4 pre[PER_T];
+    float pre_w = 0.f;
+    auto prefetch = [&](int tb) {
+#pragma unroll
+        for (int i = 0; i < PER_T; ++i) {
+            const int c = tid + i * NT;
+            const int qi = c / (kQBYTES / 16);
+            const int within = c % (kQBYTES / 16);
+            const int t = tb + qi;
+            if (c < CHUNKS && t < t_end)
+                pre[i] = *reinterpret_cast<const u32x4*>(q_idx + (int64_t)t * (kHI * kDI) + within * 8);
+        }
+        if (tid < QB * kHI) {
+            const int t = tb + tid / kHI;
+            if (t < t_end) pre_w = w[(int64_t)t * kHI + (tid % kHI)];
+        }
+    };
+
+    u32x4 breg[2][8];
+    int64_t loaded_base = -1;
+    int loaded_lim = 0;
+
+    prefetch(t_begin);
+    for (int tb = t_begin; tb < t_end; tb += QB) {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < PER_T; ++i) {
+            const int c = tid + i * NT;
+            if (c < CHUNKS) {
+                const int qi = c / (kQBYTES / 16);
+                const int within = c % (kQBYTES / 16);
+                const int r = within >> 4, col = (within & 15) << 3;
+                *reinterpret_cast<u32x4*>(&q_lds[qi][r * kQROW + col]) = pre[i];
+            }
+        }
+        if (tid < QB * kHI) w_lds[tid / kHI][tid % kHI] = pre_w;
+        __syncthreads();
+        if (tb + QB < t_end) prefetch(tb + QB);
+
+        const int nq = min(QB, t_end - tb);
+        for (int qi = 0; qi < nq; ++qi) {
+            const int t = tb + qi;
+            const int b = q_seq[t];
+            const int f = first_valid[b];
+            const int qp = q_pos[t];
+            const int n_vis = qp >= f ? (qp - f + 1) >> 2 : 0;
+            float* out = scores + (int64_t)t * stride;
+            if (p0 >= n_vis) {                            // whole tile invisible
+                const int p = p0 + lane;
+                if (p < stride) out[p] = -INFINITY;
+                continue;
+            }
+            const int64_t base = pool_base[b];
+            const int lim = min(n_vis - p0, 64);
+            if (base != loaded_base || lim > loaded_lim) {
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    const int rel = nt * 32 + n;
+                    const uint16_t* src = pools + (base + p0 + rel) * kDI + g * 64;
+                    const bool ok = rel < lim;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        u32x4 v = {0u, 0u, 0u, 0u};
+                        if (ok) v = *reinterpret_cast<const u32x4*>(src + j * 8);
+                        breg[nt][j] = v;
+                    }
+                }
+                loaded_base = base;
+                loaded_lim = lim;
+            }
+            f32x16 acc0 = {}, acc1 = {};
+            const uint16_t* qrow = &q_lds[qi][n * kQROW + g * 64];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + j * 8));
+                acc0 = mfma32(a, as_bf16x8(breg[0][j]), acc0);
+                acc1 = mfma32(a, as_bf16x8(breg[1][j]), acc1);
+            }
+            // Heads held by this lane: 8*(r/4) + 4*g + (r%4).
+            const float* wq = &w_lds[qi][4 * g];
+            float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float wh = wq[8 * (r >> 2) + (r & 3)];
+                s0 += wh * fmaxf(acc0[r], 0.f);
+                s1 += wh * fmaxf(acc1[r], 0.f);
+            }
+            s0 += __shfl_xor(s0, 32, 64);
+            s1 += __shfl_xor(s1, 32, 64);
+            const float sv = g == 0 ? s0 : s1;
+            const int p = p0 + g * 32 + n;                 // lanes 0-31: tile 0, 32-63: tile 1
+            if (p < stride) out[p] = p < n_vis ? sv : -INFINITY;
+        }
+    }
+}
+
+// Vector kernel for other geometries (tiny configurations): one thread per
+// (query, pool), fp32 dot products over bf16 inputs.
+__global__ __launch_bounds__(256) void k_scores_generic(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    const uint16_t* __restrict__ pools, const int32_t* __restrict__ first_valid,
+    const int64_t* __restrict__ pool_base, const int32_t* __restrict__ q_seq,
+    const int32_t* __restrict__ q_pos, int HI, int DI, int stride, float* __restrict__ scores) {
+    const int t = blockIdx.y;
+    const int p = blockIdx.x * 256 + threadIdx.x;
+    if (p >= stride) return;
+    const int b = q_seq[t];
+    const int f = first_valid[b];
+    const int qp = q_pos[t];
+    const int n_vis = qp >= f ? (qp - f + 1) >> 2 : 0;
+    float* out = scores + (int64_t)t * stride;
+    if (p >= n_vis) {
+        out[p] = -INFINITY;
+        return;
+    }
+    const uint16_t* pr = pools + (pool_base[b] + p) * DI;
+    const uint16_t* qr = q_idx + (int64_t)t * HI * DI;
+    float s = 0.f;
+    for (int h = 0; h < HI; ++h) {
+        float dot = 0.f;
+        for (int c = 0; c < DI; ++c) dot += bf16_to_f32(qr[h * DI + c]) * bf16_to_f32(pr[c]);
+        s += w[(int64_t)t * HI + h] * fmaxf(dot, 0.f);
+    }
+    out[p] = s;
+}
+
+}  // namespace dsa
+
+namespace dsa_host {
+
+hipError_t launch_index_scores(const dsa_dims& d, const uint16_t* q_idx, const float* w,
+                               const uint16_t* pools, const dsa_seqs& seqs, const int32_t* q_seq,
+                               const int32_t* q_pos, int32_t T, int32_t stride, float* scores,
+                               hipStream_t s) {
+    if (T == 0 || stride == 0) return hipSuccess;
+    if (d.idx_heads == dsa::kHI && d.idx_dim == dsa::kDI) {
+        if (T <= 64) {
+            // Decode: one query per workgroup, 256 pools per workgroup.
+            dim3 grid((unsigned)cdiv(stride, 256), (unsigned)T), block(256);
+            hipLaunchKernelGGL((dsa::k_scores_mfma<4, 1>), grid, block, 0, s, q_idx, w, pools,
+                               seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, 1, stride, scores);
+        } else {
+            // Prefill: 512 resident pools per workgroup, 64 queries per workgroup.
+            const int qpb = 64;
+            dim3 grid((unsigned)cdiv(stride, 512), (unsigned)cdiv(T, qpb)), block(512);
+            hipLaunchKernelGGL((dsa::k_scores_mfma<8, 4>), grid, block, 0, s, q_idx, w, pools,
+                               seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, qpb, stride, scores);
+        }
+    } else {
+        dim3 grid((unsigned)cdiv(stride, 256), (unsigned)T), block(256);
+        hipLaunchKernelGGL(dsa::k_scores_generic, grid, block, 0, s, q_idx, w, pools,
+                           seqs.first_valid, seqs.pool_base, q_seq, q_pos, d.idx_heads, d.idx_dim,
+                           stride, scores);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dsa_host

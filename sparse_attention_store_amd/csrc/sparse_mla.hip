@@ -1,0 +1,461 @@
+// sparse_mla: NoPE MLA over the rows an index list selects from the INT8
+// latent cache, with the dequantisation fused in ([Kernels] Included and
+// Install: one shared 512-d K/V latent, split-KV decode, bf16 products with
+// fp32 accumulation and softmax, negative indices as padding; [Ref]
+// Functions: mla_masked_attention).
+//
+// MFMA kernel.  A workgroup (4 waves) owns one query, 16*HT heads and a
+// contiguous span of the index list ("split"), walked in chunks of 64 rows:
+//  1. gather: each thread loads 128 bytes of one row (4 threads per 528-byte
+//     row) and converts the INT8 codes exactly to bf16 into LDS (padded rows,
+//     conflict-free 16-byte reads); the row's fp32 scale goes to LDS too.
+//  2. S = Q K^T on v_mfma_f32_16x16x32_bf16 (heads = M, rows = N, K = 512);
+//     Q stays in registers for the whole split.  The row scale and the
+//     softmax scale are applied to S in fp32, so the codes stay exact.
+//  3. online softmax in the exp2 domain (running max / sum per head; waves
+//     that share a head tile exchange their partial max and sum through LDS).
+//  4. O += P' V with P' = p * row_scale (A operand, staged through LDS) and V
+//     the bf16 codes.  P' is split into bf16 hi + lo parts (two MFMAs sharing
+//     the V operand), so the weights carry ~16 significant bits: a single
+//     dominant row of a heavy-tailed latent (|o| ~ 100) would otherwise lose
+//     ~0.2 absolute to bf16 rounding.  The B operand for V is assembled
+//     from 8-byte LDS reads of 4 adjacent columns per row, so output columns
+//     are handled in groups of 4 tiles that share each read.
+// One split writes the normalised output directly; several splits write
+// (m, l, unnormalised O) partials that k_mla_combine merges in split order,
+// so results are deterministic for a given split count.  Empty chunks are
+// skipped; an empty split contributes (m = -inf, l = 0) and is ignored.
+#include "dsa_common.h"
+#include "dsa_launch.h"
+
+namespace dsa {
+
+constexpr int kD = 512;
+constexpr int kChunk = 64;
+constexpr int kKVRow = kD + 8;       // bf16 elements per LDS row (1040 B)
+constexpr int kPRow = kChunk + 8;    // bf16 elements per P' row (144 B)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct MlaPartial {
+    float m;   // running max, log2 domain
+    float l;   // running sum
+};
+
+__device__ __forceinline__ void int8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    const uint32_t u = w ^ 0x80808080u;            // biased to unsigned: code + 128
+    const float f0 = (float)(u & 0xFFu) - 128.0f;
+    const float f1 = (float)((u >> 8) & 0xFFu) - 128.0f;
+    const float f2 = (float)((u >> 16) & 0xFFu) - 128.0f;
+    const float f3 = (float)(u >> 24) - 128.0f;
+    // Small integers are exact in bf16: keep the upper halves.
+    lo = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+    hi = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+}
+
+template <int HT>
+__global__ __launch_bounds__(256) void k_mla_mfma(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, int row_bytes,
+    const int32_t* __restrict__ indices, int W, int H, float scale_log2, int chunks_per_split,
+    int splits, float* __restrict__ part_o, MlaPartial* __restrict__ part_ml,
+    void* __restrict__ out, int out_f32, float* __restrict__ lse) {
+    constexpr int HPW = 16 * HT;
+    constexpr int WPHT = 4 / HT;          // waves per head tile
+    constexpr int NGRP = 8 / WPHT;        // 64-column groups per wave (PV)
+    __shared__ __attribute__((aligned(16))) uint16_t kv[kChunk * kKVRow];
+    __shared__ __attribute__((aligned(16))) uint16_t pl[2][HPW * kPRow];   // P' hi, lo
+    __shared__ float rs[kChunk];
+    __shared__ int rvalid[kChunk];
+    __shared__ float red_max[4][16];
+    __shared__ float red_sum[4][16];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int split = blockIdx.x, hg = blockIdx.y, t = blockIdx.z;
+    const int ht = wave / WPHT, sub = wave % WPHT;
+    const int head0 = hg * HPW + ht * 16;
+    const int n16 = lane & 15, g4 = lane >> 4;
+
+    // Q (A operand of S): head head0 + n16, k = j*32 + g4*8 + e.
+    u32x4 qa[16];
+    {
+        const uint16_t* qr = q + ((int64_t)t * H + head0 + n16) * kD + g4 * 8;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) qa[j] = *reinterpret_cast<const u32x4*>(qr + j * 32);
+    }
+
+    float m_run[4], l_run[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.f; }
+    f32x4 oacc[NGRP][4];
+#pragma unroll
+    for (int gi = 0; gi < NGRP; ++gi)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) oacc[gi][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nchunks = (W + kChunk - 1) / kChunk;
+    const int c_begin = split * chunks_per_split;
+    const int c_end = min(c_begin + chunks_per_split, nchunks);
+    const int32_t* idx_row = indices + (int64_t)t * W;
+
+    for (int c = c_begin; c < c_end; ++c) {
+        // ---- 1. gather + dequant to bf16
+        const int r = tid >> 2, sg = tid & 3;
+        const int pos = c * kChunk + r;
+        const int idx = pos < W ? idx_row[pos] : -1;
+        u32x4 raw[8];
+        if (idx >= 0) {
+            const uint8_t* src = cache + (int64_t)idx * row_bytes + sg * 128;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) raw[i] = *reinterpret_cast<const u32x4*>(src + 16 * i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) raw[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+        float rsc = 0.f;
+        if (sg == 0 && idx >= 0) rsc = *reinterpret_cast<const float*>(cache + (int64_t)idx * row_bytes + kD);
+        __syncthreads();                                   // previous chunk's readers are done
+        if (sg == 0) { rs[r] = rsc; rvalid[r] = idx >= 0; }
+        {
+            uint16_t* dst = &kv[r * kKVRow + sg * 128];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                uint32_t b[8];
+                int8x4_to_bf16x4(raw[i][0], b[0], b[1]);
+                int8x4_to_bf16x4(raw[i][1], b[2], b[3]);
+                int8x4_to_bf16x4(raw[i][2], b[4], b[5]);
+                int8x4_to_bf16x4(raw[i][3], b[6], b[7]);
+                const u32x4 o0 = {b[0], b[1], b[2], b[3]};
+                const u32x4 o1 = {b[4], b[5], b[6], b[7]};
+                *reinterpret_cast<u32x4*>(dst + 16 * i) = o0;
+                *reinterpret_cast<u32x4*>(dst + 16 * i + 8) = o1;
+            }
+        }
+        if (!__syncthreads_or(idx >= 0)) continue;          // empty chunk
+
+        // ---- 2. S for this wave's head tile and row tiles sub*HT .. sub*HT+HT-1
+        f32x4 sacc[HT];
+#pragma unroll
+        for (int rr = 0; rr < HT; ++rr) {
+            const int rt = sub * HT + rr;
+            const uint16_t* kr = &kv[(rt * 16 + n16) * kKVRow + g4 * 8];
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                a = mfma16(as_bf16x8(qa[j]), as_bf16x8(*reinterpret_cast<const u32x4*>(kr + j * 32)), a);
+            sacc[rr] = a;
+        }
+        // ---- 3. online softmax (log2 domain); lane holds row rt*16+n16, heads 4*g4+i
+        float z[HT][4];
+        float cmax[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+        for (int rr = 0; rr < HT; ++rr) {
+            const int row = (sub * HT + rr) * 16 + n16;
+            const bool ok = rvalid[row] != 0;
+            const float sc = rs[row] * scale_log2;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                z[rr][i] = ok ? sacc[rr][i] * sc : -INFINITY;
+                cmax[i] = fmaxf(cmax[i], z[rr][i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) cmax[i] = fmaxf(cmax[i], __shfl_xor(cmax[i], o, 64));
+        if (n16 == 0)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red_max[wave][4 * g4 + i] = cmax[i];
+        __syncthreads();
+        float m_new[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float mc = red_max[ht * WPHT][4 * g4 + i];
+#pragma unroll
+            for (int s2 = 1; s2 < WPHT; ++s2) mc = fmaxf(mc, red_max[ht * WPHT + s2][4 * g4 + i]);
+            m_new[i] = fmaxf(m_run[i], mc);
+        }
+        float psum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int rr = 0; rr < HT; ++rr) {
+            const int row = (sub * HT + rr) * 16 + n16;
+            const float rsv = rs[row];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = m_new[i] == -INFINITY ? 0.f : exp2f(z[rr][i] - m_new[i]);
+                psum[i] += p;
+                const float x = p * rsv;
+                const uint32_t hi = f32_to_bf16_rne(x);
+                const int o = (ht * 16 + 4 * g4 + i) * kPRow + row;
+                pl[0][o] = (uint16_t)hi;
+                pl[1][o] = (uint16_t)f32_to_bf16_rne(x - bf16_to_f32(hi));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) psum[i] += __shfl_xor(psum[i], o, 64);
+        if (n16 == 0)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red_sum[wave][4 * g4 + i] = psum[i];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float ls = 0.f;
+#pragma unroll
+            for (int s2 = 0; s2 < WPHT; ++s2) ls += red_sum[ht * WPHT + s2][4 * g4 + i];
+            const float alpha = m_run[i] == -INFINITY ? 0.f : exp2f(m_run[i] - m_new[i]);
+            l_run[i] = l_run[i] * alpha + ls;
+            m_run[i] = m_new[i];
+#pragma unroll
+            for (int gi = 0; gi < NGRP; ++gi)
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) oacc[gi][tt][i] *= alpha;
+        }
+
+        // ---- 4. O += P' V
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int po = (ht * 16 + n16) * kPRow + ks * 32 + g4 * 8;
+            const bf16x8 a_hi = as_bf16x8(*reinterpret_cast<const u32x4*>(&pl[0][po]));
+            const bf16x8 a_lo = as_bf16x8(*reinterpret_cast<const u32x4*>(&pl[1][po]));
+            const int row0 = ks * 32 + g4 * 8;
+#pragma unroll
+            for (int gi = 0; gi < NGRP; ++gi) {
+                const int col0 = 64 * (sub * NGRP + gi) + 4 * n16;
+                u32x2 v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = *reinterpret_cast<const u32x2*>(&kv[(row0 + e) * kKVRow + col0]);
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    const int wd = tt >> 1;
+                    const uint32_t sel = (tt & 1) ? 0x07060302u : 0x05040100u;
+                    u32x4 bb;
+                    bb[0] = __builtin_amdgcn_perm(v[1][wd], v[0][wd], sel);
+                    bb[1] = __builtin_amdgcn_perm(v[3][wd], v[2][wd], sel);
+                    bb[2] = __builtin_amdgcn_perm(v[5][wd], v[4][wd], sel);
+                    bb[3] = __builtin_amdgcn_perm(v[7][wd], v[6][wd], sel);
+                    oacc[gi][tt] = mfma16(a_hi, as_bf16x8(bb), oacc[gi][tt]);
+                    oacc[gi][tt] = mfma16(a_lo, as_bf16x8(bb), oacc[gi][tt]);
+                }
+            }
+        }
+    }
+
+    // ---- epilogue: lane holds heads head0 + 4*g4 + i, columns 64*grp + 4*n16 + tt
+    if (splits == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int head = head0 + 4 * g4 + i;
+            const float inv = l_run[i] > 0.f ? 1.0f / l_run[i] : 0.f;
+            const int64_t orow = ((int64_t)t * H + head) * kD;
+#pragma unroll
+            for (int gi = 0; gi < NGRP; ++gi) {
+                const int col = 64 * (sub * NGRP + gi) + 4 * n16;
+                f32x4 v = {oacc[gi][0][i] * inv, oacc[gi][1][i] * inv, oacc[gi][2][i] * inv, oacc[gi][3][i] * inv};
+                if (out_f32) {
+                    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + orow + col) = v;
+                } else {
+                    u32x2 pk;
+                    pk[0] = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+                    pk[1] = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+                    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + orow + col) = pk;
+                }
+            }
+            if (lse && sub == 0 && n16 == 0)
+                lse[(int64_t)t * H + head] = l_run[i] > 0.f ? (m_run[i] + log2f(l_run[i])) * kLn2 : -INFINITY;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int head = head0 + 4 * g4 + i;
+            const int64_t slot = ((int64_t)t * splits + split) * H + head;
+            float* po = part_o + slot * kD;
+            if (l_run[i] > 0.f) {
+#pragma unroll
+                for (int gi = 0; gi < NGRP; ++gi) {
+                    const int col = 64 * (sub * NGRP + gi) + 4 * n16;
+                    *reinterpret_cast<f32x4*>(po + col) =
+                        f32x4{oacc[gi][0][i], oacc[gi][1][i], oacc[gi][2][i], oacc[gi][3][i]};
+                }
+            }
+            if (sub == 0 && n16 == 0) part_ml[slot] = MlaPartial{m_run[i], l_run[i]};
+        }
+    }
+}
+
+// Merge split partials in split order: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+__global__ __launch_bounds__(128) void k_mla_combine(
+    const float* __restrict__ part_o, const MlaPartial* __restrict__ part_ml, int splits, int H,
+    void* __restrict__ out, int out_f32, float* __restrict__ lse) {
+    const int h = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+    float M = -INFINITY;
+    for (int s = 0; s < splits; ++s) {
+        const MlaPartial p = part_ml[((int64_t)t * splits + s) * H + h];
+        if (p.l > 0.f) M = fmaxf(M, p.m);
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+    if (M != -INFINITY) {
+        for (int s = 0; s < splits; ++s) {
+            const int64_t slot = ((int64_t)t * splits + s) * H + h;
+            const MlaPartial p = part_ml[slot];
+            if (!(p.l > 0.f)) continue;
+            const float wgt = exp2f(p.m - M);
+            L += p.l * wgt;
+            const f32x4 o = *reinterpret_cast<const f32x4*>(part_o + slot * kD + tid * 4);
+            acc += o * wgt;
+        }
+    }
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    acc *= inv;
+    const int64_t orow = ((int64_t)t * H + h) * kD + tid * 4;
+    if (out_f32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + orow) = acc;
+    } else {
+        u32x2 pk;
+        pk[0] = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+        pk[1] = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + orow) = pk;
+    }
+    if (lse && tid == 0) lse[(int64_t)t * H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
+// fp32 vector kernel for other shapes (tiny geometry, fp32 q): one wave per
+// (query, head), one pass over the list with an online softmax.
+template <bool Q_F32>
+__global__ __launch_bounds__(64) void k_mla_generic(
+    const void* __restrict__ q, const uint8_t* __restrict__ cache, int row_bytes,
+    const int32_t* __restrict__ indices, int W, int H, int D, float scale,
+    void* __restrict__ out, int out_f32, float* __restrict__ lse) {
+    constexpr int MAXV = 16;                         // D <= 1024
+    const int h = blockIdx.x, t = blockIdx.y, lane = threadIdx.x;
+    const int vpl = D / 64;
+    float qv[MAXV], o[MAXV];
+    const int64_t qoff = ((int64_t)t * H + h) * D + lane * vpl;
+#pragma unroll
+    for (int e = 0; e < MAXV; ++e) {
+        o[e] = 0.f;
+        qv[e] = 0.f;
+        if (e < vpl)
+            qv[e] = Q_F32 ? reinterpret_cast<const float*>(q)[qoff + e]
+                          : bf16_to_f32(reinterpret_cast<const uint16_t*>(q)[qoff + e]);
+    }
+    float m = -INFINITY, l = 0.f;
+    const int32_t* ir = indices + (int64_t)t * W;
+    for (int j = 0; j < W; ++j) {
+        const int idx = ir[j];
+        if (idx < 0) continue;
+        const int8_t* rowp = reinterpret_cast<const int8_t*>(cache + (int64_t)idx * row_bytes);
+        const float s = *reinterpret_cast<const float*>(rowp + D);
+        float code[MAXV];
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < MAXV; ++e) {
+            code[e] = e < vpl ? (float)rowp[lane * vpl + e] : 0.f;
+            dot += qv[e] * code[e];
+        }
+        dot = wave_sum(dot);
+        const float zz = scale * s * dot;
+        const float mn = fmaxf(m, zz);
+        const float alpha = m == -INFINITY ? 0.f : expf(m - mn);
+        const float p = expf(zz - mn);
+        l = l * alpha + p;
+#pragma unroll
+        for (int e = 0; e < MAXV; ++e) o[e] = o[e] * alpha + p * s * code[e];
+        m = mn;
+    }
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    const int64_t ooff = ((int64_t)t * H + h) * D + lane * vpl;
+#pragma unroll
+    for (int e = 0; e < MAXV; ++e) {
+        if (e < vpl) {
+            if (out_f32) reinterpret_cast<float*>(out)[ooff + e] = o[e] * inv;
+            else reinterpret_cast<uint16_t*>(out)[ooff + e] = (uint16_t)f32_to_bf16_rne(o[e] * inv);
+        }
+    }
+    if (lse && lane == 0) lse[(int64_t)t * H + h] = l > 0.f ? m + logf(l) : -INFINITY;
+}
+
+}  // namespace dsa
+
+namespace dsa_host {
+
+MlaPlan plan_sparse_mla(const dsa_dims& d, int32_t T, int32_t num_splits, int q_dtype) {
+    MlaPlan p{};
+    p.mfma = q_dtype == DSA_BF16 && d.latent_dim == dsa::kD && d.mla_heads % 16 == 0;
+    if (!p.mfma || T <= 0) {
+        p.head_tiles = 1;
+        p.head_groups = d.mla_heads;
+        p.splits = 1;
+        p.chunks_per_split = 1;
+        p.ws_bytes = 0;
+        return p;
+    }
+    const int cu = device_info().cu_count;
+    const int nchunks = (int)cdiv(d.out_width, dsa::kChunk);
+    const int tiles16 = d.mla_heads / 16;
+    int ht = 1;
+    if ((int64_t)T * tiles16 >= 2 * cu) ht = tiles16 % 4 == 0 ? 4 : (tiles16 % 2 == 0 ? 2 : 1);
+    p.head_tiles = ht;
+    p.head_groups = tiles16 / ht;
+    int want;
+    if (num_splits > 0) {
+        want = num_splits < nchunks ? num_splits : nchunks;
+    } else {
+        const int64_t base = (int64_t)T * p.head_groups;
+        want = base >= cu ? 1 : (int)std::min<int64_t>(nchunks, cdiv(2 * cu, base));
+    }
+    p.chunks_per_split = (int)cdiv(nchunks, want);
+    p.splits = (int)cdiv(nchunks, p.chunks_per_split);
+    p.ws_bytes = p.splits > 1
+                     ? (size_t)T * p.splits * d.mla_heads * (dsa::kD * sizeof(float) + sizeof(dsa::MlaPartial))
+                     : 0;
+    return p;
+}
+
+hipError_t launch_sparse_mla(const dsa_dims& d, const MlaPlan& plan, const void* q, int q_dtype,
+                             const int8_t* cache, const int32_t* indices, int32_t T, float scale,
+                             void* out, int out_dtype, float* lse, void* ws, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const int H = d.mla_heads, W = d.out_width;
+    const int out_f32 = out_dtype == DSA_F32;
+    const uint8_t* c8 = reinterpret_cast<const uint8_t*>(cache);
+    if (!plan.mfma) {
+        dim3 grid((unsigned)H, (unsigned)T);
+        if (q_dtype == DSA_F32)
+            hipLaunchKernelGGL((dsa::k_mla_generic<true>), grid, dim3(64), 0, s, q, c8, d.row_bytes, indices, W, H,
+                               d.latent_dim, scale, out, out_f32, lse);
+        else
+            hipLaunchKernelGGL((dsa::k_mla_generic<false>), grid, dim3(64), 0, s, q, c8, d.row_bytes, indices, W, H,
+                               d.latent_dim, scale, out, out_f32, lse);
+        return hipGetLastError();
+    }
+    float* part_o = reinterpret_cast<float*>(ws);
+    dsa::MlaPartial* part_ml = nullptr;
+    if (plan.splits > 1)
+        part_ml = reinterpret_cast<dsa::MlaPartial*>(part_o + (size_t)T * plan.splits * H * dsa::kD);
+    dim3 grid((unsigned)plan.splits, (unsigned)plan.head_groups, (unsigned)T);
+    const float sl2 = scale * dsa::kLog2e;
+    const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q);
+    switch (plan.head_tiles) {
+        case 4:
+            hipLaunchKernelGGL((dsa::k_mla_mfma<4>), grid, dim3(256), 0, s, q16, c8, d.row_bytes, indices, W, H, sl2,
+                               plan.chunks_per_split, plan.splits, part_o, part_ml, out, out_f32, lse);
+            break;
+        case 2:
+            hipLaunchKernelGGL((dsa::k_mla_mfma<2>), grid, dim3(256), 0, s, q16, c8, d.row_bytes, indices, W, H, sl2,
+                               plan.chunks_per_split, plan.splits, part_o, part_ml, out, out_f32, lse);
+            break;
+        default:
+            hipLaunchKernelGGL((dsa::k_mla_mfma<1>), grid, dim3(256), 0, s, q16, c8, d.row_bytes, indices, W, H, sl2,
+                               plan.chunks_per_split, plan.splits, part_o, part_ml, out, out_f32, lse);
+            break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || plan.splits == 1) return e;
+    hipLaunchKernelGGL(dsa::k_mla_combine, dim3((unsigned)H, (unsigned)T), dim3(128), 0, s, part_o, part_ml,
+                       plan.splits, H, out, out_f32, lse);
+    return hipGetLastError();
+}
+
+}  // namespace dsa_host

@@ -1,0 +1,139 @@
+"""End-to-end parity of the whole path (GPU) against the oracle chain.
+
+The GPU runs the step exactly as the bench does (dsa_harness.DeviceWorkload);
+the oracle recomputes everything from the seeded generators.  Checks:
+  * INT8 rows of every listed cache row: bit-exact;
+  * pools and scores: rtol 1e-2 with an absolute floor of 1e-2 x row RMS;
+  * selected pool sets: equal, or differing only among pools whose oracle
+    score lies within 1e-3 (relative) of the k-th oracle score;
+  * index lists: bit-exact whenever the selected sets agree;
+  * attention (fp32 out): max-abs 2e-2 and rel-L2 1e-2 over the workload,
+    on every query whose list agrees with the oracle's.
+Reduced-size workloads are checked on every output; the full-size workloads
+(the pages' shapes) on every decode query and a seeded sample of prefill
+queries.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import dsa_synth as syn
+from oracle_chain import OracleWorkload, score_close, topk_set_ok
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def harness():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dsa_harness
+    return dsa_harness
+
+
+def _check_chain(dw, queries, pool_sample=64, allow_swaps_frac=0.05):
+    wl = dw.wl
+    d = wl.dims
+    ow = OracleWorkload(wl)
+    scores = dw.scores.cpu().numpy()
+    ids = dw.pool_ids.cpu().numpy()
+    idx = dw.indices.cpu().numpy()
+    out = dw.out.float().cpu().numpy()
+    lse = dw.lse.cpu().numpy()
+    pools = dw.pools[0].float().cpu().numpy()
+    errs, refs = [], []
+    swapped = 0
+    g = np.random.default_rng(17)
+    for t in queries:
+        b = int(wl.q_seq[t])
+        r = ow.query(int(t), dw.stride)
+        n_vis = r["n_vis"]
+        # pools of this sequence (a sample at full size)
+        pb = int(wl.pool_base[b])
+        opools = ow.pools(b)
+        sel = np.arange(opools.shape[0]) if opools.shape[0] <= pool_sample else \
+            g.choice(opools.shape[0], size=pool_sample, replace=False)
+        for p in sel:
+            ok, worst = score_close(pools[pb + p], opools[p], d.idx_dim)
+            assert ok, ("pool", t, int(p), worst)
+        ok, worst = score_close(scores[t], r["scores"], n_vis)
+        assert ok, ("scores", t, worst)
+        assert np.all(np.isneginf(scores[t, n_vis:])), ("scores tail", t)
+        ok, nsw = topk_set_ok(ids[t], r["scores"], r["ids"], n_vis)
+        assert ok, ("topk", t)
+        assert np.all(ids[t][min(d.select_k, n_vis):] == -1)
+        assert np.all(np.diff(ids[t][:min(d.select_k, n_vis)]) > 0)
+        if nsw:
+            swapped += 1
+            continue
+        assert np.array_equal(ids[t], r["ids"]), ("ids", t)
+        assert np.array_equal(idx[t], r["indices"]), ("indices", t)
+        valid = idx[t][idx[t] >= 0]
+        got_rows = dw.caches[0][torch.from_numpy(valid.astype(np.int64)).cuda()].cpu().numpy().view(np.uint8)
+        assert np.array_equal(got_rows, ow.cache_rows(valid)), ("rows", t)
+        errs.append(out[t] - r["out"])
+        refs.append(r["out"])
+        if valid.size == 0:
+            assert np.all(out[t] == 0) and np.all(np.isneginf(lse[t]))
+        else:
+            assert np.allclose(lse[t], r["lse"], atol=2e-3, rtol=1e-4), ("lse", t)
+    assert swapped <= max(1, int(allow_swaps_frac * len(queries))), swapped
+    e = np.stack(errs)
+    rf = np.stack(refs)
+    assert np.abs(e).max() <= 2e-2, float(np.abs(e).max())
+    if np.linalg.norm(rf) > 0:
+        assert np.linalg.norm(e) / np.linalg.norm(rf) <= 1e-2
+    return swapped
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_seven", "tiny_padded_six", "tiny_batch", "mini_decode",
+                                  "mini_prefill", "mini_heavy"])
+def test_chain_reduced(harness, name):
+    wl = syn.get(name)
+    say(f"chain {name} T={wl.T}")
+    dw = harness.DeviceWorkload(wl, canary=0x11)
+    dw.step()
+    torch.cuda.synchronize()
+    _check_chain(dw, range(wl.T))
+
+
+def test_chain_twice_is_bitwise_identical(harness):
+    wl = syn.mini_decode()
+    say("chain determinism")
+    dw = harness.DeviceWorkload(wl)
+    dw.step()
+    a = [x.clone() for x in (dw.scores, dw.pool_ids, dw.indices, dw.out, dw.lse)]
+    dw.step()
+    torch.cuda.synchronize()
+    for x, y in zip(a, (dw.scores, dw.pool_ids, dw.indices, dw.out, dw.lse)):
+        assert torch.equal(x, y)
+
+
+FULL = ["decode_32k", "decode_262k_b8", "decode_1m_b4", "prefill_4k_on_131k"]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", FULL)
+def test_chain_full_size_sampled(harness, name):
+    if os.environ.get("DSA_SKIP_FULL") == "1":
+        pytest.skip("full-size workloads disabled by DSA_SKIP_FULL")
+    wl = syn.get(name)
+    say(f"chain full {name} T={wl.T} rows={wl.total_rows}")
+    dw = harness.DeviceWorkload(wl)
+    dw.step()
+    torch.cuda.synchronize()
+    if wl.T > 16:
+        g = np.random.default_rng(99)
+        queries = sorted(set([0, wl.T - 1] + list(g.choice(wl.T, size=6, replace=False))))
+    else:
+        queries = list(range(wl.T))
+    say(f"chain full {name}: checking {len(queries)} queries on the CPU")
+    _check_chain(dw, queries, pool_sample=64, allow_swaps_frac=0.25)
+    del dw
+    torch.cuda.empty_cache()
