@@ -1,0 +1,235 @@
+"""Decode-step throughput of the DSA path on one MI355X.
+
+One step = the whole path for one batch: store the B new tokens' INT8 rows,
+build the pools they complete, score every visible pool, select the top-k,
+expand to index lists, and run sparse MLA -- for B = 8 ragged sequences at up
+to 262,144 tokens of context, 16 MLA heads.  Inputs are seeded synthetic data
+resident in HBM; steps rotate over R replicas of the caches so the working
+set exceeds the 256 MB Infinity Cache several times over.
+
+Prints one JSON line (metric, value, ... , roofline, cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode tok-steps/s (indexer+topk+sparse MLA) @262k ctx B=8; % HBM peak"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+WORKLOAD = "decode_262k_b8"
+SCORES_SRC = os.path.join(ROOT, "sparse_attention_store_amd", "csrc", "index_scores.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "index_scores_decode_262k_b8_traffic.md")
+
+
+def algorithmic_bytes(wl) -> dict:
+    """Bytes the method must move per decode step (see the design notes)."""
+    d = wl.dims
+    tot_pools = 0
+    tot_rows = 0
+    new_pools = 0
+    for t in range(wl.T):
+        n_vis = wl.n_vis(t)
+        b = int(wl.q_seq[t])
+        f = int(wl.first_valid[b])
+        qp = int(wl.q_pos[t])
+        tot_pools += n_vis
+        tail = (qp - f + 1) - d.kpool * n_vis if qp >= f else 0
+        tot_rows += d.kpool * min(d.select_k, n_vis) + tail
+        new_pools += 1 if qp >= f and (qp - f + 1) % d.kpool == 0 else 0
+    T = wl.T
+    scores = tot_pools * (256 + 4) + T * (d.idx_heads * d.idx_dim * 2 + d.idx_heads * 4)
+    step = (tot_pools * 256 + T * (d.idx_heads * d.idx_dim * 2 + d.idx_heads * 4) + tot_rows * d.row_bytes
+            + T * 4 * d.mla_heads * d.latent_dim + T * 4 * d.out_width + T * (2 * d.latent_dim + d.row_bytes)
+            + new_pools * (2 * d.kpool * d.idx_dim * 2 + d.idx_dim * 2))
+    return {"step": step, "scores_kernel": scores, "pools": tot_pools, "rows": tot_rows}
+
+
+def traffic_from_profile():
+    """HBM bytes per scores launch from the committed rocprofv3 counter summary,
+    or None when the summary is absent or was taken on a different kernel source."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    src_hash = hashlib.sha256(open(SCORES_SRC, "rb").read()).hexdigest()[:16]
+    vals = {}
+    for ln in open(PMC_SUMMARY):
+        if ":" in ln and ln.strip().startswith("- "):
+            k, v = ln.strip()[2:].split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != src_hash:
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
+    """The oracle's per-step chain (scores, top-k, expand, attention) for every query of
+    the workload, timed on the host cores over whole decode steps.
+
+    Setup (not timed): pools of every sequence (O2, stored bf16) and the INT8 rows
+    (O1) of the rows each query's list selects."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import dsa_synth as syn
+    import oracle as O
+
+    d = wl.dims
+    lw, lb = syn.gen_ln(wl)
+    state = []
+    for t in range(wl.T):
+        b = int(wl.q_seq[t])
+        n = int(wl.seq_len[b])
+        f = int(wl.first_valid[b])
+        qp = int(wl.q_pos[t])
+        k = np.empty((n, d.idx_dim), np.float32)
+        g = np.empty((n, d.idx_dim), np.float32)
+        for x0, (kk, gg) in syn.gen_sequence_blocks(syn.gen_kgate, wl, b, 0, n):
+            k[x0:x0 + kk.shape[0]] = kk
+            g[x0:x0 + gg.shape[0]] = gg
+        pools = O.store_bf16(O.pool_states(k, g, lw, lb, d.ln_eps, f, n, d.kpool))
+        del k, g
+        qi, w, q = syn.gen_qidx(wl, t, t + 1)[0], syn.gen_w(wl, t, t + 1)[0], syn.gen_q(wl, t, t + 1)[0]
+        n_vis = O.visible_pool_count(qp, f, d.kpool)
+        idx = O.expand_selection(O.topk_pools(O.index_scores(qi, w, pools, n_vis), n_vis, d.select_k),
+                                 f, qp, 0, d.kpool, d.out_width)
+        need = idx[idx >= 0]
+        rows = np.zeros((n, d.row_bytes), dtype=np.uint8)      # only the listed rows are filled
+        blocks = sorted(set(int(x) // 65536 for x in need))
+        for blk in blocks:
+            lat = syn.gen_latent(wl, b, blk * 65536, min(n, (blk + 1) * 65536))
+            sel = need[(need >= blk * 65536) & (need < (blk + 1) * 65536)]
+            O.store_int8(lat[sel - blk * 65536], sel, rows)
+        state.append((f, qp, n_vis, pools, rows, qi, w, q))
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        for f, qp, n_vis, pools, rows, qi, w, q in state:
+            sc = O.index_scores(qi, w, pools, n_vis)
+            ids = O.topk_pools(sc, n_vis, d.select_k)
+            idx = O.expand_selection(ids, f, qp, 0, d.kpool, d.out_width)
+            O.sparse_mla(q, rows, idx, wl.scale, d.latent_dim)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": steps * wl.T / el, "unit": "tok-steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{steps} whole decode steps ({wl.T} queries each) of {wl.name}: oracle scores, "
+                      f"top-k, expansion and attention in float64, {el:.1f} s; pool and INT8-row setup "
+                      "not timed"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default=WORKLOAD)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dsa_harness
+    import dsa_synth as syn
+
+    wl = syn.get(args.workload)
+    print(f"[bench] setting up {wl.name}: B={wl.B} T={wl.T} rows={wl.total_rows} "
+          f"replicas={args.replicas}", file=sys.stderr, flush=True)
+    t_setup = time.perf_counter()
+    dw = dsa_harness.DeviceWorkload(wl, replicas=args.replicas, out_dtype=torch.bfloat16)
+    print(f"[bench] setup {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
+    R = args.replicas
+    for i in range(args.warmup):
+        dw.step(i % R)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        r = i % R
+        dw.step_store(r)
+        dw.step_pools(r)
+        ev_s[i].record(stream)
+        dw.step_scores(r)
+        ev_e[i].record(stream)
+        dw.step_select()
+        dw.step_attention(r)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    scores_us = float(np.mean([a.elapsed_time(b) for a, b in zip(ev_s, ev_e)])) * 1e3
+
+    # Per-stage breakdown (separate, untimed pass).
+    stages = {}
+    names = ["store_int8", "index_pools", "index_scores", "topk_select_expand", "sparse_mla"]
+    fns = [dw.step_store, dw.step_pools, dw.step_scores, lambda r: dw.step_select(), dw.step_attention]
+    n_b = min(args.steps, 50)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(n_b)]
+    for i in range(n_b):
+        evs[i][0].record(stream)
+        for j, fn in enumerate(fns):
+            fn(i % R)
+            evs[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    for j, nm in enumerate(names):
+        stages[nm] = round(float(np.median([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e3, 2)
+
+    ab = algorithmic_bytes(wl)
+    achieved = ab["scores_kernel"] / (scores_us * 1e-6) / 1e9
+    value = wl.T / (ms_step * 1e-3)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tok-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.B, "context_cap": 262144,
+                   "valid_tokens": [int(a - b) for a, b in zip(wl.seq_len, wl.first_valid)],
+                   "mla_heads": wl.dims.mla_heads, "index_topk": wl.dims.index_topk,
+                   "out_width": wl.dims.out_width, "replicas": R},
+        "pct_hbm_peak": round(100.0 * ab["step"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "bytes_per_step": ab["step"],
+        "roofline": {"kernel": "index_scores (k_scores_decode)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(),
+                     "algorithmic_bytes_per_launch": ab["scores_kernel"], "avg_launch_us": round(scores_us, 2)},
+        "stages_us_median": stages,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

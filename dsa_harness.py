@@ -144,8 +144,21 @@ class DeviceWorkload:
         dsa.sparse_mla(self.dims, self.q, self.caches[r], self.indices, self.wl.scale, self.out, self.lse,
                        self.num_splits, self.ws_mla)
 
+    def step_select(self):
+        """Top-k and expansion in one launch (pool ids kept for the checks)."""
+        dsa.topk_select_expand(self.dims, self.scores, self.seqs, self.q_seq, self.q_pos, self.indices,
+                               self.pool_ids, self.ws_topk)
+
     def step(self, r: int = 0):
         """One pass of the whole path over replica r."""
+        self.step_store(r)
+        self.step_pools(r)
+        self.step_scores(r)
+        self.step_select()
+        self.step_attention(r)
+
+    def step_unfused(self, r: int = 0):
+        """The same pass with top-k and expansion as separate calls."""
         self.step_store(r)
         self.step_pools(r)
         self.step_scores(r)

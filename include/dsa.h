@@ -158,21 +158,33 @@ int dsa_index_scores(const dsa_dims* dims, const uint16_t* q_idx, const float* w
  * (score descending, pool id ascending; -0 equals +0), and write their ids
  * in ascending order to pool_ids[t][0..K), then -1 up to select_k.  When
  * n_vis <= select_k every visible pool is selected.  NaN scores are outside
- * the contract.
+ * the contract.  Supported: kpool 4, select_k <= 1024 and
+ * ceil(score_stride / 4096) * select_k <= 32768 (262,144 pools at select_k 512).
  *   scores    device fp32 [T, score_stride] (as written by dsa_index_scores)
  *   pool_ids  device int32 [T, select_k]
- *   workspace device, >= dsa_topk_workspace_bytes(dims, T, score_stride) bytes,
- *             256-byte aligned.  It must be zero-filled before its first use;
- *             every call that completes returns the counters and histograms it
- *             uses to zero (the rest is scratch), so it can be reused without
- *             clearing.  Calls sharing one workspace must not overlap.  May be
- *             NULL when the size query returns 0.
+ *   workspace device scratch, >= dsa_topk_workspace_bytes(dims, T,
+ *             score_stride) bytes, 256-byte aligned; needs no initialisation
+ *             and holds nothing between calls.  Calls sharing one workspace
+ *             must not overlap.
  */
 size_t dsa_topk_workspace_bytes(const dsa_dims* dims, int32_t T, int32_t score_stride);
 int dsa_topk_select(const dsa_dims* dims, const float* scores, int32_t score_stride,
                     const dsa_seqs* seqs, int32_t num_seqs, const int32_t* q_seq,
                     const int32_t* q_pos, int32_t T, int32_t* pool_ids,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * topk_select_expand -- topk_select and expand_selection in one launch: the
+ * same selection as dsa_topk_select, written as the expanded index list
+ * (exactly what dsa_expand_selection would produce from it) and, when
+ * pool_ids is not NULL, also as pool ids.  Same workspace contract.
+ *   pool_ids  device int32 [T, select_k] or NULL
+ *   indices   device int32 [T, out_width]
+ */
+int dsa_topk_select_expand(const dsa_dims* dims, const float* scores, int32_t score_stride,
+                           const dsa_seqs* seqs, int32_t num_seqs, const int32_t* q_seq,
+                           const int32_t* q_pos, int32_t T, int32_t* pool_ids, int32_t* indices,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * expand_selection -- [Ref] Functions (expand_selection) and Traps (the -1

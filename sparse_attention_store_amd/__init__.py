@@ -98,6 +98,7 @@ def lib() -> ctypes.CDLL:
             "dsa_index_scores": (ctypes.c_int, [DP, P, P, P, SP, I32, P, P, I32, I32, P, P]),
             "dsa_topk_workspace_bytes": (SZ, [DP, I32, I32]),
             "dsa_topk_select": (ctypes.c_int, [DP, P, I32, SP, I32, P, P, I32, P, P, SZ, P]),
+            "dsa_topk_select_expand": (ctypes.c_int, [DP, P, I32, SP, I32, P, P, I32, P, P, P, SZ, P]),
             "dsa_expand_selection": (ctypes.c_int, [DP, P, SP, I32, P, P, I32, P, P]),
             "dsa_sparse_mla_workspace_bytes": (SZ, [DP, I32, I32]),
             "dsa_sparse_mla": (ctypes.c_int, [DP, P, ctypes.c_int, P, I64, P, I32, F, P, ctypes.c_int, P, I32,
@@ -209,9 +210,9 @@ def topk_workspace_bytes(dims: Dims, T: int, score_stride: int) -> int:
 
 
 def topk_workspace(dims: Dims, T: int, score_stride: int, device="cuda") -> torch.Tensor | None:
-    """A zero-filled workspace of the required size (None when no workspace is needed)."""
+    """A scratch workspace of the required size (None when no workspace is needed)."""
     n = topk_workspace_bytes(dims, T, score_stride)
-    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
 def topk_select(dims: Dims, scores: torch.Tensor, seqs: Seqs, q_seq: torch.Tensor, q_pos: torch.Tensor,
@@ -229,6 +230,27 @@ def topk_select(dims: Dims, scores: torch.Tensor, seqs: Seqs, q_seq: torch.Tenso
     _raise("dsa_topk_select", lib().dsa_topk_select(
         ctypes.byref(dims), scores.data_ptr(), scores.shape[1], ctypes.byref(seqs._c()), seqs.num_seqs,
         q_seq.data_ptr(), q_pos.data_ptr(), T, pool_ids.data_ptr(), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
+def topk_select_expand(dims: Dims, scores: torch.Tensor, seqs: Seqs, q_seq: torch.Tensor, q_pos: torch.Tensor,
+                       indices: torch.Tensor, pool_ids: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None, stream=None):
+    """Top-k selection written straight as index lists [T, out_width] (and pool ids if given)."""
+    _check(scores, torch.float32, "scores")
+    _check(indices, torch.int32, "indices")
+    if pool_ids is not None:
+        _check(pool_ids, torch.int32, "pool_ids")
+    _check(q_seq, torch.int32, "q_seq")
+    _check(q_pos, torch.int32, "q_pos")
+    T = q_pos.shape[0]
+    ws_bytes = 0
+    if workspace is not None:
+        _check(workspace, workspace.dtype, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _raise("dsa_topk_select_expand", lib().dsa_topk_select_expand(
+        ctypes.byref(dims), scores.data_ptr(), scores.shape[1], ctypes.byref(seqs._c()), seqs.num_seqs,
+        q_seq.data_ptr(), q_pos.data_ptr(), T, _ptr(pool_ids), indices.data_ptr(), _ptr(workspace), ws_bytes,
         _stream(stream)))
 
 
@@ -276,5 +298,5 @@ def sparse_mla(dims: Dims, q: torch.Tensor, cache: torch.Tensor, indices: torch.
 __all__ = [
     "DSA_F32", "DSA_BF16", "DsaError", "Dims", "Seqs", "lib", "abi_version", "status_string",
     "store_int8", "index_pools", "index_scores", "topk_workspace_bytes", "topk_workspace",
-    "topk_select", "expand_selection", "sparse_mla_workspace_bytes", "sparse_mla",
+    "topk_select", "topk_select_expand", "expand_selection", "sparse_mla_workspace_bytes", "sparse_mla",
 ]

@@ -153,26 +153,44 @@ size_t dsa_topk_workspace_bytes(const dsa_dims* dims, int32_t T, int32_t score_s
     return dsa_host::topk_workspace_bytes(*dims, T, score_stride);
 }
 
-int dsa_topk_select(const dsa_dims* dims, const float* scores, int32_t score_stride,
-                    const dsa_seqs* seqs, int32_t num_seqs, const int32_t* q_seq,
-                    const int32_t* q_pos, int32_t T, int32_t* pool_ids, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+static int topk_common(const dsa_dims* dims, const float* scores, int32_t score_stride,
+                       const dsa_seqs* seqs, int32_t num_seqs, const int32_t* q_seq,
+                       const int32_t* q_pos, int32_t T, int32_t* pool_ids, int32_t* indices,
+                       void* workspace, size_t workspace_bytes, void* stream) {
     int st = check_dims(dims);
     if (st) return st;
-    if (dims->kpool != 4) return DSA_ERR_UNSUPPORTED;
     if (T < 0 || score_stride < 0) return DSA_ERR_SIZE;
-    st = check_seqs(seqs, num_seqs, false, false, false);
+    if (dims->kpool != 4 || !dsa_host::topk_supported(*dims, score_stride)) return DSA_ERR_UNSUPPORTED;
+    st = check_seqs(seqs, num_seqs, indices != nullptr, false, false);
     if (st) return st;
     if (T == 0) return DSA_OK;
     if (T > 65535) return DSA_ERR_SIZE;
-    if (!scores || !q_seq || !q_pos || !pool_ids) return DSA_ERR_NULL;
+    if (!scores || !q_seq || !q_pos || (!pool_ids && !indices)) return DSA_ERR_NULL;
     const size_t need = dsa_host::topk_workspace_bytes(*dims, T, score_stride);
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return DSA_ERR_WORKSPACE;
         if (!aligned(workspace, 256)) return DSA_ERR_ALIGN;
     }
     return hip_status(dsa_host::launch_topk(*dims, scores, score_stride, *seqs, q_seq, q_pos, T,
-                                            pool_ids, workspace, as_stream(stream)));
+                                            pool_ids, indices, workspace, as_stream(stream)));
+}
+
+int dsa_topk_select(const dsa_dims* dims, const float* scores, int32_t score_stride,
+                    const dsa_seqs* seqs, int32_t num_seqs, const int32_t* q_seq,
+                    const int32_t* q_pos, int32_t T, int32_t* pool_ids, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    if (!pool_ids) return DSA_ERR_NULL;
+    return topk_common(dims, scores, score_stride, seqs, num_seqs, q_seq, q_pos, T, pool_ids, nullptr,
+                       workspace, workspace_bytes, stream);
+}
+
+int dsa_topk_select_expand(const dsa_dims* dims, const float* scores, int32_t score_stride,
+                           const dsa_seqs* seqs, int32_t num_seqs, const int32_t* q_seq,
+                           const int32_t* q_pos, int32_t T, int32_t* pool_ids, int32_t* indices,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    if (!indices) return DSA_ERR_NULL;
+    return topk_common(dims, scores, score_stride, seqs, num_seqs, q_seq, q_pos, T, pool_ids, indices,
+                       workspace, workspace_bytes, stream);
 }
 
 int dsa_expand_selection(const dsa_dims* dims, const int32_t* pool_ids, const dsa_seqs* seqs,

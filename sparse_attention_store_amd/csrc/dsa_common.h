@@ -76,32 +76,31 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 // Exclusive prefix sum of one uint32 per thread over a block of NT threads.
 // `sh` must hold NT / 64 + 1 entries.  Returns the exclusive prefix; *total
-// receives the block total.  Contains __syncthreads().
+// receives the block total.  Wave totals go through LDS once; every thread then
+// adds the totals of the waves before its own (no serial step).  Contains two
+// __syncthreads().
 template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* sh, uint32_t* total) {
+    constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t x = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        uint32_t y = __shfl_up(x, o, kWave);
+        const uint32_t y = __shfl_up(x, o, kWave);
         if (lane >= o) x += y;
     }
     if (lane == 63) sh[wave] = x;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t acc = 0;
-        for (int w = 0; w < NT / 64; ++w) {
-            uint32_t t = sh[w];
-            sh[w] = acc;
-            acc += t;
-        }
-        sh[NT / 64] = acc;
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const uint32_t tw = sh[w];
+        before += w < wave ? tw : 0u;
+        all += tw;
     }
+    *total = all;
     __syncthreads();
-    uint32_t r = sh[wave] + x - v;
-    *total = sh[NT / 64];
-    __syncthreads();
-    return r;
+    return before + x - v;
 }
 
 }  // namespace dsa

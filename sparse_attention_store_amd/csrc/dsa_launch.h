@@ -25,9 +25,10 @@ hipError_t launch_index_scores(const dsa_dims& d, const uint16_t* q_idx, const f
                                hipStream_t s);
 
 size_t topk_workspace_bytes(const dsa_dims& d, int32_t T, int32_t stride);
+bool topk_supported(const dsa_dims& d, int32_t stride);
 hipError_t launch_topk(const dsa_dims& d, const float* scores, int32_t stride, const dsa_seqs& seqs,
                        const int32_t* q_seq, const int32_t* q_pos, int32_t T, int32_t* pool_ids,
-                       void* ws, hipStream_t s);
+                       int32_t* indices, void* ws, hipStream_t s);
 
 hipError_t launch_expand(const dsa_dims& d, const int32_t* pool_ids, const dsa_seqs& seqs,
                          const int32_t* q_seq, const int32_t* q_pos, int32_t T, int32_t* indices,

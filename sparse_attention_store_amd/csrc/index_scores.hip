@@ -138,6 +138,127 @@ __global__ __launch_bounds__(WAVES * 64) void k_scores_mfma(
     }
 }
 
+// Decode kernel (persistent).  Work is a flat list of 256-pool tiles over all
+// queries (a query with n_vis pools has ceil(n_vis / 256) tiles), so ragged
+// lengths balance across the grid; each workgroup (4 waves) walks tiles
+// blockIdx.x, blockIdx.x + gridDim.x, ...  A tile (64 KB, contiguous in HBM)
+// is fetched with fully coalesced 16-byte loads -- consecutive lanes read
+// consecutive chunks, so each load instruction covers whole cache lines --
+// into registers one tile ahead (with the next query's A operand and head
+// weights), then stored to LDS with an XOR swizzle (chunk c of pool row r goes
+// to slot c ^ (r & 15)) so that the MFMA B-operand reads hit all 64 banks
+// once.  Each wave runs two 32-pool N-tiles of the tile.  Pools past a
+// query's visible count are written as -inf, by the partial tile and by a
+// final fill of [tiles*256, stride).
+constexpr int kDecTile = 256;
+constexpr int kDecMaxT = 64;
+__global__ __launch_bounds__(256) void k_scores_decode(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    const uint16_t* __restrict__ pools, const int32_t* __restrict__ first_valid,
+    const int64_t* __restrict__ pool_base, const int32_t* __restrict__ q_seq,
+    const int32_t* __restrict__ q_pos, int T, int stride, float* __restrict__ scores) {
+    __shared__ u32x4 tile[kDecTile * 16];
+    __shared__ int s_first[kDecMaxT + 1];     // first flat tile of each query
+    __shared__ int s_nvis[kDecMaxT];
+    __shared__ int64_t s_base[kDecMaxT];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, g = lane >> 5;
+
+    if (tid < 64) {
+        int nt = 0;
+        if (tid < T) {
+            const int b = q_seq[tid];
+            const int f = first_valid[b];
+            const int qp = q_pos[tid];
+            const int nv = qp >= f ? (qp - f + 1) >> 2 : 0;
+            s_nvis[tid] = nv;
+            s_base[tid] = pool_base[b];
+            nt = (min(nv, stride) + kDecTile - 1) / kDecTile;
+        }
+        int x = nt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o, 64);
+            if (lane >= o) x += y;
+        }
+        if (tid < T) s_first[tid] = x - nt;
+        if (tid == 63) s_first[kDecMaxT] = x;
+    }
+    __syncthreads();
+    const int total = s_first[kDecMaxT];
+
+    auto locate = [&](int i, int& t, int& p0) {
+        int q = 0;
+        while (q + 1 < T && s_first[q + 1] <= i) ++q;
+        t = q;
+        p0 = (i - s_first[q]) * kDecTile;
+    };
+    u32x4 v[16];
+    u32x4 anext[8];
+    f32x4 wnext[4];
+    auto prefetch = [&](int i) {
+        int t, p0;
+        locate(i, t, p0);
+        const int lim = min(s_nvis[t] - p0, kDecTile);
+        const u32x4* src = reinterpret_cast<const u32x4*>(pools + (s_base[t] + p0) * kDI);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int id = tid + k * 256;                    // row id >> 4, chunk id & 15
+            v[k] = (id >> 4) < lim ? src[id] : u32x4{0u, 0u, 0u, 0u};
+        }
+        // A operand: head n, k = g*64 + j*8 + e (chunk g*8 + j).  D rows: 8*(r/4) + 4*g + (r%4).
+        const uint16_t* qrow = q_idx + ((int64_t)t * kHI + n) * kDI + g * 64;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) anext[j] = *reinterpret_cast<const u32x4*>(qrow + j * 8);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) wnext[k] = *reinterpret_cast<const f32x4*>(w + (int64_t)t * kHI + 8 * k + 4 * g);
+    };
+
+    int i = blockIdx.x;
+    if (i < total) prefetch(i);
+    for (; i < total; i += gridDim.x) {
+        int t, p0;
+        locate(i, t, p0);
+        const int n_vis = s_nvis[t];
+        u32x4 areg[8];
+        f32x4 wv[4];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) areg[j] = anext[j];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) wv[k] = wnext[k];
+        __syncthreads();                                     // previous tile's LDS readers are done
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int id = tid + k * 256;
+            const int row = id >> 4;
+            tile[row * 16 + ((id & 15) ^ (row & 15))] = v[k];
+        }
+        if (i + (int)gridDim.x < total) prefetch(i + gridDim.x);
+        __syncthreads();
+        float sc[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int row = wave * 64 + nt * 32 + n;
+            f32x16 acc = {};
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc = mfma32(as_bf16x8(areg[j]), as_bf16x8(tile[row * 16 + ((g * 8 + j) ^ (row & 15))]), acc);
+            float s = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s += wv[r >> 2][r & 3] * fmaxf(acc[r], 0.f);
+            sc[nt] = s + __shfl_xor(s, 32, 64);
+        }
+        const int p = p0 + wave * 64 + g * 32 + n;            // lanes 0-31: N-tile 0, 32-63: N-tile 1
+        if (p < stride) scores[(int64_t)t * stride + p] = p < n_vis ? sc[g] : -INFINITY;
+    }
+    // Pools past the last visible tile of each query.
+    for (int t = 0; t < T; ++t) {
+        const int from = (s_first[t + 1 < T ? t + 1 : kDecMaxT] - s_first[t]) * kDecTile;
+        float* out = scores + (int64_t)t * stride;
+        for (int p = from + blockIdx.x * 256 + tid; p < stride; p += gridDim.x * 256) out[p] = -INFINITY;
+    }
+}
+
 // Vector kernel for other geometries (tiny configurations): one thread per
 // (query, pool), fp32 dot products over bf16 inputs.
 __global__ __launch_bounds__(256) void k_scores_generic(
@@ -179,10 +300,11 @@ hipError_t launch_index_scores(const dsa_dims& d, const uint16_t* q_idx, const f
     if (T == 0 || stride == 0) return hipSuccess;
     if (d.idx_heads == dsa::kHI && d.idx_dim == dsa::kDI) {
         if (T <= 64) {
-            // Decode: one query per workgroup, 256 pools per workgroup.
-            dim3 grid((unsigned)cdiv(stride, 256), (unsigned)T), block(256);
-            hipLaunchKernelGGL((dsa::k_scores_mfma<4, 1>), grid, block, 0, s, q_idx, w, pools,
-                               seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, 1, stride, scores);
+            // Decode: persistent, two 64 KB-LDS workgroups per CU over a flat tile list.
+            const int64_t tiles = cdiv(stride, dsa::kDecTile) * (int64_t)T;
+            const int grid = (int)std::min<int64_t>(tiles, 2 * (int64_t)device_info().cu_count);
+            hipLaunchKernelGGL(dsa::k_scores_decode, dim3((unsigned)grid), dim3(256), 0, s, q_idx, w, pools,
+                               seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, stride, scores);
         } else {
             // Prefill: 512 resident pools per workgroup, 64 queries per workgroup.
             const int qpb = 64;

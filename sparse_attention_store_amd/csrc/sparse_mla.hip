@@ -97,40 +97,59 @@ __global__ __launch_bounds__(256) void k_mla_mfma(
     const int c_end = min(c_begin + chunks_per_split, nchunks);
     const int32_t* idx_row = indices + (int64_t)t * W;
 
-    for (int c = c_begin; c < c_end; ++c) {
-        // ---- 1. gather + dequant to bf16
-        const int r = tid >> 2, sg = tid & 3;
+    // Row gather: thread -> (row tid/4, 128-byte segment tid%4).  Index-list
+    // entries are loaded one chunk ahead of the rows, and the rows of chunk
+    // c+1 are requested before chunk c computes, so the dependent
+    // list -> row latency is paid once per split.
+    const int r = tid >> 2, sg = tid & 3;
+    auto load_idx = [&](int c) {
         const int pos = c * kChunk + r;
-        const int idx = pos < W ? idx_row[pos] : -1;
-        u32x4 raw[8];
+        return (c < c_end && pos < W) ? idx_row[pos] : -1;
+    };
+    u32x4 raw[8];
+    float rsc = 0.f;
+    auto load_rows = [&](int idx) {
         if (idx >= 0) {
             const uint8_t* src = cache + (int64_t)idx * row_bytes + sg * 128;
 #pragma unroll
             for (int i = 0; i < 8; ++i) raw[i] = *reinterpret_cast<const u32x4*>(src + 16 * i);
+            rsc = sg == 0 ? *reinterpret_cast<const float*>(cache + (int64_t)idx * row_bytes + kD) : 0.f;
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) raw[i] = u32x4{0u, 0u, 0u, 0u};
+            rsc = 0.f;
         }
-        float rsc = 0.f;
-        if (sg == 0 && idx >= 0) rsc = *reinterpret_cast<const float*>(cache + (int64_t)idx * row_bytes + kD);
+    };
+    int idx_cur = load_idx(c_begin);
+    int idx_nxt = load_idx(c_begin + 1);
+    if (c_begin < c_end) load_rows(idx_cur);
+
+    for (int c = c_begin; c < c_end; ++c) {
+        // ---- 1. dequant the gathered rows to bf16 in LDS, then request the next chunk
         __syncthreads();                                   // previous chunk's readers are done
-        if (sg == 0) { rs[r] = rsc; rvalid[r] = idx >= 0; }
+        if (sg == 0) { rs[r] = rsc; rvalid[r] = idx_cur >= 0; }
+        const bool have = idx_cur >= 0;
         {
             uint16_t* dst = &kv[r * kKVRow + sg * 128];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                uint32_t b[8];
-                int8x4_to_bf16x4(raw[i][0], b[0], b[1]);
-                int8x4_to_bf16x4(raw[i][1], b[2], b[3]);
-                int8x4_to_bf16x4(raw[i][2], b[4], b[5]);
-                int8x4_to_bf16x4(raw[i][3], b[6], b[7]);
-                const u32x4 o0 = {b[0], b[1], b[2], b[3]};
-                const u32x4 o1 = {b[4], b[5], b[6], b[7]};
+                uint32_t bq[8];
+                int8x4_to_bf16x4(raw[i][0], bq[0], bq[1]);
+                int8x4_to_bf16x4(raw[i][1], bq[2], bq[3]);
+                int8x4_to_bf16x4(raw[i][2], bq[4], bq[5]);
+                int8x4_to_bf16x4(raw[i][3], bq[6], bq[7]);
+                const u32x4 o0 = {bq[0], bq[1], bq[2], bq[3]};
+                const u32x4 o1 = {bq[4], bq[5], bq[6], bq[7]};
                 *reinterpret_cast<u32x4*>(dst + 16 * i) = o0;
                 *reinterpret_cast<u32x4*>(dst + 16 * i + 8) = o1;
             }
         }
-        if (!__syncthreads_or(idx >= 0)) continue;          // empty chunk
+        if (c + 1 < c_end) {
+            load_rows(idx_nxt);
+            idx_cur = idx_nxt;
+            idx_nxt = load_idx(c + 2);
+        }
+        if (!__syncthreads_or(have)) continue;             // empty chunk
 
         // ---- 2. S for this wave's head tile and row tiles sub*HT .. sub*HT+HT-1
         f32x4 sacc[HT];
@@ -284,28 +303,46 @@ __global__ __launch_bounds__(256) void k_mla_mfma(
 }
 
 // Merge split partials in split order: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// The (m, l) pairs go through LDS first; then every thread issues the loads of
+// its 4 columns for all non-empty splits before accumulating them in order.
+constexpr int kMaxSplits = 64;
 __global__ __launch_bounds__(128) void k_mla_combine(
     const float* __restrict__ part_o, const MlaPartial* __restrict__ part_ml, int splits, int H,
     void* __restrict__ out, int out_f32, float* __restrict__ lse) {
+    __shared__ float wgt[kMaxSplits];
+    __shared__ float s_M, s_L;
     const int h = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
-    float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) {
-        const MlaPartial p = part_ml[((int64_t)t * splits + s) * H + h];
-        if (p.l > 0.f) M = fmaxf(M, p.m);
+    if (tid < 64) {
+        MlaPartial p = {-INFINITY, 0.f};
+        if (tid < splits) p = part_ml[((int64_t)t * splits + tid) * H + h];
+        const bool live = p.l > 0.f;
+        float M = live ? p.m : -INFINITY;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+        const float w = live ? exp2f(p.m - M) : 0.f;
+        float L = p.l * w;
+        // Sum in split order (a fixed tree over lanes 0..63) for determinism.
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
+        wgt[tid] = w;
+        if (tid == 0) { s_M = M; s_L = L; }
     }
+    __syncthreads();
+    const float L = s_L;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float L = 0.f;
-    if (M != -INFINITY) {
-        for (int s = 0; s < splits; ++s) {
-            const int64_t slot = ((int64_t)t * splits + s) * H + h;
-            const MlaPartial p = part_ml[slot];
-            if (!(p.l > 0.f)) continue;
-            const float wgt = exp2f(p.m - M);
-            L += p.l * wgt;
-            const f32x4 o = *reinterpret_cast<const f32x4*>(part_o + slot * kD + tid * 4);
-            acc += o * wgt;
-        }
+    const float* base = part_o + ((int64_t)t * splits * H + h) * kD + tid * 4;
+    const int64_t sstride = (int64_t)H * kD;
+    int s = 0;
+    for (; s + 8 <= splits; s += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            v[u] = wgt[s + u] > 0.f ? *reinterpret_cast<const f32x4*>(base + (s + u) * sstride) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += v[u] * wgt[s + u];
     }
+    for (; s < splits; ++s)
+        if (wgt[s] > 0.f) acc += *reinterpret_cast<const f32x4*>(base + s * sstride) * wgt[s];
     const float inv = L > 0.f ? 1.0f / L : 0.f;
     acc *= inv;
     const int64_t orow = ((int64_t)t * H + h) * kD + tid * 4;
@@ -317,7 +354,7 @@ __global__ __launch_bounds__(128) void k_mla_combine(
         pk[1] = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
         *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + orow) = pk;
     }
-    if (lse && tid == 0) lse[(int64_t)t * H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    if (lse && tid == 0) lse[(int64_t)t * H + h] = L > 0.f ? (s_M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 // fp32 vector kernel for other shapes (tiny geometry, fp32 q): one wave per
@@ -403,8 +440,9 @@ MlaPlan plan_sparse_mla(const dsa_dims& d, int32_t T, int32_t num_splits, int q_
         want = num_splits < nchunks ? num_splits : nchunks;
     } else {
         const int64_t base = (int64_t)T * p.head_groups;
-        want = base >= cu ? 1 : (int)std::min<int64_t>(nchunks, cdiv(2 * cu, base));
+        want = base >= cu ? 1 : (int)std::min<int64_t>(nchunks, cdiv(cu, base));
     }
+    if (want > dsa::kMaxSplits) want = dsa::kMaxSplits;
     p.chunks_per_split = (int)cdiv(nchunks, want);
     p.splits = (int)cdiv(nchunks, p.chunks_per_split);
     p.ws_bytes = p.splits > 1

@@ -1,443 +1,360 @@
 // topk_select: per query, the K = min(select_k, n_vis) best pools by
 // (score descending, pool id ascending), emitted in ascending id order and
 // padded with -1 ([Ref] Functions: topk_pools; [Flash] Stream C:
-// indexer_topk512).  Scores are mapped to order-preserving uint32 keys.
+// indexer_topk512).  Optionally the same launches also write the expanded
+// index list ([Ref] Functions: expand_selection).
 //
-// Two paths:
-//  * rows: one 1024-thread workgroup per query row, the whole row of keys in
-//    LDS.  The K-th largest key is found by range bucketing: each pass
-//    histograms the keys inside [lo, hi] into 2048 equal-width buckets
-//    (integer arithmetic on the key), keeps the bucket that holds rank K and
-//    narrows [lo, hi] to it; a 32-bit key range closes in at most 3 passes.
-//    A scan in id order then emits every key above the threshold and the
-//    first `need` keys equal to it, which is exactly the tie rule.
-//  * long: rows too long for LDS (decode at 262k..1M context) are split over
-//    many workgroups.  Launch 1 builds a 4096-bin histogram of the key's top
-//    12 bits per row (LDS histogram, then one global add per non-empty bin);
-//    the last workgroup of the row (atomic ticket) finds the bin holding rank
-//    K.  Launch 2 sends keys above that bin to a "sure" list and keys inside
-//    it to a candidate list of 64-bit (key, ~id) composites; the last
-//    workgroup selects the best candidates exactly (composites are unique, so
-//    no tie remains), bitonic-sorts the K ids and writes them.  Counters,
-//    histograms and tickets are cleared by the workgroup that consumed them,
-//    so the workspace stays zero-filled between calls.
+// Two stages, no cross-workgroup atomics and no state kept between calls:
+//  A. Each query row is cut into chunks of 4096 pools.  One 256-thread
+//     workgroup per chunk selects the chunk's best min(select_k, chunk) pools
+//     under the same order and writes them, in ascending id order, as 64-bit
+//     composites (key << 32 | ~id), where key is the order-preserving uint32
+//     image of the fp32 score (-0 mapped to +0).  Every member of the row's
+//     top-K is in its chunk's top-K under this total order, so the union of
+//     the chunk lists contains the answer.
+//  B. One 1024-thread workgroup per row selects the best K of that union (at
+//     most 64 chunks x select_k, held in registers).  The chunk lists are in
+//     ascending id order, so the same 32-bit key selection with ties taken in
+//     list order applies the tie rule, and a scan-based compaction emits the
+//     ids sorted.
+// Both stages find the K-th largest key by range bucketing in LDS: each pass
+// histograms the keys inside [lo, hi] into one bucket per thread, of width
+// 2^sh (the key offset shifted right), keeps the bucket that holds rank K and
+// narrows [lo, hi] to it, until that bucket is taken whole or (stage A) one key
+// value is left, whose first `need` occurrences in id order are taken -- the
+// tie rule.
 #include "dsa_common.h"
 #include "dsa_launch.h"
 
 namespace dsa {
 
-constexpr int kRowNT = 1024;
-constexpr int kRowBins = 2048;
-constexpr int kLongNT = 256;
-constexpr int kLongChunk = 4096;          // keys per workgroup (long path)
-constexpr int kLongBins = 4096;           // level-1 bins: key >> 20
-constexpr int kLongMaxK = 1024;           // select_k limit of the long path
-constexpr int kCandLds = 4096;            // candidates held in LDS by the finishing workgroup
+constexpr int kChunkKeys = 4096;            // pools per stage-A workgroup
+constexpr int kANT = 256, kAKPT = kChunkKeys / kANT;
+constexpr int kBNT = 1024;
+constexpr int kMaxK = 1024;                 // select_k limit
+constexpr int kMaxCand = 32 * kBNT;         // stage-B capacity (chunks x select_k)
 
-struct TopkRowHdr {                       // 64 bytes per query row
-    uint32_t hist_done, filt_done, n_sure, n_cand, thr_bin, above, pad[10];
+struct Emit {
+    int32_t* pool_ids;        // [T, select_k] or null
+    int32_t* indices;         // [T, W] or null
+    const int64_t* row_base;
+    int W;
 };
 
-__device__ __forceinline__ int n_visible(const int32_t* first_valid, const int32_t* q_seq,
-                                         const int32_t* q_pos, int t) {
-    const int b = q_seq[t];
-    const int f = first_valid[b];
-    const int qp = q_pos[t];
-    return qp >= f ? (qp - f + 1) >> 2 : 0;
+__device__ __forceinline__ void query_geom(const int32_t* first_valid, const int32_t* q_seq,
+                                           const int32_t* q_pos, int t, int& b, int& f, int& qp,
+                                           int& n_vis) {
+    b = q_seq[t];
+    f = first_valid[b];
+    qp = q_pos[t];
+    n_vis = qp >= f ? (qp - f + 1) >> 2 : 0;
 }
 
-__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Write K ascending ids (sel[0..K), or 0..K-1 when sel is null) as pool ids
+// (-1 padded) and/or as the expanded index list.  No barrier inside.
+template <int NT>
+__device__ __forceinline__ void emit_selection(const int32_t* sel, int K, int select_k, int t, int b,
+                                               int f, int qp, int n_vis, const Emit& e) {
+    const int tid = threadIdx.x;
+    if (e.pool_ids) {
+        int32_t* out = e.pool_ids + (int64_t)t * select_k;
+        for (int i = tid; i < select_k; i += NT) out[i] = i < K ? (sel ? sel[i] : i) : -1;
+    }
+    if (e.indices) {
+        const int64_t rb = e.row_base[b];
+        const int nsel = 4 * K;
+        const int tail = qp >= f ? (qp - f + 1) - 4 * n_vis : 0;
+        int32_t* out = e.indices + (int64_t)t * e.W;
+        for (int j = tid; j < e.W; j += NT) {
+            int64_t v = -1;
+            if (j < nsel) v = rb + f + 4 * (int64_t)(sel ? sel[j >> 2] : (j >> 2)) + (j & 3);
+            else if (j < nsel + tail) v = rb + f + 4 * (int64_t)n_vis + (j - nsel);
+            out[j] = (int32_t)v;
+        }
+    }
 }
 
-// ---------------------------------------------------------------- rows path
+template <typename KT>
+__device__ __forceinline__ KT shfl_xor_k(KT v, int o) {
+    if constexpr (sizeof(KT) == 8) {
+        const uint32_t lo = __shfl_xor((int)(uint32_t)v, o, 64);
+        const uint32_t hi = __shfl_xor((int)(uint32_t)(v >> 32), o, 64);
+        return ((uint64_t)hi << 32) | lo;
+    } else {
+        return (KT)__shfl_xor((int)v, o, 64);
+    }
+}
+
+template <typename KT>
+__device__ __forceinline__ int bit_len(KT v) {
+    if constexpr (sizeof(KT) == 8) return v ? 64 - __clzll((long long)v) : 0;
+    else return v ? 32 - __clz((int)v) : 0;
+}
+
+// Block min (over non-zero keys) and max of register keys.
+template <int NT, int KPT, typename KT>
+__device__ __forceinline__ void block_min_max(const KT (&key)[KPT], KT* sh, KT& kmin, KT& kmax) {
+    KT mn = ~(KT)0, mx = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        if (key[j]) mn = key[j] < mn ? key[j] : mn;
+        mx = key[j] > mx ? key[j] : mx;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const KT a = shfl_xor_k(mn, o), c = shfl_xor_k(mx, o);
+        mn = a < mn ? a : mn;
+        mx = c > mx ? c : mx;
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) { sh[2 * w] = mn; sh[2 * w + 1] = mx; }
+    __syncthreads();
+    kmin = sh[0];
+    kmax = sh[1];
+    for (int i = 1; i < NT / 64; ++i) {
+        kmin = sh[2 * i] < kmin ? sh[2 * i] : kmin;
+        kmax = sh[2 * i + 1] > kmax ? sh[2 * i + 1] : kmax;
+    }
+    __syncthreads();
+}
+
+// One bucket per thread: NT buckets per pass, double-buffered so the next
+// pass's buckets are cleared while this pass's are read.
+template <int NT>
+struct SelShared {
+    uint32_t hist[2][NT];
+    uint32_t scan[NT / 64 + 1];
+    uint32_t bin[2], above[2], cnt[2];
+};
 
 template <int NT>
-__device__ __forceinline__ uint32_t block_min_u32(uint32_t v, uint32_t* sh) {
-    for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
-    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-    __syncthreads();
-    uint32_t r = sh[0];
-    for (int w = 1; w < NT / 64; ++w) r = min(r, sh[w]);
-    __syncthreads();
-    return r;
-}
+constexpr int log2_of() { return NT == 256 ? 8 : (NT == 512 ? 9 : 10); }
 
-template <int NT>
-__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* sh) {
-    for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
-    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-    __syncthreads();
-    uint32_t r = sh[0];
-    for (int w = 1; w < NT / 64; ++w) r = max(r, sh[w]);
-    __syncthreads();
-    return r;
-}
-
-__global__ __launch_bounds__(kRowNT) void k_topk_rows(
-    const float* __restrict__ scores, int stride, const int32_t* __restrict__ first_valid,
-    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int select_k,
-    int32_t* __restrict__ pool_ids) {
-    extern __shared__ uint32_t keys[];
-    __shared__ uint32_t hist[kRowBins];
-    __shared__ uint32_t scan_sh[kRowNT / 64 + 1];
-    __shared__ uint32_t s_bin, s_above;
-
-    const int t = blockIdx.x, tid = threadIdx.x;
-    const int n = min(n_visible(first_valid, q_seq, q_pos, t), stride);
-    int32_t* out = pool_ids + (int64_t)t * select_k;
-    if (n <= select_k) {                                  // every visible pool is selected
-        for (int i = tid; i < select_k; i += kRowNT) out[i] = i < n ? i : -1;
-        return;
-    }
-    const float* row = scores + (int64_t)t * stride;
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-    for (int i = tid; i < n; i += kRowNT) {
-        const uint32_t k = f32_key(row[i]);
-        keys[i] = k;
-        kmin = min(kmin, k);
-        kmax = max(kmax, k);
-    }
-    kmin = block_min_u32<kRowNT>(kmin, scan_sh);
-    kmax = block_max_u32<kRowNT>(kmax, scan_sh);
-
-    uint32_t lo = kmin, hi = kmax, krem = (uint32_t)select_k;
-    // A 32-bit range closes in 3 passes; the cap only bounds the loop.
-    for (int pass = 0; pass < 6 && lo < hi; ++pass) {
-        const uint64_t range = (uint64_t)(hi - lo) + 1u;
-        for (int b = tid; b < kRowBins; b += kRowNT) hist[b] = 0u;
-        __syncthreads();
-        for (int i = tid; i < n; i += kRowNT) {
-            const uint32_t k = keys[i];
-            if (k >= lo && k <= hi)
-                atomicAdd(&hist[(uint32_t)(((uint64_t)(k - lo) * kRowBins) / range)], 1u);
+// Find the range [lo, hi] holding the rank-`target` key (absent keys are 0).
+// On return every key > hi is in the top `target`; `krem` of the keys inside
+// [lo, hi] complete it: all of them when `whole`, else (lo == hi) the first
+// krem in id order.  Each pass cuts the span by log2(NT) bits.
+template <int NT, int KPT, typename KT>
+__device__ __forceinline__ void bucket_select(const KT (&key)[KPT], uint32_t target, SelShared<NT>& S,
+                                              KT* mm_sh, KT& lo, KT& hi, uint32_t& krem, bool& whole) {
+    constexpr int BITS = log2_of<NT>();
+    const int tid = threadIdx.x;
+    S.hist[0][tid] = 0u;
+    S.hist[1][tid] = 0u;
+    block_min_max<NT, KPT, KT>(key, mm_sh, lo, hi);          // contains the barrier that publishes the clears
+    krem = target;
+    whole = false;
+    // The cap only bounds the loop (a 64-bit span closes in at most 8 passes).
+    for (int pass = 0; pass < 8 && lo < hi; ++pass) {
+        const int buf = pass & 1;
+        const int sh = bit_len<KT>((hi - lo) >> BITS);
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const KT k = key[j];
+            if (k >= lo && k <= hi) atomicAdd(&S.hist[buf][(uint32_t)((k - lo) >> sh)], 1u);
         }
         __syncthreads();
-        // Thread j owns buckets kRowBins-1-2j and kRowBins-2-2j (scanned from the top).
-        const int b0 = kRowBins - 1 - 2 * tid, b1 = b0 - 1;
-        const uint32_t h0 = hist[b0], h1 = hist[b1];
+        const uint32_t h = S.hist[buf][NT - 1 - tid];         // thread order = descending buckets
+        S.hist[buf ^ 1][tid] = 0u;                            // read two passes ago; free now
         uint32_t total;
-        const uint32_t above = block_exclusive_scan<kRowNT>(h0 + h1, scan_sh, &total);
-        if (above < krem && krem <= above + h0) { s_bin = b0; s_above = above; }
-        else if (above + h0 < krem && krem <= above + h0 + h1) { s_bin = b1; s_above = above + h0; }
+        const uint32_t above = block_exclusive_scan<NT>(h, S.scan, &total);
+        if (above < krem && krem <= above + h) {
+            S.bin[buf] = NT - 1 - tid;
+            S.above[buf] = above;
+            S.cnt[buf] = h;
+        }
         __syncthreads();
-        const uint64_t bin = s_bin;
-        krem -= s_above;
-        const uint32_t nlo = lo + (uint32_t)((bin * range + kRowBins - 1) / kRowBins);
-        const uint32_t nhi = lo + (uint32_t)(((bin + 1) * range + kRowBins - 1) / kRowBins) - 1u;
+        krem -= S.above[buf];
+        const KT nlo = lo + ((KT)S.bin[buf] << sh);
+        const KT nhi = nlo + (((KT)1 << sh) - 1);
         lo = nlo;
-        hi = nhi;
-        __syncthreads();
+        hi = nhi < hi ? nhi : hi;
+        whole = S.cnt[buf] == krem;
+        if (whole) break;
     }
-    const uint32_t tau = lo, need_eq = krem;
+    if (!(lo == hi && !whole)) whole = true;
+}
 
-    // Emit in id order: keys > tau, plus the first need_eq keys == tau.
-    const int per = (n + kRowNT - 1) / kRowNT;
-    const int i0 = min(tid * per, n), i1 = min(i0 + per, n);
-    uint32_t gt = 0, eq = 0;
-    for (int i = i0; i < i1; ++i) {
-        const uint32_t k = keys[i];
-        gt += k > tau;
-        eq += k == tau;
+// This thread's output slot (exclusive scan of its selected-key count) and its
+// budget `take` of keys inside [lo, hi].
+template <int NT, int KPT, typename KT>
+__device__ __forceinline__ uint32_t compaction_slot(const KT (&key)[KPT], KT lo, KT hi, uint32_t krem,
+                                                    bool whole, SelShared<NT>& S, uint32_t& take) {
+    uint32_t gt = 0, in = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        gt += key[j] > hi;
+        in += key[j] >= lo && key[j] <= hi;
     }
     uint32_t total;
-    const uint32_t eq_base = block_exclusive_scan<kRowNT>(eq, scan_sh, &total);
-    uint32_t take = need_eq > eq_base ? min(need_eq - eq_base, eq) : 0u;
-    const uint32_t pos0 = block_exclusive_scan<kRowNT>(gt + take, scan_sh, &total);
-    uint32_t pos = pos0;
-    for (int i = i0; i < i1; ++i) {
-        const uint32_t k = keys[i];
-        const bool pick = k > tau || (k == tau && take > 0);
-        if (k == tau && pick) --take;
-        if (pick && pos < (uint32_t)select_k) out[pos] = i;
+    take = in;
+    if (!whole) {
+        const uint32_t base = block_exclusive_scan<NT>(in, S.scan, &total);
+        take = krem > base ? min(krem - base, in) : 0u;
+    }
+    return block_exclusive_scan<NT>(gt + take, S.scan, &total);
+}
+
+// ---------------------------------------------------------------- stage A
+
+__global__ __launch_bounds__(kANT) void k_topk_chunks(
+    const float* __restrict__ scores, int stride, const int32_t* __restrict__ first_valid,
+    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int select_k, int nchunks,
+    uint64_t* __restrict__ cand, int32_t* __restrict__ cand_n) {
+    __shared__ SelShared<kANT> S;
+    __shared__ uint32_t mm_sh[2 * kANT / 64];
+    const int c = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+    int b, f, qp, n_vis;
+    query_geom(first_valid, q_seq, q_pos, t, b, f, qp, n_vis);
+    const int n = min(n_vis, stride);
+    if (n <= select_k) return;                               // stage B selects every pool
+    const int c0 = c * kChunkKeys;
+    const int cn = max(0, min(n - c0, kChunkKeys));          // keys in this chunk
+    uint64_t* out = cand + ((int64_t)t * nchunks + c) * select_k;
+    const float* row = scores + (int64_t)t * stride + c0;
+    if (cn <= select_k) {                                    // the whole chunk is a candidate set
+        for (int i = tid; i < cn; i += kANT)
+            out[i] = ((uint64_t)f32_key(row[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(c0 + i));
+        if (tid == 0) cand_n[t * nchunks + c] = cn;
+        return;
+    }
+    // Keys [c0 + tid*16, +16); absent keys are 0, below every real key.
+    const int i0 = tid * kAKPT;
+    uint32_t key[kAKPT];
+    const bool vec = ((stride & 3) == 0) && ((reinterpret_cast<uintptr_t>(scores) & 15) == 0);
+    if (vec && i0 + kAKPT <= cn) {
+#pragma unroll
+        for (int q = 0; q < kAKPT / 4; ++q) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(row + i0 + 4 * q);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) key[4 * q + e] = f32_key(v[e]);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kAKPT; ++j) key[j] = (i0 + j < cn) ? f32_key(row[i0 + j]) : 0u;
+    }
+    uint32_t lo, hi, krem;
+    bool whole;
+    bucket_select<kANT, kAKPT, uint32_t>(key, (uint32_t)select_k, S, mm_sh, lo, hi, krem, whole);
+    uint32_t take;
+    uint32_t pos = compaction_slot<kANT, kAKPT, uint32_t>(key, lo, hi, krem, whole, S, take);
+#pragma unroll
+    for (int j = 0; j < kAKPT; ++j) {
+        const uint32_t k = key[j];
+        const bool inr = k >= lo && k <= hi;
+        const bool pick = k > hi || (inr && take > 0);
+        take -= (inr && take > 0) ? 1u : 0u;
+        if (pick && pos < (uint32_t)select_k)
+            out[pos] = ((uint64_t)k << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(c0 + i0 + j));
         pos += pick;
     }
+    if (tid == 0) cand_n[t * nchunks + c] = select_k;
 }
 
-// ---------------------------------------------------------------- long path
+// ---------------------------------------------------------------- stage B
 
-struct LongWs {
-    TopkRowHdr* hdr;
-    uint32_t* hist;     // [T][kLongBins]
-    int32_t* sure;      // [T][select_k]
-    uint64_t* cand;     // [T][stride]
-};
-
-__device__ __forceinline__ LongWs long_ws(void* ws, int T, int select_k, int stride) {
-    char* p = reinterpret_cast<char*>(ws);
-    LongWs w;
-    w.hdr = reinterpret_cast<TopkRowHdr*>(p);
-    p += ((size_t)T * sizeof(TopkRowHdr) + 255) & ~(size_t)255;
-    w.hist = reinterpret_cast<uint32_t*>(p);
-    p += ((size_t)T * kLongBins * 4 + 255) & ~(size_t)255;
-    w.sure = reinterpret_cast<int32_t*>(p);
-    p += ((size_t)T * select_k * 4 + 255) & ~(size_t)255;
-    w.cand = reinterpret_cast<uint64_t*>(p);
-    return w;
-}
-
-__global__ __launch_bounds__(kLongNT) void k_topk_long_hist(
-    const float* __restrict__ scores, int stride, const int32_t* __restrict__ first_valid,
-    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int select_k, int T,
-    void* ws, int groups) {
-    __shared__ uint32_t h[kLongBins];
-    __shared__ uint32_t scan_sh[kLongNT / 64 + 1];
-    __shared__ int s_last;
-    const int t = blockIdx.y, tid = threadIdx.x;
-    const int n = min(n_visible(first_valid, q_seq, q_pos, t), stride);
-    if (n <= select_k) return;
-    LongWs w = long_ws(ws, T, select_k, stride);
-    TopkRowHdr* hdr = w.hdr + t;
-    uint32_t* gh = w.hist + (size_t)t * kLongBins;
-
-    for (int b = tid; b < kLongBins; b += kLongNT) h[b] = 0u;
-    __syncthreads();
-    const float* row = scores + (int64_t)t * stride;
-    const int i0 = blockIdx.x * kLongChunk, i1 = min(i0 + kLongChunk, n);
-    for (int i = i0 + tid; i < i1; i += kLongNT) atomicAdd(&h[f32_key(row[i]) >> 20], 1u);
-    __syncthreads();
-    for (int b = tid; b < kLongBins; b += kLongNT)
-        if (h[b]) atomicAdd(&gh[b], h[b]);
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&hdr->hist_done, 1u) == (uint32_t)(groups - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-
-    // Last workgroup of the row: find the bin holding rank K, scanning from the top.
-    constexpr int PER = kLongBins / kLongNT;               // 16 bins per thread
-    uint32_t loc[PER];
-    uint32_t sum = 0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        loc[j] = ld_agent(&gh[kLongBins - 1 - (tid * PER + j)]);
-        sum += loc[j];
-    }
-    uint32_t total;
-    uint32_t above = block_exclusive_scan<kLongNT>(sum, scan_sh, &total);
-    const uint32_t K = (uint32_t)select_k;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        if (above < K && K <= above + loc[j]) {
-            hdr->thr_bin = (uint32_t)(kLongBins - 1 - (tid * PER + j));
-            hdr->above = above;
-        }
-        above += loc[j];
-    }
-    for (int b = tid; b < kLongBins; b += kLongNT) gh[b] = 0u;
-    if (tid == 0) hdr->hist_done = 0u;
-}
-
-// Rank-r threshold among n unique 64-bit composites: returns the r-th largest.
-template <int NT>
-__device__ uint64_t select_u64_rank(const uint64_t* src, uint32_t n, uint32_t r, uint32_t* hist,
-                                    uint32_t* scan_sh, uint64_t* s_lo, uint64_t* s_hi,
-                                    uint32_t* s_krem) {
-    constexpr int NB = 2048;
-    const int tid = threadIdx.x;
-    uint64_t lmin = ~0ull, lmax = 0ull;
-    for (uint32_t i = tid; i < n; i += NT) {
-        const uint64_t v = src[i];
-        lmin = v < lmin ? v : lmin;
-        lmax = v > lmax ? v : lmax;
-    }
-    if (tid == 0) { *s_lo = ~0ull; *s_hi = 0ull; *s_krem = r; }
-    __syncthreads();
-    atomicMin((unsigned long long*)s_lo, (unsigned long long)lmin);
-    atomicMax((unsigned long long*)s_hi, (unsigned long long)lmax);
-    __syncthreads();
-    uint64_t lo = *s_lo, hi = *s_hi;
-    uint32_t krem = r;
-    __shared__ uint32_t s_bin, s_above;
-    // A 52-bit range closes in 5 passes; the cap only bounds the loop.
-    for (int pass = 0; pass < 8 && lo < hi; ++pass) {
-        const uint64_t range = hi - lo + 1u;                // < 2^52 (keys share their top 12 bits)
-        for (int b = tid; b < NB; b += NT) hist[b] = 0u;
-        __syncthreads();
-        for (uint32_t i = tid; i < n; i += NT) {
-            const uint64_t v = src[i];
-            if (v >= lo && v <= hi) atomicAdd(&hist[(uint32_t)(((v - lo) * NB) / range)], 1u);
-        }
-        __syncthreads();
-        constexpr int PER = NB / NT;
-        uint32_t loc[PER];
-        uint32_t sum = 0;
-        for (int j = 0; j < PER; ++j) {
-            loc[j] = hist[NB - 1 - (tid * PER + j)];
-            sum += loc[j];
-        }
-        uint32_t total;
-        uint32_t above = block_exclusive_scan<NT>(sum, scan_sh, &total);
-        for (int j = 0; j < PER; ++j) {
-            if (above < krem && krem <= above + loc[j]) {
-                s_bin = (uint32_t)(NB - 1 - (tid * PER + j));
-                s_above = above;
-            }
-            above += loc[j];
-        }
-        __syncthreads();
-        const uint64_t bin = s_bin;
-        krem -= s_above;
-        const uint64_t nlo = lo + (bin * range + NB - 1) / NB;
-        const uint64_t nhi = lo + ((bin + 1) * range + NB - 1) / NB - 1u;
-        lo = nlo;
-        hi = nhi;
-        __syncthreads();
-    }
-    return lo;
-}
-
-__global__ __launch_bounds__(kLongNT) void k_topk_long_filter(
-    const float* __restrict__ scores, int stride, const int32_t* __restrict__ first_valid,
-    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int select_k, int T,
-    void* ws, int groups, int32_t* __restrict__ pool_ids) {
-    __shared__ uint64_t l_cand[kCandLds];
-    __shared__ int32_t l_sel[kLongMaxK];
-    __shared__ uint32_t hist[2048];
-    __shared__ uint32_t scan_sh[kLongNT / 64 + 1];
-    __shared__ uint32_t l_ns, l_nc, s_sbase, s_cbase, s_krem;
-    __shared__ uint64_t s_lo, s_hi;
-    __shared__ int s_last;
-
-    const int t = blockIdx.y, tid = threadIdx.x;
-    const int n = min(n_visible(first_valid, q_seq, q_pos, t), stride);
-    int32_t* out = pool_ids + (int64_t)t * select_k;
-    if (n <= select_k) {
-        if (blockIdx.x == 0)
-            for (int i = tid; i < select_k; i += kLongNT) out[i] = i < n ? i : -1;
+template <int KPT>
+__global__ __launch_bounds__(kBNT) void k_topk_merge(
+    const int32_t* __restrict__ first_valid, const int32_t* __restrict__ q_seq,
+    const int32_t* __restrict__ q_pos, int stride, int select_k, int nchunks,
+    const uint64_t* __restrict__ cand, const int32_t* __restrict__ cand_n, Emit e) {
+    __shared__ SelShared<kBNT> S;
+    __shared__ uint32_t mm_sh[2 * kBNT / 64];
+    __shared__ int32_t sel[kMaxK];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    int b, f, qp, n_vis;
+    query_geom(first_valid, q_seq, q_pos, t, b, f, qp, n_vis);
+    const int n = min(n_vis, stride);
+    if (n <= select_k) {                                     // every visible pool is selected
+        emit_selection<kBNT>(nullptr, n, select_k, t, b, f, qp, n_vis, e);
         return;
     }
-    LongWs w = long_ws(ws, T, select_k, stride);
-    TopkRowHdr* hdr = w.hdr + t;
-    int32_t* gsure = w.sure + (size_t)t * select_k;
-    uint64_t* gcand = w.cand + (size_t)t * stride;
-    const uint32_t thr = hdr->thr_bin;
-
-    if (tid == 0) { l_ns = 0u; l_nc = 0u; }
-    __syncthreads();
-    const float* row = scores + (int64_t)t * stride;
-    const int i0 = blockIdx.x * kLongChunk, i1 = min(i0 + kLongChunk, n);
-    for (int i = i0 + tid; i < i1; i += kLongNT) {
-        const uint32_t k = f32_key(row[i]);
-        const uint32_t bin = k >> 20;
-        if (bin > thr) {
-            const uint32_t j = atomicAdd(&l_ns, 1u);       // < select_k per row in total
-            if (j < (uint32_t)kLongMaxK) l_sel[j] = i;
-        } else if (bin == thr) {
-            const uint32_t j = atomicAdd(&l_nc, 1u);       // <= kLongChunk per workgroup
-            if (j < (uint32_t)kCandLds) l_cand[j] = ((uint64_t)k << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
-        }
-    }
-    __syncthreads();
-    if (tid == 0) {
-        s_sbase = l_ns ? atomicAdd(&hdr->n_sure, l_ns) : 0u;
-        s_cbase = l_nc ? atomicAdd(&hdr->n_cand, l_nc) : 0u;
-    }
-    __syncthreads();
-    for (uint32_t j = tid; j < l_ns; j += kLongNT)
-        if (s_sbase + j < (uint32_t)select_k) gsure[s_sbase + j] = l_sel[j];
-    for (uint32_t j = tid; j < l_nc; j += kLongNT)
-        if (s_cbase + j < (uint32_t)stride) gcand[s_cbase + j] = l_cand[j];
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&hdr->filt_done, 1u) == (uint32_t)(groups - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-
-    // Last workgroup: exact selection among the threshold-bin candidates.
-    const uint32_t ns = min(ld_agent(&hdr->n_sure), (uint32_t)select_k);
-    const uint32_t nc = min(ld_agent(&hdr->n_cand), (uint32_t)stride);
-    const uint32_t need = (uint32_t)select_k - ns;
-    const uint64_t* src = gcand;
-    if (nc <= (uint32_t)kCandLds) {
-        for (uint32_t j = tid; j < nc; j += kLongNT) l_cand[j] = __hip_atomic_load(&gcand[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        src = l_cand;
-        __syncthreads();
-    }
-    const uint64_t tau = select_u64_rank<kLongNT>(src, nc, need, hist, scan_sh, &s_lo, &s_hi, &s_krem);
-    for (uint32_t j = tid; j < ns; j += kLongNT) l_sel[j] = __hip_atomic_load(&gsure[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (tid == 0) l_ns = ns;
-    __syncthreads();
-    for (uint32_t j = tid; j < nc; j += kLongNT) {
-        const uint64_t v = src[j];
-        if (v >= tau) {
-            const uint32_t s2 = atomicAdd(&l_ns, 1u);
-            if (s2 < (uint32_t)select_k) l_sel[s2] = (int32_t)(0xFFFFFFFFu - (uint32_t)v);
-        }
-    }
-    __syncthreads();
-    int P = 1;
-    while (P < select_k) P <<= 1;
-    for (int j = select_k + tid; j < P; j += kLongNT) l_sel[j] = 0x7FFFFFFF;
-    __syncthreads();
-    for (int k = 2; k <= P; k <<= 1) {
-        for (int jj = k >> 1; jj > 0; jj >>= 1) {
-            for (int i = tid; i < P; i += kLongNT) {
-                const int ixj = i ^ jj;
-                if (ixj > i) {
-                    const int a = l_sel[i], b = l_sel[ixj];
-                    const bool up = (i & k) == 0;
-                    if ((a > b) == up) { l_sel[i] = b; l_sel[ixj] = a; }
-                }
+    // Candidate slot s = chunk * select_k + i; slots past a chunk's count are absent
+    // (key 0).  Slots are in ascending pool-id order, so among equal keys the
+    // first ones in slot order have the lowest ids: the 32-bit key alone plus
+    // the in-order tie step reproduces the rule.
+    const int used = (n + kChunkKeys - 1) / kChunkKeys;      // chunks stage A wrote for this row
+    const uint64_t* cr = cand + (int64_t)t * nchunks * select_k;
+    const int M = used * select_k;
+    const int s0 = tid * KPT;
+    uint32_t key[KPT];
+    int32_t id[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int s = s0 + j;
+        key[j] = 0u;
+        id[j] = 0;
+        if (s < M) {
+            const int ch = s / select_k;
+            if (s - ch * select_k < cand_n[t * nchunks + ch]) {
+                const uint64_t v = cr[s];
+                key[j] = (uint32_t)(v >> 32);
+                id[j] = (int32_t)(0xFFFFFFFFu - (uint32_t)v);
             }
-            __syncthreads();
         }
     }
-    for (int i = tid; i < select_k; i += kLongNT) out[i] = l_sel[i];
-    if (tid == 0) {
-        hdr->n_sure = 0u;
-        hdr->n_cand = 0u;
-        hdr->filt_done = 0u;
+    uint32_t lo, hi, krem;
+    bool whole;
+    bucket_select<kBNT, KPT, uint32_t>(key, (uint32_t)select_k, S, mm_sh, lo, hi, krem, whole);
+    uint32_t take;
+    uint32_t pos = compaction_slot<kBNT, KPT, uint32_t>(key, lo, hi, krem, whole, S, take);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const uint32_t k = key[j];
+        const bool inr = k >= lo && k <= hi;
+        const bool pick = k > hi || (inr && take > 0);
+        take -= (inr && take > 0) ? 1u : 0u;
+        if (pick && pos < (uint32_t)kMaxK) sel[pos] = id[j];
+        pos += pick;
     }
+    __syncthreads();
+    emit_selection<kBNT>(sel, select_k, select_k, t, b, f, qp, n_vis, e);
 }
 
 }  // namespace dsa
 
 namespace dsa_host {
 
-static size_t rows_lds_bytes(int32_t stride) { return (size_t)stride * 4; }
-
-static bool use_rows_path(const dsa_dims& d, int32_t stride) {
-    const size_t static_lds = dsa::kRowBins * 4 + 256;
-    return rows_lds_bytes(stride) + static_lds <= device_info().max_lds_per_block ||
-           d.index_topk / d.kpool > dsa::kLongMaxK;
-}
+static int topk_chunks(int32_t stride) { return (int)cdiv(stride, dsa::kChunkKeys); }
 
 static size_t r256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+bool topk_supported(const dsa_dims& d, int32_t stride) {
+    const int sk = d.index_topk / d.kpool;
+    return sk <= dsa::kMaxK && (int64_t)topk_chunks(stride) * sk <= dsa::kMaxCand;
+}
+
 size_t topk_workspace_bytes(const dsa_dims& d, int32_t T, int32_t stride) {
-    if (T <= 0 || stride <= 0 || use_rows_path(d, stride)) return 0;
+    if (T <= 0 || stride <= 0) return 0;
     const size_t sk = (size_t)(d.index_topk / d.kpool);
-    return r256((size_t)T * sizeof(dsa::TopkRowHdr)) + r256((size_t)T * dsa::kLongBins * 4) +
-           r256((size_t)T * sk * 4) + r256((size_t)T * stride * 8);
+    const size_t nc = (size_t)topk_chunks(stride);
+    return r256((size_t)T * nc * sk * 8) + r256((size_t)T * nc * 4);
 }
 
 hipError_t launch_topk(const dsa_dims& d, const float* scores, int32_t stride, const dsa_seqs& seqs,
                        const int32_t* q_seq, const int32_t* q_pos, int32_t T, int32_t* pool_ids,
-                       void* ws, hipStream_t s) {
+                       int32_t* indices, void* ws, hipStream_t s) {
     if (T == 0) return hipSuccess;
     const int sk = d.index_topk / d.kpool;
-    if (use_rows_path(d, stride)) {
-        const size_t lds = rows_lds_bytes(stride);
-        if (lds > 64 * 1024) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(dsa::k_topk_rows),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            if (e != hipSuccess) return e;
-        }
-        hipLaunchKernelGGL(dsa::k_topk_rows, dim3((unsigned)T), dim3(dsa::kRowNT), lds, s, scores,
-                           stride, seqs.first_valid, q_seq, q_pos, sk, pool_ids);
-        return hipGetLastError();
-    }
-    const int groups = (int)cdiv(stride, dsa::kLongChunk);
-    dim3 grid((unsigned)groups, (unsigned)T);
-    hipLaunchKernelGGL(dsa::k_topk_long_hist, grid, dim3(dsa::kLongNT), 0, s, scores, stride,
-                       seqs.first_valid, q_seq, q_pos, sk, (int)T, ws, groups);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(dsa::k_topk_long_filter, grid, dim3(dsa::kLongNT), 0, s, scores, stride,
-                       seqs.first_valid, q_seq, q_pos, sk, (int)T, ws, groups, pool_ids);
+    const int nc = topk_chunks(stride);
+    uint64_t* cand = reinterpret_cast<uint64_t*>(ws);
+    int32_t* cand_n = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + r256((size_t)T * nc * sk * 8));
+    const dsa::Emit e{pool_ids, indices, seqs.row_base, d.out_width};
+    hipLaunchKernelGGL(dsa::k_topk_chunks, dim3((unsigned)nc, (unsigned)T), dim3(dsa::kANT), 0, s, scores,
+                       stride, seqs.first_valid, q_seq, q_pos, sk, nc, cand, cand_n);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int kpt = (int)cdiv((int64_t)nc * sk, dsa::kBNT);
+#define DSA_MERGE(KPT)                                                                                    \
+    hipLaunchKernelGGL((dsa::k_topk_merge<KPT>), dim3((unsigned)T), dim3(dsa::kBNT), 0, s, seqs.first_valid, \
+                       q_seq, q_pos, stride, sk, nc, cand, cand_n, e)
+    if (kpt <= 1) DSA_MERGE(1);
+    else if (kpt <= 2) DSA_MERGE(2);
+    else if (kpt <= 4) DSA_MERGE(4);
+    else if (kpt <= 8) DSA_MERGE(8);
+    else if (kpt <= 16) DSA_MERGE(16);
+    else DSA_MERGE(32);
+#undef DSA_MERGE
     return hipGetLastError();
 }
 

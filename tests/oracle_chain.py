@@ -6,6 +6,8 @@ a GPU result.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+
 import numpy as np
 
 import dsa_synth as syn
@@ -30,27 +32,37 @@ class OracleWorkload:
         if b not in self._pools:
             wl = self.wl
             n = int(wl.seq_len[b])
-            k, g = syn.gen_kgate(wl, b, 0, n)
+            k = np.empty((n, self.d.idx_dim), np.float32)
+            g = np.empty((n, self.d.idx_dim), np.float32)
+            for x0, (kk, gg) in syn.gen_sequence_blocks(syn.gen_kgate, wl, b, 0, n):
+                k[x0:x0 + kk.shape[0]] = kk
+                g[x0:x0 + gg.shape[0]] = gg
             lw, lb = syn.gen_ln(wl)
             self._pools[b] = O.pool_states(k, g, lw, lb, self.d.ln_eps, int(wl.first_valid[b]), n, self.d.kpool)
         return self._pools[b]
 
     def cache_rows(self, rows: np.ndarray) -> np.ndarray:
-        """uint8 [len(rows), row_bytes] INT8 rows (O1) for global cache rows."""
+        """uint8 [len(rows), row_bytes] INT8 rows (O1) for global cache rows.
+
+        Latent rows are generated block by block (each needed block once)."""
         wl = self.wl
         rows = np.asarray(rows, dtype=np.int64)
         out = np.zeros((rows.size, self.d.row_bytes), dtype=np.uint8)
         if rows.size == 0:
             return out
         seq_of = np.searchsorted(wl.row_base, rows, side="right") - 1
+        blk = syn.ROW_BLOCK
         for b in np.unique(seq_of):
             sel = np.nonzero(seq_of == b)[0]
             pos = rows[sel] - int(wl.row_base[b])
-            lo, hi = int(pos.min()), int(pos.max()) + 1
-            if hi - lo <= 4 * sel.size + 4096:
-                lat = syn.gen_latent(wl, int(b), lo, hi)[pos - lo]
-            else:
-                lat = np.concatenate([syn.gen_latent(wl, int(b), int(x), int(x) + 1) for x in pos])
+            lat = np.empty((sel.size, self.d.latent_dim), dtype=np.float32)
+            n_b = int(wl.seq_len[b])
+            ks = [int(k) for k in np.unique(pos // blk)]
+            with cf.ThreadPoolExecutor(max_workers=8) as ex:
+                blocks = ex.map(lambda k: syn.gen_latent(wl, int(b), k * blk, min(n_b, (k + 1) * blk)), ks)
+                for k, block in zip(ks, blocks):
+                    m = (pos // blk) == k
+                    lat[m] = block[pos[m] - k * blk]
             codes, scales = O.quantize_rows(lat)
             out[sel] = O.pack_rows(codes, scales, self.d.row_bytes)
         return out

@@ -1,0 +1,172 @@
+"""Host-only checks of the C ABI (no GPU needed, nothing is launched).
+
+The shared library must load, export every function include/dsa.h declares,
+and reject invalid host-visible arguments with the documented status codes
+before touching the device.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+OK, E_NULL, E_DIMS, E_DTYPE, E_ALIGN, E_WIDTH, E_WS, E_UNSUP, E_HIP, E_SIZE = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    import sparse_attention_store_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from sparse_attention_store_amd import build
+        build.build(verbose=False)
+    m.lib()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_path_calls():
+    names = declared_functions()
+    for want in ["dsa_store_int8", "dsa_index_pools", "dsa_index_scores", "dsa_topk_select",
+                 "dsa_topk_select_expand", "dsa_expand_selection", "dsa_sparse_mla",
+                 "dsa_topk_workspace_bytes", "dsa_sparse_mla_workspace_bytes", "dsa_status_string",
+                 "dsa_abi_version"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(dsa):
+    L = dsa.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", dsa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (dsa_[a-z0-9_]+)\b", out))
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert name in exported, name
+
+
+def test_version_and_status_strings(dsa):
+    assert dsa.abi_version() == 1
+    for code in (OK, E_NULL, E_DIMS, E_DTYPE, E_ALIGN, E_WIDTH, E_WS, E_UNSUP, E_HIP, E_SIZE):
+        assert dsa.status_string(code) and dsa.status_string(code) != "unknown status"
+    assert dsa.status_string(-123) == "unknown status"
+
+
+def prod(dsa, **kw):
+    v = dict(idx_heads=32, idx_dim=128, kpool=4, index_topk=2048, out_width=2176, mla_heads=16,
+             latent_dim=512, row_bytes=528, ln_eps=1e-5)
+    v.update(kw)
+    return dsa.Dims(*[v[k] for k in ["idx_heads", "idx_dim", "kpool", "index_topk", "out_width", "mla_heads",
+                                     "latent_dim", "row_bytes", "ln_eps"]])
+
+
+FAKE = ctypes.c_void_p(0x10000)        # never dereferenced: every case below fails validation first
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def seqs(dsa, ptr=FAKE):
+    return dsa._Seqs(ptr, ptr, ptr, ptr)
+
+
+def test_dims_validation(dsa):
+    L = dsa.lib()
+    store = lambda d: L.dsa_store_int8(ctypes.byref(d) if d is not None else None, FAKE, 1, 1, 512, FAKE, FAKE, 1, None)
+    assert L.dsa_store_int8(None, FAKE, 1, 1, 512, FAKE, FAKE, 1, None) == E_NULL
+    assert store(prod(dsa, idx_heads=0)) == E_DIMS
+    assert store(prod(dsa, index_topk=2047)) == E_DIMS                 # not a multiple of kpool
+    assert store(prod(dsa, row_bytes=520)) == E_DIMS                   # must be round_up(D + 4, 16)
+    assert store(prod(dsa, out_width=2050)) == E_WIDTH                 # < index_topk + kpool - 1
+    assert store(prod(dsa, ln_eps=-1.0)) == E_DIMS
+
+
+def test_store_int8_argument_checks(dsa):
+    L = dsa.lib()
+    d = prod(dsa)
+    bd = ctypes.byref(d)
+    assert L.dsa_store_int8(bd, FAKE, 7, 1, 512, FAKE, FAKE, 1, None) == E_DTYPE
+    assert L.dsa_store_int8(bd, FAKE, 1, -1, 512, FAKE, FAKE, 1, None) == E_SIZE
+    assert L.dsa_store_int8(bd, FAKE, 1, 0, 512, None, None, 0, None) == OK       # nothing to do
+    assert L.dsa_store_int8(bd, None, 1, 4, 512, FAKE, FAKE, 4, None) == E_NULL
+    assert L.dsa_store_int8(bd, FAKE, 1, 4, 500, FAKE, FAKE, 4, None) == E_SIZE  # ld < D
+    assert L.dsa_store_int8(bd, MISALIGNED, 1, 4, 512, FAKE, FAKE, 4, None) == E_ALIGN
+    assert L.dsa_store_int8(bd, FAKE, 1, 4, 516, FAKE, FAKE, 4, None) == E_ALIGN  # row pitch not 16 B
+    d2 = prod(dsa, latent_dim=320, row_bytes=336)
+    assert L.dsa_store_int8(ctypes.byref(d2), FAKE, 1, 4, 320, FAKE, FAKE, 4, None) == E_UNSUP
+
+
+def test_pools_scores_expand_argument_checks(dsa):
+    L = dsa.lib()
+    d = prod(dsa)
+    bd = ctypes.byref(d)
+    s = seqs(dsa)
+    assert L.dsa_index_pools(bd, FAKE, FAKE, 9, FAKE, FAKE, ctypes.byref(s), 1, FAKE, FAKE, 1, FAKE, None) == E_DTYPE
+    d3 = prod(dsa, idx_dim=64)
+    assert L.dsa_index_pools(ctypes.byref(d3), FAKE, FAKE, 1, FAKE, FAKE, ctypes.byref(s), 1, FAKE, FAKE, 1, FAKE,
+                             None) == E_UNSUP
+    assert L.dsa_index_pools(bd, FAKE, FAKE, 1, FAKE, FAKE, None, 1, FAKE, FAKE, 1, FAKE, None) == E_NULL
+    assert L.dsa_index_pools(bd, FAKE, FAKE, 1, FAKE, FAKE, ctypes.byref(s), 0, FAKE, FAKE, 1, FAKE, None) == E_SIZE
+    assert L.dsa_index_pools(bd, None, FAKE, 1, FAKE, FAKE, ctypes.byref(s), 1, FAKE, FAKE, 1, FAKE, None) == E_NULL
+    assert L.dsa_index_pools(bd, FAKE, FAKE, 1, FAKE, FAKE, ctypes.byref(s), 1, FAKE, FAKE, 0, FAKE, None) == OK
+    assert L.dsa_index_scores(bd, FAKE, FAKE, FAKE, ctypes.byref(s), 1, FAKE, FAKE, -1, 256, FAKE, None) == E_SIZE
+    assert L.dsa_index_scores(bd, None, FAKE, FAKE, ctypes.byref(s), 1, FAKE, FAKE, 4, 256, FAKE, None) == E_NULL
+    assert L.dsa_index_scores(bd, MISALIGNED, FAKE, FAKE, ctypes.byref(s), 1, FAKE, FAKE, 4, 256, FAKE,
+                              None) == E_ALIGN
+    assert L.dsa_index_scores(bd, FAKE, FAKE, FAKE, ctypes.byref(s), 1, FAKE, FAKE, 0, 256, FAKE, None) == OK
+    assert L.dsa_expand_selection(bd, None, ctypes.byref(s), 1, FAKE, FAKE, 4, FAKE, None) == E_NULL
+    sn = dsa._Seqs(FAKE, None, FAKE, FAKE)
+    assert L.dsa_expand_selection(bd, FAKE, ctypes.byref(sn), 1, FAKE, FAKE, 4, FAKE, None) == E_NULL
+
+
+def test_topk_argument_checks_and_workspace(dsa):
+    L = dsa.lib()
+    d = prod(dsa)
+    bd = ctypes.byref(d)
+    s = seqs(dsa)
+    need = L.dsa_topk_workspace_bytes(bd, 8, 65536)
+    assert need > 0 and L.dsa_topk_workspace_bytes(bd, 8, 65536 * 2) > need
+    assert L.dsa_topk_select(bd, FAKE, 65536, ctypes.byref(s), 1, FAKE, FAKE, 8, FAKE, FAKE, need - 1,
+                             None) == E_WS
+    assert L.dsa_topk_select(bd, FAKE, 65536, ctypes.byref(s), 1, FAKE, FAKE, 8, FAKE, None, need, None) == E_WS
+    assert L.dsa_topk_select(bd, FAKE, 65536, ctypes.byref(s), 1, FAKE, FAKE, 8, FAKE, MISALIGNED, need,
+                             None) == E_ALIGN
+    assert L.dsa_topk_select(bd, FAKE, 65536, ctypes.byref(s), 1, FAKE, FAKE, 8, None, FAKE, need, None) == E_NULL
+    assert L.dsa_topk_select(bd, FAKE, 300000, ctypes.byref(s), 1, FAKE, FAKE, 8, FAKE, FAKE, 1 << 30,
+                             None) == E_UNSUP                               # past the 262,144-pool limit
+    assert L.dsa_topk_select_expand(bd, FAKE, 65536, ctypes.byref(s), 1, FAKE, FAKE, 8, None, None, FAKE, need,
+                                    None) == E_NULL
+    assert L.dsa_topk_select(bd, FAKE, 65536, ctypes.byref(s), 1, FAKE, FAKE, 0, FAKE, None, 0, None) == OK
+
+
+def test_sparse_mla_argument_checks_and_workspace(dsa):
+    L = dsa.lib()
+    d = prod(dsa)
+    bd = ctypes.byref(d)
+    assert L.dsa_sparse_mla_workspace_bytes(bd, 8, 1) == 0                   # one split: no partials
+    need = L.dsa_sparse_mla_workspace_bytes(bd, 8, 5)
+    assert need == 8 * 5 * 16 * (512 * 4 + 8)
+    assert L.dsa_sparse_mla(bd, FAKE, 5, FAKE, 10, FAKE, 8, 0.04, FAKE, 0, None, 0, FAKE, 1 << 30, None) == E_DTYPE
+    assert L.dsa_sparse_mla(bd, FAKE, 1, FAKE, 10, FAKE, 8, 0.04, FAKE, 3, None, 0, FAKE, 1 << 30, None) == E_DTYPE
+    assert L.dsa_sparse_mla(bd, FAKE, 1, FAKE, 10, FAKE, -1, 0.04, FAKE, 0, None, 0, FAKE, 1 << 30, None) == E_SIZE
+    assert L.dsa_sparse_mla(bd, None, 1, FAKE, 10, FAKE, 8, 0.04, FAKE, 0, None, 0, FAKE, 1 << 30, None) == E_NULL
+    assert L.dsa_sparse_mla(bd, MISALIGNED, 1, FAKE, 10, FAKE, 8, 0.04, FAKE, 0, None, 0, FAKE, 1 << 30,
+                            None) == E_ALIGN
+    assert L.dsa_sparse_mla(bd, FAKE, 1, FAKE, 10, FAKE, 8, 0.04, FAKE, 0, None, 5, FAKE, need - 1,
+                            None) == E_WS
+    assert L.dsa_sparse_mla(bd, FAKE, 1, FAKE, 10, FAKE, 70000, 0.04, FAKE, 0, None, 1, None, 0, None) == E_SIZE
+    d4 = prod(dsa, latent_dim=2048, row_bytes=2064)
+    assert L.dsa_sparse_mla(ctypes.byref(d4), FAKE, 1, FAKE, 10, FAKE, 8, 0.04, FAKE, 0, None, 1, None, 0,
+                            None) == E_UNSUP
+
+
+def test_binding_refuses_host_tensors(dsa):
+    import torch
+    d = prod(dsa)
+    with pytest.raises((TypeError, ValueError)):
+        dsa.store_int8(d, torch.zeros(2, 512, dtype=torch.bfloat16), torch.zeros(2, dtype=torch.int64),
+                       torch.zeros(2, 528, dtype=torch.int8))

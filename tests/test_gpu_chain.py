@@ -52,6 +52,7 @@ def _check_chain(dw, queries, pool_sample=64, allow_swaps_frac=0.05):
     g = np.random.default_rng(17)
     for t in queries:
         b = int(wl.q_seq[t])
+        say(f"  oracle query {int(t)} (sequence {b}, position {int(wl.q_pos[t])})")
         r = ow.query(int(t), dw.stride)
         n_vis = r["n_vis"]
         # pools of this sequence (a sample at full size)

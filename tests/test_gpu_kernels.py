@@ -206,44 +206,57 @@ def _topk_case(dsa, T, stride, n_vis, kind, seed, select_k=512):
     dims = dsa.Dims.of(d)
     sc = syn.gen_score_rows(seed, T, stride, n_vis, kind)
     fv = np.zeros(T, dtype=np.int32)
-    seqs = dsa.Seqs(torch.from_numpy(fv).cuda(), torch.zeros(T, dtype=torch.int64, device="cuda"),
+    rb = (np.arange(T, dtype=np.int64) * 1000003)
+    seqs = dsa.Seqs(torch.from_numpy(fv).cuda(), torch.from_numpy(rb).cuda(),
                     torch.zeros(T, dtype=torch.int64, device="cuda"), torch.zeros(T, dtype=torch.int64, device="cuda"))
     q_seq = torch.arange(T, dtype=torch.int32, device="cuda")
-    q_pos = torch.from_numpy((np.asarray(n_vis) * 4 + 2).astype(np.int32)).cuda()   # n_vis pools + tail 3
+    qpos_h = (np.asarray(n_vis) * 4 + (np.arange(T) % 4) - 1).astype(np.int32)   # n_vis pools + tail 0..3
+    q_pos = torch.from_numpy(qpos_h).cuda()
     ws = dsa.topk_workspace(dims, T, stride)
+    scd = torch.from_numpy(sc).cuda()
     out = torch.full((T, select_k), 77777, dtype=torch.int32, device="cuda")
-    dsa.topk_select(dims, torch.from_numpy(sc).cuda(), seqs, q_seq, q_pos, out, ws)
+    dsa.topk_select(dims, scd, seqs, q_seq, q_pos, out, ws)
     got1 = out.cpu().numpy()
     out.fill_(-5)
-    dsa.topk_select(dims, torch.from_numpy(sc).cuda(), seqs, q_seq, q_pos, out, ws)
+    idx = torch.full((T, d.out_width), 0x7F7F7F7F, dtype=torch.int32, device="cuda")
+    dsa.topk_select_expand(dims, scd, seqs, q_seq, q_pos, idx, out, ws)      # workspace reused without clearing
     got2 = out.cpu().numpy()
-    assert np.array_equal(got1, got2)                        # workspace reused without clearing
+    gidx = idx.cpu().numpy()
+    assert np.array_equal(got1, got2)
     for t in range(T):
+        assert O.visible_pool_count(int(qpos_h[t]), 0, 4) == int(n_vis[t])
         ref = O.topk_pools(sc[t].astype(np.float64), int(n_vis[t]), select_k)
         assert np.array_equal(got1[t], ref), (kind, t, int(n_vis[t]))
+        ref_idx = O.expand_selection(ref, 0, int(qpos_h[t]), int(rb[t]), d.kpool, d.out_width)
+        assert np.array_equal(gidx[t], ref_idx), (kind, t)
     return ws is not None
 
 
 @pytest.mark.parametrize("kind", ["ties", "normal", "equal", "signed_zero"])
-def test_topk_rows_path(dsa, kind):
-    n_vis = np.array([0, 1, 300, 511, 512, 513, 600, 2000, 8192, 20000, 33792, 33000], dtype=np.int64)
-    say(f"topk rows {kind}")
-    used_ws = _topk_case(dsa, len(n_vis), 33792, n_vis, kind, seed=21)
-    assert not used_ws
+def test_topk_rows_up_to_65536(dsa, kind):
+    n_vis = np.array([0, 1, 300, 511, 512, 513, 600, 2000, 8192, 20000, 33792, 65535, 65536, 63639],
+                     dtype=np.int64)
+    say(f"topk row {kind}")
+    _topk_case(dsa, len(n_vis), 65536, n_vis, kind, seed=21)
 
 
 @pytest.mark.parametrize("kind", ["ties", "normal", "equal", "signed_zero"])
-def test_topk_long_path(dsa, kind):
-    n_vis = np.array([0, 512, 513, 4097, 65536, 40000, 65535, 12345], dtype=np.int64)
+def test_topk_rows_past_65536(dsa, kind):
+    n_vis = np.array([0, 512, 513, 4097, 65536, 40000, 70000, 69999, 12345], dtype=np.int64)
     say(f"topk long {kind}")
-    used_ws = _topk_case(dsa, len(n_vis), 65536, n_vis, kind, seed=22)
-    assert used_ws
+    _topk_case(dsa, len(n_vis), 70000, n_vis, kind, seed=22)
 
 
-def test_topk_long_path_1m_rows(dsa):
+def test_topk_rows_of_262144(dsa):
     n_vis = np.array([262144, 262143, 384, 1], dtype=np.int64)
     say("topk long 262144")
-    assert _topk_case(dsa, 4, 262144, n_vis, "ties", seed=23)
+    _topk_case(dsa, 4, 262144, n_vis, "ties", seed=23)
+
+
+def test_topk_odd_stride_scalar_loads(dsa):
+    n_vis = np.array([1001, 999, 3], dtype=np.int64)
+    say("topk odd stride")
+    _topk_case(dsa, 3, 1001, n_vis, "normal", seed=24)
 
 
 # ---------------------------------------------------------------- expand_selection
