@@ -72,13 +72,25 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// ---------------------------------------------------------------- barriers
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also fences global
+// memory, which makes the compiler drain every outstanding global load before
+// the barrier and so defeats register prefetching; none of these kernels
+// exchange global memory between the waves of a workgroup.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------- block scans
 
 // Exclusive prefix sum of one uint32 per thread over a block of NT threads.
 // `sh` must hold NT / 64 + 1 entries.  Returns the exclusive prefix; *total
 // receives the block total.  Wave totals go through LDS once; every thread then
 // adds the totals of the waves before its own (no serial step).  Contains two
-// __syncthreads().
+// LDS barriers.
 template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* sh, uint32_t* total) {
     constexpr int NW = NT / 64;
@@ -90,7 +102,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
         if (lane >= o) x += y;
     }
     if (lane == 63) sh[wave] = x;
-    __syncthreads();
+    lds_barrier();
     uint32_t before = 0, all = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -99,7 +111,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
         all += tw;
     }
     *total = all;
-    __syncthreads();
+    lds_barrier();
     return before + x - v;
 }
 

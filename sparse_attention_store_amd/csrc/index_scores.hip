@@ -66,7 +66,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scores_mfma(
 
     prefetch(t_begin);
     for (int tb = t_begin; tb < t_end; tb += QB) {
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int i = 0; i < PER_T; ++i) {
             const int c = tid + i * NT;
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scores_mfma(
             }
         }
         if (tid < QB * kHI) w_lds[tid / kHI][tid % kHI] = pre_w;
-        __syncthreads();
+        lds_barrier();
         if (tb + QB < t_end) prefetch(tb + QB);
 
         const int nq = min(QB, t_end - tb);
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256) void k_scores_decode(
         if (tid < T) s_first[tid] = x - nt;
         if (tid == 63) s_first[kDecMaxT] = x;
     }
-    __syncthreads();
+    lds_barrier();
     const int total = s_first[kDecMaxT];
 
     auto locate = [&](int i, int& t, int& p0) {
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(256) void k_scores_decode(
         for (int j = 0; j < 8; ++j) areg[j] = anext[j];
 #pragma unroll
         for (int k = 0; k < 4; ++k) wv[k] = wnext[k];
-        __syncthreads();                                     // previous tile's LDS readers are done
+        lds_barrier();                                     // previous tile's LDS readers are done
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             const int id = tid + k * 256;
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(256) void k_scores_decode(
             tile[row * 16 + ((id & 15) ^ (row & 15))] = v[k];
         }
         if (i + (int)gridDim.x < total) prefetch(i + gridDim.x);
-        __syncthreads();
+        lds_barrier();
         float sc[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {

@@ -34,6 +34,7 @@ constexpr int kD = 512;
 constexpr int kChunk = 64;
 constexpr int kKVRow = kD + 8;       // bf16 elements per LDS row (1040 B)
 constexpr int kPRow = kChunk + 8;    // bf16 elements per P' row (144 B)
+constexpr int kMaxSplitRows = 2176;  // index entries one split may cover (staged in LDS)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -68,6 +69,8 @@ __global__ __launch_bounds__(256) void k_mla_mfma(
     __shared__ int rvalid[kChunk];
     __shared__ float red_max[4][16];
     __shared__ float red_sum[4][16];
+    __shared__ int chunk_any[4];
+    __shared__ int idx_lds[kMaxSplitRows];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int split = blockIdx.x, hg = blockIdx.y, t = blockIdx.z;
@@ -97,15 +100,17 @@ __global__ __launch_bounds__(256) void k_mla_mfma(
     const int c_end = min(c_begin + chunks_per_split, nchunks);
     const int32_t* idx_row = indices + (int64_t)t * W;
 
-    // Row gather: thread -> (row tid/4, 128-byte segment tid%4).  Index-list
-    // entries are loaded one chunk ahead of the rows, and the rows of chunk
-    // c+1 are requested before chunk c computes, so the dependent
-    // list -> row latency is paid once per split.
+    // Row gather: thread -> (row tid/4, 128-byte segment tid%4).  The split's
+    // slice of the index list is staged in LDS once, so the loop issues the
+    // rows of chunk c+1 before chunk c computes without any dependent global
+    // load (or register copy of one) in between.
     const int r = tid >> 2, sg = tid & 3;
-    auto load_idx = [&](int c) {
-        const int pos = c * kChunk + r;
-        return (c < c_end && pos < W) ? idx_row[pos] : -1;
-    };
+    const int split_rows = (c_end - c_begin) * kChunk;
+    for (int i = tid; i < split_rows; i += 256) {
+        const int pos = c_begin * kChunk + i;
+        idx_lds[i] = pos < W ? idx_row[pos] : -1;
+    }
+    lds_barrier();
     u32x4 raw[8];
     float rsc = 0.f;
     auto load_rows = [&](int idx) {
@@ -120,13 +125,12 @@ __global__ __launch_bounds__(256) void k_mla_mfma(
             rsc = 0.f;
         }
     };
-    int idx_cur = load_idx(c_begin);
-    int idx_nxt = load_idx(c_begin + 1);
-    if (c_begin < c_end) load_rows(idx_cur);
+    if (c_begin < c_end) load_rows(idx_lds[r]);
 
     for (int c = c_begin; c < c_end; ++c) {
         // ---- 1. dequant the gathered rows to bf16 in LDS, then request the next chunk
-        __syncthreads();                                   // previous chunk's readers are done
+        lds_barrier();                                   // previous chunk's readers are done
+        const int idx_cur = idx_lds[(c - c_begin) * kChunk + r];
         if (sg == 0) { rs[r] = rsc; rvalid[r] = idx_cur >= 0; }
         const bool have = idx_cur >= 0;
         {
@@ -144,12 +148,11 @@ __global__ __launch_bounds__(256) void k_mla_mfma(
                 *reinterpret_cast<u32x4*>(dst + 16 * i + 8) = o1;
             }
         }
-        if (c + 1 < c_end) {
-            load_rows(idx_nxt);
-            idx_cur = idx_nxt;
-            idx_nxt = load_idx(c + 2);
-        }
-        if (!__syncthreads_or(have)) continue;             // empty chunk
+        if (c + 1 < c_end) load_rows(idx_lds[(c + 1 - c_begin) * kChunk + r]);
+        const unsigned long long vote = __ballot(have);
+        if ((tid & 63) == 0) chunk_any[wave] = vote != 0ull;
+        lds_barrier();
+        if (!(chunk_any[0] | chunk_any[1] | chunk_any[2] | chunk_any[3])) continue;   // empty chunk
 
         // ---- 2. S for this wave's head tile and row tiles sub*HT .. sub*HT+HT-1
         f32x4 sacc[HT];
@@ -184,7 +187,7 @@ __global__ __launch_bounds__(256) void k_mla_mfma(
         if (n16 == 0)
 #pragma unroll
             for (int i = 0; i < 4; ++i) red_max[wave][4 * g4 + i] = cmax[i];
-        __syncthreads();
+        lds_barrier();
         float m_new[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -216,7 +219,7 @@ __global__ __launch_bounds__(256) void k_mla_mfma(
         if (n16 == 0)
 #pragma unroll
             for (int i = 0; i < 4; ++i) red_sum[wave][4 * g4 + i] = psum[i];
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float ls = 0.f;
@@ -327,7 +330,7 @@ __global__ __launch_bounds__(128) void k_mla_combine(
         wgt[tid] = w;
         if (tid == 0) { s_M = M; s_L = L; }
     }
-    __syncthreads();
+    lds_barrier();
     const float L = s_L;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const float* base = part_o + ((int64_t)t * splits * H + h) * kD + tid * 4;
@@ -443,6 +446,8 @@ MlaPlan plan_sparse_mla(const dsa_dims& d, int32_t T, int32_t num_splits, int q_
         want = base >= cu ? 1 : (int)std::min<int64_t>(nchunks, cdiv(cu, base));
     }
     if (want > dsa::kMaxSplits) want = dsa::kMaxSplits;
+    const int min_splits = (int)cdiv(nchunks, dsa::kMaxSplitRows / dsa::kChunk);
+    if (want < min_splits) want = min_splits;
     p.chunks_per_split = (int)cdiv(nchunks, want);
     p.splits = (int)cdiv(nchunks, p.chunks_per_split);
     p.ws_bytes = p.splits > 1

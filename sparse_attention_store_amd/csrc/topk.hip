@@ -108,14 +108,14 @@ __device__ __forceinline__ void block_min_max(const KT (&key)[KPT], KT* sh, KT& 
     }
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) { sh[2 * w] = mn; sh[2 * w + 1] = mx; }
-    __syncthreads();
+    lds_barrier();
     kmin = sh[0];
     kmax = sh[1];
     for (int i = 1; i < NT / 64; ++i) {
         kmin = sh[2 * i] < kmin ? sh[2 * i] : kmin;
         kmax = sh[2 * i + 1] > kmax ? sh[2 * i + 1] : kmax;
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // One bucket per thread: NT buckets per pass, double-buffered so the next
@@ -153,7 +153,7 @@ __device__ __forceinline__ void bucket_select(const KT (&key)[KPT], uint32_t tar
             const KT k = key[j];
             if (k >= lo && k <= hi) atomicAdd(&S.hist[buf][(uint32_t)((k - lo) >> sh)], 1u);
         }
-        __syncthreads();
+        lds_barrier();
         const uint32_t h = S.hist[buf][NT - 1 - tid];         // thread order = descending buckets
         S.hist[buf ^ 1][tid] = 0u;                            // read two passes ago; free now
         uint32_t total;
@@ -163,7 +163,7 @@ __device__ __forceinline__ void bucket_select(const KT (&key)[KPT], uint32_t tar
             S.above[buf] = above;
             S.cnt[buf] = h;
         }
-        __syncthreads();
+        lds_barrier();
         krem -= S.above[buf];
         const KT nlo = lo + ((KT)S.bin[buf] << sh);
         const KT nhi = nlo + (((KT)1 << sh) - 1);
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(kBNT) void k_topk_merge(
         if (pick && pos < (uint32_t)kMaxK) sel[pos] = id[j];
         pos += pick;
     }
-    __syncthreads();
+    lds_barrier();
     emit_selection<kBNT>(sel, select_k, select_k, t, b, f, qp, n_vis, e);
 }
 
