@@ -158,8 +158,8 @@ int dsa_index_scores(const dsa_dims* dims, const uint16_t* q_idx, const float* w
  * (score descending, pool id ascending; -0 equals +0), and write their ids
  * in ascending order to pool_ids[t][0..K), then -1 up to select_k.  When
  * n_vis <= select_k every visible pool is selected.  NaN scores are outside
- * the contract.  Supported: kpool 4, select_k <= 1024 and
- * ceil(score_stride / 4096) * select_k <= 32768 (262,144 pools at select_k 512).
+ * the contract.  Supported: kpool 4, select_k <= 1024 and score_stride <=
+ * 262,144 pools.
  *   scores    device fp32 [T, score_stride] (as written by dsa_index_scores)
  *   pool_ids  device int32 [T, select_k]
  *   workspace device scratch, >= dsa_topk_workspace_bytes(dims, T,

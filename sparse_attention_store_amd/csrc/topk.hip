@@ -4,35 +4,52 @@
 // indexer_topk512).  Optionally the same launches also write the expanded
 // index list ([Ref] Functions: expand_selection).
 //
-// Two stages, no cross-workgroup atomics and no state kept between calls:
-//  A. Each query row is cut into chunks of 4096 pools.  One 256-thread
-//     workgroup per chunk selects the chunk's best min(select_k, chunk) pools
-//     under the same order and writes them, in ascending id order, as 64-bit
-//     composites (key << 32 | ~id), where key is the order-preserving uint32
-//     image of the fp32 score (-0 mapped to +0).  Every member of the row's
-//     top-K is in its chunk's top-K under this total order, so the union of
-//     the chunk lists contains the answer.
-//  B. One 1024-thread workgroup per row selects the best K of that union (at
-//     most 64 chunks x select_k, held in registers).  The chunk lists are in
-//     ascending id order, so the same 32-bit key selection with ties taken in
-//     list order applies the tie rule, and a scan-based compaction emits the
-//     ids sorted.
-// Both stages find the K-th largest key by range bucketing in LDS: each pass
+// The order is total on the 64-bit composite (key << 32 | ~id), key being the
+// order-preserving uint32 image of the fp32 score (-0 mapped to +0).
+//  A. Tiles of 256 pools: one workgroup per tile sorts the tile's composites
+//     (bitonic, in registers and LDS) and keeps its best m, m sized from the
+//     row's tile count so that m is at least 2.5 times a tile's mean share of
+//     the K (>= 16, a power of two).  The kept ones are written in ascending
+//     id order, with a flag saying whether the tile had more pools than m.
+//  B. One 1024-thread workgroup per row selects the best K of the union of
+//     the tile lists (held in registers; the lists are in ascending id order,
+//     so the 32-bit key selection with ties taken in list order applies the
+//     tie rule).  The union holds the answer unless some tile that dropped
+//     pools had all m of its kept ones selected -- then a dropped one might
+//     belong too.  The workgroup checks exactly that and, if it happens,
+//     selects again from the row's scores with an exact streaming radix
+//     select, so the result never depends on the score distribution.
+// The K-th largest key is found by range bucketing in LDS: each pass
 // histograms the keys inside [lo, hi] into one bucket per thread, of width
 // 2^sh (the key offset shifted right), keeps the bucket that holds rank K and
-// narrows [lo, hi] to it, until that bucket is taken whole or (stage A) one key
-// value is left, whose first `need` occurrences in id order are taken -- the
-// tie rule.
+// narrows [lo, hi] to it, until that bucket is taken whole or one key value is
+// left, whose first `need` occurrences in id order are taken.
 #include "dsa_common.h"
 #include "dsa_launch.h"
 
 namespace dsa {
 
-constexpr int kChunkKeys = 4096;            // pools per stage-A workgroup
-constexpr int kANT = 256, kAKPT = kChunkKeys / kANT;
+constexpr int kTile = 256;                  // pools per stage-A workgroup
 constexpr int kBNT = 1024;
 constexpr int kMaxK = 1024;                 // select_k limit
-constexpr int kMaxCand = 32 * kBNT;         // stage-B capacity (chunks x select_k)
+constexpr int kMaxTiles = 1024;             // 262,144 pools per row
+constexpr int kMaxCand = 32 * kBNT;         // stage-B capacity
+constexpr int kIncomplete = 1 << 30;        // tile count flag: the tile dropped pools
+
+// Kept per tile for a row of `ntiles` tiles.
+__host__ __device__ inline int tile_quota(int select_k, int ntiles) {
+    const int want = (5 * select_k + 2 * ntiles - 1) / (2 * ntiles);
+    int m = 16;
+    while (m < want && m < kTile) m <<= 1;
+    return m;
+}
+
+// Candidate slots per row: ntiles * tile_quota(ntiles) <= 16 ntiles + 5 K + 256
+// for every ntiles (m = 16; or m < 2 ceil(2.5 K / ntiles); or m = 256 only
+// when ntiles < 5 K / 256).
+__host__ __device__ inline int64_t cand_row_cap(int select_k, int ntiles_max) {
+    return 16LL * ntiles_max + 5LL * select_k + 256;
+}
 
 struct Emit {
     int32_t* pool_ids;        // [T, select_k] or null
@@ -197,70 +214,125 @@ __device__ __forceinline__ uint32_t compaction_slot(const KT (&key)[KPT], KT lo,
 
 // ---------------------------------------------------------------- stage A
 
-__global__ __launch_bounds__(kANT) void k_topk_chunks(
+__global__ __launch_bounds__(kTile) void k_topk_tiles(
     const float* __restrict__ scores, int stride, const int32_t* __restrict__ first_valid,
-    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int select_k, int nchunks,
-    uint64_t* __restrict__ cand, int32_t* __restrict__ cand_n) {
-    __shared__ SelShared<kANT> S;
-    __shared__ uint32_t mm_sh[2 * kANT / 64];
+    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int select_k, int64_t cap,
+    int ntiles_max, uint64_t* __restrict__ cand, int32_t* __restrict__ cand_n) {
+    __shared__ uint64_t xs[2][kTile];
+    __shared__ uint32_t wcount[kTile / 64];
+    __shared__ uint64_t theta_sh;
     const int c = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
     int b, f, qp, n_vis;
     query_geom(first_valid, q_seq, q_pos, t, b, f, qp, n_vis);
     const int n = min(n_vis, stride);
     if (n <= select_k) return;                               // stage B selects every pool
-    const int c0 = c * kChunkKeys;
-    const int cn = max(0, min(n - c0, kChunkKeys));          // keys in this chunk
-    uint64_t* out = cand + ((int64_t)t * nchunks + c) * select_k;
-    const float* row = scores + (int64_t)t * stride + c0;
-    if (cn <= select_k) {                                    // the whole chunk is a candidate set
-        for (int i = tid; i < cn; i += kANT)
-            out[i] = ((uint64_t)f32_key(row[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(c0 + i));
-        if (tid == 0) cand_n[t * nchunks + c] = cn;
-        return;
+    const int ntiles = (n + kTile - 1) / kTile;
+    if (c >= ntiles) return;
+    const int m = tile_quota(select_k, ntiles);
+    const int id = c * kTile + tid;
+    const bool valid = id < n;
+    const uint64_t comp = valid ? ((uint64_t)f32_key(scores[(int64_t)t * stride + id]) << 32) |
+                                      (uint64_t)(0xFFFFFFFFu - (uint32_t)id)
+                                : 0ull;
+    const int nvalid = min(n - c * kTile, kTile);
+    uint64_t theta = 1ull;                                   // keep composites >= theta
+    if (nvalid > m) {
+        // Bitonic sort, descending; lanes exchange by shuffles, waves through LDS.
+        uint64_t v = comp;
+        int buf = 0;
+#pragma unroll
+        for (int k = 2; k <= kTile; k <<= 1)
+#pragma unroll
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                uint64_t o;
+                if (j < 64) {
+                    o = shfl_xor_k(v, j);
+                } else {
+                    xs[buf][tid] = v;
+                    lds_barrier();
+                    o = xs[buf][tid ^ j];
+                    buf ^= 1;
+                }
+                const bool desc = (tid & k) == 0, lower = (tid & j) == 0;
+                v = (lower == desc) ? (v > o ? v : o) : (v < o ? v : o);
+            }
+        if (tid == m - 1) theta_sh = v;
+        lds_barrier();
+        theta = theta_sh;
     }
-    // Keys [c0 + tid*16, +16); absent keys are 0, below every real key.
-    const int i0 = tid * kAKPT;
-    uint32_t key[kAKPT];
-    const bool vec = ((stride & 3) == 0) && ((reinterpret_cast<uintptr_t>(scores) & 15) == 0);
-    if (vec && i0 + kAKPT <= cn) {
+    const bool pick = comp >= theta;                         // comp 0 (absent) never passes
+    const uint64_t bal = __ballot(pick);
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    const int w = tid >> 6;
+    if ((tid & 63) == 0) wcount[w] = (uint32_t)__popcll(bal);
+    lds_barrier();
+    uint32_t base = 0, total = 0;
 #pragma unroll
-        for (int q = 0; q < kAKPT / 4; ++q) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(row + i0 + 4 * q);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) key[4 * q + e] = f32_key(v[e]);
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < kAKPT; ++j) key[j] = (i0 + j < cn) ? f32_key(row[i0 + j]) : 0u;
+    for (int i = 0; i < kTile / 64; ++i) {
+        base += i < w ? wcount[i] : 0u;
+        total += wcount[i];
     }
-    uint32_t lo, hi, krem;
-    bool whole;
-    bucket_select<kANT, kAKPT, uint32_t>(key, (uint32_t)select_k, S, mm_sh, lo, hi, krem, whole);
-    uint32_t take;
-    uint32_t pos = compaction_slot<kANT, kAKPT, uint32_t>(key, lo, hi, krem, whole, S, take);
-#pragma unroll
-    for (int j = 0; j < kAKPT; ++j) {
-        const uint32_t k = key[j];
-        const bool inr = k >= lo && k <= hi;
-        const bool pick = k > hi || (inr && take > 0);
-        take -= (inr && take > 0) ? 1u : 0u;
-        if (pick && pos < (uint32_t)select_k)
-            out[pos] = ((uint64_t)k << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(c0 + i0 + j));
-        pos += pick;
-    }
-    if (tid == 0) cand_n[t * nchunks + c] = select_k;
+    if (pick) cand[(int64_t)t * cap + (int64_t)c * m + base + below] = comp;
+    if (tid == 0) cand_n[(int64_t)t * ntiles_max + c] = (int32_t)total | (nvalid > m ? kIncomplete : 0);
 }
 
 // ---------------------------------------------------------------- stage B
 
+// Exact selection straight from the row's scores (used when the tile lists
+// cannot prove they hold the answer): MSB-first radix select, 8 bits a pass,
+// then one ordered pass that takes every key above the K-th and the first
+// `need` keys equal to it.  Writes K ids, ascending, to sel.
+__device__ void topk_stream_exact(const float* __restrict__ row, int n, int K, SelShared<kBNT>& S,
+                                  int32_t* sel) {
+    const int tid = threadIdx.x;
+    uint32_t prefix = 0u, mask = 0u, need = (uint32_t)K, total;
+    for (int d = 3; d >= 0; --d) {
+        if (tid < 256) S.hist[0][tid] = 0u;
+        lds_barrier();
+        for (int i = tid; i < n; i += kBNT) {
+            const uint32_t k = f32_key(row[i]);
+            if ((k & mask) == prefix) atomicAdd(&S.hist[0][(k >> (8 * d)) & 0xFFu], 1u);
+        }
+        lds_barrier();
+        const uint32_t h = tid < 256 ? S.hist[0][255 - tid] : 0u;    // descending digits
+        const uint32_t above = block_exclusive_scan<kBNT>(h, S.scan, &total);
+        if (tid < 256 && above < need && need <= above + h) {
+            S.bin[0] = 255u - (uint32_t)tid;
+            S.above[0] = above;
+        }
+        lds_barrier();
+        need -= S.above[0];
+        prefix |= S.bin[0] << (8 * d);
+        mask |= 0xFFu << (8 * d);
+        lds_barrier();
+    }
+    uint32_t out_base = 0u, eq_base = 0u;
+    for (int i0 = 0; i0 < n; i0 += kBNT) {
+        const int i = i0 + tid;
+        const uint32_t k = i < n ? f32_key(row[i]) : 0u;
+        const uint32_t gt = (i < n && k > prefix) ? 1u : 0u;
+        const uint32_t eq = (i < n && k == prefix) ? 1u : 0u;
+        uint32_t eq_tot, pick_tot;
+        const uint32_t eq_rank = eq_base + block_exclusive_scan<kBNT>(eq, S.scan, &eq_tot);
+        const uint32_t pick = gt | ((eq && eq_rank < need) ? 1u : 0u);
+        const uint32_t pos = out_base + block_exclusive_scan<kBNT>(pick, S.scan, &pick_tot);
+        if (pick && pos < (uint32_t)kMaxK) sel[pos] = i;
+        out_base += pick_tot;
+        eq_base += eq_tot;
+    }
+}
+
 template <int KPT>
-__global__ __launch_bounds__(kBNT) void k_topk_merge(
-    const int32_t* __restrict__ first_valid, const int32_t* __restrict__ q_seq,
-    const int32_t* __restrict__ q_pos, int stride, int select_k, int nchunks,
-    const uint64_t* __restrict__ cand, const int32_t* __restrict__ cand_n, Emit e) {
+__global__ __launch_bounds__(kBNT) void k_topk_rows(
+    const float* __restrict__ scores, const int32_t* __restrict__ first_valid,
+    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int stride, int select_k,
+    int64_t cap, int ntiles_max, const uint64_t* __restrict__ cand, const int32_t* __restrict__ cand_n, Emit e) {
     __shared__ SelShared<kBNT> S;
     __shared__ uint32_t mm_sh[2 * kBNT / 64];
     __shared__ int32_t sel[kMaxK];
+    __shared__ uint32_t tpicked[kMaxTiles];
+    __shared__ int fail;
     const int t = blockIdx.x, tid = threadIdx.x;
     int b, f, qp, n_vis;
     query_geom(first_valid, q_seq, q_pos, t, b, f, qp, n_vis);
@@ -269,13 +341,14 @@ __global__ __launch_bounds__(kBNT) void k_topk_merge(
         emit_selection<kBNT>(nullptr, n, select_k, t, b, f, qp, n_vis, e);
         return;
     }
-    // Candidate slot s = chunk * select_k + i; slots past a chunk's count are absent
-    // (key 0).  Slots are in ascending pool-id order, so among equal keys the
-    // first ones in slot order have the lowest ids: the 32-bit key alone plus
-    // the in-order tie step reproduces the rule.
-    const int used = (n + kChunkKeys - 1) / kChunkKeys;      // chunks stage A wrote for this row
-    const uint64_t* cr = cand + (int64_t)t * nchunks * select_k;
-    const int M = used * select_k;
+    const int ntiles = (n + kTile - 1) / kTile;
+    const int m = tile_quota(select_k, ntiles);
+    const int msh = __ffs(m) - 1;
+    const int M = ntiles * m;                                // slots: tile c at [c*m, c*m + count_c)
+    const int32_t* cn = cand_n + (int64_t)t * ntiles_max;
+    const uint64_t* cr = cand + (int64_t)t * cap;
+    if (tid < kMaxTiles) tpicked[tid] = 0u;
+    if (tid == 0) fail = 0;
     const int s0 = tid * KPT;
     uint32_t key[KPT];
     int32_t id[KPT];
@@ -284,13 +357,10 @@ __global__ __launch_bounds__(kBNT) void k_topk_merge(
         const int s = s0 + j;
         key[j] = 0u;
         id[j] = 0;
-        if (s < M) {
-            const int ch = s / select_k;
-            if (s - ch * select_k < cand_n[t * nchunks + ch]) {
-                const uint64_t v = cr[s];
-                key[j] = (uint32_t)(v >> 32);
-                id[j] = (int32_t)(0xFFFFFFFFu - (uint32_t)v);
-            }
+        if (s < M && (s & (m - 1)) < (cn[s >> msh] & (kIncomplete - 1))) {
+            const uint64_t v = cr[s];
+            key[j] = (uint32_t)(v >> 32);
+            id[j] = (int32_t)(0xFFFFFFFFu - (uint32_t)v);
         }
     }
     uint32_t lo, hi, krem;
@@ -298,14 +368,31 @@ __global__ __launch_bounds__(kBNT) void k_topk_merge(
     bucket_select<kBNT, KPT, uint32_t>(key, (uint32_t)select_k, S, mm_sh, lo, hi, krem, whole);
     uint32_t take;
     uint32_t pos = compaction_slot<kBNT, KPT, uint32_t>(key, lo, hi, krem, whole, S, take);
+    uint32_t picks = 0u;                                     // bit j: slot s0 + j selected
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
         const uint32_t k = key[j];
         const bool inr = k >= lo && k <= hi;
-        const bool pick = k > hi || (inr && take > 0);
+        const bool pk = k > hi || (inr && take > 0);
         take -= (inr && take > 0) ? 1u : 0u;
-        if (pick && pos < (uint32_t)kMaxK) sel[pos] = id[j];
-        pos += pick;
+        picks |= pk ? (1u << j) : 0u;
+        if (pk) atomicAdd(&tpicked[(s0 + j) >> msh], 1u);
+    }
+    lds_barrier();
+    // A tile that dropped pools and had all m kept ones selected cannot vouch
+    // for the pools it dropped.
+    for (int c = tid; c < ntiles; c += kBNT)
+        if ((cn[c] & kIncomplete) && tpicked[c] == (uint32_t)m) fail = 1;
+    lds_barrier();
+    if (fail) {
+        topk_stream_exact(scores + (int64_t)t * stride, n, select_k, S, sel);
+    } else {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const bool pk = (picks >> j) & 1u;
+            if (pk && pos < (uint32_t)kMaxK) sel[pos] = id[j];
+            pos += pk;
+        }
     }
     lds_barrier();
     emit_selection<kBNT>(sel, select_k, select_k, t, b, f, qp, n_vis, e);
@@ -315,20 +402,21 @@ __global__ __launch_bounds__(kBNT) void k_topk_merge(
 
 namespace dsa_host {
 
-static int topk_chunks(int32_t stride) { return (int)cdiv(stride, dsa::kChunkKeys); }
+static int topk_tiles(int32_t stride) { return (int)cdiv(stride, dsa::kTile); }
 
 static size_t r256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool topk_supported(const dsa_dims& d, int32_t stride) {
     const int sk = d.index_topk / d.kpool;
-    return sk <= dsa::kMaxK && (int64_t)topk_chunks(stride) * sk <= dsa::kMaxCand;
+    return sk <= dsa::kMaxK && topk_tiles(stride) <= dsa::kMaxTiles &&
+           dsa::cand_row_cap(sk, topk_tiles(stride)) <= dsa::kMaxCand;
 }
 
 size_t topk_workspace_bytes(const dsa_dims& d, int32_t T, int32_t stride) {
     if (T <= 0 || stride <= 0) return 0;
-    const size_t sk = (size_t)(d.index_topk / d.kpool);
-    const size_t nc = (size_t)topk_chunks(stride);
-    return r256((size_t)T * nc * sk * 8) + r256((size_t)T * nc * 4);
+    const int sk = d.index_topk / d.kpool;
+    const int nt = topk_tiles(stride);
+    return r256((size_t)T * (size_t)dsa::cand_row_cap(sk, nt) * 8) + r256((size_t)T * nt * 4);
 }
 
 hipError_t launch_topk(const dsa_dims& d, const float* scores, int32_t stride, const dsa_seqs& seqs,
@@ -336,25 +424,27 @@ hipError_t launch_topk(const dsa_dims& d, const float* scores, int32_t stride, c
                        int32_t* indices, void* ws, hipStream_t s) {
     if (T == 0) return hipSuccess;
     const int sk = d.index_topk / d.kpool;
-    const int nc = topk_chunks(stride);
+    const int nt = topk_tiles(stride);
+    const int64_t cap = dsa::cand_row_cap(sk, nt);
     uint64_t* cand = reinterpret_cast<uint64_t*>(ws);
-    int32_t* cand_n = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + r256((size_t)T * nc * sk * 8));
+    int32_t* cand_n = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + r256((size_t)T * cap * 8));
     const dsa::Emit e{pool_ids, indices, seqs.row_base, d.out_width};
-    hipLaunchKernelGGL(dsa::k_topk_chunks, dim3((unsigned)nc, (unsigned)T), dim3(dsa::kANT), 0, s, scores,
-                       stride, seqs.first_valid, q_seq, q_pos, sk, nc, cand, cand_n);
+    hipLaunchKernelGGL(dsa::k_topk_tiles, dim3((unsigned)nt, (unsigned)T), dim3(dsa::kTile), 0, s, scores,
+                       stride, seqs.first_valid, q_seq, q_pos, sk, cap, nt, cand, cand_n);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const int kpt = (int)cdiv((int64_t)nc * sk, dsa::kBNT);
-#define DSA_MERGE(KPT)                                                                                    \
-    hipLaunchKernelGGL((dsa::k_topk_merge<KPT>), dim3((unsigned)T), dim3(dsa::kBNT), 0, s, seqs.first_valid, \
-                       q_seq, q_pos, stride, sk, nc, cand, cand_n, e)
-    if (kpt <= 1) DSA_MERGE(1);
-    else if (kpt <= 2) DSA_MERGE(2);
-    else if (kpt <= 4) DSA_MERGE(4);
-    else if (kpt <= 8) DSA_MERGE(8);
-    else if (kpt <= 16) DSA_MERGE(16);
-    else DSA_MERGE(32);
-#undef DSA_MERGE
+    // Slots per row are at most ntiles * tile_quota(ntiles) <= cap.
+    const int kpt = (int)cdiv(cap, dsa::kBNT);
+#define DSA_ROWS(KPT)                                                                                     \
+    hipLaunchKernelGGL((dsa::k_topk_rows<KPT>), dim3((unsigned)T), dim3(dsa::kBNT), 0, s, scores,          \
+                       seqs.first_valid, q_seq, q_pos, stride, sk, cap, nt, cand, cand_n, e)
+    if (kpt <= 1) DSA_ROWS(1);
+    else if (kpt <= 2) DSA_ROWS(2);
+    else if (kpt <= 4) DSA_ROWS(4);
+    else if (kpt <= 8) DSA_ROWS(8);
+    else if (kpt <= 16) DSA_ROWS(16);
+    else DSA_ROWS(32);
+#undef DSA_ROWS
     return hipGetLastError();
 }
 
