@@ -27,6 +27,7 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 WORKLOAD = "decode_262k_b8"
 SCORES_SRC = os.path.join(ROOT, "sparse_attention_store_amd", "csrc", "index_scores.hip")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "index_scores_decode_262k_b8_traffic.md")
+COPY_BYTES = 256 << 20          # calibration copy: bytes read (and written) per launch
 
 
 def algorithmic_bytes(wl) -> dict:
@@ -69,6 +70,59 @@ def traffic_from_profile():
         return int(float(vals["hbm_bytes_per_launch"]))
     except (KeyError, ValueError):
         return None
+
+
+def _csv_rows(d: str, suffix: str):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return list(csv.DictReader(open(files[0])))
+
+
+def summarize_trace(d: str) -> str:
+    """Per-kernel durations of the library's kernels from a rocprofv3 kernel trace."""
+    import collections
+    import statistics
+    by = collections.defaultdict(list)
+    for r in _csv_rows(d, "kernel_trace.csv"):
+        if "dsa::" in r["Kernel_Name"]:
+            by[r["Kernel_Name"].split("(")[0]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = ["| kernel | dispatches | mean us | median us | min us |", "|---|---|---|---|---|"]
+    for k, v in sorted(by.items(), key=lambda kv: -statistics.mean(kv[1])):
+        out.append(f"| `{k}` | {len(v)} | {statistics.mean(v):.2f} | {statistics.median(v):.2f} | {min(v):.2f} |")
+    return "\n".join(out)
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, kernel: str) -> str:
+    """HBM bytes per dispatch of `kernel` from FETCH_SIZE and WRITE_SIZE runs, each scaled by
+    what the same counter reads for the calibration copy (COPY_BYTES read and written)."""
+    import statistics
+    vals = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _csv_rows(d, "counter_collection.csv") if r["Counter_Name"] == name]
+        cal = [float(r["Counter_Value"]) * 1024 for r in rows if "neg_kernel" in r["Kernel_Name"]]
+        ker = [float(r["Counter_Value"]) * 1024 for r in rows if kernel in r["Kernel_Name"]]
+        if not cal or not ker:
+            raise SystemExit(f"{name}: calibration copy or kernel {kernel!r} not found")
+        factor = COPY_BYTES / statistics.median(cal)
+        vals[name] = (statistics.median(ker), factor, len(ker))
+    f_raw, f_fac, n_f = vals["FETCH_SIZE"]
+    w_raw, w_fac, n_w = vals["WRITE_SIZE"]
+    total = f_raw * f_fac + w_raw * w_fac
+    src = os.path.join(ROOT, "sparse_attention_store_amd", "csrc", "index_scores.hip")
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    return "\n".join([
+        f"- kernel: {kernel}",
+        f"- dispatches: {n_f} (FETCH_SIZE run), {n_w} (WRITE_SIZE run)",
+        f"- fetch_bytes_raw_median: {f_raw:.0f}",
+        f"- fetch_scale_from_copy: {f_fac:.4f}",
+        f"- write_bytes_raw_median: {w_raw:.0f}",
+        f"- write_scale_from_copy: {w_fac:.4f}",
+        f"- hbm_bytes_per_launch: {total:.0f}",
+        f"- kernel_source_sha256_16: {h}",
+    ])
 
 
 def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
@@ -137,7 +191,21 @@ def main():
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 256 MiB elementwise copy (torch.neg) three times: a "
+                         "known-size kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print a markdown summary of DIR/*kernel_trace.csv (rocprofv3 --kernel-trace) and exit")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print a markdown traffic summary from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--kernel", default="k_scores_decode", help="kernel name substring for --summarize-pmc")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.kernel))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -156,6 +224,13 @@ def main():
     dw = dsa_harness.DeviceWorkload(wl, replicas=args.replicas, out_dtype=torch.bfloat16)
     print(f"[bench] setup {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
     R = args.replicas
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)          # reads and writes COPY_BYTES
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         dw.step(i % R)
     torch.cuda.synchronize()
