@@ -25,8 +25,11 @@ if ROOT not in sys.path:
 METRIC = "decode tok-steps/s (indexer+topk+sparse MLA) @262k ctx B=8; % HBM peak"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 WORKLOAD = "decode_262k_b8"
-SCORES_SRC = os.path.join(ROOT, "sparse_attention_store_amd", "csrc", "index_scores.hip")
+_CSRC = os.path.join(ROOT, "sparse_attention_store_amd", "csrc")
+SCORES_SRC = [os.path.join(_CSRC, "index_scores.hip")]
+STEP_SRC = [os.path.join(_CSRC, f) for f in ("decode_step.hip", "mla_core.h", "topk_core.h", "dsa_common.h")]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "index_scores_decode_262k_b8_traffic.md")
+PMC_SUMMARY_STEP = os.path.join(ROOT, "profiles", "decode_step_decode_262k_b8_traffic.md")
 COPY_BYTES = 256 << 20          # calibration copy: bytes read (and written) per launch
 
 
@@ -50,17 +53,27 @@ def algorithmic_bytes(wl) -> dict:
     step = (tot_pools * 256 + T * (d.idx_heads * d.idx_dim * 2 + d.idx_heads * 4) + tot_rows * d.row_bytes
             + T * 4 * d.mla_heads * d.latent_dim + T * 4 * d.out_width + T * (2 * d.latent_dim + d.row_bytes)
             + new_pools * (2 * d.kpool * d.idx_dim * 2 + d.idx_dim * 2))
-    return {"step": step, "scores_kernel": scores, "pools": tot_pools, "rows": tot_rows}
+    new_tokens = T * (2 * d.latent_dim + d.row_bytes) + new_pools * (2 * d.kpool * d.idx_dim * 2 + d.idx_dim * 2)
+    return {"step": step, "scores_kernel": scores, "decode_kernel": step - new_tokens, "pools": tot_pools,
+            "rows": tot_rows}
 
 
-def traffic_from_profile():
-    """HBM bytes per scores launch from the committed rocprofv3 counter summary,
-    or None when the summary is absent or was taken on a different kernel source."""
-    if not os.path.exists(PMC_SUMMARY):
+def _source_hash(srcs) -> str:
+    h = hashlib.sha256()
+    for f in srcs:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(summary: str, srcs):
+    """HBM bytes per launch of the dominant kernel from a committed rocprofv3
+    counter summary, or None when the summary is absent or was taken on
+    different kernel sources."""
+    if not os.path.exists(summary):
         return None
-    src_hash = hashlib.sha256(open(SCORES_SRC, "rb").read()).hexdigest()[:16]
+    src_hash = _source_hash(srcs)
     vals = {}
-    for ln in open(PMC_SUMMARY):
+    for ln in open(summary):
         if ":" in ln and ln.strip().startswith("- "):
             k, v = ln.strip()[2:].split(":", 1)
             vals[k.strip()] = v.strip()
@@ -111,8 +124,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, kernel: str) -> str:
     f_raw, f_fac, n_f = vals["FETCH_SIZE"]
     w_raw, w_fac, n_w = vals["WRITE_SIZE"]
     total = f_raw * f_fac + w_raw * w_fac
-    src = os.path.join(ROOT, "sparse_attention_store_amd", "csrc", "index_scores.hip")
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    h = _source_hash(STEP_SRC if "decode_step" in kernel else SCORES_SRC)
     return "\n".join([
         f"- kernel: {kernel}",
         f"- dispatches: {n_f} (FETCH_SIZE run), {n_w} (WRITE_SIZE run)",
@@ -191,6 +203,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--path", choices=["fused", "separate"], default="separate",
+                    help="fused: new tokens, then one dsa_decode_step launch; separate: one call per step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB elementwise copy (torch.neg) three times: a "
                          "known-size kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -221,7 +235,9 @@ def main():
     print(f"[bench] setting up {wl.name}: B={wl.B} T={wl.T} rows={wl.total_rows} "
           f"replicas={args.replicas}", file=sys.stderr, flush=True)
     t_setup = time.perf_counter()
-    dw = dsa_harness.DeviceWorkload(wl, replicas=args.replicas, out_dtype=torch.bfloat16)
+    fused = args.path == "fused"
+    dw = dsa_harness.DeviceWorkload(wl, replicas=args.replicas, out_dtype=torch.bfloat16,
+                                    num_splits=17 if fused else 0)
     print(f"[bench] setup {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
     R = args.replicas
     if args.calibrate_copy:
@@ -231,8 +247,9 @@ def main():
             torch.neg(src, out=dst)          # reads and writes COPY_BYTES
         torch.cuda.synchronize()
         del src, dst
+    step = dw.step_fused if fused else dw.step
     for i in range(args.warmup):
-        dw.step(i % R)
+        step(i % R)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -247,10 +264,14 @@ def main():
         dw.step_store(r)
         dw.step_pools(r)
         ev_s[i].record(stream)
-        dw.step_scores(r)
-        ev_e[i].record(stream)
-        dw.step_select()
-        dw.step_attention(r)
+        if fused:
+            dw.step_decode(r)
+            ev_e[i].record(stream)
+        else:
+            dw.step_scores(r)
+            ev_e[i].record(stream)
+            dw.step_select()
+            dw.step_attention(r)
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
@@ -259,8 +280,12 @@ def main():
 
     # Per-stage breakdown (separate, untimed pass).
     stages = {}
-    names = ["store_int8", "index_pools", "index_scores", "topk_select_expand", "sparse_mla"]
-    fns = [dw.step_store, dw.step_pools, dw.step_scores, lambda r: dw.step_select(), dw.step_attention]
+    if fused:
+        names = ["store_int8", "index_pools", "decode_step"]
+        fns = [dw.step_store, dw.step_pools, dw.step_decode]
+    else:
+        names = ["store_int8", "index_pools", "index_scores", "topk_select_expand", "sparse_mla"]
+        fns = [dw.step_store, dw.step_pools, dw.step_scores, lambda r: dw.step_select(), dw.step_attention]
     n_b = min(args.steps, 50)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(n_b)]
     for i in range(n_b):
@@ -273,7 +298,8 @@ def main():
         stages[nm] = round(float(np.median([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e3, 2)
 
     ab = algorithmic_bytes(wl)
-    achieved = ab["scores_kernel"] / (scores_us * 1e-6) / 1e9
+    kern_bytes = ab["decode_kernel"] if fused else ab["scores_kernel"]
+    achieved = kern_bytes / (scores_us * 1e-6) / 1e9
     value = wl.T / (ms_step * 1e-3)
     line = {
         "metric": METRIC,
@@ -294,10 +320,13 @@ def main():
                    "out_width": wl.dims.out_width, "replicas": R},
         "pct_hbm_peak": round(100.0 * ab["step"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "bytes_per_step": ab["step"],
-        "roofline": {"kernel": "index_scores (k_scores_decode)", "bound": "hbm",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(),
-                     "algorithmic_bytes_per_launch": ab["scores_kernel"], "avg_launch_us": round(scores_us, 2)},
+        "roofline": {"kernel": "decode_step (k_decode_step)" if fused else "index_scores (k_scores_decode)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profile(PMC_SUMMARY_STEP if fused else PMC_SUMMARY,
+                                                     STEP_SRC if fused else SCORES_SRC),
+                     "algorithmic_bytes_per_launch": kern_bytes, "avg_launch_us": round(scores_us, 2)},
+        "path": args.path,
         "stages_us_median": stages,
     }
     if not args.no_cpu_baseline:

@@ -7,6 +7,8 @@ outputs and workspaces, and runs one decode/prefill step of the path:
   store_int8 (the step's new tokens) -> index_pools (pools those tokens
   complete) -> index_scores -> topk_select -> expand_selection -> sparse_mla
 
+either as separate calls or with the last four in one dsa_decode_step launch.
+
 This module only marshals data; every computation runs in libdsa's kernels.
 """
 from __future__ import annotations
@@ -93,6 +95,7 @@ class DeviceWorkload:
         self.ws_topk = dsa.topk_workspace(self.dims, T, self.stride, device=dev)
         n = dsa.sparse_mla_workspace_bytes(self.dims, T, num_splits)
         self.ws_mla = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
+        self.ws_step = None
         if build:
             self.build_caches()
 
@@ -148,6 +151,20 @@ class DeviceWorkload:
         """Top-k and expansion in one launch (pool ids kept for the checks)."""
         dsa.topk_select_expand(self.dims, self.scores, self.seqs, self.q_seq, self.q_pos, self.indices,
                                self.pool_ids, self.ws_topk)
+
+    def step_decode(self, r: int = 0):
+        """Scores, top-k, expansion and attention in one launch (dsa_decode_step)."""
+        if self.ws_step is None:
+            self.ws_step = dsa.decode_step_workspace(self.dims, self.wl.T, self.stride, device=self.device)
+        dsa.decode_step(self.dims, self.q_idx, self.w, self.pools[r], self.seqs, self.q_seq, self.q_pos,
+                        self.stride, self.q, self.caches[r], self.wl.scale, self.out, self.ws_step, lse=self.lse,
+                        pool_ids=self.pool_ids, indices=self.indices)
+
+    def step_fused(self, r: int = 0):
+        """One pass of the whole path: the new tokens, then the fused decode launch."""
+        self.step_store(r)
+        self.step_pools(r)
+        self.step_decode(r)
 
     def step(self, r: int = 0):
         """One pass of the whole path over replica r."""

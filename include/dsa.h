@@ -228,6 +228,41 @@ int dsa_sparse_mla(const dsa_dims* dims, const void* q, int q_dtype, const int8_
                    void* out, int out_dtype, float* lse, int32_t num_splits,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * decode_step -- one launch for a decode step's index_scores, topk_select,
+ * expand_selection and sparse_mla (the chain of [Ref] Functions:
+ * index_scores, topk_pools, expand_selection, mla_masked_attention, and
+ * [Kernels] Included: split-KV decode with a combine).  The results are the
+ * ones the separate calls produce: out/lse as dsa_sparse_mla over the list
+ * dsa_topk_select_expand would write (same selection, same tie rule), and,
+ * when not NULL, that list (indices) and the selected pool ids (pool_ids).
+ * The step's new tokens must already be stored (dsa_store_int8) and the
+ * pools they complete built (dsa_index_pools).
+ *   q_idx, w, pools, seqs, q_seq, q_pos   as dsa_index_scores
+ *   score_stride   >= every query's visible pool count; <= 65,536
+ *   q, cache, scale, out, out_dtype, lse  as dsa_sparse_mla (q bf16 only)
+ *   pool_ids       device int32 [T, select_k] or NULL
+ *   indices        device int32 [T, out_width] or NULL
+ *   workspace      device, >= dsa_decode_step_workspace_bytes(dims, T,
+ *                  score_stride) bytes, 256-byte aligned.  It must be
+ *                  zero-filled before its first use; every call leaves its
+ *                  control words zero again, so one allocation serves any
+ *                  number of calls.  Calls sharing a workspace must not
+ *                  overlap.  The uint32 at byte offset 8 of the workspace
+ *                  becomes nonzero if a wait inside the launch ever timed out
+ *                  (the results of that call are then invalid).
+ * Supported: idx_heads 32, idx_dim 128, kpool 4, select_k <= 512,
+ * latent_dim 512, mla_heads a multiple of 16 up to 64, T <= 64,
+ * out_width <= 8192; else DSA_ERR_UNSUPPORTED.
+ */
+size_t dsa_decode_step_workspace_bytes(const dsa_dims* dims, int32_t T, int32_t score_stride);
+int dsa_decode_step(const dsa_dims* dims, const uint16_t* q_idx, const float* w,
+                    const uint16_t* pools, const dsa_seqs* seqs, int32_t num_seqs,
+                    const int32_t* q_seq, const int32_t* q_pos, int32_t T, int32_t score_stride,
+                    const void* q, int q_dtype, const int8_t* cache, int64_t cache_rows,
+                    float scale, void* out, int out_dtype, float* lse, int32_t* pool_ids,
+                    int32_t* indices, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

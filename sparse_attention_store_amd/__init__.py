@@ -103,6 +103,9 @@ def lib() -> ctypes.CDLL:
             "dsa_sparse_mla_workspace_bytes": (SZ, [DP, I32, I32]),
             "dsa_sparse_mla": (ctypes.c_int, [DP, P, ctypes.c_int, P, I64, P, I32, F, P, ctypes.c_int, P, I32,
                                               P, SZ, P]),
+            "dsa_decode_step_workspace_bytes": (SZ, [DP, I32, I32]),
+            "dsa_decode_step": (ctypes.c_int, [DP, P, P, P, SP, I32, P, P, I32, I32, P, ctypes.c_int, P, I64, F,
+                                               P, ctypes.c_int, P, P, P, P, SZ, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -295,8 +298,54 @@ def sparse_mla(dims: Dims, q: torch.Tensor, cache: torch.Tensor, indices: torch.
         _stream(stream)))
 
 
+def decode_step_workspace_bytes(dims: Dims, T: int, score_stride: int) -> int:
+    """Workspace of dsa_decode_step (0 when the geometry is not supported)."""
+    return int(lib().dsa_decode_step_workspace_bytes(ctypes.byref(dims), int(T), int(score_stride)))
+
+
+def decode_step_workspace(dims: Dims, T: int, score_stride: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for dsa_decode_step (reusable across calls)."""
+    n = decode_step_workspace_bytes(dims, T, score_stride)
+    if n == 0:
+        raise DsaError("dsa_decode_step_workspace_bytes", -7, "geometry not supported")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def decode_step_error(workspace: torch.Tensor) -> int:
+    """The workspace's error word (nonzero once a wait inside a launch timed out)."""
+    return int(workspace[8:12].view(torch.int32).item())
+
+
+def decode_step(dims: Dims, q_idx: torch.Tensor, w: torch.Tensor, pools: torch.Tensor, seqs: Seqs,
+                q_seq: torch.Tensor, q_pos: torch.Tensor, score_stride: int, q: torch.Tensor, cache: torch.Tensor,
+                scale: float, out: torch.Tensor, workspace: torch.Tensor, lse: torch.Tensor | None = None,
+                pool_ids: torch.Tensor | None = None, indices: torch.Tensor | None = None, stream=None):
+    """One launch: scores, top-k, expansion and sparse MLA for a decode batch."""
+    _check(q_idx, torch.bfloat16, "q_idx")
+    _check(w, torch.float32, "w")
+    _check(pools, torch.bfloat16, "pools")
+    _check(q_seq, torch.int32, "q_seq")
+    _check(q_pos, torch.int32, "q_pos")
+    _check(q, torch.bfloat16, "q")
+    _check(cache, torch.int8, "cache")
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bf16 or fp32")
+    _check(out, out.dtype, "out")
+    _check(workspace, workspace.dtype, "workspace")
+    for name, t in (("lse", lse), ("pool_ids", pool_ids), ("indices", indices)):
+        if t is not None:
+            _check(t, torch.float32 if name == "lse" else torch.int32, name)
+    T = q_pos.shape[0]
+    _raise("dsa_decode_step", lib().dsa_decode_step(
+        ctypes.byref(dims), q_idx.data_ptr(), w.data_ptr(), pools.data_ptr(), ctypes.byref(seqs._c()),
+        seqs.num_seqs, q_seq.data_ptr(), q_pos.data_ptr(), T, int(score_stride), q.data_ptr(), DSA_BF16,
+        cache.data_ptr(), cache.shape[0], float(scale), out.data_ptr(), _dt(out), _ptr(lse), _ptr(pool_ids),
+        _ptr(indices), workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
 __all__ = [
     "DSA_F32", "DSA_BF16", "DsaError", "Dims", "Seqs", "lib", "abi_version", "status_string",
     "store_int8", "index_pools", "index_scores", "topk_workspace_bytes", "topk_workspace",
     "topk_select", "topk_select_expand", "expand_selection", "sparse_mla_workspace_bytes", "sparse_mla",
+    "decode_step_workspace_bytes", "decode_step_workspace", "decode_step_error", "decode_step",
 ]

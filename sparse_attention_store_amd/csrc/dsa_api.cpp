@@ -235,4 +235,39 @@ int dsa_sparse_mla(const dsa_dims* dims, const void* q, int q_dtype, const int8_
                                                   out_dtype, lse, workspace, as_stream(stream)));
 }
 
+size_t dsa_decode_step_workspace_bytes(const dsa_dims* dims, int32_t T, int32_t score_stride) {
+    if (check_dims(dims) != DSA_OK || T <= 0 || score_stride <= 0) return 0;
+    if (!dsa_host::decode_step_supported(*dims, T, score_stride)) return 0;
+    return dsa_host::decode_step_workspace_bytes(*dims, T, score_stride);
+}
+
+int dsa_decode_step(const dsa_dims* dims, const uint16_t* q_idx, const float* w, const uint16_t* pools,
+                    const dsa_seqs* seqs, int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos,
+                    int32_t T, int32_t score_stride, const void* q, int q_dtype, const int8_t* cache,
+                    int64_t cache_rows, float scale, void* out, int out_dtype, float* lse,
+                    int32_t* pool_ids, int32_t* indices, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (q_dtype != DSA_F32 && q_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    if (out_dtype != DSA_F32 && out_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    if (T < 0 || score_stride < 0 || cache_rows < 0) return DSA_ERR_SIZE;
+    st = check_seqs(seqs, num_seqs, true, false, true);
+    if (st) return st;
+    if (T == 0) return DSA_OK;
+    if (q_dtype != DSA_BF16 || !dsa_host::decode_step_supported(*dims, T, score_stride))
+        return DSA_ERR_UNSUPPORTED;
+    if (!q_idx || !w || !pools || !q_seq || !q_pos || !q || !cache || !out) return DSA_ERR_NULL;
+    if (!aligned(q_idx, 16) || !aligned(w, 16) || !aligned(pools, 16) || !aligned(q, 16) ||
+        !aligned(cache, 16) || !aligned(out, 16))
+        return DSA_ERR_ALIGN;
+    const size_t need = dsa_host::decode_step_workspace_bytes(*dims, T, score_stride);
+    if (!workspace || workspace_bytes < need) return DSA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return DSA_ERR_ALIGN;
+    return hip_status(dsa_host::launch_decode_step(*dims, q_idx, w, pools, *seqs, q_seq, q_pos, T, score_stride,
+                                                   reinterpret_cast<const uint16_t*>(q), cache, scale, out,
+                                                   out_dtype, lse, pool_ids, indices, workspace,
+                                                   as_stream(stream)));
+}
+
 }  // extern "C"

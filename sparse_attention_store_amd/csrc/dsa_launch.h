@@ -47,4 +47,12 @@ hipError_t launch_sparse_mla(const dsa_dims& d, const MlaPlan& plan, const void*
                              const int8_t* cache, const int32_t* indices, int32_t T, float scale,
                              void* out, int out_dtype, float* lse, void* ws, hipStream_t s);
 
+bool decode_step_supported(const dsa_dims& d, int32_t T, int32_t stride);
+size_t decode_step_workspace_bytes(const dsa_dims& d, int32_t T, int32_t stride);
+hipError_t launch_decode_step(const dsa_dims& d, const uint16_t* q_idx, const float* w, const uint16_t* pools,
+                              const dsa_seqs& seqs, const int32_t* q_seq, const int32_t* q_pos, int32_t T,
+                              int32_t stride, const uint16_t* q, const int8_t* cache, float scale, void* out,
+                              int out_dtype, float* lse, int32_t* pool_ids, int32_t* indices, void* ws,
+                              hipStream_t s);
+
 }  // namespace dsa_host

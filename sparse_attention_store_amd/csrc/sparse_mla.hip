@@ -40,75 +40,9 @@
 // skipped; an empty split contributes (m = -inf, l = 0) and is ignored.
 #include "dsa_common.h"
 #include "dsa_launch.h"
+#include "mla_core.h"
 
 namespace dsa {
-
-constexpr int kD = 512;
-constexpr int kChunk = 64;
-constexpr int kKVRow = kD + 8;       // bf16 elements per LDS row (1040 B)
-constexpr int kPRow = kChunk + 8;    // bf16 elements per P' row (144 B)
-constexpr int kMaxSplitRows = 2176;  // index entries one split may cover (staged in LDS)
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-struct MlaPartial {
-    float m;   // running max, log2 domain
-    float l;   // running sum
-};
-
-__device__ __forceinline__ void int8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
-    const uint32_t u = w ^ 0x80808080u;            // biased to unsigned: code + 128
-    const float f0 = (float)(u & 0xFFu) - 128.0f;
-    const float f1 = (float)((u >> 8) & 0xFFu) - 128.0f;
-    const float f2 = (float)((u >> 16) & 0xFFu) - 128.0f;
-    const float f3 = (float)(u >> 24) - 128.0f;
-    // Small integers are exact in bf16: keep the upper halves.
-    lo = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
-    hi = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
-}
-
-// ------------------------------------------------------------------ k_mla_rows
-constexpr int kRChunk = 128;          // rows per workgroup iteration (4 waves x 32)
-constexpr int kRStride = kD + 8;      // bf16 elements per LDS row
-constexpr float kLazyMax = 8.0f;      // raise the running max only beyond 2^8
-
-// Physical row (within a 16-row tile) of MFMA row slot s: bits 2 and 3 swapped.
-__device__ __forceinline__ int row_of_slot(int s) { return (s & 3) | ((s & 4) << 1) | ((s & 8) >> 1); }
-
-// 4 INT8 codes -> bf16 of (code + 128), 0..255, exact: one byte-to-float
-// conversion per code (v_cvt_f32_ubyteN) and the upper halves packed.
-__device__ __forceinline__ void biased4_to_bf16(uint32_t w, uint32_t& lo, uint32_t& hi) {
-    const uint32_t u = w ^ 0x80808080u;
-    const float f0 = (float)(u & 0xFFu);
-    const float f1 = (float)((u >> 8) & 0xFFu);
-    const float f2 = (float)((u >> 16) & 0xFFu);
-    const float f3 = (float)(u >> 24);
-    lo = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
-    hi = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
-}
-
-__device__ __forceinline__ u32x4 codes8_to_biased_bf16(uint32_t a, uint32_t b) {
-    uint32_t r0, r1, r2, r3;
-    biased4_to_bf16(a, r0, r1);
-    biased4_to_bf16(b, r2, r3);
-    return u32x4{r0, r1, r2, r3};
-}
-
-__device__ __forceinline__ void wave_lds_fence() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-}
-
-constexpr int kPLS = kRChunk + 8;     // bf16 per head row of P'
-
-struct MlaRowsSmem {
-    uint16_t kv[kRChunk * kRStride];     // the chunk's rows as bf16 (code + 128)
-    uint16_t pl[2][16 * kPLS];           // P' hi, lo: [head][row]
-    float red_max[4][16];
-    float red_l[4][16];
-    float red_p[4][16];
-};
 
 __global__ __launch_bounds__(256, 1) void k_mla_rows(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, int row_bytes,
@@ -116,262 +50,13 @@ __global__ __launch_bounds__(256, 1) void k_mla_rows(
     int splits, float* __restrict__ part_o, MlaPartial* __restrict__ part_ml,
     void* __restrict__ out, int out_f32, float* __restrict__ lse) {
     __shared__ __attribute__((aligned(16))) MlaRowsSmem sm;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int split = blockIdx.x, head0 = blockIdx.y * 16, t = blockIdx.z;
-    const int n16 = lane & 15, g4 = lane >> 4;
-    const int prow = row_of_slot(n16);            // row (within a 16-row tile) this lane loads
-    const int srow = row_of_slot(4 * g4);         // first of the 4 rows this lane's S^T values cover
-
+    const int split = blockIdx.x, t = blockIdx.z;
     const int nchunks = (W + kRChunk - 1) / kRChunk;
     const int c_begin = split * chunks_per_split;
     const int c_end = min(c_begin + chunks_per_split, nchunks);
     const int32_t* irow = indices + (int64_t)t * W;
-
-    auto load_idx = [&](int c, int* id) {
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            const int pos = c * kRChunk + 32 * w + 16 * rt + prow;
-            id[rt] = pos < W ? irow[pos] : -1;
-        }
-    };
-    u32x4 raw[2][8];
-    float rsc[2];
-    auto load_rows = [&](const int* id) {
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            if (id[rt] >= 0) {
-                const uint8_t* src = cache + (int64_t)id[rt] * row_bytes;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) raw[rt][i] = *reinterpret_cast<const u32x4*>(src + g4 * 128 + 16 * i);
-                rsc[rt] = *reinterpret_cast<const float*>(src + kD);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) raw[rt][i] = u32x4{0u, 0u, 0u, 0u};
-                rsc[rt] = -1.0f;                 // marks an empty slot
-            }
-        }
-    };
-
-    // The dependent chain index -> row bytes goes first; Q loads overlap it.
-    int id_cur[2] = {-1, -1}, id_next[2] = {-1, -1};
-    if (c_begin < c_end) {
-        load_idx(c_begin, id_cur);
-        if (c_begin + 1 < c_end) load_idx(c_begin + 1, id_next);
-        load_rows(id_cur);
-    }
-
-    // Q^T operand (B of S^T): head head0 + n16, reduction index g4*128 + 8j + e.
-    u32x4 qb[16];
-    {
-        const uint16_t* qr = q + ((int64_t)t * H + head0 + n16) * kD + g4 * 128;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) qb[j] = *reinterpret_cast<const u32x4*>(qr + 8 * j);
-    }
-    // The K and V operands hold code + 128 (exact in bf16, one conversion per
-    // code); the bias is removed afterwards: S -= 128 * sum_k q_k per head and
-    // O -= 128 * sum_j P'_j over the same bf16 P' values the products used.
-    float qsum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            qsum += bf16_to_f32(qb[j][k] & 0xFFFFu) + bf16_to_f32(qb[j][k] >> 16);
-    qsum += __shfl_xor(qsum, 16, 64);
-    qsum += __shfl_xor(qsum, 32, 64);
-    const float sbias = 128.0f * qsum;
-
-    // Running softmax state of head n16 (the same in every wave); l and the
-    // P' sum cover this lane's own rows and are added up at the end.
-    float m_run = -INFINITY, l_run = 0.f, p_run = 0.f;
-    f32x4 acc[2][4];                             // O^T: cols 128w + 64G + 16g4 + 4i + u, head n16
-#pragma unroll
-    for (int G = 0; G < 2; ++G)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) acc[G][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int c = c_begin; c < c_end; ++c) {
-        const bool live = __ballot(id_cur[0] >= 0 || id_cur[1] >= 0) != 0ull;
-        const float rs_now[2] = {rsc[0], rsc[1]};
-        f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        if (live) {
-            // ---- convert this wave's 32 rows, S^T = K Q^T (4 independent
-            //      accumulation chains), and stage the rows for V^T
-            f32x4 sc4[2][2];
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) sc4[rt][0] = sc4[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
-                    const u32x4 kb =
-                        codes8_to_biased_bf16(raw[rt][j >> 1][(j & 1) * 2], raw[rt][j >> 1][(j & 1) * 2 + 1]);
-                    sc4[rt][j & 1] = mfma16(as_bf16x8(kb), as_bf16x8(qb[j]), sc4[rt][j & 1]);
-                    *reinterpret_cast<u32x4*>(&sm.kv[(32 * w + 16 * rt + prow) * kRStride + g4 * 128 + 8 * j]) = kb;
-                }
-            }
-            s[0] = sc4[0][0] + sc4[0][1];
-            s[1] = sc4[1][0] + sc4[1][1];
-        }
-        // ---- next chunk's rows in flight while this one computes
-        if (c + 1 < c_end) {
-            load_rows(id_next);
-            id_cur[0] = id_next[0];
-            id_cur[1] = id_next[1];
-            if (c + 2 < c_end) load_idx(c + 2, id_next);
-        }
-
-        // ---- chunk max per head across the 4 waves (lane: head n16, rows slot 4*g4 + i)
-        float z[2][4], sc[2][4];
-        float cmax = -INFINITY;
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sc[rt][i] = __shfl(rs_now[rt], 4 * g4 + i, 64);
-                z[rt][i] = sc[rt][i] > 0.f ? (s[rt][i] - sbias) * (sc[rt][i] * scale_log2) : -INFINITY;
-                cmax = fmaxf(cmax, z[rt][i]);
-            }
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-        if (g4 == 0) sm.red_max[w][n16] = cmax;
-        lds_barrier();
-        float wmax[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) wmax[k] = sm.red_max[k][n16];
-        const float chunk_max = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-        // Source waves with a live row: the same answer for every head.
-        bool src_live[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) src_live[k] = __ballot(wmax[k] != -INFINITY) != 0ull;
-
-        // The running max is raised only when the chunk exceeds it by 2^8.
-        const float m_new = (m_run == -INFINITY || chunk_max > m_run + kLazyMax) ? chunk_max : m_run;
-        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        if (__ballot(alpha != 1.0f && m_run != -INFINITY) != 0ull) {
-#pragma unroll
-            for (int G = 0; G < 2; ++G)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) acc[G][u] *= alpha;
-        }
-        l_run *= alpha;
-        p_run *= alpha;
-        m_run = m_new;
-
-        // ---- P' = p * scale as bf16 hi + lo, to LDS as [head][row]
-        uint32_t bh[2][2], bl[2][2];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int i2 = 0; i2 < 2; ++i2) {
-                float x[2];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int i = 2 * i2 + h;
-                    const float p = m_new == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[rt][i] - m_new);
-                    l_run += p;
-                    x[h] = p * fmaxf(sc[rt][i], 0.f);
-                }
-                const uint32_t h0 = f32_to_bf16_rne(x[0]), h1 = f32_to_bf16_rne(x[1]);
-                const uint32_t l0 = f32_to_bf16_rne(x[0] - bf16_to_f32(h0));
-                const uint32_t l1 = f32_to_bf16_rne(x[1] - bf16_to_f32(h1));
-                bh[rt][i2] = h0 | (h1 << 16);
-                bl[rt][i2] = l0 | (l1 << 16);
-                p_run += (bf16_to_f32(h0) + bf16_to_f32(l0)) + (bf16_to_f32(h1) + bf16_to_f32(l1));
-            }
-        if (live) {
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const int r0 = 32 * w + 16 * rt + srow;
-                *reinterpret_cast<u32x2*>(&sm.pl[0][n16 * kPLS + r0]) = u32x2{bh[rt][0], bh[rt][1]};
-                *reinterpret_cast<u32x2*>(&sm.pl[1][n16 * kPLS + r0]) = u32x2{bl[rt][0], bl[rt][1]};
-            }
-        }
-        lds_barrier();                               // rows and P' of all waves visible
-
-        // ---- O^T += V^T P'^T over the chunk's 128 rows, this wave's 128 columns
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            if (!src_live[ks]) continue;             // that wave staged no rows
-            const int r0 = 32 * ks + 8 * g4;         // k-slot e <-> row r0 + e
-            const bf16x8 p_hi = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.pl[0][n16 * kPLS + r0]));
-            const bf16x8 p_lo = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.pl[1][n16 * kPLS + r0]));
-#pragma unroll
-            for (int G = 0; G < 2; ++G) {
-                const uint16_t* vb = &sm.kv[r0 * kRStride + 128 * w + 64 * G + 4 * n16];
-                u32x2 v[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = *reinterpret_cast<const u32x2*>(vb + e * kRStride);
-                u32x4 a[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int wd = u >> 1;
-                    const uint32_t sel = (u & 1) ? 0x07060302u : 0x05040100u;
-                    a[u][0] = __builtin_amdgcn_perm(v[1][wd], v[0][wd], sel);
-                    a[u][1] = __builtin_amdgcn_perm(v[3][wd], v[2][wd], sel);
-                    a[u][2] = __builtin_amdgcn_perm(v[5][wd], v[4][wd], sel);
-                    a[u][3] = __builtin_amdgcn_perm(v[7][wd], v[6][wd], sel);
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) acc[G][u] = mfma16(as_bf16x8(a[u]), p_hi, acc[G][u]);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) acc[G][u] = mfma16(as_bf16x8(a[u]), p_lo, acc[G][u]);
-            }
-        }
-        if (c + 1 < c_end) lds_barrier();            // rows and P' are rewritten next
-    }
-
-    // ---- totals over the 4 waves' rows, then this wave's 128 columns out
-    l_run += __shfl_xor(l_run, 16, 64);
-    l_run += __shfl_xor(l_run, 32, 64);
-    p_run += __shfl_xor(p_run, 16, 64);
-    p_run += __shfl_xor(p_run, 32, 64);
-    if (g4 == 0) {
-        sm.red_l[w][n16] = l_run;
-        sm.red_p[w][n16] = p_run;
-    }
-    lds_barrier();
-    float L = 0.f, PS = 0.f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        L += sm.red_l[k][n16];
-        PS += sm.red_p[k][n16];
-    }
-    const float obias = 128.0f * PS;
-    const int head = head0 + n16;
-    if (splits == 1) {
-        const float inv = L > 0.f ? 1.0f / L : 0.f;
-        const int64_t orow = ((int64_t)t * H + head) * kD;
-#pragma unroll
-        for (int G = 0; G < 2; ++G)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int col = 128 * w + 64 * G + 16 * g4 + 4 * i;
-                const f32x4 o = (f32x4{acc[G][0][i], acc[G][1][i], acc[G][2][i], acc[G][3][i]} - obias) * inv;
-                if (out_f32) {
-                    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + orow + col) = o;
-                } else {
-                    u32x2 pk;
-                    pk[0] = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
-                    pk[1] = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
-                    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + orow + col) = pk;
-                }
-            }
-        if (lse && w == 0 && g4 == 0) lse[(int64_t)t * H + head] = L > 0.f ? (m_run + log2f(L)) * kLn2 : -INFINITY;
-    } else {
-        const int64_t slot = ((int64_t)t * splits + split) * H + head;
-        if (L > 0.f) {
-            float* po = part_o + slot * kD;
-#pragma unroll
-            for (int G = 0; G < 2; ++G)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int col = 128 * w + 64 * G + 16 * g4 + 4 * i;
-                    *reinterpret_cast<f32x4*>(po + col) =
-                        f32x4{acc[G][0][i], acc[G][1][i], acc[G][2][i], acc[G][3][i]} - obias;
-                }
-        }
-        if (w == 0 && g4 == 0) part_ml[slot] = MlaPartial{m_run, L};
-    }
+    mla_rows_split<false>(sm, q, cache, row_bytes, [&](int pos) { return irow[pos]; }, W, H, scale_log2, t,
+                          blockIdx.y * 16, split, c_begin, c_end, splits, part_o, part_ml, out, out_f32, lse);
 }
 
 // ------------------------------------------------------------------ k_mla_mfma
@@ -629,7 +314,6 @@ __global__ __launch_bounds__(256) void k_mla_mfma(
 // Merge split partials in split order: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
 // The (m, l) pairs go through LDS first; then every thread issues the loads of
 // its 4 columns for all non-empty splits before accumulating them in order.
-constexpr int kMaxSplits = 64;
 __global__ __launch_bounds__(128) void k_mla_combine(
     const float* __restrict__ part_o, const MlaPartial* __restrict__ part_ml, int splits, int H,
     void* __restrict__ out, int out_f32, float* __restrict__ lse) {

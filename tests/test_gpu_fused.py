@@ -1,0 +1,101 @@
+"""The single-launch decode step (dsa_decode_step) on the GPU.
+
+It must reproduce, bit for bit, the separate calls it replaces (scores ->
+topk_select_expand -> sparse_mla with one split per 128 list positions), and
+match the oracle chain under the same rules as tests/test_gpu_chain.py.  Its
+workspace control words must come back zero (every call leaves the queue and
+the per-query counters reset), so a second call gives the same bits, and no
+internal wait may time out.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dsa_synth as syn
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def harness():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dsa_harness
+    return dsa_harness
+
+
+def _fused_vs_separate(harness, wl, splits):
+    import sparse_attention_store_amd as dsa
+    dw = harness.DeviceWorkload(wl, num_splits=splits)
+    dw.step()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (dw.pool_ids, dw.indices, dw.out, dw.lse)]
+    for x in (dw.pool_ids, dw.indices):
+        x.fill_(0x5A5A5A5A)
+    dw.out.fill_(float("nan"))
+    dw.lse.fill_(float("nan"))
+    for rep in range(2):
+        dw.step_decode()
+        torch.cuda.synchronize()
+        assert dsa.decode_step_error(dw.ws_step) == 0
+        ctl = dw.ws_step[:16].view(torch.int32).cpu().numpy()
+        assert ctl[0] == 0 and ctl[1] == 0, ("queue not reset", ctl)
+        for name, a, b in zip(("pool_ids", "indices", "out", "lse"), ref, (dw.pool_ids, dw.indices, dw.out, dw.lse)):
+            assert torch.equal(a, b), (name, rep)
+    return dw
+
+
+@pytest.mark.parametrize("name", ["mini_decode", "mini_heavy"])
+def test_decode_step_matches_separate_calls(harness, name):
+    wl = syn.get(name)
+    say(f"decode step {name} T={wl.T} H={wl.dims.mla_heads}")
+    _fused_vs_separate(harness, wl, splits=17)
+
+
+def test_decode_step_matches_oracle(harness):
+    from test_gpu_chain import _check_chain
+    wl = syn.mini_decode()
+    say(f"decode step vs oracle {wl.name}")
+    dw = harness.DeviceWorkload(wl, num_splits=17)
+    dw.step()                                   # fills dw.scores (checked by the chain rules)
+    dw.step_decode()
+    torch.cuda.synchronize()
+    _check_chain(dw, range(wl.T))
+
+
+def test_decode_step_forced_fallback(harness):
+    """Equal scores everywhere (q_idx = 0): every kept-group list is full and
+    every certificate fails, so each sparse query takes the exact streaming
+    select over its scores; the result must still be the lowest ids."""
+    import sparse_attention_store_amd as dsa
+    wl = syn.decode_32k()
+    say("decode step with all-equal scores (fallback path)")
+    dw = harness.DeviceWorkload(wl, num_splits=17)
+    dw.q_idx.zero_()
+    dw.step()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (dw.pool_ids, dw.indices, dw.out, dw.lse)]
+    dw.step_decode()
+    torch.cuda.synchronize()
+    assert dsa.decode_step_error(dw.ws_step) == 0
+    sk = wl.dims.select_k
+    assert np.array_equal(dw.pool_ids[0].cpu().numpy(), np.arange(sk))
+    for a, b in zip(ref, (dw.pool_ids, dw.indices, dw.out, dw.lse)):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["decode_32k", "decode_262k_b8"])
+def test_decode_step_full_size(harness, name):
+    from test_gpu_chain import _check_chain
+    wl = syn.get(name)
+    say(f"decode step full {name} T={wl.T}")
+    dw = _fused_vs_separate(harness, wl, splits=17)
+    say(f"decode step full {name}: oracle check of {wl.T} queries")
+    _check_chain(dw, list(range(wl.T)), pool_sample=64, allow_swaps_frac=0.25)
+    del dw
+    torch.cuda.empty_cache()
