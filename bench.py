@@ -268,9 +268,9 @@ def main():
             dw.step_decode(r)
             ev_e[i].record(stream)
         else:
-            dw.step_scores(r)
+            dw.step_scores_groups(r)
             ev_e[i].record(stream)
-            dw.step_select()
+            dw.step_select_groups()
             dw.step_attention(r)
     end.record(stream)
     torch.cuda.synchronize()
@@ -284,8 +284,9 @@ def main():
         names = ["store_int8", "index_pools", "decode_step"]
         fns = [dw.step_store, dw.step_pools, dw.step_decode]
     else:
-        names = ["store_int8", "index_pools", "index_scores", "topk_select_expand", "sparse_mla"]
-        fns = [dw.step_store, dw.step_pools, dw.step_scores, lambda r: dw.step_select(), dw.step_attention]
+        names = ["store_int8", "index_pools", "index_scores_groups", "topk_select_groups", "sparse_mla"]
+        fns = [dw.step_store, dw.step_pools, dw.step_scores_groups, lambda r: dw.step_select_groups(),
+               dw.step_attention]
     n_b = min(args.steps, 50)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(n_b)]
     for i in range(n_b):
@@ -320,7 +321,7 @@ def main():
                    "out_width": wl.dims.out_width, "replicas": R},
         "pct_hbm_peak": round(100.0 * ab["step"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "bytes_per_step": ab["step"],
-        "roofline": {"kernel": "decode_step (k_decode_step)" if fused else "index_scores (k_scores_decode)",
+        "roofline": {"kernel": "decode_step (k_decode_step)" if fused else "index_scores_groups (k_scores_decode)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile(PMC_SUMMARY_STEP if fused else PMC_SUMMARY,

@@ -96,6 +96,7 @@ class DeviceWorkload:
         n = dsa.sparse_mla_workspace_bytes(self.dims, T, num_splits)
         self.ws_mla = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
         self.ws_step = None
+        self.ws_ss = None
         if build:
             self.build_caches()
 
@@ -147,6 +148,24 @@ class DeviceWorkload:
         dsa.sparse_mla(self.dims, self.q, self.caches[r], self.indices, self.wl.scale, self.out, self.lse,
                        self.num_splits, self.ws_mla)
 
+    def _ws_ss(self):
+        if self.ws_ss is None:
+            self.ws_ss = dsa.index_scores_select_workspace(self.dims, self.wl.T, self.stride, device=self.device)
+        return self.ws_ss
+
+    def step_scores_groups(self, r: int = 0):
+        dsa.index_scores_groups(self.dims, self.q_idx, self.w, self.pools[r], self.seqs, self.q_seq, self.q_pos,
+                                self.scores, self._ws_ss())
+
+    def step_select_groups(self):
+        dsa.topk_select_groups(self.dims, self.scores, self.seqs, self.q_seq, self.q_pos, self.indices, self._ws_ss(),
+                               pool_ids=self.pool_ids)
+
+    def step_scores_select(self, r: int = 0):
+        """Scores, selection and expansion (dsa_index_scores_select: two launches for decode)."""
+        dsa.index_scores_select(self.dims, self.q_idx, self.w, self.pools[r], self.seqs, self.q_seq, self.q_pos,
+                                self.scores, self.indices, pool_ids=self.pool_ids, workspace=self._ws_ss())
+
     def step_select(self):
         """Top-k and expansion in one launch (pool ids kept for the checks)."""
         dsa.topk_select_expand(self.dims, self.scores, self.seqs, self.q_seq, self.q_pos, self.indices,
@@ -168,6 +187,13 @@ class DeviceWorkload:
 
     def step(self, r: int = 0):
         """One pass of the whole path over replica r."""
+        self.step_store(r)
+        self.step_pools(r)
+        self.step_scores_select(r)
+        self.step_attention(r)
+
+    def step_calls(self, r: int = 0):
+        """The same pass with scoring and selection as their own calls."""
         self.step_store(r)
         self.step_pools(r)
         self.step_scores(r)

@@ -187,6 +187,41 @@ int dsa_topk_select_expand(const dsa_dims* dims, const float* scores, int32_t sc
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * index_scores_select -- dsa_index_scores followed by dsa_topk_select_expand,
+ * with the same results (scores, pool_ids, indices), in two launches: for
+ * decode batches (T <= 64, 32 x 128 indexer heads, select_k <= 512,
+ * score_stride <= 65,536) the scoring pass also keeps each 64-pool group's
+ * best pools, so the selection reads those lists instead of a per-tile pass
+ * over the scores; other shapes run the two calls unchanged.
+ *   arguments as dsa_index_scores and dsa_topk_select_expand
+ *   workspace  device, >= dsa_index_scores_select_workspace_bytes(dims, T,
+ *              score_stride) bytes, 256-byte aligned; scratch only.
+ */
+size_t dsa_index_scores_select_workspace_bytes(const dsa_dims* dims, int32_t T, int32_t score_stride);
+/*
+ * The two halves of dsa_index_scores_select for decode shapes, as separate
+ * calls sharing one workspace (same size): dsa_index_scores_groups writes the
+ * scores and, into the workspace, each 64-pool group's best pools;
+ * dsa_topk_select_groups then selects from those lists (reading the scores
+ * only if it must fall back to an exact pass).  Other shapes:
+ * DSA_ERR_UNSUPPORTED.
+ */
+int dsa_index_scores_groups(const dsa_dims* dims, const uint16_t* q_idx, const float* w,
+                            const uint16_t* pools, const dsa_seqs* seqs, int32_t num_seqs,
+                            const int32_t* q_seq, const int32_t* q_pos, int32_t T,
+                            int32_t score_stride, float* scores, void* workspace,
+                            size_t workspace_bytes, void* stream);
+int dsa_topk_select_groups(const dsa_dims* dims, const float* scores, int32_t score_stride,
+                           const dsa_seqs* seqs, int32_t num_seqs, const int32_t* q_seq,
+                           const int32_t* q_pos, int32_t T, int32_t* pool_ids, int32_t* indices,
+                           void* workspace, size_t workspace_bytes, void* stream);
+int dsa_index_scores_select(const dsa_dims* dims, const uint16_t* q_idx, const float* w,
+                            const uint16_t* pools, const dsa_seqs* seqs, int32_t num_seqs,
+                            const int32_t* q_seq, const int32_t* q_pos, int32_t T,
+                            int32_t score_stride, float* scores, int32_t* pool_ids, int32_t* indices,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * expand_selection -- [Ref] Functions (expand_selection) and Traps (the -1
  * sentinel, fully written output): for each query, the selected pools (the
  * leading non-negative entries of pool_ids[t], ascending) become their kpool

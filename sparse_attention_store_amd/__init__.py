@@ -103,6 +103,10 @@ def lib() -> ctypes.CDLL:
             "dsa_sparse_mla_workspace_bytes": (SZ, [DP, I32, I32]),
             "dsa_sparse_mla": (ctypes.c_int, [DP, P, ctypes.c_int, P, I64, P, I32, F, P, ctypes.c_int, P, I32,
                                               P, SZ, P]),
+            "dsa_index_scores_select_workspace_bytes": (SZ, [DP, I32, I32]),
+            "dsa_index_scores_select": (ctypes.c_int, [DP, P, P, P, SP, I32, P, P, I32, I32, P, P, P, P, SZ, P]),
+            "dsa_index_scores_groups": (ctypes.c_int, [DP, P, P, P, SP, I32, P, P, I32, I32, P, P, SZ, P]),
+            "dsa_topk_select_groups": (ctypes.c_int, [DP, P, I32, SP, I32, P, P, I32, P, P, P, SZ, P]),
             "dsa_decode_step_workspace_bytes": (SZ, [DP, I32, I32]),
             "dsa_decode_step": (ctypes.c_int, [DP, P, P, P, SP, I32, P, P, I32, I32, P, ctypes.c_int, P, I64, F,
                                                P, ctypes.c_int, P, P, P, P, SZ, P]),
@@ -298,6 +302,66 @@ def sparse_mla(dims: Dims, q: torch.Tensor, cache: torch.Tensor, indices: torch.
         _stream(stream)))
 
 
+def index_scores_select_workspace(dims: Dims, T: int, score_stride: int, device="cuda") -> torch.Tensor | None:
+    n = int(lib().dsa_index_scores_select_workspace_bytes(ctypes.byref(dims), int(T), int(score_stride)))
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def index_scores_select(dims: Dims, q_idx: torch.Tensor, w: torch.Tensor, pools: torch.Tensor, seqs: Seqs,
+                        q_seq: torch.Tensor, q_pos: torch.Tensor, scores: torch.Tensor, indices: torch.Tensor,
+                        pool_ids: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+    """index_scores then topk_select_expand (decode batches: one scoring pass that also keeps group lists)."""
+    _check(q_idx, torch.bfloat16, "q_idx")
+    _check(w, torch.float32, "w")
+    _check(pools, torch.bfloat16, "pools")
+    _check(q_seq, torch.int32, "q_seq")
+    _check(q_pos, torch.int32, "q_pos")
+    _check(scores, torch.float32, "scores")
+    _check(indices, torch.int32, "indices")
+    if pool_ids is not None:
+        _check(pool_ids, torch.int32, "pool_ids")
+    ws_bytes = 0
+    if workspace is not None:
+        _check(workspace, workspace.dtype, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _raise("dsa_index_scores_select", lib().dsa_index_scores_select(
+        ctypes.byref(dims), q_idx.data_ptr(), w.data_ptr(), pools.data_ptr(), ctypes.byref(seqs._c()),
+        seqs.num_seqs, q_seq.data_ptr(), q_pos.data_ptr(), q_pos.shape[0], scores.shape[1], scores.data_ptr(),
+        _ptr(pool_ids), indices.data_ptr(), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def index_scores_groups(dims: Dims, q_idx: torch.Tensor, w: torch.Tensor, pools: torch.Tensor, seqs: Seqs,
+                        q_seq: torch.Tensor, q_pos: torch.Tensor, scores: torch.Tensor, workspace: torch.Tensor,
+                        stream=None):
+    """Decode scoring pass that also keeps each 64-pool group's best pools in `workspace`."""
+    for name, t, dt in (("q_idx", q_idx, torch.bfloat16), ("w", w, torch.float32), ("pools", pools, torch.bfloat16),
+                        ("q_seq", q_seq, torch.int32), ("q_pos", q_pos, torch.int32),
+                        ("scores", scores, torch.float32)):
+        _check(t, dt, name)
+    _check(workspace, workspace.dtype, "workspace")
+    _raise("dsa_index_scores_groups", lib().dsa_index_scores_groups(
+        ctypes.byref(dims), q_idx.data_ptr(), w.data_ptr(), pools.data_ptr(), ctypes.byref(seqs._c()),
+        seqs.num_seqs, q_seq.data_ptr(), q_pos.data_ptr(), q_pos.shape[0], scores.shape[1], scores.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def topk_select_groups(dims: Dims, scores: torch.Tensor, seqs: Seqs, q_seq: torch.Tensor, q_pos: torch.Tensor,
+                       indices: torch.Tensor, workspace: torch.Tensor, pool_ids: torch.Tensor | None = None,
+                       stream=None):
+    """Selection and expansion from the group lists index_scores_groups left in `workspace`."""
+    _check(scores, torch.float32, "scores")
+    _check(indices, torch.int32, "indices")
+    _check(q_seq, torch.int32, "q_seq")
+    _check(q_pos, torch.int32, "q_pos")
+    if pool_ids is not None:
+        _check(pool_ids, torch.int32, "pool_ids")
+    _check(workspace, workspace.dtype, "workspace")
+    _raise("dsa_topk_select_groups", lib().dsa_topk_select_groups(
+        ctypes.byref(dims), scores.data_ptr(), scores.shape[1], ctypes.byref(seqs._c()), seqs.num_seqs,
+        q_seq.data_ptr(), q_pos.data_ptr(), q_pos.shape[0], _ptr(pool_ids), indices.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
 def decode_step_workspace_bytes(dims: Dims, T: int, score_stride: int) -> int:
     """Workspace of dsa_decode_step (0 when the geometry is not supported)."""
     return int(lib().dsa_decode_step_workspace_bytes(ctypes.byref(dims), int(T), int(score_stride)))
@@ -347,5 +411,6 @@ __all__ = [
     "DSA_F32", "DSA_BF16", "DsaError", "Dims", "Seqs", "lib", "abi_version", "status_string",
     "store_int8", "index_pools", "index_scores", "topk_workspace_bytes", "topk_workspace",
     "topk_select", "topk_select_expand", "expand_selection", "sparse_mla_workspace_bytes", "sparse_mla",
+    "index_scores_select_workspace", "index_scores_select", "index_scores_groups", "topk_select_groups",
     "decode_step_workspace_bytes", "decode_step_workspace", "decode_step_error", "decode_step",
 ]

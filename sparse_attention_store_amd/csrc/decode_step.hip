@@ -47,13 +47,12 @@ namespace dsa {
 
 constexpr int kStepMaxT = 64;
 constexpr int kSTile = 512;              // pools per scoring task (two 256-pool halves)
-constexpr int kSGroup = 64;              // pools per kept-list group (one wave)
-constexpr int kStepMaxGroups = 1024;     // score_stride <= 65,536 pools
-constexpr int kStepCandCap = 8192;       // kept entries per query
+constexpr int kSGroup = kGroupPools;
+constexpr int kStepMaxGroups = kMaxGroups;
+constexpr int kStepCandCap = kGroupCandCap;
 constexpr int kStepNT = 256;
 constexpr int kStepKPT = kStepCandCap / kStepNT;
-constexpr int kStepMaxK = 512;
-constexpr int kGroupDropped = 1 << 30;   // group count flag: the group dropped pools
+constexpr int kStepMaxK = kGroupMaxK;
 constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr int kCombHeads = 4;            // heads per combine task
 
@@ -94,20 +93,6 @@ struct StepArgs {
     float* part_o;
     MlaPartial* part_ml;
 };
-
-// Kept entries per 64-pool group for a query of n visible pools (n > K): a
-// power of two >= lambda + 5 sqrt(lambda) + 4, lambda = 64 K / n being a
-// group's mean share of the K, so that a group needing more than m is a
-// > 5-sigma event; at least 8, at most 64 and at most kStepCandCap / groups.
-__device__ __forceinline__ int group_quota(int K, int n) {
-    const int groups = (n + kSGroup - 1) / kSGroup;
-    const float lam = 64.0f * (float)K / (float)n;
-    const float want = lam + 5.0f * sqrtf(lam) + 4.0f;
-    int m = 8;
-    while ((float)m < want && m < kSGroup) m <<= 1;
-    while (m > 8 && groups * m > kStepCandCap) m >>= 1;
-    return m;
-}
 
 // ---------------------------------------------------------------- coherent access
 
@@ -188,8 +173,7 @@ struct StepPlan {
 };
 
 struct StepSelSmem {
-    SelShared<kStepNT> S;
-    uint32_t mm_sh[2 * kStepNT / 64];
+    TopSelShared<kStepNT, kStepKPT> T;
     int32_t sel[kStepMaxK];
     uint32_t gpicked[kStepMaxGroups];
     uint32_t gcount[kStepMaxGroups];
@@ -296,27 +280,18 @@ __device__ void step_select(const StepArgs& a, StepSelSmem& sm, StepPlan& plan, 
         key[j] = ok ? (uint32_t)(raw[j] >> 32) : 0u;
         id[j] = (int32_t)(0xFFFFFFFFu - (uint32_t)raw[j]);
     }
-    uint32_t lo, hi, krem;
-    bool whole;
-    bucket_select<kStepNT, kStepKPT, uint32_t>(key, (uint32_t)K, sm.S, sm.mm_sh, lo, hi, krem, whole);
-    uint32_t take;
-    uint32_t pos = compaction_slot<kStepNT, kStepKPT, uint32_t>(key, lo, hi, krem, whole, sm.S, take);
-    uint32_t picks = 0u;
+    const uint32_t picks = select_top_slots<kStepNT, kStepKPT>(key, (uint32_t)K, sm.T);
+    uint32_t total;
+    uint32_t pos = block_exclusive_scan<kStepNT>((uint32_t)__popc(picks), sm.T.S.scan, &total);
 #pragma unroll
-    for (int j = 0; j < kStepKPT; ++j) {
-        const uint32_t k = key[j];
-        const bool inr = k >= lo && k <= hi;
-        const bool pk = k > hi || (inr && take > 0);
-        take -= (inr && take > 0) ? 1u : 0u;
-        picks |= pk ? (1u << j) : 0u;
-        if (pk) atomicAdd(&sm.gpicked[(s0 + j) >> msh], 1u);
-    }
+    for (int j = 0; j < kStepKPT; ++j)
+        if ((picks >> j) & 1u) atomicAdd(&sm.gpicked[(s0 + j) >> msh], 1u);
     lds_barrier();
     for (int g = tid; g < groups; g += kStepNT)
         if ((sm.gcount[g] & kGroupDropped) && sm.gpicked[g] == (uint32_t)m) sm.fail = 1;
     lds_barrier();
     if (sm.fail) {
-        step_stream_exact(a.scores + (int64_t)t * a.stride, n, K, sm.S, sm.sel);
+        step_stream_exact(a.scores + (int64_t)t * a.stride, n, K, sm.T.S, sm.sel);
     } else {
 #pragma unroll
         for (int j = 0; j < kStepKPT; ++j) {
@@ -494,33 +469,11 @@ __global__ __launch_bounds__(kStepNT, 1) void k_decode_step(StepArgs a) {
                 const float s = sc[g];
                 const bool valid = p < nvis;
                 if (valid) st_coh32(a.scores + (int64_t)t * a.stride + p, __float_as_uint(s));
-                if (m > 0) {
-                    // keep this group's best m: the m-th largest key by 32 ballot steps
-                    const uint32_t key = valid ? f32_key(s) : 0u;
-                    const int nvalid = __popcll(__ballot(valid));
-                    bool pick = valid;
-                    if (nvalid > m) {
-                        uint32_t x = 0u;
-                        for (int bit = 31; bit >= 0; --bit) {
-                            const uint32_t y = x | (1u << bit);
-                            if (__popcll(__ballot(key >= y)) >= m) x = y;
-                        }
-                        // keys above x, then the lowest-id lanes holding x
-                        const unsigned long long eqm = __ballot(key == x);
-                        const int above = __popcll(__ballot(key > x));
-                        const int eq_before = __popcll(eqm & ((1ull << lane) - 1ull));
-                        pick = key > x || (key == x && eq_before < m - above);
-                    }
-                    const unsigned long long pm = __ballot(pick);
-                    const int slot = __popcll(pm & ((1ull << lane) - 1ull));
-                    const int grp = (p0 + half * 256) / kSGroup + wave;
-                    if (pick)
-                        st_coh64(a.cand + (int64_t)t * kStepCandCap + (int64_t)grp * m + slot,
-                                 ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)p));
-                    if (lane == 0)
-                        st_coh32(a.cand_n + (int64_t)t * kStepMaxGroups + grp,
-                                 (uint32_t)(__popcll(pm) | (nvalid > m ? kGroupDropped : 0)));
-                }
+                if (m > 0)
+                    keep_group_best(s, valid, p, (p0 + half * 256) / kSGroup + wave, m,
+                                    a.cand + (int64_t)t * kStepCandCap, a.cand_n + (int64_t)t * kStepMaxGroups,
+                                    [](uint64_t* q, uint64_t v) { st_coh64(q, v); },
+                                    [](int32_t* q, uint32_t v) { st_coh32(q, v); });
             }
             if (nvis > a.select_k) publish(&C->tiles_done[t]);   // dense queries need no hand-off
             lds_barrier();                                 // LDS reused by the next task

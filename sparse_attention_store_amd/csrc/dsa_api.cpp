@@ -193,6 +193,83 @@ int dsa_topk_select_expand(const dsa_dims* dims, const float* scores, int32_t sc
                        workspace, workspace_bytes, stream);
 }
 
+size_t dsa_index_scores_select_workspace_bytes(const dsa_dims* dims, int32_t T, int32_t score_stride) {
+    if (check_dims(dims) != DSA_OK || T <= 0 || score_stride <= 0) return 0;
+    if (dsa_host::scores_select_grouped(*dims, T, score_stride)) return dsa_host::scores_select_group_bytes(T);
+    return dsa_host::topk_workspace_bytes(*dims, T, score_stride);
+}
+
+static int groups_common(const dsa_dims* dims, const dsa_seqs* seqs, int32_t num_seqs, int32_t T,
+                         int32_t score_stride, void* workspace, size_t workspace_bytes) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (T < 0 || score_stride < 0) return DSA_ERR_SIZE;
+    st = check_seqs(seqs, num_seqs, true, false, true);
+    if (st) return st;
+    if (T > 0 && !dsa_host::scores_select_grouped(*dims, T, score_stride)) return DSA_ERR_UNSUPPORTED;
+    if (T == 0 || score_stride == 0) return DSA_OK;
+    if (!workspace || workspace_bytes < dsa_host::scores_select_group_bytes(T)) return DSA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return DSA_ERR_ALIGN;
+    return DSA_OK;
+}
+
+int dsa_index_scores_groups(const dsa_dims* dims, const uint16_t* q_idx, const float* w, const uint16_t* pools,
+                            const dsa_seqs* seqs, int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos,
+                            int32_t T, int32_t score_stride, float* scores, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    int st = groups_common(dims, seqs, num_seqs, T, score_stride, workspace, workspace_bytes);
+    if (st || T == 0 || score_stride == 0) return st;
+    if (!q_idx || !w || !pools || !q_seq || !q_pos || !scores) return DSA_ERR_NULL;
+    if (!aligned(q_idx, 16) || !aligned(pools, 16) || !aligned(w, 16)) return DSA_ERR_ALIGN;
+    return hip_status(dsa_host::launch_scores_with_groups(*dims, q_idx, w, pools, *seqs, q_seq, q_pos, T,
+                                                          score_stride, scores, workspace, as_stream(stream)));
+}
+
+int dsa_topk_select_groups(const dsa_dims* dims, const float* scores, int32_t score_stride, const dsa_seqs* seqs,
+                           int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos, int32_t T,
+                           int32_t* pool_ids, int32_t* indices, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    int st = groups_common(dims, seqs, num_seqs, T, score_stride, workspace, workspace_bytes);
+    if (st || T == 0 || score_stride == 0) return st;
+    if (!scores || !q_seq || !q_pos || !indices) return DSA_ERR_NULL;
+    return hip_status(dsa_host::launch_topk_groups(*dims, scores, score_stride, *seqs, q_seq, q_pos, T, pool_ids,
+                                                   indices, workspace, as_stream(stream)));
+}
+
+int dsa_index_scores_select(const dsa_dims* dims, const uint16_t* q_idx, const float* w, const uint16_t* pools,
+                            const dsa_seqs* seqs, int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos,
+                            int32_t T, int32_t score_stride, float* scores, int32_t* pool_ids, int32_t* indices,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (T < 0 || score_stride < 0) return DSA_ERR_SIZE;
+    st = check_seqs(seqs, num_seqs, true, false, true);
+    if (st) return st;
+    if (dims->kpool != 4 || !dsa_host::topk_supported(*dims, score_stride)) return DSA_ERR_UNSUPPORTED;
+    if (T == 0 || score_stride == 0) return DSA_OK;
+    if (T > 65535) return DSA_ERR_SIZE;
+    if (!q_idx || !w || !pools || !q_seq || !q_pos || !scores || !indices) return DSA_ERR_NULL;
+    if (!aligned(q_idx, 16) || !aligned(pools, 16) || !aligned(w, 16)) return DSA_ERR_ALIGN;
+    const size_t need = dsa_index_scores_select_workspace_bytes(dims, T, score_stride);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return DSA_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return DSA_ERR_ALIGN;
+    }
+    hipStream_t s = as_stream(stream);
+    if (dsa_host::scores_select_grouped(*dims, T, score_stride)) {
+        hipError_t e = dsa_host::launch_scores_with_groups(*dims, q_idx, w, pools, *seqs, q_seq, q_pos, T,
+                                                           score_stride, scores, workspace, s);
+        if (e != hipSuccess) return DSA_ERR_HIP;
+        return hip_status(dsa_host::launch_topk_groups(*dims, scores, score_stride, *seqs, q_seq, q_pos, T,
+                                                       pool_ids, indices, workspace, s));
+    }
+    hipError_t e = dsa_host::launch_index_scores(*dims, q_idx, w, pools, *seqs, q_seq, q_pos, T, score_stride,
+                                                 scores, s);
+    if (e != hipSuccess) return DSA_ERR_HIP;
+    return hip_status(dsa_host::launch_topk(*dims, scores, score_stride, *seqs, q_seq, q_pos, T, pool_ids,
+                                            indices, workspace, s));
+}
+
 int dsa_expand_selection(const dsa_dims* dims, const int32_t* pool_ids, const dsa_seqs* seqs,
                          int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos, int32_t T,
                          int32_t* indices, void* stream) {

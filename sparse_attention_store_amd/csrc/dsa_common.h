@@ -47,6 +47,39 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// ---------------------------------------------------------------- DPP wave scans (integers)
+// Inclusive scans over the 64 lanes with row shifts and row broadcasts: a
+// handful of VALU operations instead of cross-lane shuffles through the LDS
+// pipe.  Lanes whose source lies outside the row read the identity.
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x, uint32_t identity) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)x, CTRL, ROW_MASK, 0xF, false);
+}
+
+template <class Op>
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x, uint32_t identity, Op op) {
+    x = op(x, dpp_u32<0x111, 0xF>(x, identity));      // row_shr:1
+    x = op(x, dpp_u32<0x112, 0xF>(x, identity));      // row_shr:2
+    x = op(x, dpp_u32<0x114, 0xF>(x, identity));      // row_shr:4
+    x = op(x, dpp_u32<0x118, 0xF>(x, identity));      // row_shr:8
+    x = op(x, dpp_u32<0x142, 0xA>(x, identity));      // row_bcast:15 into rows 1 and 3
+    x = op(x, dpp_u32<0x143, 0xC>(x, identity));      // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+__device__ __forceinline__ uint32_t wave_incl_sum_u32(uint32_t x) {
+    return wave_incl_scan_u32(x, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+    return __builtin_amdgcn_readlane(
+        wave_incl_scan_u32(x, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; }), 63);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+    return __builtin_amdgcn_readlane(
+        wave_incl_scan_u32(x, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return a < b ? a : b; }), 63);
+}
+
 // ---------------------------------------------------------------- ordering keys
 // Order-preserving map from fp32 to uint32 (larger float -> larger key),
 // with -0 mapped onto +0 so the two compare equal.
@@ -88,19 +121,14 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Exclusive prefix sum of one uint32 per thread over a block of NT threads.
 // `sh` must hold NT / 64 + 1 entries.  Returns the exclusive prefix; *total
-// receives the block total.  Wave totals go through LDS once; every thread then
-// adds the totals of the waves before its own (no serial step).  Contains two
-// LDS barriers.
+// receives the block total.  Waves scan with DPP; wave totals go through LDS
+// once and every thread adds the totals of the waves before its own.
+// Contains two LDS barriers.
 template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* sh, uint32_t* total) {
     constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o, kWave);
-        if (lane >= o) x += y;
-    }
+    const uint32_t x = wave_incl_sum_u32(v);
     if (lane == 63) sh[wave] = x;
     lds_barrier();
     uint32_t before = 0, all = 0;

@@ -14,6 +14,7 @@
 // reused (MFMA bound).
 #include "dsa_common.h"
 #include "dsa_launch.h"
+#include "topk_core.h"
 
 namespace dsa {
 
@@ -150,13 +151,18 @@ __global__ __launch_bounds__(WAVES * 64) void k_scores_mfma(
 // once.  Each wave runs two 32-pool N-tiles of the tile.  Pools past a
 // query's visible count are written as -inf, by the partial tile and by a
 // final fill of [tiles*256, stride).
+// With CANDS, each wave also keeps its 64-pool group's best m pools for the
+// selection (keep_group_best), for queries with more visible pools than
+// select_k.
 constexpr int kDecTile = 256;
 constexpr int kDecMaxT = 64;
+template <bool CANDS>
 __global__ __launch_bounds__(256) void k_scores_decode(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint16_t* __restrict__ pools, const int32_t* __restrict__ first_valid,
     const int64_t* __restrict__ pool_base, const int32_t* __restrict__ q_seq,
-    const int32_t* __restrict__ q_pos, int T, int stride, float* __restrict__ scores) {
+    const int32_t* __restrict__ q_pos, int T, int stride, float* __restrict__ scores,
+    int select_k, uint64_t* __restrict__ cand, int32_t* __restrict__ cand_n) {
     __shared__ u32x4 tile[kDecTile * 16];
     __shared__ int s_first[kDecMaxT + 1];     // first flat tile of each query
     __shared__ int s_nvis[kDecMaxT];
@@ -250,6 +256,13 @@ __global__ __launch_bounds__(256) void k_scores_decode(
         }
         const int p = p0 + wave * 64 + g * 32 + n;            // lanes 0-31: N-tile 0, 32-63: N-tile 1
         if (p < stride) scores[(int64_t)t * stride + p] = p < n_vis ? sc[g] : -INFINITY;
+        if constexpr (CANDS) {
+            const int nn = min(n_vis, stride);
+            if (nn > select_k)                                  // lane order is id order
+                keep_group_best(sc[g], p < nn, p, p / kGroupPools, group_quota(select_k, nn),
+                                cand + (int64_t)t * kGroupCandCap, cand_n + (int64_t)t * kMaxGroups,
+                                [](uint64_t* q, uint64_t v) { *q = v; }, [](int32_t* q, uint32_t v) { *q = (int32_t)v; });
+        }
     }
     // Pools past the last visible tile of each query.
     for (int t = 0; t < T; ++t) {
@@ -303,8 +316,9 @@ hipError_t launch_index_scores(const dsa_dims& d, const uint16_t* q_idx, const f
             // Decode: persistent, two 64 KB-LDS workgroups per CU over a flat tile list.
             const int64_t tiles = cdiv(stride, dsa::kDecTile) * (int64_t)T;
             const int grid = (int)std::min<int64_t>(tiles, 2 * (int64_t)device_info().cu_count);
-            hipLaunchKernelGGL(dsa::k_scores_decode, dim3((unsigned)grid), dim3(256), 0, s, q_idx, w, pools,
-                               seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, stride, scores);
+            hipLaunchKernelGGL((dsa::k_scores_decode<false>), dim3((unsigned)grid), dim3(256), 0, s, q_idx, w,
+                               pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, stride, scores, 0,
+                               nullptr, nullptr);
         } else {
             // Prefill: 512 resident pools per workgroup, 64 queries per workgroup.
             const int qpb = 64;
@@ -318,6 +332,31 @@ hipError_t launch_index_scores(const dsa_dims& d, const uint16_t* q_idx, const f
                            seqs.first_valid, seqs.pool_base, q_seq, q_pos, d.idx_heads, d.idx_dim,
                            stride, scores);
     }
+    return hipGetLastError();
+}
+
+bool scores_select_grouped(const dsa_dims& d, int32_t T, int32_t stride) {
+    return d.idx_heads == dsa::kHI && d.idx_dim == dsa::kDI && T <= dsa::kDecMaxT && d.kpool == 4 &&
+           stride <= dsa::kMaxGroups * dsa::kGroupPools && d.index_topk / d.kpool <= dsa::kGroupMaxK;
+}
+
+size_t scores_select_group_bytes(int32_t T) {
+    return ((size_t)T * dsa::kGroupCandCap * 8 + 255) / 256 * 256 + ((size_t)T * dsa::kMaxGroups * 4 + 255) / 256 * 256;
+}
+
+hipError_t launch_scores_with_groups(const dsa_dims& d, const uint16_t* q_idx, const float* w,
+                                     const uint16_t* pools, const dsa_seqs& seqs, const int32_t* q_seq,
+                                     const int32_t* q_pos, int32_t T, int32_t stride, float* scores, void* ws,
+                                     hipStream_t s) {
+    if (T == 0 || stride == 0) return hipSuccess;
+    uint64_t* cand = reinterpret_cast<uint64_t*>(ws);
+    int32_t* cand_n = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) +
+                                                 ((size_t)T * dsa::kGroupCandCap * 8 + 255) / 256 * 256);
+    const int64_t tiles = cdiv(stride, dsa::kDecTile) * (int64_t)T;
+    const int grid = (int)std::min<int64_t>(tiles, 2 * (int64_t)device_info().cu_count);
+    hipLaunchKernelGGL((dsa::k_scores_decode<true>), dim3((unsigned)grid), dim3(256), 0, s, q_idx, w, pools,
+                       seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, stride, scores, d.index_topk / d.kpool,
+                       cand, cand_n);
     return hipGetLastError();
 }
 

@@ -169,8 +169,7 @@ __global__ __launch_bounds__(kBNT) void k_topk_rows(
     const float* __restrict__ scores, const int32_t* __restrict__ first_valid,
     const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int stride, int select_k,
     int64_t cap, int ntiles_max, const uint64_t* __restrict__ cand, const int32_t* __restrict__ cand_n, Emit e) {
-    __shared__ SelShared<kBNT> S;
-    __shared__ uint32_t mm_sh[2 * kBNT / 64];
+    __shared__ TopSelShared<kBNT, KPT> T;
     __shared__ int32_t sel[kMaxK];
     __shared__ uint32_t tpicked[kMaxTiles];
     __shared__ int fail;
@@ -204,21 +203,12 @@ __global__ __launch_bounds__(kBNT) void k_topk_rows(
             id[j] = (int32_t)(0xFFFFFFFFu - (uint32_t)v);
         }
     }
-    uint32_t lo, hi, krem;
-    bool whole;
-    bucket_select<kBNT, KPT, uint32_t>(key, (uint32_t)select_k, S, mm_sh, lo, hi, krem, whole);
-    uint32_t take;
-    uint32_t pos = compaction_slot<kBNT, KPT, uint32_t>(key, lo, hi, krem, whole, S, take);
-    uint32_t picks = 0u;                                     // bit j: slot s0 + j selected
+    const uint32_t picks = select_top_slots<kBNT, KPT>(key, (uint32_t)select_k, T);
+    uint32_t total;
+    uint32_t pos = block_exclusive_scan<kBNT>((uint32_t)__popc(picks), T.S.scan, &total);
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-        const uint32_t k = key[j];
-        const bool inr = k >= lo && k <= hi;
-        const bool pk = k > hi || (inr && take > 0);
-        take -= (inr && take > 0) ? 1u : 0u;
-        picks |= pk ? (1u << j) : 0u;
-        if (pk) atomicAdd(&tpicked[(s0 + j) >> msh], 1u);
-    }
+    for (int j = 0; j < KPT; ++j)
+        if ((picks >> j) & 1u) atomicAdd(&tpicked[(s0 + j) >> msh], 1u);
     lds_barrier();
     // A tile that dropped pools and had all m kept ones selected cannot vouch
     // for the pools it dropped.
@@ -226,7 +216,7 @@ __global__ __launch_bounds__(kBNT) void k_topk_rows(
         if ((cn[c] & kIncomplete) && tpicked[c] == (uint32_t)m) fail = 1;
     lds_barrier();
     if (fail) {
-        topk_stream_exact(scores + (int64_t)t * stride, n, select_k, S, sel);
+        topk_stream_exact(scores + (int64_t)t * stride, n, select_k, T.S, sel);
     } else {
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
@@ -239,9 +229,93 @@ __global__ __launch_bounds__(kBNT) void k_topk_rows(
     emit_selection<kBNT>(sel, select_k, select_k, t, b, f, qp, n_vis, e);
 }
 
+// Stage B over 64-pool group lists written by the scoring pass (one
+// 1024-thread workgroup per row; 8 slots per thread).
+__global__ __launch_bounds__(kBNT) void k_topk_groups(
+    const float* __restrict__ scores, const int32_t* __restrict__ first_valid,
+    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int stride, int select_k,
+    const uint64_t* __restrict__ cand, const int32_t* __restrict__ cand_n, Emit e) {
+    constexpr int KPT = kGroupCandCap / kBNT;
+    __shared__ TopSelShared<kBNT, KPT> T;
+    __shared__ int32_t sel[kGroupMaxK];
+    __shared__ uint32_t gcount[kMaxGroups];
+    __shared__ uint32_t gpicked[kMaxGroups];
+    __shared__ int fail;
+    const int t = blockIdx.x, tid = threadIdx.x;
+    int b, f, qp, n_vis;
+    query_geom(first_valid, q_seq, q_pos, t, b, f, qp, n_vis);
+    const int n = min(n_vis, stride);
+    if (n <= select_k) {
+        emit_selection<kBNT>(nullptr, n, select_k, t, b, f, qp, n_vis, e);
+        return;
+    }
+    const int groups = (n + kGroupPools - 1) / kGroupPools;
+    const int m = group_quota(select_k, n);
+    const int msh = __ffs(m) - 1;
+    const int M = groups * m;
+    const int s0 = tid * KPT;
+    // every load at once: this thread's group count and its KPT slots
+    const uint32_t gc = tid < groups ? (uint32_t)cand_n[(int64_t)t * kMaxGroups + tid] : 0u;
+    uint64_t raw[KPT];
+    const u32x4* src = reinterpret_cast<const u32x4*>(cand + (int64_t)t * kGroupCandCap + s0);
+#pragma unroll
+    for (int j = 0; j < KPT; j += 2) {
+        const u32x4 v = src[j / 2];
+        raw[j] = ((uint64_t)v[1] << 32) | v[0];
+        raw[j + 1] = ((uint64_t)v[3] << 32) | v[2];
+    }
+    gcount[tid] = gc;
+    gpicked[tid] = 0u;
+    if (tid == 0) fail = 0;
+    lds_barrier();
+    uint32_t key[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int sl = s0 + j;
+        const bool ok = sl < M && (sl & (m - 1)) < (int)(gcount[sl >> msh] & (kGroupDropped - 1));
+        key[j] = ok ? (uint32_t)(raw[j] >> 32) : 0u;
+    }
+    const uint32_t picks = select_top_slots<kBNT, KPT>(key, (uint32_t)select_k, T);
+    uint32_t total;
+    uint32_t pos = block_exclusive_scan<kBNT>((uint32_t)__popc(picks), T.S.scan, &total);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+        if ((picks >> j) & 1u) atomicAdd(&gpicked[(s0 + j) >> msh], 1u);
+    lds_barrier();
+    if (tid < groups && (gcount[tid] & kGroupDropped) && gpicked[tid] == (uint32_t)m) fail = 1;
+    lds_barrier();
+    if (fail) {
+        topk_stream_exact(scores + (int64_t)t * stride, n, select_k, T.S, sel);
+    } else {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            if ((picks >> j) & 1u) {
+                if (pos < (uint32_t)kGroupMaxK) sel[pos] = (int32_t)(0xFFFFFFFFu - (uint32_t)raw[j]);
+                ++pos;
+            }
+        }
+    }
+    lds_barrier();
+    emit_selection<kBNT>(sel, select_k, select_k, t, b, f, qp, n_vis, e);
+}
+
 }  // namespace dsa
 
 namespace dsa_host {
+
+hipError_t launch_topk_groups(const dsa_dims& d, const float* scores, int32_t stride, const dsa_seqs& seqs,
+                              const int32_t* q_seq, const int32_t* q_pos, int32_t T, int32_t* pool_ids,
+                              int32_t* indices, const void* ws, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const uint64_t* cand = reinterpret_cast<const uint64_t*>(ws);
+    const int32_t* cand_n = reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(ws) +
+                                                             ((size_t)T * dsa::kGroupCandCap * 8 + 255) / 256 * 256);
+    const dsa::Emit e{pool_ids, indices, seqs.row_base, d.out_width};
+    hipLaunchKernelGGL(dsa::k_topk_groups, dim3((unsigned)T), dim3(dsa::kBNT), 0, s, scores, seqs.first_valid,
+                       q_seq, q_pos, stride, d.index_topk / d.kpool, cand, cand_n, e);
+    return hipGetLastError();
+}
+
 
 static int topk_tiles(int32_t stride) { return (int)cdiv(stride, dsa::kTile); }
 

@@ -74,11 +74,16 @@ __device__ __forceinline__ void block_min_max(const KT (&key)[KPT], KT* sh, KT& 
         if (key[j]) mn = key[j] < mn ? key[j] : mn;
         mx = key[j] > mx ? key[j] : mx;
     }
+    if constexpr (sizeof(KT) == 4) {
+        mn = wave_min_u32(mn);
+        mx = wave_max_u32(mx);
+    } else {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const KT a = shfl_xor_k(mn, o), c = shfl_xor_k(mx, o);
-        mn = a < mn ? a : mn;
-        mx = c > mx ? c : mx;
+        for (int o = 32; o > 0; o >>= 1) {
+            const KT a = shfl_xor_k(mn, o), c = shfl_xor_k(mx, o);
+            mn = a < mn ? a : mn;
+            mx = c > mx ? c : mx;
+        }
     }
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) { sh[2 * w] = mn; sh[2 * w + 1] = mx; }
@@ -167,6 +172,187 @@ __device__ __forceinline__ uint32_t compaction_slot(const KT (&key)[KPT], KT lo,
         take = krem > base ? min(krem - base, in) : 0u;
     }
     return block_exclusive_scan<NT>(gt + take, S.scan, &total);
+}
+
+// ---------------------------------------------------------------- 64-pool group candidates
+// A scoring pass can keep, for each 64-pool group (one wave), its best m
+// pools by (score desc, id asc); the union of the group lists holds the top-K
+// unless a group that dropped pools has all m kept ones selected, which the
+// selection checks (falling back to an exact select over the scores).
+constexpr int kGroupPools = 64;
+constexpr int kMaxGroups = 1024;          // 65,536 pools per row
+constexpr int kGroupCandCap = 8192;       // kept entries per row
+constexpr int kGroupMaxK = 512;
+constexpr int kGroupDropped = 1 << 30;    // group count flag: the group dropped pools
+
+// Kept entries per group for a row of n visible pools (n > K): a power of two
+// >= lambda + 5 sqrt(lambda) + 4, lambda = 64 K / n being a group's mean share
+// of the K (so a group needing more than m is a > 5-sigma event); at least 8,
+// at most 64 and at most kGroupCandCap / groups.
+__device__ __forceinline__ int group_quota(int K, int n) {
+    const int groups = (n + kGroupPools - 1) / kGroupPools;
+    const float lam = 64.0f * (float)K / (float)n;
+    const float want = lam + 5.0f * sqrtf(lam) + 4.0f;
+    int m = 8;
+    while ((float)m < want && m < kGroupPools) m <<= 1;
+    while (m > 8 && groups * m > kGroupCandCap) m >>= 1;
+    return m;
+}
+
+// One wave's group: lanes hold consecutive pools p (lane order = id order),
+// `valid` for visible ones.  Writes the group's best m (key << 32 | ~p) in id
+// order to cand[group * m ..] and the count (| kGroupDropped when more than m
+// were valid) to cand_n[group].  The m-th largest key is found with 32
+// ballot-and-popcount steps; ties at it go to the lowest ids.  Store is the
+// memory policy for the two writes.
+template <class Store64, class Store32>
+__device__ __forceinline__ void keep_group_best(float s, bool valid, int p, int group, int m, uint64_t* cand,
+                                                int32_t* cand_n, Store64 st64, Store32 st32) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t key = valid ? f32_key(s) : 0u;
+    const int nvalid = __popcll(__ballot(valid));
+    bool pick = valid;
+    if (nvalid > m) {
+        uint32_t x = 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t y = x | (1u << bit);
+            if (__popcll(__ballot(key >= y)) >= m) x = y;
+        }
+        const unsigned long long eqm = __ballot(key == x);
+        const int above = __popcll(__ballot(key > x));
+        const int eq_before = __popcll(eqm & ((1ull << lane) - 1ull));
+        pick = key > x || (key == x && eq_before < m - above);
+    }
+    const unsigned long long pm = __ballot(pick);
+    const int slot = __popcll(pm & ((1ull << lane) - 1ull));
+    if (pick) st64(cand + (int64_t)group * m + slot, ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)p));
+    if (lane == 0) st32(cand_n + group, (uint32_t)(__popcll(pm) | (nvalid > m ? kGroupDropped : 0)));
+}
+
+// ---------------------------------------------------------------- exact top-K of register keys
+
+// Exact top `target` of register keys (0 = absent) under (key descending,
+// slot ascending), slot = threadIdx.x * KPT + j, i.e. ties go to the earlier
+// slot.  Range bucketing narrows [lo, hi] to the bucket holding rank target
+// and stops as soon as that bucket holds at most kBoundCap keys; those are
+// ranked exactly by one wave (each compares itself with all of them), so a
+// selection usually takes one or two histogram passes.  A bucket of more than
+// kBoundCap equal keys is taken in slot order by a block scan.  Returns this
+// thread's selected slots as a bitmask.
+constexpr int kBoundCap = 64;
+
+template <int NT, int KPT>
+struct TopSelShared {
+    SelShared<NT> S;
+    uint32_t mm[2 * NT / 64];
+    uint32_t nb;
+    uint32_t bkey[kBoundCap];
+    uint32_t bslot[kBoundCap];
+    uint32_t flag[(NT * KPT + 31) / 32];
+};
+
+template <int NT, int KPT>
+__device__ __forceinline__ uint32_t select_top_slots(const uint32_t (&key)[KPT], uint32_t target,
+                                                     TopSelShared<NT, KPT>& T) {
+    constexpr int BITS = log2_of<NT>();
+    constexpr int FW = (NT * KPT + 31) / 32;
+    const int tid = threadIdx.x;
+    T.S.hist[0][tid] = 0u;
+    T.S.hist[1][tid] = 0u;
+    for (int i = tid; i < FW; i += NT) T.flag[i] = 0u;
+    if (tid == 0) T.nb = 0u;
+    uint32_t lo, hi;
+    block_min_max<NT, KPT, uint32_t>(key, T.mm, lo, hi);     // its barriers publish the clears
+    uint32_t krem = target, cnt = 0xFFFFFFFFu;
+    bool whole = false;
+    for (int pass = 0; pass < 4 && lo < hi && cnt > (uint32_t)kBoundCap; ++pass) {
+        const int buf = pass & 1;
+        const int sh = bit_len<uint32_t>((hi - lo) >> BITS);
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const uint32_t k = key[j];
+            if (k >= lo && k <= hi) atomicAdd(&T.S.hist[buf][(k - lo) >> sh], 1u);
+        }
+        lds_barrier();
+        const uint32_t h = T.S.hist[buf][NT - 1 - tid];       // thread order = descending buckets
+        T.S.hist[buf ^ 1][tid] = 0u;
+        uint32_t total;
+        const uint32_t above = block_exclusive_scan<NT>(h, T.S.scan, &total);
+        if (above < krem && krem <= above + h) {
+            T.S.bin[buf] = NT - 1 - tid;
+            T.S.above[buf] = above;
+            T.S.cnt[buf] = h;
+        }
+        lds_barrier();
+        krem -= T.S.above[buf];
+        cnt = T.S.cnt[buf];
+        const uint32_t nlo = lo + (T.S.bin[buf] << sh);
+        const uint32_t nhi = nlo + ((1u << sh) - 1u);
+        lo = nlo;
+        hi = nhi < hi ? nhi : hi;
+        if (cnt == krem) {
+            whole = true;
+            break;
+        }
+    }
+    if (lo == hi && cnt == 0xFFFFFFFFu) {                    // every present key equal (or one key)
+        uint32_t c = 0;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) c += key[j] == lo ? 1u : 0u;
+        uint32_t tot;
+        block_exclusive_scan<NT>(c, T.S.scan, &tot);
+        cnt = tot;
+        whole = tot == krem;
+    }
+    uint32_t picks = 0u;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+        if (key[j] > hi || (whole && key[j] != 0u && key[j] >= lo && key[j] <= hi)) picks |= 1u << j;
+    if (whole) return picks;
+    if (cnt <= (uint32_t)kBoundCap) {
+        // gather the boundary bucket and rank it in one wave
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            if (key[j] != 0u && key[j] >= lo && key[j] <= hi) {
+                const uint32_t e = atomicAdd(&T.nb, 1u);
+                T.bkey[e] = key[j];
+                T.bslot[e] = (uint32_t)(tid * KPT + j);
+            }
+        }
+        lds_barrier();
+        const uint32_t nb = T.nb;
+        if ((uint32_t)tid < nb) {
+            const uint32_t mk = T.bkey[tid], ms = T.bslot[tid];
+            uint32_t rank = 0;
+            for (uint32_t i = 0; i < nb; ++i) {
+                const uint32_t k = T.bkey[i];
+                rank += (k > mk || (k == mk && T.bslot[i] < ms)) ? 1u : 0u;
+            }
+            if (rank < krem) atomicOr(&T.flag[ms >> 5], 1u << (ms & 31));
+        }
+        lds_barrier();
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const uint32_t sl = (uint32_t)(tid * KPT + j);
+            if ((T.flag[sl >> 5] >> (sl & 31)) & 1u) picks |= 1u << j;
+        }
+    } else {
+        // more than kBoundCap equal keys (lo == hi): the first krem in slot order
+        uint32_t c = 0;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) c += (key[j] != 0u && key[j] == lo) ? 1u : 0u;
+        uint32_t tot;
+        const uint32_t before = block_exclusive_scan<NT>(c, T.S.scan, &tot);
+        uint32_t take = krem > before ? min(krem - before, c) : 0u;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            if (key[j] != 0u && key[j] == lo && take > 0u) {
+                picks |= 1u << j;
+                --take;
+            }
+        }
+    }
+    return picks;
 }
 
 }  // namespace dsa

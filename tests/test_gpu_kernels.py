@@ -367,3 +367,34 @@ def test_sparse_mla_tiny_fp32(dsa):
     wl = syn.tiny()
     valid = np.array([0, 1, 5, 19, 24, 16] * 3, dtype=np.int64)
     _mla_case(dsa, wl, len(valid), valid, 0)
+
+
+# ---------------------------------------------------------------- scoring with group lists
+
+def _scores_select_case(name, zero_q=False):
+    import dsa_harness
+    wl = syn.get(name)
+    dw = dsa_harness.DeviceWorkload(wl)
+    if zero_q:
+        dw.q_idx.zero_()                     # all-equal scores: every group certificate fails
+    dw.step_calls()                          # index_scores + topk_select_expand, one call each
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (dw.scores, dw.pool_ids, dw.indices)]
+    for x in (dw.pool_ids, dw.indices):
+        x.fill_(0x5A5A5A5A)
+    dw.scores.fill_(float("nan"))
+    dw.step_scores_select()
+    torch.cuda.synchronize()
+    for nm, a, b in zip(("scores", "pool_ids", "indices"), ref, (dw.scores, dw.pool_ids, dw.indices)):
+        assert torch.equal(a, b), nm
+
+
+@pytest.mark.parametrize("name", ["mini_decode", "mini_heavy", "decode_32k"])
+def test_index_scores_select_matches_separate_calls(dsa, name):
+    say(f"index_scores_select {name}")
+    _scores_select_case(name)
+
+
+def test_index_scores_select_forced_fallback(dsa):
+    say("index_scores_select with all-equal scores")
+    _scores_select_case("decode_32k", zero_q=True)
