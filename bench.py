@@ -261,8 +261,7 @@ def main():
     start.record(stream)
     for i in range(args.steps):
         r = i % R
-        dw.step_store(r)
-        dw.step_pools(r)
+        dw.step_append(r)
         ev_s[i].record(stream)
         if fused:
             dw.step_decode(r)
@@ -281,12 +280,11 @@ def main():
     # Per-stage breakdown (separate, untimed pass).
     stages = {}
     if fused:
-        names = ["store_int8", "index_pools", "decode_step"]
-        fns = [dw.step_store, dw.step_pools, dw.step_decode]
+        names = ["append_tokens", "decode_step"]
+        fns = [dw.step_append, dw.step_decode]
     else:
-        names = ["store_int8", "index_pools", "index_scores_groups", "topk_select_groups", "sparse_mla"]
-        fns = [dw.step_store, dw.step_pools, dw.step_scores_groups, lambda r: dw.step_select_groups(),
-               dw.step_attention]
+        names = ["append_tokens", "index_scores_groups", "topk_select_groups", "sparse_mla"]
+        fns = [dw.step_append, dw.step_scores_groups, lambda r: dw.step_select_groups(), dw.step_attention]
     n_b = min(args.steps, 50)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(n_b)]
     for i in range(n_b):

@@ -134,6 +134,17 @@ class DeviceWorkload:
             dsa.index_pools(self.dims, self.k, self.gate, self.ln_w, self.ln_b, self.seqs,
                             self.step_pool_begin, self.step_pool_end, self.step_max_pools, self.pools[r])
 
+    def step_append(self, r: int = 0):
+        """The step's new tokens (INT8 rows and completed pools) in one launch
+        (two calls when the latent rows and the indexer keys differ in dtype)."""
+        if self.latent_q.dtype != self.k.dtype:
+            self.step_store(r)
+            self.step_pools(r)
+            return
+        dsa.append_tokens(self.dims, self.latent_q, self.slots_q, self.caches[r], self.k, self.gate, self.ln_w,
+                          self.ln_b, self.seqs, self.step_pool_begin, self.step_pool_end, self.step_max_pools,
+                          self.pools[r])
+
     def step_scores(self, r: int = 0):
         dsa.index_scores(self.dims, self.q_idx, self.w, self.pools[r], self.seqs, self.q_seq, self.q_pos,
                          self.scores)
@@ -181,14 +192,12 @@ class DeviceWorkload:
 
     def step_fused(self, r: int = 0):
         """One pass of the whole path: the new tokens, then the fused decode launch."""
-        self.step_store(r)
-        self.step_pools(r)
+        self.step_append(r)
         self.step_decode(r)
 
     def step(self, r: int = 0):
         """One pass of the whole path over replica r."""
-        self.step_store(r)
-        self.step_pools(r)
+        self.step_append(r)
         self.step_scores_select(r)
         self.step_attention(r)
 

@@ -134,6 +134,24 @@ int dsa_index_pools(const dsa_dims* dims, const void* k, const void* gate, int k
                     int32_t max_pools, uint16_t* pools, void* stream);
 
 /*
+ * append_tokens -- a step's new tokens in one launch: exactly dsa_store_int8
+ * (latent, n, ld, slots, cache, cache_rows) followed by dsa_index_pools (k,
+ * gate, ln_w, ln_b, seqs, num_seqs, pool_begin, pool_end, max_pools, pools),
+ * with one dtype (DSA_BF16 or DSA_F32) for latent, k and gate.  The results
+ * are bit-identical to the two calls.  The two parts touch disjoint buffers:
+ * the pools are built from k and gate, not from the cache rows.
+ *   n == 0 skips the rows (latent, slots, cache may be NULL); max_pools == 0
+ *   skips the pools (k .. pools and seqs may be NULL).
+ * Supported: the union of the two calls' limits (latent_dim in {64, 128,
+ * 256, 512}; kpool 4, idx_dim in {32, 128}).
+ */
+int dsa_append_tokens(const dsa_dims* dims, int dtype, const void* latent, int64_t n, int64_t ld,
+                      const int64_t* slots, int8_t* cache, int64_t cache_rows, const void* k,
+                      const void* gate, const float* ln_w, const float* ln_b, const dsa_seqs* seqs,
+                      int32_t num_seqs, const int32_t* pool_begin, const int32_t* pool_end,
+                      int32_t max_pools, uint16_t* pools, void* stream);
+
+/*
  * index_scores -- [Ref] Functions (index_scores): matmul, ReLU, head-weighted
  * sum.  For query t (sequence q_seq[t], position q_pos[t]) and pool p:
  *   scores[t][p] = sum_h w[t][h] * max(0, q_idx[t][h] . pool[p])   for p < n_vis(t)

@@ -95,6 +95,8 @@ def lib() -> ctypes.CDLL:
             "dsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "dsa_store_int8": (ctypes.c_int, [DP, P, ctypes.c_int, I64, I64, P, P, I64, P]),
             "dsa_index_pools": (ctypes.c_int, [DP, P, P, ctypes.c_int, P, P, SP, I32, P, P, I32, P, P]),
+            "dsa_append_tokens": (ctypes.c_int, [DP, ctypes.c_int, P, I64, I64, P, P, I64, P, P, P, P, SP, I32,
+                                                 P, P, I32, P, P]),
             "dsa_index_scores": (ctypes.c_int, [DP, P, P, P, SP, I32, P, P, I32, I32, P, P]),
             "dsa_topk_workspace_bytes": (SZ, [DP, I32, I32]),
             "dsa_topk_select": (ctypes.c_int, [DP, P, I32, SP, I32, P, P, I32, P, P, SZ, P]),
@@ -162,7 +164,7 @@ def status_string(status: int) -> str:
 
 def store_int8(dims: Dims, latent: torch.Tensor, slots: torch.Tensor, cache: torch.Tensor, stream=None):
     """Quantise latent rows [n, D] (bf16/fp32) into INT8 rows of cache [rows, row_bytes] at slots."""
-    if latent.dim() != 2 or latent.stride(1) != 1:
+    if latent.dim() != 2 or (latent.shape[0] > 0 and latent.stride(1) != 1):
         raise ValueError("latent must be [n, D] with unit stride in D")
     if latent.dtype not in (torch.bfloat16, torch.float32) or not latent.is_cuda:
         raise TypeError("latent must be a bf16/fp32 device tensor")
@@ -192,6 +194,33 @@ def index_pools(dims: Dims, k: torch.Tensor, gate: torch.Tensor, ln_w: torch.Ten
         ctypes.byref(dims), k.data_ptr(), gate.data_ptr(), _dt(k), ln_w.data_ptr(), ln_b.data_ptr(),
         ctypes.byref(seqs._c()), seqs.num_seqs, pool_begin.data_ptr(), pool_end.data_ptr(),
         int(max_pools), pools.data_ptr(), _stream(stream)))
+
+
+def append_tokens(dims: Dims, latent: torch.Tensor, slots: torch.Tensor, cache: torch.Tensor,
+                  k: torch.Tensor, gate: torch.Tensor, ln_w: torch.Tensor, ln_b: torch.Tensor, seqs: Seqs,
+                  pool_begin: torch.Tensor, pool_end: torch.Tensor, max_pools: int, pools: torch.Tensor,
+                  stream=None):
+    """store_int8(latent, slots, cache) and index_pools(k, gate, ...) in one launch (one dtype for all)."""
+    if latent.dim() != 2 or (latent.shape[0] > 0 and latent.stride(1) != 1):
+        raise ValueError("latent must be [n, D] with unit stride in D")
+    if latent.dtype not in (torch.bfloat16, torch.float32) or not latent.is_cuda:
+        raise TypeError("latent must be a bf16/fp32 device tensor")
+    _check(slots, torch.int64, "slots")
+    _check(cache, torch.int8, "cache")
+    if slots.numel() != latent.shape[0]:
+        raise ValueError("slots must have one entry per latent row")
+    for name, t in (("k", k), ("gate", gate)):
+        _check(t, latent.dtype, name)
+    _check(ln_w, torch.float32, "ln_w")
+    _check(ln_b, torch.float32, "ln_b")
+    _check(pool_begin, torch.int32, "pool_begin")
+    _check(pool_end, torch.int32, "pool_end")
+    _check(pools, torch.bfloat16, "pools")
+    _raise("dsa_append_tokens", lib().dsa_append_tokens(
+        ctypes.byref(dims), _dt(latent), latent.data_ptr(), latent.shape[0], latent.stride(0), slots.data_ptr(),
+        cache.data_ptr(), cache.shape[0], k.data_ptr(), gate.data_ptr(), ln_w.data_ptr(), ln_b.data_ptr(),
+        ctypes.byref(seqs._c()), seqs.num_seqs, pool_begin.data_ptr(), pool_end.data_ptr(), int(max_pools),
+        pools.data_ptr(), _stream(stream)))
 
 
 def index_scores(dims: Dims, q_idx: torch.Tensor, w: torch.Tensor, pools: torch.Tensor, seqs: Seqs,

@@ -5,12 +5,12 @@
 //
 // Every workgroup (one per CU, 256 threads) claims tasks from one queue.  For
 // the query of rank r (queries ranked by decreasing length) the queue holds:
-//   * scoring tasks: 512 pools each.  A task's pools (128 KB) are loaded one
-//     task ahead into registers and staged through LDS, then scored in two
-//     256-pool halves exactly as k_scores_decode scores a tile; each 64-pool
-//     group (one wave of a half) then keeps its best m pools by (score desc,
-//     id asc): the m-th largest key is found with 32 ballot-and-popcount
-//     steps, no LDS;
+//   * scoring tasks: 512 pools each, two 64-pool groups per wave.  A wave
+//     loads its groups one task ahead straight into MFMA registers and scores
+//     each with the same per-wave group code as the standalone decode scoring
+//     kernel (so the two agree bit for bit); each group then keeps its best m
+//     pools by (score desc, id asc): the m-th largest key is found with 32
+//     ballot-and-popcount steps, no LDS;
 //   * one selection task (sparse queries only): the best K of the group
 //     lists, checked against the same certificate as the standalone top-k (a
 //     group that dropped pools must not have all m kept ones selected), with
@@ -41,6 +41,7 @@
 #include "dsa_common.h"
 #include "dsa_launch.h"
 #include "mla_core.h"
+#include "scores_core.h"
 #include "topk_core.h"
 
 namespace dsa {
@@ -115,7 +116,7 @@ __device__ __forceinline__ uint64_t ld_coh64(const void* p) {
 // (the bit the relaxed agent-scope atomic loads above carry).
 constexpr int kCachePolicySC1 = 16;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t coh_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+    return buffer_rsrc(base, bytes);
 }
 __device__ __forceinline__ u32x4 ld_coh128(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCachePolicySC1);
@@ -186,7 +187,6 @@ struct StepCombSmem {
 };
 
 union StepSmem {
-    u32x4 tile[kSTile * 16];
     StepSelSmem sel;
     MlaRowsSmem mla;
     StepCombSmem comb;
@@ -378,32 +378,22 @@ __global__ __launch_bounds__(kStepNT, 1) void k_decode_step(StepArgs a) {
         return __hip_atomic_fetch_add(&C->queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
 
-    // ---- scoring registers (one tile ahead)
-    u32x4 v[32];
-    u32x4 anext[8];
-    f32x4 wnext[4];
+    // ---- scoring registers: the wave's two 64-pool groups of a task and the
+    // task's query, loaded one task ahead (each group is reloaded as soon as
+    // its MFMAs have consumed it).
+    u32x4 v[2][16];
+    IdxQuery Q;
     auto is_tile = [&](int i) {
         if (i >= n_total) return false;
         int st, t, j;
         locate(i, st, t, j);
         return st == 0;
     };
-    auto prefetch = [&](int i) {
-        int st, t, j;
-        locate(i, st, t, j);
-        const int p0 = j * kSTile;
-        const int lim = min(plan.nvis[t] - p0, kSTile);
-        const u32x4* src = reinterpret_cast<const u32x4*>(a.pools + (plan.pbase[t] + p0) * 128);
-#pragma unroll
-        for (int k = 0; k < 32; ++k) {
-            const int id = tid + k * 256;
-            v[k] = (id >> 4) < lim ? src[id] : u32x4{0u, 0u, 0u, 0u};
-        }
-        const uint16_t* qrow = a.q_idx + ((int64_t)t * 32 + n) * 128 + g * 64;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) anext[j] = *reinterpret_cast<const u32x4*>(qrow + j * 8);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) wnext[k] = *reinterpret_cast<const f32x4*>(a.w + (int64_t)t * 32 + 8 * k + 4 * g);
+    // Pools p0 + 256 half + 64 wave .. +64 of query t (nothing when none is visible).
+    auto load_half = [&](int t, int p0, int half) {
+        const int g0 = uniform32(p0 + half * 256 + wave * 64);
+        const int lim = plan.nvis[t] - g0;
+        if (lim > 0) load_pool_group(a.pools + (plan.pbase[t] + g0) * kDI, lim, v[half]);
     };
 
     // ---- the task loop.  A run of consecutive scoring tasks is one inner loop
@@ -420,7 +410,13 @@ __global__ __launch_bounds__(kStepNT, 1) void k_decode_step(StepArgs a) {
         locate(cur, stage, t, jj);
         if (stage == 0) {
           uint32_t pending = 0;
-          prefetch(cur);
+          {
+            int st0, t0, j0;
+            locate(cur, st0, t0, j0);
+            load_half(t0, j0 * kSTile, 0);
+            load_half(t0, j0 * kSTile, 1);
+            load_idx_query(a.q_idx, a.w, t0, Q);
+          }
           if (tid == 0) pending = claim();
           while (true) {
             locate(cur, stage, t, jj);
@@ -430,53 +426,34 @@ __global__ __launch_bounds__(kStepNT, 1) void k_decode_step(StepArgs a) {
             lds_barrier();
             const bool nxt_tile = is_tile(nxt);
             if (tid == 0 && nxt_tile) pending = claim();
+            int nt = 0, np0 = 0;                               // the next task's query and first pool
+            if (nxt_tile) {
+                int st2, j2;
+                locate(nxt, st2, nt, j2);
+                np0 = j2 * kSTile;
+            }
             // ============================ scoring tile
             const int p0 = jj * kSTile;
             const int nvis = plan.nvis[t];
-            u32x4 areg[8];
-            f32x4 wv[4];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) areg[j] = anext[j];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) wv[k] = wnext[k];
-#pragma unroll
-            for (int k = 0; k < 32; ++k) {
-                const int id = tid + k * 256;
-                const int row = id >> 4;
-                sm.tile[row * 16 + ((id & 15) ^ (row & 15))] = v[k];
-            }
-            lds_barrier();
-            if (nxt_tile) prefetch(nxt);
             const int m = nvis > a.select_k ? group_quota(a.select_k, nvis) : 0;
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                float sc[2];
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    const int row = half * 256 + wave * 64 + nt * 32 + n;
-                    f32x16 acc = {};
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        acc = mfma32(as_bf16x8(areg[j]), as_bf16x8(sm.tile[row * 16 + ((g * 8 + j) ^ (row & 15))]),
-                                     acc);
-                    float s = 0.f;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) s += wv[r >> 2][r & 3] * fmaxf(acc[r], 0.f);
-                    sc[nt] = s + __shfl_xor(s, 32, 64);
+                const float s = score_pool_group(Q, v[half]);
+                if (nxt_tile) {
+                    load_half(nt, np0, half);
+                    if (half == 1) load_idx_query(a.q_idx, a.w, nt, Q);
                 }
-                // lane (g, n) holds pool p0 + half*256 + wave*64 + lane: lanes are in id order
+                // lane l holds pool p0 + half*256 + wave*64 + l: lanes are in id order
                 const int p = p0 + half * 256 + wave * 64 + lane;
-                const float s = sc[g];
                 const bool valid = p < nvis;
                 if (valid) st_coh32(a.scores + (int64_t)t * a.stride + p, __float_as_uint(s));
                 if (m > 0)
                     keep_group_best(s, valid, p, (p0 + half * 256) / kSGroup + wave, m,
                                     a.cand + (int64_t)t * kStepCandCap, a.cand_n + (int64_t)t * kStepMaxGroups,
-                                    [](uint64_t* q, uint64_t v) { st_coh64(q, v); },
-                                    [](int32_t* q, uint32_t v) { st_coh32(q, v); });
+                                    [](uint64_t* q, uint64_t x) { st_coh64(q, x); },
+                                    [](int32_t* q, uint32_t x) { st_coh32(q, x); });
             }
             if (nvis > a.select_k) publish(&C->tiles_done[t]);   // dense queries need no hand-off
-            lds_barrier();                                 // LDS reused by the next task
             cur = nxt;
             if (!nxt_tile) break;
           }

@@ -130,6 +130,39 @@ int dsa_index_pools(const dsa_dims* dims, const void* k, const void* gate, int k
                                                    as_stream(stream)));
 }
 
+int dsa_append_tokens(const dsa_dims* dims, int dtype, const void* latent, int64_t n, int64_t ld,
+                      const int64_t* slots, int8_t* cache, int64_t cache_rows, const void* k,
+                      const void* gate, const float* ln_w, const float* ln_b, const dsa_seqs* seqs,
+                      int32_t num_seqs, const int32_t* pool_begin, const int32_t* pool_end,
+                      int32_t max_pools, uint16_t* pools, void* stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (dtype != DSA_F32 && dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    const int D = dims->latent_dim;
+    if (D != 64 && D != 128 && D != 256 && D != 512) return DSA_ERR_UNSUPPORTED;
+    if (dims->kpool != 4 || (dims->idx_dim != 128 && dims->idx_dim != 32)) return DSA_ERR_UNSUPPORTED;
+    if (n < 0 || cache_rows < 0 || max_pools < 0) return DSA_ERR_SIZE;
+    if (n > 0) {
+        if (!latent || !slots || !cache) return DSA_ERR_NULL;
+        if (ld < D) return DSA_ERR_SIZE;
+        const size_t esz = dtype == DSA_F32 ? 4 : 2;
+        if (!aligned(latent, 16) || (ld * esz) % 16 != 0 || !aligned(cache, 16)) return DSA_ERR_ALIGN;
+    }
+    if (max_pools > 0) {
+        st = check_seqs(seqs, num_seqs, false, true, true);
+        if (st) return st;
+        if (num_seqs > 65535) return DSA_ERR_SIZE;
+        if (!k || !gate || !ln_w || !ln_b || !pool_begin || !pool_end || !pools) return DSA_ERR_NULL;
+        if (!aligned(k, 4) || !aligned(gate, 4) || !aligned(pools, 4)) return DSA_ERR_ALIGN;
+    }
+    if (n == 0 && max_pools == 0) return DSA_OK;
+    const dsa_seqs none{};
+    return hip_status(dsa_host::launch_append_tokens(*dims, dtype, latent, n, ld, slots, cache, k, gate, ln_w,
+                                                     ln_b, max_pools > 0 ? *seqs : none,
+                                                     max_pools > 0 ? num_seqs : 0, pool_begin, pool_end,
+                                                     max_pools, pools, as_stream(stream)));
+}
+
 int dsa_index_scores(const dsa_dims* dims, const uint16_t* q_idx, const float* w,
                      const uint16_t* pools, const dsa_seqs* seqs, int32_t num_seqs,
                      const int32_t* q_seq, const int32_t* q_pos, int32_t T, int32_t score_stride,

@@ -117,6 +117,35 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Raw buffer descriptor over [base, base + bytes) (both wave-uniform).  Loads
+// through it take the base from SGPRs and a 32-bit lane offset; lane offsets
+// past `bytes` read zero, but the SGPR offset is outside that check, so
+// callers keep every access in bounds themselves.
+// A value every lane of the wave holds, moved to SGPRs (the compiler cannot
+// always prove that a value read from LDS or derived from threadIdx is uniform).
+__device__ __forceinline__ int uniform32(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ uint64_t uniform64(uint64_t x) {
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(x >> 32)) << 32) |
+           (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    void* b = reinterpret_cast<void*>(uniform64(reinterpret_cast<uint64_t>(base)));
+    return __builtin_amdgcn_make_buffer_rsrc(b, (short)0, uniform32((int)bytes), 0x00020000);
+}
+// voff: the lane's byte offset; soff: a wave-uniform byte offset (SGPR).
+__device__ __forceinline__ u32x4 ld_buf128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+
+// Orders LDS writes of this wave before its later LDS reads of other lanes'
+// entries (no workgroup barrier).
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
 // ---------------------------------------------------------------- block scans
 
 // Exclusive prefix sum of one uint32 per thread over a block of NT threads.

@@ -18,6 +18,11 @@ hipError_t launch_index_pools(const dsa_dims& d, const void* k, const void* gate
                               int32_t num_seqs, const int32_t* pool_begin,
                               const int32_t* pool_end, int32_t max_pools, uint16_t* pools,
                               hipStream_t s);
+hipError_t launch_append_tokens(const dsa_dims& d, int dtype, const void* latent, int64_t n, int64_t ld,
+                                const int64_t* slots, int8_t* cache, const void* k, const void* gate,
+                                const float* ln_w, const float* ln_b, const dsa_seqs& seqs, int32_t num_seqs,
+                                const int32_t* pool_begin, const int32_t* pool_end, int32_t max_pools,
+                                uint16_t* pools, hipStream_t s);
 
 hipError_t launch_index_scores(const dsa_dims& d, const uint16_t* q_idx, const float* w,
                                const uint16_t* pools, const dsa_seqs& seqs, const int32_t* q_seq,

@@ -14,11 +14,12 @@
 // reused (MFMA bound).
 #include "dsa_common.h"
 #include "dsa_launch.h"
+#include "scores_core.h"
 #include "topk_core.h"
 
 namespace dsa {
 
-constexpr int kHI = 32, kDI = 128, kQROW = kDI + 8;   // padded LDS row (bf16 elements)
+constexpr int kQROW = kDI + 8;                        // padded LDS row (bf16 elements)
 constexpr int kQBYTES = kHI * kDI * 2;                // 8 KB per query
 
 template <int WAVES, int QB>
@@ -139,136 +140,83 @@ __global__ __launch_bounds__(WAVES * 64) void k_scores_mfma(
     }
 }
 
-// Decode kernel (persistent).  Work is a flat list of 256-pool tiles over all
-// queries (a query with n_vis pools has ceil(n_vis / 256) tiles), so ragged
-// lengths balance across the grid; each workgroup (4 waves) walks tiles
-// blockIdx.x, blockIdx.x + gridDim.x, ...  A tile (64 KB, contiguous in HBM)
-// is fetched with fully coalesced 16-byte loads -- consecutive lanes read
-// consecutive chunks, so each load instruction covers whole cache lines --
-// into registers one tile ahead (with the next query's A operand and head
-// weights), then stored to LDS with an XOR swizzle (chunk c of pool row r goes
-// to slot c ^ (r & 15)) so that the MFMA B-operand reads hit all 64 banks
-// once.  Each wave runs two 32-pool N-tiles of the tile.  Pools past a
-// query's visible count are written as -inf, by the partial tile and by a
-// final fill of [tiles*256, stride).
-// With CANDS, each wave also keeps its 64-pool group's best m pools for the
-// selection (keep_group_best), for queries with more visible pools than
-// select_k.
-constexpr int kDecTile = 256;
+// Decode kernel: one wave per 64-pool group.  The visible groups of all
+// queries form one flat list that the waves walk (wave w takes groups w,
+// w + W, ...); the grid is sized to be resident at once, so every wave reads
+// the queries' geometry (lane t: query t) while memory is still idle and
+// then issues its first group's loads -- 16 KB of pool rows straight into
+// MFMA B-operand registers, the query's A operand and head weights -- with
+// no LDS staging or barrier between a load and its MFMAs.  The visible index
+// thus streams from HBM as one wave of requests.  Rows past a query's visible
+// count inside its last group, and every pool after that group up to the row
+// stride, are written as -inf.
+// With CANDS, each wave also keeps its group's best m pools for the selection
+// (keep_group_best) when the query has more visible pools than select_k.
 constexpr int kDecMaxT = 64;
+struct QueryGeom {
+    int64_t base;      // pool_base of the query's sequence
+    uint32_t first;    // flat index of the query's first group
+    uint32_t ng;       // groups of visible pools
+    int32_t nn;        // visible pools, capped at the row stride
+    int32_t pad;
+};
 template <bool CANDS>
-__global__ __launch_bounds__(256) void k_scores_decode(
+__global__ __launch_bounds__(256, 4) void k_scores_groups(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint16_t* __restrict__ pools, const int32_t* __restrict__ first_valid,
     const int64_t* __restrict__ pool_base, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_pos, int T, int stride, float* __restrict__ scores,
     int select_k, uint64_t* __restrict__ cand, int32_t* __restrict__ cand_n) {
-    __shared__ u32x4 tile[kDecTile * 16];
-    __shared__ int s_first[kDecMaxT + 1];     // first flat tile of each query
-    __shared__ int s_nvis[kDecMaxT];
-    __shared__ int64_t s_base[kDecMaxT];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n = lane & 31, g = lane >> 5;
-
-    if (tid < 64) {
-        int nt = 0;
-        if (tid < T) {
-            const int b = q_seq[tid];
+    __shared__ QueryGeom s_geom[4][kDecMaxT];          // one table per wave
+    const int lane = threadIdx.x & 63;
+    const int gw = uniform32(blockIdx.x * 4 + (threadIdx.x >> 6));
+    const int W = gridDim.x * 4;
+    QueryGeom* geom = s_geom[threadIdx.x >> 6];
+    int total;
+    {
+        int nn = 0;                     // visible pools of query `lane`, capped at the stride
+        int64_t base = 0;
+        if (lane < T) {
+            const int b = q_seq[lane];
             const int f = first_valid[b];
-            const int qp = q_pos[tid];
-            const int nv = qp >= f ? (qp - f + 1) >> 2 : 0;
-            s_nvis[tid] = nv;
-            s_base[tid] = pool_base[b];
-            nt = (min(nv, stride) + kDecTile - 1) / kDecTile;
+            const int qp = q_pos[lane];
+            nn = min(qp >= f ? (qp - f + 1) >> 2 : 0, stride);
+            base = pool_base[b];
         }
-        int x = nt;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(x, o, 64);
-            if (lane >= o) x += y;
-        }
-        if (tid < T) s_first[tid] = x - nt;
-        if (tid == 63) s_first[kDecMaxT] = x;
+        const uint32_t ng = (uint32_t)(nn + kGroupPools - 1) / kGroupPools;
+        const uint32_t incl = wave_incl_sum_u32(ng);
+        geom[lane] = QueryGeom{base, incl - ng, ng, nn};
+        total = (int)__builtin_amdgcn_readlane(incl, 63);
     }
-    lds_barrier();
-    const int total = s_first[kDecMaxT];
-
-    auto locate = [&](int i, int& t, int& p0) {
-        int q = 0;
-        while (q + 1 < T && s_first[q + 1] <= i) ++q;
-        t = q;
-        p0 = (i - s_first[q]) * kDecTile;
-    };
-    u32x4 v[16];
-    u32x4 anext[8];
-    f32x4 wnext[4];
-    auto prefetch = [&](int i) {
-        int t, p0;
-        locate(i, t, p0);
-        const int lim = min(s_nvis[t] - p0, kDecTile);
-        const u32x4* src = reinterpret_cast<const u32x4*>(pools + (s_base[t] + p0) * kDI);
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int id = tid + k * 256;                    // row id >> 4, chunk id & 15
-            v[k] = (id >> 4) < lim ? src[id] : u32x4{0u, 0u, 0u, 0u};
-        }
-        // A operand: head n, k = g*64 + j*8 + e (chunk g*8 + j).  D rows: 8*(r/4) + 4*g + (r%4).
-        const uint16_t* qrow = q_idx + ((int64_t)t * kHI + n) * kDI + g * 64;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) anext[j] = *reinterpret_cast<const u32x4*>(qrow + j * 8);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) wnext[k] = *reinterpret_cast<const f32x4*>(w + (int64_t)t * kHI + 8 * k + 4 * g);
-    };
-
-    int i = blockIdx.x;
-    if (i < total) prefetch(i);
-    for (; i < total; i += gridDim.x) {
-        int t, p0;
-        locate(i, t, p0);
-        const int n_vis = s_nvis[t];
-        u32x4 areg[8];
-        f32x4 wv[4];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) areg[j] = anext[j];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) wv[k] = wnext[k];
-        lds_barrier();                                     // previous tile's LDS readers are done
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int id = tid + k * 256;
-            const int row = id >> 4;
-            tile[row * 16 + ((id & 15) ^ (row & 15))] = v[k];
-        }
-        if (i + (int)gridDim.x < total) prefetch(i + gridDim.x);
-        lds_barrier();
-        float sc[2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const int row = wave * 64 + nt * 32 + n;
-            f32x16 acc = {};
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                acc = mfma32(as_bf16x8(areg[j]), as_bf16x8(tile[row * 16 + ((g * 8 + j) ^ (row & 15))]), acc);
-            float s = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s += wv[r >> 2][r & 3] * fmaxf(acc[r], 0.f);
-            sc[nt] = s + __shfl_xor(s, 32, 64);
-        }
-        const int p = p0 + wave * 64 + g * 32 + n;            // lanes 0-31: N-tile 0, 32-63: N-tile 1
-        if (p < stride) scores[(int64_t)t * stride + p] = p < n_vis ? sc[g] : -INFINITY;
+    wave_lds_fence();
+    for (int gi = gw; gi < total; gi += W) {
+        // query of group gi: the number of queries whose groups all come before it
+        const int t = __popcll(__ballot(geom[lane].first + geom[lane].ng <= (uint32_t)gi));
+        const int64_t b0 = (int64_t)uniform64((uint64_t)geom[t].base);
+        const int grp = gi - uniform32((int)geom[t].first);
+        const int n_vis = uniform32(geom[t].nn);
+        const int p0 = grp * kGroupPools;
+        IdxQuery Q;
+        load_idx_query(q_idx, w, t, Q);
+        u32x4 v[16];
+        load_pool_group(pools + (b0 + p0) * kDI, n_vis - p0, v);
+        __builtin_amdgcn_sched_barrier(0);      // every load in flight before the first MFMA
+        const float s = score_pool_group(Q, v);
+        const int p = p0 + lane;
+        if (p < stride) scores[(int64_t)t * stride + p] = p < n_vis ? s : -INFINITY;
         if constexpr (CANDS) {
-            const int nn = min(n_vis, stride);
-            if (nn > select_k)                                  // lane order is id order
-                keep_group_best(sc[g], p < nn, p, p / kGroupPools, group_quota(select_k, nn),
+            if (n_vis > select_k)
+                keep_group_best(s, p < n_vis, p, grp, group_quota(select_k, n_vis),
                                 cand + (int64_t)t * kGroupCandCap, cand_n + (int64_t)t * kMaxGroups,
-                                [](uint64_t* q, uint64_t v) { *q = v; }, [](int32_t* q, uint32_t v) { *q = (int32_t)v; });
+                                [](uint64_t* q, uint64_t x) { *q = x; },
+                                [](int32_t* q, uint32_t x) { *q = (int32_t)x; });
         }
     }
-    // Pools past the last visible tile of each query.
+    // Pools past each query's last visible group.
     for (int t = 0; t < T; ++t) {
-        const int from = (s_first[t + 1 < T ? t + 1 : kDecMaxT] - s_first[t]) * kDecTile;
+        const int from = (int)geom[t].ng * kGroupPools;
         float* out = scores + (int64_t)t * stride;
-        for (int p = from + blockIdx.x * 256 + tid; p < stride; p += gridDim.x * 256) out[p] = -INFINITY;
+        for (int p = from + gw * kGroupPools + lane; p < stride; p += W * kGroupPools) out[p] = -INFINITY;
     }
 }
 
@@ -306,19 +254,24 @@ __global__ __launch_bounds__(256) void k_scores_generic(
 
 namespace dsa_host {
 
+// Workgroups (4 waves, one 64-pool group each) for k_scores_groups: every
+// group of every query if that fits, else 4 per CU, which stay resident.
+static unsigned scores_groups_grid(int32_t T, int32_t stride) {
+    const int64_t wgs = cdiv(cdiv(stride, dsa::kGroupPools) * (int64_t)T, 4);
+    return (unsigned)std::min<int64_t>(wgs, 4 * (int64_t)device_info().cu_count);
+}
+
 hipError_t launch_index_scores(const dsa_dims& d, const uint16_t* q_idx, const float* w,
                                const uint16_t* pools, const dsa_seqs& seqs, const int32_t* q_seq,
                                const int32_t* q_pos, int32_t T, int32_t stride, float* scores,
                                hipStream_t s) {
     if (T == 0 || stride == 0) return hipSuccess;
     if (d.idx_heads == dsa::kHI && d.idx_dim == dsa::kDI) {
-        if (T <= 64) {
-            // Decode: persistent, two 64 KB-LDS workgroups per CU over a flat tile list.
-            const int64_t tiles = cdiv(stride, dsa::kDecTile) * (int64_t)T;
-            const int grid = (int)std::min<int64_t>(tiles, 2 * (int64_t)device_info().cu_count);
-            hipLaunchKernelGGL((dsa::k_scores_decode<false>), dim3((unsigned)grid), dim3(256), 0, s, q_idx, w,
-                               pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, stride, scores, 0,
-                               nullptr, nullptr);
+        if (T <= dsa::kDecMaxT) {
+            // Decode: one wave per 64-pool group, a resident grid.
+            hipLaunchKernelGGL((dsa::k_scores_groups<false>), dim3(scores_groups_grid(T, stride)), dim3(256), 0, s,
+                               q_idx, w, pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, stride, scores,
+                               0, nullptr, nullptr);
         } else {
             // Prefill: 512 resident pools per workgroup, 64 queries per workgroup.
             const int qpb = 64;
@@ -352,11 +305,9 @@ hipError_t launch_scores_with_groups(const dsa_dims& d, const uint16_t* q_idx, c
     uint64_t* cand = reinterpret_cast<uint64_t*>(ws);
     int32_t* cand_n = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) +
                                                  ((size_t)T * dsa::kGroupCandCap * 8 + 255) / 256 * 256);
-    const int64_t tiles = cdiv(stride, dsa::kDecTile) * (int64_t)T;
-    const int grid = (int)std::min<int64_t>(tiles, 2 * (int64_t)device_info().cu_count);
-    hipLaunchKernelGGL((dsa::k_scores_decode<true>), dim3((unsigned)grid), dim3(256), 0, s, q_idx, w, pools,
-                       seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, stride, scores, d.index_topk / d.kpool,
-                       cand, cand_n);
+    hipLaunchKernelGGL((dsa::k_scores_groups<true>), dim3(scores_groups_grid(T, stride)), dim3(256), 0, s, q_idx,
+                       w, pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, stride, scores,
+                       d.index_topk / d.kpool, cand, cand_n);
     return hipGetLastError();
 }
 

@@ -59,12 +59,6 @@ __device__ __forceinline__ u32x4 codes8_to_biased_bf16(uint32_t a, uint32_t b) {
     return u32x4{r0, r1, r2, r3};
 }
 
-__device__ __forceinline__ void wave_lds_fence() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-}
-
 constexpr int kPLS = kRChunk + 8;     // bf16 per head row of P'
 
 struct MlaRowsSmem {

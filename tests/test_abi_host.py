@@ -85,6 +85,30 @@ def test_dims_validation(dsa):
     assert store(prod(dsa, ln_eps=-1.0)) == E_DIMS
 
 
+def test_append_tokens_argument_checks(dsa):
+    L = dsa.lib()
+    d = prod(dsa)
+    bd = ctypes.byref(d)
+    S = seqs(dsa)
+    call = lambda dt=1, lat=FAKE, n=4, ld=512, sl=FAKE, c=FAKE, k=FAKE, mp=2, sq=ctypes.byref(S), dims=bd: \
+        L.dsa_append_tokens(dims, dt, lat, n, ld, sl, c, 64, k, FAKE, FAKE, FAKE, sq, 2, FAKE, FAKE, mp, FAKE, None)
+    assert call(dims=None) == E_NULL
+    assert call(dims=ctypes.byref(prod(dsa, idx_heads=0))) == E_DIMS
+    assert call(dt=7) == E_DTYPE
+    assert call(dims=ctypes.byref(prod(dsa, latent_dim=96, row_bytes=112))) == E_UNSUP
+    assert call(dims=ctypes.byref(prod(dsa, idx_dim=64))) == E_UNSUP
+    assert call(n=-1) == E_SIZE
+    assert call(mp=-1) == E_SIZE
+    assert call(lat=None) == E_NULL
+    assert call(ld=500) == E_SIZE
+    assert call(lat=MISALIGNED) == E_ALIGN
+    assert call(k=None) == E_NULL
+    assert call(k=ctypes.c_void_p(0x10002)) == E_ALIGN          # k and gate need 4-byte alignment
+    assert call(sq=None) == E_NULL
+    # nothing to do: no launch, no pointer needed
+    assert call(n=0, mp=0, lat=None, sl=None, c=None, k=None, sq=None) == OK
+
+
 def test_store_int8_argument_checks(dsa):
     L = dsa.lib()
     d = prod(dsa)

@@ -166,6 +166,64 @@ def test_index_pools_partial_range_and_f32_state(dsa):
     assert np.all(got[pb:pb + 100] == 3.0) and np.all(got[pb + 357:] == 3.0)
 
 
+# ---------------------------------------------------------------- append_tokens
+
+@pytest.mark.parametrize("name,dt,rows,pools_on", [("mini_decode", torch.bfloat16, True, True),
+                                                   ("mini_prefill", torch.bfloat16, True, True),
+                                                   ("mini_decode", torch.float32, True, True),
+                                                   ("tiny_batch", torch.bfloat16, False, True),
+                                                   ("tiny_batch", torch.bfloat16, True, False)])
+def test_append_tokens_matches_separate_calls(dsa, name, dt, rows, pools_on):
+    """One launch of rows + pools gives the bytes of store_int8 then index_pools."""
+    wl = syn.get(name)
+    d = wl.dims
+    dims = dsa.Dims.of(d)
+    say(f"append_tokens {name} {dt} rows={rows} pools={pools_on}")
+    k = torch.zeros((wl.total_tokens, d.idx_dim), dtype=dt, device="cuda")
+    gate = torch.zeros_like(k)
+    for b in range(wl.B):
+        kk, gg = syn.gen_kgate(wl, b, 0, int(wl.seq_len[b]))
+        tb = int(wl.tok_base[b])
+        if dt == torch.float32:
+            k[tb:tb + kk.shape[0]] = torch.from_numpy(kk).cuda()
+            gate[tb:tb + gg.shape[0]] = torch.from_numpy(gg).cuda()
+        else:
+            k[tb:tb + kk.shape[0]] = dev_bf16(kk)
+            gate[tb:tb + gg.shape[0]] = dev_bf16(gg)
+    lw, lb = syn.gen_ln(wl)
+    lw, lb = torch.from_numpy(lw).cuda(), torch.from_numpy(lb).cuda()
+    ends = [wl.n_pools(b) for b in range(wl.B)] if pools_on else [0] * wl.B
+    begin = torch.tensor([max(e - 5, 0) for e in ends], dtype=torch.int32, device="cuda")
+    end = torch.tensor(ends, dtype=torch.int32, device="cuda")
+    max_pools = 5 if pools_on else 0
+    n = 37 if rows else 0
+    lat = syn.gen_latent(wl, 0, 0, max(n, 1))[:n]
+    lt = torch.from_numpy(lat).cuda() if dt == torch.float32 else dev_bf16(lat)
+    lt = lt.reshape(n, d.latent_dim)
+    nrows = 64
+    slots = torch.from_numpy(np.random.default_rng(3).permutation(nrows)[:n].astype(np.int64)).cuda()
+    npools = max(wl.total_pools, 1) + 3
+    outs = []
+    for fused in (False, True):
+        cache = torch.full((nrows, d.row_bytes), 0x5B, dtype=torch.int8, device="cuda")
+        pools = torch.full((npools, d.idx_dim), 7.0, dtype=torch.bfloat16, device="cuda")
+        if fused:
+            dsa.append_tokens(dims, lt, slots, cache, k, gate, lw, lb, seqs_of(dsa, wl), begin, end, max_pools, pools)
+        else:
+            if n:
+                dsa.store_int8(dims, lt, slots, cache)
+            if max_pools:
+                dsa.index_pools(dims, k, gate, lw, lb, seqs_of(dsa, wl), begin, end, max_pools, pools)
+        torch.cuda.synchronize()
+        outs.append((cache.cpu(), pools.view(torch.int16).cpu()))
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1])
+    if rows:
+        assert not torch.all(outs[1][0] == 0x5B)
+    if pools_on:
+        assert not torch.all(outs[1][1] == outs[1][1].flatten()[0])
+
+
 # ---------------------------------------------------------------- index_scores
 
 @pytest.mark.parametrize("name", ["tiny", "tiny_batch", "mini_decode", "mini_prefill"])
