@@ -59,15 +59,19 @@ __device__ __forceinline__ u32x4 codes8_to_biased_bf16(uint32_t a, uint32_t b) {
     return u32x4{r0, r1, r2, r3};
 }
 
-constexpr int kPLS = kRChunk + 8;     // bf16 per head row of P'
-
-struct MlaRowsSmem {
-    uint16_t kv[kRChunk * kRStride];     // the chunk's rows as bf16 (code + 128)
-    uint16_t pl[2][16 * kPLS];           // P' hi, lo: [head][row]
+// LDS of one split walking chunks of 64 * RT rows (4 waves of RT 16-row tiles).
+template <int RT>
+struct MlaRowsSmemT {
+    static constexpr int kRows = 64 * RT;
+    static constexpr int kPLS = kRows + 8;   // bf16 per head row of P'
+    uint16_t kv[kRows * kRStride];           // the chunk's rows as bf16 (code + 128)
+    uint16_t qs[16 * kRStride];              // the 16 heads of q, [head][dim]
+    uint16_t pl[2][16 * kPLS];               // P' hi, lo: [head][row]
     float red_max[4][16];
     float red_l[4][16];
     float red_p[4][16];
 };
+using MlaRowsSmem = MlaRowsSmemT<2>;         // 128-row chunks (kRChunk)
 
 
 // Output stores of a split: plain, or agent-coherent (relaxed agent-scope
@@ -98,14 +102,15 @@ __device__ __forceinline__ void store_partial(MlaPartial* p, MlaPartial v) {
 }
 
 // One split of k_mla_rows: query t, heads [head0, head0 + 16), list chunks
-// [c_begin, c_end) of kRChunk positions.  idx_at(pos) gives the cache row of
-// list position pos (< W), or a negative value for an empty slot.  COH makes
-// the partial results agent-coherent (read back by another workgroup of the
-// same launch) instead of plain stores.  Every thread of the block must call
-// it; it contains workgroup barriers.
-template <bool COH, class IdxFn>
+// [c_begin, c_end) of 64 * RT positions (each wave owns RT 16-row tiles of a
+// chunk).  idx_at(pos) gives the cache row of list position pos (< W), or a
+// negative value for an empty slot.  COH makes the partial results
+// agent-coherent (read back by another workgroup of the same launch) instead
+// of plain stores.  Every thread of the block must call it; it contains
+// workgroup barriers.
+template <int RT, bool COH, class IdxFn>
 __device__ __forceinline__ void mla_rows_split(
-    MlaRowsSmem& sm, const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, int row_bytes,
+    MlaRowsSmemT<RT>& sm, const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, int row_bytes,
     IdxFn idx_at, int W, int H, float scale_log2, int t, int head0, int split, int c_begin, int c_end,
     int splits, float* __restrict__ part_o, MlaPartial* __restrict__ part_ml, void* __restrict__ out,
     int out_f32, float* __restrict__ lse) {
@@ -113,23 +118,26 @@ __device__ __forceinline__ void mla_rows_split(
     const int n16 = lane & 15, g4 = lane >> 4;
     const int prow = row_of_slot(n16);            // row (within a 16-row tile) this lane loads
     const int srow = row_of_slot(4 * g4);         // first of the 4 rows this lane's S^T values cover
+    constexpr int CH = 64 * RT;                   // rows per chunk
+    constexpr int PLS = MlaRowsSmemT<RT>::kPLS;
+    constexpr int NKS = CH / 32;                  // 32-row k-steps of O^T += V^T P'^T
 
     auto load_idx = [&](int c, int* id) {
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            const int pos = c * kRChunk + 32 * w + 16 * rt + prow;
+        for (int rt = 0; rt < RT; ++rt) {
+            const int pos = c * CH + 16 * RT * w + 16 * rt + prow;
             id[rt] = pos < W ? idx_at(pos) : -1;
         }
     };
-    u32x4 raw[2][8];
-    float rsc[2];
+    u32x4 raw[RT][8];
+    float rsc[RT];
     auto load_rows = [&](const int* id) {
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
+        for (int rt = 0; rt < RT; ++rt) {
             if (id[rt] >= 0) {
                 const uint8_t* src = cache + (int64_t)id[rt] * row_bytes;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) raw[rt][i] = *reinterpret_cast<const u32x4*>(src + g4 * 128 + 16 * i);
+                for (int i = 0; i < 8; ++i) raw[rt][i] = *reinterpret_cast<const u32x4*>(src + 64 * i + 16 * g4);
                 rsc[rt] = *reinterpret_cast<const float*>(src + kD);
             } else {
 #pragma unroll
@@ -139,21 +147,37 @@ __device__ __forceinline__ void mla_rows_split(
         }
     };
 
-    // The dependent chain index -> row bytes goes first; Q loads overlap it.
-    int id_cur[2] = {-1, -1}, id_next[2] = {-1, -1};
+    // q (16 heads x 512, 16 KB) is read once per workgroup, 64 bytes per
+    // thread, and handed to the waves through LDS; its loads go out first and
+    // overlap the dependent chain index -> row bytes.
+    u32x4 qv[4];
+    {
+        const uint16_t* qh = q + ((int64_t)t * H + head0) * kD;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qv[i] = *reinterpret_cast<const u32x4*>(qh + 8 * (tid + 256 * i));
+    }
+    int id_cur[RT], id_next[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) id_cur[rt] = id_next[rt] = -1;
     if (c_begin < c_end) {
         load_idx(c_begin, id_cur);
         if (c_begin + 1 < c_end) load_idx(c_begin + 1, id_next);
         load_rows(id_cur);
     }
-
-    // Q^T operand (B of S^T): head head0 + n16, reduction index g4*128 + 8j + e.
-    u32x4 qb[16];
-    {
-        const uint16_t* qr = q + ((int64_t)t * H + head0 + n16) * kD + g4 * 128;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) qb[j] = *reinterpret_cast<const u32x4*>(qr + 8 * j);
+    for (int i = 0; i < 4; ++i) {
+        const int k = tid + 256 * i;                   // 16-byte piece k: head k / 64, dims 8 (k % 64) ..
+        *reinterpret_cast<u32x4*>(&sm.qs[(k >> 6) * kRStride + 8 * (k & 63)]) = qv[i];
     }
+    lds_barrier();
+
+    // Q^T operand (B of S^T): head head0 + n16, reduction index
+    // 64 (j/2) + 16 g4 + 8 (j%2) + e -- the bytes this lane holds of its row.
+    // (The padded head rows make these 16-byte LDS reads conflict free.)
+    u32x4 qb[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        qb[j] = *reinterpret_cast<const u32x4*>(&sm.qs[n16 * kRStride + 64 * (j >> 1) + 16 * g4 + 8 * (j & 1)]);
     // The K and V operands hold code + 128 (exact in bf16, one conversion per
     // code); the bias is removed afterwards: S -= 128 * sum_k q_k per head and
     // O -= 128 * sum_j P'_j over the same bf16 P' values the products used.
@@ -177,41 +201,53 @@ __device__ __forceinline__ void mla_rows_split(
         for (int u = 0; u < 4; ++u) acc[G][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     for (int c = c_begin; c < c_end; ++c) {
-        const bool live = __ballot(id_cur[0] >= 0 || id_cur[1] >= 0) != 0ull;
-        const float rs_now[2] = {rsc[0], rsc[1]};
-        f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        if (live) {
-            // ---- convert this wave's 32 rows, S^T = K Q^T (4 independent
-            //      accumulation chains), and stage the rows for V^T
-            f32x4 sc4[2][2];
+        // A wave with no row in the chunk skips its work.  With one tile per
+        // wave, a 32-row k-step of the PV product spans two waves, so every
+        // wave stages its rows (empty ones hold code 0 with P' = 0).
+        bool any = false;
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) sc4[rt][0] = sc4[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int rt = 0; rt < RT; ++rt) any = any || id_cur[rt] >= 0;
+        const bool live = RT == 1 || __ballot(any) != 0ull;
+        float rs_now[RT];
+        f32x4 s[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            rs_now[rt] = rsc[rt];
+            s[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        if (live) {
+            // ---- convert this wave's rows, S^T = K Q^T (2 RT independent
+            //      accumulation chains), and stage the rows for V^T
+            f32x4 sc4[RT][2];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) sc4[rt][0] = sc4[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
+                for (int rt = 0; rt < RT; ++rt) {
                     const u32x4 kb =
                         codes8_to_biased_bf16(raw[rt][j >> 1][(j & 1) * 2], raw[rt][j >> 1][(j & 1) * 2 + 1]);
                     sc4[rt][j & 1] = mfma16(as_bf16x8(kb), as_bf16x8(qb[j]), sc4[rt][j & 1]);
-                    *reinterpret_cast<u32x4*>(&sm.kv[(32 * w + 16 * rt + prow) * kRStride + g4 * 128 + 8 * j]) = kb;
+                    *reinterpret_cast<u32x4*>(
+                        &sm.kv[(16 * RT * w + 16 * rt + prow) * kRStride + 64 * (j >> 1) + 16 * g4 + 8 * (j & 1)]) = kb;
                 }
             }
-            s[0] = sc4[0][0] + sc4[0][1];
-            s[1] = sc4[1][0] + sc4[1][1];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) s[rt] = sc4[rt][0] + sc4[rt][1];
         }
         // ---- next chunk's rows in flight while this one computes
         if (c + 1 < c_end) {
             load_rows(id_next);
-            id_cur[0] = id_next[0];
-            id_cur[1] = id_next[1];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) id_cur[rt] = id_next[rt];
             if (c + 2 < c_end) load_idx(c + 2, id_next);
         }
 
         // ---- chunk max per head across the 4 waves (lane: head n16, rows slot 4*g4 + i)
-        float z[2][4], sc[2][4];
+        float z[RT][4], sc[RT][4];
         float cmax = -INFINITY;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 sc[rt][i] = __shfl(rs_now[rt], 4 * g4 + i, 64);
@@ -226,10 +262,17 @@ __device__ __forceinline__ void mla_rows_split(
 #pragma unroll
         for (int k = 0; k < 4; ++k) wmax[k] = sm.red_max[k][n16];
         const float chunk_max = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-        // Source waves with a live row: the same answer for every head.
-        bool src_live[4];
+        // k-steps with a live row (their source waves' maxima): the same
+        // answer for every head.
+        bool src_live[NKS];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) src_live[k] = __ballot(wmax[k] != -INFINITY) != 0ull;
+        for (int ks = 0; ks < NKS; ++ks) {
+            bool lv = false;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)                 // wave k's rows start at 16 RT k
+                if ((16 * RT * k) / 32 == ks) lv = lv || wmax[k] != -INFINITY;
+            src_live[ks] = __ballot(lv) != 0ull;
+        }
 
         // The running max is raised only when the chunk exceeds it by 2^8.
         const float m_new = (m_run == -INFINITY || chunk_max > m_run + kLazyMax) ? chunk_max : m_run;
@@ -245,9 +288,9 @@ __device__ __forceinline__ void mla_rows_split(
         m_run = m_new;
 
         // ---- P' = p * scale as bf16 hi + lo, to LDS as [head][row]
-        uint32_t bh[2][2], bl[2][2];
+        uint32_t bh[RT][2], bl[RT][2];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int i2 = 0; i2 < 2; ++i2) {
                 float x[2];
@@ -267,21 +310,21 @@ __device__ __forceinline__ void mla_rows_split(
             }
         if (live) {
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const int r0 = 32 * w + 16 * rt + srow;
-                *reinterpret_cast<u32x2*>(&sm.pl[0][n16 * kPLS + r0]) = u32x2{bh[rt][0], bh[rt][1]};
-                *reinterpret_cast<u32x2*>(&sm.pl[1][n16 * kPLS + r0]) = u32x2{bl[rt][0], bl[rt][1]};
+            for (int rt = 0; rt < RT; ++rt) {
+                const int r0 = 16 * RT * w + 16 * rt + srow;
+                *reinterpret_cast<u32x2*>(&sm.pl[0][n16 * PLS + r0]) = u32x2{bh[rt][0], bh[rt][1]};
+                *reinterpret_cast<u32x2*>(&sm.pl[1][n16 * PLS + r0]) = u32x2{bl[rt][0], bl[rt][1]};
             }
         }
         lds_barrier();                               // rows and P' of all waves visible
 
-        // ---- O^T += V^T P'^T over the chunk's 128 rows, this wave's 128 columns
+        // ---- O^T += V^T P'^T over the chunk's rows, this wave's 128 columns
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            if (!src_live[ks]) continue;             // that wave staged no rows
+        for (int ks = 0; ks < NKS; ++ks) {
+            if (!src_live[ks]) continue;             // no staged row in these 32
             const int r0 = 32 * ks + 8 * g4;         // k-slot e <-> row r0 + e
-            const bf16x8 p_hi = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.pl[0][n16 * kPLS + r0]));
-            const bf16x8 p_lo = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.pl[1][n16 * kPLS + r0]));
+            const bf16x8 p_hi = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.pl[0][n16 * PLS + r0]));
+            const bf16x8 p_lo = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.pl[1][n16 * PLS + r0]));
 #pragma unroll
             for (int G = 0; G < 2; ++G) {
                 const uint16_t* vb = &sm.kv[r0 * kRStride + 128 * w + 64 * G + 4 * n16];

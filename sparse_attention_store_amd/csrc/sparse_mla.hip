@@ -12,23 +12,29 @@
 // dominant row of a heavy-tailed latent (|o| ~ 100) needs to stay within
 // 2e-2 absolute.
 //
-// k_mla_rows (16 heads per workgroup; decode).  Each of the 4 waves owns 32
-// rows of every 128-row chunk and runs its own softmax over them, so the
-// chunk loop has no workgroup barrier:
-//  * a lane loads 128 contiguous bytes of one row straight into the K
-//    operand of S^T = K Q^T (v_mfma_f32_16x16x32_bf16, rows = M, heads = N);
-//    the reduction axis is permuted identically in K and Q, so q is loaded
-//    to match and no LDS pass is needed for S;
-//  * S^T leaves lane (head h, group g) holding 4 rows of head h per row
-//    tile, which is exactly the B operand P'^T of O^T = V^T P'^T for the
-//    wave's 32 rows: P' never leaves registers;
-//  * V^T comes from the wave's own rows written to LDS as bf16 during the
-//    conversion (8-byte reads of 4 adjacent columns, assembled with v_perm).
-//    Rows are placed with bits 2 and 3 of the slot swapped so that both the
-//    16-byte writes and the 8-byte reads are free of bank conflicts.
-//  The running max is only raised when a chunk exceeds it by more than 2^8,
-//  so the accumulators are rescaled rarely (never in a one-chunk split).
-//  At the end the 4 waves merge (m, l, O) through LDS in wave order.
+// k_mla_rows (16 heads per workgroup; decode).  The list is walked in chunks
+// of 64 RT rows (RT = 2 here: 128-row chunks, one workgroup per CU); each of
+// the 4 waves owns 16 RT rows of a chunk:
+//  * q (16 heads x 512) is read once per workgroup, before the dependent
+//    chain index -> rows, and handed to the waves through LDS (every wave
+//    needs all of it: 4 copies per workgroup from L2 cost more than the
+//    row gather itself);
+//  * the 4 lanes that share a row read it straight into the K operand of
+//    S^T = K Q^T (v_mfma_f32_16x16x32_bf16, rows = M, heads = N), 64
+//    contiguous bytes per load instruction (lane group g takes bytes
+//    64 i + 16 g .. +16); the reduction axis is permuted identically in K and
+//    Q, so q is loaded to match and no LDS pass is needed for S;
+//  * during the conversion each wave also writes its rows to LDS as bf16
+//    (code + 128); the per-head chunk max is exchanged through LDS, and
+//    P' = p * row scale goes to LDS as bf16 hi + lo, [head][row];
+//  * O^T += V^T P'^T is split by columns: each wave accumulates its own 128
+//    columns over every row of the chunk (8-byte LDS reads of 4 adjacent
+//    columns assembled with v_perm).  Rows are placed with bits 2 and 3 of
+//    the slot swapped so that both the 16-byte writes and the 8-byte reads
+//    are free of bank conflicts;
+//  * the running max is only raised when a chunk exceeds it by more than
+//    2^8, so the accumulators are rescaled rarely (never in a one-chunk
+//    split); at the end the waves add up l and the P' sums through LDS.
 //
 // k_mla_mfma<HT> (16*HT heads per workgroup, HT = 2 or 4; prefill and
 // many-query batches).  Waves own head tiles instead and walk 64-row chunks
@@ -44,19 +50,20 @@
 
 namespace dsa {
 
+template <int RT>
 __global__ __launch_bounds__(256, 1) void k_mla_rows(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, int row_bytes,
     const int32_t* __restrict__ indices, int W, int H, float scale_log2, int chunks_per_split,
     int splits, float* __restrict__ part_o, MlaPartial* __restrict__ part_ml,
     void* __restrict__ out, int out_f32, float* __restrict__ lse) {
-    __shared__ __attribute__((aligned(16))) MlaRowsSmem sm;
+    __shared__ __attribute__((aligned(16))) MlaRowsSmemT<RT> sm;
     const int split = blockIdx.x, t = blockIdx.z;
-    const int nchunks = (W + kRChunk - 1) / kRChunk;
+    const int nchunks = (W + 64 * RT - 1) / (64 * RT);
     const int c_begin = split * chunks_per_split;
     const int c_end = min(c_begin + chunks_per_split, nchunks);
     const int32_t* irow = indices + (int64_t)t * W;
-    mla_rows_split<false>(sm, q, cache, row_bytes, [&](int pos) { return irow[pos]; }, W, H, scale_log2, t,
-                          blockIdx.y * 16, split, c_begin, c_end, splits, part_o, part_ml, out, out_f32, lse);
+    mla_rows_split<RT, false>(sm, q, cache, row_bytes, [&](int pos) { return irow[pos]; }, W, H, scale_log2, t,
+                              blockIdx.y * 16, split, c_begin, c_end, splits, part_o, part_ml, out, out_f32, lse);
 }
 
 // ------------------------------------------------------------------ k_mla_mfma
@@ -431,6 +438,7 @@ MlaPlan plan_sparse_mla(const dsa_dims& d, int32_t T, int32_t num_splits, int q_
     if (!p.mfma || T <= 0) {
         p.head_tiles = 1;
         p.head_groups = d.mla_heads;
+        p.rows_rt = 2;
         p.splits = 1;
         p.chunks_per_split = 1;
         p.ws_bytes = 0;
@@ -444,7 +452,8 @@ MlaPlan plan_sparse_mla(const dsa_dims& d, int32_t T, int32_t num_splits, int q_
     p.head_groups = tiles16 / ht;
     // k_mla_rows walks 128-row chunks; k_mla_mfma 64-row chunks with the
     // split's index slice staged in LDS (at most kMaxSplitRows entries).
-    const int chunk = ht == 1 ? dsa::kRChunk : dsa::kChunk;
+    p.rows_rt = 2;
+    const int chunk = ht == 1 ? 64 * p.rows_rt : dsa::kChunk;
     const int nchunks = (int)cdiv(d.out_width, chunk);
     int want;
     if (num_splits > 0) {
@@ -500,7 +509,7 @@ hipError_t launch_sparse_mla(const dsa_dims& d, const MlaPlan& plan, const void*
                                plan.chunks_per_split, plan.splits, part_o, part_ml, out, out_f32, lse);
             break;
         default:
-            hipLaunchKernelGGL(dsa::k_mla_rows, grid, dim3(256), 0, s, q16, c8, d.row_bytes, indices, W, H, sl2,
+            hipLaunchKernelGGL(dsa::k_mla_rows<2>, grid, dim3(256), 0, s, q16, c8, d.row_bytes, indices, W, H, sl2,
                                plan.chunks_per_split, plan.splits, part_o, part_ml, out, out_f32, lse);
             break;
     }
