@@ -140,25 +140,27 @@ __global__ __launch_bounds__(WAVES * 64) void k_scores_mfma(
     }
 }
 
-// Decode kernel: one wave per 64-pool group.  The visible groups of all
-// queries form one flat list that the waves walk (wave w takes groups w,
-// w + W, ...); the grid is sized to be resident at once, so every wave reads
-// the queries' geometry (lane t: query t) while memory is still idle and
-// then issues its first group's loads -- 16 KB of pool rows straight into
-// MFMA B-operand registers, the query's A operand and head weights -- with
-// no LDS staging or barrier between a load and its MFMAs.  The visible index
-// thus streams from HBM as one wave of requests.  Rows past a query's visible
-// count inside its last group, and every pool after that group up to the row
-// stride, are written as -inf.
+// Decode kernel.  Work is a flat list of 256-pool tiles over the visible
+// pools of all queries (a query with ng 64-pool groups has ceil(ng / 4)
+// tiles); workgroup tasks are tiles, wave w of a task scores group 4 j + w of
+// tile j.  The grid is sized to be resident at once, so every workgroup reads
+// the queries' geometry while memory is still idle.  Per tile, the query's
+// 8 KB A operand (and its head weights) is loaded once by the workgroup, ahead
+// of the pool rows, and shared through LDS (padded rows: conflict-free 16-byte
+// reads); each wave loads its group's 16 KB of pool rows straight into MFMA
+// B-operand registers, all loads in flight before the first MFMA.  Rows past a
+// query's visible count inside its last group, and every pool after that group
+// up to the row stride, are written as -inf.
 // With CANDS, each wave also keeps its group's best m pools for the selection
 // (keep_group_best) when the query has more visible pools than select_k.
 constexpr int kDecMaxT = 64;
+constexpr int kQStride = kDI + 8;          // bf16 per LDS row of the shared A operand
 struct QueryGeom {
     int64_t base;      // pool_base of the query's sequence
-    uint32_t first;    // flat index of the query's first group
-    uint32_t ng;       // groups of visible pools
+    uint32_t first;    // flat index of the query's first tile
+    uint32_t ntiles;   // 256-pool tiles of visible pools
+    int32_t ng;        // 64-pool groups of visible pools
     int32_t nn;        // visible pools, capped at the row stride
-    int32_t pad;
 };
 template <bool CANDS>
 __global__ __launch_bounds__(256, 4) void k_scores_groups(
@@ -167,14 +169,13 @@ __global__ __launch_bounds__(256, 4) void k_scores_groups(
     const int64_t* __restrict__ pool_base, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_pos, int T, int stride, float* __restrict__ scores,
     int select_k, uint64_t* __restrict__ cand, int32_t* __restrict__ cand_n) {
-    __shared__ QueryGeom s_geom[4][kDecMaxT];          // one table per wave
+    __shared__ QueryGeom geom[kDecMaxT];
+    __shared__ __attribute__((aligned(16))) uint16_t s_q[kHI * kQStride];
+    __shared__ __attribute__((aligned(16))) float s_w[kHI];
     const int lane = threadIdx.x & 63;
-    const int gw = uniform32(blockIdx.x * 4 + (threadIdx.x >> 6));
-    const int W = gridDim.x * 4;
-    QueryGeom* geom = s_geom[threadIdx.x >> 6];
-    int total;
-    {
-        int nn = 0;                     // visible pools of query `lane`, capped at the stride
+    const int wave = uniform32(threadIdx.x >> 6);
+    if (wave == 0) {
+        int nn = 0;
         int64_t base = 0;
         if (lane < T) {
             const int b = q_seq[lane];
@@ -183,38 +184,62 @@ __global__ __launch_bounds__(256, 4) void k_scores_groups(
             nn = min(qp >= f ? (qp - f + 1) >> 2 : 0, stride);
             base = pool_base[b];
         }
-        const uint32_t ng = (uint32_t)(nn + kGroupPools - 1) / kGroupPools;
-        const uint32_t incl = wave_incl_sum_u32(ng);
-        geom[lane] = QueryGeom{base, incl - ng, ng, nn};
-        total = (int)__builtin_amdgcn_readlane(incl, 63);
+        const int ng = (nn + kGroupPools - 1) / kGroupPools;
+        const uint32_t nt = (uint32_t)(ng + 3) >> 2;
+        const uint32_t incl = wave_incl_sum_u32(nt);
+        geom[lane] = QueryGeom{base, incl - nt, nt, ng, nn};
     }
-    wave_lds_fence();
-    for (int gi = gw; gi < total; gi += W) {
-        // query of group gi: the number of queries whose groups all come before it
-        const int t = __popcll(__ballot(geom[lane].first + geom[lane].ng <= (uint32_t)gi));
-        const int64_t b0 = (int64_t)uniform64((uint64_t)geom[t].base);
-        const int grp = gi - uniform32((int)geom[t].first);
+    lds_barrier();
+    const int total = (int)(geom[63].first + geom[63].ntiles);
+    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+        // query of the tile: the number of queries whose tiles all come before it
+        const int t = __popcll(__ballot(geom[lane].first + geom[lane].ntiles <= (uint32_t)tile));
+        const int grp = 4 * (tile - uniform32((int)geom[t].first)) + wave;
+        const bool has = grp < uniform32(geom[t].ng);
         const int n_vis = uniform32(geom[t].nn);
         const int p0 = grp * kGroupPools;
-        IdxQuery Q;
-        load_idx_query(q_idx, w, t, Q);
-        u32x4 v[16];
-        load_pool_group(pools + (b0 + p0) * kDI, n_vis - p0, v);
-        __builtin_amdgcn_sched_barrier(0);      // every load in flight before the first MFMA
-        const float s = score_pool_group(Q, v);
-        const int p = p0 + lane;
-        if (p < stride) scores[(int64_t)t * stride + p] = p < n_vis ? s : -INFINITY;
-        if constexpr (CANDS) {
-            if (n_vis > select_k)
-                keep_group_best(s, p < n_vis, p, grp, group_quota(select_k, n_vis),
-                                cand + (int64_t)t * kGroupCandCap, cand_n + (int64_t)t * kMaxGroups,
-                                [](uint64_t* q, uint64_t x) { *q = x; },
-                                [](int32_t* q, uint32_t x) { *q = (int32_t)x; });
+        // The tile's A operand: wave w loads heads 8 w .. 8 w + 7 (two 16-byte
+        // pieces per lane), plus the head weights; issued before the pool rows.
+        u32x4 qv[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int k = lane + 64 * i;               // piece k: head 8 w + k / 16, dims 8 (k % 16) ..
+            qv[i] = *reinterpret_cast<const u32x4*>(q_idx + ((int64_t)t * kHI + 8 * wave + (k >> 4)) * kDI + 8 * (k & 15));
         }
+        const float wt = lane < 8 ? w[(int64_t)t * kHI + 8 * wave + lane] : 0.f;
+        // A wave past the query's last group re-reads the tile's first row
+        // (unconditional loads keep the wait counts exact).
+        u32x4 v[16];
+        const int lp0 = has ? p0 : p0 - kGroupPools * wave;
+        load_pool_group(pools + ((int64_t)uniform64((uint64_t)geom[t].base) + lp0) * kDI, has ? n_vis - p0 : 1, v);
+        __builtin_amdgcn_sched_barrier(0);             // every load in flight before the A operand is shared
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int k = lane + 64 * i;
+            *reinterpret_cast<u32x4*>(&s_q[(8 * wave + (k >> 4)) * kQStride + 8 * (k & 15)]) = qv[i];
+        }
+        if (lane < 8) s_w[8 * wave + lane] = wt;
+        lds_barrier();
+        if (has) {
+            IdxQuery Q;
+            load_idx_query_lds(s_q, kQStride, s_w, Q);
+            const float s = score_pool_group(Q, v);
+            const int p = p0 + lane;
+            if (p < stride) scores[(int64_t)t * stride + p] = p < n_vis ? s : -INFINITY;
+            if constexpr (CANDS) {
+                if (n_vis > select_k)
+                    keep_group_best(s, p < n_vis, p, grp, group_quota(select_k, n_vis),
+                                    cand + (int64_t)t * kGroupCandCap, cand_n + (int64_t)t * kMaxGroups,
+                                    [](uint64_t* q, uint64_t x) { *q = x; },
+                                    [](int32_t* q, uint32_t x) { *q = (int32_t)x; });
+            }
+        }
+        if (tile + (int)gridDim.x < total) lds_barrier();   // s_q is rewritten by the next tile
     }
     // Pools past each query's last visible group.
+    const int gw = blockIdx.x * 4 + wave, W = gridDim.x * 4;
     for (int t = 0; t < T; ++t) {
-        const int from = (int)geom[t].ng * kGroupPools;
+        const int from = geom[t].ng * kGroupPools;
         float* out = scores + (int64_t)t * stride;
         for (int p = from + gw * kGroupPools + lane; p < stride; p += W * kGroupPools) out[p] = -INFINITY;
     }
@@ -254,10 +279,10 @@ __global__ __launch_bounds__(256) void k_scores_generic(
 
 namespace dsa_host {
 
-// Workgroups (4 waves, one 64-pool group each) for k_scores_groups: every
-// group of every query if that fits, else 4 per CU, which stay resident.
+// Workgroups (one 256-pool tile each) for k_scores_groups: every tile of
+// every query if that fits, else 4 per CU, which stay resident.
 static unsigned scores_groups_grid(int32_t T, int32_t stride) {
-    const int64_t wgs = cdiv(cdiv(stride, dsa::kGroupPools) * (int64_t)T, 4);
+    const int64_t wgs = cdiv(cdiv(stride, dsa::kGroupPools), 4) * (int64_t)T;
     return (unsigned)std::min<int64_t>(wgs, 4 * (int64_t)device_info().cu_count);
 }
 

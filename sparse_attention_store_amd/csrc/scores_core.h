@@ -48,6 +48,19 @@ __device__ __forceinline__ void load_idx_query(const uint16_t* __restrict__ q_id
         Q.w[mt] = __builtin_bit_cast(f32x4, ld_buf128(rw, (uint32_t)(16 * g), (uint32_t)(64 * mt)));
 }
 
+// The same operand from a copy of q in LDS ([head][dim], row stride qs
+// elements) and the head weights in LDS.
+__device__ __forceinline__ void load_idx_query_lds(const uint16_t* q_lds, int qs, const float* w_lds, IdxQuery& Q) {
+    const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            Q.a[mt][s] = *reinterpret_cast<const u32x4*>(&q_lds[(16 * mt + c) * qs + 32 * s + 8 * g]);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) Q.w[mt] = *reinterpret_cast<const f32x4*>(&w_lds[16 * mt + 4 * g]);
+}
+
 // rows: the group's first pool row (wave-uniform); lim (>= 1): rows of the
 // group that exist.  Rows at or past lim re-read row lim - 1, so every access
 // stays inside the group's existing rows (their scores are meaningless and
