@@ -174,7 +174,7 @@ struct StepPlan {
 };
 
 struct StepSelSmem {
-    TopSelShared<kStepNT, kStepKPT> T;
+    TopSelSmall<kStepNT, kStepKPT, 1024> T;
     int32_t sel[kStepMaxK];
     uint32_t gpicked[kStepMaxGroups];
     uint32_t gcount[kStepMaxGroups];
@@ -280,7 +280,7 @@ __device__ void step_select(const StepArgs& a, StepSelSmem& sm, StepPlan& plan, 
         key[j] = ok ? (uint32_t)(raw[j] >> 32) : 0u;
         id[j] = (int32_t)(0xFFFFFFFFu - (uint32_t)raw[j]);
     }
-    const uint32_t picks = select_top_slots<kStepNT, kStepKPT>(key, (uint32_t)K, sm.T);
+    const uint32_t picks = select_top_slots_small<kStepNT, kStepKPT, 1024>(key, (uint32_t)K, sm.T);
     uint32_t total;
     uint32_t pos = block_exclusive_scan<kStepNT>((uint32_t)__popc(picks), sm.T.S.scan, &total);
 #pragma unroll

@@ -124,20 +124,21 @@ __global__ __launch_bounds__(kTile) void k_topk_tiles(
 // cannot prove they hold the answer): MSB-first radix select, 8 bits a pass,
 // then one ordered pass that takes every key above the K-th and the first
 // `need` keys equal to it.  Writes K ids, ascending, to sel.
-__device__ void topk_stream_exact(const float* __restrict__ row, int n, int K, SelShared<kBNT>& S,
-                                  int32_t* sel) {
+template <int NT>
+__device__ void topk_stream_exact(const float* __restrict__ row, int n, int K, SelShared<NT>& S, int32_t* sel) {
+    static_assert(NT >= 256, "one thread per digit");
     const int tid = threadIdx.x;
     uint32_t prefix = 0u, mask = 0u, need = (uint32_t)K, total;
     for (int d = 3; d >= 0; --d) {
         if (tid < 256) S.hist[0][tid] = 0u;
         lds_barrier();
-        for (int i = tid; i < n; i += kBNT) {
+        for (int i = tid; i < n; i += NT) {
             const uint32_t k = f32_key(row[i]);
             if ((k & mask) == prefix) atomicAdd(&S.hist[0][(k >> (8 * d)) & 0xFFu], 1u);
         }
         lds_barrier();
         const uint32_t h = tid < 256 ? S.hist[0][255 - tid] : 0u;    // descending digits
-        const uint32_t above = block_exclusive_scan<kBNT>(h, S.scan, &total);
+        const uint32_t above = block_exclusive_scan<NT>(h, S.scan, &total);
         if (tid < 256 && above < need && need <= above + h) {
             S.bin[0] = 255u - (uint32_t)tid;
             S.above[0] = above;
@@ -149,15 +150,15 @@ __device__ void topk_stream_exact(const float* __restrict__ row, int n, int K, S
         lds_barrier();
     }
     uint32_t out_base = 0u, eq_base = 0u;
-    for (int i0 = 0; i0 < n; i0 += kBNT) {
+    for (int i0 = 0; i0 < n; i0 += NT) {
         const int i = i0 + tid;
         const uint32_t k = i < n ? f32_key(row[i]) : 0u;
         const uint32_t gt = (i < n && k > prefix) ? 1u : 0u;
         const uint32_t eq = (i < n && k == prefix) ? 1u : 0u;
         uint32_t eq_tot, pick_tot;
-        const uint32_t eq_rank = eq_base + block_exclusive_scan<kBNT>(eq, S.scan, &eq_tot);
+        const uint32_t eq_rank = eq_base + block_exclusive_scan<NT>(eq, S.scan, &eq_tot);
         const uint32_t pick = gt | ((eq && eq_rank < need) ? 1u : 0u);
-        const uint32_t pos = out_base + block_exclusive_scan<kBNT>(pick, S.scan, &pick_tot);
+        const uint32_t pos = out_base + block_exclusive_scan<NT>(pick, S.scan, &pick_tot);
         if (pick && pos < (uint32_t)kMaxK) sel[pos] = i;
         out_base += pick_tot;
         eq_base += eq_tot;
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(kBNT) void k_topk_rows(
         if ((cn[c] & kIncomplete) && tpicked[c] == (uint32_t)m) fail = 1;
     lds_barrier();
     if (fail) {
-        topk_stream_exact(scores + (int64_t)t * stride, n, select_k, T.S, sel);
+        topk_stream_exact<kBNT>(scores + (int64_t)t * stride, n, select_k, T.S, sel);
     } else {
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
@@ -285,7 +286,7 @@ __global__ __launch_bounds__(kBNT) void k_topk_groups(
     if (tid < groups && (gcount[tid] & kGroupDropped) && gpicked[tid] == (uint32_t)m) fail = 1;
     lds_barrier();
     if (fail) {
-        topk_stream_exact(scores + (int64_t)t * stride, n, select_k, T.S, sel);
+        topk_stream_exact<kBNT>(scores + (int64_t)t * stride, n, select_k, T.S, sel);
     } else {
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {

@@ -106,8 +106,8 @@ struct SelShared {
     uint32_t bin[2], above[2], cnt[2];
 };
 
-template <int NT>
-constexpr int log2_of() { return NT == 256 ? 8 : (NT == 512 ? 9 : 10); }
+template <int N>
+constexpr int log2_of() { return N == 256 ? 8 : (N == 512 ? 9 : (N == 1024 ? 10 : 11)); }
 
 // Find the range [lo, hi] holding the rank-`target` key (absent keys are 0).
 // On return every key > hi is in the top `target`; `krem` of the keys inside
@@ -335,6 +335,228 @@ __device__ __forceinline__ uint32_t select_top_slots(const uint32_t (&key)[KPT],
         for (int j = 0; j < KPT; ++j) {
             const uint32_t sl = (uint32_t)(tid * KPT + j);
             if ((T.flag[sl >> 5] >> (sl & 31)) & 1u) picks |= 1u << j;
+        }
+    } else {
+        // more than kBoundCap equal keys (lo == hi): the first krem in slot order
+        uint32_t c = 0;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) c += (key[j] != 0u && key[j] == lo) ? 1u : 0u;
+        uint32_t tot;
+        const uint32_t before = block_exclusive_scan<NT>(c, T.S.scan, &tot);
+        uint32_t take = krem > before ? min(krem - before, c) : 0u;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            if (key[j] != 0u && key[j] == lo && take > 0u) {
+                picks |= 1u << j;
+                --take;
+            }
+        }
+    }
+    return picks;
+}
+
+// ---------------------------------------------------------------- exact top-K, small workgroups
+
+// The same selection as select_top_slots (same result) for workgroups of a
+// few waves holding many keys per thread: every pass has a histogram of its
+// own (NB buckets, independent of NT), all cleared up front, and after its
+// one barrier every wave finds the rank-target bucket by itself (DPP sums over
+// the buckets, read in a bank-conflict-free order), so a pass costs a single
+// workgroup barrier; the boundary keys are ranked by every wave too and each
+// thread reads its own picks from the resulting ballot.  (With 16 waves the
+// repeated per-wave work costs more than it saves, and select_top_slots is
+// the faster of the two; a large workgroup here searches and ranks in wave 0
+// and hands the result over through LDS.)
+constexpr int kSelPasses = 4;
+
+// NB buckets per pass (256, 512 or 1024), independent of the NT threads.
+template <int NT, int KPT, int NB = NT>
+struct TopSelSmall {
+    SelShared<NT> S;                     // block scans (and the fallbacks' state)
+    uint32_t hist[kSelPasses][NB];       // one histogram per pass
+    uint32_t mm[2 * NT / 64];
+    uint32_t nb;
+    uint32_t res[4];                     // a pass's bucket (one-wave search) / the boundary picks
+    uint32_t bkey[kBoundCap];
+    uint32_t bslot[kBoundCap];
+};
+
+template <int NT, int KPT, int NB = NT>
+__device__ __forceinline__ uint32_t select_top_slots_small(const uint32_t (&key)[KPT], uint32_t target,
+                                                     TopSelSmall<NT, KPT, NB>& T) {
+    constexpr int BITS = log2_of<NB>();
+    constexpr int NW = NT / 64;
+    constexpr int PER = NB / 64;                             // buckets per lane in the bucket search
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    for (int i = tid; i < kSelPasses * NB; i += NT) (&T.hist[0][0])[i] = 0u;
+    if (tid == 0) T.nb = 0u;
+    // smallest present key and largest key; the barrier also publishes the clears
+    uint32_t lo = ~0u, hi = 0u;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        if (key[j]) lo = min(lo, key[j]);
+        hi = max(hi, key[j]);
+    }
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+    if (lane == 0) {
+        T.mm[2 * w] = lo;
+        T.mm[2 * w + 1] = hi;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        lo = min(lo, T.mm[2 * i]);
+        hi = max(hi, T.mm[2 * i + 1]);
+    }
+    uint32_t krem = target, cnt = 0xFFFFFFFFu;
+    bool whole = false;
+    for (int pass = 0; pass < kSelPasses && lo < hi && cnt > (uint32_t)kBoundCap; ++pass) {
+        uint32_t* H = T.hist[pass];
+        const int sh = bit_len<uint32_t>((hi - lo) >> BITS);
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const uint32_t k = key[j];
+            if (k >= lo && k <= hi) atomicAdd(&H[(k - lo) >> sh], 1u);
+        }
+        lds_barrier();
+        // The rank-krem bucket (d = NB-1-bucket, descending), found by every
+        // wave of a small workgroup, or by wave 0 and handed over through LDS
+        // in a large one (there the 16-fold repeated search costs more than a
+        // second barrier).
+        uint32_t d = 0u, above = 0u;
+        bool none = false;
+        auto search = [&]() {
+            // lane l sums d in [l PER, (l+1) PER), read in a rotated order
+            // that keeps the 64 lanes on distinct banks
+            uint32_t lsum = 0u;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) lsum += H[NB - 1 - (lane * PER + ((i + lane / (64 / PER)) & (PER - 1)))];
+            const uint32_t incl = wave_incl_sum_u32(lsum), excl = incl - lsum;
+            const unsigned long long hit = __ballot(excl < krem && krem <= incl);
+            if (hit == 0ull) {                               // fewer keys than target: take them all
+                none = true;
+                return;
+            }
+            const int L = __ffsll((long long)hit) - 1;
+            // walk lane L's buckets (same address in every lane: broadcast reads)
+            uint32_t acc = __builtin_amdgcn_readlane(excl, L);
+            cnt = 0u;
+            bool found = false;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const uint32_t c = H[NB - 1 - (L * PER + i)];
+                if (!found && krem <= acc + c) {
+                    found = true;
+                    d = (uint32_t)(L * PER + i);
+                    above = acc;
+                    cnt = c;
+                }
+                acc += c;
+            }
+        };
+        if constexpr (NW >= 8) {
+            if (w == 0) {
+                search();
+                if (lane == 0) {
+                    T.res[0] = d;
+                    T.res[1] = above;
+                    T.res[2] = cnt;
+                    T.res[3] = none ? 1u : 0u;
+                }
+            }
+            lds_barrier();
+            d = T.res[0];
+            above = T.res[1];
+            cnt = T.res[2];
+            none = T.res[3] != 0u;
+        } else {
+            search();
+        }
+        if (none) {
+            whole = true;
+            break;
+        }
+        krem -= above;
+        const uint32_t nlo = lo + ((NB - 1 - d) << sh);
+        const uint32_t nhi = nlo + ((1u << sh) - 1u);
+        lo = nlo;
+        hi = nhi < hi ? nhi : hi;
+        if (cnt == krem) {
+            whole = true;
+            break;
+        }
+    }
+    if (lo == hi && cnt == 0xFFFFFFFFu) {                    // every present key equal (or one key)
+        uint32_t c = 0;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) c += key[j] == lo ? 1u : 0u;
+        uint32_t tot;
+        block_exclusive_scan<NT>(c, T.S.scan, &tot);
+        cnt = tot;
+        whole = tot == krem;
+    }
+    uint32_t picks = 0u;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+        if (key[j] > hi || (whole && key[j] != 0u && key[j] >= lo && key[j] <= hi)) picks |= 1u << j;
+    if (whole) return picks;
+    if (cnt <= (uint32_t)kBoundCap) {
+        // gather the boundary bucket (a thread's keys take consecutive entries)
+        uint32_t mine = 0u;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) mine += (key[j] != 0u && key[j] >= lo && key[j] <= hi) ? 1u : 0u;
+        uint32_t e0 = 0u;
+        if (mine) {
+            e0 = atomicAdd(&T.nb, mine);
+            uint32_t e = e0;
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
+                if (key[j] != 0u && key[j] >= lo && key[j] <= hi) {
+                    T.bkey[e] = key[j];
+                    T.bslot[e] = (uint32_t)(tid * KPT + j);
+                    ++e;
+                }
+            }
+        }
+        lds_barrier();
+        // rank the entries (lane i: entry i): every wave of a small
+        // workgroup, wave 0 of a large one (handing the picks over in LDS)
+        auto rank_entries = [&]() -> unsigned long long {
+            const uint32_t nb = T.nb;
+            bool pk = false;
+            if ((uint32_t)lane < nb) {
+                const uint32_t mk = T.bkey[lane], ms = T.bslot[lane];
+                uint32_t rank = 0;
+                for (uint32_t i = 0; i < nb; ++i) {
+                    const uint32_t k = T.bkey[i];
+                    rank += (k > mk || (k == mk && T.bslot[i] < ms)) ? 1u : 0u;
+                }
+                pk = rank < krem;
+            }
+            return __ballot(pk);
+        };
+        unsigned long long pm;
+        if constexpr (NW >= 8) {
+            if (w == 0) {
+                pm = rank_entries();
+                if (lane == 0) {
+                    T.res[0] = (uint32_t)pm;
+                    T.res[1] = (uint32_t)(pm >> 32);
+                }
+            }
+            lds_barrier();
+            pm = ((unsigned long long)T.res[1] << 32) | T.res[0];
+        } else {
+            pm = rank_entries();
+        }
+        uint32_t e = e0;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            if (key[j] != 0u && key[j] >= lo && key[j] <= hi) {
+                if ((pm >> e) & 1ull) picks |= 1u << j;
+                ++e;
+            }
         }
     } else {
         // more than kBoundCap equal keys (lo == hi): the first krem in slot order
