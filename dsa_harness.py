@@ -97,6 +97,7 @@ class DeviceWorkload:
         self.ws_mla = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
         self.ws_step = None
         self.ws_ss = None
+        self._bound = {}
         if build:
             self.build_caches()
 
@@ -126,69 +127,96 @@ class DeviceWorkload:
         torch.cuda.synchronize()
 
     # ------------------------------------------------------------------ the step
-    def step_store(self, r: int = 0):
-        dsa.store_int8(self.dims, self.latent_q, self.slots_q, self.caches[r])
+    # Every stage takes (r, prepare): with prepare=True it returns the prepared
+    # call(s) of the binding instead of launching (see bound / run below).
+    def step_store(self, r: int = 0, prepare: bool = False):
+        return dsa.store_int8(self.dims, self.latent_q, self.slots_q, self.caches[r], prepare=prepare)
 
-    def step_pools(self, r: int = 0):
+    def step_pools(self, r: int = 0, prepare: bool = False):
         if self.step_max_pools > 0:
-            dsa.index_pools(self.dims, self.k, self.gate, self.ln_w, self.ln_b, self.seqs,
-                            self.step_pool_begin, self.step_pool_end, self.step_max_pools, self.pools[r])
+            return dsa.index_pools(self.dims, self.k, self.gate, self.ln_w, self.ln_b, self.seqs,
+                                   self.step_pool_begin, self.step_pool_end, self.step_max_pools, self.pools[r],
+                                   prepare=prepare)
+        return None
 
-    def step_append(self, r: int = 0):
+    def step_append(self, r: int = 0, prepare: bool = False):
         """The step's new tokens (INT8 rows and completed pools) in one launch
         (two calls when the latent rows and the indexer keys differ in dtype)."""
         if self.latent_q.dtype != self.k.dtype:
-            self.step_store(r)
-            self.step_pools(r)
-            return
-        dsa.append_tokens(self.dims, self.latent_q, self.slots_q, self.caches[r], self.k, self.gate, self.ln_w,
-                          self.ln_b, self.seqs, self.step_pool_begin, self.step_pool_end, self.step_max_pools,
-                          self.pools[r])
+            return [self.step_store(r, prepare), self.step_pools(r, prepare)]
+        return dsa.append_tokens(self.dims, self.latent_q, self.slots_q, self.caches[r], self.k, self.gate,
+                                 self.ln_w, self.ln_b, self.seqs, self.step_pool_begin, self.step_pool_end,
+                                 self.step_max_pools, self.pools[r], prepare=prepare)
 
-    def step_scores(self, r: int = 0):
-        dsa.index_scores(self.dims, self.q_idx, self.w, self.pools[r], self.seqs, self.q_seq, self.q_pos,
-                         self.scores)
+    def step_scores(self, r: int = 0, prepare: bool = False):
+        return dsa.index_scores(self.dims, self.q_idx, self.w, self.pools[r], self.seqs, self.q_seq, self.q_pos,
+                                self.scores, prepare=prepare)
 
-    def step_topk(self):
-        dsa.topk_select(self.dims, self.scores, self.seqs, self.q_seq, self.q_pos, self.pool_ids, self.ws_topk)
+    def step_topk(self, r: int = 0, prepare: bool = False):
+        return dsa.topk_select(self.dims, self.scores, self.seqs, self.q_seq, self.q_pos, self.pool_ids,
+                               self.ws_topk, prepare=prepare)
 
-    def step_expand(self):
-        dsa.expand_selection(self.dims, self.pool_ids, self.seqs, self.q_seq, self.q_pos, self.indices)
+    def step_expand(self, r: int = 0, prepare: bool = False):
+        return dsa.expand_selection(self.dims, self.pool_ids, self.seqs, self.q_seq, self.q_pos, self.indices,
+                                    prepare=prepare)
 
-    def step_attention(self, r: int = 0):
-        dsa.sparse_mla(self.dims, self.q, self.caches[r], self.indices, self.wl.scale, self.out, self.lse,
-                       self.num_splits, self.ws_mla)
+    def step_attention(self, r: int = 0, prepare: bool = False):
+        return dsa.sparse_mla(self.dims, self.q, self.caches[r], self.indices, self.wl.scale, self.out, self.lse,
+                              self.num_splits, self.ws_mla, prepare=prepare)
 
     def _ws_ss(self):
         if self.ws_ss is None:
             self.ws_ss = dsa.index_scores_select_workspace(self.dims, self.wl.T, self.stride, device=self.device)
         return self.ws_ss
 
-    def step_scores_groups(self, r: int = 0):
-        dsa.index_scores_groups(self.dims, self.q_idx, self.w, self.pools[r], self.seqs, self.q_seq, self.q_pos,
-                                self.scores, self._ws_ss())
+    def step_scores_groups(self, r: int = 0, prepare: bool = False):
+        return dsa.index_scores_groups(self.dims, self.q_idx, self.w, self.pools[r], self.seqs, self.q_seq,
+                                       self.q_pos, self.scores, self._ws_ss(), prepare=prepare)
 
-    def step_select_groups(self):
-        dsa.topk_select_groups(self.dims, self.scores, self.seqs, self.q_seq, self.q_pos, self.indices, self._ws_ss(),
-                               pool_ids=self.pool_ids)
+    def step_select_groups(self, r: int = 0, prepare: bool = False):
+        return dsa.topk_select_groups(self.dims, self.scores, self.seqs, self.q_seq, self.q_pos, self.indices,
+                                      self._ws_ss(), pool_ids=self.pool_ids, prepare=prepare)
 
-    def step_scores_select(self, r: int = 0):
+    def step_scores_select(self, r: int = 0, prepare: bool = False):
         """Scores, selection and expansion (dsa_index_scores_select: two launches for decode)."""
-        dsa.index_scores_select(self.dims, self.q_idx, self.w, self.pools[r], self.seqs, self.q_seq, self.q_pos,
-                                self.scores, self.indices, pool_ids=self.pool_ids, workspace=self._ws_ss())
+        return dsa.index_scores_select(self.dims, self.q_idx, self.w, self.pools[r], self.seqs, self.q_seq,
+                                       self.q_pos, self.scores, self.indices, pool_ids=self.pool_ids,
+                                       workspace=self._ws_ss(), prepare=prepare)
 
-    def step_select(self):
+    def step_select(self, r: int = 0, prepare: bool = False):
         """Top-k and expansion in one launch (pool ids kept for the checks)."""
-        dsa.topk_select_expand(self.dims, self.scores, self.seqs, self.q_seq, self.q_pos, self.indices,
-                               self.pool_ids, self.ws_topk)
+        return dsa.topk_select_expand(self.dims, self.scores, self.seqs, self.q_seq, self.q_pos, self.indices,
+                                      self.pool_ids, self.ws_topk, prepare=prepare)
 
-    def step_decode(self, r: int = 0):
+    def step_decode(self, r: int = 0, prepare: bool = False):
         """Scores, top-k, expansion and attention in one launch (dsa_decode_step)."""
         if self.ws_step is None:
             self.ws_step = dsa.decode_step_workspace(self.dims, self.wl.T, self.stride, device=self.device)
-        dsa.decode_step(self.dims, self.q_idx, self.w, self.pools[r], self.seqs, self.q_seq, self.q_pos,
-                        self.stride, self.q, self.caches[r], self.wl.scale, self.out, self.ws_step, lse=self.lse,
-                        pool_ids=self.pool_ids, indices=self.indices)
+        return dsa.decode_step(self.dims, self.q_idx, self.w, self.pools[r], self.seqs, self.q_seq, self.q_pos,
+                               self.stride, self.q, self.caches[r], self.wl.scale, self.out, self.ws_step,
+                               lse=self.lse, pool_ids=self.pool_ids, indices=self.indices, prepare=prepare)
+
+    def bound(self, stage: str, r: int = 0):
+        """Stage `stage` (step_<stage>) of replica r as prepared calls: validated
+        and converted once, then cached, so a timed loop pays one ctypes call
+        per launch."""
+        key = (stage, r)
+        b = self._bound.get(key)
+        if b is None:
+            out = getattr(self, "step_" + stage)(r, prepare=True)
+            b = tuple(x for x in (out if isinstance(out, list) else [out]) if x is not None)
+            self._bound[key] = b
+        return b
+
+    def run(self, stage: str, r: int = 0):
+        for call in self.bound(stage, r):
+            call()
+
+    def step_fast(self, r: int = 0):
+        """step() through prepared calls."""
+        self.run("append", r)
+        self.run("scores_select", r)
+        self.run("attention", r)
 
     def step_fused(self, r: int = 0):
         """One pass of the whole path: the new tokens, then the fused decode launch."""

@@ -3,7 +3,9 @@
 Thin ctypes marshalling over the C ABI declared in include/dsa.h: each
 function checks tensor dtypes/devices/shapes, passes device pointers, the
 dims struct and the current HIP stream, and raises DsaError on a non-zero
-status.  Every step of the path runs in the library's HIP kernels; PyTorch
+status.  With prepare=True a function returns a Bound call instead: the
+checks and the argument conversion happen once, and each call of it only
+launches (a decode loop calls its steps many times on the same buffers).  Every step of the path runs in the library's HIP kernels; PyTorch
 only provides device memory and streams.  There is no fallback: if the
 shared library is missing, importing any entry point raises.
 """
@@ -146,6 +148,33 @@ def _raise(fn: str, st: int):
         raise DsaError(fn, st, lib().dsa_status_string(st).decode())
 
 
+class Bound:
+    """A validated call whose C arguments were converted once (prepare=True):
+    calling it only launches, on the stream that was current when it was
+    prepared, with the buffers it was prepared with."""
+    __slots__ = ("_name", "_fn", "_args")
+
+    def __init__(self, name: str, args):
+        fn = getattr(lib(), name)
+        self._name, self._fn = name, fn
+        conv = []
+        for a, t in zip(args, fn.argtypes):
+            conv.append(a if isinstance(a, (ctypes._SimpleCData, ctypes.Structure)) or type(a).__name__ == "CArgObject"
+                        else t(a))
+        self._args = tuple(conv)
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st:
+            _raise(self._name, st)
+
+
+def _call(name: str, prepare: bool, *args):
+    if prepare:
+        return Bound(name, args)
+    _raise(name, getattr(lib(), name)(*args))
+
+
 def _dt(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return DSA_F32
@@ -162,7 +191,7 @@ def status_string(status: int) -> str:
     return lib().dsa_status_string(status).decode()
 
 
-def store_int8(dims: Dims, latent: torch.Tensor, slots: torch.Tensor, cache: torch.Tensor, stream=None):
+def store_int8(dims: Dims, latent: torch.Tensor, slots: torch.Tensor, cache: torch.Tensor, stream=None, prepare: bool = False):
     """Quantise latent rows [n, D] (bf16/fp32) into INT8 rows of cache [rows, row_bytes] at slots."""
     if latent.dim() != 2 or (latent.shape[0] > 0 and latent.stride(1) != 1):
         raise ValueError("latent must be [n, D] with unit stride in D")
@@ -172,14 +201,14 @@ def store_int8(dims: Dims, latent: torch.Tensor, slots: torch.Tensor, cache: tor
     _check(cache, torch.int8, "cache")
     if slots.numel() != latent.shape[0]:
         raise ValueError("slots must have one entry per latent row")
-    _raise("dsa_store_int8", lib().dsa_store_int8(
+    return _call("dsa_store_int8", prepare, 
         ctypes.byref(dims), latent.data_ptr(), _dt(latent), latent.shape[0], latent.stride(0),
-        slots.data_ptr(), cache.data_ptr(), cache.shape[0], _stream(stream)))
+        slots.data_ptr(), cache.data_ptr(), cache.shape[0], _stream(stream))
 
 
 def index_pools(dims: Dims, k: torch.Tensor, gate: torch.Tensor, ln_w: torch.Tensor, ln_b: torch.Tensor,
                 seqs: Seqs, pool_begin: torch.Tensor, pool_end: torch.Tensor, max_pools: int,
-                pools: torch.Tensor, stream=None):
+                pools: torch.Tensor, stream=None, prepare: bool = False):
     """Build pools [pool_begin[b], pool_end[b]) of each sequence into pools (bf16 [*, idx_dim])."""
     if k.dtype != gate.dtype:
         raise TypeError("k and gate must share a dtype")
@@ -190,16 +219,16 @@ def index_pools(dims: Dims, k: torch.Tensor, gate: torch.Tensor, ln_w: torch.Ten
     _check(pool_begin, torch.int32, "pool_begin")
     _check(pool_end, torch.int32, "pool_end")
     _check(pools, torch.bfloat16, "pools")
-    _raise("dsa_index_pools", lib().dsa_index_pools(
+    return _call("dsa_index_pools", prepare, 
         ctypes.byref(dims), k.data_ptr(), gate.data_ptr(), _dt(k), ln_w.data_ptr(), ln_b.data_ptr(),
         ctypes.byref(seqs._c()), seqs.num_seqs, pool_begin.data_ptr(), pool_end.data_ptr(),
-        int(max_pools), pools.data_ptr(), _stream(stream)))
+        int(max_pools), pools.data_ptr(), _stream(stream))
 
 
 def append_tokens(dims: Dims, latent: torch.Tensor, slots: torch.Tensor, cache: torch.Tensor,
                   k: torch.Tensor, gate: torch.Tensor, ln_w: torch.Tensor, ln_b: torch.Tensor, seqs: Seqs,
                   pool_begin: torch.Tensor, pool_end: torch.Tensor, max_pools: int, pools: torch.Tensor,
-                  stream=None):
+                  stream=None, prepare: bool = False):
     """store_int8(latent, slots, cache) and index_pools(k, gate, ...) in one launch (one dtype for all)."""
     if latent.dim() != 2 or (latent.shape[0] > 0 and latent.stride(1) != 1):
         raise ValueError("latent must be [n, D] with unit stride in D")
@@ -216,15 +245,15 @@ def append_tokens(dims: Dims, latent: torch.Tensor, slots: torch.Tensor, cache: 
     _check(pool_begin, torch.int32, "pool_begin")
     _check(pool_end, torch.int32, "pool_end")
     _check(pools, torch.bfloat16, "pools")
-    _raise("dsa_append_tokens", lib().dsa_append_tokens(
+    return _call("dsa_append_tokens", prepare, 
         ctypes.byref(dims), _dt(latent), latent.data_ptr(), latent.shape[0], latent.stride(0), slots.data_ptr(),
         cache.data_ptr(), cache.shape[0], k.data_ptr(), gate.data_ptr(), ln_w.data_ptr(), ln_b.data_ptr(),
         ctypes.byref(seqs._c()), seqs.num_seqs, pool_begin.data_ptr(), pool_end.data_ptr(), int(max_pools),
-        pools.data_ptr(), _stream(stream)))
+        pools.data_ptr(), _stream(stream))
 
 
 def index_scores(dims: Dims, q_idx: torch.Tensor, w: torch.Tensor, pools: torch.Tensor, seqs: Seqs,
-                 q_seq: torch.Tensor, q_pos: torch.Tensor, scores: torch.Tensor, stream=None):
+                 q_seq: torch.Tensor, q_pos: torch.Tensor, scores: torch.Tensor, stream=None, prepare: bool = False):
     """scores [T, stride] (fp32) from q_idx [T, Hi, Di] (bf16), w [T, Hi] (fp32), pools (bf16)."""
     _check(q_idx, torch.bfloat16, "q_idx")
     _check(w, torch.float32, "w")
@@ -235,10 +264,10 @@ def index_scores(dims: Dims, q_idx: torch.Tensor, w: torch.Tensor, pools: torch.
     T = q_pos.shape[0]
     if scores.dim() != 2 or scores.shape[0] != T:
         raise ValueError("scores must be [T, stride]")
-    _raise("dsa_index_scores", lib().dsa_index_scores(
+    return _call("dsa_index_scores", prepare, 
         ctypes.byref(dims), q_idx.data_ptr(), w.data_ptr(), pools.data_ptr(), ctypes.byref(seqs._c()),
         seqs.num_seqs, q_seq.data_ptr(), q_pos.data_ptr(), T, scores.shape[1], scores.data_ptr(),
-        _stream(stream)))
+        _stream(stream))
 
 
 def topk_workspace_bytes(dims: Dims, T: int, score_stride: int) -> int:
@@ -252,7 +281,7 @@ def topk_workspace(dims: Dims, T: int, score_stride: int, device="cuda") -> torc
 
 
 def topk_select(dims: Dims, scores: torch.Tensor, seqs: Seqs, q_seq: torch.Tensor, q_pos: torch.Tensor,
-                pool_ids: torch.Tensor, workspace: torch.Tensor | None = None, stream=None):
+                pool_ids: torch.Tensor, workspace: torch.Tensor | None = None, stream=None, prepare: bool = False):
     """pool_ids [T, select_k] (int32): ascending selected pool ids, -1 padded."""
     _check(scores, torch.float32, "scores")
     _check(pool_ids, torch.int32, "pool_ids")
@@ -263,15 +292,15 @@ def topk_select(dims: Dims, scores: torch.Tensor, seqs: Seqs, q_seq: torch.Tenso
     if workspace is not None:
         _check(workspace, workspace.dtype, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
-    _raise("dsa_topk_select", lib().dsa_topk_select(
+    return _call("dsa_topk_select", prepare, 
         ctypes.byref(dims), scores.data_ptr(), scores.shape[1], ctypes.byref(seqs._c()), seqs.num_seqs,
         q_seq.data_ptr(), q_pos.data_ptr(), T, pool_ids.data_ptr(), _ptr(workspace), ws_bytes,
-        _stream(stream)))
+        _stream(stream))
 
 
 def topk_select_expand(dims: Dims, scores: torch.Tensor, seqs: Seqs, q_seq: torch.Tensor, q_pos: torch.Tensor,
                        indices: torch.Tensor, pool_ids: torch.Tensor | None = None,
-                       workspace: torch.Tensor | None = None, stream=None):
+                       workspace: torch.Tensor | None = None, stream=None, prepare: bool = False):
     """Top-k selection written straight as index lists [T, out_width] (and pool ids if given)."""
     _check(scores, torch.float32, "scores")
     _check(indices, torch.int32, "indices")
@@ -284,22 +313,22 @@ def topk_select_expand(dims: Dims, scores: torch.Tensor, seqs: Seqs, q_seq: torc
     if workspace is not None:
         _check(workspace, workspace.dtype, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
-    _raise("dsa_topk_select_expand", lib().dsa_topk_select_expand(
+    return _call("dsa_topk_select_expand", prepare, 
         ctypes.byref(dims), scores.data_ptr(), scores.shape[1], ctypes.byref(seqs._c()), seqs.num_seqs,
         q_seq.data_ptr(), q_pos.data_ptr(), T, _ptr(pool_ids), indices.data_ptr(), _ptr(workspace), ws_bytes,
-        _stream(stream)))
+        _stream(stream))
 
 
 def expand_selection(dims: Dims, pool_ids: torch.Tensor, seqs: Seqs, q_seq: torch.Tensor,
-                     q_pos: torch.Tensor, indices: torch.Tensor, stream=None):
+                     q_pos: torch.Tensor, indices: torch.Tensor, stream=None, prepare: bool = False):
     """indices [T, out_width] (int32) from pool_ids [T, select_k]."""
     _check(pool_ids, torch.int32, "pool_ids")
     _check(indices, torch.int32, "indices")
     _check(q_seq, torch.int32, "q_seq")
     _check(q_pos, torch.int32, "q_pos")
-    _raise("dsa_expand_selection", lib().dsa_expand_selection(
+    return _call("dsa_expand_selection", prepare, 
         ctypes.byref(dims), pool_ids.data_ptr(), ctypes.byref(seqs._c()), seqs.num_seqs,
-        q_seq.data_ptr(), q_pos.data_ptr(), q_pos.shape[0], indices.data_ptr(), _stream(stream)))
+        q_seq.data_ptr(), q_pos.data_ptr(), q_pos.shape[0], indices.data_ptr(), _stream(stream))
 
 
 def sparse_mla_workspace_bytes(dims: Dims, T: int, num_splits: int = 0) -> int:
@@ -308,7 +337,7 @@ def sparse_mla_workspace_bytes(dims: Dims, T: int, num_splits: int = 0) -> int:
 
 def sparse_mla(dims: Dims, q: torch.Tensor, cache: torch.Tensor, indices: torch.Tensor, scale: float,
                out: torch.Tensor, lse: torch.Tensor | None = None, num_splits: int = 0,
-               workspace: torch.Tensor | None = None, stream=None):
+               workspace: torch.Tensor | None = None, stream=None, prepare: bool = False):
     """out [T, H, D] = sparse NoPE MLA of q [T, H, D] over the INT8 rows listed in indices [T, W]."""
     if q.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("q must be bf16 or fp32")
@@ -325,10 +354,10 @@ def sparse_mla(dims: Dims, q: torch.Tensor, cache: torch.Tensor, indices: torch.
     if workspace is not None:
         _check(workspace, workspace.dtype, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
-    _raise("dsa_sparse_mla", lib().dsa_sparse_mla(
+    return _call("dsa_sparse_mla", prepare, 
         ctypes.byref(dims), q.data_ptr(), _dt(q), cache.data_ptr(), cache.shape[0], indices.data_ptr(),
         T, float(scale), out.data_ptr(), _dt(out), _ptr(lse), int(num_splits), _ptr(workspace), ws_bytes,
-        _stream(stream)))
+        _stream(stream))
 
 
 def index_scores_select_workspace(dims: Dims, T: int, score_stride: int, device="cuda") -> torch.Tensor | None:
@@ -338,7 +367,7 @@ def index_scores_select_workspace(dims: Dims, T: int, score_stride: int, device=
 
 def index_scores_select(dims: Dims, q_idx: torch.Tensor, w: torch.Tensor, pools: torch.Tensor, seqs: Seqs,
                         q_seq: torch.Tensor, q_pos: torch.Tensor, scores: torch.Tensor, indices: torch.Tensor,
-                        pool_ids: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+                        pool_ids: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None, prepare: bool = False):
     """index_scores then topk_select_expand (decode batches: one scoring pass that also keeps group lists)."""
     _check(q_idx, torch.bfloat16, "q_idx")
     _check(w, torch.float32, "w")
@@ -353,30 +382,30 @@ def index_scores_select(dims: Dims, q_idx: torch.Tensor, w: torch.Tensor, pools:
     if workspace is not None:
         _check(workspace, workspace.dtype, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
-    _raise("dsa_index_scores_select", lib().dsa_index_scores_select(
+    return _call("dsa_index_scores_select", prepare, 
         ctypes.byref(dims), q_idx.data_ptr(), w.data_ptr(), pools.data_ptr(), ctypes.byref(seqs._c()),
         seqs.num_seqs, q_seq.data_ptr(), q_pos.data_ptr(), q_pos.shape[0], scores.shape[1], scores.data_ptr(),
-        _ptr(pool_ids), indices.data_ptr(), _ptr(workspace), ws_bytes, _stream(stream)))
+        _ptr(pool_ids), indices.data_ptr(), _ptr(workspace), ws_bytes, _stream(stream))
 
 
 def index_scores_groups(dims: Dims, q_idx: torch.Tensor, w: torch.Tensor, pools: torch.Tensor, seqs: Seqs,
                         q_seq: torch.Tensor, q_pos: torch.Tensor, scores: torch.Tensor, workspace: torch.Tensor,
-                        stream=None):
+                        stream=None, prepare: bool = False):
     """Decode scoring pass that also keeps each 64-pool group's best pools in `workspace`."""
     for name, t, dt in (("q_idx", q_idx, torch.bfloat16), ("w", w, torch.float32), ("pools", pools, torch.bfloat16),
                         ("q_seq", q_seq, torch.int32), ("q_pos", q_pos, torch.int32),
                         ("scores", scores, torch.float32)):
         _check(t, dt, name)
     _check(workspace, workspace.dtype, "workspace")
-    _raise("dsa_index_scores_groups", lib().dsa_index_scores_groups(
+    return _call("dsa_index_scores_groups", prepare, 
         ctypes.byref(dims), q_idx.data_ptr(), w.data_ptr(), pools.data_ptr(), ctypes.byref(seqs._c()),
         seqs.num_seqs, q_seq.data_ptr(), q_pos.data_ptr(), q_pos.shape[0], scores.shape[1], scores.data_ptr(),
-        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
 
 
 def topk_select_groups(dims: Dims, scores: torch.Tensor, seqs: Seqs, q_seq: torch.Tensor, q_pos: torch.Tensor,
                        indices: torch.Tensor, workspace: torch.Tensor, pool_ids: torch.Tensor | None = None,
-                       stream=None):
+                       stream=None, prepare: bool = False):
     """Selection and expansion from the group lists index_scores_groups left in `workspace`."""
     _check(scores, torch.float32, "scores")
     _check(indices, torch.int32, "indices")
@@ -385,10 +414,10 @@ def topk_select_groups(dims: Dims, scores: torch.Tensor, seqs: Seqs, q_seq: torc
     if pool_ids is not None:
         _check(pool_ids, torch.int32, "pool_ids")
     _check(workspace, workspace.dtype, "workspace")
-    _raise("dsa_topk_select_groups", lib().dsa_topk_select_groups(
+    return _call("dsa_topk_select_groups", prepare, 
         ctypes.byref(dims), scores.data_ptr(), scores.shape[1], ctypes.byref(seqs._c()), seqs.num_seqs,
         q_seq.data_ptr(), q_pos.data_ptr(), q_pos.shape[0], _ptr(pool_ids), indices.data_ptr(),
-        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
 
 
 def decode_step_workspace_bytes(dims: Dims, T: int, score_stride: int) -> int:
@@ -412,7 +441,7 @@ def decode_step_error(workspace: torch.Tensor) -> int:
 def decode_step(dims: Dims, q_idx: torch.Tensor, w: torch.Tensor, pools: torch.Tensor, seqs: Seqs,
                 q_seq: torch.Tensor, q_pos: torch.Tensor, score_stride: int, q: torch.Tensor, cache: torch.Tensor,
                 scale: float, out: torch.Tensor, workspace: torch.Tensor, lse: torch.Tensor | None = None,
-                pool_ids: torch.Tensor | None = None, indices: torch.Tensor | None = None, stream=None):
+                pool_ids: torch.Tensor | None = None, indices: torch.Tensor | None = None, stream=None, prepare: bool = False):
     """One launch: scores, top-k, expansion and sparse MLA for a decode batch."""
     _check(q_idx, torch.bfloat16, "q_idx")
     _check(w, torch.float32, "w")
@@ -429,11 +458,11 @@ def decode_step(dims: Dims, q_idx: torch.Tensor, w: torch.Tensor, pools: torch.T
         if t is not None:
             _check(t, torch.float32 if name == "lse" else torch.int32, name)
     T = q_pos.shape[0]
-    _raise("dsa_decode_step", lib().dsa_decode_step(
+    return _call("dsa_decode_step", prepare, 
         ctypes.byref(dims), q_idx.data_ptr(), w.data_ptr(), pools.data_ptr(), ctypes.byref(seqs._c()),
         seqs.num_seqs, q_seq.data_ptr(), q_pos.data_ptr(), T, int(score_stride), q.data_ptr(), DSA_BF16,
         cache.data_ptr(), cache.shape[0], float(scale), out.data_ptr(), _dt(out), _ptr(lse), _ptr(pool_ids),
-        _ptr(indices), workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+        _ptr(indices), workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
 
 
 __all__ = [

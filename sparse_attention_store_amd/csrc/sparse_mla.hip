@@ -319,14 +319,23 @@ __global__ __launch_bounds__(256) void k_mla_mfma(
 }
 
 // Merge split partials in split order: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-// The (m, l) pairs go through LDS first; then every thread issues the loads of
-// its 4 columns for all non-empty splits before accumulating them in order.
+// Every thread issues the loads of its 4 columns of the first kPre splits
+// together with the (m, l) loads (one round trip, not two: an empty split's
+// partial was never written, so it is dropped by a select, never multiplied);
+// the (m, l) pairs go through LDS; the partials are accumulated in split order.
+constexpr int kPre = 24;
 __global__ __launch_bounds__(128) void k_mla_combine(
     const float* __restrict__ part_o, const MlaPartial* __restrict__ part_ml, int splits, int H,
     void* __restrict__ out, int out_f32, float* __restrict__ lse) {
     __shared__ float wgt[kMaxSplits];
     __shared__ float s_M, s_L;
     const int h = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+    const float* base = part_o + ((int64_t)t * splits * H + h) * kD + tid * 4;
+    const int64_t sstride = (int64_t)H * kD;
+    f32x4 pre[kPre];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u)
+        pre[u] = u < splits ? *reinterpret_cast<const f32x4*>(base + u * sstride) : f32x4{0.f, 0.f, 0.f, 0.f};
     if (tid < 64) {
         MlaPartial p = {-INFINITY, 0.f};
         if (tid < splits) p = part_ml[((int64_t)t * splits + tid) * H + h];
@@ -345,19 +354,17 @@ __global__ __launch_bounds__(128) void k_mla_combine(
     lds_barrier();
     const float L = s_L;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const float* base = part_o + ((int64_t)t * splits * H + h) * kD + tid * 4;
-    const int64_t sstride = (int64_t)H * kD;
-    int s = 0;
-    for (; s + 8 <= splits; s += 8) {
-        f32x4 v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            v[u] = wgt[s + u] > 0.f ? *reinterpret_cast<const f32x4*>(base + (s + u) * sstride) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int u = 0; u < 8; ++u) acc += v[u] * wgt[s + u];
+    for (int u = 0; u < kPre; ++u) {
+        const float wu = u < splits ? wgt[u] : 0.f;
+        const f32x4 c = pre[u] * wu;
+        if (wu > 0.f) acc += c;
     }
-    for (; s < splits; ++s)
-        if (wgt[s] > 0.f) acc += *reinterpret_cast<const f32x4*>(base + s * sstride) * wgt[s];
+    for (int s = kPre; s < splits; ++s) {
+        const float ws = wgt[s];
+        const f32x4 v = *reinterpret_cast<const f32x4*>(base + s * sstride);
+        if (ws > 0.f) acc += v * ws;
+    }
     const float inv = L > 0.f ? 1.0f / L : 0.f;
     acc *= inv;
     const int64_t orow = ((int64_t)t * H + h) * kD + tid * 4;

@@ -242,7 +242,22 @@ __global__ __launch_bounds__(kBNT) void k_topk_groups(
     __shared__ uint32_t gcount[kMaxGroups];
     __shared__ uint32_t gpicked[kMaxGroups];
     __shared__ int fail;
+    static_assert(KPT == 8 && kBNT == kMaxGroups, "8 list slots and one group count per thread");
     const int t = blockIdx.x, tid = threadIdx.x;
+    const int s0 = tid * KPT;
+    // every load at once, before the row geometry they do not depend on: this
+    // thread's group count and its KPT slots
+    const uint32_t gc = (uint32_t)cand_n[(int64_t)t * kMaxGroups + tid];
+    uint64_t raw[KPT];
+    {
+        const u32x4* src = reinterpret_cast<const u32x4*>(cand + (int64_t)t * kGroupCandCap + s0);
+#pragma unroll
+        for (int j = 0; j < KPT; j += 2) {
+            const u32x4 v = src[j / 2];
+            raw[j] = ((uint64_t)v[1] << 32) | v[0];
+            raw[j + 1] = ((uint64_t)v[3] << 32) | v[2];
+        }
+    }
     int b, f, qp, n_vis;
     query_geom(first_valid, q_seq, q_pos, t, b, f, qp, n_vis);
     const int n = min(n_vis, stride);
@@ -254,26 +269,17 @@ __global__ __launch_bounds__(kBNT) void k_topk_groups(
     const int m = group_quota(select_k, n);
     const int msh = __ffs(m) - 1;
     const int M = groups * m;
-    const int s0 = tid * KPT;
-    // every load at once: this thread's group count and its KPT slots
-    const uint32_t gc = tid < groups ? (uint32_t)cand_n[(int64_t)t * kMaxGroups + tid] : 0u;
-    uint64_t raw[KPT];
-    const u32x4* src = reinterpret_cast<const u32x4*>(cand + (int64_t)t * kGroupCandCap + s0);
-#pragma unroll
-    for (int j = 0; j < KPT; j += 2) {
-        const u32x4 v = src[j / 2];
-        raw[j] = ((uint64_t)v[1] << 32) | v[0];
-        raw[j + 1] = ((uint64_t)v[3] << 32) | v[2];
-    }
     gcount[tid] = gc;
     gpicked[tid] = 0u;
     if (tid == 0) fail = 0;
     lds_barrier();
+    // a thread's 8 slots lie in one group (m >= 8): one count, read unconditionally
+    const uint32_t gcnt = gcount[min(s0, M - 1) >> msh] & (kGroupDropped - 1);
     uint32_t key[KPT];
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
         const int sl = s0 + j;
-        const bool ok = sl < M && (sl & (m - 1)) < (int)(gcount[sl >> msh] & (kGroupDropped - 1));
+        const bool ok = sl < M && (uint32_t)(sl & (m - 1)) < gcnt;
         key[j] = ok ? (uint32_t)(raw[j] >> 32) : 0u;
     }
     const uint32_t picks = select_top_slots<kBNT, KPT>(key, (uint32_t)select_k, T);

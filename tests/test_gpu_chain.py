@@ -138,3 +138,25 @@ def test_chain_full_size_sampled(harness, name):
     _check_chain(dw, queries, pool_sample=64, allow_swaps_frac=0.25)
     del dw
     torch.cuda.empty_cache()
+
+
+def test_prepared_calls_match_the_calls(harness):
+    """The prepared (validated-once) calls give the same bits as the calls."""
+    import torch
+    wl = syn.get("mini_decode")
+    dw = harness.DeviceWorkload(wl, replicas=2)
+    say("prepared calls mini_decode")
+    for r in range(2):
+        dw.step(r)
+        torch.cuda.synchronize()
+        ref = [x.clone() for x in (dw.scores, dw.pool_ids, dw.indices, dw.out, dw.lse)]
+        for x in (dw.pool_ids, dw.indices):
+            x.fill_(0x5A5A5A5A)
+        for x in (dw.scores, dw.out, dw.lse):
+            x.fill_(float("nan"))
+        dw.step_fast(r)
+        dw.step_fast(r)                 # a second launch of the same prepared calls
+        torch.cuda.synchronize()
+        for name, a, b in zip(("scores", "pool_ids", "indices", "out", "lse"), ref,
+                              (dw.scores, dw.pool_ids, dw.indices, dw.out, dw.lse)):
+            assert torch.equal(a, b), (name, r)
