@@ -26,7 +26,7 @@ METRIC = "decode tok-steps/s (indexer+topk+sparse MLA) @262k ctx B=8; % HBM peak
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 WORKLOAD = "decode_262k_b8"
 _CSRC = os.path.join(ROOT, "sparse_attention_store_amd", "csrc")
-SCORES_SRC = [os.path.join(_CSRC, f) for f in ("index_scores.hip", "scores_core.h", "topk_core.h", "dsa_common.h")]
+SCORES_SRC = [os.path.join(_CSRC, f) for f in ("index_scores.hip", "scores_core.h", "topk_core.h", "new_tokens.h", "dsa_common.h")]
 STEP_SRC = [os.path.join(_CSRC, f) for f in ("decode_step.hip", "mla_core.h", "scores_core.h", "topk_core.h",
                                              "dsa_common.h")]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "index_scores_decode_262k_b8_traffic.md")
@@ -56,8 +56,8 @@ def algorithmic_bytes(wl) -> dict:
             + T * 4 * d.mla_heads * d.latent_dim + T * 4 * d.out_width + T * (2 * d.latent_dim + d.row_bytes)
             + new_pools * (2 * d.kpool * d.idx_dim * 2 + d.idx_dim * 2))
     new_tokens = T * (2 * d.latent_dim + d.row_bytes) + new_pools * (2 * d.kpool * d.idx_dim * 2 + d.idx_dim * 2)
-    return {"step": step, "scores_kernel": scores, "decode_kernel": step - new_tokens, "pools": tot_pools,
-            "rows": tot_rows}
+    return {"step": step, "scores_kernel": scores + new_tokens, "decode_kernel": step - new_tokens,
+            "pools": tot_pools, "rows": tot_rows}
 
 
 def _source_hash(srcs) -> str:
@@ -252,7 +252,7 @@ def main():
     # The timed loop launches through prepared calls (validated and converted
     # once per replica): each launch then costs one ctypes call on the host, so
     # the host keeps ahead of the GPU.
-    timed_stages = ["append", "decode"] if fused else ["append", "scores_groups", "select_groups", "attention"]
+    timed_stages = ["append", "decode"] if fused else ["append_scores", "select_groups", "attention"]
     for r in range(R):
         for st in timed_stages:
             dw.bound(st, r)
@@ -274,15 +274,17 @@ def main():
     start.record(stream)
     for i in range(args.steps):
         r = i % R
-        dw.run("append", r)
-        if i in ev_s:
-            ev_s[i].record(stream)
         if fused:
+            dw.run("append", r)
+            if i in ev_s:
+                ev_s[i].record(stream)
             dw.run("decode", r)
             if i in ev_e:
                 ev_e[i].record(stream)
         else:
-            dw.run("scores_groups", r)
+            if i in ev_s:
+                ev_s[i].record(stream)
+            dw.run("append_scores", r)
             if i in ev_e:
                 ev_e[i].record(stream)
             dw.run("select_groups", r)
@@ -299,7 +301,7 @@ def main():
         names = ["append_tokens", "decode_step"]
         fns = [lambda r: dw.run("append", r), lambda r: dw.run("decode", r)]
     else:
-        names = ["append_tokens", "index_scores_groups", "topk_select_groups", "sparse_mla"]
+        names = ["append_scores_groups", "topk_select_groups", "sparse_mla"]
         fns = [lambda r, st=st: dw.run(st, r) for st in timed_stages]
     n_b = min(args.steps, 50)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(n_b)]
@@ -316,7 +318,7 @@ def main():
     # it alone (cycling the replicas, so its pools come from HBM) between one
     # event pair.  An event pair around a single launch inside a step also
     # counts that launch's dispatch latency (reported as avg_launch_us_in_step).
-    dom_stage = "decode" if fused else "scores_groups"
+    dom_stage = "decode" if fused else "append_scores"
     dom = lambda r: dw.run(dom_stage, r)
     n_burst = 4 * R
     b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -351,7 +353,7 @@ def main():
                    "out_width": wl.dims.out_width, "replicas": R},
         "pct_hbm_peak": round(100.0 * ab["step"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "bytes_per_step": ab["step"],
-        "roofline": {"kernel": "decode_step (k_decode_step)" if fused else "index_scores_groups (k_scores_groups)",
+        "roofline": {"kernel": "decode_step (k_decode_step)" if fused else "append_scores_groups (k_scores_groups)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile(PMC_SUMMARY_STEP if fused else PMC_SUMMARY,

@@ -173,6 +173,15 @@ class DeviceWorkload:
         return dsa.index_scores_groups(self.dims, self.q_idx, self.w, self.pools[r], self.seqs, self.q_seq,
                                        self.q_pos, self.scores, self._ws_ss(), prepare=prepare)
 
+    def step_append_scores(self, r: int = 0, prepare: bool = False):
+        """The new tokens and the scoring pass with group lists (one launch for bf16 tokens)."""
+        if self.latent_q.dtype != self.k.dtype:
+            return [self.step_store(r, prepare), self.step_pools(r, prepare), self.step_scores_groups(r, prepare)]
+        return dsa.append_scores_groups(self.dims, self.latent_q, self.slots_q, self.caches[r], self.k, self.gate,
+                                        self.ln_w, self.ln_b, self.step_pool_begin, self.step_pool_end,
+                                        self.step_max_pools, self.pools[r], self.q_idx, self.w, self.seqs, self.q_seq,
+                                        self.q_pos, self.scores, self._ws_ss(), prepare=prepare)
+
     def step_select_groups(self, r: int = 0, prepare: bool = False):
         return dsa.topk_select_groups(self.dims, self.scores, self.seqs, self.q_seq, self.q_pos, self.indices,
                                       self._ws_ss(), pool_ids=self.pool_ids, prepare=prepare)
@@ -213,9 +222,10 @@ class DeviceWorkload:
             call()
 
     def step_fast(self, r: int = 0):
-        """step() through prepared calls."""
-        self.run("append", r)
-        self.run("scores_select", r)
+        """The pass through prepared calls: the new tokens with the scoring
+        pass (one launch), the selection, then attention."""
+        self.run("append_scores", r)
+        self.run("select_groups", r)
         self.run("attention", r)
 
     def step_fused(self, r: int = 0):

@@ -233,6 +233,30 @@ int dsa_topk_select_groups(const dsa_dims* dims, const float* scores, int32_t sc
                            const dsa_seqs* seqs, int32_t num_seqs, const int32_t* q_seq,
                            const int32_t* q_pos, int32_t T, int32_t* pool_ids, int32_t* indices,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * append_scores_groups -- dsa_append_tokens followed by
+ * dsa_index_scores_groups, with the same results (cache rows, pools, scores
+ * and the group lists in the workspace), in one launch when the new tokens
+ * are bf16 and idx_dim is 128 (else the two launches).  The scoring part of
+ * the launch runs while the new rows and pools are still being written: a
+ * wave whose 64-pool group holds a pool the step completes builds that pool
+ * itself (the same arithmetic as dsa_index_pools, so the same bits) and
+ * scores it from registers, never from the pools buffer.
+ *   dtype .. pools      as dsa_append_tokens (seqs and num_seqs shared)
+ *   q_idx .. workspace  as dsa_index_scores_groups; pools is the buffer both
+ *                       parts use
+ *   T == 0 or score_stride == 0 does the new tokens only.
+ * Supported: what both calls support; DSA_ERR_UNSUPPORTED otherwise.
+ */
+int dsa_append_scores_groups(const dsa_dims* dims, int dtype, const void* latent, int64_t n, int64_t ld,
+                             const int64_t* slots, int8_t* cache, int64_t cache_rows, const void* k,
+                             const void* gate, const float* ln_w, const float* ln_b,
+                             const int32_t* pool_begin, const int32_t* pool_end, int32_t max_pools,
+                             uint16_t* pools, const uint16_t* q_idx, const float* w, const dsa_seqs* seqs,
+                             int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos, int32_t T,
+                             int32_t score_stride, float* scores, void* workspace, size_t workspace_bytes,
+                             void* stream);
 int dsa_index_scores_select(const dsa_dims* dims, const uint16_t* q_idx, const float* w,
                             const uint16_t* pools, const dsa_seqs* seqs, int32_t num_seqs,
                             const int32_t* q_seq, const int32_t* q_pos, int32_t T,

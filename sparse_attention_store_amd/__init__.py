@@ -111,6 +111,8 @@ def lib() -> ctypes.CDLL:
             "dsa_index_scores_select": (ctypes.c_int, [DP, P, P, P, SP, I32, P, P, I32, I32, P, P, P, P, SZ, P]),
             "dsa_index_scores_groups": (ctypes.c_int, [DP, P, P, P, SP, I32, P, P, I32, I32, P, P, SZ, P]),
             "dsa_topk_select_groups": (ctypes.c_int, [DP, P, I32, SP, I32, P, P, I32, P, P, P, SZ, P]),
+            "dsa_append_scores_groups": (ctypes.c_int, [DP, ctypes.c_int, P, I64, I64, P, P, I64, P, P, P, P, P, P,
+                                                        I32, P, P, P, SP, I32, P, P, I32, I32, P, P, SZ, P]),
             "dsa_decode_step_workspace_bytes": (SZ, [DP, I32, I32]),
             "dsa_decode_step": (ctypes.c_int, [DP, P, P, P, SP, I32, P, P, I32, I32, P, ctypes.c_int, P, I64, F,
                                                P, ctypes.c_int, P, P, P, P, SZ, P]),
@@ -401,6 +403,38 @@ def index_scores_groups(dims: Dims, q_idx: torch.Tensor, w: torch.Tensor, pools:
         ctypes.byref(dims), q_idx.data_ptr(), w.data_ptr(), pools.data_ptr(), ctypes.byref(seqs._c()),
         seqs.num_seqs, q_seq.data_ptr(), q_pos.data_ptr(), q_pos.shape[0], scores.shape[1], scores.data_ptr(),
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def append_scores_groups(dims: Dims, latent: torch.Tensor, slots: torch.Tensor, cache: torch.Tensor,
+                         k: torch.Tensor, gate: torch.Tensor, ln_w: torch.Tensor, ln_b: torch.Tensor,
+                         pool_begin: torch.Tensor, pool_end: torch.Tensor, max_pools: int, pools: torch.Tensor,
+                         q_idx: torch.Tensor, w: torch.Tensor, seqs: Seqs, q_seq: torch.Tensor, q_pos: torch.Tensor,
+                         scores: torch.Tensor, workspace: torch.Tensor, stream=None, prepare: bool = False):
+    """append_tokens then index_scores_groups (one launch for bf16 new tokens)."""
+    if latent.dim() != 2 or (latent.shape[0] > 0 and latent.stride(1) != 1):
+        raise ValueError("latent must be [n, D] with unit stride in D")
+    if latent.dtype not in (torch.bfloat16, torch.float32) or not latent.is_cuda:
+        raise TypeError("latent must be a bf16/fp32 device tensor")
+    _check(slots, torch.int64, "slots")
+    _check(cache, torch.int8, "cache")
+    if slots.numel() != latent.shape[0]:
+        raise ValueError("slots must have one entry per latent row")
+    for name, t in (("k", k), ("gate", gate)):
+        _check(t, latent.dtype, name)
+    for name, t, dt in (("ln_w", ln_w, torch.float32), ("ln_b", ln_b, torch.float32),
+                        ("pool_begin", pool_begin, torch.int32), ("pool_end", pool_end, torch.int32),
+                        ("pools", pools, torch.bfloat16), ("q_idx", q_idx, torch.bfloat16), ("w", w, torch.float32),
+                        ("q_seq", q_seq, torch.int32), ("q_pos", q_pos, torch.int32),
+                        ("scores", scores, torch.float32)):
+        _check(t, dt, name)
+    _check(workspace, workspace.dtype, "workspace")
+    return _call("dsa_append_scores_groups", prepare,
+        ctypes.byref(dims), _dt(latent), latent.data_ptr(), latent.shape[0], latent.stride(0), slots.data_ptr(),
+        cache.data_ptr(), cache.shape[0], k.data_ptr(), gate.data_ptr(), ln_w.data_ptr(), ln_b.data_ptr(),
+        pool_begin.data_ptr(), pool_end.data_ptr(), int(max_pools), pools.data_ptr(), q_idx.data_ptr(),
+        w.data_ptr(), ctypes.byref(seqs._c()), seqs.num_seqs, q_seq.data_ptr(), q_pos.data_ptr(), q_pos.shape[0],
+        scores.shape[1], scores.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream(stream))
 
 
 def topk_select_groups(dims: Dims, scores: torch.Tensor, seqs: Seqs, q_seq: torch.Tensor, q_pos: torch.Tensor,

@@ -258,6 +258,61 @@ int dsa_index_scores_groups(const dsa_dims* dims, const uint16_t* q_idx, const f
                                                           score_stride, scores, workspace, as_stream(stream)));
 }
 
+int dsa_append_scores_groups(const dsa_dims* dims, int dtype, const void* latent, int64_t n, int64_t ld,
+                             const int64_t* slots, int8_t* cache, int64_t cache_rows, const void* k,
+                             const void* gate, const float* ln_w, const float* ln_b, const int32_t* pool_begin,
+                             const int32_t* pool_end, int32_t max_pools, uint16_t* pools, const uint16_t* q_idx,
+                             const float* w, const dsa_seqs* seqs, int32_t num_seqs, const int32_t* q_seq,
+                             const int32_t* q_pos, int32_t T, int32_t score_stride, float* scores, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    // The new tokens' part: exactly what dsa_append_tokens checks.
+    int st = check_dims(dims);
+    if (st) return st;
+    if (dtype != DSA_F32 && dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    const int D = dims->latent_dim;
+    if (D != 64 && D != 128 && D != 256 && D != 512) return DSA_ERR_UNSUPPORTED;
+    if (dims->kpool != 4 || (dims->idx_dim != 128 && dims->idx_dim != 32)) return DSA_ERR_UNSUPPORTED;
+    if (n < 0 || cache_rows < 0 || max_pools < 0) return DSA_ERR_SIZE;
+    if (n > 0) {
+        if (!latent || !slots || !cache) return DSA_ERR_NULL;
+        if (ld < D) return DSA_ERR_SIZE;
+        const size_t esz = dtype == DSA_F32 ? 4 : 2;
+        if (!aligned(latent, 16) || (ld * esz) % 16 != 0 || !aligned(cache, 16)) return DSA_ERR_ALIGN;
+    }
+    // The scoring part: exactly what dsa_index_scores_groups checks.
+    st = groups_common(dims, seqs, num_seqs, T, score_stride, workspace, workspace_bytes);
+    if (st) return st;
+    if (max_pools > 0) {
+        st = check_seqs(seqs, num_seqs, false, true, true);
+        if (st) return st;
+        if (num_seqs > 65535) return DSA_ERR_SIZE;
+        if (!k || !gate || !ln_w || !ln_b || !pool_begin || !pool_end || !pools) return DSA_ERR_NULL;
+        if (!aligned(k, 4) || !aligned(gate, 4) || !aligned(pools, 4)) return DSA_ERR_ALIGN;
+    }
+    const bool scoring = T > 0 && score_stride > 0;
+    if (scoring) {
+        if (!q_idx || !w || !pools || !q_seq || !q_pos || !scores) return DSA_ERR_NULL;
+        if (!aligned(q_idx, 16) || !aligned(pools, 16) || !aligned(w, 16)) return DSA_ERR_ALIGN;
+    }
+    hipStream_t s = as_stream(stream);
+    const dsa_seqs none{};
+    if (!scoring || !dsa_host::append_scores_fused(*dims, dtype)) {
+        if (n > 0 || max_pools > 0) {
+            hipError_t e = dsa_host::launch_append_tokens(*dims, dtype, latent, n, ld, slots, cache, k, gate, ln_w,
+                                                          ln_b, max_pools > 0 ? *seqs : none,
+                                                          max_pools > 0 ? num_seqs : 0, pool_begin, pool_end,
+                                                          max_pools, pools, s);
+            if (e != hipSuccess) return DSA_ERR_HIP;
+        }
+        if (!scoring) return DSA_OK;
+        return hip_status(dsa_host::launch_scores_with_groups(*dims, q_idx, w, pools, *seqs, q_seq, q_pos, T,
+                                                              score_stride, scores, workspace, s));
+    }
+    return hip_status(dsa_host::launch_append_scores_groups(
+        *dims, latent, n, ld, slots, cache, k, gate, ln_w, ln_b, *seqs, max_pools > 0 ? num_seqs : 0, pool_begin,
+        pool_end, max_pools, pools, q_idx, w, q_seq, q_pos, T, score_stride, scores, workspace, s));
+}
+
 int dsa_topk_select_groups(const dsa_dims* dims, const float* scores, int32_t score_stride, const dsa_seqs* seqs,
                            int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos, int32_t T,
                            int32_t* pool_ids, int32_t* indices, void* workspace, size_t workspace_bytes,

@@ -117,10 +117,12 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Raw buffer descriptor over [base, base + bytes) (both wave-uniform).  Loads
-// through it take the base from SGPRs and a 32-bit lane offset; lane offsets
-// past `bytes` read zero, but the SGPR offset is outside that check, so
-// callers keep every access in bounds themselves.
+// Set bits of a wave mask in the lanes below this one (v_mbcnt: no per-lane
+// mask has to be built or kept).
+__device__ __forceinline__ int popc_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 // A value every lane of the wave holds, moved to SGPRs (the compiler cannot
 // always prove that a value read from LDS or derived from threadIdx is uniform).
 __device__ __forceinline__ int uniform32(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -129,6 +131,10 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t x) {
            (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
 }
 
+// Raw buffer descriptor over [base, base + bytes) (both wave-uniform).  Loads
+// through it take the base from SGPRs and a 32-bit lane offset; lane offsets
+// past `bytes` read zero, but the SGPR offset is outside that check, so
+// callers keep every access in bounds themselves.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
     void* b = reinterpret_cast<void*>(uniform64(reinterpret_cast<uint64_t>(base)));
     return __builtin_amdgcn_make_buffer_rsrc(b, (short)0, uniform32((int)bytes), 0x00020000);

@@ -35,6 +35,14 @@ hipError_t launch_scores_with_groups(const dsa_dims& d, const uint16_t* q_idx, c
                                      const uint16_t* pools, const dsa_seqs& seqs, const int32_t* q_seq,
                                      const int32_t* q_pos, int32_t T, int32_t stride, float* scores, void* ws,
                                      hipStream_t s);
+bool append_scores_fused(const dsa_dims& d, int dtype);
+hipError_t launch_append_scores_groups(const dsa_dims& d, const void* latent, int64_t n, int64_t ld,
+                                       const int64_t* slots, int8_t* cache, const void* k, const void* gate,
+                                       const float* ln_w, const float* ln_b, const dsa_seqs& seqs, int32_t num_seqs,
+                                       const int32_t* pool_begin, const int32_t* pool_end, int32_t max_pools,
+                                       uint16_t* pools, const uint16_t* q_idx, const float* w, const int32_t* q_seq,
+                                       const int32_t* q_pos, int32_t T, int32_t stride, float* scores, void* ws,
+                                       hipStream_t s);
 hipError_t launch_topk_groups(const dsa_dims& d, const float* scores, int32_t stride, const dsa_seqs& seqs,
                               const int32_t* q_seq, const int32_t* q_pos, int32_t T, int32_t* pool_ids,
                               int32_t* indices, const void* ws, hipStream_t s);

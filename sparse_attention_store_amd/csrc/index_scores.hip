@@ -16,6 +16,7 @@
 #include "dsa_launch.h"
 #include "scores_core.h"
 #include "topk_core.h"
+#include "new_tokens.h"
 
 namespace dsa {
 
@@ -153,6 +154,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_scores_mfma(
 // up to the row stride, are written as -inf.
 // With CANDS, each wave also keeps its group's best m pools for the selection
 // (keep_group_best) when the query has more visible pools than select_k.
+//
+// With AD (the latent width), the launch also does the step's new tokens
+// (the work of append_tokens): after the tiles, tasks of 4 waves store the
+// INT8 rows and build the completed pools with the same device code.  Those
+// pools may be scored by this very launch while they are being written, so a
+// wave whose group holds one rebuilds it from k and gate itself (again the
+// same code), puts it into its B-operand registers and scores that; the rows
+// it read from memory for it are never used.
 constexpr int kDecMaxT = 64;
 constexpr int kQStride = kDI + 8;          // bf16 per LDS row of the shared A operand
 struct QueryGeom {
@@ -161,37 +170,65 @@ struct QueryGeom {
     uint32_t ntiles;   // 256-pool tiles of visible pools
     int32_t ng;        // 64-pool groups of visible pools
     int32_t nn;        // visible pools, capped at the row stride
+    int64_t tok0;      // with new tokens: the sequence's first pooled token row
+    int32_t pb, pe;    // with new tokens: the pools this step completes
 };
-template <bool CANDS>
+struct AppendArgs {    // the step's new tokens (append_tokens' arguments)
+    const uint16_t* latent;
+    int64_t n, ld;
+    const int64_t* slots;
+    int8_t* cache;
+    int row_bytes;
+    const uint16_t* k;
+    const uint16_t* gate;
+    const float* ln_w;
+    const float* ln_b;
+    float eps;
+    const int64_t* tok_base;
+    const int32_t* pool_begin;
+    const int32_t* pool_end;
+    uint16_t* pools;   // the same buffer the tiles read
+    int pool_bx;       // 4-pool blocks per sequence (0: no pools)
+    int pool_tasks;    // num_seqs * pool_bx
+    int tasks;         // pool_tasks + ceil(n / 4)
+};
+template <bool CANDS, int AD>
 __global__ __launch_bounds__(256, 4) void k_scores_groups(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
-    const uint16_t* __restrict__ pools, const int32_t* __restrict__ first_valid,
+    const uint16_t* pools, const int32_t* __restrict__ first_valid,
     const int64_t* __restrict__ pool_base, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_pos, int T, int stride, float* __restrict__ scores,
-    int select_k, uint64_t* __restrict__ cand, int32_t* __restrict__ cand_n) {
+    int select_k, uint64_t* __restrict__ cand, int32_t* __restrict__ cand_n, AppendArgs ap) {
     __shared__ QueryGeom geom[kDecMaxT];
     __shared__ __attribute__((aligned(16))) uint16_t s_q[kHI * kQStride];
     __shared__ __attribute__((aligned(16))) float s_w[kHI];
+    __shared__ __attribute__((aligned(16))) uint32_t s_new[AD ? 4 : 1][kDI / 2];
     const int lane = threadIdx.x & 63;
     const int wave = uniform32(threadIdx.x >> 6);
     if (wave == 0) {
-        int nn = 0;
-        int64_t base = 0;
+        int nn = 0, pb = 0, pe = 0;
+        int64_t base = 0, tok0 = 0;
         if (lane < T) {
             const int b = q_seq[lane];
             const int f = first_valid[b];
             const int qp = q_pos[lane];
             nn = min(qp >= f ? (qp - f + 1) >> 2 : 0, stride);
             base = pool_base[b];
+            if (AD && ap.pool_bx > 0) {
+                pb = ap.pool_begin[b];
+                pe = min(ap.pool_end[b], pb + 4 * ap.pool_bx);   // what the pool tasks build
+                tok0 = ap.tok_base[b] + f;
+            }
         }
         const int ng = (nn + kGroupPools - 1) / kGroupPools;
         const uint32_t nt = (uint32_t)(ng + 3) >> 2;
         const uint32_t incl = wave_incl_sum_u32(nt);
-        geom[lane] = QueryGeom{base, incl - nt, nt, ng, nn};
+        geom[lane] = QueryGeom{base, incl - nt, nt, ng, nn, tok0, pb, pe};
     }
     lds_barrier();
     const int total = (int)(geom[63].first + geom[63].ntiles);
-    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    int tile = blockIdx.x;
+    for (; tile < total; tile += gridDim.x) {
         // query of the tile: the number of queries whose tiles all come before it
         const int t = __popcll(__ballot(geom[lane].first + geom[lane].ntiles <= (uint32_t)tile));
         const int grp = 4 * (tile - uniform32((int)geom[t].first)) + wave;
@@ -200,13 +237,17 @@ __global__ __launch_bounds__(256, 4) void k_scores_groups(
         const int p0 = grp * kGroupPools;
         // The tile's A operand: wave w loads heads 8 w .. 8 w + 7 (two 16-byte
         // pieces per lane), plus the head weights; issued before the pool rows.
+        // (Buffer loads: the lane part of each address is a 32-bit offset.)
         u32x4 qv[2];
+        {
+            const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(q_idx + (int64_t)t * (kHI * kDI), kHI * kDI * 2);
+            const uint32_t loff = (uint32_t)((lane >> 4) * (kDI * 2) + (lane & 15) * 16);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int k = lane + 64 * i;               // piece k: head 8 w + k / 16, dims 8 (k % 16) ..
-            qv[i] = *reinterpret_cast<const u32x4*>(q_idx + ((int64_t)t * kHI + 8 * wave + (k >> 4)) * kDI + 8 * (k & 15));
+            for (int i = 0; i < 2; ++i)              // piece lane + 64 i: head 8 w + 4 i + lane / 16, dims 8 (lane % 16) ..
+                qv[i] = ld_buf128(rq, loff, (uint32_t)((8 * wave + 4 * i) * (kDI * 2)));
         }
-        const float wt = lane < 8 ? w[(int64_t)t * kHI + 8 * wave + lane] : 0.f;
+        const float wt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            buffer_rsrc(w + (int64_t)t * kHI, kHI * 4), (uint32_t)min(lane, 7) * 4u, (uint32_t)(32 * wave), 0));
         // A wave past the query's last group re-reads the tile's first row
         // (unconditional loads keep the wait counts exact).
         u32x4 v[16];
@@ -221,9 +262,39 @@ __global__ __launch_bounds__(256, 4) void k_scores_groups(
         if (lane < 8) s_w[8 * wave + lane] = wt;
         lds_barrier();
         if (has) {
+            // A completed pool's row, built with the pool tasks' code, into s_new[wave].
+            auto build = [&](const PoolRaw128& r) {
+                PoolIn<kDI, uint16_t> in;
+                pool_raw_in(r, in);
+                uint16_t ov[2];
+                pool_values<kDI, uint16_t>(in, ap.ln_w, ap.ln_b, ap.eps, ov);
+                s_new[AD ? wave : 0][lane] = (uint32_t)ov[0] | ((uint32_t)ov[1] << 16);
+                wave_lds_fence();
+            };
             IdxQuery Q;
             load_idx_query_lds(s_q, kQStride, s_w, Q);
-            const float s = score_pool_group(Q, v);
+            float s = score_pool_group(Q, v);
+            if constexpr (AD != 0) {
+                // Score each rebuilt pool (score_pool_column: lane pp - p0 gets
+                // the bits the group's own scoring would have given it).
+                const int nb = max(uniform32(geom[t].pb), p0);
+                const int ne = min(min(uniform32(geom[t].pe), p0 + kGroupPools), n_vis);
+                const int64_t tok0 = (int64_t)uniform64((uint64_t)geom[t].tok0);
+                for (int pp = nb; pp < ne; ++pp) {
+                    PoolRaw128 r;
+                    pool_raw_load(ap.k, ap.gate, tok0 + 4 * (int64_t)pp, r);
+                    build(r);
+                    const int g = lane >> 4;
+                    u32x4 nb4[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) nb4[i] = *reinterpret_cast<const u32x4*>(&s_new[wave][16 * i + 4 * g]);
+                    IdxQuery Q2;                       // reloaded: Q is not kept through the rebuild
+                    load_idx_query_lds(s_q, kQStride, s_w, Q2);
+                    const float s2 = score_pool_column(Q2, nb4);
+                    if (lane == pp - p0) s = s2;
+                    wave_lds_fence();                  // s_new is rewritten by the next pool
+                }
+            }
             const int p = p0 + lane;
             if (p < stride) scores[(int64_t)t * stride + p] = p < n_vis ? s : -INFINITY;
             if constexpr (CANDS) {
@@ -235,6 +306,19 @@ __global__ __launch_bounds__(256, 4) void k_scores_groups(
             }
         }
         if (tile + (int)gridDim.x < total) lds_barrier();   // s_q is rewritten by the next tile
+    }
+    if constexpr (AD != 0) {
+        // New tokens: tasks total .. total + tasks - 1, 4 pools or 4 rows each.
+        for (; tile < total + ap.tasks; tile += gridDim.x) {
+            const int a = tile - total;
+            if (a < ap.pool_tasks)
+                index_pool_row<kDI, uint16_t>(ap.k, ap.gate, ap.ln_w, ap.ln_b, ap.eps, first_valid, ap.tok_base,
+                                              pool_base, ap.pool_begin, ap.pool_end, ap.pools, a / ap.pool_bx,
+                                              (a % ap.pool_bx) * 4 + wave);
+            else
+                store_int8_row<AD, false>(ap.latent, ap.n, ap.ld, ap.slots, ap.cache, ap.row_bytes,
+                                          (int64_t)(a - ap.pool_tasks) * 4 + wave);
+        }
     }
     // Pools past each query's last visible group.
     const int gw = blockIdx.x * 4 + wave, W = gridDim.x * 4;
@@ -294,9 +378,9 @@ hipError_t launch_index_scores(const dsa_dims& d, const uint16_t* q_idx, const f
     if (d.idx_heads == dsa::kHI && d.idx_dim == dsa::kDI) {
         if (T <= dsa::kDecMaxT) {
             // Decode: one wave per 64-pool group, a resident grid.
-            hipLaunchKernelGGL((dsa::k_scores_groups<false>), dim3(scores_groups_grid(T, stride)), dim3(256), 0, s,
-                               q_idx, w, pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, stride, scores,
-                               0, nullptr, nullptr);
+            hipLaunchKernelGGL((dsa::k_scores_groups<false, 0>), dim3(scores_groups_grid(T, stride)), dim3(256), 0,
+                               s, q_idx, w, pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, stride, scores,
+                               0, nullptr, nullptr, dsa::AppendArgs{});
         } else {
             // Prefill: 512 resident pools per workgroup, 64 queries per workgroup.
             const int qpb = 64;
@@ -330,9 +414,62 @@ hipError_t launch_scores_with_groups(const dsa_dims& d, const uint16_t* q_idx, c
     uint64_t* cand = reinterpret_cast<uint64_t*>(ws);
     int32_t* cand_n = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) +
                                                  ((size_t)T * dsa::kGroupCandCap * 8 + 255) / 256 * 256);
-    hipLaunchKernelGGL((dsa::k_scores_groups<true>), dim3(scores_groups_grid(T, stride)), dim3(256), 0, s, q_idx,
-                       w, pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, stride, scores,
-                       d.index_topk / d.kpool, cand, cand_n);
+    hipLaunchKernelGGL((dsa::k_scores_groups<true, 0>), dim3(scores_groups_grid(T, stride)), dim3(256), 0, s,
+                       q_idx, w, pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, stride, scores,
+                       d.index_topk / d.kpool, cand, cand_n, dsa::AppendArgs{});
+    return hipGetLastError();
+}
+
+bool append_scores_fused(const dsa_dims& d, int dtype) {
+    return dtype == DSA_BF16 && d.idx_dim == dsa::kDI &&
+           (d.latent_dim == 64 || d.latent_dim == 128 || d.latent_dim == 256 || d.latent_dim == 512);
+}
+
+hipError_t launch_append_scores_groups(const dsa_dims& d, const void* latent, int64_t n, int64_t ld,
+                                       const int64_t* slots, int8_t* cache, const void* k, const void* gate,
+                                       const float* ln_w, const float* ln_b, const dsa_seqs& seqs, int32_t num_seqs,
+                                       const int32_t* pool_begin, const int32_t* pool_end, int32_t max_pools,
+                                       uint16_t* pools, const uint16_t* q_idx, const float* w, const int32_t* q_seq,
+                                       const int32_t* q_pos, int32_t T, int32_t stride, float* scores, void* ws,
+                                       hipStream_t s) {
+    uint64_t* cand = reinterpret_cast<uint64_t*>(ws);
+    int32_t* cand_n = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) +
+                                                 ((size_t)T * dsa::kGroupCandCap * 8 + 255) / 256 * 256);
+    dsa::AppendArgs ap{};
+    ap.latent = reinterpret_cast<const uint16_t*>(latent);
+    ap.n = n;
+    ap.ld = ld;
+    ap.slots = slots;
+    ap.cache = cache;
+    ap.row_bytes = d.row_bytes;
+    ap.k = reinterpret_cast<const uint16_t*>(k);
+    ap.gate = reinterpret_cast<const uint16_t*>(gate);
+    ap.ln_w = ln_w;
+    ap.ln_b = ln_b;
+    ap.eps = d.ln_eps;
+    ap.tok_base = seqs.tok_base;
+    ap.pool_begin = pool_begin;
+    ap.pool_end = pool_end;
+    ap.pools = pools;
+    ap.pool_bx = max_pools > 0 ? (int)cdiv(max_pools, 4) : 0;
+    const int64_t pool_tasks = (int64_t)ap.pool_bx * num_seqs;
+    const int64_t tasks = pool_tasks + cdiv(n, 4);
+    if (tasks > 0x3FFFFFFF) return hipErrorInvalidValue;
+    ap.pool_tasks = (int)pool_tasks;
+    ap.tasks = (int)tasks;
+    const int64_t want = cdiv(cdiv(stride, dsa::kGroupPools), 4) * (int64_t)T + tasks;
+    const unsigned grid = (unsigned)std::min<int64_t>(std::max<int64_t>(want, 1), 4 * (int64_t)device_info().cu_count);
+#define DSA_APPEND_SCORES(D)                                                                                        \
+    hipLaunchKernelGGL((dsa::k_scores_groups<true, D>), dim3(grid), dim3(256), 0, s, q_idx, w, pools,             \
+                       seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, stride, scores, d.index_topk / d.kpool, \
+                       cand, cand_n, ap)
+    switch (d.latent_dim) {
+        case 512: DSA_APPEND_SCORES(512); break;
+        case 256: DSA_APPEND_SCORES(256); break;
+        case 128: DSA_APPEND_SCORES(128); break;
+        default: DSA_APPEND_SCORES(64); break;
+    }
+#undef DSA_APPEND_SCORES
     return hipGetLastError();
 }
 

@@ -96,6 +96,121 @@ __device__ __forceinline__ float load_val(const T* p);
 template <> __device__ __forceinline__ float load_val<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
 template <> __device__ __forceinline__ float load_val<float>(const float* p) { return *p; }
 
+// One pool's inputs: this lane's channels of the kpool token rows of k and
+// gate, from token row tok0 on.
+template <int DI, typename T>
+struct PoolIn {
+    static constexpr int KP = 4;
+    static constexpr int CPL = DI >= 64 ? DI / 64 : 1;       // channels per lane
+    float x[KP][CPL], g[KP][CPL];
+};
+
+template <int DI, typename T>
+__device__ __forceinline__ void pool_inputs(const T* __restrict__ k, const T* __restrict__ gate, int64_t tok0,
+                                            PoolIn<DI, T>& in) {
+    constexpr int KP = PoolIn<DI, T>::KP, CPL = PoolIn<DI, T>::CPL;
+    const int lane = threadIdx.x & 63;
+    const bool active = DI >= 64 || lane < DI;
+    const int c0 = active ? lane * CPL : 0;
+#pragma unroll
+    for (int s = 0; s < KP; ++s) {
+        const T* kr = k + (tok0 + s) * DI + c0;
+        const T* gr = gate + (tok0 + s) * DI + c0;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            in.x[s][c] = active ? load_val<T>(kr + c) : 0.f;
+            in.g[s][c] = active ? load_val<T>(gr + c) : 0.f;
+        }
+    }
+}
+
+// The same inputs for bf16 k and gate with idx_dim 128, kept as raw bit
+// pairs (one 4-byte load per token row and lane): no conversion waits on the
+// loads, so they can be issued long before the values are needed.
+struct PoolRaw128 {
+    uint32_t k[4], g[4];
+};
+
+// tok0 wave-uniform; the four rows of k and gate go through buffer
+// descriptors over them, so a lane's address is one 32-bit offset.
+__device__ __forceinline__ void pool_raw_load(const uint16_t* k, const uint16_t* gate, int64_t tok0, PoolRaw128& r) {
+    const uint32_t off = (uint32_t)(threadIdx.x & 63) * 4u;
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k + tok0 * 128, 4 * 128 * 2);
+    const __amdgpu_buffer_rsrc_t rg = buffer_rsrc(gate + tok0 * 128, 4 * 128 * 2);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        r.k[s] = __builtin_amdgcn_raw_buffer_load_b32(rk, off, (uint32_t)(256 * s), 0);
+        r.g[s] = __builtin_amdgcn_raw_buffer_load_b32(rg, off, (uint32_t)(256 * s), 0);
+    }
+}
+
+__device__ __forceinline__ void pool_raw_in(const PoolRaw128& r, PoolIn<128, uint16_t>& in) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        in.x[s][0] = __uint_as_float(r.k[s] << 16);
+        in.x[s][1] = __uint_as_float(r.k[s] & 0xFFFF0000u);
+        in.g[s][0] = __uint_as_float(r.g[s] << 16);
+        in.g[s][1] = __uint_as_float(r.g[s] & 0xFFFF0000u);
+    }
+}
+
+// The pool's values at this lane's channels (bf16, round to nearest even):
+// LayerNorm of each token row, then the slot softmax.  Every lane of the wave
+// calls it (wave sums); lanes past DI get zeros.
+// Contraction is off and the fused multiply-adds are written out, so every
+// kernel that inlines this produces the same bits.
+template <int DI, typename T>
+__device__ __forceinline__ void pool_values(const PoolIn<DI, T>& in, const float* __restrict__ ln_w,
+                                            const float* __restrict__ ln_b, float eps,
+                                            uint16_t (&outv)[PoolIn<DI, T>::CPL]) {
+#pragma clang fp contract(off)
+    constexpr int KP = PoolIn<DI, T>::KP, CPL = PoolIn<DI, T>::CPL;
+    const int lane = threadIdx.x & 63;
+    const bool active = DI >= 64 || lane < DI;
+    const int c0 = active ? lane * CPL : 0;
+    // ln_w / ln_b through buffer descriptors: the lane's offset is a 32-bit
+    // value, cheap to recompute, so no per-lane pointer is kept live.
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(ln_w, DI * 4), rb = buffer_rsrc(ln_b, DI * 4);
+    float wv[CPL], bv[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        wv[c] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw, (uint32_t)(c0 + c) * 4u, 0, 0));
+        bv[c] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, (uint32_t)(c0 + c) * 4u, 0, 0));
+    }
+    float y[KP][CPL];
+#pragma unroll
+    for (int s = 0; s < KP; ++s) {
+        float sum = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) sum += in.x[s][c];
+        const float mean = wave_sum(sum) * (1.0f / DI);
+        float sq = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const float dx = active ? in.x[s][c] - mean : 0.f;
+            sq = __builtin_fmaf(dx, dx, sq);
+        }
+        const float var = wave_sum(sq) * (1.0f / DI);
+        const float rstd = 1.0f / sqrtf(var + eps);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) y[s][c] = __builtin_fmaf((in.x[s][c] - mean) * rstd, wv[c], bv[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        float m = in.g[0][c];
+#pragma unroll
+        for (int s = 1; s < KP; ++s) m = fmaxf(m, in.g[s][c]);
+        float den = 0.f, num = 0.f;
+#pragma unroll
+        for (int s = 0; s < KP; ++s) {
+            const float e = expf(in.g[s][c] - m);
+            den += e;
+            num = __builtin_fmaf(e, y[s][c], num);
+        }
+        outv[c] = active ? (uint16_t)f32_to_bf16_rne(num / den) : (uint16_t)0;
+    }
+}
+
 // Pool pool_begin[b] + j of sequence b, if below pool_end[b] (one wave;
 // every lane of the wave calls it).
 template <int DI, typename T>
@@ -105,62 +220,17 @@ __device__ __forceinline__ void index_pool_row(
     const int64_t* __restrict__ tok_base, const int64_t* __restrict__ pool_base,
     const int32_t* __restrict__ pool_begin, const int32_t* __restrict__ pool_end,
     uint16_t* __restrict__ pools, int b, int j) {
-    constexpr int KP = 4;
-    constexpr int CPL = DI >= 64 ? DI / 64 : 1;       // channels per lane
+    constexpr int CPL = PoolIn<DI, T>::CPL;
     const int lane = threadIdx.x & 63;
     const int p = pool_begin[b] + j;
     if (p >= pool_end[b]) return;
-    const bool active = DI >= 64 || lane < DI;
-    const int c0 = active ? lane * CPL : 0;
-    const int64_t tok0 = tok_base[b] + first_valid[b] + (int64_t)KP * p;
-
-    float wv[CPL], bv[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) { wv[c] = ln_w[c0 + c]; bv[c] = ln_b[c0 + c]; }
-
-    float y[KP][CPL], g[KP][CPL];
-#pragma unroll
-    for (int s = 0; s < KP; ++s) {
-        const T* kr = k + (tok0 + s) * DI + c0;
-        const T* gr = gate + (tok0 + s) * DI + c0;
-        float x[CPL];
-        float sum = 0.f;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            x[c] = active ? load_val<T>(kr + c) : 0.f;
-            g[s][c] = active ? load_val<T>(gr + c) : 0.f;
-            sum += x[c];
-        }
-        const float mean = wave_sum(sum) * (1.0f / DI);
-        float sq = 0.f;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const float dx = active ? x[c] - mean : 0.f;
-            sq += dx * dx;
-        }
-        const float var = wave_sum(sq) * (1.0f / DI);
-        const float rstd = 1.0f / sqrtf(var + eps);
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) y[s][c] = (x[c] - mean) * rstd * wv[c] + bv[c];
-    }
-    if (!active) return;
-
+    const int64_t tok0 = tok_base[b] + first_valid[b] + 4 * (int64_t)p;
+    PoolIn<DI, T> in;
+    pool_inputs<DI, T>(k, gate, tok0, in);
     uint16_t outv[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        float m = g[0][c];
-#pragma unroll
-        for (int s = 1; s < KP; ++s) m = fmaxf(m, g[s][c]);
-        float den = 0.f, num = 0.f;
-#pragma unroll
-        for (int s = 0; s < KP; ++s) {
-            const float e = expf(g[s][c] - m);
-            den += e;
-            num += e * y[s][c];
-        }
-        outv[c] = (uint16_t)f32_to_bf16_rne(num / den);
-    }
-    uint16_t* dst = pools + (pool_base[b] + p) * (int64_t)DI + c0;
+    pool_values<DI, T>(in, ln_w, ln_b, eps, outv);
+    if (!(DI >= 64 || lane < DI)) return;
+    uint16_t* dst = pools + (pool_base[b] + p) * (int64_t)DI + lane * CPL;
     if constexpr (CPL == 2) {
         *reinterpret_cast<uint32_t*>(dst) = (uint32_t)outv[0] | ((uint32_t)outv[1] << 16);
     } else {

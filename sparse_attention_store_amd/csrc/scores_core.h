@@ -104,4 +104,25 @@ __device__ __forceinline__ float score_pool_group(const IdxQuery& Q, const u32x4
     return (j ? k1 : k0) + __shfl_xor(j ? k0 : k1, 16, 64);
 }
 
+// The score of one more pool, given as a single N-tile's B operand b[s]
+// (column c = lane % 16 holds it in every lane group): lane l gets exactly
+// what score_pool_group returns in lane l for a group whose N-tile l / 16
+// column l % 16 holds that pool -- the same MFMAs, the same per-lane partial
+// and the same two shuffle-adds in the same order.
+__device__ __forceinline__ float score_pool_column(const IdxQuery& Q, const u32x4 (&b)[4]) {
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        acc0 = mfma16(as_bf16x8(Q.a[0][s]), as_bf16x8(b[s]), acc0);
+        acc1 = mfma16(as_bf16x8(Q.a[1][s]), as_bf16x8(b[s]), acc1);
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sum += Q.w[0][i] * fmaxf(acc0[i], 0.f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sum += Q.w[1][i] * fmaxf(acc1[i], 0.f);
+    const float k = sum + __shfl_xor(sum, 32, 64);
+    return k + __shfl_xor(k, 16, 64);
+}
+
 }  // namespace dsa

@@ -220,11 +220,11 @@ __device__ __forceinline__ void keep_group_best(float s, bool valid, int p, int 
         }
         const unsigned long long eqm = __ballot(key == x);
         const int above = __popcll(__ballot(key > x));
-        const int eq_before = __popcll(eqm & ((1ull << lane) - 1ull));
+        const int eq_before = popc_below(eqm);
         pick = key > x || (key == x && eq_before < m - above);
     }
     const unsigned long long pm = __ballot(pick);
-    const int slot = __popcll(pm & ((1ull << lane) - 1ull));
+    const int slot = popc_below(pm);
     if (pick) st64(cand + (int64_t)group * m + slot, ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)p));
     if (lane == 0) st32(cand_n + group, (uint32_t)(__popcll(pm) | (nvalid > m ? kGroupDropped : 0)));
 }

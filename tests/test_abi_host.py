@@ -109,6 +109,37 @@ def test_append_tokens_argument_checks(dsa):
     assert call(n=0, mp=0, lat=None, sl=None, c=None, k=None, sq=None) == OK
 
 
+def test_append_scores_groups_argument_checks(dsa):
+    L = dsa.lib()
+    d = prod(dsa)
+    bd = ctypes.byref(d)
+    S = seqs(dsa)
+    ws_need = L.dsa_index_scores_select_workspace_bytes(bd, 8, 65536)
+    assert ws_need > 0
+
+    def call(dims=bd, dt=1, lat=FAKE, n=8, mp=1, k=FAKE, q_idx=FAKE, sq=ctypes.byref(S), T=8, stride=65536,
+             ws=FAKE, ws_bytes=ws_need):
+        return L.dsa_append_scores_groups(dims, dt, lat, n, 512, FAKE, FAKE, 64, k, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                          mp, FAKE, q_idx, FAKE, sq, 8, FAKE, FAKE, T, stride, FAKE, ws, ws_bytes,
+                                          None)
+    assert call(dims=None) == E_NULL
+    assert call(dt=7) == E_DTYPE
+    assert call(dims=ctypes.byref(prod(dsa, idx_dim=64))) == E_UNSUP
+    assert call(n=-1) == E_SIZE
+    assert call(lat=None) == E_NULL
+    assert call(lat=MISALIGNED) == E_ALIGN
+    assert call(ws_bytes=ws_need - 1) == E_WS
+    assert call(ws=None) == E_WS
+    assert call(T=65) == E_UNSUP                                # no group lists for more than 64 queries
+    assert call(sq=None) == E_NULL
+    assert call(k=None) == E_NULL
+    assert call(k=ctypes.c_void_p(0x10002)) == E_ALIGN
+    assert call(q_idx=None) == E_NULL
+    assert call(q_idx=MISALIGNED) == E_ALIGN
+    # nothing to do: no launch
+    assert call(n=0, mp=0, T=0, lat=None, k=None, q_idx=None, ws=None, ws_bytes=0) == OK
+
+
 def test_store_int8_argument_checks(dsa):
     L = dsa.lib()
     d = prod(dsa)

@@ -13,6 +13,7 @@ Reduced-size workloads are checked on every output; the full-size workloads
 (the pages' shapes) on every decode query and a seeded sample of prefill
 queries.
 """
+import ctypes
 import os
 
 import numpy as np
@@ -160,3 +161,57 @@ def test_prepared_calls_match_the_calls(harness):
         for name, a, b in zip(("scores", "pool_ids", "indices", "out", "lse"), ref,
                               (dw.scores, dw.pool_ids, dw.indices, dw.out, dw.lse)):
             assert torch.equal(a, b), (name, r)
+
+
+@pytest.mark.parametrize("name,span", [("mini_decode", 3), ("mini_decode", 70), ("mini_heavy", 5),
+                                       ("mini_heavy", 130), ("decode_32k", 4)])
+def test_append_scores_groups_matches_separate_calls(harness, name, span):
+    """append_scores_groups gives the bytes of append_tokens then
+    index_scores_groups (cache rows, pools, scores, group lists, and the
+    selection made from them), with the pools the step completes poisoned
+    beforehand: the single launch must rebuild them, not read them."""
+    import sparse_attention_store_amd as dsa
+    wl = syn.get(name)
+    if wl.T > 64:
+        pytest.skip("group lists are kept for at most 64 queries")
+    say(f"append_scores_groups {name} span={span}")
+    dw = harness.DeviceWorkload(wl)
+    d = wl.dims
+    pb, pe = [], []
+    for b in range(wl.B):
+        f = int(wl.first_valid[b])
+        nv = [(int(x) - f + 1) // d.kpool for x in wl.q_pos[wl.q_seq == b] if int(x) >= f]
+        e = max(nv) if nv else 0
+        pe.append(e)
+        pb.append(max(e - span, 0))
+    max_pools = max(e - s for s, e in zip(pb, pe))
+    begin = torch.tensor(pb, dtype=torch.int32, device="cuda")
+    end = torch.tensor(pe, dtype=torch.int32, device="cuda")
+    pools0 = dw.pools[0].clone()
+    for b in range(wl.B):
+        base = int(wl.pool_base[b])
+        pools0[base + pb[b]: base + pe[b]] = 7.0
+    cache0 = dw.caches[0].clone()
+    ws_bytes = dsa.lib().dsa_index_scores_select_workspace_bytes(ctypes.byref(dw.dims), wl.T, dw.stride)
+    outs = []
+    for fused in (False, True):
+        pools, cache = pools0.clone(), cache0.clone()
+        ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+        scores = torch.full_like(dw.scores, float("nan"))
+        idx = torch.full_like(dw.indices, 0x5A5A5A5A)
+        pid = torch.full_like(dw.pool_ids, 0x5A5A5A5A)
+        if fused:
+            dsa.append_scores_groups(dw.dims, dw.latent_q, dw.slots_q, cache, dw.k, dw.gate, dw.ln_w, dw.ln_b,
+                                     begin, end, max_pools, pools, dw.q_idx, dw.w, dw.seqs, dw.q_seq, dw.q_pos,
+                                     scores, ws)
+        else:
+            dsa.append_tokens(dw.dims, dw.latent_q, dw.slots_q, cache, dw.k, dw.gate, dw.ln_w, dw.ln_b, dw.seqs,
+                              begin, end, max_pools, pools)
+            dsa.index_scores_groups(dw.dims, dw.q_idx, dw.w, pools, dw.seqs, dw.q_seq, dw.q_pos, scores, ws)
+        dsa.topk_select_groups(dw.dims, scores, dw.seqs, dw.q_seq, dw.q_pos, idx, ws, pool_ids=pid)
+        torch.cuda.synchronize()
+        outs.append([x.cpu() for x in (cache, pools.view(torch.int16), scores, ws, idx, pid)])
+    # the separate calls rebuilt the poisoned pools exactly as the cache build did
+    assert torch.equal(outs[0][1], dw.pools[0].view(torch.int16).cpu())
+    for what, a, b in zip(("cache", "pools", "scores", "workspace", "indices", "pool_ids"), outs[0], outs[1]):
+        assert torch.equal(a, b), what
