@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kTile) void k_topk_tiles(
 // then one ordered pass that takes every key above the K-th and the first
 // `need` keys equal to it.  Writes K ids, ascending, to sel.
 template <int NT>
-__device__ void topk_stream_exact(const float* __restrict__ row, int n, int K, SelShared<NT>& S, int32_t* sel) {
+__device__ __noinline__ void topk_stream_exact(const float* __restrict__ row, int n, int K, SelShared<NT>& S, int32_t* sel) {
     static_assert(NT >= 256, "one thread per digit");
     const int tid = threadIdx.x;
     uint32_t prefix = 0u, mask = 0u, need = (uint32_t)K, total;
@@ -231,19 +231,41 @@ __global__ __launch_bounds__(kBNT) void k_topk_rows(
 }
 
 // Stage B over 64-pool group lists written by the scoring pass (one
-// 1024-thread workgroup per row; 8 slots per thread).
+// 1024-thread workgroup per row; 8 list slots per thread, so a thread's slots
+// lie in one group).  The selection is the one select_top_slots makes (range
+// bucketing, then an exact rank of the boundary bucket), arranged around as
+// few workgroup barriers as the data flow allows, since at one workgroup per
+// row the barriers are the cost:
+//   A  list slots are valid by position alone (empty slots hold key 0), so
+//      the per-wave min/max is published with the group counts;
+//   B, C per bucketing pass: the histogram, then wave 0's search of it;
+//   D  the boundary bucket's entries: each thread then ranks its own;
+//   E  per-wave pick counts (output order) and the list check, both local:
+//      a group that dropped pools and has all m kept entries picked fails
+//      it (the exact pass over the scores then decides);
+//   F  the selection in LDS, then the index list.
+struct GroupSel {
+    uint32_t hist[kSelPasses][kBNT];
+    uint32_t mm[2 * kBNT / 64];
+    uint32_t res[4];
+    uint32_t nb, fail;
+    uint32_t bkey[kBoundCap];
+    uint32_t bslot[kBoundCap];
+    uint32_t wsum[kBNT / 64];
+    uint32_t gcount[kMaxGroups];
+    int32_t sel[kGroupMaxK];
+    SelShared<kBNT> S;                       // the exact pass
+};
+
 __global__ __launch_bounds__(kBNT) void k_topk_groups(
     const float* __restrict__ scores, const int32_t* __restrict__ first_valid,
     const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int stride, int select_k,
     const uint64_t* __restrict__ cand, const int32_t* __restrict__ cand_n, Emit e) {
-    constexpr int KPT = kGroupCandCap / kBNT;
-    __shared__ TopSelShared<kBNT, KPT> T;
-    __shared__ int32_t sel[kGroupMaxK];
-    __shared__ uint32_t gcount[kMaxGroups];
-    __shared__ uint32_t gpicked[kMaxGroups];
-    __shared__ int fail;
+    constexpr int KPT = kGroupCandCap / kBNT, NW = kBNT / 64, NB = kBNT, PER = NB / 64;
+    constexpr int BITS = log2_of<NB>();
+    __shared__ GroupSel G;
     static_assert(KPT == 8 && kBNT == kMaxGroups, "8 list slots and one group count per thread");
-    const int t = blockIdx.x, tid = threadIdx.x;
+    const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int s0 = tid * KPT;
     // every load at once, before the row geometry they do not depend on: this
     // thread's group count and its KPT slots
@@ -260,50 +282,205 @@ __global__ __launch_bounds__(kBNT) void k_topk_groups(
     }
     int b, f, qp, n_vis;
     query_geom(first_valid, q_seq, q_pos, t, b, f, qp, n_vis);
+    const int64_t rb = e.indices ? e.row_base[b] : 0;
     const int n = min(n_vis, stride);
     if (n <= select_k) {
-        emit_selection<kBNT>(nullptr, n, select_k, t, b, f, qp, n_vis, e);
+        emit_selection<kBNT>(nullptr, n, select_k, t, b, f, qp, n_vis, e, rb);
         return;
     }
     const int groups = (n + kGroupPools - 1) / kGroupPools;
     const int m = group_quota(select_k, n);
     const int msh = __ffs(m) - 1;
     const int M = groups * m;
-    gcount[tid] = gc;
-    gpicked[tid] = 0u;
-    if (tid == 0) fail = 0;
-    lds_barrier();
-    // a thread's 8 slots lie in one group (m >= 8): one count, read unconditionally
-    const uint32_t gcnt = gcount[min(s0, M - 1) >> msh] & (kGroupDropped - 1);
     uint32_t key[KPT];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-        const int sl = s0 + j;
-        const bool ok = sl < M && (uint32_t)(sl & (m - 1)) < gcnt;
-        key[j] = ok ? (uint32_t)(raw[j] >> 32) : 0u;
+    for (int j = 0; j < KPT; ++j) key[j] = s0 + j < M ? (uint32_t)(raw[j] >> 32) : 0u;
+
+    // ---- A: counts, cleared histograms, per-wave min (present keys) / max
+    G.gcount[tid] = gc;
+#pragma unroll
+    for (int i = 0; i < kSelPasses; ++i) G.hist[i][tid] = 0u;
+    if (tid == 0) {
+        G.nb = 0u;
+        G.fail = 0u;
     }
-    const uint32_t picks = select_top_slots<kBNT, KPT>(key, (uint32_t)select_k, T);
-    uint32_t total;
-    uint32_t pos = block_exclusive_scan<kBNT>((uint32_t)__popc(picks), T.S.scan, &total);
+    uint32_t lo = ~0u, hi = 0u;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        if (key[j]) lo = min(lo, key[j]);
+        hi = max(hi, key[j]);
+    }
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+    if (lane == 0) {
+        G.mm[2 * w] = lo;
+        G.mm[2 * w + 1] = hi;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        lo = min(lo, G.mm[2 * i]);
+        hi = max(hi, G.mm[2 * i + 1]);
+    }
+
+    // ---- B, C: bucketing passes
+    const uint32_t target = (uint32_t)select_k;
+    uint32_t krem = target, cnt = 0xFFFFFFFFu;
+    bool whole = false;
+#pragma unroll 1
+    for (int pass = 0; pass < kSelPasses && lo < hi && cnt > (uint32_t)kBoundCap; ++pass) {
+        uint32_t* H = G.hist[pass];
+        const int sh = bit_len<uint32_t>((hi - lo) >> BITS);
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const uint32_t k = key[j];
+            if (k >= lo && k <= hi) atomicAdd(&H[(k - lo) >> sh], 1u);
+        }
+        lds_barrier();
+        if (w == 0) {
+            // bucket d (descending: bucket NB-1-d) holding rank krem; lane l
+            // sums d in [l PER, (l+1) PER), read in a rotated, conflict-free order
+            uint32_t lsum = 0u;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) lsum += H[NB - 1 - (lane * PER + ((i + lane / (64 / PER)) & (PER - 1)))];
+            const uint32_t incl = wave_incl_sum_u32(lsum), excl = incl - lsum;
+            const unsigned long long hit = __ballot(excl < krem && krem <= incl);
+            uint32_t d = 0u, above = 0u, c = 0u, none = 1u;
+            if (hit != 0ull) {
+                none = 0u;
+                const int L = __ffsll((long long)hit) - 1;
+                uint32_t acc = __builtin_amdgcn_readlane(excl, L);
+                bool found = false;
+#pragma unroll
+                for (int i = 0; i < PER; ++i) {
+                    const uint32_t v = H[NB - 1 - (L * PER + i)];
+                    if (!found && krem <= acc + v) {
+                        found = true;
+                        d = (uint32_t)(L * PER + i);
+                        above = acc;
+                        c = v;
+                    }
+                    acc += v;
+                }
+            }
+            if (lane == 0) {
+                G.res[0] = d;
+                G.res[1] = above;
+                G.res[2] = c;
+                G.res[3] = none;
+            }
+        }
+        lds_barrier();
+        if (G.res[3]) {                      // fewer present keys than the target: all of them
+            whole = true;
+            break;
+        }
+        krem -= G.res[1];
+        cnt = G.res[2];
+        const uint32_t nlo = lo + ((NB - 1 - G.res[0]) << sh);
+        const uint32_t nhi = nlo + ((1u << sh) - 1u);
+        lo = nlo;
+        hi = nhi < hi ? nhi : hi;
+        if (cnt == krem) {
+            whole = true;
+            break;
+        }
+    }
+    if (lo == hi && cnt == 0xFFFFFFFFu) {    // every present key equal (or one key)
+        uint32_t c = 0;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) c += key[j] == lo ? 1u : 0u;
+        uint32_t tot;
+        block_exclusive_scan<kBNT>(c, G.S.scan, &tot);
+        cnt = tot;
+        whole = tot == krem;
+    }
+    uint32_t picks = 0u;
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-        if ((picks >> j) & 1u) atomicAdd(&gpicked[(s0 + j) >> msh], 1u);
+        if (key[j] > hi || (whole && key[j] != 0u && key[j] >= lo && key[j] <= hi)) picks |= 1u << j;
+
+    // ---- D: the boundary bucket [lo, hi]; each thread ranks its own entries
+    if (!whole) {
+        if (cnt <= (uint32_t)kBoundCap) {
+            uint32_t mine = 0u;
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) mine += (key[j] != 0u && key[j] >= lo && key[j] <= hi) ? 1u : 0u;
+            uint32_t e0 = 0u;
+            if (mine) {
+                e0 = atomicAdd(&G.nb, mine);
+                uint32_t e = e0;
+#pragma unroll
+                for (int j = 0; j < KPT; ++j) {
+                    if (key[j] != 0u && key[j] >= lo && key[j] <= hi) {
+                        G.bkey[e] = key[j];
+                        G.bslot[e] = (uint32_t)(s0 + j);
+                        ++e;
+                    }
+                }
+            }
+            lds_barrier();
+            // this thread's entries are [e0, e0 + mine)
+            const uint32_t nb = G.nb;
+            for (uint32_t me = e0; me < e0 + mine; ++me) {
+                const uint32_t mk = G.bkey[me], ms = G.bslot[me];
+                uint32_t rank = 0;
+                for (uint32_t i = 0; i < nb; ++i) {
+                    const uint32_t k = G.bkey[i];
+                    rank += (k > mk || (k == mk && G.bslot[i] < ms)) ? 1u : 0u;
+                }
+                if (rank < krem) picks |= 1u << (ms - (uint32_t)s0);
+            }
+        } else {
+            // more than kBoundCap equal keys (lo == hi): the first krem in slot order
+            uint32_t c = 0;
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) c += (key[j] != 0u && key[j] == lo) ? 1u : 0u;
+            uint32_t tot;
+            const uint32_t before = block_exclusive_scan<kBNT>(c, G.S.scan, &tot);
+            uint32_t take = krem > before ? min(krem - before, c) : 0u;
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
+                if (key[j] != 0u && key[j] == lo && take > 0u) {
+                    picks |= 1u << j;
+                    --take;
+                }
+            }
+        }
+    }
+
+    // ---- E: output positions (per-wave counts) and the list check
+    const uint32_t c = (uint32_t)__popc(picks);
+    const uint32_t incl = wave_incl_sum_u32(c);
+    if (lane == 63) G.wsum[w] = incl;
+    {
+        // threads tpg * g' .. tpg * g' + tpg - 1 of this wave hold group g's m slots
+        const int tpg = m >> 3;
+        const unsigned long long full = __ballot(picks == 0xFFu);
+        const int l0 = lane & ~(tpg - 1);
+        const unsigned long long gm = ((tpg >= 64 ? ~0ull : ((1ull << tpg) - 1ull))) << l0;
+        const bool bad = (lane & (tpg - 1)) == 0 && s0 < M && (G.gcount[s0 >> msh] & kGroupDropped) &&
+                         (full & gm) == gm;
+        if (__ballot(bad) != 0ull && lane == 0) G.fail = 1u;
+    }
     lds_barrier();
-    if (tid < groups && (gcount[tid] & kGroupDropped) && gpicked[tid] == (uint32_t)m) fail = 1;
-    lds_barrier();
-    if (fail) {
-        topk_stream_exact<kBNT>(scores + (int64_t)t * stride, n, select_k, T.S, sel);
+    uint32_t pos = incl - c;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) pos += i < w ? G.wsum[i] : 0u;
+    if (G.fail) {
+        topk_stream_exact<kBNT>(scores + (int64_t)t * stride, n, select_k, G.S, G.sel);
     } else {
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
             if ((picks >> j) & 1u) {
-                if (pos < (uint32_t)kGroupMaxK) sel[pos] = (int32_t)(0xFFFFFFFFu - (uint32_t)raw[j]);
+                if (pos < (uint32_t)kGroupMaxK) G.sel[pos] = (int32_t)(0xFFFFFFFFu - (uint32_t)raw[j]);
                 ++pos;
             }
         }
     }
+    // ---- F
     lds_barrier();
-    emit_selection<kBNT>(sel, select_k, select_k, t, b, f, qp, n_vis, e);
+    emit_selection<kBNT>(G.sel, select_k, select_k, t, b, f, qp, n_vis, e, rb);
 }
 
 }  // namespace dsa

@@ -26,16 +26,17 @@ __device__ __forceinline__ void query_geom(const int32_t* first_valid, const int
 
 // Write K ascending ids (sel[0..K), or 0..K-1 when sel is null) as pool ids
 // (-1 padded) and/or as the expanded index list.  No barrier inside.
+// rb: row_base[b] when the caller loaded it already (-1: load it here).
 template <int NT>
 __device__ __forceinline__ void emit_selection(const int32_t* sel, int K, int select_k, int t, int b,
-                                               int f, int qp, int n_vis, const Emit& e) {
+                                               int f, int qp, int n_vis, const Emit& e, int64_t rb_pre = -1) {
     const int tid = threadIdx.x;
     if (e.pool_ids) {
         int32_t* out = e.pool_ids + (int64_t)t * select_k;
         for (int i = tid; i < select_k; i += NT) out[i] = i < K ? (sel ? sel[i] : i) : -1;
     }
     if (e.indices) {
-        const int64_t rb = e.row_base[b];
+        const int64_t rb = rb_pre >= 0 ? rb_pre : e.row_base[b];
         const int nsel = 4 * K;
         const int tail = qp >= f ? (qp - f + 1) - 4 * n_vis : 0;
         int32_t* out = e.indices + (int64_t)t * e.W;
@@ -201,8 +202,9 @@ __device__ __forceinline__ int group_quota(int K, int n) {
 
 // One wave's group: lanes hold consecutive pools p (lane order = id order),
 // `valid` for visible ones.  Writes the group's best m (key << 32 | ~p) in id
-// order to cand[group * m ..] and the count (| kGroupDropped when more than m
-// were valid) to cand_n[group].  The m-th largest key is found with 32
+// order to cand[group * m ..], zeros in the list's remaining slots (key 0
+// marks an empty slot), and the count (| kGroupDropped when more than m were
+// valid) to cand_n[group].  The m-th largest key is found with 32
 // ballot-and-popcount steps; ties at it go to the lowest ids.  Store is the
 // memory policy for the two writes.
 template <class Store64, class Store32>
@@ -225,8 +227,10 @@ __device__ __forceinline__ void keep_group_best(float s, bool valid, int p, int 
     }
     const unsigned long long pm = __ballot(pick);
     const int slot = popc_below(pm);
+    const int npk = __popcll(pm);
     if (pick) st64(cand + (int64_t)group * m + slot, ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)p));
-    if (lane == 0) st32(cand_n + group, (uint32_t)(__popcll(pm) | (nvalid > m ? kGroupDropped : 0)));
+    if (lane >= npk && lane < m) st64(cand + (int64_t)group * m + lane, 0ull);
+    if (lane == 0) st32(cand_n + group, (uint32_t)(npk | (nvalid > m ? kGroupDropped : 0)));
 }
 
 // ---------------------------------------------------------------- exact top-K of register keys
