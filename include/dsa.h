@@ -310,9 +310,10 @@ int dsa_sparse_mla(const dsa_dims* dims, const void* q, int q_dtype, const int8_
  * expand_selection and sparse_mla (the chain of [Ref] Functions:
  * index_scores, topk_pools, expand_selection, mla_masked_attention, and
  * [Kernels] Included: split-KV decode with a combine).  The results are the
- * ones the separate calls produce: out/lse as dsa_sparse_mla over the list
- * dsa_topk_select_expand would write (same selection, same tie rule), and,
- * when not NULL, that list (indices) and the selected pool ids (pool_ids).
+ * ones the separate calls produce: the list dsa_topk_select_expand would
+ * write (same selection, same tie rule) as indices and pool_ids when not
+ * NULL, bit for bit, and out/lse as dsa_sparse_mla over that list up to the
+ * grouping of its floating-point sums (a few fp32 ulps).
  * The step's new tokens must already be stored (dsa_store_int8) and the
  * pools they complete built (dsa_index_pools).
  *   q_idx, w, pools, seqs, q_seq, q_pos   as dsa_index_scores

@@ -61,7 +61,7 @@ struct MlaPlan {
     bool mfma;          // MFMA kernel (bf16 q, latent 512, heads % 16 == 0)
     int head_tiles;     // 16-head tiles per workgroup (MFMA path)
     int head_groups;    // workgroups along the head axis
-    int rows_rt;        // k_mla_rows: 16-row tiles per wave (chunk = 64 * rows_rt rows)
+    int rows_chunk;     // k_mla_rows: list positions per chunk (16 RT NW)
     int chunks_per_split;
     int splits;         // list partitions per query
     size_t ws_bytes;    // partial results (0 when splits == 1)

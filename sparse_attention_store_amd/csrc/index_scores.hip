@@ -172,6 +172,8 @@ struct QueryGeom {
     int32_t nn;        // visible pools, capped at the row stride
     int64_t tok0;      // with new tokens: the sequence's first pooled token row
     int32_t pb, pe;    // with new tokens: the pools this step completes
+    int32_t rank;      // with new tokens: rank among the queries that have tiles
+    int32_t pad;
 };
 struct AppendArgs {    // the step's new tokens (append_tokens' arguments)
     const uint16_t* latent;
@@ -221,17 +223,35 @@ __global__ __launch_bounds__(256, 4) void k_scores_groups(
             }
         }
         const int ng = (nn + kGroupPools - 1) / kGroupPools;
-        const uint32_t nt = (uint32_t)(ng + 3) >> 2;
+        uint32_t nt = (uint32_t)(ng + 3) >> 2;
+        // With new tokens, every query's last tile (the one holding the pools
+        // the step completes, which its waves rebuild) comes first, in query
+        // order, so that extra work is done early, not in the launch's tail;
+        // the other tiles follow.  `first`/`ntiles` then describe those others.
+        const unsigned long long lead = __ballot(nt > 0);
+        const int rank = nt > 0 ? popc_below(lead) : -1;
+        uint32_t off = 0;
+        if constexpr (AD != 0) {
+            nt = nt > 0 ? nt - 1 : 0;
+            off = (uint32_t)__popcll(lead);
+        }
         const uint32_t incl = wave_incl_sum_u32(nt);
-        geom[lane] = QueryGeom{base, incl - nt, nt, ng, nn, tok0, pb, pe};
+        geom[lane] = QueryGeom{base, off + incl - nt, nt, ng, nn, tok0, pb, pe, rank, 0};
     }
     lds_barrier();
     const int total = (int)(geom[63].first + geom[63].ntiles);
     int tile = blockIdx.x;
     for (; tile < total; tile += gridDim.x) {
-        // query of the tile: the number of queries whose tiles all come before it
-        const int t = __popcll(__ballot(geom[lane].first + geom[lane].ntiles <= (uint32_t)tile));
-        const int grp = 4 * (tile - uniform32((int)geom[t].first)) + wave;
+        int t, j;
+        if (AD != 0 && tile < (int)uniform32((int)geom[0].first)) {
+            t = __ffsll((long long)__ballot(geom[lane].rank == tile)) - 1;   // the tile-th query's last tile
+            j = (uniform32(geom[t].ng) - 1) >> 2;
+        } else {
+            // query of the tile: the number of queries whose tiles all come before it
+            t = __popcll(__ballot(geom[lane].first + geom[lane].ntiles <= (uint32_t)tile));
+            j = tile - uniform32((int)geom[t].first);
+        }
+        const int grp = 4 * j + wave;
         const bool has = grp < uniform32(geom[t].ng);
         const int n_vis = uniform32(geom[t].nn);
         const int p0 = grp * kGroupPools;
@@ -296,7 +316,13 @@ __global__ __launch_bounds__(256, 4) void k_scores_groups(
                 }
             }
             const int p = p0 + lane;
-            if (p < stride) scores[(int64_t)t * stride + p] = p < n_vis ? s : -INFINITY;
+            {
+                // a buffer store: pools at or past the row stride fall outside its range
+                const __amdgpu_buffer_rsrc_t rs =
+                    buffer_rsrc(scores + (int64_t)t * stride + p0, (uint32_t)(min(stride - p0, kGroupPools) * 4));
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(p < n_vis ? s : -INFINITY), rs,
+                                                      (uint32_t)lane * 4u, 0, 0);
+            }
             if constexpr (CANDS) {
                 if (n_vis > select_k)
                     keep_group_best(s, p < n_vis, p, grp, group_quota(select_k, n_vis),

@@ -33,7 +33,7 @@ __device__ __forceinline__ void int8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint3
 }
 
 // ------------------------------------------------------------------ k_mla_rows
-constexpr int kRChunk = 128;          // rows per workgroup iteration (4 waves x 32)
+constexpr int kRChunk = 128;          // list positions per chunk of k_mla_rows and the fused step
 constexpr int kRStride = kD + 8;      // bf16 elements per LDS row
 constexpr float kLazyMax = 8.0f;      // raise the running max only beyond 2^8
 
@@ -59,17 +59,18 @@ __device__ __forceinline__ u32x4 codes8_to_biased_bf16(uint32_t a, uint32_t b) {
     return u32x4{r0, r1, r2, r3};
 }
 
-// LDS of one split walking chunks of 64 * RT rows (4 waves of RT 16-row tiles).
-template <int RT>
+// LDS of one split walking chunks of 16 * RT * NW rows (NW waves of RT
+// 16-row tiles).
+template <int RT, int NW = 4>
 struct MlaRowsSmemT {
-    static constexpr int kRows = 64 * RT;
+    static constexpr int kRows = 16 * RT * NW;
     static constexpr int kPLS = kRows + 8;   // bf16 per head row of P'
     uint16_t kv[kRows * kRStride];           // the chunk's rows as bf16 (code + 128)
     uint16_t qs[16 * kRStride];              // the 16 heads of q, [head][dim]
     uint16_t pl[2][16 * kPLS];               // P' hi, lo: [head][row]
-    float red_max[4][16];
-    float red_l[4][16];
-    float red_p[4][16];
+    float red_max[NW][16];
+    float red_l[NW][16];
+    float red_p[NW][16];
 };
 using MlaRowsSmem = MlaRowsSmemT<2>;         // 128-row chunks (kRChunk)
 
@@ -102,15 +103,15 @@ __device__ __forceinline__ void store_partial(MlaPartial* p, MlaPartial v) {
 }
 
 // One split of k_mla_rows: query t, heads [head0, head0 + 16), list chunks
-// [c_begin, c_end) of 64 * RT positions (each wave owns RT 16-row tiles of a
-// chunk).  idx_at(pos) gives the cache row of list position pos (< W), or a
+// [c_begin, c_end) of 16 * RT * NW positions (each of the NW waves owns RT
+// 16-row tiles of a chunk and 512 / NW columns of the output).  idx_at(pos) gives the cache row of list position pos (< W), or a
 // negative value for an empty slot.  COH makes the partial results
 // agent-coherent (read back by another workgroup of the same launch) instead
 // of plain stores.  Every thread of the block must call it; it contains
 // workgroup barriers.
-template <int RT, bool COH, class IdxFn>
+template <int RT, bool COH, int NW = 4, class IdxFn>
 __device__ __forceinline__ void mla_rows_split(
-    MlaRowsSmemT<RT>& sm, const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, int row_bytes,
+    MlaRowsSmemT<RT, NW>& sm, const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, int row_bytes,
     IdxFn idx_at, int W, int H, float scale_log2, int t, int head0, int split, int c_begin, int c_end,
     int splits, float* __restrict__ part_o, MlaPartial* __restrict__ part_ml, void* __restrict__ out,
     int out_f32, float* __restrict__ lse) {
@@ -118,9 +119,14 @@ __device__ __forceinline__ void mla_rows_split(
     const int n16 = lane & 15, g4 = lane >> 4;
     const int prow = row_of_slot(n16);            // row (within a 16-row tile) this lane loads
     const int srow = row_of_slot(4 * g4);         // first of the 4 rows this lane's S^T values cover
-    constexpr int CH = 64 * RT;                   // rows per chunk
-    constexpr int PLS = MlaRowsSmemT<RT>::kPLS;
+    constexpr int NT = 64 * NW;
+    constexpr int CH = 16 * RT * NW;              // rows per chunk
+    constexpr int PLS = MlaRowsSmemT<RT, NW>::kPLS;
     constexpr int NKS = CH / 32;                  // 32-row k-steps of O^T += V^T P'^T
+    constexpr int CW = kD / NW;                   // output columns per wave
+    constexpr int NG = CW / 64;                   // 64-column groups per wave
+    constexpr int QP = 16 * kD * 2 / 16 / NT;     // 16-byte pieces of q per thread
+    static_assert(NG >= 1 && QP >= 1 && CH % 32 == 0, "unsupported split shape");
 
     auto load_idx = [&](int c, int* id) {
 #pragma unroll
@@ -150,11 +156,11 @@ __device__ __forceinline__ void mla_rows_split(
     // q (16 heads x 512, 16 KB) is read once per workgroup, 64 bytes per
     // thread, and handed to the waves through LDS; its loads go out first and
     // overlap the dependent chain index -> row bytes.
-    u32x4 qv[4];
+    u32x4 qv[QP];
     {
         const uint16_t* qh = q + ((int64_t)t * H + head0) * kD;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) qv[i] = *reinterpret_cast<const u32x4*>(qh + 8 * (tid + 256 * i));
+        for (int i = 0; i < QP; ++i) qv[i] = *reinterpret_cast<const u32x4*>(qh + 8 * (tid + NT * i));
     }
     int id_cur[RT], id_next[RT];
 #pragma unroll
@@ -165,8 +171,8 @@ __device__ __forceinline__ void mla_rows_split(
         load_rows(id_cur);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int k = tid + 256 * i;                   // 16-byte piece k: head k / 64, dims 8 (k % 64) ..
+    for (int i = 0; i < QP; ++i) {
+        const int k = tid + NT * i;                    // 16-byte piece k: head k / 64, dims 8 (k % 64) ..
         *reinterpret_cast<u32x4*>(&sm.qs[(k >> 6) * kRStride + 8 * (k & 63)]) = qv[i];
     }
     lds_barrier();
@@ -194,9 +200,9 @@ __device__ __forceinline__ void mla_rows_split(
     // Running softmax state of head n16 (the same in every wave); l and the
     // P' sum cover this lane's own rows and are added up at the end.
     float m_run = -INFINITY, l_run = 0.f, p_run = 0.f;
-    f32x4 acc[2][4];                             // O^T: cols 128w + 64G + 16g4 + 4i + u, head n16
+    f32x4 acc[NG][4];                            // O^T: cols CW w + 64G + 16g4 + 4i + u, head n16
 #pragma unroll
-    for (int G = 0; G < 2; ++G)
+    for (int G = 0; G < NG; ++G)
 #pragma unroll
         for (int u = 0; u < 4; ++u) acc[G][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -243,7 +249,7 @@ __device__ __forceinline__ void mla_rows_split(
             if (c + 2 < c_end) load_idx(c + 2, id_next);
         }
 
-        // ---- chunk max per head across the 4 waves (lane: head n16, rows slot 4*g4 + i)
+        // ---- chunk max per head across the NW waves (lane: head n16, rows slot 4*g4 + i)
         float z[RT][4], sc[RT][4];
         float cmax = -INFINITY;
 #pragma unroll
@@ -258,10 +264,12 @@ __device__ __forceinline__ void mla_rows_split(
         cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
         if (g4 == 0) sm.red_max[w][n16] = cmax;
         lds_barrier();
-        float wmax[4];
+        float wmax[NW];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) wmax[k] = sm.red_max[k][n16];
-        const float chunk_max = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+        for (int k = 0; k < NW; ++k) wmax[k] = sm.red_max[k][n16];
+        float chunk_max = wmax[0];
+#pragma unroll
+        for (int k = 1; k < NW; ++k) chunk_max = fmaxf(chunk_max, wmax[k]);
         // k-steps with a live row (their source waves' maxima): the same
         // answer for every head.
         bool src_live[NKS];
@@ -269,7 +277,7 @@ __device__ __forceinline__ void mla_rows_split(
         for (int ks = 0; ks < NKS; ++ks) {
             bool lv = false;
 #pragma unroll
-            for (int k = 0; k < 4; ++k)                 // wave k's rows start at 16 RT k
+            for (int k = 0; k < NW; ++k)                // wave k's rows start at 16 RT k
                 if ((16 * RT * k) / 32 == ks) lv = lv || wmax[k] != -INFINITY;
             src_live[ks] = __ballot(lv) != 0ull;
         }
@@ -279,7 +287,7 @@ __device__ __forceinline__ void mla_rows_split(
         const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
         if (__ballot(alpha != 1.0f && m_run != -INFINITY) != 0ull) {
 #pragma unroll
-            for (int G = 0; G < 2; ++G)
+            for (int G = 0; G < NG; ++G)
 #pragma unroll
                 for (int u = 0; u < 4; ++u) acc[G][u] *= alpha;
         }
@@ -318,7 +326,7 @@ __device__ __forceinline__ void mla_rows_split(
         }
         lds_barrier();                               // rows and P' of all waves visible
 
-        // ---- O^T += V^T P'^T over the chunk's rows, this wave's 128 columns
+        // ---- O^T += V^T P'^T over the chunk's rows, this wave's CW columns
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             if (!src_live[ks]) continue;             // no staged row in these 32
@@ -326,8 +334,8 @@ __device__ __forceinline__ void mla_rows_split(
             const bf16x8 p_hi = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.pl[0][n16 * PLS + r0]));
             const bf16x8 p_lo = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.pl[1][n16 * PLS + r0]));
 #pragma unroll
-            for (int G = 0; G < 2; ++G) {
-                const uint16_t* vb = &sm.kv[r0 * kRStride + 128 * w + 64 * G + 4 * n16];
+            for (int G = 0; G < NG; ++G) {
+                const uint16_t* vb = &sm.kv[r0 * kRStride + CW * w + 64 * G + 4 * n16];
                 u32x2 v[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] = *reinterpret_cast<const u32x2*>(vb + e * kRStride);
@@ -350,7 +358,7 @@ __device__ __forceinline__ void mla_rows_split(
         if (c + 1 < c_end) lds_barrier();            // rows and P' are rewritten next
     }
 
-    // ---- totals over the 4 waves' rows, then this wave's 128 columns out
+    // ---- totals over the NW waves' rows, then this wave's CW columns out
     l_run += __shfl_xor(l_run, 16, 64);
     l_run += __shfl_xor(l_run, 32, 64);
     p_run += __shfl_xor(p_run, 16, 64);
@@ -362,7 +370,7 @@ __device__ __forceinline__ void mla_rows_split(
     lds_barrier();
     float L = 0.f, PS = 0.f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < NW; ++k) {
         L += sm.red_l[k][n16];
         PS += sm.red_p[k][n16];
     }
@@ -372,10 +380,10 @@ __device__ __forceinline__ void mla_rows_split(
         const float inv = L > 0.f ? 1.0f / L : 0.f;
         const int64_t orow = ((int64_t)t * H + head) * kD;
 #pragma unroll
-        for (int G = 0; G < 2; ++G)
+        for (int G = 0; G < NG; ++G)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int col = 128 * w + 64 * G + 16 * g4 + 4 * i;
+                const int col = CW * w + 64 * G + 16 * g4 + 4 * i;
                 const f32x4 o = (f32x4{acc[G][0][i], acc[G][1][i], acc[G][2][i], acc[G][3][i]} - obias) * inv;
                 if (out_f32) {
                     *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + orow + col) = o;
@@ -392,10 +400,10 @@ __device__ __forceinline__ void mla_rows_split(
         if (L > 0.f) {
             float* po = part_o + slot * kD;
 #pragma unroll
-            for (int G = 0; G < 2; ++G)
+            for (int G = 0; G < NG; ++G)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int col = 128 * w + 64 * G + 16 * g4 + 4 * i;
+                    const int col = CW * w + 64 * G + 16 * g4 + 4 * i;
                     store_f32x4<COH>(po + col, f32x4{acc[G][0][i], acc[G][1][i], acc[G][2][i], acc[G][3][i]} - obias);
                 }
         }

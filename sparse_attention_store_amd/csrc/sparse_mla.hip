@@ -12,9 +12,10 @@
 // dominant row of a heavy-tailed latent (|o| ~ 100) needs to stay within
 // 2e-2 absolute.
 //
-// k_mla_rows (16 heads per workgroup; decode).  The list is walked in chunks
-// of 64 RT rows (RT = 2 here: 128-row chunks, one workgroup per CU); each of
-// the 4 waves owns 16 RT rows of a chunk:
+// k_mla_rows<RT, NW> (16 heads per workgroup; decode).  The list is walked
+// in chunks of 16 RT NW rows (here RT = 1, NW = 8: 128-row chunks, one
+// 512-thread workgroup per CU, two waves per SIMD to hide each other's
+// latencies); each of the NW waves owns RT 16-row tiles of a chunk:
 //  * q (16 heads x 512) is read once per workgroup, before the dependent
 //    chain index -> rows, and handed to the waves through LDS (every wave
 //    needs all of it: 4 copies per workgroup from L2 cost more than the
@@ -27,8 +28,8 @@
 //  * during the conversion each wave also writes its rows to LDS as bf16
 //    (code + 128); the per-head chunk max is exchanged through LDS, and
 //    P' = p * row scale goes to LDS as bf16 hi + lo, [head][row];
-//  * O^T += V^T P'^T is split by columns: each wave accumulates its own 128
-//    columns over every row of the chunk (8-byte LDS reads of 4 adjacent
+//  * O^T += V^T P'^T is split by columns: each wave accumulates its own
+//    512 / NW columns over every row of the chunk (8-byte LDS reads of 4 adjacent
 //    columns assembled with v_perm).  Rows are placed with bits 2 and 3 of
 //    the slot swapped so that both the 16-byte writes and the 8-byte reads
 //    are free of bank conflicts;
@@ -50,19 +51,20 @@
 
 namespace dsa {
 
-template <int RT>
-__global__ __launch_bounds__(256, 1) void k_mla_rows(
+template <int RT, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void k_mla_rows(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, int row_bytes,
     const int32_t* __restrict__ indices, int W, int H, float scale_log2, int chunks_per_split,
     int splits, float* __restrict__ part_o, MlaPartial* __restrict__ part_ml,
     void* __restrict__ out, int out_f32, float* __restrict__ lse) {
-    __shared__ __attribute__((aligned(16))) MlaRowsSmemT<RT> sm;
+    __shared__ __attribute__((aligned(16))) MlaRowsSmemT<RT, NW> sm;
+    constexpr int CH = 16 * RT * NW;
     const int split = blockIdx.x, t = blockIdx.z;
-    const int nchunks = (W + 64 * RT - 1) / (64 * RT);
+    const int nchunks = (W + CH - 1) / CH;
     const int c_begin = split * chunks_per_split;
     const int c_end = min(c_begin + chunks_per_split, nchunks);
     const int32_t* irow = indices + (int64_t)t * W;
-    mla_rows_split<RT, false>(sm, q, cache, row_bytes, [&](int pos) { return irow[pos]; }, W, H, scale_log2, t,
+    mla_rows_split<RT, false, NW>(sm, q, cache, row_bytes, [&](int pos) { return irow[pos]; }, W, H, scale_log2, t,
                               blockIdx.y * 16, split, c_begin, c_end, splits, part_o, part_ml, out, out_f32, lse);
 }
 
@@ -445,7 +447,7 @@ MlaPlan plan_sparse_mla(const dsa_dims& d, int32_t T, int32_t num_splits, int q_
     if (!p.mfma || T <= 0) {
         p.head_tiles = 1;
         p.head_groups = d.mla_heads;
-        p.rows_rt = 2;
+        p.rows_chunk = dsa::kRChunk;
         p.splits = 1;
         p.chunks_per_split = 1;
         p.ws_bytes = 0;
@@ -459,8 +461,8 @@ MlaPlan plan_sparse_mla(const dsa_dims& d, int32_t T, int32_t num_splits, int q_
     p.head_groups = tiles16 / ht;
     // k_mla_rows walks 128-row chunks; k_mla_mfma 64-row chunks with the
     // split's index slice staged in LDS (at most kMaxSplitRows entries).
-    p.rows_rt = 2;
-    const int chunk = ht == 1 ? 64 * p.rows_rt : dsa::kChunk;
+    p.rows_chunk = dsa::kRChunk;
+    const int chunk = ht == 1 ? p.rows_chunk : dsa::kChunk;
     const int nchunks = (int)cdiv(d.out_width, chunk);
     int want;
     if (num_splits > 0) {
@@ -516,7 +518,8 @@ hipError_t launch_sparse_mla(const dsa_dims& d, const MlaPlan& plan, const void*
                                plan.chunks_per_split, plan.splits, part_o, part_ml, out, out_f32, lse);
             break;
         default:
-            hipLaunchKernelGGL(dsa::k_mla_rows<2>, grid, dim3(256), 0, s, q16, c8, d.row_bytes, indices, W, H, sl2,
+            static_assert(16 * 1 * 8 == dsa::kRChunk, "k_mla_rows<1, 8> walks kRChunk-row chunks");
+            hipLaunchKernelGGL((dsa::k_mla_rows<1, 8>), grid, dim3(512), 0, s, q16, c8, d.row_bytes, indices, W, H, sl2,
                                plan.chunks_per_split, plan.splits, part_o, part_ml, out, out_f32, lse);
             break;
     }
