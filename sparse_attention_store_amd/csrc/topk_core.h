@@ -204,9 +204,10 @@ __device__ __forceinline__ int group_quota(int K, int n) {
 // `valid` for visible ones.  Writes the group's best m (key << 32 | ~p) in id
 // order to cand[group * m ..], zeros in the list's remaining slots (key 0
 // marks an empty slot), and the count (| kGroupDropped when more than m were
-// valid) to cand_n[group].  The m-th largest key is found with 32
-// ballot-and-popcount steps; ties at it go to the lowest ids.  Store is the
-// memory policy for the two writes.
+// valid) to cand_n[group].  The best m are taken by repeated wave maxima for
+// m <= 16, else through the m-th largest key (32 ballot-and-popcount steps);
+// either way ties go to the lowest ids.  Store is the memory policy for the
+// two writes.
 template <class Store64, class Store32>
 __device__ __forceinline__ void keep_group_best(float s, bool valid, int p, int group, int m, uint64_t* cand,
                                                 int32_t* cand_n, Store64 st64, Store32 st32) {
@@ -214,8 +215,22 @@ __device__ __forceinline__ void keep_group_best(float s, bool valid, int p, int 
     const uint32_t key = valid ? f32_key(s) : 0u;
     const int nvalid = __popcll(__ballot(valid));
     bool pick = valid;
-    if (nvalid > m) {
+    if (nvalid > m && m <= 16) {
+        // Small m: take the largest remaining key m times (a DPP wave max,
+        // then the lowest lane holding it) -- mostly vector work, where a
+        // bitwise threshold search is a long chain of scalar instructions
+        // that the waves of a CU would all issue at once.
+        uint32_t k = key;
+        pick = false;
+        for (int i = 0; i < m; ++i) {
+            const uint32_t mx = wave_max_u32(valid && !pick ? k : 0u);
+            const unsigned long long at = __ballot(valid && !pick && k == mx);
+            if (lane == __ffsll((long long)at) - 1) pick = true;
+        }
+    } else if (nvalid > m) {
+        // x = the m-th largest key: the largest x with at least m keys >= x
         uint32_t x = 0u;
+#pragma unroll
         for (int bit = 31; bit >= 0; --bit) {
             const uint32_t y = x | (1u << bit);
             if (__popcll(__ballot(key >= y)) >= m) x = y;
