@@ -153,23 +153,24 @@ __device__ __forceinline__ void mla_rows_split(
         }
     };
 
-    // q (16 heads x 512, 16 KB) is read once per workgroup, 64 bytes per
-    // thread, and handed to the waves through LDS; its loads go out first and
-    // overlap the dependent chain index -> row bytes.
-    u32x4 qv[QP];
-    {
-        const uint16_t* qh = q + ((int64_t)t * H + head0) * kD;
-#pragma unroll
-        for (int i = 0; i < QP; ++i) qv[i] = *reinterpret_cast<const u32x4*>(qh + 8 * (tid + NT * i));
-    }
+    // The index loads go out first (the rows wait on them, and loads complete
+    // in issue order as far as the wait counters go), then q (16 heads x 512,
+    // 16 KB, read once per workgroup, 64 bytes per thread, handed to the
+    // waves through LDS), then the first chunk's rows.
     int id_cur[RT], id_next[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) id_cur[rt] = id_next[rt] = -1;
     if (c_begin < c_end) {
         load_idx(c_begin, id_cur);
         if (c_begin + 1 < c_end) load_idx(c_begin + 1, id_next);
-        load_rows(id_cur);
     }
+    u32x4 qv[QP];
+    {
+        const uint16_t* qh = q + ((int64_t)t * H + head0) * kD;
+#pragma unroll
+        for (int i = 0; i < QP; ++i) qv[i] = *reinterpret_cast<const u32x4*>(qh + 8 * (tid + NT * i));
+    }
+    if (c_begin < c_end) load_rows(id_cur);
 #pragma unroll
     for (int i = 0; i < QP; ++i) {
         const int k = tid + NT * i;                    // 16-byte piece k: head k / 64, dims 8 (k % 64) ..
