@@ -68,6 +68,15 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x, uint32_t iden
     return x;
 }
 
+// Inclusive sum within each row of 16 lanes (the first four steps above).
+__device__ __forceinline__ uint32_t row_incl_sum_u32(uint32_t x) {
+    x += dpp_u32<0x111, 0xF>(x, 0u);
+    x += dpp_u32<0x112, 0xF>(x, 0u);
+    x += dpp_u32<0x114, 0xF>(x, 0u);
+    x += dpp_u32<0x118, 0xF>(x, 0u);
+    return x;
+}
+
 __device__ __forceinline__ uint32_t wave_incl_sum_u32(uint32_t x) {
     return wave_incl_scan_u32(x, 0u, [](uint32_t a, uint32_t b) { return a + b; });
 }

@@ -249,8 +249,7 @@ struct GroupSel {
     uint32_t mm[2 * kBNT / 64];
     uint32_t res[4];
     uint32_t nb, fail;
-    uint32_t bkey[kBoundCap];
-    uint32_t bslot[kBoundCap];
+    uint64_t bent[kBoundCap];                // boundary entries: key << 32 | ~slot, 0 past the end
     uint32_t wsum[kBNT / 64];
     uint32_t gcount[kMaxGroups];
     int32_t sel[kGroupMaxK];
@@ -265,6 +264,7 @@ __global__ __launch_bounds__(kBNT) void k_topk_groups(
     constexpr int BITS = log2_of<NB>();
     __shared__ GroupSel G;
     static_assert(KPT == 8 && kBNT == kMaxGroups, "8 list slots and one group count per thread");
+    static_assert(PER == 16 && kBoundCap % 8 == 0, "one 16-lane row per bucket run; rank in steps of 8");
     const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int s0 = tid * KPT;
     // every load at once, before the row geometry they do not depend on: this
@@ -304,6 +304,7 @@ __global__ __launch_bounds__(kBNT) void k_topk_groups(
         G.nb = 0u;
         G.fail = 0u;
     }
+    if (tid < kBoundCap) G.bent[tid] = 0ull;
     uint32_t lo = ~0u, hi = 0u;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
@@ -347,21 +348,17 @@ __global__ __launch_bounds__(kBNT) void k_topk_groups(
             const unsigned long long hit = __ballot(excl < krem && krem <= incl);
             uint32_t d = 0u, above = 0u, c = 0u, none = 1u;
             if (hit != 0ull) {
+                // within lane L's run: lane i of each row reads its bucket L PER + i,
+                // a row scan gives the running counts, the first that reaches krem wins
                 none = 0u;
                 const int L = __ffsll((long long)hit) - 1;
-                uint32_t acc = __builtin_amdgcn_readlane(excl, L);
-                bool found = false;
-#pragma unroll
-                for (int i = 0; i < PER; ++i) {
-                    const uint32_t v = H[NB - 1 - (L * PER + i)];
-                    if (!found && krem <= acc + v) {
-                        found = true;
-                        d = (uint32_t)(L * PER + i);
-                        above = acc;
-                        c = v;
-                    }
-                    acc += v;
-                }
+                const uint32_t acc = __builtin_amdgcn_readlane(excl, L);
+                const uint32_t v = H[NB - 1 - (L * PER + (lane & (PER - 1)))];
+                const uint32_t run = row_incl_sum_u32(v);
+                const int i = __ffsll((long long)(__ballot(krem <= acc + run) & 0xFFFFull)) - 1;
+                d = (uint32_t)(L * PER + i);
+                c = __builtin_amdgcn_readlane(v, i);
+                above = acc + __builtin_amdgcn_readlane(run, i) - c;
             }
             if (lane == 0) {
                 G.res[0] = d;
@@ -403,33 +400,37 @@ __global__ __launch_bounds__(kBNT) void k_topk_groups(
     // ---- D: the boundary bucket [lo, hi]; each thread ranks its own entries
     if (!whole) {
         if (cnt <= (uint32_t)kBoundCap) {
+            // entry = key << 32 | ~slot: a larger entry is a larger key, or an
+            // equal key at a lower slot, so an entry's rank is the number of
+            // larger entries; one atomic per wave places this wave's entries
             uint32_t mine = 0u;
 #pragma unroll
             for (int j = 0; j < KPT; ++j) mine += (key[j] != 0u && key[j] >= lo && key[j] <= hi) ? 1u : 0u;
-            uint32_t e0 = 0u;
+            const uint32_t wrun = wave_incl_sum_u32(mine);
+            uint32_t wbase = 0u;
+            if (lane == 63 && wrun != 0u) wbase = atomicAdd(&G.nb, wrun);
+            const uint32_t e0 = __builtin_amdgcn_readlane(wbase, 63) + wrun - mine;
             if (mine) {
-                e0 = atomicAdd(&G.nb, mine);
                 uint32_t e = e0;
 #pragma unroll
                 for (int j = 0; j < KPT; ++j) {
                     if (key[j] != 0u && key[j] >= lo && key[j] <= hi) {
-                        G.bkey[e] = key[j];
-                        G.bslot[e] = (uint32_t)(s0 + j);
+                        G.bent[e] = ((uint64_t)key[j] << 32) | (0xFFFFFFFFu - (uint32_t)(s0 + j));
                         ++e;
                     }
                 }
             }
             lds_barrier();
-            // this thread's entries are [e0, e0 + mine)
-            const uint32_t nb = G.nb;
+            // this thread's entries are [e0, e0 + mine); entries past nb are 0
+            const uint32_t nb8 = (G.nb + 7u) & ~7u;
             for (uint32_t me = e0; me < e0 + mine; ++me) {
-                const uint32_t mk = G.bkey[me], ms = G.bslot[me];
+                const uint64_t mk = G.bent[me];
                 uint32_t rank = 0;
-                for (uint32_t i = 0; i < nb; ++i) {
-                    const uint32_t k = G.bkey[i];
-                    rank += (k > mk || (k == mk && G.bslot[i] < ms)) ? 1u : 0u;
+                for (uint32_t i = 0; i < nb8; i += 8) {
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) rank += G.bent[i + u] > mk ? 1u : 0u;
                 }
-                if (rank < krem) picks |= 1u << (ms - (uint32_t)s0);
+                if (rank < krem) picks |= 1u << ((0xFFFFFFFFu - (uint32_t)mk) - (uint32_t)s0);
             }
         } else {
             // more than kBoundCap equal keys (lo == hi): the first krem in slot order
