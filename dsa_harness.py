@@ -186,6 +186,12 @@ class DeviceWorkload:
         return dsa.topk_select_groups(self.dims, self.scores, self.seqs, self.q_seq, self.q_pos, self.indices,
                                       self._ws_ss(), pool_ids=self.pool_ids, prepare=prepare)
 
+    def step_select_attention(self, r: int = 0, prepare: bool = False):
+        """Selection from the group lists, expansion and attention (dsa_topk_sparse_mla)."""
+        return dsa.topk_sparse_mla(self.dims, self.scores, self.seqs, self.q_seq, self.q_pos, self.indices,
+                                   self._ws_ss(), self.q, self.caches[r], self.wl.scale, self.out, self.lse,
+                                   self.num_splits, self.ws_mla, pool_ids=self.pool_ids, prepare=prepare)
+
     def step_scores_select(self, r: int = 0, prepare: bool = False):
         """Scores, selection and expansion (dsa_index_scores_select: two launches for decode)."""
         return dsa.index_scores_select(self.dims, self.q_idx, self.w, self.pools[r], self.seqs, self.q_seq,

@@ -306,6 +306,36 @@ int dsa_sparse_mla(const dsa_dims* dims, const void* q, int q_dtype, const int8_
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * topk_sparse_mla -- dsa_topk_select_groups followed by dsa_sparse_mla over
+ * the list it writes, with the same results bit for bit (pool_ids, indices,
+ * out, lse for the same num_splits), in two launches instead of three: each
+ * attention workgroup makes its query's selection from the group lists
+ * itself ([Ref] Functions: topk_pools, expand_selection,
+ * mla_masked_attention) and reads its rows from the ids it holds; the
+ * partials are then merged as in dsa_sparse_mla.
+ *   dims .. T, pool_ids, indices   as dsa_topk_select_groups (pool_ids may
+ *                  be NULL; indices is written in full)
+ *   select_workspace, select_workspace_bytes   the group lists, as written
+ *                  by dsa_index_scores_groups / dsa_append_scores_groups for
+ *                  the same queries
+ *   q .. num_splits   as dsa_sparse_mla
+ *   mla_workspace  device, >= dsa_sparse_mla_workspace_bytes(dims, T,
+ *                  num_splits) bytes, 256-byte aligned (NULL allowed when
+ *                  that size is 0).
+ * Supported: what dsa_topk_select_groups supports, with score_stride > 0;
+ * else DSA_ERR_UNSUPPORTED.  Attention shapes the one-launch form does not
+ * cover (not bf16 q, latent_dim != 512, or more than one 16-head tile per
+ * workgroup) run the two calls.
+ */
+int dsa_topk_sparse_mla(const dsa_dims* dims, const float* scores, int32_t score_stride,
+                        const dsa_seqs* seqs, int32_t num_seqs, const int32_t* q_seq,
+                        const int32_t* q_pos, int32_t T, int32_t* pool_ids, int32_t* indices,
+                        const void* select_workspace, size_t select_workspace_bytes, const void* q,
+                        int q_dtype, const int8_t* cache, int64_t cache_rows, float scale, void* out,
+                        int out_dtype, float* lse, int32_t num_splits, void* mla_workspace,
+                        size_t mla_workspace_bytes, void* stream);
+
+/*
  * decode_step -- one launch for a decode step's index_scores, topk_select,
  * expand_selection and sparse_mla (the chain of [Ref] Functions:
  * index_scores, topk_pools, expand_selection, mla_masked_attention, and

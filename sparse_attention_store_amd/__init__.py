@@ -113,6 +113,8 @@ def lib() -> ctypes.CDLL:
             "dsa_topk_select_groups": (ctypes.c_int, [DP, P, I32, SP, I32, P, P, I32, P, P, P, SZ, P]),
             "dsa_append_scores_groups": (ctypes.c_int, [DP, ctypes.c_int, P, I64, I64, P, P, I64, P, P, P, P, P, P,
                                                         I32, P, P, P, SP, I32, P, P, I32, I32, P, P, SZ, P]),
+            "dsa_topk_sparse_mla": (ctypes.c_int, [DP, P, I32, SP, I32, P, P, I32, P, P, P, SZ, P, ctypes.c_int, P,
+                                                   I64, F, P, ctypes.c_int, P, I32, P, SZ, P]),
             "dsa_decode_step_workspace_bytes": (SZ, [DP, I32, I32]),
             "dsa_decode_step": (ctypes.c_int, [DP, P, P, P, SP, I32, P, P, I32, I32, P, ctypes.c_int, P, I64, F,
                                                P, ctypes.c_int, P, P, P, P, SZ, P]),
@@ -452,6 +454,40 @@ def topk_select_groups(dims: Dims, scores: torch.Tensor, seqs: Seqs, q_seq: torc
         ctypes.byref(dims), scores.data_ptr(), scores.shape[1], ctypes.byref(seqs._c()), seqs.num_seqs,
         q_seq.data_ptr(), q_pos.data_ptr(), q_pos.shape[0], _ptr(pool_ids), indices.data_ptr(),
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def topk_sparse_mla(dims: Dims, scores: torch.Tensor, seqs: Seqs, q_seq: torch.Tensor, q_pos: torch.Tensor,
+                    indices: torch.Tensor, select_workspace: torch.Tensor, q: torch.Tensor, cache: torch.Tensor,
+                    scale: float, out: torch.Tensor, lse: torch.Tensor | None = None, num_splits: int = 0,
+                    mla_workspace: torch.Tensor | None = None, pool_ids: torch.Tensor | None = None,
+                    stream=None, prepare: bool = False):
+    """topk_select_groups then sparse_mla over its list (the attention launch makes the selection itself)."""
+    _check(scores, torch.float32, "scores")
+    _check(indices, torch.int32, "indices")
+    _check(q_seq, torch.int32, "q_seq")
+    _check(q_pos, torch.int32, "q_pos")
+    if pool_ids is not None:
+        _check(pool_ids, torch.int32, "pool_ids")
+    _check(select_workspace, select_workspace.dtype, "select_workspace")
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q must be bf16 or fp32")
+    _check(q, q.dtype, "q")
+    _check(cache, torch.int8, "cache")
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bf16 or fp32")
+    _check(out, out.dtype, "out")
+    if lse is not None:
+        _check(lse, torch.float32, "lse")
+    ws_bytes = 0
+    if mla_workspace is not None:
+        _check(mla_workspace, mla_workspace.dtype, "mla_workspace")
+        ws_bytes = mla_workspace.numel() * mla_workspace.element_size()
+    return _call("dsa_topk_sparse_mla", prepare,
+        ctypes.byref(dims), scores.data_ptr(), scores.shape[1], ctypes.byref(seqs._c()), seqs.num_seqs,
+        q_seq.data_ptr(), q_pos.data_ptr(), q_pos.shape[0], _ptr(pool_ids), indices.data_ptr(),
+        select_workspace.data_ptr(), select_workspace.numel() * select_workspace.element_size(),
+        q.data_ptr(), _dt(q), cache.data_ptr(), cache.shape[0], float(scale), out.data_ptr(), _dt(out),
+        _ptr(lse), int(num_splits), _ptr(mla_workspace), ws_bytes, _stream(stream))
 
 
 def decode_step_workspace_bytes(dims: Dims, T: int, score_stride: int) -> int:

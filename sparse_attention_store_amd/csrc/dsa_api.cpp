@@ -400,6 +400,36 @@ int dsa_sparse_mla(const dsa_dims* dims, const void* q, int q_dtype, const int8_
                                                   out_dtype, lse, workspace, as_stream(stream)));
 }
 
+int dsa_topk_sparse_mla(const dsa_dims* dims, const float* scores, int32_t score_stride, const dsa_seqs* seqs,
+                        int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos, int32_t T, int32_t* pool_ids,
+                        int32_t* indices, const void* select_workspace, size_t select_workspace_bytes,
+                        const void* q, int q_dtype, const int8_t* cache, int64_t cache_rows, float scale, void* out,
+                        int out_dtype, float* lse, int32_t num_splits, void* mla_workspace,
+                        size_t mla_workspace_bytes, void* stream) {
+    // the selection half: what dsa_topk_select_groups checks
+    int st = groups_common(dims, seqs, num_seqs, T, score_stride, const_cast<void*>(select_workspace),
+                           select_workspace_bytes);
+    if (st) return st;
+    if (T == 0) return DSA_OK;
+    if (score_stride == 0) return DSA_ERR_UNSUPPORTED;
+    if (!scores || !q_seq || !q_pos || !indices) return DSA_ERR_NULL;
+    // the attention half: what dsa_sparse_mla checks
+    if (q_dtype != DSA_F32 && q_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    if (out_dtype != DSA_F32 && out_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    if (cache_rows < 0 || num_splits < 0) return DSA_ERR_SIZE;
+    if (dims->latent_dim % 64 != 0 || dims->latent_dim > 1024) return DSA_ERR_UNSUPPORTED;
+    if (!q || !cache || !out) return DSA_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(out, 16)) return DSA_ERR_ALIGN;
+    const dsa_host::MlaPlan plan = dsa_host::plan_sparse_mla(*dims, T, num_splits, q_dtype);
+    if (plan.ws_bytes > 0) {
+        if (!mla_workspace || mla_workspace_bytes < plan.ws_bytes) return DSA_ERR_WORKSPACE;
+        if (!aligned(mla_workspace, 256)) return DSA_ERR_ALIGN;
+    }
+    return hip_status(dsa_host::launch_select_mla(*dims, plan, scores, score_stride, *seqs, q_seq, q_pos, T,
+                                                  pool_ids, indices, select_workspace, q, q_dtype, cache, scale,
+                                                  out, out_dtype, lse, mla_workspace, as_stream(stream)));
+}
+
 size_t dsa_decode_step_workspace_bytes(const dsa_dims* dims, int32_t T, int32_t score_stride) {
     if (check_dims(dims) != DSA_OK || T <= 0 || score_stride <= 0) return 0;
     if (!dsa_host::decode_step_supported(*dims, T, score_stride)) return 0;

@@ -71,6 +71,18 @@ hipError_t launch_sparse_mla(const dsa_dims& d, const MlaPlan& plan, const void*
                              const int8_t* cache, const int32_t* indices, int32_t T, float scale,
                              void* out, int out_dtype, float* lse, void* ws, hipStream_t s);
 
+// The merge of a split plan's partials (nothing when plan.splits == 1).
+hipError_t launch_mla_merge(const dsa_dims& d, const MlaPlan& plan, int32_t T, void* ws, void* out, int out_dtype,
+                            float* lse, hipStream_t s);
+// Selection from the group lists, the expanded list and the split attention
+// in one launch, then the merge; shapes the one-launch form does not cover
+// run launch_topk_groups + launch_sparse_mla.
+hipError_t launch_select_mla(const dsa_dims& d, const MlaPlan& plan, const float* scores, int32_t stride,
+                             const dsa_seqs& seqs, const int32_t* q_seq, const int32_t* q_pos, int32_t T,
+                             int32_t* pool_ids, int32_t* indices, const void* sel_ws, const void* q, int q_dtype,
+                             const int8_t* cache, float scale, void* out, int out_dtype, float* lse, void* mla_ws,
+                             hipStream_t s);
+
 bool decode_step_supported(const dsa_dims& d, int32_t T, int32_t stride);
 size_t decode_step_workspace_bytes(const dsa_dims& d, int32_t T, int32_t stride);
 hipError_t launch_decode_step(const dsa_dims& d, const uint16_t* q_idx, const float* w, const uint16_t* pools,

@@ -524,9 +524,19 @@ hipError_t launch_sparse_mla(const dsa_dims& d, const MlaPlan& plan, const void*
             break;
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || plan.splits == 1) return e;
+    if (e != hipSuccess) return e;
+    return launch_mla_merge(d, plan, T, ws, out, out_dtype, lse, s);
+}
+
+hipError_t launch_mla_merge(const dsa_dims& d, const MlaPlan& plan, int32_t T, void* ws, void* out, int out_dtype,
+                            float* lse, hipStream_t s) {
+    if (T == 0 || plan.splits == 1) return hipSuccess;
+    const int H = d.mla_heads;
+    float* part_o = reinterpret_cast<float*>(ws);
+    const dsa::MlaPartial* part_ml =
+        reinterpret_cast<const dsa::MlaPartial*>(part_o + (size_t)T * plan.splits * H * dsa::kD);
     hipLaunchKernelGGL(dsa::k_mla_combine, dim3((unsigned)H, (unsigned)T), dim3(128), 0, s, part_o, part_ml,
-                       plan.splits, H, out, out_f32, lse);
+                       plan.splits, H, out, out_dtype == DSA_F32 ? 1 : 0, lse);
     return hipGetLastError();
 }
 

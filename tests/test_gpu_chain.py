@@ -137,6 +137,19 @@ def test_chain_full_size_sampled(harness, name):
         queries = list(range(wl.T))
     say(f"chain full {name}: checking {len(queries)} queries on the CPU")
     _check_chain(dw, queries, pool_sample=64, allow_swaps_frac=0.25)
+    if wl.T <= 64:
+        # the launches the bench times (prepared calls) give the same bits
+        say(f"chain full {name}: the timed launches")
+        ref = [x.clone() for x in (dw.scores, dw.pool_ids, dw.indices, dw.out, dw.lse)]
+        for x in (dw.pool_ids, dw.indices):
+            x.fill_(0x5A5A5A5A)
+        for x in (dw.scores, dw.out, dw.lse):
+            x.fill_(float("nan"))
+        dw.step_fast()
+        torch.cuda.synchronize()
+        for what, a, b in zip(("scores", "pool_ids", "indices", "out", "lse"), ref,
+                              (dw.scores, dw.pool_ids, dw.indices, dw.out, dw.lse)):
+            assert torch.equal(a, b), what
     del dw
     torch.cuda.empty_cache()
 
@@ -214,4 +227,42 @@ def test_append_scores_groups_matches_separate_calls(harness, name, span):
     # the separate calls rebuilt the poisoned pools exactly as the cache build did
     assert torch.equal(outs[0][1], dw.pools[0].view(torch.int16).cpu())
     for what, a, b in zip(("cache", "pools", "scores", "workspace", "indices", "pool_ids"), outs[0], outs[1]):
+        assert torch.equal(a, b), what
+
+
+@pytest.mark.parametrize("name,splits,case", [("mini_decode", 17, "lists"), ("mini_decode", 0, "lists"),
+                                              ("mini_decode", 1, "lists"), ("mini_heavy", 17, "lists"),
+                                              ("mini_heavy", 3, "lists"), ("decode_32k", 17, "lists"),
+                                              ("decode_32k", 17, "equal_scores"), ("mini_decode", 17, "fp32_q")])
+def test_topk_sparse_mla_matches_separate_calls(harness, name, splits, case):
+    """topk_sparse_mla gives the bits of topk_select_groups then sparse_mla
+    over its list: pool ids, index list, out and lse.  equal_scores (q_idx =
+    0) fails every list check, so each workgroup takes the exact pass over the
+    scores; fp32 q runs the two calls (no one-launch form)."""
+    import sparse_attention_store_amd as dsa
+    wl = syn.get(name)
+    say(f"topk_sparse_mla {name} splits={splits} {case}")
+    dw = harness.DeviceWorkload(wl, num_splits=splits)
+    if case == "equal_scores":
+        dw.q_idx.zero_()
+    q = dw.q.float() if case == "fp32_q" else dw.q
+    dw.step_append()
+    dw.step_scores_groups()
+    outs = []
+    for fused in (False, True):
+        pid = torch.full_like(dw.pool_ids, 0x5A5A5A5A)
+        idx = torch.full_like(dw.indices, 0x5A5A5A5A)
+        out = torch.full_like(dw.out, float("nan"))
+        lse = torch.full_like(dw.lse, float("nan"))
+        if fused:
+            dsa.topk_sparse_mla(dw.dims, dw.scores, dw.seqs, dw.q_seq, dw.q_pos, idx, dw._ws_ss(), q, dw.caches[0],
+                                wl.scale, out, lse, splits, dw.ws_mla, pool_ids=pid)
+        else:
+            dsa.topk_select_groups(dw.dims, dw.scores, dw.seqs, dw.q_seq, dw.q_pos, idx, dw._ws_ss(), pool_ids=pid)
+            dsa.sparse_mla(dw.dims, q, dw.caches[0], idx, wl.scale, out, lse, splits, dw.ws_mla)
+        torch.cuda.synchronize()
+        outs.append([x.cpu() for x in (pid, idx, out, lse)])
+    if case == "equal_scores":
+        assert np.array_equal(outs[0][0][0].numpy(), np.arange(wl.dims.select_k))
+    for what, a, b in zip(("pool_ids", "indices", "out", "lse"), outs[0], outs[1]):
         assert torch.equal(a, b), what
