@@ -252,7 +252,7 @@ def main():
     # The timed loop launches through prepared calls (validated and converted
     # once per replica): each launch then costs one ctypes call on the host, so
     # the host keeps ahead of the GPU.
-    timed_stages = ["append", "decode"] if fused else ["append_scores", "select_groups", "attention"]
+    timed_stages = ["append", "decode"] if fused else ["append_scores", "select_attention"]
     for r in range(R):
         for st in timed_stages:
             dw.bound(st, r)
@@ -287,8 +287,7 @@ def main():
             dw.run("append_scores", r)
             if i in ev_e:
                 ev_e[i].record(stream)
-            dw.run("select_groups", r)
-            dw.run("attention", r)
+            dw.run("select_attention", r)
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
@@ -301,7 +300,7 @@ def main():
         names = ["append_tokens", "decode_step"]
         fns = [lambda r: dw.run("append", r), lambda r: dw.run("decode", r)]
     else:
-        names = ["append_scores_groups", "topk_select_groups", "sparse_mla"]
+        names = ["append_scores_groups", "topk_sparse_mla"]
         fns = [lambda r, st=st: dw.run(st, r) for st in timed_stages]
     n_b = min(args.steps, 50)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(n_b)]
