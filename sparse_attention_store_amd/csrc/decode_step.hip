@@ -489,8 +489,9 @@ __global__ __launch_bounds__(kStepNT, 1) void k_decode_step(StepArgs a) {
                 for (int i = tid; i < a.select_k; i += kStepNT)
                     a.pool_ids[(int64_t)t * a.select_k + i] =
                         i < K ? (sparse ? (int)ld_coh32(selt + i) : i) : -1;
-            mla_rows_split<2, true>(sm.mla, a.q, a.cache, a.row_bytes, idx_at, a.W, a.H, a.scale_log2, t, head0,
-                                 split, split, split + 1, a.splits, a.part_o, a.part_ml, a.out, a.out_f32, a.lse);
+            mla_rows_split<2, true>(sm.mla, [&](int i) { return mla_q_piece<kStepNT>(a.q, t, a.H, head0, i); },
+                                    a.cache, a.row_bytes, idx_at, a.W, a.H, a.scale_log2, t, head0, split, split,
+                                    split + 1, a.splits, a.part_o, a.part_ml, a.out, a.out_f32, a.lse);
             if (a.splits > 1) publish(&C->splits_done[t]);
             lds_barrier();
         } else {

@@ -9,7 +9,8 @@
 // allows, since at one workgroup per row the barriers are the cost:
 //   A  list slots are valid by position alone (empty slots hold key 0), so
 //      the per-wave min/max is published with the group counts;
-//   B, C per bucketing pass: the histogram, then wave 0's search of it;
+//   B, C per bucketing pass: the histogram, then the search of it (by every
+//      wave when there are at most 8, so C needs no barrier of its own);
 //   D  the boundary bucket's entries: each thread then ranks its own;
 //   E  per-wave pick counts (output order) and the list check, both local:
 //      a group that dropped pools and has all m kept entries picked fails
@@ -106,6 +107,7 @@ __device__ __forceinline__ GroupQuery select_from_groups(
     constexpr int GPT = kMaxGroups / NT;     // group counts per thread
     constexpr int BITS = log2_of<NB>();
     constexpr uint32_t ALL = (1u << KPT) - 1u;
+    constexpr bool kWaveSearch = NW <= 8;
     static_assert(KPT >= 8 && KPT <= 16 && GPT * NT == kMaxGroups, "8 or 16 list slots per thread");
     static_assert(PER == 16 && kBoundCap % 8 == 0, "one 16-lane row per bucket run; rank in steps of 8");
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -193,43 +195,51 @@ __device__ __forceinline__ GroupQuery select_from_groups(
             atomicAdd(&H[off <= span ? (off >> sh) : (uint32_t)(NB + lane)], 1u);
         }
         lds_barrier();
-        if (w == 0) {
-            // bucket d (descending: bucket NB-1-d) holding rank krem; lane l
-            // sums d in [l PER, (l+1) PER), read in a rotated, conflict-free order
+        // bucket d (descending: bucket NB-1-d) holding rank krem; lane l sums
+        // d in [l PER, (l+1) PER), read in a rotated, conflict-free order.
+        // With at most 8 waves every wave searches (the same answer, no second
+        // barrier); with more, wave 0 searches and publishes the result.
+        uint32_t r_d = 0u, r_above = 0u, r_c = 0u, r_none = 1u;
+        if (kWaveSearch || w == 0) {
             uint32_t lsum = 0u;
 #pragma unroll
             for (int i = 0; i < PER; ++i) lsum += H[NB - 1 - (lane * PER + ((i + lane / (64 / PER)) & (PER - 1)))];
             const uint32_t incl = wave_incl_sum_u32(lsum), excl = incl - lsum;
             const unsigned long long hit = __ballot(excl < krem && krem <= incl);
-            uint32_t d = 0u, above = 0u, c = 0u, none = 1u;
             if (hit != 0ull) {
                 // within lane L's run: lane i of each row reads its bucket L PER + i,
                 // a row scan gives the running counts, the first that reaches krem wins
-                none = 0u;
+                r_none = 0u;
                 const int L = __ffsll((long long)hit) - 1;
                 const uint32_t acc = __builtin_amdgcn_readlane(excl, L);
                 const uint32_t v = H[NB - 1 - (L * PER + (lane & (PER - 1)))];
                 const uint32_t run = row_incl_sum_u32(v);
                 const int i = __ffsll((long long)(__ballot(krem <= acc + run) & 0xFFFFull)) - 1;
-                d = (uint32_t)(L * PER + i);
-                c = __builtin_amdgcn_readlane(v, i);
-                above = acc + __builtin_amdgcn_readlane(run, i) - c;
+                r_d = (uint32_t)(L * PER + i);
+                r_c = __builtin_amdgcn_readlane(v, i);
+                r_above = acc + __builtin_amdgcn_readlane(run, i) - r_c;
             }
-            if (lane == 0) {
-                G.res[0] = d;
-                G.res[1] = above;
-                G.res[2] = c;
-                G.res[3] = none;
+            if (!kWaveSearch && lane == 0) {
+                G.res[0] = r_d;
+                G.res[1] = r_above;
+                G.res[2] = r_c;
+                G.res[3] = r_none;
             }
         }
-        lds_barrier();
-        if (G.res[3]) {                      // fewer present keys than the target: all of them
+        if constexpr (!kWaveSearch) {
+            lds_barrier();
+            r_d = G.res[0];
+            r_above = G.res[1];
+            r_c = G.res[2];
+            r_none = G.res[3];
+        }
+        if (r_none) {                        // fewer present keys than the target: all of them
             whole = true;
             break;
         }
-        krem -= G.res[1];
-        cnt = G.res[2];
-        const uint32_t nlo = lo + ((NB - 1 - G.res[0]) << sh);
+        krem -= r_above;
+        cnt = r_c;
+        const uint32_t nlo = lo + ((NB - 1 - r_d) << sh);
         const uint32_t nhi = nlo + ((1u << sh) - 1u);
         lo = nlo;
         hi = nhi < hi ? nhi : hi;

@@ -102,16 +102,25 @@ __device__ __forceinline__ void store_partial(MlaPartial* p, MlaPartial v) {
     }
 }
 
+// 16-byte piece i of this thread's share of q (16 heads x 512 bf16 of query
+// t from head0; piece k = tid + NT i holds head k / 64, dims 8 (k % 64) ..).
+template <int NT>
+__device__ __forceinline__ u32x4 mla_q_piece(const uint16_t* __restrict__ q, int t, int H, int head0, int i) {
+    return *reinterpret_cast<const u32x4*>(q + ((int64_t)t * H + head0) * kD + 8 * (threadIdx.x + NT * i));
+}
+
 // One split of k_mla_rows: query t, heads [head0, head0 + 16), list chunks
 // [c_begin, c_end) of 16 * RT * NW positions (each of the NW waves owns RT
-// 16-row tiles of a chunk and 512 / NW columns of the output).  idx_at(pos) gives the cache row of list position pos (< W), or a
-// negative value for an empty slot.  COH makes the partial results
+// 16-row tiles of a chunk and 512 / NW columns of the output).  idx_at(pos)
+// gives the cache row of list position pos (< W), or a negative value for an
+// empty slot; q_piece(i) gives piece i of this thread's share of q (see
+// mla_q_piece), loaded there or earlier.  COH makes the partial results
 // agent-coherent (read back by another workgroup of the same launch) instead
 // of plain stores.  Every thread of the block must call it; it contains
 // workgroup barriers.
-template <int RT, bool COH, int NW = 4, class IdxFn>
+template <int RT, bool COH, int NW = 4, class IdxFn, class QFn>
 __device__ __forceinline__ void mla_rows_split(
-    MlaRowsSmemT<RT, NW>& sm, const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, int row_bytes,
+    MlaRowsSmemT<RT, NW>& sm, QFn q_piece, const uint8_t* __restrict__ cache, int row_bytes,
     IdxFn idx_at, int W, int H, float scale_log2, int t, int head0, int split, int c_begin, int c_end,
     int splits, float* __restrict__ part_o, MlaPartial* __restrict__ part_ml, void* __restrict__ out,
     int out_f32, float* __restrict__ lse) {
@@ -165,11 +174,8 @@ __device__ __forceinline__ void mla_rows_split(
         if (c_begin + 1 < c_end) load_idx(c_begin + 1, id_next);
     }
     u32x4 qv[QP];
-    {
-        const uint16_t* qh = q + ((int64_t)t * H + head0) * kD;
 #pragma unroll
-        for (int i = 0; i < QP; ++i) qv[i] = *reinterpret_cast<const u32x4*>(qh + 8 * (tid + NT * i));
-    }
+    for (int i = 0; i < QP; ++i) qv[i] = q_piece(i);
     if (c_begin < c_end) load_rows(id_cur);
 #pragma unroll
     for (int i = 0; i < QP; ++i) {

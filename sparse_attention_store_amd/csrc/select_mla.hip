@@ -38,7 +38,12 @@ __global__ __launch_bounds__(64 * NW, 1) void k_select_mla(
     MlaPartial* __restrict__ part_ml, void* __restrict__ out, int out_f32, float* __restrict__ lse) {
     constexpr int NT = 64 * NW, CH = 16 * NW;
     __shared__ __attribute__((aligned(16))) SelectMlaSmem<NW> sm;
-    const int split = blockIdx.x, t = blockIdx.z;
+    const int split = blockIdx.x, t = blockIdx.z, head0 = blockIdx.y * 16;
+    // q is read now, so that it has arrived when the attention starts
+    constexpr int QP = 16 * kD * 2 / 16 / NT;
+    u32x4 qv[QP];
+#pragma unroll
+    for (int i = 0; i < QP; ++i) qv[i] = mla_q_piece<NT>(q, t, H, head0, i);
     const GroupQuery g = select_from_groups<NT>(sm.u.g, sm.sel, scores, first_valid, q_seq, q_pos, e.row_base,
                                                 stride, select_k, cand, cand_n, t);
     const int32_t* sel = g.listed ? sm.sel : nullptr;
@@ -58,8 +63,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_select_mla(
     const int nchunks = (W + CH - 1) / CH;
     const int c_begin = split * chunks_per_split;
     const int c_end = min(c_begin + chunks_per_split, nchunks);
-    mla_rows_split<1, false, NW>(sm.u.m, q, cache, row_bytes, idx_at, W, H, scale_log2, t, blockIdx.y * 16, split,
-                                 c_begin, c_end, splits, part_o, part_ml, out, out_f32, lse);
+    mla_rows_split<1, false, NW>(sm.u.m, [&](int i) { return qv[i]; }, cache, row_bytes, idx_at, W, H, scale_log2, t,
+                                 head0, split, c_begin, c_end, splits, part_o, part_ml, out, out_f32, lse);
 }
 
 }  // namespace dsa

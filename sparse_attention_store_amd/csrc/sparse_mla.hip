@@ -64,8 +64,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_mla_rows(
     const int c_begin = split * chunks_per_split;
     const int c_end = min(c_begin + chunks_per_split, nchunks);
     const int32_t* irow = indices + (int64_t)t * W;
-    mla_rows_split<RT, false, NW>(sm, q, cache, row_bytes, [&](int pos) { return irow[pos]; }, W, H, scale_log2, t,
-                              blockIdx.y * 16, split, c_begin, c_end, splits, part_o, part_ml, out, out_f32, lse);
+    const int head0 = blockIdx.y * 16;
+    mla_rows_split<RT, false, NW>(sm, [&](int i) { return mla_q_piece<64 * NW>(q, t, H, head0, i); }, cache, row_bytes,
+                                  [&](int pos) { return irow[pos]; }, W, H, scale_log2, t, head0, split, c_begin,
+                                  c_end, splits, part_o, part_ml, out, out_f32, lse);
 }
 
 // ------------------------------------------------------------------ k_mla_mfma
