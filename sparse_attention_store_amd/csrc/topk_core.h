@@ -216,20 +216,22 @@ __device__ __forceinline__ void keep_group_best(float s, bool valid, int p, int 
     const int nvalid = __popcll(__ballot(valid));
     bool pick = valid;
     if (nvalid > m && m <= 8) {
-        // Small m: take the largest remaining key m times (a DPP wave max,
-        // then the lowest lane holding it) -- mostly vector work, where a
-        // bitwise threshold search is a long chain of scalar instructions
-        // that the waves of a CU would all issue at once.  Each round costs
-        // about a sixth of the 32-step search, so from m = 16 on the search
-        // is the cheaper one (measured per wave: m = 16 rounds 2.7 us,
-        // search 1.6 us).
-        uint32_t k = key;
-        pick = false;
-        for (int i = 0; i < m; ++i) {
-            const uint32_t mx = wave_max_u32(valid && !pick ? k : 0u);
-            const unsigned long long at = __ballot(valid && !pick && k == mx);
-            if (lane == __ffsll((long long)at) - 1) pick = true;
+        // m = 8: take the largest remaining key 8 times (a DPP wave max, then
+        // the lowest lane holding it, which drops out) -- a dozen mostly
+        // vector instructions a round, where the 32-step threshold search
+        // below is a chain of scalar ones that the waves of a CU would all
+        // issue at once.  From m = 16 on the search is the cheaper one
+        // (measured per wave: 16 rounds 2.7 us, the search 1.6 us).
+        uint32_t cur = key;                     // 0: invalid or taken
+        unsigned long long taken = 0ull;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t mx = wave_max_u32(cur);
+            const int first = __ffsll((long long)__ballot(cur == mx)) - 1;
+            taken |= 1ull << first;
+            cur = lane == first ? 0u : cur;
         }
+        pick = (taken >> lane) & 1ull;
     } else if (nvalid > m) {
         // x = the m-th largest key: the largest x with at least m keys >= x
         uint32_t x = 0u;
