@@ -173,7 +173,7 @@ struct QueryGeom {
     int64_t tok0;      // with new tokens: the sequence's first pooled token row
     int32_t pb, pe;    // with new tokens: the pools this step completes
     int32_t rank;      // with new tokens: rank among the queries that have tiles
-    int32_t gm;        // group list length (group_quota), 0 if no lists are kept
+    int32_t pad;
 };
 struct AppendArgs {    // the step's new tokens (append_tokens' arguments)
     const uint16_t* latent;
@@ -236,8 +236,7 @@ __global__ __launch_bounds__(256, 4) void k_scores_groups(
             off = (uint32_t)__popcll(lead);
         }
         const uint32_t incl = wave_incl_sum_u32(nt);
-        const int gm = CANDS && nn > select_k ? group_quota(select_k, nn) : 0;
-        geom[lane] = QueryGeom{base, off + incl - nt, nt, ng, nn, tok0, pb, pe, rank, gm};
+        geom[lane] = QueryGeom{base, off + incl - nt, nt, ng, nn, tok0, pb, pe, rank, 0};
     }
     lds_barrier();
     const int total = (int)(geom[63].first + geom[63].ntiles);
@@ -275,6 +274,8 @@ __global__ __launch_bounds__(256, 4) void k_scores_groups(
         const int lp0 = has ? p0 : p0 - kGroupPools * wave;
         load_pool_group(pools + ((int64_t)uniform64((uint64_t)geom[t].base) + lp0) * kDI, has ? n_vis - p0 : 1, v);
         __builtin_amdgcn_sched_barrier(0);             // every load in flight before the A operand is shared
+        // the group list length, while the rows are in flight
+        const int gm = CANDS && n_vis > select_k ? group_quota(select_k, n_vis) : 0;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int k = lane + 64 * i;
@@ -326,7 +327,7 @@ __global__ __launch_bounds__(256, 4) void k_scores_groups(
             }
             if constexpr (CANDS) {
                 if (n_vis > select_k)
-                    keep_group_best(s, p < n_vis, p, grp, uniform32(geom[t].gm),
+                    keep_group_best(s, p < n_vis, p, grp, gm,
                                     cand + (int64_t)t * kGroupCandCap, cand_n + (int64_t)t * kMaxGroups,
                                     [](uint64_t* q, uint64_t x) { *q = x; },
                                     [](int32_t* q, uint32_t x) { *q = (int32_t)x; });
