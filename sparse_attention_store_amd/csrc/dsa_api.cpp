@@ -177,7 +177,7 @@ int dsa_index_scores(const dsa_dims* dims, const uint16_t* q_idx, const float* w
     if (T > 65535 * 64) return DSA_ERR_SIZE;
     if (!q_idx || !w || !pools || !q_seq || !q_pos || !scores) return DSA_ERR_NULL;
     if (!aligned(q_idx, 16) || !aligned(pools, 16) || !aligned(scores, 4)) return DSA_ERR_ALIGN;
-    return hip_status(dsa_host::launch_index_scores(*dims, q_idx, w, pools, *seqs, q_seq, q_pos, T,
+    return hip_status(dsa_host::launch_index_scores(*dims, q_idx, w, pools, *seqs, num_seqs, q_seq, q_pos, T,
                                                     score_stride, scores, as_stream(stream)));
 }
 
@@ -254,7 +254,7 @@ int dsa_index_scores_groups(const dsa_dims* dims, const uint16_t* q_idx, const f
     if (st || T == 0 || score_stride == 0) return st;
     if (!q_idx || !w || !pools || !q_seq || !q_pos || !scores) return DSA_ERR_NULL;
     if (!aligned(q_idx, 16) || !aligned(pools, 16) || !aligned(w, 16)) return DSA_ERR_ALIGN;
-    return hip_status(dsa_host::launch_scores_with_groups(*dims, q_idx, w, pools, *seqs, q_seq, q_pos, T,
+    return hip_status(dsa_host::launch_scores_with_groups(*dims, q_idx, w, pools, *seqs, num_seqs, q_seq, q_pos, T,
                                                           score_stride, scores, workspace, as_stream(stream)));
 }
 
@@ -305,11 +305,11 @@ int dsa_append_scores_groups(const dsa_dims* dims, int dtype, const void* latent
             if (e != hipSuccess) return DSA_ERR_HIP;
         }
         if (!scoring) return DSA_OK;
-        return hip_status(dsa_host::launch_scores_with_groups(*dims, q_idx, w, pools, *seqs, q_seq, q_pos, T,
+        return hip_status(dsa_host::launch_scores_with_groups(*dims, q_idx, w, pools, *seqs, num_seqs, q_seq, q_pos, T,
                                                               score_stride, scores, workspace, s));
     }
     return hip_status(dsa_host::launch_append_scores_groups(
-        *dims, latent, n, ld, slots, cache, k, gate, ln_w, ln_b, *seqs, max_pools > 0 ? num_seqs : 0, pool_begin,
+        *dims, latent, n, ld, slots, cache, k, gate, ln_w, ln_b, *seqs, num_seqs, pool_begin,
         pool_end, max_pools, pools, q_idx, w, q_seq, q_pos, T, score_stride, scores, workspace, s));
 }
 
@@ -345,13 +345,13 @@ int dsa_index_scores_select(const dsa_dims* dims, const uint16_t* q_idx, const f
     }
     hipStream_t s = as_stream(stream);
     if (dsa_host::scores_select_grouped(*dims, T, score_stride)) {
-        hipError_t e = dsa_host::launch_scores_with_groups(*dims, q_idx, w, pools, *seqs, q_seq, q_pos, T,
+        hipError_t e = dsa_host::launch_scores_with_groups(*dims, q_idx, w, pools, *seqs, num_seqs, q_seq, q_pos, T,
                                                            score_stride, scores, workspace, s);
         if (e != hipSuccess) return DSA_ERR_HIP;
         return hip_status(dsa_host::launch_topk_groups(*dims, scores, score_stride, *seqs, q_seq, q_pos, T,
                                                        pool_ids, indices, workspace, s));
     }
-    hipError_t e = dsa_host::launch_index_scores(*dims, q_idx, w, pools, *seqs, q_seq, q_pos, T, score_stride,
+    hipError_t e = dsa_host::launch_index_scores(*dims, q_idx, w, pools, *seqs, num_seqs, q_seq, q_pos, T, score_stride,
                                                  scores, s);
     if (e != hipSuccess) return DSA_ERR_HIP;
     return hip_status(dsa_host::launch_topk(*dims, scores, score_stride, *seqs, q_seq, q_pos, T, pool_ids,

@@ -25,14 +25,16 @@ hipError_t launch_append_tokens(const dsa_dims& d, int dtype, const void* latent
                                 uint16_t* pools, hipStream_t s);
 
 hipError_t launch_index_scores(const dsa_dims& d, const uint16_t* q_idx, const float* w,
-                               const uint16_t* pools, const dsa_seqs& seqs, const int32_t* q_seq,
+                               const uint16_t* pools, const dsa_seqs& seqs, int32_t num_seqs,
+                               const int32_t* q_seq,
                                const int32_t* q_pos, int32_t T, int32_t stride, float* scores,
                                hipStream_t s);
 
 bool scores_select_grouped(const dsa_dims& d, int32_t T, int32_t stride);
 size_t scores_select_group_bytes(int32_t T);
 hipError_t launch_scores_with_groups(const dsa_dims& d, const uint16_t* q_idx, const float* w,
-                                     const uint16_t* pools, const dsa_seqs& seqs, const int32_t* q_seq,
+                                     const uint16_t* pools, const dsa_seqs& seqs, int32_t num_seqs,
+                                     const int32_t* q_seq,
                                      const int32_t* q_pos, int32_t T, int32_t stride, float* scores, void* ws,
                                      hipStream_t s);
 bool append_scores_fused(const dsa_dims& d, int dtype);

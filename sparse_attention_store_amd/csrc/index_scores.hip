@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256, 4) void k_scores_groups(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint16_t* pools, const int32_t* __restrict__ first_valid,
     const int64_t* __restrict__ pool_base, const int32_t* __restrict__ q_seq,
-    const int32_t* __restrict__ q_pos, int T, int stride, float* __restrict__ scores,
+    const int32_t* __restrict__ q_pos, int T, int nseq, int stride, float* __restrict__ scores,
     int select_k, uint64_t* __restrict__ cand, int32_t* __restrict__ cand_n, AppendArgs ap) {
     __shared__ QueryGeom geom[kDecMaxT];
     __shared__ __attribute__((aligned(16))) uint16_t s_q[kHI * kQStride];
@@ -208,18 +208,46 @@ __global__ __launch_bounds__(256, 4) void k_scores_groups(
     const int lane = threadIdx.x & 63;
     const int wave = uniform32(threadIdx.x >> 6);
     if (wave == 0) {
+        // One memory round trip: lane t < T reads query t's fields while lane
+        // s < nseq reads sequence s's (bounded buffer loads: absent fields
+        // read 0), then each query takes its sequence's from that lane.  With
+        // more than 64 sequences they are read by query, after q_seq.
+        const bool pools_ad = AD && ap.pool_bx > 0;
+        const uint32_t l4 = (uint32_t)lane * 4u;
+        const uint32_t qb = (uint32_t)min(T, kWave) * 4u;
+        const int b = (int)__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(q_seq, qb), l4, 0, 0);
+        const int qp = (int)__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(q_pos, qb), l4, 0, 0);
+        const uint32_t sb = (uint32_t)nseq * 4u, pbb = pools_ad ? sb : 0u;
+        int f, pb_s, pe_s;
+        u32x2 bs, ts;
+        auto fields = [&](uint32_t s4) {
+            f = (int)__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(first_valid, sb), s4, 0, 0);
+            bs = __builtin_amdgcn_raw_buffer_load_b64(buffer_rsrc(pool_base, 2u * sb), 2u * s4, 0, 0);
+            pb_s = (int)__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(ap.pool_begin, pbb), s4, 0, 0);
+            pe_s = (int)__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(ap.pool_end, pbb), s4, 0, 0);
+            ts = __builtin_amdgcn_raw_buffer_load_b64(buffer_rsrc(ap.tok_base, 2u * pbb), 2u * s4, 0, 0);
+        };
+        if (nseq <= kWave) {
+            fields(l4);                                 // independent of b: issued with the query loads
+            f = __shfl(f, b);
+            bs[0] = (uint32_t)__shfl((int)bs[0], b);
+            bs[1] = (uint32_t)__shfl((int)bs[1], b);
+            pb_s = __shfl(pb_s, b);
+            pe_s = __shfl(pe_s, b);
+            ts[0] = (uint32_t)__shfl((int)ts[0], b);
+            ts[1] = (uint32_t)__shfl((int)ts[1], b);
+        } else {
+            fields((uint32_t)b * 4u);
+        }
         int nn = 0, pb = 0, pe = 0;
         int64_t base = 0, tok0 = 0;
         if (lane < T) {
-            const int b = q_seq[lane];
-            const int f = first_valid[b];
-            const int qp = q_pos[lane];
             nn = min(qp >= f ? (qp - f + 1) >> 2 : 0, stride);
-            base = pool_base[b];
-            if (AD && ap.pool_bx > 0) {
-                pb = ap.pool_begin[b];
-                pe = min(ap.pool_end[b], pb + 4 * ap.pool_bx);   // what the pool tasks build
-                tok0 = ap.tok_base[b] + f;
+            base = (int64_t)(((uint64_t)bs[1] << 32) | bs[0]);
+            if (pools_ad) {
+                pb = pb_s;
+                pe = min(pe_s, pb + 4 * ap.pool_bx);          // what the pool tasks build
+                tok0 = (int64_t)(((uint64_t)ts[1] << 32) | ts[0]) + f;
             }
         }
         const int ng = (nn + kGroupPools - 1) / kGroupPools;
@@ -399,7 +427,8 @@ static unsigned scores_groups_grid(int32_t T, int32_t stride) {
 }
 
 hipError_t launch_index_scores(const dsa_dims& d, const uint16_t* q_idx, const float* w,
-                               const uint16_t* pools, const dsa_seqs& seqs, const int32_t* q_seq,
+                               const uint16_t* pools, const dsa_seqs& seqs, int32_t num_seqs,
+                               const int32_t* q_seq,
                                const int32_t* q_pos, int32_t T, int32_t stride, float* scores,
                                hipStream_t s) {
     if (T == 0 || stride == 0) return hipSuccess;
@@ -407,8 +436,8 @@ hipError_t launch_index_scores(const dsa_dims& d, const uint16_t* q_idx, const f
         if (T <= dsa::kDecMaxT) {
             // Decode: one wave per 64-pool group, a resident grid.
             hipLaunchKernelGGL((dsa::k_scores_groups<false, 0>), dim3(scores_groups_grid(T, stride)), dim3(256), 0,
-                               s, q_idx, w, pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, stride, scores,
-                               0, nullptr, nullptr, dsa::AppendArgs{});
+                               s, q_idx, w, pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, num_seqs,
+                               stride, scores, 0, nullptr, nullptr, dsa::AppendArgs{});
         } else {
             // Prefill: 512 resident pools per workgroup, 64 queries per workgroup.
             const int qpb = 64;
@@ -435,7 +464,8 @@ size_t scores_select_group_bytes(int32_t T) {
 }
 
 hipError_t launch_scores_with_groups(const dsa_dims& d, const uint16_t* q_idx, const float* w,
-                                     const uint16_t* pools, const dsa_seqs& seqs, const int32_t* q_seq,
+                                     const uint16_t* pools, const dsa_seqs& seqs, int32_t num_seqs,
+                                     const int32_t* q_seq,
                                      const int32_t* q_pos, int32_t T, int32_t stride, float* scores, void* ws,
                                      hipStream_t s) {
     if (T == 0 || stride == 0) return hipSuccess;
@@ -443,8 +473,8 @@ hipError_t launch_scores_with_groups(const dsa_dims& d, const uint16_t* q_idx, c
     int32_t* cand_n = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) +
                                                  ((size_t)T * dsa::kGroupCandCap * 8 + 255) / 256 * 256);
     hipLaunchKernelGGL((dsa::k_scores_groups<true, 0>), dim3(scores_groups_grid(T, stride)), dim3(256), 0, s,
-                       q_idx, w, pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, stride, scores,
-                       d.index_topk / d.kpool, cand, cand_n, dsa::AppendArgs{});
+                       q_idx, w, pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, num_seqs, stride,
+                       scores, d.index_topk / d.kpool, cand, cand_n, dsa::AppendArgs{});
     return hipGetLastError();
 }
 
@@ -480,7 +510,7 @@ hipError_t launch_append_scores_groups(const dsa_dims& d, const void* latent, in
     ap.pool_end = pool_end;
     ap.pools = pools;
     ap.pool_bx = max_pools > 0 ? (int)cdiv(max_pools, 4) : 0;
-    const int64_t pool_tasks = (int64_t)ap.pool_bx * num_seqs;
+    const int64_t pool_tasks = (int64_t)ap.pool_bx * num_seqs;   // 0 without pools
     const int64_t tasks = pool_tasks + cdiv(n, 4);
     if (tasks > 0x3FFFFFFF) return hipErrorInvalidValue;
     ap.pool_tasks = (int)pool_tasks;
@@ -489,8 +519,8 @@ hipError_t launch_append_scores_groups(const dsa_dims& d, const void* latent, in
     const unsigned grid = (unsigned)std::min<int64_t>(std::max<int64_t>(want, 1), 4 * (int64_t)device_info().cu_count);
 #define DSA_APPEND_SCORES(D)                                                                                        \
     hipLaunchKernelGGL((dsa::k_scores_groups<true, D>), dim3(grid), dim3(256), 0, s, q_idx, w, pools,             \
-                       seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, stride, scores, d.index_topk / d.kpool, \
-                       cand, cand_n, ap)
+                       seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, num_seqs, stride, scores,             \
+                       d.index_topk / d.kpool, cand, cand_n, ap)
     switch (d.latent_dim) {
         case 512: DSA_APPEND_SCORES(512); break;
         case 256: DSA_APPEND_SCORES(256); break;
