@@ -97,12 +97,15 @@ struct GroupQuery {
 // Row t's selection from its group lists cand / cand_n.  Every thread of the
 // workgroup must call it.  When `listed`, it returns after a workgroup
 // barrier with sel[0 .. K) written and G no longer in use; otherwise it
-// returns before touching G or sel (and without a barrier).
-template <int NT>
+// returns before touching G or sel (and without a barrier).  issued() runs
+// right after the group lists' loads are issued (the caller's own early
+// loads go there, behind them).
+template <int NT, class Issued>
 __device__ __forceinline__ GroupQuery select_from_groups(
     GroupSelCore<NT>& G, int32_t* sel, const float* __restrict__ scores, const int32_t* __restrict__ first_valid,
     const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, const int64_t* __restrict__ row_base,
-    int stride, int select_k, const uint64_t* __restrict__ cand, const int32_t* __restrict__ cand_n, int t) {
+    int stride, int select_k, const uint64_t* __restrict__ cand, const int32_t* __restrict__ cand_n, int t,
+    Issued issued) {
     constexpr int KPT = kGroupCandCap / NT, NW = NT / 64, NB = kSelBuckets, PER = NB / 64;
     constexpr int GPT = kMaxGroups / NT;     // group counts per thread
     constexpr int BITS = log2_of<NB>();
@@ -127,6 +130,8 @@ __device__ __forceinline__ GroupQuery select_from_groups(
             raw[j + 1] = ((uint64_t)v[3] << 32) | v[2];
         }
     }
+    __builtin_amdgcn_sched_barrier(0);       // the list loads leave first
+    issued();
     GroupQuery g;
     query_geom(first_valid, q_seq, q_pos, t, g.b, g.f, g.qp, g.n_vis);
     g.rb = row_base ? row_base[g.b] : 0;

@@ -39,13 +39,16 @@ __global__ __launch_bounds__(64 * NW, 1) void k_select_mla(
     constexpr int NT = 64 * NW, CH = 16 * NW;
     __shared__ __attribute__((aligned(16))) SelectMlaSmem<NW> sm;
     const int split = blockIdx.x, t = blockIdx.z, head0 = blockIdx.y * 16;
-    // q is read now, so that it has arrived when the attention starts
+    // q is read right behind the group lists, so that it has arrived when
+    // the attention starts
     constexpr int QP = 16 * kD * 2 / 16 / NT;
     u32x4 qv[QP];
-#pragma unroll
-    for (int i = 0; i < QP; ++i) qv[i] = mla_q_piece<NT>(q, t, H, head0, i);
     const GroupQuery g = select_from_groups<NT>(sm.u.g, sm.sel, scores, first_valid, q_seq, q_pos, e.row_base,
-                                                stride, select_k, cand, cand_n, t);
+                                                stride, select_k, cand, cand_n, t, [&] {
+#pragma unroll
+                                                    for (int i = 0; i < QP; ++i)
+                                                        qv[i] = mla_q_piece<NT>(q, t, H, head0, i);
+                                                });
     const int32_t* sel = g.listed ? sm.sel : nullptr;
     if (split == 0 && blockIdx.y == 0) emit_selection<NT>(sel, g.K, select_k, t, g.b, g.f, g.qp, g.n_vis, e, g.rb);
     // list position -> cache row, exactly as emit_selection writes it
