@@ -336,10 +336,19 @@ __global__ __launch_bounds__(128) void k_mla_combine(
     const int h = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
     const float* base = part_o + ((int64_t)t * splits * H + h) * kD + tid * 4;
     const int64_t sstride = (int64_t)H * kD;
+    // The first kPre splits' pieces through one bounded buffer descriptor:
+    // splits past the last read 0, so the loads need no branch and all leave
+    // at once.
     f32x4 pre[kPre];
+    {
+        const uint32_t rec = (uint32_t)(((int64_t)(splits - 1) * H + 1) * kD * 4);
+        const __amdgpu_buffer_rsrc_t rp = buffer_rsrc(part_o + ((int64_t)t * splits * H + h) * kD, rec);
 #pragma unroll
-    for (int u = 0; u < kPre; ++u)
-        pre[u] = u < splits ? *reinterpret_cast<const f32x4*>(base + u * sstride) : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < kPre; ++u) {
+            const u32x4 v = ld_buf128(rp, (uint32_t)(tid * 16 + u * H * kD * 4));
+            pre[u] = f32x4{__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3])};
+        }
+    }
     if (tid < 64) {
         MlaPartial p = {-INFINITY, 0.f};
         if (tid < splits) p = part_ml[((int64_t)t * splits + tid) * H + h];
