@@ -99,13 +99,14 @@ struct GroupQuery {
 // barrier with sel[0 .. K) written and G no longer in use; otherwise it
 // returns before touching G or sel (and without a barrier).  issued() runs
 // right after the group lists' loads are issued (the caller's own early
-// loads go there, behind them).
-template <int NT, class Issued>
+// loads go there, behind them); staged() runs just before the last barrier
+// (LDS writes of the caller's outside G ride on it).
+template <int NT, class Issued, class Staged>
 __device__ __forceinline__ GroupQuery select_from_groups(
     GroupSelCore<NT>& G, int32_t* sel, const float* __restrict__ scores, const int32_t* __restrict__ first_valid,
     const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, const int64_t* __restrict__ row_base,
     int stride, int select_k, const uint64_t* __restrict__ cand, const int32_t* __restrict__ cand_n, int t,
-    Issued issued) {
+    Issued issued, Staged staged) {
     constexpr int KPT = kGroupCandCap / NT, NW = NT / 64, NB = kSelBuckets, PER = NB / 64;
     constexpr int GPT = kMaxGroups / NT;     // group counts per thread
     constexpr int BITS = log2_of<NB>();
@@ -368,6 +369,7 @@ __device__ __forceinline__ GroupQuery select_from_groups(
         }
     }
     // ---- F
+    staged();
     lds_barrier();
     return g;
 }

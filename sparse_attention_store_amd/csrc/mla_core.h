@@ -102,6 +102,17 @@ __device__ __forceinline__ void store_partial(MlaPartial* p, MlaPartial v) {
     }
 }
 
+// This thread's pieces of q (see mla_q_piece) into the padded LDS rows the
+// waves read it from.
+template <int NT, int QP>
+__device__ __forceinline__ void mla_stage_q(uint16_t* qs, const u32x4 (&qv)[QP]) {
+#pragma unroll
+    for (int i = 0; i < QP; ++i) {
+        const int k = threadIdx.x + NT * i;            // 16-byte piece k: head k / 64, dims 8 (k % 64) ..
+        *reinterpret_cast<u32x4*>(&qs[(k >> 6) * kRStride + 8 * (k & 63)]) = qv[i];
+    }
+}
+
 // 16-byte piece i of this thread's share of q (16 heads x 512 bf16 of query
 // t from head0; piece k = tid + NT i holds head k / 64, dims 8 (k % 64) ..).
 template <int NT>
@@ -118,7 +129,7 @@ __device__ __forceinline__ u32x4 mla_q_piece(const uint16_t* __restrict__ q, int
 // agent-coherent (read back by another workgroup of the same launch) instead
 // of plain stores.  Every thread of the block must call it; it contains
 // workgroup barriers.
-template <int RT, bool COH, int NW = 4, class IdxFn, class QFn>
+template <int RT, bool COH, int NW = 4, bool QS_READY = false, class IdxFn, class QFn>
 __device__ __forceinline__ void mla_rows_split(
     MlaRowsSmemT<RT, NW>& sm, QFn q_piece, const uint8_t* __restrict__ cache, int row_bytes,
     IdxFn idx_at, int W, int H, float scale_log2, int t, int head0, int split, int c_begin, int c_end,
@@ -173,16 +184,17 @@ __device__ __forceinline__ void mla_rows_split(
         load_idx(c_begin, id_cur);
         if (c_begin + 1 < c_end) load_idx(c_begin + 1, id_next);
     }
-    u32x4 qv[QP];
+    if constexpr (QS_READY) {
+        // the caller has staged q in sm.qs (mla_stage_q) behind a barrier
+        if (c_begin < c_end) load_rows(id_cur);
+    } else {
+        u32x4 qv[QP];
 #pragma unroll
-    for (int i = 0; i < QP; ++i) qv[i] = q_piece(i);
-    if (c_begin < c_end) load_rows(id_cur);
-#pragma unroll
-    for (int i = 0; i < QP; ++i) {
-        const int k = tid + NT * i;                    // 16-byte piece k: head k / 64, dims 8 (k % 64) ..
-        *reinterpret_cast<u32x4*>(&sm.qs[(k >> 6) * kRStride + 8 * (k & 63)]) = qv[i];
+        for (int i = 0; i < QP; ++i) qv[i] = q_piece(i);
+        if (c_begin < c_end) load_rows(id_cur);
+        mla_stage_q<NT>(sm.qs, qv);
+        lds_barrier();
     }
-    lds_barrier();
 
     // Q^T operand (B of S^T): head head0 + n16, reduction index
     // 64 (j/2) + 16 g4 + 8 (j%2) + e -- the bytes this lane holds of its row.

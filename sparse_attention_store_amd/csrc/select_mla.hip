@@ -48,7 +48,11 @@ __global__ __launch_bounds__(64 * NW, 1) void k_select_mla(
 #pragma unroll
                                                     for (int i = 0; i < QP; ++i)
                                                         qv[i] = mla_q_piece<NT>(q, t, H, head0, i);
-                                                });
+                                                }, [&] { mla_stage_q<NT>(sm.u.m.qs, qv); });
+    if (!g.listed) {                                // no barrier was taken: stage q now
+        mla_stage_q<NT>(sm.u.m.qs, qv);
+        lds_barrier();
+    }
     const int32_t* sel = g.listed ? sm.sel : nullptr;
     if (split == 0 && blockIdx.y == 0) emit_selection<NT>(sel, g.K, select_k, t, g.b, g.f, g.qp, g.n_vis, e, g.rb);
     // list position -> cache row, exactly as emit_selection writes it
@@ -66,7 +70,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_select_mla(
     const int nchunks = (W + CH - 1) / CH;
     const int c_begin = split * chunks_per_split;
     const int c_end = min(c_begin + chunks_per_split, nchunks);
-    mla_rows_split<1, false, NW>(sm.u.m, [&](int i) { return qv[i]; }, cache, row_bytes, idx_at, W, H, scale_log2, t,
+    mla_rows_split<1, false, NW, true>(sm.u.m, [&](int i) { return qv[i]; }, cache, row_bytes, idx_at, W, H, scale_log2, t,
                                  head0, split, c_begin, c_end, splits, part_o, part_ml, out, out_f32, lse);
 }
 

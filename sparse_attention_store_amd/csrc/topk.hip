@@ -199,7 +199,7 @@ __global__ __launch_bounds__(kBNT) void k_topk_groups(
     const int t = blockIdx.x;
     const GroupQuery g = select_from_groups<kBNT>(G, sel, scores, first_valid, q_seq, q_pos,
                                                   e.indices ? e.row_base : nullptr, stride, select_k, cand, cand_n, t,
-                                                  [] {});
+                                                  [] {}, [] {});
     emit_selection<kBNT>(g.listed ? sel : nullptr, g.K, select_k, t, g.b, g.f, g.qp, g.n_vis, e, g.rb);
 }
 
