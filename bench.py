@@ -313,10 +313,13 @@ def main():
     for j, nm in enumerate(names):
         stages[nm] = round(float(np.median([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e3, 2)
 
-    # The dominant kernel's launch duration: a burst of back-to-back launches of
-    # it alone (cycling the replicas, so its pools come from HBM) between one
-    # event pair.  An event pair around a single launch inside a step also
-    # counts that launch's dispatch latency (reported as avg_launch_us_in_step).
+    # The dominant kernel's launch duration.  A burst of back-to-back launches
+    # of it alone (cycling the replicas, so its pools come from HBM) between
+    # one event pair also counts the gaps between launches (avg_launch_us_burst);
+    # the scoring launch can record HIP events around the kernel itself
+    # (hipExtLaunchKernel), which give its own duration (avg_launch_us).  An
+    # event pair around a single launch inside a step also counts that
+    # launch's dispatch latency (avg_launch_us_in_step).
     dom_stage = "decode" if fused else "append_scores"
     dom = lambda r: dw.run(dom_stage, r)
     n_burst = 4 * R
@@ -327,7 +330,20 @@ def main():
         dom(i % R)
     b1.record(stream)
     torch.cuda.synchronize()
-    launch_us = b0.elapsed_time(b1) * 1e3 / n_burst
+    burst_us = b0.elapsed_time(b1) * 1e3 / n_burst
+    launch_us = burst_us
+    if not fused:
+        import sparse_attention_store_amd as dsa
+        kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_burst)]
+        for a, b in kev:                        # creates the events
+            a.record(stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        for i in range(n_burst):
+            dsa.time_next_scoring_launch(*kev[i])
+            dom(i % R)
+        torch.cuda.synchronize()
+        launch_us = float(np.mean([a.elapsed_time(b) for a, b in kev])) * 1e3
 
     ab = algorithmic_bytes(wl)
     kern_bytes = ab["decode_kernel"] if fused else ab["scores_kernel"]
@@ -358,6 +374,7 @@ def main():
                      "traffic": traffic_from_profile(PMC_SUMMARY_STEP if fused else PMC_SUMMARY,
                                                      STEP_SRC if fused else SCORES_SRC),
                      "algorithmic_bytes_per_launch": kern_bytes, "avg_launch_us": round(launch_us, 2),
+                     "avg_launch_us_burst": round(burst_us, 2),
                      "avg_launch_us_in_step": round(scores_us, 2)},
         "path": args.path,
         "stages_us_median": stages,

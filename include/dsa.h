@@ -257,6 +257,16 @@ int dsa_append_scores_groups(const dsa_dims* dims, int dtype, const void* latent
                              int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos, int32_t T,
                              int32_t score_stride, float* scores, void* workspace, size_t workspace_bytes,
                              void* stream);
+/*
+ * time_next_scoring_launch -- measurement hook.  The next scoring launch that
+ * dsa_append_scores_groups makes on the calling thread records start_event
+ * when the kernel starts and stop_event when it ends (hipExtLaunchKernel),
+ * so that hipEventElapsedTime gives the kernel's own duration, without the
+ * gap between launches.  One-shot; both NULL cancels.  The events are HIP
+ * events created beforehand on the launch's device; the library does not
+ * own them.  Returns DSA_ERR_NULL if exactly one of them is NULL.
+ */
+int dsa_time_next_scoring_launch(void* start_event, void* stop_event);
 int dsa_index_scores_select(const dsa_dims* dims, const uint16_t* q_idx, const float* w,
                             const uint16_t* pools, const dsa_seqs* seqs, int32_t num_seqs,
                             const int32_t* q_seq, const int32_t* q_pos, int32_t T,

@@ -115,6 +115,7 @@ def lib() -> ctypes.CDLL:
                                                         I32, P, P, P, SP, I32, P, P, I32, I32, P, P, SZ, P]),
             "dsa_topk_sparse_mla": (ctypes.c_int, [DP, P, I32, SP, I32, P, P, I32, P, P, P, SZ, P, ctypes.c_int, P,
                                                    I64, F, P, ctypes.c_int, P, I32, P, SZ, P]),
+            "dsa_time_next_scoring_launch": (ctypes.c_int, [P, P]),
             "dsa_decode_step_workspace_bytes": (SZ, [DP, I32, I32]),
             "dsa_decode_step": (ctypes.c_int, [DP, P, P, P, SP, I32, P, P, I32, I32, P, ctypes.c_int, P, I64, F,
                                                P, ctypes.c_int, P, P, P, P, SZ, P]),
@@ -488,6 +489,14 @@ def topk_sparse_mla(dims: Dims, scores: torch.Tensor, seqs: Seqs, q_seq: torch.T
         select_workspace.data_ptr(), select_workspace.numel() * select_workspace.element_size(),
         q.data_ptr(), _dt(q), cache.data_ptr(), cache.shape[0], float(scale), out.data_ptr(), _dt(out),
         _ptr(lse), int(num_splits), _ptr(mla_workspace), ws_bytes, _stream(stream))
+
+
+def time_next_scoring_launch(start_event, stop_event):
+    """The next append_scores_groups scoring launch on this thread records the two
+    (already created) torch.cuda.Events around the kernel itself."""
+    st = lib().dsa_time_next_scoring_launch(start_event.cuda_event, stop_event.cuda_event)
+    if st:
+        raise DsaError("dsa_time_next_scoring_launch", st, "")
 
 
 def decode_step_workspace_bytes(dims: Dims, T: int, score_stride: int) -> int:

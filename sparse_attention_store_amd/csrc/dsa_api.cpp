@@ -313,6 +313,13 @@ int dsa_append_scores_groups(const dsa_dims* dims, int dtype, const void* latent
         pool_end, max_pools, pools, q_idx, w, q_seq, q_pos, T, score_stride, scores, workspace, s));
 }
 
+int dsa_time_next_scoring_launch(void* start_event, void* stop_event) {
+    if ((start_event == nullptr) != (stop_event == nullptr)) return DSA_ERR_NULL;
+    dsa_host::time_next_scoring_launch(reinterpret_cast<hipEvent_t>(start_event),
+                                       reinterpret_cast<hipEvent_t>(stop_event));
+    return DSA_OK;
+}
+
 int dsa_topk_select_groups(const dsa_dims* dims, const float* scores, int32_t score_stride, const dsa_seqs* seqs,
                            int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos, int32_t T,
                            int32_t* pool_ids, int32_t* indices, void* workspace, size_t workspace_bytes,

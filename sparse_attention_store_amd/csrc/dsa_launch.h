@@ -38,6 +38,9 @@ hipError_t launch_scores_with_groups(const dsa_dims& d, const uint16_t* q_idx, c
                                      const int32_t* q_pos, int32_t T, int32_t stride, float* scores, void* ws,
                                      hipStream_t s);
 bool append_scores_fused(const dsa_dims& d, int dtype);
+// Events the next scoring launch of launch_append_scores_groups on this
+// thread records around the kernel (one-shot).
+void time_next_scoring_launch(hipEvent_t start, hipEvent_t stop);
 hipError_t launch_append_scores_groups(const dsa_dims& d, const void* latent, int64_t n, int64_t ld,
                                        const int64_t* slots, int8_t* cache, const void* k, const void* gate,
                                        const float* ln_w, const float* ln_b, const dsa_seqs& seqs, int32_t num_seqs,

@@ -12,6 +12,8 @@
 // Decode launches one query per workgroup (pure pool streaming, HBM bound);
 // prefill launches many queries per workgroup so the resident pools are
 // reused (MFMA bound).
+#include <hip/hip_ext.h>
+
 #include "dsa_common.h"
 #include "dsa_launch.h"
 #include "scores_core.h"
@@ -478,6 +480,15 @@ hipError_t launch_scores_with_groups(const dsa_dims& d, const uint16_t* q_idx, c
     return hipGetLastError();
 }
 
+namespace {
+thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+}
+
+void time_next_scoring_launch(hipEvent_t start, hipEvent_t stop) {
+    t_ev_start = start;
+    t_ev_stop = stop;
+}
+
 bool append_scores_fused(const dsa_dims& d, int dtype) {
     return dtype == DSA_BF16 && d.idx_dim == dsa::kDI &&
            (d.latent_dim == 64 || d.latent_dim == 128 || d.latent_dim == 256 || d.latent_dim == 512);
@@ -517,10 +528,12 @@ hipError_t launch_append_scores_groups(const dsa_dims& d, const void* latent, in
     ap.tasks = (int)tasks;
     const int64_t want = cdiv(cdiv(stride, dsa::kGroupPools), 4) * (int64_t)T + tasks;
     const unsigned grid = (unsigned)std::min<int64_t>(std::max<int64_t>(want, 1), 4 * (int64_t)device_info().cu_count);
+    const hipEvent_t ev0 = t_ev_start, ev1 = t_ev_stop;
+    t_ev_start = t_ev_stop = nullptr;
 #define DSA_APPEND_SCORES(D)                                                                                        \
-    hipLaunchKernelGGL((dsa::k_scores_groups<true, D>), dim3(grid), dim3(256), 0, s, q_idx, w, pools,             \
-                       seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, num_seqs, stride, scores,             \
-                       d.index_topk / d.kpool, cand, cand_n, ap)
+    hipExtLaunchKernelGGL((dsa::k_scores_groups<true, D>), dim3(grid), dim3(256), 0, s, ev0, ev1, 0, q_idx, w,    \
+                          pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, num_seqs, stride, scores,   \
+                          d.index_topk / d.kpool, cand, cand_n, ap)
     switch (d.latent_dim) {
         case 512: DSA_APPEND_SCORES(512); break;
         case 256: DSA_APPEND_SCORES(256); break;

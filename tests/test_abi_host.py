@@ -225,3 +225,11 @@ def test_binding_refuses_host_tensors(dsa):
     with pytest.raises((TypeError, ValueError)):
         dsa.store_int8(d, torch.zeros(2, 512, dtype=torch.bfloat16), torch.zeros(2, dtype=torch.int64),
                        torch.zeros(2, 528, dtype=torch.int8))
+
+
+def test_time_next_scoring_launch_argument_checks(dsa):
+    """The timing hook takes both events or neither (no GPU call is made)."""
+    L = dsa.lib()
+    assert L.dsa_time_next_scoring_launch(FAKE, None) == -1
+    assert L.dsa_time_next_scoring_launch(None, FAKE) == -1
+    assert L.dsa_time_next_scoring_launch(None, None) == 0

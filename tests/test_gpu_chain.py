@@ -267,3 +267,25 @@ def test_topk_sparse_mla_matches_separate_calls(harness, name, splits, case):
         assert np.array_equal(outs[0][0][0].numpy(), np.arange(wl.dims.select_k))
     for what, a, b in zip(("pool_ids", "indices", "out", "lse"), outs[0], outs[1]):
         assert torch.equal(a, b), what
+
+
+def test_timed_scoring_launch_gives_the_same_bits(harness):
+    """A scoring launch that records its kernel events (the bench's timing
+    hook) makes the bits of an ordinary one, and the events bracket it."""
+    import sparse_attention_store_amd as dsa
+    wl = syn.get("mini_decode")
+    say("timed scoring launch mini_decode")
+    dw = harness.DeviceWorkload(wl)
+    dw.step_append_scores()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (dw.scores, dw._ws_ss())]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    b.record()
+    torch.cuda.synchronize()
+    dw.scores.fill_(float("nan"))
+    dsa.time_next_scoring_launch(a, b)
+    dw.step_append_scores()
+    torch.cuda.synchronize()
+    assert a.elapsed_time(b) > 0.0
+    assert torch.equal(ref[0], dw.scores) and torch.equal(ref[1], dw._ws_ss())
