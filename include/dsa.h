@@ -14,7 +14,9 @@
  *    current for the calling thread; "host" pointers are read before the call
  *    returns.  The caller owns every buffer, including workspaces; the library
  *    allocates nothing and keeps no per-call state (it caches device
- *    properties only) and is safe to call from several host threads.
+ *    properties only; dsa_time_next_scoring_launch keeps two event handles
+ *    per thread until the next scoring launch) and is safe to call from
+ *    several host threads.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream), never synchronises, and returns a dsa_status.  Only host-visible
  *    arguments are validated; on any error nothing is launched.  Device data
