@@ -233,3 +233,36 @@ def test_time_next_scoring_launch_argument_checks(dsa):
     assert L.dsa_time_next_scoring_launch(FAKE, None) == -1
     assert L.dsa_time_next_scoring_launch(None, FAKE) == -1
     assert L.dsa_time_next_scoring_launch(None, None) == 0
+
+
+def test_topk_sparse_mla_argument_checks(dsa):
+    """dsa_topk_sparse_mla checks what dsa_topk_select_groups and dsa_sparse_mla
+    check (host-visible arguments only; every call here fails before a launch,
+    except T = 0, which has nothing to do)."""
+    L = dsa.lib()
+    d = prod(dsa)
+    bd = ctypes.byref(d)
+    S = seqs(dsa)
+    ws_need = L.dsa_index_scores_select_workspace_bytes(bd, 8, 65536)
+    mla_need = L.dsa_sparse_mla_workspace_bytes(bd, 8, 17)
+    assert ws_need > 0 and mla_need > 0
+
+    def call(dims=bd, stride=65536, sq=ctypes.byref(S), T=8, idx=FAKE, ws=FAKE, ws_bytes=ws_need, q=FAKE,
+             q_dt=1, out=FAKE, out_dt=0, splits=17, mws=FAKE, mws_bytes=mla_need, scores=FAKE):
+        return L.dsa_topk_sparse_mla(dims, scores, stride, sq, 8, FAKE, FAKE, T, FAKE, idx, ws, ws_bytes, q, q_dt,
+                                     FAKE, 1 << 20, 0.044, out, out_dt, FAKE, splits, mws, mws_bytes, None)
+    assert call(dims=None) == E_NULL
+    assert call(sq=None) == E_NULL
+    assert call(T=65) == E_UNSUP                      # group lists: at most 64 queries
+    assert call(stride=0) == E_UNSUP                  # no lists without pools
+    assert call(ws_bytes=ws_need - 1) == E_WS
+    assert call(idx=None) == E_NULL
+    assert call(scores=None) == E_NULL
+    assert call(q_dt=7) == E_DTYPE
+    assert call(out_dt=7) == E_DTYPE
+    assert call(splits=-1) == E_SIZE
+    assert call(q=None) == E_NULL
+    assert call(q=MISALIGNED) == E_ALIGN
+    assert call(mws=None) == E_WS
+    assert call(mws_bytes=mla_need - 1) == E_WS
+    assert call(T=0, idx=None, ws=None, ws_bytes=0) == OK
