@@ -378,8 +378,13 @@ __global__ __launch_bounds__(256, 4) void k_scores_groups(
                                           (int64_t)(a - ap.pool_tasks) * 4 + wave);
         }
     }
-    // Pools past each query's last visible group.
-    const int gw = blockIdx.x * 4 + wave, W = gridDim.x * 4;
+    // Pools past each query's last visible group: written by the workgroups
+    // that had neither a tile nor a task when there are such, so that the
+    // waves finishing the last tiles have nothing more to do.
+    const int busy = total + (AD != 0 ? ap.tasks : 0);
+    const int first = busy < (int)gridDim.x ? busy : 0;
+    if ((int)blockIdx.x < first) return;
+    const int gw = ((int)blockIdx.x - first) * 4 + wave, W = ((int)gridDim.x - first) * 4;
     for (int t = 0; t < T; ++t) {
         const int from = geom[t].ng * kGroupPools;
         float* out = scores + (int64_t)t * stride;
