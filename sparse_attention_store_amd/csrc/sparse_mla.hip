@@ -331,9 +331,7 @@ constexpr int kPre = 24;
 __global__ __launch_bounds__(128) void k_mla_combine(
     const float* __restrict__ part_o, const MlaPartial* __restrict__ part_ml, int splits, int H,
     void* __restrict__ out, int out_f32, float* __restrict__ lse) {
-    __shared__ float wgt[kMaxSplits];
-    __shared__ float s_M, s_L;
-    const int h = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+    const int h = blockIdx.x, t = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
     const float* base = part_o + ((int64_t)t * splits * H + h) * kD + tid * 4;
     const int64_t sstride = (int64_t)H * kD;
     // The first kPre splits' pieces through one bounded buffer descriptor:
@@ -349,32 +347,28 @@ __global__ __launch_bounds__(128) void k_mla_combine(
             pre[u] = f32x4{__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3])};
         }
     }
-    if (tid < 64) {
-        MlaPartial p = {-INFINITY, 0.f};
-        if (tid < splits) p = part_ml[((int64_t)t * splits + tid) * H + h];
-        const bool live = p.l > 0.f;
-        float M = live ? p.m : -INFINITY;
+    // Each wave derives the split weights itself (lane s: split s, at most 64
+    // splits), so the two waves need no exchange and no barrier.
+    MlaPartial p = {-INFINITY, 0.f};
+    if (lane < splits) p = part_ml[((int64_t)t * splits + lane) * H + h];
+    const bool live = p.l > 0.f;
+    float M = live ? p.m : -INFINITY;
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-        const float w = live ? exp2f(p.m - M) : 0.f;
-        float L = p.l * w;
-        // Sum in split order (a fixed tree over lanes 0..63) for determinism.
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    const float w = live ? exp2f(p.m - M) : 0.f;
+    float L = p.l * w;
+    // Sum in split order (a fixed tree over lanes 0..63) for determinism.
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
-        wgt[tid] = w;
-        if (tid == 0) { s_M = M; s_L = L; }
-    }
-    lds_barrier();
-    const float L = s_L;
+    for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < kPre; ++u) {
-        const float wu = u < splits ? wgt[u] : 0.f;
+        const float wu = u < splits ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u)) : 0.f;
         const f32x4 c = pre[u] * wu;
         if (wu > 0.f) acc += c;
     }
     for (int s = kPre; s < splits; ++s) {
-        const float ws = wgt[s];
+        const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s));
         const f32x4 v = *reinterpret_cast<const f32x4*>(base + s * sstride);
         if (ws > 0.f) acc += v * ws;
     }
@@ -389,7 +383,7 @@ __global__ __launch_bounds__(128) void k_mla_combine(
         pk[1] = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
         *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + orow) = pk;
     }
-    if (lse && tid == 0) lse[(int64_t)t * H + h] = L > 0.f ? (s_M + log2f(L)) * kLn2 : -INFINITY;
+    if (lse && tid == 0) lse[(int64_t)t * H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 // fp32 vector kernel for other shapes (tiny geometry, fp32 q): one wave per
