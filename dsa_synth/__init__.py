@@ -369,6 +369,21 @@ def mini_decode(seed: int = 11) -> Workload:
     return _mk("mini_decode", seed, production_dims(16), fv, sl, 4100, 1025, qs, qp)
 
 
+def mini_decode_64(seed: int = 14) -> Workload:
+    """The most queries a decode launch takes: 64, over 8 ragged sequences
+    (8 queries each at seeded positions, the last position among them)."""
+    fv = [0, 1, 3, 2, 0, 3, 1, 2]
+    v = [4096, 3001, 2050, 517, 3900, 2100, 800, 2600]
+    sl = [a + b for a, b in zip(fv, v)]
+    qs, qp = [], []
+    g = _rng(seed, "queries", 0, 0)
+    for b in range(8):
+        qs.append(b); qp.append(sl[b] - 1)
+        for x in g.integers(fv[b], sl[b], size=7):
+            qs.append(b); qp.append(int(x))
+    return _mk("mini_decode_64", seed, production_dims(16), fv, sl, 4100, 1025, qs, qp)
+
+
 def mini_prefill(seed: int = 12) -> Workload:
     """Prefill chunk of 200 queries on a 3,000-token context, 64 MLA heads."""
     n_ctx, n_q = 3000, 200
@@ -392,7 +407,8 @@ WORKLOADS = {
     "decode_32k": decode_32k, "decode_262k_b8": decode_262k_b8,
     "decode_262k_b8_full": decode_262k_b8_full,
     "prefill_4k_on_131k": prefill_4k_on_131k, "decode_1m_b4": decode_1m_b4,
-    "mini_decode": mini_decode, "mini_prefill": mini_prefill, "mini_heavy": mini_heavy,
+    "mini_decode": mini_decode, "mini_decode_64": mini_decode_64, "mini_prefill": mini_prefill,
+    "mini_heavy": mini_heavy,
 }
 
 

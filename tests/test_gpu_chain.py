@@ -94,7 +94,7 @@ def _check_chain(dw, queries, pool_sample=64, allow_swaps_frac=0.05):
     return swapped
 
 
-@pytest.mark.parametrize("name", ["tiny", "tiny_seven", "tiny_padded_six", "tiny_batch", "mini_decode",
+@pytest.mark.parametrize("name", ["tiny", "tiny_seven", "tiny_padded_six", "tiny_batch", "mini_decode", "mini_decode_64",
                                   "mini_prefill", "mini_heavy"])
 def test_chain_reduced(harness, name):
     wl = syn.get(name)
@@ -177,7 +177,7 @@ def test_prepared_calls_match_the_calls(harness):
             assert torch.equal(a, b), (name, r)
 
 
-@pytest.mark.parametrize("name,span", [("mini_decode", 3), ("mini_decode", 70), ("mini_heavy", 5),
+@pytest.mark.parametrize("name,span", [("mini_decode", 3), ("mini_decode", 70), ("mini_decode_64", 5), ("mini_heavy", 5),
                                        ("mini_heavy", 130), ("decode_32k", 4)])
 def test_append_scores_groups_matches_separate_calls(harness, name, span):
     """append_scores_groups gives the bytes of append_tokens then
@@ -234,7 +234,8 @@ def test_append_scores_groups_matches_separate_calls(harness, name, span):
 @pytest.mark.parametrize("name,splits,case", [("mini_decode", 17, "lists"), ("mini_decode", 0, "lists"),
                                               ("mini_decode", 1, "lists"), ("mini_heavy", 17, "lists"),
                                               ("mini_heavy", 3, "lists"), ("decode_32k", 17, "lists"),
-                                              ("decode_32k", 17, "equal_scores"), ("mini_decode", 17, "fp32_q")])
+                                              ("decode_32k", 17, "equal_scores"), ("mini_decode", 17, "fp32_q"),
+                                              ("mini_decode_64", 17, "lists")])
 def test_topk_sparse_mla_matches_separate_calls(harness, name, splits, case):
     """topk_sparse_mla gives the bits of topk_select_groups then sparse_mla
     over its list: pool ids, index list, out and lse.  equal_scores (q_idx =
