@@ -18,6 +18,7 @@ __all__ = [
     "store_int8", "dequantize_rows", "layer_norm", "slot_softmax", "pool_states",
     "store_bf16", "visible", "visible_pool_count", "index_scores", "topk_pools", "expand_selection",
     "topk_to_mask", "sparse_mla", "masked_attention", "attention_unquantized",
+    "quantize_pools", "dequantize_pools", "index_scores_int8", "int8_accuracy",
 ]
 
 
@@ -69,7 +70,11 @@ def store_int8(latent: np.ndarray, slots: np.ndarray, cache: np.ndarray) -> None
 
 
 def dequantize_rows(rows: np.ndarray, latent_dim: int) -> np.ndarray:
-    """float64 values int8_code * scale of each stored row (uint8 [n, row_bytes])."""
+    """float64 values int8_code * scale of each stored row (uint8 [n, row_bytes]).
+
+    Pinned against rows assembled byte by byte (two's-complement codes, the
+    little-endian scale at bytes D .. D+4, pad bytes ignored) and against the
+    s/2 round-trip bound of stored rows."""
     rows = np.ascontiguousarray(rows, dtype=np.uint8)
     codes = rows[:, :latent_dim].view(np.int8).astype(np.float64)
     scales = rows[:, latent_dim:latent_dim + 4].copy().view("<f4").astype(np.float64)
@@ -263,3 +268,43 @@ def masked_attention(q: np.ndarray, keys: np.ndarray, mask: np.ndarray, scale: f
 def attention_unquantized(q: np.ndarray, latent_rows: np.ndarray, scale: float) -> np.ndarray:
     """Attention over the source (unquantised) latents, for the INT8 accuracy report."""
     return masked_attention(q, latent_rows, np.ones(latent_rows.shape[0], dtype=bool), scale)[0]
+
+
+# ---------------------------------------------------------------------------
+# O2q / O3q  INT8 pool cache -- [Flash] What is quantized (the indexer state
+# cache row): the sibling port keeps its indexer cache as INT8 codes with one
+# FP32 scale per row.  Readings: the quantiser is the one of the latent rows
+# (O1: amax floored at 1e-4, scale = amax / 127 in IEEE fp32, round half to
+# even, symmetric +-127), applied to each pool's fp32 state (the state
+# precision the page names), with no bf16 step in between and no Hadamard
+# rotation: the query stays in bf16 and is not quantised, so an orthonormal
+# rotation of both operands would leave q . pool unchanged (reading R20).
+# Scores are O3 on the dequantised pools.
+# ---------------------------------------------------------------------------
+
+def quantize_pools(pools: np.ndarray):
+    """Pool states (any float dtype) -> (codes int8 [P, Di], scales float32 [P]):
+    the fp32 state, quantised per row by the O1 formula."""
+    return quantize_rows(np.asarray(pools, dtype=np.float64).astype(np.float32))
+
+
+def dequantize_pools(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """float64 code * scale per pool row."""
+    return np.asarray(codes, np.float64) * np.asarray(scales, np.float64)[:, None]
+
+
+def index_scores_int8(q_idx: np.ndarray, w: np.ndarray, codes: np.ndarray, scales: np.ndarray, n_vis: int,
+                      stride: int | None = None) -> np.ndarray:
+    """O3 over INT8 pools: sum_h w[h] * max(0, q_idx[h] . (scale_p * code_p)) for p < n_vis, -inf after."""
+    n = min(int(n_vis), codes.shape[0])
+    return index_scores(q_idx, w, dequantize_pools(codes[:n], scales[:n]), n_vis, stride)
+
+
+def int8_accuracy(o_int8: np.ndarray, o_ref: np.ndarray):
+    """NMSE and cosine similarity of an attention output against a reference
+    output (the accuracy figures [Kernels] Measurements reports for INT8 MLA
+    against BF16 latents): NMSE = |o - r|^2 / |r|^2, cosine = o.r / (|o| |r|),
+    each over one query's heads and channels."""
+    o = np.asarray(o_int8, np.float64).ravel()
+    r = np.asarray(o_ref, np.float64).ravel()
+    return float(np.sum((o - r) ** 2) / np.sum(r * r)), float(o @ r / (np.linalg.norm(o) * np.linalg.norm(r)))

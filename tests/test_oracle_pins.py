@@ -87,6 +87,66 @@ def test_store_int8_skips_negative_slots():
 
 # ------------------------------------------------------------------ O2 pools
 
+# ------------------------------------------------------------------ O1 read back: dequantize_rows
+
+def _row_bytes_by_hand(codes, scale, row_bytes, pad_byte=0):
+    """One stored row assembled with struct, independently of pack_rows: the
+    codes as two's-complement bytes, the scale as a little-endian IEEE float,
+    then pad bytes ([GLM-5.3 Kernels, Included]: codes, one fp32 scale, padding)."""
+    import struct
+    body = struct.pack("<%db" % len(codes), *codes) + struct.pack("<f", scale)
+    return np.frombuffer(body + bytes([pad_byte]) * (row_bytes - len(body)), dtype=np.uint8)
+
+
+def _dequant_pins_hold(fn):
+    """The facts a correct read-back of the row layout must reproduce; returns
+    the first one that fails (None when all hold)."""
+    # (a) hand-built rows: negative codes read as negative, the scale read from
+    # bytes D .. D+4 (pad bytes are not the scale), exact products
+    codes = [-127, -1, 0, 1, 2, 127, -2, -64] + [5] * 56
+    rows = np.stack([_row_bytes_by_hand(codes, 0.5, 80, pad_byte=0x3F),
+                     _row_bytes_by_hand(codes[::-1], 2.0 ** -7, 80, pad_byte=0x41)])
+    got = fn(rows, 64)
+    want = np.stack([np.array(codes, np.float64) * 0.5, np.array(codes[::-1], np.float64) * 2.0 ** -7])
+    if got.shape != want.shape or not np.array_equal(got, want):
+        return "hand-built rows"
+    # (b) round trip through the stored bytes: within s/2 of the source, signs kept
+    g = np.random.default_rng(5)
+    x = (g.standard_t(3, size=(64, 512)) * g.uniform(1e-3, 40, size=(64, 1))).astype(np.float32)
+    cache = np.zeros((64, 528), dtype=np.uint8)
+    O.store_int8(x, np.arange(64), cache)
+    deq = fn(cache, 512)
+    s = np.abs(x).max(axis=1).astype(np.float64) / 127.0
+    if not np.all(np.abs(deq - x) <= s[:, None] / 2 * (1 + 2.0 ** -15)):
+        return "round trip error above s/2"
+    if not np.all((np.sign(deq) == np.sign(x)) | (deq == 0)):
+        return "sign flipped"
+    return None
+
+
+def test_dequantize_rows_reads_the_stored_layout():
+    assert _dequant_pins_hold(O.dequantize_rows) is None
+
+
+def test_dequantize_pins_reject_plausible_mistakes():
+    """Mistakes planted in copies of the read-back (on the CPU): codes read as
+    uint8, the scale taken from the pad bytes, the scale read big-endian."""
+    def as_uint8(rows, d):
+        rows = np.ascontiguousarray(rows, dtype=np.uint8)
+        return rows[:, :d].astype(np.float64) * rows[:, d:d + 4].copy().view("<f4").astype(np.float64)
+
+    def scale_from_pad(rows, d):
+        rows = np.ascontiguousarray(rows, dtype=np.uint8)
+        return rows[:, :d].view(np.int8).astype(np.float64) * rows[:, d + 4:d + 8].copy().view("<f4").astype(np.float64)
+
+    def big_endian(rows, d):
+        rows = np.ascontiguousarray(rows, dtype=np.uint8)
+        return rows[:, :d].view(np.int8).astype(np.float64) * rows[:, d:d + 4].copy().view(">f4").astype(np.float64)
+
+    for bad in (as_uint8, scale_from_pad, big_endian):
+        assert _dequant_pins_hold(bad) is not None, bad.__name__
+
+
 def _torch_pools(k_rows, gate_rows, w, b, eps):
     """Textbook reference for one pool: torch layer_norm, softmax over the 4 slots."""
     k = torch.tensor(k_rows, dtype=torch.float64)
@@ -380,3 +440,109 @@ def test_generator_blocks_are_reproducible_and_bf16_exact():
     assert np.array_equal(syn.bf16_round(a), a)
     k, _ = syn.gen_kgate(wl, 2, 0, 8)
     assert np.all(np.abs(k[:3]) == syn.POISON) and not np.any(np.abs(k[3:]) == syn.POISON)
+
+
+# ------------------------------------------------------------------ O2q/O3q INT8 pool cache
+
+def test_pool_int8_worked_row_and_score():
+    vals, codes, score = [], [], None
+    for ln in _golden_lines("pool_int8_worked.txt"):
+        parts = ln.split()
+        if parts[0] == "score":
+            score = float(parts[1])
+            continue
+        vals.append(float(parts[1]))
+        codes.append(int(parts[2]))
+    pool = np.array([vals], dtype=np.float64)
+    c, s = O.quantize_pools(pool)
+    assert np.array_equal(c[0], np.array(codes, dtype=np.int8))
+    assert s[0] == np.float32(1.0)
+    q = np.zeros((2, 8))
+    q[0, 0], q[0, 1] = 1.0, -1.0
+    q[1, 0], q[1, 1] = 1.0, 2.0
+    got = O.index_scores_int8(q, np.array([1.0, 0.5]), c, s, 1)
+    assert got[0] == score
+
+
+def test_int8_scores_equal_exact_scores_when_pools_are_on_the_grid():
+    """Pools whose values are integers times 2^-3 with amax 127 * 2^-3 quantise
+    without error (scale 2^-3 exactly), so the INT8 scores are O3's."""
+    g = np.random.default_rng(21)
+    codes = g.integers(-127, 128, size=(300, 128))
+    codes[:, 5] = 127
+    pools = codes * 2.0 ** -3
+    c, s = O.quantize_pools(pools)
+    assert np.all(s == np.float32(2.0 ** -3)) and np.array_equal(c.astype(np.int64), codes)
+    qi = g.standard_normal((32, 128))
+    w = g.random(32)
+    assert np.array_equal(O.index_scores_int8(qi, w, c, s, 300, 320), O.index_scores(qi, w, pools, 300, 320))
+
+
+def test_int8_scores_are_homogeneous_in_the_pool_scale():
+    """Scaling a pool by a power of two leaves its codes unchanged and scales
+    its scale, so its INT8 score scales by exactly that power of two."""
+    g = np.random.default_rng(22)
+    pools = g.standard_normal((64, 128)) * 3
+    qi = g.standard_normal((32, 128))
+    w = g.random(32)
+    c1, s1 = O.quantize_pools(pools)
+    c2, s2 = O.quantize_pools(pools * 8.0)
+    assert np.array_equal(c1, c2) and np.array_equal(s2, s1 * np.float32(8.0))
+    a = O.index_scores_int8(qi, w, c1, s1, 64)
+    b = O.index_scores_int8(qi, w, c2, s2, 64)
+    assert np.allclose(b, 8.0 * a, rtol=1e-14, atol=0)
+
+
+def test_int8_pool_round_trip_within_half_a_step():
+    g = np.random.default_rng(23)
+    pools = g.standard_t(3, size=(500, 128)) * g.uniform(1e-3, 30, size=(500, 1))
+    c, s = O.quantize_pools(pools)
+    x32 = pools.astype(np.float32).astype(np.float64)
+    err = np.abs(O.dequantize_pools(c, s) - x32)
+    assert np.all(err <= s[:, None].astype(np.float64) / 2 * (1 + 2.0 ** -15))
+    assert np.all(np.abs(c[np.arange(500), np.argmax(np.abs(pools), axis=1)].astype(int)) == 127)
+
+
+def test_accuracy_figures_closed_forms():
+    g = np.random.default_rng(24)
+    r = g.standard_normal((4, 64))
+    assert O.int8_accuracy(r, r) == (0.0, pytest.approx(1.0, abs=1e-15))
+    nmse, cos = O.int8_accuracy(2 * r, r)
+    assert nmse == pytest.approx(1.0, rel=1e-12) and cos == pytest.approx(1.0, abs=1e-12)
+    a = np.zeros(8); a[0] = 1
+    b = np.zeros(8); b[1] = 1
+    assert O.int8_accuracy(a, b) == (pytest.approx(2.0), pytest.approx(0.0))
+
+
+def test_int8_mla_accuracy_against_bf16_latents():
+    """The accuracy figures of INT8 MLA against attention over the source bf16
+    latents on the same list (reported, not gated): decode_32k's query on its
+    oracle list, and the heavy-tailed mini_heavy queries.  The loose bounds
+    below only catch a broken quantiser."""
+    import sys
+    sys.path.insert(0, os.path.dirname(__file__))
+    from oracle_chain import OracleWorkload
+    rep = []
+    for name in ("decode_32k", "mini_heavy"):
+        wl = syn.get(name)
+        ow = OracleWorkload(wl)
+        for t in range(wl.T):
+            r = ow.query(t)
+            b = int(wl.q_seq[t])
+            valid = r["indices"][r["indices"] >= 0] - int(wl.row_base[b])
+            if valid.size == 0:
+                continue
+            blk = syn.ROW_BLOCK
+            lat = np.stack([ow._latent_block(b, int(x) // blk)[int(x) % blk] for x in valid])
+            q = syn.gen_q(wl, t, t + 1)[0]
+            o_ref = O.attention_unquantized(q, lat, wl.scale)
+            nmse, cos = O.int8_accuracy(r["out"], o_ref)
+            rep.append((name, t, nmse, cos))
+    for name, t, nmse, cos in rep:
+        print(f"int8 MLA vs bf16 latents: {name} query {t}: NMSE {nmse:.3e}, cosine {cos:.7f}")
+    # normal latents sit near the figures the pages report (NMSE ~5e-5, cosine
+    # ~0.99997); Student-t(3) rows lose more to their per-row scale
+    normal = [x for x in rep if x[0] == "decode_32k"]
+    heavy = [x for x in rep if x[0] == "mini_heavy"]
+    assert max(x[2] for x in normal) < 2e-4 and min(x[3] for x in normal) > 0.9999
+    assert max(x[2] for x in heavy) < 5e-2 and min(x[3] for x in heavy) > 0.98
