@@ -1,13 +1,18 @@
-"""Decode-step throughput of the DSA path on one MI355X.
+"""Throughput of the DSA path on one MI355X.
 
-One step = the whole path for one batch: store the B new tokens' INT8 rows,
+One step = the whole path for one batch: store the new tokens' INT8 rows,
 build the pools they complete, score every visible pool, select the top-k,
-expand to index lists, and run sparse MLA -- for B = 8 ragged sequences at up
-to 262,144 tokens of context, 16 MLA heads.  Inputs are seeded synthetic data
-resident in HBM; steps rotate over R replicas of the caches so the working
-set exceeds the 256 MB Infinity Cache several times over.
+expand to index lists, and run sparse MLA.  The default workload is the
+decode batch the metric is quoted on: B = 8 ragged sequences at up to
+262,144 tokens of context, 16 MLA heads.  --workload picks another
+configuration: decode_32k (B = 1), decode_1m_b4 (B = 4 at 1,048,576
+positions, 64 heads) or prefill_4k_on_131k (4,096 causal queries on a
+131,072-token context, 64 heads, scored 512 queries at a time).  Inputs are
+seeded synthetic data resident in HBM; decode steps rotate over R replicas of
+the caches so the working set exceeds the 256 MB Infinity Cache several
+times over.
 
-Prints one JSON line (metric, value, ... , roofline, cpu_baseline).
+Prints one JSON line (metric, value, ..., roofline, cpu_baseline).
 """
 from __future__ import annotations
 
@@ -23,15 +28,30 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "decode tok-steps/s (indexer+topk+sparse MLA) @262k ctx B=8; % HBM peak"
+METRICS = {
+    "decode_262k_b8": METRIC,
+    "decode_262k_b8_full": "decode tok-steps/s (indexer+topk+sparse MLA) @262k ctx B=8, all sequences full; % HBM peak",
+    "decode_32k": "decode tok-steps/s (indexer+topk+sparse MLA) @32k ctx B=1; % HBM peak",
+    "decode_1m_b4": "decode tok-steps/s (indexer+topk+sparse MLA) @1M ctx B=4, 64 heads; % HBM peak",
+    "prefill_4k_on_131k": "prefill tokens/s (indexer+topk+sparse MLA), 4096 queries on 131k ctx, 64 heads; % MFMA peak",
+}
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 WORKLOAD = "decode_262k_b8"
 _CSRC = os.path.join(ROOT, "sparse_attention_store_amd", "csrc")
 SCORES_SRC = [os.path.join(_CSRC, f) for f in ("index_scores.hip", "scores_core.h", "topk_core.h", "new_tokens.h", "dsa_common.h")]
-STEP_SRC = [os.path.join(_CSRC, f) for f in ("decode_step.hip", "mla_core.h", "scores_core.h", "topk_core.h",
-                                             "dsa_common.h")]
+# the sources each profiled kernel is built from (a counter summary names their hash)
+KERNEL_SRC = {
+    "k_scores_groups": SCORES_SRC,
+    "k_scores_mfma": SCORES_SRC,
+    "k_select_mla": [os.path.join(_CSRC, f) for f in ("select_mla.hip", "group_select.h", "mla_core.h",
+                                                      "topk_core.h", "dsa_common.h")],
+    "k_mla_mfma": [os.path.join(_CSRC, f) for f in ("sparse_mla.hip", "mla_core.h", "dsa_common.h")],
+    "k_mla_combine": [os.path.join(_CSRC, f) for f in ("sparse_mla.hip", "mla_core.h", "dsa_common.h")],
+    "k_decode_step": [os.path.join(_CSRC, f) for f in ("decode_step.hip", "mla_core.h", "scores_core.h",
+                                                       "topk_core.h", "dsa_common.h")],
+}
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "index_scores_decode_262k_b8_traffic.md")
-PMC_SUMMARY_STEP = os.path.join(ROOT, "profiles", "decode_step_decode_262k_b8_traffic.md")
-EV_EVERY = 8                    # timed steps between two event-bracketed kernel samples
 COPY_BYTES = 256 << 20          # calibration copy: bytes read (and written) per launch
 
 
@@ -126,7 +146,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, kernel: str) -> str:
     f_raw, f_fac, n_f = vals["FETCH_SIZE"]
     w_raw, w_fac, n_w = vals["WRITE_SIZE"]
     total = f_raw * f_fac + w_raw * w_fac
-    h = _source_hash(STEP_SRC if "decode_step" in kernel else SCORES_SRC)
+    h = _source_hash(next((v for k, v in KERNEL_SRC.items() if k in kernel), SCORES_SRC))
     return "\n".join([
         f"- kernel: {kernel}",
         f"- dispatches: {n_f} (FETCH_SIZE run), {n_w} (WRITE_SIZE run)",
@@ -139,74 +159,271 @@ def summarize_pmc(fetch_dir: str, write_dir: str, kernel: str) -> str:
     ])
 
 
-def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
-    """The oracle's per-step chain (scores, top-k, expand, attention) for every query of
-    the workload, timed on the host cores over whole decode steps.
+def prefill_work(wl) -> dict:
+    """Algorithmic flops and bytes of one prefill step (all queries)."""
+    d = wl.dims
+    nvis = 0
+    rows = 0
+    for t in range(wl.T):
+        n_vis = wl.n_vis(t)
+        b = int(wl.q_seq[t])
+        f = int(wl.first_valid[b])
+        qp = int(wl.q_pos[t])
+        nvis += n_vis
+        tail = (qp - f + 1) - d.kpool * n_vis if qp >= f else 0
+        rows += d.kpool * min(d.select_k, n_vis) + tail
+    score_flops = 2 * d.idx_heads * d.idx_dim * nvis
+    attn_flops = 4 * d.mla_heads * d.latent_dim * rows
+    uniq_rows = int(sum(int(wl.seq_len[b]) - int(wl.first_valid[b]) for b in range(wl.B)))
+    bytes_ = (wl.T * (d.idx_heads * d.idx_dim * 2 + d.idx_heads * 4) + wl.total_pools * 256
+              + wl.T * 4 * d.mla_heads * d.latent_dim + wl.T * 4 * d.out_width + uniq_rows * d.row_bytes)
+    return {"score_flops": score_flops, "attn_flops": attn_flops, "sum_n_vis": nvis, "rows": rows, "bytes": bytes_}
 
-    Setup (not timed): pools of every sequence (O2, stored bf16) and the INT8 rows
-    (O1) of the rows each query's list selects."""
+
+def _oracle_state(wl, t, O, syn, d, lw, lb, pools_cache, rows_cache):
+    """Per-query oracle inputs (not timed): the sequence's pools (O2, stored bf16)
+    and the INT8 rows (O1) of the positions the query's list selects."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    b = int(wl.q_seq[t])
+    n = int(wl.seq_len[b])
+    f = int(wl.first_valid[b])
+    qp = int(wl.q_pos[t])
+    if b not in pools_cache:
+        k = np.empty((n, d.idx_dim), np.float32)
+        g = np.empty((n, d.idx_dim), np.float32)
+        for x0, (kk, gg) in syn.gen_sequence_blocks(syn.gen_kgate, wl, b, 0, n):
+            k[x0:x0 + kk.shape[0]] = kk
+            g[x0:x0 + gg.shape[0]] = gg
+        pools_cache[b] = O.store_bf16(O.pool_states(k, g, lw, lb, d.ln_eps, f, n, d.kpool))
+        del k, g
+    pools = pools_cache[b]
+    qi, w, q = syn.gen_qidx(wl, t, t + 1)[0], syn.gen_w(wl, t, t + 1)[0], syn.gen_q(wl, t, t + 1)[0]
+    n_vis = O.visible_pool_count(qp, f, d.kpool)
+    idx = O.expand_selection(O.topk_pools(O.index_scores(qi, w, pools, n_vis), n_vis, d.select_k),
+                             f, qp, 0, d.kpool, d.out_width)
+    need = idx[idx >= 0]
+    if b not in rows_cache:
+        rows_cache[b] = (np.zeros((n, d.row_bytes), dtype=np.uint8), set())
+    rows, done = rows_cache[b]
+    blk = 65536
+    for k0 in sorted(set(int(x) // blk for x in need) - done):
+        lat = syn.gen_latent(wl, b, k0 * blk, min(n, (k0 + 1) * blk))
+        O.store_int8(lat, np.arange(k0 * blk, k0 * blk + lat.shape[0]), rows)
+        done.add(k0)
+    return (f, qp, n_vis, pools, rows, qi, w, q)
+
+
+def cpu_baseline(wl, budget_s: float = 12.0, max_queries: int | None = None) -> dict:
+    """The oracle's per-query chain (scores, top-k, expansion, attention), timed
+    on the host cores: whole decode steps (every query of the batch) for decode
+    workloads, a seeded sample of queries for prefill.  Setup (pools of every
+    sequence, O2; INT8 rows, O1) is not timed.  Timed twice: with the BLAS
+    threads set to the cores this process may run on, then with one thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
 
     import dsa_synth as syn
     import oracle as O
 
     d = wl.dims
     lw, lb = syn.gen_ln(wl)
-    state = []
-    for t in range(wl.T):
-        b = int(wl.q_seq[t])
-        n = int(wl.seq_len[b])
-        f = int(wl.first_valid[b])
-        qp = int(wl.q_pos[t])
-        k = np.empty((n, d.idx_dim), np.float32)
-        g = np.empty((n, d.idx_dim), np.float32)
-        for x0, (kk, gg) in syn.gen_sequence_blocks(syn.gen_kgate, wl, b, 0, n):
-            k[x0:x0 + kk.shape[0]] = kk
-            g[x0:x0 + gg.shape[0]] = gg
-        pools = O.store_bf16(O.pool_states(k, g, lw, lb, d.ln_eps, f, n, d.kpool))
-        del k, g
-        qi, w, q = syn.gen_qidx(wl, t, t + 1)[0], syn.gen_w(wl, t, t + 1)[0], syn.gen_q(wl, t, t + 1)[0]
-        n_vis = O.visible_pool_count(qp, f, d.kpool)
-        idx = O.expand_selection(O.topk_pools(O.index_scores(qi, w, pools, n_vis), n_vis, d.select_k),
-                                 f, qp, 0, d.kpool, d.out_width)
-        need = idx[idx >= 0]
-        rows = np.zeros((n, d.row_bytes), dtype=np.uint8)      # only the listed rows are filled
-        blocks = sorted(set(int(x) // 65536 for x in need))
-        for blk in blocks:
-            lat = syn.gen_latent(wl, b, blk * 65536, min(n, (blk + 1) * 65536))
-            sel = need[(need >= blk * 65536) & (need < (blk + 1) * 65536)]
-            O.store_int8(lat[sel - blk * 65536], sel, rows)
-        state.append((f, qp, n_vis, pools, rows, qi, w, q))
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        for f, qp, n_vis, pools, rows, qi, w, q in state:
-            sc = O.index_scores(qi, w, pools, n_vis)
-            ids = O.topk_pools(sc, n_vis, d.select_k)
-            idx = O.expand_selection(ids, f, qp, 0, d.kpool, d.out_width)
-            O.sparse_mla(q, rows, idx, wl.scale, d.latent_dim)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": steps * wl.T / el, "unit": "tok-steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{steps} whole decode steps ({wl.T} queries each) of {wl.name}: oracle scores, "
-                      f"top-k, expansion and attention in float64, {el:.1f} s; pool and INT8-row setup "
-                      "not timed"}
+    if max_queries is not None and wl.T > max_queries:
+        g = np.random.default_rng(7)
+        queries = sorted(int(x) for x in g.choice(wl.T, size=max_queries, replace=False))
+    else:
+        queries = list(range(wl.T))
+    pools_cache, rows_cache = {}, {}
+    state = [_oracle_state(wl, t, O, syn, d, lw, lb, pools_cache, rows_cache) for t in queries]
+
+    def run(limit_s):
+        passes = 0
+        t0 = time.perf_counter()
+        while True:
+            for f, qp, n_vis, pools, rows, qi, w, q in state:
+                sc = O.index_scores(qi, w, pools, n_vis)
+                ids = O.topk_pools(sc, n_vis, d.select_k)
+                idx = O.expand_selection(ids, f, qp, 0, d.kpool, d.out_width)
+                O.sparse_mla(q, rows, idx, wl.scale, d.latent_dim)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= limit_s:
+                return passes * len(state) / el, passes, el
+
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores):
+        v, passes, el = run(budget_s)
+    with threadpool_limits(limits=1):
+        v1, passes1, el1 = run(budget_s / 2)
+    prefill = wl.T > 64
+    unit = "tok/s" if prefill else "tok-steps/s"
+    what = (f"{passes} passes over a seeded sample of {len(state)} of the {wl.T} prefill queries"
+            if len(state) < wl.T else f"{passes} whole decode steps ({wl.T} queries each)")
+    return {"value": v, "unit": unit, "cores": cores, "kind": "oracle",
+            "sample": f"{what} of {wl.name}: oracle scores, top-k, expansion and attention in float64, "
+                      f"{el:.1f} s with {cores} BLAS threads; pool and INT8-row setup not timed",
+            "value_1thread": v1, "sample_1thread": f"{passes1} passes, {el1:.1f} s, 1 thread"}
+
+
+def _ev():
+    import torch
+    return torch.cuda.Event(enable_timing=True)
+
+
+def copy_rate_gbs(reps: int = 10) -> float:
+    """A plain device copy of COPY_BYTES (read + write), the practical HBM ceiling."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a, b = _ev(), _ev()
+    stream = torch.cuda.current_stream()
+    a.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    gbs = 2 * COPY_BYTES * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
+
+
+def _pct(v, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(v), q))
+
+
+def time_steps(dw, steps: int, warmup: int, R: int, group: int):
+    """Warm up, then time `steps` steps (stages dw.timed_stages(), replica i % R)
+    bracketed by one event pair; an event between every `group` steps gives the
+    per-step spread (median, p10, p90 of the group means)."""
+    import torch
+    stages = dw.timed_stages()
+    for r in range(R):
+        for st in stages:
+            dw.bound(st, r)
+    for i in range(warmup):
+        dw.step_timed(i % R)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    marks = [_ev() for _ in range(steps // group + 2)]
+    torch.cuda.synchronize()
+    marks[0].record(stream)
+    k = 1
+    for i in range(steps):
+        dw.step_timed(i % R)
+        if (i + 1) % group == 0 or i + 1 == steps:
+            marks[k].record(stream)
+            k += 1
+    torch.cuda.synchronize()
+    total_ms = marks[0].elapsed_time(marks[k - 1])
+    per = []
+    done = 0
+    for j in range(1, k):
+        n = min(group, steps - done)
+        per.append(marks[j - 1].elapsed_time(marks[j]) * 1e3 / n)
+        done += n
+    return total_ms / steps, per
+
+
+def stage_breakdown(dw, R: int, n: int):
+    """Median time of each stage inside a step (events between the stages, an
+    untimed pass)."""
+    import numpy as np
+    import torch
+    stages = dw.timed_stages()
+    stream = torch.cuda.current_stream()
+    evs = [[_ev() for _ in range(len(stages) + 1)] for _ in range(n)]
+    for i in range(n):
+        evs[i][0].record(stream)
+        for j, st in enumerate(stages):
+            dw.run(st, i % R)
+            evs[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    return {st: round(float(np.median([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e3, 2)
+            for j, st in enumerate(stages)}
+
+
+def scoring_launch_us(dw, R: int, n: int):
+    """The decode scoring kernel's own duration: HIP events recorded around the
+    kernel itself (dsa_time_next_scoring_launch), over n launches of its stage
+    alone cycling the replicas (mean); plus the same n launches back to back
+    between one event pair (burst, which also counts the gaps)."""
+    import numpy as np
+    import torch
+    import sparse_attention_store_amd as dsa
+    stage = dw.timed_stages()[0] if dw.fast_supported() else "scores_select"
+    stream = torch.cuda.current_stream()
+    b0, b1 = _ev(), _ev()
+    torch.cuda.synchronize()
+    b0.record(stream)
+    for i in range(n):
+        dw.run(stage, i % R)
+    b1.record(stream)
+    torch.cuda.synchronize()
+    burst = b0.elapsed_time(b1) * 1e3 / n
+    kev = [(_ev(), _ev()) for _ in range(n)]
+    for a, b in kev:                        # creates the events
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    for i in range(n):
+        dsa.time_next_scoring_launch(*kev[i])
+        dw.run(stage, i % R)
+    torch.cuda.synchronize()
+    own = [a.elapsed_time(b) * 1e3 for a, b in kev]
+    return float(np.mean(own)), float(np.median(own)), burst
+
+
+def prefill_kernel_us(dw, reps: int = 3):
+    """Durations of the prefill's two MFMA kernels: the scoring kernel on one
+    chunk of dw.prefill_chunk queries (events recorded around the kernel itself),
+    and the attention launch over all queries (an event pair around the call;
+    at milliseconds per launch the pair's own cost is negligible)."""
+    import numpy as np
+    import torch
+    import sparse_attention_store_amd as dsa
+    c = dw.prefill_chunk
+    sc = torch.empty((c, dw.stride), dtype=torch.float32, device=dw.device)
+    stream = torch.cuda.current_stream()
+    kev = [(_ev(), _ev()) for _ in range(reps)]
+    for a, b in kev:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    # the chunk in the middle of the prefill (its average visible pool count)
+    t0 = (dw.wl.T // c // 2) * c
+    args = (dw.dims, dw.q_idx[t0:t0 + c], dw.w[t0:t0 + c], dw.pools[0], dw.seqs, dw.q_seq[t0:t0 + c],
+            dw.q_pos[t0:t0 + c], sc)
+    for a, b in kev:
+        dsa.time_next_scoring_launch(a, b)
+        dsa.index_scores(*args)
+    torch.cuda.synchronize()
+    score_us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in kev]))
+    chunk_nvis = sum(dw.wl.n_vis(t) for t in range(t0, t0 + c))
+    a, b = _ev(), _ev()
+    dw.run("attention", 0)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        dw.run("attention", 0)
+    b.record(stream)
+    torch.cuda.synchronize()
+    attn_us = a.elapsed_time(b) * 1e3 / reps
+    del sc
+    return score_us, chunk_nvis, attn_us
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 200 decode, 10 prefill)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps first (default 20 decode, 2 prefill)")
+    ap.add_argument("--replicas", type=int, default=None, help="cache replicas cycled by the steps (default 8 decode, "
+                                                               "1 prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default=WORKLOAD)
-    ap.add_argument("--path", choices=["fused", "separate"], default="separate",
-                    help="fused: new tokens, then one dsa_decode_step launch; separate: one call per step")
+    ap.add_argument("--workload", default=WORKLOAD, choices=sorted(METRICS))
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB elementwise copy (torch.neg) three times: a "
                          "known-size kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -223,25 +440,26 @@ def main():
         print(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.kernel))
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (no multi-GPU path exists)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import dsa_harness
     import dsa_synth as syn
 
     wl = syn.get(args.workload)
-    print(f"[bench] setting up {wl.name}: B={wl.B} T={wl.T} rows={wl.total_rows} "
-          f"replicas={args.replicas}", file=sys.stderr, flush=True)
+    prefill = wl.T > 64
+    steps = args.steps if args.steps is not None else (10 if prefill else 200)
+    warmup = args.warmup if args.warmup is not None else (2 if prefill else 20)
+    R = args.replicas if args.replicas is not None else (1 if prefill else 8)
+    print(f"[bench] setting up {wl.name}: B={wl.B} T={wl.T} rows={wl.total_rows} replicas={R}",
+          file=sys.stderr, flush=True)
     t_setup = time.perf_counter()
-    fused = args.path == "fused"
-    dw = dsa_harness.DeviceWorkload(wl, replicas=args.replicas, out_dtype=torch.bfloat16,
-                                    num_splits=17 if fused else 0)
-    print(f"[bench] setup {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
-    R = args.replicas
+    dw = dsa_harness.DeviceWorkload(wl, replicas=R, out_dtype=torch.bfloat16)
+    print(f"[bench] setup {time.perf_counter() - t_setup:.1f} s; stages {dw.timed_stages()}",
+          file=sys.stderr, flush=True)
     if args.calibrate_copy:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -249,139 +467,82 @@ def main():
             torch.neg(src, out=dst)          # reads and writes COPY_BYTES
         torch.cuda.synchronize()
         del src, dst
-    # The timed loop launches through prepared calls (validated and converted
-    # once per replica): each launch then costs one ctypes call on the host, so
-    # the host keeps ahead of the GPU.
-    timed_stages = ["append", "decode"] if fused else ["append_scores", "select_attention"]
-    for r in range(R):
-        for st in timed_stages:
-            dw.bound(st, r)
-    for i in range(args.warmup):
-        for st in timed_stages:
-            dw.run(st, i % R)
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream()
-    # The dominant kernel is bracketed by HIP events on every EV_EVERY-th timed
-    # step only: an event pair costs several microseconds of stream time, which
-    # would otherwise be charged to every step.
-    sampled = list(range(0, args.steps, EV_EVERY))
-    ev_s = {i: torch.cuda.Event(enable_timing=True) for i in sampled}
-    ev_e = {i: torch.cuda.Event(enable_timing=True) for i in sampled}
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(args.steps):
-        r = i % R
-        if fused:
-            dw.run("append", r)
-            if i in ev_s:
-                ev_s[i].record(stream)
-            dw.run("decode", r)
-            if i in ev_e:
-                ev_e[i].record(stream)
-        else:
-            if i in ev_s:
-                ev_s[i].record(stream)
-            dw.run("append_scores", r)
-            if i in ev_e:
-                ev_e[i].record(stream)
-            dw.run("select_attention", r)
-    end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_step = total_ms / args.steps
-    scores_us = float(np.mean([ev_s[i].elapsed_time(ev_e[i]) for i in sampled])) * 1e3
-
-    # Per-stage breakdown (separate, untimed pass).
-    stages = {}
-    if fused:
-        names = ["append_tokens", "decode_step"]
-        fns = [lambda r: dw.run("append", r), lambda r: dw.run("decode", r)]
-    else:
-        names = ["append_scores_groups", "topk_sparse_mla"]
-        fns = [lambda r, st=st: dw.run(st, r) for st in timed_stages]
-    n_b = min(args.steps, 50)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(n_b)]
-    for i in range(n_b):
-        evs[i][0].record(stream)
-        for j, fn in enumerate(fns):
-            fn(i % R)
-            evs[i][j + 1].record(stream)
-    torch.cuda.synchronize()
-    for j, nm in enumerate(names):
-        stages[nm] = round(float(np.median([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e3, 2)
-
-    # The dominant kernel's launch duration.  A burst of back-to-back launches
-    # of it alone (cycling the replicas, so its pools come from HBM) between
-    # one event pair also counts the gaps between launches (avg_launch_us_burst);
-    # the scoring launch can record HIP events around the kernel itself
-    # (hipExtLaunchKernel), which give its own duration (avg_launch_us).  An
-    # event pair around a single launch inside a step also counts that
-    # launch's dispatch latency (avg_launch_us_in_step).
-    dom_stage = "decode" if fused else "append_scores"
-    dom = lambda r: dw.run(dom_stage, r)
-    n_burst = 4 * R
-    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    b0.record(stream)
-    for i in range(n_burst):
-        dom(i % R)
-    b1.record(stream)
-    torch.cuda.synchronize()
-    burst_us = b0.elapsed_time(b1) * 1e3 / n_burst
-    launch_us = burst_us
-    if not fused:
-        import sparse_attention_store_amd as dsa
-        kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_burst)]
-        for a, b in kev:                        # creates the events
-            a.record(stream)
-            b.record(stream)
-        torch.cuda.synchronize()
-        for i in range(n_burst):
-            dsa.time_next_scoring_launch(*kev[i])
-            dom(i % R)
-        torch.cuda.synchronize()
-        launch_us = float(np.mean([a.elapsed_time(b) for a, b in kev])) * 1e3
-
-    ab = algorithmic_bytes(wl)
-    kern_bytes = ab["decode_kernel"] if fused else ab["scores_kernel"]
-    achieved = kern_bytes / (launch_us * 1e-6) / 1e9
+    copy_gbs = copy_rate_gbs()
+    ms_step, per_step_us = time_steps(dw, steps, warmup, R, group=R if not prefill else 1)
+    stages = stage_breakdown(dw, R, min(steps, 50 if not prefill else 5))
     value = wl.T / (ms_step * 1e-3)
     line = {
-        "metric": METRIC,
+        "metric": METRICS[wl.name],
         "value": round(value, 1),
-        "unit": "tok-steps/s",
+        "unit": "tok/s" if prefill else "tok-steps/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "batch": wl.B, "context_cap": 262144,
-                   "valid_tokens": [int(a - b) for a, b in zip(wl.seq_len, wl.first_valid)],
+        "config": {"workload": wl.name, "batch": wl.B, "queries": wl.T,
+                   "context_cap": int(wl.row_base[1] - wl.row_base[0]) if wl.B > 1 else int(wl.seq_len[0]),
+                   "valid_tokens": [int(a - b) for a, b in zip(wl.seq_len, wl.first_valid)][:16],
                    "mla_heads": wl.dims.mla_heads, "index_topk": wl.dims.index_topk,
                    "out_width": wl.dims.out_width, "replicas": R},
-        "pct_hbm_peak": round(100.0 * ab["step"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
-        "bytes_per_step": ab["step"],
-        "roofline": {"kernel": "decode_step (k_decode_step)" if fused else "append_scores_groups (k_scores_groups)",
-                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profile(PMC_SUMMARY_STEP if fused else PMC_SUMMARY,
-                                                     STEP_SRC if fused else SCORES_SRC),
-                     "algorithmic_bytes_per_launch": kern_bytes, "avg_launch_us": round(launch_us, 2),
-                     "avg_launch_us_burst": round(burst_us, 2),
-                     "avg_launch_us_in_step": round(scores_us, 2)},
-        "path": args.path,
+        "step_us": {"mean": round(ms_step * 1e3, 2), "median": round(_pct(per_step_us, 50), 2),
+                    "p10": round(_pct(per_step_us, 10), 2), "p90": round(_pct(per_step_us, 90), 2),
+                    "samples": len(per_step_us), "steps_per_sample": R if not prefill else 1},
+        "copy_gbs": round(copy_gbs, 1),
         "stages_us_median": stages,
     }
+    if prefill:
+        pw = prefill_work(wl)
+        score_us, chunk_nvis, attn_us = prefill_kernel_us(dw)
+        chunk_flops = 2 * wl.dims.idx_heads * wl.dims.idx_dim * chunk_nvis
+        n_chunks = -(-wl.T // dw.prefill_chunk)
+        s_tf = chunk_flops / (score_us * 1e-6) / 1e12
+        a_tf = pw["attn_flops"] / (attn_us * 1e-6) / 1e12
+        kernels = {
+            "index_scores (k_scores_mfma<8,4>), one 512-query chunk": {
+                "avg_launch_us": round(score_us, 1), "flops_per_launch": chunk_flops,
+                "achieved_tflops": round(s_tf, 1), "frac": round(s_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                "launches_per_step": n_chunks},
+            "sparse_mla (k_mla_mfma<4>)": {
+                "avg_launch_us": round(attn_us, 1), "flops_per_launch": pw["attn_flops"],
+                "achieved_tflops": round(a_tf, 1), "frac": round(a_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                "launches_per_step": 1},
+        }
+        dom_attn = attn_us >= score_us * n_chunks
+        line["pct_mfma_peak"] = round(100.0 * (pw["score_flops"] + pw["attn_flops"]) / (ms_step * 1e-3) / 1e12
+                                      / MFMA_BF16_PEAK_TFLOPS, 2)
+        line["flops_per_step"] = pw["score_flops"] + pw["attn_flops"]
+        line["roofline"] = {
+            "kernel": "sparse_mla (k_mla_mfma<4>)" if dom_attn else "index_scores (k_scores_mfma<8,4>)",
+            "bound": "mfma", "achieved": round(a_tf if dom_attn else s_tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round((a_tf if dom_attn else s_tf) / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None, "flops_per_launch": pw["attn_flops"] if dom_attn else chunk_flops,
+            "avg_launch_us": round(attn_us if dom_attn else score_us, 1)}
+        line["kernels"] = kernels
+    else:
+        ab = algorithmic_bytes(wl)
+        fast = dw.fast_supported()
+        kern_bytes = ab["scores_kernel"] if fast else ab["scores_kernel"] - (ab["step"] - ab["decode_kernel"])
+        own_mean, own_median, burst = scoring_launch_us(dw, R, 4 * R)
+        achieved = kern_bytes / (own_mean * 1e-6) / 1e9
+        line["pct_hbm_peak"] = round(100.0 * ab["step"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)
+        line["bytes_per_step"] = ab["step"]
+        line["roofline"] = {
+            "kernel": ("append_scores_groups (k_scores_groups<true, 512>)" if fast else
+                       "index_scores_select (k_scores_groups<false, 0>)"),
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profile(PMC_SUMMARY, SCORES_SRC) if wl.name == WORKLOAD and fast else None,
+            "algorithmic_bytes_per_launch": kern_bytes, "avg_launch_us": round(own_mean, 2),
+            "median_launch_us": round(own_median, 2), "avg_launch_us_burst": round(burst, 2),
+            "frac_of_copy": round(achieved / copy_gbs, 4)}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(wl)
+        line["cpu_baseline"] = cpu_baseline(wl, max_queries=32 if prefill else None)
     print(json.dumps(line), flush=True)
 
 

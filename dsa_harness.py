@@ -33,8 +33,10 @@ class DeviceWorkload:
 
     def __init__(self, wl: syn.Workload, device="cuda", replicas: int = 1, score_stride: int | None = None,
                  out_dtype=torch.float32, num_splits: int = 0, build: bool = True, gen_workers: int = 8,
-                 canary: int | None = None):
+                 canary: int | None = None, prefill_chunk: int = 512):
         self.wl = wl
+        self.prefill_chunk = prefill_chunk
+        self.ws_chunk = None
         self.device = torch.device(device)
         d = wl.dims
         self.dims = dsa.Dims.of(d)
@@ -203,6 +205,16 @@ class DeviceWorkload:
         return dsa.topk_select_expand(self.dims, self.scores, self.seqs, self.q_seq, self.q_pos, self.indices,
                                       self.pool_ids, self.ws_topk, prepare=prepare)
 
+    def step_prefill_select(self, r: int = 0, prepare: bool = False):
+        """Scores, top-k and expansion of every query, prefill_chunk queries at a
+        time through a bounded scoring workspace (dsa_index_select_chunked)."""
+        if self.ws_chunk is None:
+            self.ws_chunk = dsa.index_select_chunked_workspace(self.dims, self.prefill_chunk, self.stride,
+                                                               device=self.device)
+        return dsa.index_select_chunked(self.dims, self.q_idx, self.w, self.pools[r], self.seqs, self.q_seq,
+                                        self.q_pos, self.stride, self.prefill_chunk, self.indices, self.ws_chunk,
+                                        pool_ids=self.pool_ids, prepare=prepare)
+
     def step_decode(self, r: int = 0, prepare: bool = False):
         """Scores, top-k, expansion and attention in one launch (dsa_decode_step)."""
         if self.ws_step is None:
@@ -227,12 +239,35 @@ class DeviceWorkload:
         for call in self.bound(stage, r):
             call()
 
+    # The launches bench.py times for a decode step (prepared calls): the new
+    # tokens with the scoring pass and its group lists (dsa_append_scores_groups,
+    # one launch), then the selection, expansion and attention
+    # (dsa_topk_sparse_mla: k_select_mla, then the split merge).
+    TIMED_STAGES = ("append_scores", "select_attention")
+
+    def fast_supported(self) -> bool:
+        """Group lists are kept for at most 64 queries of at most 65,536 pools."""
+        return self.wl.T <= 64 and self.stride <= 65536 and self.wl.dims.idx_heads == 32 and \
+            self.wl.dims.idx_dim == 128
+
     def step_fast(self, r: int = 0):
-        """The pass through prepared calls: the new tokens with the scoring
-        pass (one launch), the selection, then attention."""
-        self.run("append_scores", r)
-        self.run("select_groups", r)
-        self.run("attention", r)
+        """One decode step through exactly the launches the bench times."""
+        for st in self.TIMED_STAGES:
+            self.run(st, r)
+
+    def timed_stages(self):
+        """The stages bench.py times for this workload: the decode launches
+        above when they apply; the new tokens, the chunked selection and the
+        attention for many queries (prefill); else the general chain."""
+        if self.fast_supported():
+            return self.TIMED_STAGES
+        if self.wl.T > 64:
+            return ("append", "prefill_select", "attention")
+        return ("append", "scores_select", "attention")
+
+    def step_timed(self, r: int = 0):
+        for st in self.timed_stages():
+            self.run(st, r)
 
     def step_fused(self, r: int = 0):
         """One pass of the whole path: the new tokens, then the fused decode launch."""

@@ -59,7 +59,8 @@ typedef enum dsa_status {
     DSA_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required */
     DSA_ERR_UNSUPPORTED = -7, /* valid dims this build has no kernel for */
     DSA_ERR_HIP = -8,         /* a HIP runtime call or launch failed */
-    DSA_ERR_SIZE = -9         /* negative count or a stride smaller than needed */
+    DSA_ERR_SIZE = -9,        /* negative count or a stride smaller than needed */
+    DSA_ERR_TIMEOUT = -10     /* dsa_decode_step_status: a wait inside the launch timed out */
 } dsa_status;
 
 typedef enum dsa_dtype {
@@ -260,8 +261,10 @@ int dsa_append_scores_groups(const dsa_dims* dims, int dtype, const void* latent
                              int32_t score_stride, float* scores, void* workspace, size_t workspace_bytes,
                              void* stream);
 /*
- * time_next_scoring_launch -- measurement hook.  The next scoring launch that
- * dsa_append_scores_groups makes on the calling thread records start_event
+ * time_next_scoring_launch -- measurement hook.  The next decode scoring
+ * launch made on the calling thread (by dsa_append_scores_groups,
+ * dsa_index_scores_groups, dsa_index_scores_select, or dsa_index_scores with
+ * T <= 64 and 32 x 128 indexer heads) records start_event
  * when the kernel starts and stop_event when it ends (hipExtLaunchKernel),
  * so that hipEventElapsedTime gives the kernel's own duration, without the
  * gap between launches.  One-shot; both NULL cancels.  The events are HIP
@@ -274,6 +277,31 @@ int dsa_index_scores_select(const dsa_dims* dims, const uint16_t* q_idx, const f
                             const int32_t* q_seq, const int32_t* q_pos, int32_t T,
                             int32_t score_stride, float* scores, int32_t* pool_ids, int32_t* indices,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * index_select_chunked -- index_scores and topk_select_expand for many
+ * queries (a prefill chunk) with a bounded scoring workspace: the queries are
+ * taken `chunk` at a time, each group's fp32 scores [chunk, score_stride] are
+ * written to the workspace, selected and expanded, then overwritten by the
+ * next group (the pages' integration keeps the indexer's workspaces bounded:
+ * [Kernels] Included).  pool_ids and indices are those dsa_index_scores +
+ * dsa_topk_select_expand give for all T queries at once; the scores are not
+ * kept.
+ *   q_idx .. score_stride   as dsa_index_scores
+ *   chunk      host: queries per group (1 .. 65,535); the workspace holds
+ *              chunk x score_stride scores, e.g. 512 x 33,792 x 4 B = 69 MB
+ *   pool_ids   device int32 [T, select_k] or NULL; indices device int32
+ *              [T, out_width]
+ *   workspace  device, >= dsa_index_select_chunked_workspace_bytes(dims,
+ *              chunk, score_stride) bytes, 256-byte aligned; scratch only.
+ * Supported: what dsa_topk_select supports.
+ */
+size_t dsa_index_select_chunked_workspace_bytes(const dsa_dims* dims, int32_t chunk, int32_t score_stride);
+int dsa_index_select_chunked(const dsa_dims* dims, const uint16_t* q_idx, const float* w,
+                             const uint16_t* pools, const dsa_seqs* seqs, int32_t num_seqs,
+                             const int32_t* q_seq, const int32_t* q_pos, int32_t T, int32_t score_stride,
+                             int32_t chunk, int32_t* pool_ids, int32_t* indices, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /*
  * expand_selection -- [Ref] Functions (expand_selection) and Traps (the -1
@@ -376,6 +404,15 @@ int dsa_topk_sparse_mla(const dsa_dims* dims, const float* scores, int32_t score
  * out_width <= 8192; else DSA_ERR_UNSUPPORTED.
  */
 size_t dsa_decode_step_workspace_bytes(const dsa_dims* dims, int32_t T, int32_t score_stride);
+/*
+ * decode_step_status -- reads the error word of a dsa_decode_step workspace
+ * after the work enqueued on `stream` so far (this call synchronises the
+ * stream): DSA_OK, or DSA_ERR_TIMEOUT when a wait inside some launch that
+ * used the workspace timed out (that launch's outputs are then invalid; the
+ * word stays set until the caller zero-fills the workspace again).
+ *   workspace  device, as passed to dsa_decode_step; workspace_bytes >= 12.
+ */
+int dsa_decode_step_status(const void* workspace, size_t workspace_bytes, void* stream);
 int dsa_decode_step(const dsa_dims* dims, const uint16_t* q_idx, const float* w,
                     const uint16_t* pools, const dsa_seqs* seqs, int32_t num_seqs,
                     const int32_t* q_seq, const int32_t* q_pos, int32_t T, int32_t score_stride,

@@ -117,6 +117,9 @@ def lib() -> ctypes.CDLL:
                                                    I64, F, P, ctypes.c_int, P, I32, P, SZ, P]),
             "dsa_time_next_scoring_launch": (ctypes.c_int, [P, P]),
             "dsa_decode_step_workspace_bytes": (SZ, [DP, I32, I32]),
+            "dsa_decode_step_status": (ctypes.c_int, [P, SZ, P]),
+            "dsa_index_select_chunked_workspace_bytes": (SZ, [DP, I32, I32]),
+            "dsa_index_select_chunked": (ctypes.c_int, [DP, P, P, P, SP, I32, P, P, I32, I32, I32, P, P, P, SZ, P]),
             "dsa_decode_step": (ctypes.c_int, [DP, P, P, P, SP, I32, P, P, I32, I32, P, ctypes.c_int, P, I64, F,
                                                P, ctypes.c_int, P, P, P, P, SZ, P]),
         }
@@ -365,6 +368,32 @@ def sparse_mla(dims: Dims, q: torch.Tensor, cache: torch.Tensor, indices: torch.
         _stream(stream))
 
 
+def index_select_chunked_workspace(dims: Dims, chunk: int, score_stride: int, device="cuda") -> torch.Tensor:
+    n = int(lib().dsa_index_select_chunked_workspace_bytes(ctypes.byref(dims), int(chunk), int(score_stride)))
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def index_select_chunked(dims: Dims, q_idx: torch.Tensor, w: torch.Tensor, pools: torch.Tensor, seqs: Seqs,
+                         q_seq: torch.Tensor, q_pos: torch.Tensor, score_stride: int, chunk: int,
+                         indices: torch.Tensor, workspace: torch.Tensor, pool_ids: torch.Tensor | None = None,
+                         stream=None, prepare: bool = False):
+    """Scores, top-k and expansion of many queries, `chunk` queries at a time
+    through a bounded scoring workspace (the scores are not kept)."""
+    _check(q_idx, torch.bfloat16, "q_idx")
+    _check(w, torch.float32, "w")
+    _check(pools, torch.bfloat16, "pools")
+    _check(q_seq, torch.int32, "q_seq")
+    _check(q_pos, torch.int32, "q_pos")
+    _check(indices, torch.int32, "indices")
+    _check(workspace, workspace.dtype, "workspace")
+    if pool_ids is not None:
+        _check(pool_ids, torch.int32, "pool_ids")
+    return _call("dsa_index_select_chunked", prepare, ctypes.byref(dims), q_idx.data_ptr(), w.data_ptr(),
+                 pools.data_ptr(), ctypes.byref(seqs._c()), seqs.num_seqs, q_seq.data_ptr(), q_pos.data_ptr(),
+                 q_seq.shape[0], int(score_stride), int(chunk), _ptr(pool_ids), indices.data_ptr(),
+                 workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
+
+
 def index_scores_select_workspace(dims: Dims, T: int, score_stride: int, device="cuda") -> torch.Tensor | None:
     n = int(lib().dsa_index_scores_select_workspace_bytes(ctypes.byref(dims), int(T), int(score_stride)))
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
@@ -512,9 +541,12 @@ def decode_step_workspace(dims: Dims, T: int, score_stride: int, device="cuda") 
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
-def decode_step_error(workspace: torch.Tensor) -> int:
-    """The workspace's error word (nonzero once a wait inside a launch timed out)."""
-    return int(workspace[8:12].view(torch.int32).item())
+def decode_step_error(workspace: torch.Tensor, stream=None) -> int:
+    """dsa_decode_step_status: 0 when no wait inside a launch that used this
+    workspace timed out, else the DSA_ERR_TIMEOUT status (synchronises the stream)."""
+    _check(workspace, workspace.dtype, "workspace")
+    return int(lib().dsa_decode_step_status(workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                            _stream(stream)))
 
 
 def decode_step(dims: Dims, q_idx: torch.Tensor, w: torch.Tensor, pools: torch.Tensor, seqs: Seqs,
@@ -550,4 +582,6 @@ __all__ = [
     "topk_select", "topk_select_expand", "expand_selection", "sparse_mla_workspace_bytes", "sparse_mla",
     "index_scores_select_workspace", "index_scores_select", "index_scores_groups", "topk_select_groups",
     "decode_step_workspace_bytes", "decode_step_workspace", "decode_step_error", "decode_step",
+    "index_select_chunked_workspace",
+    "index_select_chunked",
 ]

@@ -3,6 +3,7 @@
 // Nothing here allocates device memory or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -88,6 +89,7 @@ const char* dsa_status_string(int status) {
         case DSA_ERR_UNSUPPORTED: return "dims not supported by this build";
         case DSA_ERR_HIP: return "HIP runtime error";
         case DSA_ERR_SIZE: return "negative count or stride too small";
+        case DSA_ERR_TIMEOUT: return "a wait inside the launch timed out; its results are invalid";
         default: return "unknown status";
     }
 }
@@ -365,6 +367,50 @@ int dsa_index_scores_select(const dsa_dims* dims, const uint16_t* q_idx, const f
                                             indices, workspace, s));
 }
 
+static size_t chunk_scores_bytes(int32_t chunk, int32_t score_stride) {
+    return ((size_t)chunk * (size_t)score_stride * 4 + 255) / 256 * 256;
+}
+
+size_t dsa_index_select_chunked_workspace_bytes(const dsa_dims* dims, int32_t chunk, int32_t score_stride) {
+    if (check_dims(dims) != DSA_OK || chunk <= 0 || score_stride <= 0) return 0;
+    return chunk_scores_bytes(chunk, score_stride) + dsa_host::topk_workspace_bytes(*dims, chunk, score_stride);
+}
+
+int dsa_index_select_chunked(const dsa_dims* dims, const uint16_t* q_idx, const float* w, const uint16_t* pools,
+                             const dsa_seqs* seqs, int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos,
+                             int32_t T, int32_t score_stride, int32_t chunk, int32_t* pool_ids, int32_t* indices,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (T < 0 || score_stride < 0 || chunk <= 0) return DSA_ERR_SIZE;
+    st = check_seqs(seqs, num_seqs, true, false, true);
+    if (st) return st;
+    if (dims->kpool != 4 || !dsa_host::topk_supported(*dims, score_stride)) return DSA_ERR_UNSUPPORTED;
+    if (T == 0) return DSA_OK;
+    if (score_stride == 0) return DSA_ERR_SIZE;
+    if (chunk > 65535) return DSA_ERR_SIZE;
+    if (!q_idx || !w || !pools || !q_seq || !q_pos || !indices) return DSA_ERR_NULL;
+    if (!aligned(q_idx, 16) || !aligned(pools, 16) || !aligned(w, 16)) return DSA_ERR_ALIGN;
+    const size_t need = dsa_index_select_chunked_workspace_bytes(dims, chunk, score_stride);
+    if (!workspace || workspace_bytes < need) return DSA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return DSA_ERR_ALIGN;
+    float* scores = reinterpret_cast<float*>(workspace);
+    void* tws = reinterpret_cast<char*>(workspace) + chunk_scores_bytes(chunk, score_stride);
+    const int HI = dims->idx_heads, DI = dims->idx_dim, K = dims->index_topk / dims->kpool, W = dims->out_width;
+    hipStream_t s = as_stream(stream);
+    for (int32_t t0 = 0; t0 < T; t0 += chunk) {
+        const int32_t n = std::min(chunk, T - t0);
+        hipError_t e = dsa_host::launch_index_scores(*dims, q_idx + (int64_t)t0 * HI * DI, w + (int64_t)t0 * HI,
+                                                     pools, *seqs, num_seqs, q_seq + t0, q_pos + t0, n, score_stride,
+                                                     scores, s);
+        if (e != hipSuccess) return DSA_ERR_HIP;
+        e = dsa_host::launch_topk(*dims, scores, score_stride, *seqs, q_seq + t0, q_pos + t0, n,
+                                  pool_ids ? pool_ids + (int64_t)t0 * K : nullptr, indices + (int64_t)t0 * W, tws, s);
+        if (e != hipSuccess) return DSA_ERR_HIP;
+    }
+    return DSA_OK;
+}
+
 int dsa_expand_selection(const dsa_dims* dims, const int32_t* pool_ids, const dsa_seqs* seqs,
                          int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos, int32_t T,
                          int32_t* indices, void* stream) {
@@ -470,6 +516,17 @@ int dsa_decode_step(const dsa_dims* dims, const uint16_t* q_idx, const float* w,
                                                    reinterpret_cast<const uint16_t*>(q), cache, scale, out,
                                                    out_dtype, lse, pool_ids, indices, workspace,
                                                    as_stream(stream)));
+}
+
+int dsa_decode_step_status(const void* workspace, size_t workspace_bytes, void* stream) {
+    if (!workspace) return DSA_ERR_NULL;
+    if (workspace_bytes < 12) return DSA_ERR_WORKSPACE;
+    uint32_t word = 0;
+    hipError_t e = hipMemcpyAsync(&word, reinterpret_cast<const char*>(workspace) + 8, 4, hipMemcpyDeviceToHost,
+                                  as_stream(stream));
+    if (e == hipSuccess) e = hipStreamSynchronize(as_stream(stream));
+    if (e != hipSuccess) return DSA_ERR_HIP;
+    return word ? DSA_ERR_TIMEOUT : DSA_OK;
 }
 
 }  // extern "C"

@@ -426,6 +426,22 @@ __global__ __launch_bounds__(256) void k_scores_generic(
 
 namespace dsa_host {
 
+// Events the next decode scoring launch (k_scores_groups, from any entry
+// point) records around the kernel itself; one-shot.
+namespace {
+thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+void take_events(hipEvent_t& a, hipEvent_t& b) {
+    a = t_ev_start;
+    b = t_ev_stop;
+    t_ev_start = t_ev_stop = nullptr;
+}
+}  // namespace
+
+void time_next_scoring_launch(hipEvent_t start, hipEvent_t stop) {
+    t_ev_start = start;
+    t_ev_stop = stop;
+}
+
 // Workgroups (one 256-pool tile each) for k_scores_groups: every tile of
 // every query if that fits, else 4 per CU, which stay resident.
 static unsigned scores_groups_grid(int32_t T, int32_t stride) {
@@ -442,9 +458,11 @@ hipError_t launch_index_scores(const dsa_dims& d, const uint16_t* q_idx, const f
     if (d.idx_heads == dsa::kHI && d.idx_dim == dsa::kDI) {
         if (T <= dsa::kDecMaxT) {
             // Decode: one wave per 64-pool group, a resident grid.
-            hipLaunchKernelGGL((dsa::k_scores_groups<false, 0>), dim3(scores_groups_grid(T, stride)), dim3(256), 0,
-                               s, q_idx, w, pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, num_seqs,
-                               stride, scores, 0, nullptr, nullptr, dsa::AppendArgs{});
+            hipEvent_t ev0, ev1;
+            take_events(ev0, ev1);
+            hipExtLaunchKernelGGL((dsa::k_scores_groups<false, 0>), dim3(scores_groups_grid(T, stride)), dim3(256), 0,
+                                  s, ev0, ev1, 0, q_idx, w, pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T,
+                                  num_seqs, stride, scores, 0, nullptr, nullptr, dsa::AppendArgs{});
         } else {
             // Prefill: 512 resident pools per workgroup, 64 queries per workgroup.
             const int qpb = 64;
@@ -479,20 +497,14 @@ hipError_t launch_scores_with_groups(const dsa_dims& d, const uint16_t* q_idx, c
     uint64_t* cand = reinterpret_cast<uint64_t*>(ws);
     int32_t* cand_n = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) +
                                                  ((size_t)T * dsa::kGroupCandCap * 8 + 255) / 256 * 256);
-    hipLaunchKernelGGL((dsa::k_scores_groups<true, 0>), dim3(scores_groups_grid(T, stride)), dim3(256), 0, s,
-                       q_idx, w, pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, num_seqs, stride,
-                       scores, d.index_topk / d.kpool, cand, cand_n, dsa::AppendArgs{});
+    hipEvent_t ev0, ev1;
+    take_events(ev0, ev1);
+    hipExtLaunchKernelGGL((dsa::k_scores_groups<true, 0>), dim3(scores_groups_grid(T, stride)), dim3(256), 0, s,
+                          ev0, ev1, 0, q_idx, w, pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, num_seqs,
+                          stride, scores, d.index_topk / d.kpool, cand, cand_n, dsa::AppendArgs{});
     return hipGetLastError();
 }
 
-namespace {
-thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
-}
-
-void time_next_scoring_launch(hipEvent_t start, hipEvent_t stop) {
-    t_ev_start = start;
-    t_ev_stop = stop;
-}
 
 bool append_scores_fused(const dsa_dims& d, int dtype) {
     return dtype == DSA_BF16 && d.idx_dim == dsa::kDI &&
@@ -533,8 +545,8 @@ hipError_t launch_append_scores_groups(const dsa_dims& d, const void* latent, in
     ap.tasks = (int)tasks;
     const int64_t want = cdiv(cdiv(stride, dsa::kGroupPools), 4) * (int64_t)T + tasks;
     const unsigned grid = (unsigned)std::min<int64_t>(std::max<int64_t>(want, 1), 4 * (int64_t)device_info().cu_count);
-    const hipEvent_t ev0 = t_ev_start, ev1 = t_ev_stop;
-    t_ev_start = t_ev_stop = nullptr;
+    hipEvent_t ev0, ev1;
+    take_events(ev0, ev1);
 #define DSA_APPEND_SCORES(D)                                                                                        \
     hipExtLaunchKernelGGL((dsa::k_scores_groups<true, D>), dim3(grid), dim3(256), 0, s, ev0, ev1, 0, q_idx, w,    \
                           pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, num_seqs, stride, scores,   \

@@ -15,11 +15,24 @@ import oracle as O
 
 
 class OracleWorkload:
-    def __init__(self, wl: syn.Workload):
+    def __init__(self, wl: syn.Workload, block_cache_bytes: int = 1 << 30):
         self.wl = wl
         self.d = wl.dims
         self._pools = {}
         self._stored = {}
+        self._blocks = {}                 # (sequence, block) -> latent rows, bounded by block_cache_bytes
+        self._block_cap = max(1, block_cache_bytes // (syn.ROW_BLOCK * self.d.latent_dim * 4))
+
+    def _latent_block(self, b: int, k: int) -> np.ndarray:
+        key = (b, k)
+        blk = self._blocks.get(key)
+        if blk is None:
+            n_b = int(self.wl.seq_len[b])
+            blk = syn.gen_latent(self.wl, b, k * syn.ROW_BLOCK, min(n_b, (k + 1) * syn.ROW_BLOCK))
+            if len(self._blocks) >= self._block_cap:
+                self._blocks.pop(next(iter(self._blocks)))
+            self._blocks[key] = blk
+        return blk
 
     def pools_stored(self, b: int) -> np.ndarray:
         """Pools of sequence b as stored: O2 in fp64, rounded once to bf16."""
@@ -56,10 +69,9 @@ class OracleWorkload:
             sel = np.nonzero(seq_of == b)[0]
             pos = rows[sel] - int(wl.row_base[b])
             lat = np.empty((sel.size, self.d.latent_dim), dtype=np.float32)
-            n_b = int(wl.seq_len[b])
             ks = [int(k) for k in np.unique(pos // blk)]
             with cf.ThreadPoolExecutor(max_workers=8) as ex:
-                blocks = ex.map(lambda k: syn.gen_latent(wl, int(b), k * blk, min(n_b, (k + 1) * blk)), ks)
+                blocks = ex.map(lambda k: self._latent_block(int(b), k), ks)
                 for k, block in zip(ks, blocks):
                     m = (pos // blk) == k
                     lat[m] = block[pos[m] - k * blk]
@@ -120,3 +132,90 @@ def score_close(gpu: np.ndarray, ref: np.ndarray, n_vis: int, rtol: float = 1e-2
     err = np.abs(g - r)
     bound = rtol * np.abs(r) + floor * rms
     return bool(np.all(err <= bound)), float(np.max(err / np.maximum(bound, 1e-300)))
+
+
+def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
+    """Half a bf16 unit in the last place at |x| (the rounding of a bf16 output)."""
+    ax = np.maximum(np.abs(np.asarray(x, np.float64)), 2.0 ** -126)
+    return np.ldexp(1.0, np.floor(np.log2(ax)).astype(np.int64) - 8)
+
+
+def check_chain(dw, queries, pool_sample: int = 64, say=print) -> dict:
+    """Every stage of the step dw ran, for each query in `queries`:
+
+    * pools (a sample per sequence) and scores against the oracle's (O2, O3):
+      rtol 1e-2 with a floor of 1e-2 x RMS of the oracle row; score tails -inf;
+    * stage-isolated selection: the oracle's top-k (O4) and expansion (O5) run
+      on the GPU's own fp32 score row must reproduce pool_ids and the index
+      list bit for bit;
+    * end-to-end selection: the GPU's set may differ from the oracle's fp64
+      chain only among pools within 1e-3 (relative) of the k-th oracle score;
+    * cache rows of the GPU's list: bit-exact against O1;
+    * attention: O6 on the GPU's list and cache bytes, max-abs 2e-2 (plus half a
+      bf16 ulp of the reference for a bf16 output) and rel-L2 1e-2 over all the
+      checked queries; an empty list gives exactly 0 and lse -inf.
+    No query is skipped.  Returns counts for the report."""
+    import torch
+    queries = [int(t) for t in queries]
+    wl = dw.wl
+    d = wl.dims
+    ow = OracleWorkload(wl)
+    scores = dw.scores.cpu().numpy()
+    ids = dw.pool_ids.cpu().numpy()
+    idx = dw.indices.cpu().numpy()
+    out_bf16 = dw.out.dtype == torch.bfloat16
+    out = dw.out.float().cpu().numpy()
+    lse = dw.lse.cpu().numpy()
+    pools = dw.pools[0].float().cpu().numpy()
+    errs, refs, allow = [], [], []
+    near_ties = 0
+    g = np.random.default_rng(17)
+    checked_pools = set()
+    for t in queries:
+        t = int(t)
+        b = int(wl.q_seq[t])
+        f = int(wl.first_valid[b])
+        qp = int(wl.q_pos[t])
+        say(f"  oracle query {t} (sequence {b}, position {qp})")
+        r = ow.query(t, dw.stride)
+        n_vis = r["n_vis"]
+        if b not in checked_pools:
+            checked_pools.add(b)
+            pb = int(wl.pool_base[b])
+            opools = ow.pools_stored(b)
+            sel = np.arange(opools.shape[0]) if opools.shape[0] <= pool_sample else \
+                g.choice(opools.shape[0], size=pool_sample, replace=False)
+            for p in sel:
+                ok, worst = score_close(pools[pb + p], ow.pools(b)[p], d.idx_dim)
+                assert ok, ("pool", t, int(p), worst)
+        ok, worst = score_close(scores[t], r["scores"], n_vis)
+        assert ok, ("scores", t, worst)
+        assert np.all(np.isneginf(scores[t, n_vis:])), ("scores tail", t)
+        # stage-isolated: O4 + O5 on the GPU's own scores
+        iso_ids = O.topk_pools(scores[t].astype(np.float64), n_vis, d.select_k)
+        assert np.array_equal(ids[t], iso_ids), ("pool_ids vs O4 on the GPU scores", t)
+        iso_idx = O.expand_selection(iso_ids, f, qp, int(wl.row_base[b]), d.kpool, d.out_width)
+        assert np.array_equal(idx[t], iso_idx), ("indices vs O5", t)
+        # end-to-end: near-ties only
+        ok, nsw = topk_set_ok(ids[t], r["scores"], r["ids"], n_vis)
+        assert ok, ("top-k set beyond near-ties", t)
+        near_ties += nsw > 0
+        # rows of the GPU's own list, then O6 on them
+        valid = idx[t][idx[t] >= 0]
+        got_rows = dw.caches[0][torch.from_numpy(valid.astype(np.int64)).to(dw.device)].cpu().numpy().view(np.uint8)
+        assert np.array_equal(got_rows, ow.cache_rows(valid)), ("rows", t)
+        q = syn.gen_q(wl, t, t + 1)[0]
+        if valid.size == 0:
+            assert np.all(out[t] == 0) and np.all(np.isneginf(lse[t])), ("empty list", t)
+            continue
+        o_ref, lse_ref = O.sparse_mla(q, got_rows, np.arange(valid.size), wl.scale, d.latent_dim)
+        errs.append(out[t] - o_ref)
+        refs.append(o_ref)
+        allow.append(2e-2 + (bf16_half_ulp(o_ref) if out_bf16 else np.zeros_like(o_ref)))
+        assert np.allclose(lse[t], lse_ref, atol=2e-3, rtol=1e-4), ("lse", t)
+    if errs:
+        e, rf, al = np.stack(errs), np.stack(refs), np.stack(allow)
+        assert np.all(np.abs(e) <= al), float(np.max(np.abs(e) - al))
+        if np.linalg.norm(rf) > 0:
+            assert np.linalg.norm(e) / np.linalg.norm(rf) <= 1e-2
+    return {"queries": len(queries), "near_tie_queries": int(near_ties)}

@@ -266,3 +266,38 @@ def test_topk_sparse_mla_argument_checks(dsa):
     assert call(mws=None) == E_WS
     assert call(mws_bytes=mla_need - 1) == E_WS
     assert call(T=0, idx=None, ws=None, ws_bytes=0) == OK
+
+
+def test_chunked_selection_argument_checks(dsa):
+    L = dsa.lib()
+    d = prod(dsa)
+    bd = ctypes.byref(d)
+    s = ctypes.byref(seqs(dsa))
+    # workspace size: one chunk's fp32 scores (rounded to 256 B) plus the top-k scratch of one chunk
+    n = L.dsa_index_select_chunked_workspace_bytes(bd, 512, 33792)
+    assert n >= 512 * 33792 * 4 and n < 512 * 33792 * 4 + (64 << 20)
+    assert L.dsa_index_select_chunked_workspace_bytes(bd, 0, 33792) == 0
+    args = [bd, FAKE, FAKE, FAKE, s, 1, FAKE, FAKE, 4096, 33792, 512, FAKE, FAKE, FAKE, n, None]
+    bad = list(args)
+    bad[10] = 0                                            # chunk
+    assert L.dsa_index_select_chunked(*bad) == E_SIZE
+    bad = list(args)
+    bad[12] = None                                         # indices
+    assert L.dsa_index_select_chunked(*bad) == E_NULL
+    bad = list(args)
+    bad[14] = n - 1                                        # workspace too small
+    assert L.dsa_index_select_chunked(*bad) == E_WS
+    bad = list(args)
+    bad[1] = MISALIGNED
+    assert L.dsa_index_select_chunked(*bad) == E_ALIGN
+    bad = list(args)
+    bad[8] = 0                                             # no queries: nothing to do
+    assert L.dsa_index_select_chunked(*bad) == OK
+
+
+def test_decode_step_status_argument_checks(dsa):
+    L = dsa.lib()
+    assert L.dsa_decode_step_status(None, 64, None) == E_NULL
+    assert L.dsa_decode_step_status(FAKE, 8, None) == E_WS
+    for code in (-10,):
+        assert dsa.status_string(code) != "unknown status"

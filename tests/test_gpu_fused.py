@@ -77,14 +77,16 @@ def test_decode_step_matches_separate_calls(harness, name):
 
 
 def test_decode_step_matches_oracle(harness):
-    from test_gpu_chain import _check_chain
+    from oracle_chain import check_chain
+    import sparse_attention_store_amd as dsa
     wl = syn.mini_decode()
     say(f"decode step vs oracle {wl.name}")
     dw = harness.DeviceWorkload(wl, num_splits=17)
     dw.step()                                   # fills dw.scores (checked by the chain rules)
     dw.step_decode()
     torch.cuda.synchronize()
-    _check_chain(dw, range(wl.T))
+    assert dsa.decode_step_error(dw.ws_step) == 0
+    check_chain(dw, range(wl.T), say=say)
 
 
 def test_decode_step_forced_fallback(harness):
@@ -112,11 +114,13 @@ def test_decode_step_forced_fallback(harness):
 @pytest.mark.slow
 @pytest.mark.parametrize("name", ["decode_32k", "decode_262k_b8"])
 def test_decode_step_full_size(harness, name):
-    from test_gpu_chain import _check_chain
+    from oracle_chain import check_chain
+    import sparse_attention_store_amd as dsa
     wl = syn.get(name)
     say(f"decode step full {name} T={wl.T}")
     dw = _fused_vs_separate(harness, wl, splits=17)
+    assert dsa.decode_step_error(dw.ws_step) == 0
     say(f"decode step full {name}: oracle check of {wl.T} queries")
-    _check_chain(dw, list(range(wl.T)), pool_sample=64, allow_swaps_frac=0.25)
+    check_chain(dw, list(range(wl.T)), say=say)
     del dw
     torch.cuda.empty_cache()
