@@ -60,7 +60,8 @@ typedef enum dsa_status {
     DSA_ERR_UNSUPPORTED = -7, /* valid dims this build has no kernel for */
     DSA_ERR_HIP = -8,         /* a HIP runtime call or launch failed */
     DSA_ERR_SIZE = -9,        /* negative count or a stride smaller than needed */
-    DSA_ERR_TIMEOUT = -10     /* dsa_decode_step_status: a wait inside the launch timed out */
+    DSA_ERR_TIMEOUT = -10,    /* dsa_decode_step_status: a wait inside the launch timed out */
+    DSA_ERR_SCRATCH = -11     /* dsa_sparse_mla_noalloc: the call needs more than its fixed scratch */
 } dsa_status;
 
 typedef enum dsa_dtype {
@@ -344,6 +345,26 @@ int dsa_sparse_mla(const dsa_dims* dims, const void* q, int q_dtype, const int8_
                    int64_t cache_rows, const int32_t* indices, int32_t T, float scale,
                    void* out, int out_dtype, float* lse, int32_t num_splits,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sparse_mla_noalloc -- dsa_sparse_mla for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments without the workspace, the same
+ * kernels and the same results bit for bit (for the same num_splits).  The
+ * split partials go to a fixed device array of
+ * dsa_sparse_mla_noalloc_scratch_bytes() bytes (16 MiB) that the library
+ * holds on each device it runs on until the process ends; its address is
+ * resolved on the first call on a device.  The call allocates nothing.
+ * A call whose partials would not fit (dsa_sparse_mla_workspace_bytes(dims,
+ * T, num_splits) larger than that) returns DSA_ERR_SCRATCH and launches
+ * nothing.  All calls on one GPU share that GPU's array: calls that overlap
+ * on one GPU (other streams, other host threads) race and must be ordered by
+ * the caller.  The array needs no initialisation.
+ */
+size_t dsa_sparse_mla_noalloc_scratch_bytes(void);
+int dsa_sparse_mla_noalloc(const dsa_dims* dims, const void* q, int q_dtype, const int8_t* cache,
+                           int64_t cache_rows, const int32_t* indices, int32_t T, float scale,
+                           void* out, int out_dtype, float* lse, int32_t num_splits, void* stream);
 
 /*
  * topk_sparse_mla -- dsa_topk_select_groups followed by dsa_sparse_mla over

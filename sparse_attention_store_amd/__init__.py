@@ -120,6 +120,9 @@ def lib() -> ctypes.CDLL:
             "dsa_decode_step_status": (ctypes.c_int, [P, SZ, P]),
             "dsa_index_select_chunked_workspace_bytes": (SZ, [DP, I32, I32]),
             "dsa_index_select_chunked": (ctypes.c_int, [DP, P, P, P, SP, I32, P, P, I32, I32, I32, P, P, P, SZ, P]),
+            "dsa_sparse_mla_noalloc_scratch_bytes": (SZ, []),
+            "dsa_sparse_mla_noalloc": (ctypes.c_int, [DP, P, ctypes.c_int, P, I64, P, I32, F, P, ctypes.c_int, P,
+                                                      I32, P]),
             "dsa_decode_step": (ctypes.c_int, [DP, P, P, P, SP, I32, P, P, I32, I32, P, ctypes.c_int, P, I64, F,
                                                P, ctypes.c_int, P, P, P, P, SZ, P]),
         }
@@ -368,6 +371,29 @@ def sparse_mla(dims: Dims, q: torch.Tensor, cache: torch.Tensor, indices: torch.
         _stream(stream))
 
 
+def sparse_mla_noalloc_scratch_bytes() -> int:
+    return int(lib().dsa_sparse_mla_noalloc_scratch_bytes())
+
+
+def sparse_mla_noalloc(dims: Dims, q: torch.Tensor, cache: torch.Tensor, indices: torch.Tensor, scale: float,
+                       out: torch.Tensor, lse: torch.Tensor | None = None, num_splits: int = 0, stream=None,
+                       prepare: bool = False):
+    """sparse_mla with its split partials in the library's fixed device array (no workspace)."""
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q must be bf16 or fp32")
+    _check(q, q.dtype, "q")
+    _check(cache, torch.int8, "cache")
+    _check(indices, torch.int32, "indices")
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bf16 or fp32")
+    _check(out, out.dtype, "out")
+    if lse is not None:
+        _check(lse, torch.float32, "lse")
+    return _call("dsa_sparse_mla_noalloc", prepare,
+                 ctypes.byref(dims), q.data_ptr(), _dt(q), cache.data_ptr(), cache.shape[0], indices.data_ptr(),
+                 q.shape[0], float(scale), out.data_ptr(), _dt(out), _ptr(lse), int(num_splits), _stream(stream))
+
+
 def index_select_chunked_workspace(dims: Dims, chunk: int, score_stride: int, device="cuda") -> torch.Tensor:
     n = int(lib().dsa_index_select_chunked_workspace_bytes(ctypes.byref(dims), int(chunk), int(score_stride)))
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
@@ -582,6 +608,6 @@ __all__ = [
     "topk_select", "topk_select_expand", "expand_selection", "sparse_mla_workspace_bytes", "sparse_mla",
     "index_scores_select_workspace", "index_scores_select", "index_scores_groups", "topk_select_groups",
     "decode_step_workspace_bytes", "decode_step_workspace", "decode_step_error", "decode_step",
-    "index_select_chunked_workspace",
+    "sparse_mla_noalloc_scratch_bytes", "sparse_mla_noalloc", "index_select_chunked_workspace",
     "index_select_chunked",
 ]

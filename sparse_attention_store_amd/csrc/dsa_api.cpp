@@ -90,6 +90,7 @@ const char* dsa_status_string(int status) {
         case DSA_ERR_HIP: return "HIP runtime error";
         case DSA_ERR_SIZE: return "negative count or stride too small";
         case DSA_ERR_TIMEOUT: return "a wait inside the launch timed out; its results are invalid";
+        case DSA_ERR_SCRATCH: return "the call needs more scratch than the no-allocation entry point holds";
         default: return "unknown status";
     }
 }
@@ -451,6 +452,32 @@ int dsa_sparse_mla(const dsa_dims* dims, const void* q, int q_dtype, const int8_
     }
     return hip_status(dsa_host::launch_sparse_mla(*dims, plan, q, q_dtype, cache, indices, T, scale, out,
                                                   out_dtype, lse, workspace, as_stream(stream)));
+}
+
+size_t dsa_sparse_mla_noalloc_scratch_bytes(void) { return dsa::kNoAllocScratchBytes; }
+
+int dsa_sparse_mla_noalloc(const dsa_dims* dims, const void* q, int q_dtype, const int8_t* cache,
+                           int64_t cache_rows, const int32_t* indices, int32_t T, float scale, void* out,
+                           int out_dtype, float* lse, int32_t num_splits, void* stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (q_dtype != DSA_F32 && q_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    if (out_dtype != DSA_F32 && out_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    if (T < 0 || cache_rows < 0 || num_splits < 0) return DSA_ERR_SIZE;
+    if (dims->latent_dim % 64 != 0 || dims->latent_dim > 1024) return DSA_ERR_UNSUPPORTED;
+    if (T == 0) return DSA_OK;
+    if (T > 65535) return DSA_ERR_SIZE;
+    if (!q || !cache || !indices || !out) return DSA_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(out, 16)) return DSA_ERR_ALIGN;
+    const dsa_host::MlaPlan plan = dsa_host::plan_sparse_mla(*dims, T, num_splits, q_dtype);
+    if (plan.ws_bytes > dsa::kNoAllocScratchBytes) return DSA_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (plan.ws_bytes > 0) {
+        st = hip_status(dsa_host::noalloc_scratch(&ws));
+        if (st) return st;
+    }
+    return hip_status(dsa_host::launch_sparse_mla(*dims, plan, q, q_dtype, cache, indices, T, scale, out,
+                                                  out_dtype, lse, ws, as_stream(stream)));
 }
 
 int dsa_topk_sparse_mla(const dsa_dims* dims, const float* scores, int32_t score_stride, const dsa_seqs* seqs,

@@ -189,6 +189,11 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
 
 }  // namespace dsa
 
+namespace dsa {
+// Size of the fixed device array behind dsa_sparse_mla_noalloc (split partials).
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+}  // namespace dsa
+
 // Host-side helpers shared by the launchers.
 namespace dsa_host {
 

@@ -88,6 +88,10 @@ hipError_t launch_select_mla(const dsa_dims& d, const MlaPlan& plan, const float
                              const int8_t* cache, float scale, void* out, int out_dtype, float* lse, void* mla_ws,
                              hipStream_t s);
 
+// The device address of the no-allocation entry point's fixed array on the
+// current device (resolved once per device).
+hipError_t noalloc_scratch(void** out);
+
 bool decode_step_supported(const dsa_dims& d, int32_t T, int32_t stride);
 size_t decode_step_workspace_bytes(const dsa_dims& d, int32_t T, int32_t stride);
 hipError_t launch_decode_step(const dsa_dims& d, const uint16_t* q_idx, const float* w, const uint16_t* pools,

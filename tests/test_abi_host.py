@@ -299,5 +299,5 @@ def test_decode_step_status_argument_checks(dsa):
     L = dsa.lib()
     assert L.dsa_decode_step_status(None, 64, None) == E_NULL
     assert L.dsa_decode_step_status(FAKE, 8, None) == E_WS
-    for code in (-10,):
+    for code in (-10, -11):
         assert dsa.status_string(code) != "unknown status"
