@@ -34,15 +34,19 @@ METRICS = {
     "decode_32k": "decode tok-steps/s (indexer+topk+sparse MLA) @32k ctx B=1; % HBM peak",
     "decode_1m_b4": "decode tok-steps/s (indexer+topk+sparse MLA) @1M ctx B=4, 64 heads; % HBM peak",
     "prefill_4k_on_131k": "prefill tokens/s (indexer+topk+sparse MLA), 4096 queries on 131k ctx, 64 heads; % MFMA peak",
+    "decode_262k_b8_mtp": "decode tok-steps/s (indexer+topk+sparse MLA) @262k ctx B=8, 4 queries per sequence "
+                          "(1 + 3 drafts); % HBM peak",
 }
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 WORKLOAD = "decode_262k_b8"
 _CSRC = os.path.join(ROOT, "sparse_attention_store_amd", "csrc")
-SCORES_SRC = [os.path.join(_CSRC, f) for f in ("index_scores.hip", "scores_core.h", "topk_core.h", "new_tokens.h", "dsa_common.h")]
+_SCORES_HDR = ("scores_core.h", "scores_decode.h", "topk_core.h", "new_tokens.h", "dsa_common.h")
+SCORES_SRC = [os.path.join(_CSRC, f) for f in ("index_scores.hip",) + _SCORES_HDR]
 # the sources each profiled kernel is built from (a counter summary names their hash)
 KERNEL_SRC = {
     "k_scores_groups": SCORES_SRC,
+    "k_scores_runs": [os.path.join(_CSRC, f) for f in ("index_scores_runs.hip",) + _SCORES_HDR],
     "k_scores_mfma": SCORES_SRC,
     "k_select_mla": [os.path.join(_CSRC, f) for f in ("select_mla.hip", "group_select.h", "mla_core.h",
                                                       "topk_core.h", "dsa_common.h")],
@@ -55,27 +59,40 @@ PMC_SUMMARY = os.path.join(ROOT, "profiles", "index_scores_decode_262k_b8_traffi
 COPY_BYTES = 256 << 20          # calibration copy: bytes read (and written) per launch
 
 
-def algorithmic_bytes(wl) -> dict:
-    """Bytes the method must move per decode step (see the design notes)."""
+def algorithmic_bytes(wl, pool_bytes: int = 256, share: int = 1) -> dict:
+    """Bytes the method must move per decode step (see the design notes).
+    pool_bytes: a stored pool (256 in bf16; 132 as INT8 codes plus an fp32 scale).
+    share > 1: runs of up to `share` consecutive queries of one sequence read
+    its pools once (the largest visible count of the run)."""
     d = wl.dims
     tot_pools = 0
     tot_rows = 0
     new_pools = 0
+    run_len, run_max = 0, 0
     for t in range(wl.T):
         n_vis = wl.n_vis(t)
         b = int(wl.q_seq[t])
         f = int(wl.first_valid[b])
         qp = int(wl.q_pos[t])
-        tot_pools += n_vis
+        if run_len and b == int(wl.q_seq[t - 1]) and run_len < share:
+            run_len += 1
+            tot_pools += max(0, n_vis - run_max)
+            run_max = max(run_max, n_vis)
+        else:
+            run_len, run_max = 1, n_vis
+            tot_pools += n_vis
         tail = (qp - f + 1) - d.kpool * n_vis if qp >= f else 0
         tot_rows += d.kpool * min(d.select_k, n_vis) + tail
         new_pools += 1 if qp >= f and (qp - f + 1) % d.kpool == 0 else 0
+    # the score rows and q_idx are per query, the pools per run
+    score_writes = sum(wl.n_vis(t) for t in range(wl.T))
     T = wl.T
-    scores = tot_pools * (256 + 4) + T * (d.idx_heads * d.idx_dim * 2 + d.idx_heads * 4)
-    step = (tot_pools * 256 + T * (d.idx_heads * d.idx_dim * 2 + d.idx_heads * 4) + tot_rows * d.row_bytes
+    scores = tot_pools * pool_bytes + score_writes * 4 + T * (d.idx_heads * d.idx_dim * 2 + d.idx_heads * 4)
+    new_pool_out = d.idx_dim * 2 if pool_bytes == 256 else pool_bytes
+    step = (tot_pools * pool_bytes + T * (d.idx_heads * d.idx_dim * 2 + d.idx_heads * 4) + tot_rows * d.row_bytes
             + T * 4 * d.mla_heads * d.latent_dim + T * 4 * d.out_width + T * (2 * d.latent_dim + d.row_bytes)
-            + new_pools * (2 * d.kpool * d.idx_dim * 2 + d.idx_dim * 2))
-    new_tokens = T * (2 * d.latent_dim + d.row_bytes) + new_pools * (2 * d.kpool * d.idx_dim * 2 + d.idx_dim * 2)
+            + new_pools * (2 * d.kpool * d.idx_dim * 2 + new_pool_out))
+    new_tokens = T * (2 * d.latent_dim + d.row_bytes) + new_pools * (2 * d.kpool * d.idx_dim * 2 + new_pool_out)
     return {"step": step, "scores_kernel": scores + new_tokens, "decode_kernel": step - new_tokens,
             "pools": tot_pools, "rows": tot_rows}
 
@@ -180,9 +197,10 @@ def prefill_work(wl) -> dict:
     return {"score_flops": score_flops, "attn_flops": attn_flops, "sum_n_vis": nvis, "rows": rows, "bytes": bytes_}
 
 
-def _oracle_state(wl, t, O, syn, d, lw, lb, pools_cache, rows_cache):
-    """Per-query oracle inputs (not timed): the sequence's pools (O2, stored bf16)
-    and the INT8 rows (O1) of the positions the query's list selects."""
+def _oracle_state(wl, t, O, syn, d, lw, lb, pools_cache, rows_cache, int8=False):
+    """Per-query oracle inputs (not timed): the sequence's pools (O2, stored bf16,
+    or with int8 as codes and scales, O2q) and the INT8 rows (O1) of the
+    positions the query's list selects."""
     import numpy as np
     b = int(wl.q_seq[t])
     n = int(wl.seq_len[b])
@@ -194,13 +212,14 @@ def _oracle_state(wl, t, O, syn, d, lw, lb, pools_cache, rows_cache):
         for x0, (kk, gg) in syn.gen_sequence_blocks(syn.gen_kgate, wl, b, 0, n):
             k[x0:x0 + kk.shape[0]] = kk
             g[x0:x0 + gg.shape[0]] = gg
-        pools_cache[b] = O.store_bf16(O.pool_states(k, g, lw, lb, d.ln_eps, f, n, d.kpool))
+        ps = O.pool_states(k, g, lw, lb, d.ln_eps, f, n, d.kpool)
+        pools_cache[b] = O.quantize_pools(ps) if int8 else O.store_bf16(ps)
         del k, g
     pools = pools_cache[b]
     qi, w, q = syn.gen_qidx(wl, t, t + 1)[0], syn.gen_w(wl, t, t + 1)[0], syn.gen_q(wl, t, t + 1)[0]
     n_vis = O.visible_pool_count(qp, f, d.kpool)
-    idx = O.expand_selection(O.topk_pools(O.index_scores(qi, w, pools, n_vis), n_vis, d.select_k),
-                             f, qp, 0, d.kpool, d.out_width)
+    sc = O.index_scores_int8(qi, w, pools[0], pools[1], n_vis) if int8 else O.index_scores(qi, w, pools, n_vis)
+    idx = O.expand_selection(O.topk_pools(sc, n_vis, d.select_k), f, qp, 0, d.kpool, d.out_width)
     need = idx[idx >= 0]
     if b not in rows_cache:
         rows_cache[b] = (np.zeros((n, d.row_bytes), dtype=np.uint8), set())
@@ -213,7 +232,7 @@ def _oracle_state(wl, t, O, syn, d, lw, lb, pools_cache, rows_cache):
     return (f, qp, n_vis, pools, rows, qi, w, q)
 
 
-def cpu_baseline(wl, budget_s: float = 12.0, max_queries: int | None = None) -> dict:
+def cpu_baseline(wl, budget_s: float = 12.0, max_queries: int | None = None, int8: bool = False) -> dict:
     """The oracle's per-query chain (scores, top-k, expansion, attention), timed
     on the host cores: whole decode steps (every query of the batch) for decode
     workloads, a seeded sample of queries for prefill.  Setup (pools of every
@@ -233,14 +252,15 @@ def cpu_baseline(wl, budget_s: float = 12.0, max_queries: int | None = None) -> 
     else:
         queries = list(range(wl.T))
     pools_cache, rows_cache = {}, {}
-    state = [_oracle_state(wl, t, O, syn, d, lw, lb, pools_cache, rows_cache) for t in queries]
+    state = [_oracle_state(wl, t, O, syn, d, lw, lb, pools_cache, rows_cache, int8) for t in queries]
 
     def run(limit_s):
         passes = 0
         t0 = time.perf_counter()
         while True:
             for f, qp, n_vis, pools, rows, qi, w, q in state:
-                sc = O.index_scores(qi, w, pools, n_vis)
+                sc = O.index_scores_int8(qi, w, pools[0], pools[1], n_vis) if int8 else \
+                    O.index_scores(qi, w, pools, n_vis)
                 ids = O.topk_pools(sc, n_vis, d.select_k)
                 idx = O.expand_selection(ids, f, qp, 0, d.kpool, d.out_width)
                 O.sparse_mla(q, rows, idx, wl.scale, d.latent_dim)
@@ -259,7 +279,8 @@ def cpu_baseline(wl, budget_s: float = 12.0, max_queries: int | None = None) -> 
     what = (f"{passes} passes over a seeded sample of {len(state)} of the {wl.T} prefill queries"
             if len(state) < wl.T else f"{passes} whole decode steps ({wl.T} queries each)")
     return {"value": v, "unit": unit, "cores": cores, "kind": "oracle",
-            "sample": f"{what} of {wl.name}: oracle scores, top-k, expansion and attention in float64, "
+            "sample": f"{what} of {wl.name}: oracle scores{' over INT8 pools' if int8 else ''}, top-k, expansion "
+                      f"and attention in float64, "
                       f"{el:.1f} s with {cores} BLAS threads; pool and INT8-row setup not timed",
             "value_1thread": v1, "sample_1thread": f"{passes1} passes, {el1:.1f} s, 1 thread"}
 
@@ -424,6 +445,12 @@ def main():
                                                                "1 prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=WORKLOAD, choices=sorted(METRICS))
+    ap.add_argument("--share", type=int, default=None,
+                    help="queries per run sharing one pass over a sequence's pools (1-4; default 4 for the "
+                         "4-queries-per-sequence workload, else 1)")
+    ap.add_argument("--pools", default="bf16", choices=["bf16", "int8"],
+                    help="pool cache format: bf16 rows (the metric's configuration) or INT8 codes with an fp32 "
+                         "scale per pool (decode workloads of at most 65,536 pools per sequence)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB elementwise copy (torch.neg) three times: a "
                          "known-size kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -457,7 +484,11 @@ def main():
     print(f"[bench] setting up {wl.name}: B={wl.B} T={wl.T} rows={wl.total_rows} replicas={R}",
           file=sys.stderr, flush=True)
     t_setup = time.perf_counter()
-    dw = dsa_harness.DeviceWorkload(wl, replicas=R, out_dtype=torch.bfloat16)
+    int8 = args.pools == "int8"
+    share = args.share if args.share is not None else (4 if wl.name.endswith("_mtp") else 1)
+    dw = dsa_harness.DeviceWorkload(wl, replicas=R, out_dtype=torch.bfloat16, pool_format=args.pools, share=share)
+    if int8 and not dw.fast_supported():
+        raise SystemExit("--pools int8 covers decode workloads of at most 64 queries and 65,536 pools per sequence")
     print(f"[bench] setup {time.perf_counter() - t_setup:.1f} s; stages {dw.timed_stages()}",
           file=sys.stderr, flush=True)
     if args.calibrate_copy:
@@ -472,7 +503,7 @@ def main():
     stages = stage_breakdown(dw, R, min(steps, 50 if not prefill else 5))
     value = wl.T / (ms_step * 1e-3)
     line = {
-        "metric": METRICS[wl.name],
+        "metric": METRICS[wl.name] + ("; INT8 pool cache" if int8 else ""),
         "value": round(value, 1),
         "unit": "tok/s" if prefill else "tok-steps/s",
         "n_gpus": 1,
@@ -488,7 +519,7 @@ def main():
                    "context_cap": int(wl.row_base[1] - wl.row_base[0]) if wl.B > 1 else int(wl.seq_len[0]),
                    "valid_tokens": [int(a - b) for a, b in zip(wl.seq_len, wl.first_valid)][:16],
                    "mla_heads": wl.dims.mla_heads, "index_topk": wl.dims.index_topk,
-                   "out_width": wl.dims.out_width, "replicas": R},
+                   "out_width": wl.dims.out_width, "replicas": R, "pool_cache": args.pools, "share": share},
         "step_us": {"mean": round(ms_step * 1e3, 2), "median": round(_pct(per_step_us, 50), 2),
                     "p10": round(_pct(per_step_us, 10), 2), "p90": round(_pct(per_step_us, 90), 2),
                     "samples": len(per_step_us), "steps_per_sample": R if not prefill else 1},
@@ -524,7 +555,7 @@ def main():
             "avg_launch_us": round(attn_us if dom_attn else score_us, 1)}
         line["kernels"] = kernels
     else:
-        ab = algorithmic_bytes(wl)
+        ab = algorithmic_bytes(wl, 132 if int8 else 256, share)
         fast = dw.fast_supported()
         kern_bytes = ab["scores_kernel"] if fast else ab["scores_kernel"] - (ab["step"] - ab["decode_kernel"])
         own_mean, own_median, burst = scoring_launch_us(dw, R, 4 * R)
@@ -532,17 +563,21 @@ def main():
         line["pct_hbm_peak"] = round(100.0 * ab["step"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)
         line["bytes_per_step"] = ab["step"]
         line["roofline"] = {
-            "kernel": ("append_scores_groups (k_scores_groups<true, 512>)" if fast else
-                       "index_scores_select (k_scores_groups<false, 0>)"),
+            "kernel": ("append_scores_groups_shared (k_scores_runs<true, 512, %s>)" % ("true" if int8 else "false")
+                       if share > 1 else
+                       "append_scores_groups_int8 (k_scores_groups<true, 512, true>)" if int8 else
+                       "append_scores_groups (k_scores_groups<true, 512, false>)" if fast else
+                       "index_scores_select (k_scores_groups<false, 0, false>)"),
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic_from_profile(PMC_SUMMARY, SCORES_SRC) if wl.name == WORKLOAD and fast else None,
+            "traffic": (traffic_from_profile(PMC_SUMMARY, SCORES_SRC)
+                        if wl.name == WORKLOAD and fast and not int8 and share == 1 else None),
             "algorithmic_bytes_per_launch": kern_bytes, "avg_launch_us": round(own_mean, 2),
             "median_launch_us": round(own_median, 2), "avg_launch_us_burst": round(burst, 2),
             "frac_of_copy": round(achieved / copy_gbs, 4)}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(wl, max_queries=32 if prefill else None)
+        line["cpu_baseline"] = cpu_baseline(wl, max_queries=32 if prefill else None, int8=int8)
     print(json.dumps(line), flush=True)
 
 

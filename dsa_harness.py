@@ -33,8 +33,12 @@ class DeviceWorkload:
 
     def __init__(self, wl: syn.Workload, device="cuda", replicas: int = 1, score_stride: int | None = None,
                  out_dtype=torch.float32, num_splits: int = 0, build: bool = True, gen_workers: int = 8,
-                 canary: int | None = None, prefill_chunk: int = 512):
+                 canary: int | None = None, prefill_chunk: int = 512, pool_format: str = "bf16", share: int = 1):
         self.wl = wl
+        self.share = share              # > 1: runs of consecutive queries of a sequence share the pool pass
+        if pool_format not in ("bf16", "int8"):
+            raise ValueError(pool_format)
+        self.int8 = pool_format == "int8"
         self.prefill_chunk = prefill_chunk
         self.ws_chunk = None
         self.device = torch.device(device)
@@ -55,8 +59,14 @@ class DeviceWorkload:
         fill = canary if canary is not None else 0
         self.caches = [torch.full((rows, d.row_bytes), fill, dtype=torch.int8, device=dev)
                        for _ in range(replicas)]
-        self.pools = [torch.zeros((npools, d.idx_dim), dtype=torch.bfloat16, device=dev)
-                      for _ in range(replicas)]
+        if self.int8:
+            # INT8 pool cache: code rows and one fp32 scale per pool
+            self.pool_codes = [torch.zeros((npools, d.idx_dim), dtype=torch.int8, device=dev) for _ in range(replicas)]
+            self.pool_scales = [torch.zeros(npools, dtype=torch.float32, device=dev) for _ in range(replicas)]
+            self.pools = None
+        else:
+            self.pools = [torch.zeros((npools, d.idx_dim), dtype=torch.bfloat16, device=dev)
+                          for _ in range(replicas)]
         self.k = torch.zeros((toks, d.idx_dim), dtype=torch.bfloat16, device=dev)
         self.gate = torch.zeros((toks, d.idx_dim), dtype=torch.bfloat16, device=dev)
         lw, lb = syn.gen_ln(wl)
@@ -107,7 +117,7 @@ class DeviceWorkload:
     def build_caches(self):
         """Store every position's INT8 row and build every complete pool (replica 0, then copies)."""
         wl, d, dev = self.wl, self.wl.dims, self.device
-        cache, pools = self.caches[0], self.pools[0]
+        cache = self.caches[0]
         for b in range(wl.B):
             n = int(wl.seq_len[b])
             rb, tb = int(wl.row_base[b]), int(wl.tok_base[b])
@@ -120,12 +130,21 @@ class DeviceWorkload:
                 self.gate[tb + x0: tb + x0 + g.shape[0]] = _bits_to_bf16(g, dev)
         ends = [wl.n_pools(b) for b in range(wl.B)]
         if max(ends) > 0:
-            dsa.index_pools(self.dims, self.k, self.gate, self.ln_w, self.ln_b, self.seqs,
-                            torch.zeros(wl.B, dtype=torch.int32, device=dev),
-                            torch.tensor(ends, dtype=torch.int32, device=dev), max(ends), pools)
+            begin = torch.zeros(wl.B, dtype=torch.int32, device=dev)
+            end = torch.tensor(ends, dtype=torch.int32, device=dev)
+            if self.int8:
+                dsa.index_pools_int8(self.dims, self.k, self.gate, self.ln_w, self.ln_b, self.seqs, begin, end,
+                                     max(ends), self.pool_codes[0], self.pool_scales[0])
+            else:
+                dsa.index_pools(self.dims, self.k, self.gate, self.ln_w, self.ln_b, self.seqs, begin, end,
+                                max(ends), self.pools[0])
         for r in range(1, len(self.caches)):
             self.caches[r].copy_(cache)
-            self.pools[r].copy_(pools)
+            if self.int8:
+                self.pool_codes[r].copy_(self.pool_codes[0])
+                self.pool_scales[r].copy_(self.pool_scales[0])
+            else:
+                self.pools[r].copy_(self.pools[0])
         torch.cuda.synchronize()
 
     # ------------------------------------------------------------------ the step
@@ -135,6 +154,10 @@ class DeviceWorkload:
         return dsa.store_int8(self.dims, self.latent_q, self.slots_q, self.caches[r], prepare=prepare)
 
     def step_pools(self, r: int = 0, prepare: bool = False):
+        if self.step_max_pools > 0 and self.int8:
+            return dsa.index_pools_int8(self.dims, self.k, self.gate, self.ln_w, self.ln_b, self.seqs,
+                                        self.step_pool_begin, self.step_pool_end, self.step_max_pools,
+                                        self.pool_codes[r], self.pool_scales[r], prepare=prepare)
         if self.step_max_pools > 0:
             return dsa.index_pools(self.dims, self.k, self.gate, self.ln_w, self.ln_b, self.seqs,
                                    self.step_pool_begin, self.step_pool_end, self.step_max_pools, self.pools[r],
@@ -144,13 +167,16 @@ class DeviceWorkload:
     def step_append(self, r: int = 0, prepare: bool = False):
         """The step's new tokens (INT8 rows and completed pools) in one launch
         (two calls when the latent rows and the indexer keys differ in dtype)."""
-        if self.latent_q.dtype != self.k.dtype:
+        if self.latent_q.dtype != self.k.dtype or self.int8:
             return [self.step_store(r, prepare), self.step_pools(r, prepare)]
         return dsa.append_tokens(self.dims, self.latent_q, self.slots_q, self.caches[r], self.k, self.gate,
                                  self.ln_w, self.ln_b, self.seqs, self.step_pool_begin, self.step_pool_end,
                                  self.step_max_pools, self.pools[r], prepare=prepare)
 
     def step_scores(self, r: int = 0, prepare: bool = False):
+        if self.int8:
+            return dsa.index_scores_int8(self.dims, self.q_idx, self.w, self.pool_codes[r], self.pool_scales[r],
+                                         self.seqs, self.q_seq, self.q_pos, self.scores, prepare=prepare)
         return dsa.index_scores(self.dims, self.q_idx, self.w, self.pools[r], self.seqs, self.q_seq, self.q_pos,
                                 self.scores, prepare=prepare)
 
@@ -172,11 +198,28 @@ class DeviceWorkload:
         return self.ws_ss
 
     def step_scores_groups(self, r: int = 0, prepare: bool = False):
+        if self.int8:
+            return dsa.index_scores_groups_int8(self.dims, self.q_idx, self.w, self.pool_codes[r],
+                                                self.pool_scales[r], self.seqs, self.q_seq, self.q_pos, self.scores,
+                                                self._ws_ss(), prepare=prepare)
         return dsa.index_scores_groups(self.dims, self.q_idx, self.w, self.pools[r], self.seqs, self.q_seq,
                                        self.q_pos, self.scores, self._ws_ss(), prepare=prepare)
 
     def step_append_scores(self, r: int = 0, prepare: bool = False):
         """The new tokens and the scoring pass with group lists (one launch for bf16 tokens)."""
+        if self.share > 1:
+            return dsa.append_scores_groups_shared(
+                self.dims, self.latent_q, self.slots_q, self.caches[r], self.k, self.gate, self.ln_w, self.ln_b,
+                self.step_pool_begin, self.step_pool_end, self.step_max_pools,
+                self.pool_codes[r] if self.int8 else self.pools[r], self.pool_scales[r] if self.int8 else None,
+                self.q_idx, self.w, self.seqs, self.q_seq, self.q_pos, self.scores, self._ws_ss(), self.share,
+                prepare=prepare)
+        if self.int8:
+            return dsa.append_scores_groups_int8(self.dims, self.latent_q, self.slots_q, self.caches[r], self.k,
+                                                 self.gate, self.ln_w, self.ln_b, self.step_pool_begin,
+                                                 self.step_pool_end, self.step_max_pools, self.pool_codes[r],
+                                                 self.pool_scales[r], self.q_idx, self.w, self.seqs, self.q_seq,
+                                                 self.q_pos, self.scores, self._ws_ss(), prepare=prepare)
         if self.latent_q.dtype != self.k.dtype:
             return [self.step_store(r, prepare), self.step_pools(r, prepare), self.step_scores_groups(r, prepare)]
         return dsa.append_scores_groups(self.dims, self.latent_q, self.slots_q, self.caches[r], self.k, self.gate,
@@ -196,6 +239,8 @@ class DeviceWorkload:
 
     def step_scores_select(self, r: int = 0, prepare: bool = False):
         """Scores, selection and expansion (dsa_index_scores_select: two launches for decode)."""
+        if self.int8:
+            return [self.step_scores_groups(r, prepare), self.step_select_groups(r, prepare)]
         return dsa.index_scores_select(self.dims, self.q_idx, self.w, self.pools[r], self.seqs, self.q_seq,
                                        self.q_pos, self.scores, self.indices, pool_ids=self.pool_ids,
                                        workspace=self._ws_ss(), prepare=prepare)
@@ -248,7 +293,7 @@ class DeviceWorkload:
     def fast_supported(self) -> bool:
         """Group lists are kept for at most 64 queries of at most 65,536 pools."""
         return self.wl.T <= 64 and self.stride <= 65536 and self.wl.dims.idx_heads == 32 and \
-            self.wl.dims.idx_dim == 128
+            self.wl.dims.idx_dim == 128 and (not self.int8 or self.latent_q.dtype == torch.bfloat16)
 
     def step_fast(self, r: int = 0):
         """One decode step through exactly the launches the bench times."""

@@ -401,6 +401,34 @@ def mini_heavy(seed: int = 13) -> Workload:
                np.arange(3), np.array(sl) - 1, latent_dist="t3")
 
 
+def _with_drafts(wl: Workload, name: str, k: int = 4, note: str = "") -> Workload:
+    """The same sequences, each issuing k queries at its last k positions (a
+    speculative decode step: the accepted token and k - 1 drafts, scored
+    together), queries of one sequence consecutive."""
+    qs, qp = [], []
+    for b in range(wl.B):
+        for i in range(k):
+            qs.append(b)
+            qp.append(int(wl.seq_len[b]) - k + i)
+    return dataclasses.replace(wl, name=name, q_seq=np.asarray(qs, dtype=np.int32),
+                               q_pos=np.asarray(qp, dtype=np.int32), note=note)
+
+
+def mini_mtp(seed: int = 15) -> Workload:
+    """mini_decode's sequences with 4 queries each at their last 4 positions."""
+    fv = [0, 1, 3, 2]
+    v = [4096, 3001, 2050, 517]
+    sl = [a + b for a, b in zip(fv, v)]
+    base = _mk("mini_mtp", seed, production_dims(16), fv, sl, 4100, 1025, [0], [0])
+    return _with_drafts(base, "mini_mtp", 4, "4 queries per sequence (1 + 3 drafts)")
+
+
+def decode_262k_b8_mtp(seed: int = 2) -> Workload:
+    """decode_262k_b8's eight ragged sequences, each issuing 4 queries (the
+    accepted token and 3 drafts) at its last 4 positions: 32 queries."""
+    return _with_drafts(decode_262k_b8(seed), "decode_262k_b8_mtp", 4, "4 queries per sequence (1 + 3 drafts)")
+
+
 WORKLOADS = {
     "tiny": tiny, "tiny_seven": tiny_seven, "tiny_padded_six": tiny_padded_six,
     "tiny_batch": tiny_batch,
@@ -408,7 +436,7 @@ WORKLOADS = {
     "decode_262k_b8_full": decode_262k_b8_full,
     "prefill_4k_on_131k": prefill_4k_on_131k, "decode_1m_b4": decode_1m_b4,
     "mini_decode": mini_decode, "mini_decode_64": mini_decode_64, "mini_prefill": mini_prefill,
-    "mini_heavy": mini_heavy,
+    "mini_heavy": mini_heavy, "mini_mtp": mini_mtp, "decode_262k_b8_mtp": decode_262k_b8_mtp,
 }
 
 

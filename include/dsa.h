@@ -262,10 +262,11 @@ int dsa_append_scores_groups(const dsa_dims* dims, int dtype, const void* latent
                              int32_t score_stride, float* scores, void* workspace, size_t workspace_bytes,
                              void* stream);
 /*
- * time_next_scoring_launch -- measurement hook.  The next decode scoring
- * launch made on the calling thread (by dsa_append_scores_groups,
- * dsa_index_scores_groups, dsa_index_scores_select, or dsa_index_scores with
- * T <= 64 and 32 x 128 indexer heads) records start_event
+ * time_next_scoring_launch -- measurement hook.  The next scoring launch
+ * made on the calling thread for 32 x 128 indexer heads (by
+ * dsa_append_scores_groups, dsa_index_scores_groups, dsa_index_scores_select,
+ * dsa_index_scores, dsa_index_select_chunked or their INT8-pool forms)
+ * records start_event
  * when the kernel starts and stop_event when it ends (hipExtLaunchKernel),
  * so that hipEventElapsedTime gives the kernel's own duration, without the
  * gap between launches.  One-shot; both NULL cancels.  The events are HIP
@@ -278,6 +279,86 @@ int dsa_index_scores_select(const dsa_dims* dims, const uint16_t* q_idx, const f
                             const int32_t* q_seq, const int32_t* q_pos, int32_t T,
                             int32_t score_stride, float* scores, int32_t* pool_ids, int32_t* indices,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * INT8 pool cache -- [Flash] What is quantized (the indexer state cache row:
+ * the sibling port stores its indexer cache as INT8 with one FP32 scale per
+ * row).  A pool is kept as idx_dim INT8 codes (one row of idx_dim bytes) and
+ * one fp32 scale, 132 bytes per pool instead of 256 in bf16.  The codes and
+ * the scale are those of dsa_store_int8's quantiser applied to the pool's
+ * fp32 state (amax over the row floored at 1e-4, s = amax / 127 in IEEE
+ * fp32, round half to even, +-127); there is no bf16 step in between.
+ * Scores are computed on the dequantised pools:
+ *   scores[t][p] = sum_h w[t][h] * max(0, q_idx[t][h] . (scale[p] * code[p]))
+ * (as s * sum_h w[h] * relu(q . code), bf16 products and fp32 sums), -inf
+ * past the visible pools, exactly as dsa_index_scores lays them out.
+ *
+ * index_pools_int8 -- dsa_index_pools in the INT8 form.
+ *   k .. max_pools  as dsa_index_pools
+ *   pool_codes   device int8 [*, idx_dim], row pool_base[b] + p; 16-byte aligned
+ *   pool_scales  device fp32 [*], same rows
+ *   pools_f32    device fp32 [*, idx_dim] or NULL: when set, also receives
+ *                each pool's fp32 values before quantisation (for checks)
+ * Supported: kpool 4, idx_dim in {32, 128}.
+ */
+int dsa_index_pools_int8(const dsa_dims* dims, const void* k, const void* gate, int kg_dtype,
+                         const float* ln_w, const float* ln_b, const dsa_seqs* seqs, int32_t num_seqs,
+                         const int32_t* pool_begin, const int32_t* pool_end, int32_t max_pools,
+                         int8_t* pool_codes, float* pool_scales, float* pools_f32, void* stream);
+/*
+ * index_scores_int8 / index_scores_groups_int8 / append_scores_groups_int8 --
+ * dsa_index_scores, dsa_index_scores_groups and dsa_append_scores_groups over
+ * INT8 pools (pool_codes, pool_scales in place of the bf16 pools; the new
+ * tokens' pools are built in the INT8 form).  The group lists in the
+ * workspace are those the selection calls read (dsa_topk_select_groups,
+ * dsa_topk_sparse_mla), with the same workspace size.  In the single launch,
+ * a pool the step completes is built, quantised and scored by the wave that
+ * scores its group, so its score is the one a separate scoring pass over the
+ * stored pool gives.
+ * Supported: idx_heads 32, idx_dim 128, kpool 4, T <= 64; bf16 new tokens
+ * for the single launch; else DSA_ERR_UNSUPPORTED.
+ */
+int dsa_index_scores_int8(const dsa_dims* dims, const uint16_t* q_idx, const float* w,
+                          const int8_t* pool_codes, const float* pool_scales, const dsa_seqs* seqs,
+                          int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos, int32_t T,
+                          int32_t score_stride, float* scores, void* stream);
+int dsa_index_scores_groups_int8(const dsa_dims* dims, const uint16_t* q_idx, const float* w,
+                                 const int8_t* pool_codes, const float* pool_scales, const dsa_seqs* seqs,
+                                 int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos, int32_t T,
+                                 int32_t score_stride, float* scores, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+int dsa_append_scores_groups_int8(const dsa_dims* dims, int dtype, const void* latent, int64_t n, int64_t ld,
+                                  const int64_t* slots, int8_t* cache, int64_t cache_rows, const void* k,
+                                  const void* gate, const float* ln_w, const float* ln_b,
+                                  const int32_t* pool_begin, const int32_t* pool_end, int32_t max_pools,
+                                  int8_t* pool_codes, float* pool_scales, const uint16_t* q_idx, const float* w,
+                                  const dsa_seqs* seqs, int32_t num_seqs, const int32_t* q_seq,
+                                  const int32_t* q_pos, int32_t T, int32_t score_stride, float* scores,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * append_scores_groups_shared -- dsa_append_scores_groups (pool_scales NULL:
+ * bf16 pools) or dsa_append_scores_groups_int8 (pool_scales set: `pools`
+ * holds the INT8 code rows) for batches whose queries come in runs of one
+ * sequence, as in a speculative decode step that scores the accepted token
+ * and its drafts together ([Flash] Deployment target: MTP with 3 speculative
+ * tokens; Stream C: indexer_share_mtp).  Consecutive queries with the same
+ * q_seq form runs of at most `share` (1 .. 4); the pools of a run's sequence
+ * are read once for the whole run instead of once per query.  Results
+ * (cache rows, pools, scores, group lists) are bit for bit those of the
+ * one-query call; share == 1 is that call.  Arguments as
+ * dsa_append_scores_groups, plus pool_scales and share; n == 0 and
+ * max_pools == 0 score only.
+ * Supported: what dsa_append_scores_groups_int8 supports (bf16 new tokens).
+ */
+int dsa_append_scores_groups_shared(const dsa_dims* dims, int dtype, const void* latent, int64_t n, int64_t ld,
+                                    const int64_t* slots, int8_t* cache, int64_t cache_rows, const void* k,
+                                    const void* gate, const float* ln_w, const float* ln_b,
+                                    const int32_t* pool_begin, const int32_t* pool_end, int32_t max_pools,
+                                    void* pools, float* pool_scales, const uint16_t* q_idx, const float* w,
+                                    const dsa_seqs* seqs, int32_t num_seqs, const int32_t* q_seq,
+                                    const int32_t* q_pos, int32_t T, int32_t score_stride, float* scores,
+                                    void* workspace, size_t workspace_bytes, int32_t share, void* stream);
 
 /*
  * index_select_chunked -- index_scores and topk_select_expand for many

@@ -118,6 +118,15 @@ def lib() -> ctypes.CDLL:
             "dsa_time_next_scoring_launch": (ctypes.c_int, [P, P]),
             "dsa_decode_step_workspace_bytes": (SZ, [DP, I32, I32]),
             "dsa_decode_step_status": (ctypes.c_int, [P, SZ, P]),
+            "dsa_index_pools_int8": (ctypes.c_int, [DP, P, P, ctypes.c_int, P, P, SP, I32, P, P, I32, P, P, P, P]),
+            "dsa_index_scores_int8": (ctypes.c_int, [DP, P, P, P, P, SP, I32, P, P, I32, I32, P, P]),
+            "dsa_index_scores_groups_int8": (ctypes.c_int, [DP, P, P, P, P, SP, I32, P, P, I32, I32, P, P, SZ, P]),
+            "dsa_append_scores_groups_int8": (ctypes.c_int, [DP, ctypes.c_int, P, I64, I64, P, P, I64, P, P, P, P, P,
+                                                             P, I32, P, P, P, P, SP, I32, P, P, I32, I32, P, P, SZ,
+                                                             P]),
+            "dsa_append_scores_groups_shared": (ctypes.c_int, [DP, ctypes.c_int, P, I64, I64, P, P, I64, P, P, P, P, P,
+                                                               P, I32, P, P, P, P, SP, I32, P, P, I32, I32, P, P, SZ,
+                                                               I32, P]),
             "dsa_index_select_chunked_workspace_bytes": (SZ, [DP, I32, I32]),
             "dsa_index_select_chunked": (ctypes.c_int, [DP, P, P, P, SP, I32, P, P, I32, I32, I32, P, P, P, SZ, P]),
             "dsa_sparse_mla_noalloc_scratch_bytes": (SZ, []),
@@ -394,6 +403,114 @@ def sparse_mla_noalloc(dims: Dims, q: torch.Tensor, cache: torch.Tensor, indices
                  q.shape[0], float(scale), out.data_ptr(), _dt(out), _ptr(lse), int(num_splits), _stream(stream))
 
 
+def index_pools_int8(dims: Dims, k: torch.Tensor, gate: torch.Tensor, ln_w: torch.Tensor, ln_b: torch.Tensor,
+                     seqs: Seqs, pool_begin: torch.Tensor, pool_end: torch.Tensor, max_pools: int,
+                     codes: torch.Tensor, scales: torch.Tensor, pools_f32: torch.Tensor | None = None, stream=None,
+                     prepare: bool = False):
+    """Pools [pool_begin, pool_end) of each sequence as INT8 code rows [*, Di] and fp32 scales [*]."""
+    if k.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("k must be bf16 or fp32")
+    _check(k, k.dtype, "k")
+    _check(gate, k.dtype, "gate")
+    _check(ln_w, torch.float32, "ln_w")
+    _check(ln_b, torch.float32, "ln_b")
+    _check(pool_begin, torch.int32, "pool_begin")
+    _check(pool_end, torch.int32, "pool_end")
+    _check(codes, torch.int8, "codes")
+    _check(scales, torch.float32, "scales")
+    if pools_f32 is not None:
+        _check(pools_f32, torch.float32, "pools_f32")
+    return _call("dsa_index_pools_int8", prepare, ctypes.byref(dims), k.data_ptr(), gate.data_ptr(), _dt(k),
+                 ln_w.data_ptr(), ln_b.data_ptr(), ctypes.byref(seqs._c()), seqs.num_seqs, pool_begin.data_ptr(),
+                 pool_end.data_ptr(), int(max_pools), codes.data_ptr(), scales.data_ptr(), _ptr(pools_f32),
+                 _stream(stream))
+
+
+def index_scores_int8(dims: Dims, q_idx: torch.Tensor, w: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                      seqs: Seqs, q_seq: torch.Tensor, q_pos: torch.Tensor, scores: torch.Tensor, stream=None,
+                      prepare: bool = False):
+    """scores [T, stride] over INT8 pools (codes [*, Di] int8, scales [*] fp32)."""
+    for t, dt, n in ((q_idx, torch.bfloat16, "q_idx"), (w, torch.float32, "w"), (codes, torch.int8, "codes"),
+                     (scales, torch.float32, "scales"), (q_seq, torch.int32, "q_seq"), (q_pos, torch.int32, "q_pos"),
+                     (scores, torch.float32, "scores")):
+        _check(t, dt, n)
+    return _call("dsa_index_scores_int8", prepare, ctypes.byref(dims), q_idx.data_ptr(), w.data_ptr(),
+                 codes.data_ptr(), scales.data_ptr(), ctypes.byref(seqs._c()), seqs.num_seqs, q_seq.data_ptr(),
+                 q_pos.data_ptr(), q_seq.shape[0], scores.shape[1], scores.data_ptr(), _stream(stream))
+
+
+def index_scores_groups_int8(dims: Dims, q_idx: torch.Tensor, w: torch.Tensor, codes: torch.Tensor,
+                             scales: torch.Tensor, seqs: Seqs, q_seq: torch.Tensor, q_pos: torch.Tensor,
+                             scores: torch.Tensor, workspace: torch.Tensor, stream=None, prepare: bool = False):
+    """index_scores_int8 that also keeps each 64-pool group's best pools in the workspace."""
+    for t, dt, n in ((q_idx, torch.bfloat16, "q_idx"), (w, torch.float32, "w"), (codes, torch.int8, "codes"),
+                     (scales, torch.float32, "scales"), (q_seq, torch.int32, "q_seq"), (q_pos, torch.int32, "q_pos"),
+                     (scores, torch.float32, "scores")):
+        _check(t, dt, n)
+    _check(workspace, workspace.dtype, "workspace")
+    return _call("dsa_index_scores_groups_int8", prepare, ctypes.byref(dims), q_idx.data_ptr(), w.data_ptr(),
+                 codes.data_ptr(), scales.data_ptr(), ctypes.byref(seqs._c()), seqs.num_seqs, q_seq.data_ptr(),
+                 q_pos.data_ptr(), q_seq.shape[0], scores.shape[1], scores.data_ptr(), workspace.data_ptr(),
+                 workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def append_scores_groups_int8(dims: Dims, latent: torch.Tensor, slots: torch.Tensor, cache: torch.Tensor,
+                              k: torch.Tensor, gate: torch.Tensor, ln_w: torch.Tensor, ln_b: torch.Tensor,
+                              pool_begin: torch.Tensor, pool_end: torch.Tensor, max_pools: int, codes: torch.Tensor,
+                              scales: torch.Tensor, q_idx: torch.Tensor, w: torch.Tensor, seqs: Seqs,
+                              q_seq: torch.Tensor, q_pos: torch.Tensor, scores: torch.Tensor, workspace: torch.Tensor,
+                              stream=None, prepare: bool = False):
+    """The new tokens (INT8 rows; pools in the INT8 form) and the scoring pass with group lists, one launch."""
+    for t, dt, n in ((latent, torch.bfloat16, "latent"), (slots, torch.int64, "slots"), (cache, torch.int8, "cache"),
+                     (k, torch.bfloat16, "k"), (gate, torch.bfloat16, "gate"), (ln_w, torch.float32, "ln_w"),
+                     (ln_b, torch.float32, "ln_b"), (pool_begin, torch.int32, "pool_begin"),
+                     (pool_end, torch.int32, "pool_end"), (codes, torch.int8, "codes"),
+                     (scales, torch.float32, "scales"), (q_idx, torch.bfloat16, "q_idx"), (w, torch.float32, "w"),
+                     (q_seq, torch.int32, "q_seq"), (q_pos, torch.int32, "q_pos"), (scores, torch.float32, "scores")):
+        _check(t, dt, n)
+    _check(workspace, workspace.dtype, "workspace")
+    return _call("dsa_append_scores_groups_int8", prepare, ctypes.byref(dims), DSA_BF16, latent.data_ptr(),
+                 latent.shape[0], latent.stride(0), slots.data_ptr(), cache.data_ptr(), cache.shape[0], k.data_ptr(),
+                 gate.data_ptr(), ln_w.data_ptr(), ln_b.data_ptr(), pool_begin.data_ptr(), pool_end.data_ptr(),
+                 int(max_pools), codes.data_ptr(), scales.data_ptr(), q_idx.data_ptr(), w.data_ptr(),
+                 ctypes.byref(seqs._c()), seqs.num_seqs, q_seq.data_ptr(), q_pos.data_ptr(), q_seq.shape[0],
+                 scores.shape[1], scores.data_ptr(), workspace.data_ptr(),
+                 workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def append_scores_groups_shared(dims: Dims, latent: torch.Tensor | None, slots: torch.Tensor | None,
+                                cache: torch.Tensor | None, k: torch.Tensor, gate: torch.Tensor, ln_w: torch.Tensor,
+                                ln_b: torch.Tensor, pool_begin: torch.Tensor, pool_end: torch.Tensor, max_pools: int,
+                                pools: torch.Tensor, pool_scales: torch.Tensor | None, q_idx: torch.Tensor,
+                                w: torch.Tensor, seqs: Seqs, q_seq: torch.Tensor, q_pos: torch.Tensor,
+                                scores: torch.Tensor, workspace: torch.Tensor, share: int, stream=None,
+                                prepare: bool = False):
+    """New tokens and scoring with group lists where runs of up to `share`
+    consecutive queries of one sequence read its pools once (pools bf16, or
+    INT8 codes when pool_scales is given)."""
+    for t, dt, nm in ((k, torch.bfloat16, "k"), (gate, torch.bfloat16, "gate"), (ln_w, torch.float32, "ln_w"),
+                      (ln_b, torch.float32, "ln_b"), (pool_begin, torch.int32, "pool_begin"),
+                      (pool_end, torch.int32, "pool_end"), (q_idx, torch.bfloat16, "q_idx"), (w, torch.float32, "w"),
+                      (q_seq, torch.int32, "q_seq"), (q_pos, torch.int32, "q_pos"), (scores, torch.float32, "scores")):
+        _check(t, dt, nm)
+    _check(pools, torch.int8 if pool_scales is not None else torch.bfloat16, "pools")
+    if pool_scales is not None:
+        _check(pool_scales, torch.float32, "pool_scales")
+    _check(workspace, workspace.dtype, "workspace")
+    n = 0 if latent is None else latent.shape[0]
+    if n:
+        _check(latent, torch.bfloat16, "latent")
+        _check(slots, torch.int64, "slots")
+        _check(cache, torch.int8, "cache")
+    return _call("dsa_append_scores_groups_shared", prepare, ctypes.byref(dims), DSA_BF16, _ptr(latent) if n else None,
+                 n, latent.stride(0) if n else 0, _ptr(slots) if n else None, _ptr(cache) if n else None,
+                 cache.shape[0] if n else 0, k.data_ptr(), gate.data_ptr(), ln_w.data_ptr(), ln_b.data_ptr(),
+                 pool_begin.data_ptr(), pool_end.data_ptr(), int(max_pools), pools.data_ptr(), _ptr(pool_scales),
+                 q_idx.data_ptr(), w.data_ptr(), ctypes.byref(seqs._c()), seqs.num_seqs, q_seq.data_ptr(),
+                 q_pos.data_ptr(), q_seq.shape[0], scores.shape[1], scores.data_ptr(), workspace.data_ptr(),
+                 workspace.numel() * workspace.element_size(), int(share), _stream(stream))
+
+
 def index_select_chunked_workspace(dims: Dims, chunk: int, score_stride: int, device="cuda") -> torch.Tensor:
     n = int(lib().dsa_index_select_chunked_workspace_bytes(ctypes.byref(dims), int(chunk), int(score_stride)))
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
@@ -609,5 +726,6 @@ __all__ = [
     "index_scores_select_workspace", "index_scores_select", "index_scores_groups", "topk_select_groups",
     "decode_step_workspace_bytes", "decode_step_workspace", "decode_step_error", "decode_step",
     "sparse_mla_noalloc_scratch_bytes", "sparse_mla_noalloc", "index_select_chunked_workspace",
-    "index_select_chunked",
+    "index_select_chunked", "index_pools_int8", "index_scores_int8", "index_scores_groups_int8",
+    "append_scores_groups_int8", "append_scores_groups_shared",
 ]

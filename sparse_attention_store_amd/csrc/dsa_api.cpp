@@ -316,6 +316,167 @@ int dsa_append_scores_groups(const dsa_dims* dims, int dtype, const void* latent
         pool_end, max_pools, pools, q_idx, w, q_seq, q_pos, T, score_stride, scores, workspace, s));
 }
 
+// ------------------------------------------------------------------ INT8 pool cache
+
+int dsa_index_pools_int8(const dsa_dims* dims, const void* k, const void* gate, int kg_dtype, const float* ln_w,
+                         const float* ln_b, const dsa_seqs* seqs, int32_t num_seqs, const int32_t* pool_begin,
+                         const int32_t* pool_end, int32_t max_pools, int8_t* pool_codes, float* pool_scales,
+                         float* pools_f32, void* stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (kg_dtype != DSA_F32 && kg_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    if (dims->kpool != 4 || (dims->idx_dim != 128 && dims->idx_dim != 32)) return DSA_ERR_UNSUPPORTED;
+    st = check_seqs(seqs, num_seqs, false, true, true);
+    if (st) return st;
+    if (max_pools < 0) return DSA_ERR_SIZE;
+    if (max_pools == 0) return DSA_OK;
+    if (num_seqs > 65535) return DSA_ERR_SIZE;
+    if (!k || !gate || !ln_w || !ln_b || !pool_begin || !pool_end || !pool_codes || !pool_scales) return DSA_ERR_NULL;
+    if (!aligned(pool_codes, 16) || !aligned(pool_scales, 4) || !aligned(pools_f32, 4)) return DSA_ERR_ALIGN;
+    return hip_status(dsa_host::launch_index_pools_int8(*dims, k, gate, kg_dtype, ln_w, ln_b, *seqs, num_seqs,
+                                                        pool_begin, pool_end, max_pools, pool_codes, pool_scales,
+                                                        pools_f32, as_stream(stream)));
+}
+
+static bool int8_scoring_supported(const dsa_dims* d, int32_t T) {
+    return d->idx_heads == 32 && d->idx_dim == 128 && d->kpool == 4 && T <= 64;
+}
+
+int dsa_index_scores_int8(const dsa_dims* dims, const uint16_t* q_idx, const float* w, const int8_t* pool_codes,
+                          const float* pool_scales, const dsa_seqs* seqs, int32_t num_seqs, const int32_t* q_seq,
+                          const int32_t* q_pos, int32_t T, int32_t score_stride, float* scores, void* stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (T < 0 || score_stride < 0) return DSA_ERR_SIZE;
+    st = check_seqs(seqs, num_seqs, false, false, true);
+    if (st) return st;
+    if (!int8_scoring_supported(dims, T)) return DSA_ERR_UNSUPPORTED;
+    if (T == 0 || score_stride == 0) return DSA_OK;
+    if (!q_idx || !w || !pool_codes || !pool_scales || !q_seq || !q_pos || !scores) return DSA_ERR_NULL;
+    if (!aligned(q_idx, 16) || !aligned(w, 16) || !aligned(pool_codes, 16) || !aligned(pool_scales, 4) ||
+        !aligned(scores, 4))
+        return DSA_ERR_ALIGN;
+    return hip_status(dsa_host::launch_index_scores_int8(*dims, q_idx, w, pool_codes, pool_scales, *seqs, num_seqs,
+                                                         q_seq, q_pos, T, score_stride, scores, as_stream(stream)));
+}
+
+int dsa_index_scores_groups_int8(const dsa_dims* dims, const uint16_t* q_idx, const float* w,
+                                 const int8_t* pool_codes, const float* pool_scales, const dsa_seqs* seqs,
+                                 int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos, int32_t T,
+                                 int32_t score_stride, float* scores, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    int st = groups_common(dims, seqs, num_seqs, T, score_stride, workspace, workspace_bytes);
+    if (st || T == 0 || score_stride == 0) return st;
+    if (!q_idx || !w || !pool_codes || !pool_scales || !q_seq || !q_pos || !scores) return DSA_ERR_NULL;
+    if (!aligned(q_idx, 16) || !aligned(w, 16) || !aligned(pool_codes, 16) || !aligned(pool_scales, 4))
+        return DSA_ERR_ALIGN;
+    return hip_status(dsa_host::launch_scores_with_groups_int8(*dims, q_idx, w, pool_codes, pool_scales, *seqs,
+                                                               num_seqs, q_seq, q_pos, T, score_stride, scores,
+                                                               workspace, as_stream(stream)));
+}
+
+int dsa_append_scores_groups_int8(const dsa_dims* dims, int dtype, const void* latent, int64_t n, int64_t ld,
+                                  const int64_t* slots, int8_t* cache, int64_t cache_rows, const void* k,
+                                  const void* gate, const float* ln_w, const float* ln_b, const int32_t* pool_begin,
+                                  const int32_t* pool_end, int32_t max_pools, int8_t* pool_codes, float* pool_scales,
+                                  const uint16_t* q_idx, const float* w, const dsa_seqs* seqs, int32_t num_seqs,
+                                  const int32_t* q_seq, const int32_t* q_pos, int32_t T, int32_t score_stride,
+                                  float* scores, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (dtype != DSA_BF16) return dtype == DSA_F32 ? DSA_ERR_UNSUPPORTED : DSA_ERR_DTYPE;
+    const int D = dims->latent_dim;
+    if (D != 64 && D != 128 && D != 256 && D != 512) return DSA_ERR_UNSUPPORTED;
+    if (n < 0 || cache_rows < 0 || max_pools < 0) return DSA_ERR_SIZE;
+    if (n > 0) {
+        if (!latent || !slots || !cache) return DSA_ERR_NULL;
+        if (ld < D) return DSA_ERR_SIZE;
+        if (!aligned(latent, 16) || (ld * 2) % 16 != 0 || !aligned(cache, 16)) return DSA_ERR_ALIGN;
+    }
+    st = groups_common(dims, seqs, num_seqs, T, score_stride, workspace, workspace_bytes);
+    if (st) return st;
+    if (!int8_scoring_supported(dims, T)) return DSA_ERR_UNSUPPORTED;
+    if (max_pools > 0) {
+        st = check_seqs(seqs, num_seqs, false, true, true);
+        if (st) return st;
+        if (num_seqs > 65535) return DSA_ERR_SIZE;
+        if (!k || !gate || !ln_w || !ln_b || !pool_begin || !pool_end) return DSA_ERR_NULL;
+        if (!aligned(k, 4) || !aligned(gate, 4)) return DSA_ERR_ALIGN;
+    }
+    if (!pool_codes || !pool_scales) return DSA_ERR_NULL;
+    if (!aligned(pool_codes, 16) || !aligned(pool_scales, 4)) return DSA_ERR_ALIGN;
+    const bool scoring = T > 0 && score_stride > 0;
+    if (scoring) {
+        if (!q_idx || !w || !q_seq || !q_pos || !scores) return DSA_ERR_NULL;
+        if (!aligned(q_idx, 16) || !aligned(w, 16)) return DSA_ERR_ALIGN;
+    }
+    if (!scoring && n == 0 && max_pools == 0) return DSA_OK;
+    const dsa_seqs none{};
+    return hip_status(dsa_host::launch_append_scores_groups_int8(
+        *dims, latent, n, ld, slots, cache, k, gate, ln_w, ln_b, num_seqs > 0 && seqs ? *seqs : none, num_seqs,
+        pool_begin, pool_end, max_pools, pool_codes, pool_scales, q_idx, w, q_seq, q_pos, scoring ? T : 0,
+        scoring ? score_stride : 0, scores, workspace, as_stream(stream)));
+}
+
+int dsa_append_scores_groups_shared(const dsa_dims* dims, int dtype, const void* latent, int64_t n, int64_t ld,
+                                    const int64_t* slots, int8_t* cache, int64_t cache_rows, const void* k,
+                                    const void* gate, const float* ln_w, const float* ln_b, const int32_t* pool_begin,
+                                    const int32_t* pool_end, int32_t max_pools, void* pools, float* pool_scales,
+                                    const uint16_t* q_idx, const float* w, const dsa_seqs* seqs, int32_t num_seqs,
+                                    const int32_t* q_seq, const int32_t* q_pos, int32_t T, int32_t score_stride,
+                                    float* scores, void* workspace, size_t workspace_bytes, int32_t share,
+                                    void* stream) {
+    if (share < 1 || share > 4) return DSA_ERR_SIZE;
+    if (share == 1) {
+        if (pool_scales)
+            return dsa_append_scores_groups_int8(dims, dtype, latent, n, ld, slots, cache, cache_rows, k, gate, ln_w,
+                                                 ln_b, pool_begin, pool_end, max_pools,
+                                                 reinterpret_cast<int8_t*>(pools), pool_scales, q_idx, w, seqs,
+                                                 num_seqs, q_seq, q_pos, T, score_stride, scores, workspace,
+                                                 workspace_bytes, stream);
+        return dsa_append_scores_groups(dims, dtype, latent, n, ld, slots, cache, cache_rows, k, gate, ln_w, ln_b,
+                                        pool_begin, pool_end, max_pools, reinterpret_cast<uint16_t*>(pools), q_idx,
+                                        w, seqs, num_seqs, q_seq, q_pos, T, score_stride, scores, workspace,
+                                        workspace_bytes, stream);
+    }
+    int st = check_dims(dims);
+    if (st) return st;
+    if (dtype != DSA_F32 && dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    const int D = dims->latent_dim;
+    if (D != 64 && D != 128 && D != 256 && D != 512) return DSA_ERR_UNSUPPORTED;
+    if (n < 0 || cache_rows < 0 || max_pools < 0) return DSA_ERR_SIZE;
+    const bool tokens = n > 0 || max_pools > 0;
+    if (tokens && dtype != DSA_BF16) return DSA_ERR_UNSUPPORTED;
+    if (n > 0) {
+        if (!latent || !slots || !cache) return DSA_ERR_NULL;
+        if (ld < D) return DSA_ERR_SIZE;
+        if (!aligned(latent, 16) || (ld * 2) % 16 != 0 || !aligned(cache, 16)) return DSA_ERR_ALIGN;
+    }
+    st = groups_common(dims, seqs, num_seqs, T, score_stride, workspace, workspace_bytes);
+    if (st) return st;
+    if (!int8_scoring_supported(dims, T)) return DSA_ERR_UNSUPPORTED;
+    if (max_pools > 0) {
+        st = check_seqs(seqs, num_seqs, false, true, true);
+        if (st) return st;
+        if (num_seqs > 65535) return DSA_ERR_SIZE;
+        if (!k || !gate || !ln_w || !ln_b || !pool_begin || !pool_end) return DSA_ERR_NULL;
+        if (!aligned(k, 4) || !aligned(gate, 4)) return DSA_ERR_ALIGN;
+    }
+    if (!pools) return DSA_ERR_NULL;
+    if (!aligned(pools, 16) || !aligned(pool_scales, 4)) return DSA_ERR_ALIGN;
+    const bool scoring = T > 0 && score_stride > 0;
+    if (scoring) {
+        if (!q_idx || !w || !q_seq || !q_pos || !scores) return DSA_ERR_NULL;
+        if (!aligned(q_idx, 16) || !aligned(w, 16)) return DSA_ERR_ALIGN;
+    }
+    if (!scoring && !tokens) return DSA_OK;
+    const dsa_seqs none{};
+    return hip_status(dsa_host::launch_append_scores_groups_runs(
+        *dims, latent, n, ld, slots, cache, k, gate, ln_w, ln_b, num_seqs > 0 && seqs ? *seqs : none, num_seqs,
+        pool_begin, pool_end, max_pools, pools, pool_scales, q_idx, w, q_seq, q_pos, scoring ? T : 0,
+        scoring ? score_stride : 0, scores, workspace, share, as_stream(stream)));
+}
+
 int dsa_time_next_scoring_launch(void* start_event, void* stop_event) {
     if ((start_event == nullptr) != (stop_event == nullptr)) return DSA_ERR_NULL;
     dsa_host::time_next_scoring_launch(reinterpret_cast<hipEvent_t>(start_event),

@@ -52,6 +52,37 @@ hipError_t launch_topk_groups(const dsa_dims& d, const float* scores, int32_t st
                               const int32_t* q_seq, const int32_t* q_pos, int32_t T, int32_t* pool_ids,
                               int32_t* indices, const void* ws, hipStream_t s);
 
+// k_scores_runs: runs of up to `share` consecutive queries of one sequence
+// share one pass over its pools; pools are bf16 rows, or INT8 code rows when
+// scales is not null.  n == 0 and max_pools == 0: no new tokens.
+hipError_t launch_append_scores_groups_runs(const dsa_dims& d, const void* latent, int64_t n, int64_t ld,
+                                            const int64_t* slots, int8_t* cache, const void* k, const void* gate,
+                                            const float* ln_w, const float* ln_b, const dsa_seqs& seqs,
+                                            int32_t num_seqs, const int32_t* pool_begin, const int32_t* pool_end,
+                                            int32_t max_pools, void* pools, float* scales, const uint16_t* q_idx,
+                                            const float* w, const int32_t* q_seq, const int32_t* q_pos, int32_t T,
+                                            int32_t stride, float* scores, void* ws, int share, hipStream_t s);
+
+// INT8 pools (code rows of idx_dim bytes and one fp32 scale per pool).
+hipError_t launch_index_pools_int8(const dsa_dims& d, const void* k, const void* gate, int dtype,
+                                   const float* ln_w, const float* ln_b, const dsa_seqs& seqs, int32_t num_seqs,
+                                   const int32_t* pool_begin, const int32_t* pool_end, int32_t max_pools,
+                                   int8_t* codes, float* scales, float* pools_f32, hipStream_t s);
+hipError_t launch_index_scores_int8(const dsa_dims& d, const uint16_t* q_idx, const float* w, const int8_t* codes,
+                                    const float* scales, const dsa_seqs& seqs, int32_t num_seqs, const int32_t* q_seq,
+                                    const int32_t* q_pos, int32_t T, int32_t stride, float* scores, hipStream_t s);
+hipError_t launch_scores_with_groups_int8(const dsa_dims& d, const uint16_t* q_idx, const float* w,
+                                          const int8_t* codes, const float* scales, const dsa_seqs& seqs,
+                                          int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos, int32_t T,
+                                          int32_t stride, float* scores, void* ws, hipStream_t s);
+hipError_t launch_append_scores_groups_int8(const dsa_dims& d, const void* latent, int64_t n, int64_t ld,
+                                            const int64_t* slots, int8_t* cache, const void* k, const void* gate,
+                                            const float* ln_w, const float* ln_b, const dsa_seqs& seqs,
+                                            int32_t num_seqs, const int32_t* pool_begin, const int32_t* pool_end,
+                                            int32_t max_pools, int8_t* codes, float* scales, const uint16_t* q_idx,
+                                            const float* w, const int32_t* q_seq, const int32_t* q_pos, int32_t T,
+                                            int32_t stride, float* scores, void* ws, hipStream_t s);
+
 size_t topk_workspace_bytes(const dsa_dims& d, int32_t T, int32_t stride);
 bool topk_supported(const dsa_dims& d, int32_t stride);
 hipError_t launch_topk(const dsa_dims& d, const float* scores, int32_t stride, const dsa_seqs& seqs,

@@ -19,6 +19,7 @@
 #include "scores_core.h"
 #include "topk_core.h"
 #include "new_tokens.h"
+#include "scores_decode.h"
 
 namespace dsa {
 
@@ -164,8 +165,6 @@ __global__ __launch_bounds__(WAVES * 64) void k_scores_mfma(
 // wave whose group holds one rebuilds it from k and gate itself (again the
 // same code), puts it into its B-operand registers and scores that; the rows
 // it read from memory for it are never used.
-constexpr int kDecMaxT = 64;
-constexpr int kQStride = kDI + 8;          // bf16 per LDS row of the shared A operand
 struct QueryGeom {
     int64_t base;      // pool_base of the query's sequence
     uint32_t first;    // flat index of the query's first tile
@@ -177,36 +176,24 @@ struct QueryGeom {
     int32_t rank;      // with new tokens: rank among the queries that have tiles
     int32_t pad;
 };
-struct AppendArgs {    // the step's new tokens (append_tokens' arguments)
-    const uint16_t* latent;
-    int64_t n, ld;
-    const int64_t* slots;
-    int8_t* cache;
-    int row_bytes;
-    const uint16_t* k;
-    const uint16_t* gate;
-    const float* ln_w;
-    const float* ln_b;
-    float eps;
-    const int64_t* tok_base;
-    const int32_t* pool_begin;
-    const int32_t* pool_end;
-    uint16_t* pools;   // the same buffer the tiles read
-    int pool_bx;       // 4-pool blocks per sequence (0: no pools)
-    int pool_tasks;    // num_seqs * pool_bx
-    int tasks;         // pool_tasks + ceil(n / 4)
-};
-template <bool CANDS, int AD>
+//
+// With I8 the pools are INT8 code rows with one fp32 scale each
+// (score_pool_group_i8): each wave loads 8 KB of codes and its pools' scales,
+// and a rebuilt pool is quantised the way the pool tasks store it.
+template <bool CANDS, int AD, bool I8 = false>
 __global__ __launch_bounds__(256, 4) void k_scores_groups(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
-    const uint16_t* pools, const int32_t* __restrict__ first_valid,
+    const void* pools_v, const int32_t* __restrict__ first_valid,
     const int64_t* __restrict__ pool_base, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_pos, int T, int nseq, int stride, float* __restrict__ scores,
-    int select_k, uint64_t* __restrict__ cand, int32_t* __restrict__ cand_n, AppendArgs ap) {
+    int select_k, uint64_t* __restrict__ cand, int32_t* __restrict__ cand_n, AppendArgs ap,
+    float* pool_scales) {
     __shared__ QueryGeom geom[kDecMaxT];
     __shared__ __attribute__((aligned(16))) uint16_t s_q[kHI * kQStride];
     __shared__ __attribute__((aligned(16))) float s_w[kHI];
     __shared__ __attribute__((aligned(16))) uint32_t s_new[AD ? 4 : 1][kDI / 2];
+    const uint16_t* pools = reinterpret_cast<const uint16_t*>(pools_v);
+    const int8_t* codes = reinterpret_cast<const int8_t*>(pools_v);
     const int lane = threadIdx.x & 63;
     const int wave = uniform32(threadIdx.x >> 6);
     if (wave == 0) {
@@ -300,9 +287,21 @@ __global__ __launch_bounds__(256, 4) void k_scores_groups(
             buffer_rsrc(w + (int64_t)t * kHI, kHI * 4), (uint32_t)min(lane, 7) * 4u, (uint32_t)(32 * wave), 0));
         // A wave past the query's last group re-reads the tile's first row
         // (unconditional loads keep the wait counts exact).
-        u32x4 v[16];
+        u32x4 v[I8 ? 8 : 16];
+        float psc = 0.f;                               // INT8: the scale of pool p0 + lane
         const int lp0 = has ? p0 : p0 - kGroupPools * wave;
-        load_pool_group(pools + ((int64_t)uniform64((uint64_t)geom[t].base) + lp0) * kDI, has ? n_vis - p0 : 1, v);
+        {
+            const int64_t row0 = (int64_t)uniform64((uint64_t)geom[t].base) + lp0;
+            const int lim = has ? n_vis - p0 : 1;
+            if constexpr (I8) {
+                load_pool_group_i8(codes + row0 * kDI, lim, v);
+                psc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    buffer_rsrc(pool_scales + row0, (uint32_t)(min(lim, 64) * 4)), (uint32_t)min(lane, lim - 1) * 4u,
+                    0, 0));
+            } else {
+                load_pool_group(pools + row0 * kDI, lim, v);
+            }
+        }
         __builtin_amdgcn_sched_barrier(0);             // every load in flight before the A operand is shared
         // the group list length, while the rows are in flight
         const int gm = CANDS && n_vis > select_k ? group_quota(select_k, n_vis) : 0;
@@ -323,10 +322,44 @@ __global__ __launch_bounds__(256, 4) void k_scores_groups(
                 s_new[AD ? wave : 0][lane] = (uint32_t)ov[0] | ((uint32_t)ov[1] << 16);
                 wave_lds_fence();
             };
-            IdxQuery Q;
-            load_idx_query_lds(s_q, kQStride, s_w, Q);
-            float s = score_pool_group(Q, v);
-            if constexpr (AD != 0) {
+            float s;
+            if constexpr (I8) {
+                IdxQueryI8 Q;
+                load_idx_query_lds_i8(s_q, kQStride, s_w, Q);
+                s = score_pool_group_i8(Q, v, psc);
+            } else {
+                IdxQuery Q;
+                load_idx_query_lds(s_q, kQStride, s_w, Q);
+                s = score_pool_group(Q, v);
+            }
+            if constexpr (AD != 0 && I8) {
+                // Rebuilt pools in the INT8 form: the pool tasks' values and
+                // quantiser, the codes through s_new[wave] as 128 bytes.
+                const int nb = max(uniform32(geom[t].pb), p0);
+                const int ne = min(min(uniform32(geom[t].pe), p0 + kGroupPools), n_vis);
+                const int64_t tok0 = (int64_t)uniform64((uint64_t)geom[t].tok0);
+                for (int pp = nb; pp < ne; ++pp) {
+                    PoolRaw128 r;
+                    pool_raw_load(ap.k, ap.gate, tok0 + 4 * (int64_t)pp, r);
+                    PoolIn<kDI, uint16_t> in;
+                    pool_raw_in(r, in);
+                    float f[2];
+                    pool_values_f32<kDI, uint16_t>(in, ap.ln_w, ap.ln_b, ap.eps, f);
+                    int8_t code[2];
+                    const float sc = quantize_pool<2>(f, code);
+                    reinterpret_cast<uint16_t*>(s_new[wave])[lane] =
+                        (uint16_t)((uint8_t)code[0] | ((uint32_t)(uint8_t)code[1] << 8));
+                    wave_lds_fence();
+                    const char* nbytes = reinterpret_cast<const char*>(s_new[wave]) + 32 * (lane >> 4);
+                    const u32x4 w0 = *reinterpret_cast<const u32x4*>(nbytes);
+                    const u32x4 w1 = *reinterpret_cast<const u32x4*>(nbytes + 16);
+                    IdxQueryI8 Q2;                     // reloaded: Q is not kept through the rebuild
+                    load_idx_query_lds_i8(s_q, kQStride, s_w, Q2);
+                    const float s2 = score_pool_column_i8(Q2, w0, w1, sc);
+                    if (lane == pp - p0) s = s2;
+                    wave_lds_fence();                  // s_new is rewritten by the next pool
+                }
+            } else if constexpr (AD != 0) {
                 // Score each rebuilt pool (score_pool_column: lane pp - p0 gets
                 // the bits the group's own scoring would have given it).
                 const int nb = max(uniform32(geom[t].pb), p0);
@@ -369,11 +402,18 @@ __global__ __launch_bounds__(256, 4) void k_scores_groups(
         // New tokens: tasks total .. total + tasks - 1, 4 pools or 4 rows each.
         for (; tile < total + ap.tasks; tile += gridDim.x) {
             const int a = tile - total;
-            if (a < ap.pool_tasks)
-                index_pool_row<kDI, uint16_t>(ap.k, ap.gate, ap.ln_w, ap.ln_b, ap.eps, first_valid, ap.tok_base,
-                                              pool_base, ap.pool_begin, ap.pool_end, ap.pools, a / ap.pool_bx,
-                                              (a % ap.pool_bx) * 4 + wave);
-            else
+            if (a < ap.pool_tasks) {
+                if constexpr (I8)
+                    index_pool_row_int8<kDI, uint16_t>(ap.k, ap.gate, ap.ln_w, ap.ln_b, ap.eps, first_valid,
+                                                       ap.tok_base, pool_base, ap.pool_begin, ap.pool_end,
+                                                       PoolDst{nullptr, reinterpret_cast<int8_t*>(ap.pools),
+                                                               pool_scales, nullptr},
+                                                       a / ap.pool_bx, (a % ap.pool_bx) * 4 + wave);
+                else
+                    index_pool_row<kDI, uint16_t>(ap.k, ap.gate, ap.ln_w, ap.ln_b, ap.eps, first_valid, ap.tok_base,
+                                                  pool_base, ap.pool_begin, ap.pool_end, ap.pools, a / ap.pool_bx,
+                                                  (a % ap.pool_bx) * 4 + wave);
+            } else
                 store_int8_row<AD, false>(ap.latent, ap.n, ap.ld, ap.slots, ap.cache, ap.row_bytes,
                                           (int64_t)(a - ap.pool_tasks) * 4 + wave);
         }
@@ -426,16 +466,17 @@ __global__ __launch_bounds__(256) void k_scores_generic(
 
 namespace dsa_host {
 
-// Events the next decode scoring launch (k_scores_groups, from any entry
-// point) records around the kernel itself; one-shot.
+// Events the next scoring launch (k_scores_groups or k_scores_mfma, from any
+// entry point) records around the kernel itself; one-shot.
 namespace {
 thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+}  // namespace
+
 void take_events(hipEvent_t& a, hipEvent_t& b) {
     a = t_ev_start;
     b = t_ev_stop;
     t_ev_start = t_ev_stop = nullptr;
 }
-}  // namespace
 
 void time_next_scoring_launch(hipEvent_t start, hipEvent_t stop) {
     t_ev_start = start;
@@ -461,14 +502,16 @@ hipError_t launch_index_scores(const dsa_dims& d, const uint16_t* q_idx, const f
             hipEvent_t ev0, ev1;
             take_events(ev0, ev1);
             hipExtLaunchKernelGGL((dsa::k_scores_groups<false, 0>), dim3(scores_groups_grid(T, stride)), dim3(256), 0,
-                                  s, ev0, ev1, 0, q_idx, w, pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T,
-                                  num_seqs, stride, scores, 0, nullptr, nullptr, dsa::AppendArgs{});
+                                  s, ev0, ev1, 0, q_idx, w, pools, seqs.first_valid, seqs.pool_base, q_seq,
+                                  q_pos, T, num_seqs, stride, scores, 0, nullptr, nullptr, dsa::AppendArgs{}, nullptr);
         } else {
             // Prefill: 512 resident pools per workgroup, 64 queries per workgroup.
             const int qpb = 64;
             dim3 grid((unsigned)cdiv(stride, 512), (unsigned)cdiv(T, qpb)), block(512);
-            hipLaunchKernelGGL((dsa::k_scores_mfma<8, 4>), grid, block, 0, s, q_idx, w, pools,
-                               seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, qpb, stride, scores);
+            hipEvent_t ev0, ev1;
+            take_events(ev0, ev1);
+            hipExtLaunchKernelGGL((dsa::k_scores_mfma<8, 4>), grid, block, 0, s, ev0, ev1, 0, q_idx, w, pools,
+                                  seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, qpb, stride, scores);
         }
     } else {
         dim3 grid((unsigned)cdiv(stride, 256), (unsigned)T), block(256);
@@ -494,14 +537,14 @@ hipError_t launch_scores_with_groups(const dsa_dims& d, const uint16_t* q_idx, c
                                      const int32_t* q_pos, int32_t T, int32_t stride, float* scores, void* ws,
                                      hipStream_t s) {
     if (T == 0 || stride == 0) return hipSuccess;
-    uint64_t* cand = reinterpret_cast<uint64_t*>(ws);
-    int32_t* cand_n = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) +
-                                                 ((size_t)T * dsa::kGroupCandCap * 8 + 255) / 256 * 256);
+    uint64_t* cand;
+    int32_t* cand_n;
+    group_lists(ws, T, cand, cand_n);
     hipEvent_t ev0, ev1;
     take_events(ev0, ev1);
     hipExtLaunchKernelGGL((dsa::k_scores_groups<true, 0>), dim3(scores_groups_grid(T, stride)), dim3(256), 0, s,
-                          ev0, ev1, 0, q_idx, w, pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, num_seqs,
-                          stride, scores, d.index_topk / d.kpool, cand, cand_n, dsa::AppendArgs{});
+                          ev0, ev1, 0, q_idx, w, pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T,
+                          num_seqs, stride, scores, d.index_topk / d.kpool, cand, cand_n, dsa::AppendArgs{}, nullptr);
     return hipGetLastError();
 }
 
@@ -511,6 +554,7 @@ bool append_scores_fused(const dsa_dims& d, int dtype) {
            (d.latent_dim == 64 || d.latent_dim == 128 || d.latent_dim == 256 || d.latent_dim == 512);
 }
 
+
 hipError_t launch_append_scores_groups(const dsa_dims& d, const void* latent, int64_t n, int64_t ld,
                                        const int64_t* slots, int8_t* cache, const void* k, const void* gate,
                                        const float* ln_w, const float* ln_b, const dsa_seqs& seqs, int32_t num_seqs,
@@ -518,39 +562,20 @@ hipError_t launch_append_scores_groups(const dsa_dims& d, const void* latent, in
                                        uint16_t* pools, const uint16_t* q_idx, const float* w, const int32_t* q_seq,
                                        const int32_t* q_pos, int32_t T, int32_t stride, float* scores, void* ws,
                                        hipStream_t s) {
-    uint64_t* cand = reinterpret_cast<uint64_t*>(ws);
-    int32_t* cand_n = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) +
-                                                 ((size_t)T * dsa::kGroupCandCap * 8 + 255) / 256 * 256);
-    dsa::AppendArgs ap{};
-    ap.latent = reinterpret_cast<const uint16_t*>(latent);
-    ap.n = n;
-    ap.ld = ld;
-    ap.slots = slots;
-    ap.cache = cache;
-    ap.row_bytes = d.row_bytes;
-    ap.k = reinterpret_cast<const uint16_t*>(k);
-    ap.gate = reinterpret_cast<const uint16_t*>(gate);
-    ap.ln_w = ln_w;
-    ap.ln_b = ln_b;
-    ap.eps = d.ln_eps;
-    ap.tok_base = seqs.tok_base;
-    ap.pool_begin = pool_begin;
-    ap.pool_end = pool_end;
-    ap.pools = pools;
-    ap.pool_bx = max_pools > 0 ? (int)cdiv(max_pools, 4) : 0;
-    const int64_t pool_tasks = (int64_t)ap.pool_bx * num_seqs;   // 0 without pools
-    const int64_t tasks = pool_tasks + cdiv(n, 4);
-    if (tasks > 0x3FFFFFFF) return hipErrorInvalidValue;
-    ap.pool_tasks = (int)pool_tasks;
-    ap.tasks = (int)tasks;
-    const int64_t want = cdiv(cdiv(stride, dsa::kGroupPools), 4) * (int64_t)T + tasks;
-    const unsigned grid = (unsigned)std::min<int64_t>(std::max<int64_t>(want, 1), 4 * (int64_t)device_info().cu_count);
+    uint64_t* cand;
+    int32_t* cand_n;
+    group_lists(ws, T, cand, cand_n);
+    dsa::AppendArgs ap;
+    if (!make_append_args(d, latent, n, ld, slots, cache, k, gate, ln_w, ln_b, seqs, num_seqs, pool_begin, pool_end,
+                          max_pools, pools, nullptr, ap))
+        return hipErrorInvalidValue;
+    const unsigned grid = fused_grid(T, stride, ap.tasks);
     hipEvent_t ev0, ev1;
     take_events(ev0, ev1);
 #define DSA_APPEND_SCORES(D)                                                                                        \
     hipExtLaunchKernelGGL((dsa::k_scores_groups<true, D>), dim3(grid), dim3(256), 0, s, ev0, ev1, 0, q_idx, w,    \
-                          pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, num_seqs, stride, scores,   \
-                          d.index_topk / d.kpool, cand, cand_n, ap)
+                          pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, num_seqs, stride,  \
+                          scores, d.index_topk / d.kpool, cand, cand_n, ap, nullptr)
     switch (d.latent_dim) {
         case 512: DSA_APPEND_SCORES(512); break;
         case 256: DSA_APPEND_SCORES(256); break;
@@ -558,6 +583,69 @@ hipError_t launch_append_scores_groups(const dsa_dims& d, const void* latent, in
         default: DSA_APPEND_SCORES(64); break;
     }
 #undef DSA_APPEND_SCORES
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ INT8 pools
+
+hipError_t launch_index_scores_int8(const dsa_dims& d, const uint16_t* q_idx, const float* w, const int8_t* codes,
+                                    const float* scales, const dsa_seqs& seqs, int32_t num_seqs, const int32_t* q_seq,
+                                    const int32_t* q_pos, int32_t T, int32_t stride, float* scores, hipStream_t s) {
+    if (T == 0 || stride == 0) return hipSuccess;
+    hipEvent_t ev0, ev1;
+    take_events(ev0, ev1);
+    hipExtLaunchKernelGGL((dsa::k_scores_groups<false, 0, true>), dim3(scores_groups_grid(T, stride)), dim3(256), 0, s,
+                          ev0, ev1, 0, q_idx, w, codes, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T,
+                          num_seqs, stride, scores, 0, nullptr, nullptr, dsa::AppendArgs{},
+                          const_cast<float*>(scales));
+    return hipGetLastError();
+}
+
+hipError_t launch_scores_with_groups_int8(const dsa_dims& d, const uint16_t* q_idx, const float* w,
+                                          const int8_t* codes, const float* scales, const dsa_seqs& seqs,
+                                          int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos, int32_t T,
+                                          int32_t stride, float* scores, void* ws, hipStream_t s) {
+    if (T == 0 || stride == 0) return hipSuccess;
+    uint64_t* cand;
+    int32_t* cand_n;
+    group_lists(ws, T, cand, cand_n);
+    hipEvent_t ev0, ev1;
+    take_events(ev0, ev1);
+    hipExtLaunchKernelGGL((dsa::k_scores_groups<true, 0, true>), dim3(scores_groups_grid(T, stride)), dim3(256), 0, s,
+                          ev0, ev1, 0, q_idx, w, codes, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T,
+                          num_seqs, stride, scores, d.index_topk / d.kpool, cand, cand_n, dsa::AppendArgs{},
+                          const_cast<float*>(scales));
+    return hipGetLastError();
+}
+
+hipError_t launch_append_scores_groups_int8(const dsa_dims& d, const void* latent, int64_t n, int64_t ld,
+                                            const int64_t* slots, int8_t* cache, const void* k, const void* gate,
+                                            const float* ln_w, const float* ln_b, const dsa_seqs& seqs,
+                                            int32_t num_seqs, const int32_t* pool_begin, const int32_t* pool_end,
+                                            int32_t max_pools, int8_t* codes, float* scales, const uint16_t* q_idx,
+                                            const float* w, const int32_t* q_seq, const int32_t* q_pos, int32_t T,
+                                            int32_t stride, float* scores, void* ws, hipStream_t s) {
+    uint64_t* cand;
+    int32_t* cand_n;
+    group_lists(ws, T, cand, cand_n);
+    dsa::AppendArgs ap;
+    if (!make_append_args(d, latent, n, ld, slots, cache, k, gate, ln_w, ln_b, seqs, num_seqs, pool_begin, pool_end,
+                          max_pools, nullptr, codes, ap))
+        return hipErrorInvalidValue;
+    const unsigned grid = fused_grid(T, stride, ap.tasks);
+    hipEvent_t ev0, ev1;
+    take_events(ev0, ev1);
+#define DSA_APPEND_SCORES8(D)                                                                                       \
+    hipExtLaunchKernelGGL((dsa::k_scores_groups<true, D, true>), dim3(grid), dim3(256), 0, s, ev0, ev1, 0, q_idx, \
+                          w, codes, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, num_seqs, stride, \
+                          scores, d.index_topk / d.kpool, cand, cand_n, ap, scales)
+    switch (d.latent_dim) {
+        case 512: DSA_APPEND_SCORES8(512); break;
+        case 256: DSA_APPEND_SCORES8(256); break;
+        case 128: DSA_APPEND_SCORES8(128); break;
+        default: DSA_APPEND_SCORES8(64); break;
+    }
+#undef DSA_APPEND_SCORES8
     return hipGetLastError();
 }
 

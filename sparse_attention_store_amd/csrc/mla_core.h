@@ -40,24 +40,6 @@ constexpr float kLazyMax = 8.0f;      // raise the running max only beyond 2^8
 // Physical row (within a 16-row tile) of MFMA row slot s: bits 2 and 3 swapped.
 __device__ __forceinline__ int row_of_slot(int s) { return (s & 3) | ((s & 4) << 1) | ((s & 8) >> 1); }
 
-// 4 INT8 codes -> bf16 of (code + 128), 0..255, exact: one byte-to-float
-// conversion per code (v_cvt_f32_ubyteN) and the upper halves packed.
-__device__ __forceinline__ void biased4_to_bf16(uint32_t w, uint32_t& lo, uint32_t& hi) {
-    const uint32_t u = w ^ 0x80808080u;
-    const float f0 = (float)(u & 0xFFu);
-    const float f1 = (float)((u >> 8) & 0xFFu);
-    const float f2 = (float)((u >> 16) & 0xFFu);
-    const float f3 = (float)(u >> 24);
-    lo = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
-    hi = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
-}
-
-__device__ __forceinline__ u32x4 codes8_to_biased_bf16(uint32_t a, uint32_t b) {
-    uint32_t r0, r1, r2, r3;
-    biased4_to_bf16(a, r0, r1);
-    biased4_to_bf16(b, r2, r3);
-    return u32x4{r0, r1, r2, r3};
-}
 
 // LDS of one split walking chunks of 16 * RT * NW rows (NW waves of RT
 // 16-row tiles).

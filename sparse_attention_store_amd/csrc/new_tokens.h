@@ -211,6 +211,91 @@ __device__ __forceinline__ void pool_values(const PoolIn<DI, T>& in, const float
     }
 }
 
+// The same values in fp32, before any rounding (the INT8 pool form quantises
+// these).  The arithmetic is pool_values' up to its final rounding, written
+// out again rather than shared so that the bf16 kernels' code is unchanged.
+template <int DI, typename T>
+__device__ __forceinline__ void pool_values_f32(const PoolIn<DI, T>& in, const float* __restrict__ ln_w,
+                                                const float* __restrict__ ln_b, float eps,
+                                                float (&outv)[PoolIn<DI, T>::CPL]) {
+#pragma clang fp contract(off)
+    constexpr int KP = PoolIn<DI, T>::KP, CPL = PoolIn<DI, T>::CPL;
+    const int lane = threadIdx.x & 63;
+    const bool active = DI >= 64 || lane < DI;
+    const int c0 = active ? lane * CPL : 0;
+    // ln_w / ln_b through buffer descriptors: the lane's offset is a 32-bit
+    // value, cheap to recompute, so no per-lane pointer is kept live.
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(ln_w, DI * 4), rb = buffer_rsrc(ln_b, DI * 4);
+    float wv[CPL], bv[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        wv[c] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw, (uint32_t)(c0 + c) * 4u, 0, 0));
+        bv[c] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, (uint32_t)(c0 + c) * 4u, 0, 0));
+    }
+    float y[KP][CPL];
+#pragma unroll
+    for (int s = 0; s < KP; ++s) {
+        float sum = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) sum += in.x[s][c];
+        const float mean = wave_sum(sum) * (1.0f / DI);
+        float sq = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const float dx = active ? in.x[s][c] - mean : 0.f;
+            sq = __builtin_fmaf(dx, dx, sq);
+        }
+        const float var = wave_sum(sq) * (1.0f / DI);
+        const float rstd = 1.0f / sqrtf(var + eps);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) y[s][c] = __builtin_fmaf((in.x[s][c] - mean) * rstd, wv[c], bv[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        float m = in.g[0][c];
+#pragma unroll
+        for (int s = 1; s < KP; ++s) m = fmaxf(m, in.g[s][c]);
+        float den = 0.f, num = 0.f;
+#pragma unroll
+        for (int s = 0; s < KP; ++s) {
+            const float e = expf(in.g[s][c] - m);
+            den += e;
+            num = __builtin_fmaf(e, y[s][c], num);
+        }
+        outv[c] = active ? num / den : 0.f;
+    }
+}
+
+// A pool's fp32 values as INT8 codes with one fp32 scale for the row ([Flash]
+// What is quantized: the INT8 indexer cache, one scale per row), by the
+// quantiser of the latent rows: amax over the row (a wave max; lanes past DI
+// hold zeros), s = max(amax, 1e-4) / 127 (IEEE division), code =
+// clamp(round_half_even(x / s), -127, 127).  Every lane of the wave calls it.
+template <int CPL>
+__device__ __forceinline__ float quantize_pool(const float (&f)[CPL], int8_t (&code)[CPL]) {
+    float amax = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) amax = fmaxf(amax, fabsf(f[c]));
+    amax = wave_max(amax);
+    const float s = fmaxf(amax, 1e-4f) / 127.0f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        float r = rintf(f[c] / s);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        code[c] = (int8_t)(int)r;
+    }
+    return s;
+}
+
+// Where built pools go: bf16 rows, or INT8 code rows with a scale per row
+// (and, when f32 is set, the fp32 values before quantisation).
+struct PoolDst {
+    uint16_t* bf16;    // [*, DI] bf16, or null for the INT8 form
+    int8_t* codes;     // [*, DI] int8 (INT8 form)
+    float* scales;     // [*] fp32 (INT8 form)
+    float* f32;        // [*, DI] fp32 or null (INT8 form only)
+};
+
 // Pool pool_begin[b] + j of sequence b, if below pool_end[b] (one wave;
 // every lane of the wave calls it).
 template <int DI, typename T>
@@ -236,6 +321,42 @@ __device__ __forceinline__ void index_pool_row(
     } else {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) dst[c] = outv[c];
+    }
+}
+
+// The same pool in the INT8 form: codes, its scale, and the fp32 values when
+// dst.f32 is set.
+template <int DI, typename T>
+__device__ __forceinline__ void index_pool_row_int8(
+    const T* __restrict__ k, const T* __restrict__ gate, const float* __restrict__ ln_w,
+    const float* __restrict__ ln_b, float eps, const int32_t* __restrict__ first_valid,
+    const int64_t* __restrict__ tok_base, const int64_t* __restrict__ pool_base,
+    const int32_t* __restrict__ pool_begin, const int32_t* __restrict__ pool_end, const PoolDst& dst, int b,
+    int j) {
+    constexpr int CPL = PoolIn<DI, T>::CPL;
+    const int lane = threadIdx.x & 63;
+    const int p = pool_begin[b] + j;
+    if (p >= pool_end[b]) return;
+    const int64_t tok0 = tok_base[b] + first_valid[b] + 4 * (int64_t)p;
+    PoolIn<DI, T> in;
+    pool_inputs<DI, T>(k, gate, tok0, in);
+    float f[CPL];
+    pool_values_f32<DI, T>(in, ln_w, ln_b, eps, f);
+    int8_t code[CPL];
+    const float s = quantize_pool<CPL>(f, code);
+    const int64_t row = pool_base[b] + p;
+    if (lane == 0) dst.scales[row] = s;
+    if (!(DI >= 64 || lane < DI)) return;
+    int8_t* cd = dst.codes + row * (int64_t)DI + lane * CPL;
+    if constexpr (CPL == 2) {
+        *reinterpret_cast<uint16_t*>(cd) = (uint16_t)((uint8_t)code[0] | ((uint32_t)(uint8_t)code[1] << 8));
+    } else {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) cd[c] = code[c];
+    }
+    if (dst.f32) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) dst.f32[row * (int64_t)DI + lane * CPL + c] = f[c];
     }
 }
 

@@ -76,9 +76,20 @@ __device__ __forceinline__ void load_pool_group(const uint16_t* __restrict__ row
     }
 }
 
+// part[r]: this lane's partial of pool 16 r + c.  Lane group g holds a
+// partial of pools 16 r + c for every r; lane group g ends with the full sum
+// of N-tile r = g, so lane l holds pool l.
+__device__ __forceinline__ float reduce_group_parts(const float (&part)[4]) {
+    const int lane = threadIdx.x & 63;
+    const bool h = (lane & 32) != 0;     // keeps N-tiles 2h, 2h + 1
+    const float k0 = (h ? part[2] : part[0]) + __shfl_xor(h ? part[0] : part[2], 32, 64);
+    const float k1 = (h ? part[3] : part[1]) + __shfl_xor(h ? part[1] : part[3], 32, 64);
+    const bool j = (lane & 16) != 0;     // keeps N-tile 2h + j
+    return (j ? k1 : k0) + __shfl_xor(j ? k0 : k1, 16, 64);
+}
+
 // Returns the score of pool (lane) of the group.
 __device__ __forceinline__ float score_pool_group(const IdxQuery& Q, const u32x4 (&v)[16]) {
-    const int lane = threadIdx.x & 63;
     float part[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -95,13 +106,7 @@ __device__ __forceinline__ float score_pool_group(const IdxQuery& Q, const u32x4
         for (int i = 0; i < 4; ++i) sum += Q.w[1][i] * fmaxf(acc1[i], 0.f);
         part[r] = sum;
     }
-    // Lane group g holds a partial of pools 16 r + c for every r; lane group
-    // g ends with the full sum of N-tile r = g.
-    const bool h = (lane & 32) != 0;     // keeps N-tiles 2h, 2h + 1
-    const float k0 = (h ? part[2] : part[0]) + __shfl_xor(h ? part[0] : part[2], 32, 64);
-    const float k1 = (h ? part[3] : part[1]) + __shfl_xor(h ? part[1] : part[3], 32, 64);
-    const bool j = (lane & 16) != 0;     // keeps N-tile 2h + j
-    return (j ? k1 : k0) + __shfl_xor(j ? k0 : k1, 16, 64);
+    return reduce_group_parts(part);
 }
 
 // The score of one more pool, given as a single N-tile's B operand b[s]
@@ -123,6 +128,113 @@ __device__ __forceinline__ float score_pool_column(const IdxQuery& Q, const u32x
     for (int i = 0; i < 4; ++i) sum += Q.w[1][i] * fmaxf(acc1[i], 0.f);
     const float k = sum + __shfl_xor(sum, 32, 64);
     return k + __shfl_xor(k, 16, 64);
+}
+
+// ------------------------------------------------------------------ INT8 pools
+// Pools stored as INT8 codes (128-byte rows) with one fp32 scale per pool
+// ([Flash] What is quantized: the INT8 indexer cache).  For pool p with scale
+// s_p > 0, relu(q . (s_p code_p)) = s_p relu(q . code_p), so
+//   score[p] = s_p * sum_h w[h] * relu(q[h] . code_p),
+// one multiply per pool after the head sum.  The codes go into the B operand
+// as bf16 of (code + 128) (exact; one conversion per code), and the bias is
+// taken off the dot products exactly as the bf16 sum 128 * sum_d q[h][d]
+// (computed once per tile in fp32).
+// Lane l = 16 g + c loads, for N-tile r, bytes 32 g .. 32 g + 32 of pool
+// 16 r + c (two 16-byte loads: dims 32 g .. 32 g + 31); K-step s uses dims
+// 32 g + 8 s .. + 8 of them.  The reduction axis is permuted the same way in
+// the A operand (load_idx_query_lds_i8), so the products are unchanged.
+
+struct IdxQueryI8 {
+    IdxQuery q;        // A operand in the permuted order, head weights
+    f32x4 bias[2];     // 128 * sum_d q[h][d] for heads 16 mt + 4 g + i
+};
+
+__device__ __forceinline__ void load_idx_query_lds_i8(const uint16_t* q_lds, int qs, const float* w_lds,
+                                                      IdxQueryI8& Q) {
+    const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
+    float qsum[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        float acc = 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            Q.q.a[mt][s] = *reinterpret_cast<const u32x4*>(&q_lds[(16 * mt + c) * qs + 32 * g + 8 * s]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc += bf16_to_f32(Q.q.a[mt][s][e] & 0xFFFFu) + bf16_to_f32(Q.q.a[mt][s][e] >> 16);
+        }
+        acc += __shfl_xor(acc, 16, 64);
+        qsum[mt] = acc + __shfl_xor(acc, 32, 64);          // head 16 mt + c, in every lane group
+    }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        Q.q.w[mt] = *reinterpret_cast<const f32x4*>(&w_lds[16 * mt + 4 * g]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Q.bias[mt][i] = 128.0f * __shfl(qsum[mt], 4 * g + i, 64);
+    }
+}
+
+// rows: the group's first code row (wave-uniform); lim (>= 1) rows exist;
+// rows at or past lim re-read row lim - 1 (masked by the caller).
+__device__ __forceinline__ void load_pool_group_i8(const int8_t* __restrict__ rows, int lim, u32x4 (&v)[8]) {
+    const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
+    const __amdgpu_buffer_rsrc_t rr = buffer_rsrc(rows, (uint32_t)(min(lim, 64) * kDI));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t loff = (uint32_t)(min(16 * r + c, lim - 1) * kDI + 32 * g);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) v[2 * r + j] = ld_buf128(rr, loff, (uint32_t)(16 * j));
+    }
+}
+
+// K-step s of the B operand from this lane's 32 code bytes (w0 = bytes 0-15, w1 = bytes 16-31).
+__device__ __forceinline__ u32x4 i8_kstep(const u32x4& w0, const u32x4& w1, int s) {
+    const u32x4& w = s < 2 ? w0 : w1;
+    return codes8_to_biased_bf16(w[(s & 1) * 2], w[(s & 1) * 2 + 1]);
+}
+
+// The head sum of one N-tile's accumulators (heads 16 mt + 4 g + i), bias off.
+__device__ __forceinline__ float i8_head_sum(const IdxQueryI8& Q, const f32x4& acc0, const f32x4& acc1) {
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sum += Q.q.w[0][i] * fmaxf(acc0[i] - Q.bias[0][i], 0.f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sum += Q.q.w[1][i] * fmaxf(acc1[i] - Q.bias[1][i], 0.f);
+    return sum;
+}
+
+// Score of pool (lane) of the group; scale: that pool's scale.
+__device__ __forceinline__ float score_pool_group_i8(const IdxQueryI8& Q, const u32x4 (&v)[8], float scale) {
+    float part[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const u32x4 b = i8_kstep(v[2 * r], v[2 * r + 1], s);
+            acc0 = mfma16(as_bf16x8(Q.q.a[0][s]), as_bf16x8(b), acc0);
+            acc1 = mfma16(as_bf16x8(Q.q.a[1][s]), as_bf16x8(b), acc1);
+        }
+        part[r] = i8_head_sum(Q, acc0, acc1);
+    }
+    return reduce_group_parts(part) * scale;
+}
+
+// One more pool as a single N-tile column (its 32 code bytes for this lane
+// group in w0, w1 in every lane of the group): lane l gets exactly what
+// score_pool_group_i8 returns in lane l for a group holding that pool there.
+__device__ __forceinline__ float score_pool_column_i8(const IdxQueryI8& Q, const u32x4& w0, const u32x4& w1,
+                                                      float scale) {
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const u32x4 b = i8_kstep(w0, w1, s);
+        acc0 = mfma16(as_bf16x8(Q.q.a[0][s]), as_bf16x8(b), acc0);
+        acc1 = mfma16(as_bf16x8(Q.q.a[1][s]), as_bf16x8(b), acc1);
+    }
+    const float sum = i8_head_sum(Q, acc0, acc1);
+    const float k = sum + __shfl_xor(sum, 32, 64);
+    return (k + __shfl_xor(k, 16, 64)) * scale;
 }
 
 }  // namespace dsa

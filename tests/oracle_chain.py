@@ -79,17 +79,22 @@ class OracleWorkload:
             out[sel] = O.pack_rows(codes, scales, self.d.row_bytes)
         return out
 
-    def query(self, t: int, stride: int | None = None):
-        """Dict with the oracle's scores, pool ids, index list and attention for query t."""
+    def query(self, t: int, stride: int | None = None, int8_pools=None):
+        """Dict with the oracle's scores, pool ids, index list and attention for query t.
+
+        int8_pools: (codes, scales) of the sequence's pools in the INT8 form;
+        the scores are then O3q over them (else O3 over the stored bf16 pools)."""
         wl, d = self.wl, self.d
         b = int(wl.q_seq[t])
         f = int(wl.first_valid[b])
         qp = int(wl.q_pos[t])
         n_vis = O.visible_pool_count(qp, f, d.kpool)
-        pools = self.pools_stored(b)
         qi = syn.gen_qidx(wl, t, t + 1)[0]
         w = syn.gen_w(wl, t, t + 1)[0]
-        scores = O.index_scores(qi, w, pools, n_vis, stride)
+        if int8_pools is not None:
+            scores = O.index_scores_int8(qi, w, int8_pools[0], int8_pools[1], n_vis, stride)
+        else:
+            scores = O.index_scores(qi, w, self.pools_stored(b), n_vis, stride)
         ids = O.topk_pools(scores, n_vis, d.select_k)
         idx = O.expand_selection(ids, f, qp, int(wl.row_base[b]), d.kpool, d.out_width)
         valid = idx[idx >= 0]
@@ -134,6 +139,26 @@ def score_close(gpu: np.ndarray, ref: np.ndarray, n_vis: int, rtol: float = 1e-2
     return bool(np.all(err <= bound)), float(np.max(err / np.maximum(bound, 1e-300)))
 
 
+# A GPU pool's fp32 state differs from the oracle's fp64 state rounded to fp32
+# by a few fp32 rounding steps (LayerNorm, softmax, sums): well under 2^-18 of
+# the row's amax, i.e. under 127 * 2^-18 < 5e-4 of one code step.  A code may
+# therefore differ from the oracle's by one only where the oracle's x / s lies
+# within that distance of a rounding boundary (k + 1/2).
+INT8_BOUNDARY = 5e-4
+
+
+def check_int8_pools(codes: np.ndarray, scales: np.ndarray, opools: np.ndarray, where) -> None:
+    """GPU INT8 pools against the oracle's quantiser (O2q) of its fp64 pools."""
+    oc, osc = O.quantize_pools(opools)
+    assert np.allclose(scales.astype(np.float64), osc.astype(np.float64), rtol=2e-6, atol=0), ("pool scales", where)
+    diff = codes.astype(np.int64) - oc.astype(np.int64)
+    assert np.all(np.abs(diff) <= 1), ("pool codes", where)
+    if np.any(diff):
+        ratio = np.asarray(opools, np.float64).astype(np.float32).astype(np.float64) / osc.astype(np.float64)[:, None]
+        near = np.abs(np.abs(ratio - np.floor(ratio)) - 0.5) <= INT8_BOUNDARY
+        assert np.all(near[diff != 0]), ("pool code off a rounding boundary", where)
+
+
 def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
     """Half a bf16 unit in the last place at |x| (the rounding of a bf16 output)."""
     ax = np.maximum(np.abs(np.asarray(x, np.float64)), 2.0 ** -126)
@@ -144,7 +169,9 @@ def check_chain(dw, queries, pool_sample: int = 64, say=print) -> dict:
     """Every stage of the step dw ran, for each query in `queries`:
 
     * pools (a sample per sequence) and scores against the oracle's (O2, O3):
-      rtol 1e-2 with a floor of 1e-2 x RMS of the oracle row; score tails -inf;
+      rtol 1e-2 with a floor of 1e-2 x RMS of the oracle row; score tails -inf.
+      INT8 pools (dw.int8): codes and scales against the oracle's quantiser
+      (check_int8_pools), and the scores against O3q on the GPU's own codes;
     * stage-isolated selection: the oracle's top-k (O4) and expansion (O5) run
       on the GPU's own fp32 score row must reproduce pool_ids and the index
       list bit for bit;
@@ -166,7 +193,12 @@ def check_chain(dw, queries, pool_sample: int = 64, say=print) -> dict:
     out_bf16 = dw.out.dtype == torch.bfloat16
     out = dw.out.float().cpu().numpy()
     lse = dw.lse.cpu().numpy()
-    pools = dw.pools[0].float().cpu().numpy()
+    int8 = getattr(dw, "int8", False)
+    if int8:
+        codes = dw.pool_codes[0].cpu().numpy()
+        pscales = dw.pool_scales[0].cpu().numpy()
+    else:
+        pools = dw.pools[0].float().cpu().numpy()
     errs, refs, allow = [], [], []
     near_ties = 0
     g = np.random.default_rng(17)
@@ -177,17 +209,26 @@ def check_chain(dw, queries, pool_sample: int = 64, say=print) -> dict:
         f = int(wl.first_valid[b])
         qp = int(wl.q_pos[t])
         say(f"  oracle query {t} (sequence {b}, position {qp})")
-        r = ow.query(t, dw.stride)
+        pb = int(wl.pool_base[b])
+        if int8:
+            # the oracle's scores on the GPU's own INT8 pools (O3q); the codes
+            # themselves are checked against the oracle's quantiser below
+            n_p = wl.n_pools(b)
+            r = ow.query(t, dw.stride, int8_pools=(codes[pb:pb + n_p], pscales[pb:pb + n_p]))
+        else:
+            r = ow.query(t, dw.stride)
         n_vis = r["n_vis"]
         if b not in checked_pools:
             checked_pools.add(b)
-            pb = int(wl.pool_base[b])
-            opools = ow.pools_stored(b)
+            opools = ow.pools(b)
             sel = np.arange(opools.shape[0]) if opools.shape[0] <= pool_sample else \
                 g.choice(opools.shape[0], size=pool_sample, replace=False)
-            for p in sel:
-                ok, worst = score_close(pools[pb + p], ow.pools(b)[p], d.idx_dim)
-                assert ok, ("pool", t, int(p), worst)
+            if int8:
+                check_int8_pools(codes[pb + sel], pscales[pb + sel], opools[sel], (t, b))
+            else:
+                for p in sel:
+                    ok, worst = score_close(pools[pb + p], opools[p], d.idx_dim)
+                    assert ok, ("pool", t, int(p), worst)
         ok, worst = score_close(scores[t], r["scores"], n_vis)
         assert ok, ("scores", t, worst)
         assert np.all(np.isneginf(scores[t, n_vis:])), ("scores tail", t)

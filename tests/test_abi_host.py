@@ -301,3 +301,35 @@ def test_decode_step_status_argument_checks(dsa):
     assert L.dsa_decode_step_status(FAKE, 8, None) == E_WS
     for code in (-10, -11):
         assert dsa.status_string(code) != "unknown status"
+
+
+def test_int8_pool_argument_checks(dsa):
+    L = dsa.lib()
+    d = prod(dsa)
+    bd = ctypes.byref(d)
+    s = ctypes.byref(seqs(dsa))
+    # pool build: dtype, unsupported geometry, missing scales, misaligned codes
+    assert L.dsa_index_pools_int8(bd, FAKE, FAKE, 9, FAKE, FAKE, s, 1, FAKE, FAKE, 4, FAKE, FAKE, None, None) == E_DTYPE
+    d64 = prod(dsa, idx_dim=64)
+    assert L.dsa_index_pools_int8(ctypes.byref(d64), FAKE, FAKE, 1, FAKE, FAKE, s, 1, FAKE, FAKE, 4, FAKE, FAKE, None,
+                                  None) == E_UNSUP
+    assert L.dsa_index_pools_int8(bd, FAKE, FAKE, 1, FAKE, FAKE, s, 1, FAKE, FAKE, 4, FAKE, None, None, None) == E_NULL
+    assert L.dsa_index_pools_int8(bd, FAKE, FAKE, 1, FAKE, FAKE, s, 1, FAKE, FAKE, 4, MISALIGNED, FAKE, None,
+                                  None) == E_ALIGN
+    assert L.dsa_index_pools_int8(bd, FAKE, FAKE, 1, FAKE, FAKE, s, 1, FAKE, FAKE, 0, FAKE, FAKE, None, None) == OK
+    # scoring: decode shapes only (at most 64 queries)
+    assert L.dsa_index_scores_int8(bd, FAKE, FAKE, FAKE, FAKE, s, 1, FAKE, FAKE, 65, 256, FAKE, None) == E_UNSUP
+    assert L.dsa_index_scores_int8(bd, FAKE, FAKE, None, FAKE, s, 1, FAKE, FAKE, 4, 256, FAKE, None) == E_NULL
+    assert L.dsa_index_scores_int8(bd, FAKE, FAKE, MISALIGNED, FAKE, s, 1, FAKE, FAKE, 4, 256, FAKE, None) == E_ALIGN
+    ws = L.dsa_index_scores_select_workspace_bytes(bd, 4, 256)
+    assert L.dsa_index_scores_groups_int8(bd, FAKE, FAKE, FAKE, FAKE, s, 1, FAKE, FAKE, 4, 256, FAKE, FAKE, ws - 1,
+                                          None) == E_WS
+    # the single launch: bf16 new tokens only
+    args = [bd, 1, FAKE, 4, 512, FAKE, FAKE, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, s, 1,
+            FAKE, FAKE, 4, 256, FAKE, FAKE, ws, None]
+    bad = list(args)
+    bad[1] = 0
+    assert L.dsa_append_scores_groups_int8(*bad) == E_UNSUP
+    bad = list(args)
+    bad[16] = None                                         # scales
+    assert L.dsa_append_scores_groups_int8(*bad) == E_NULL
