@@ -341,3 +341,104 @@ class DeviceWorkload:
         self.step_topk()
         self.step_expand()
         self.step_attention(r)
+
+
+class PagedWorkload:
+    """The workload's caches in paged form: each sequence's positions in blocks
+    of 256, the physical blocks a seeded permutation (with spare blocks that no
+    sequence owns), built and stepped through the paged calls:
+
+      store_int8 (physical slots) -> index_pools_paged -> index_scores_groups_paged
+      -> topk_select_groups_paged -> sparse_mla
+
+    This class only marshals data; every computation runs in libdsa."""
+
+    def __init__(self, wl: syn.Workload, device="cuda", out_dtype=torch.float32, num_splits: int = 0,
+                 spare_blocks: int = 3, seed: int = 5, gen_workers: int = 8):
+        self.wl = wl
+        d = wl.dims
+        self.dims = dsa.Dims.of(d)
+        dev = self.device = torch.device(device)
+        self.num_splits = num_splits
+        nblk = [max(1, -(-int(n) // 256)) for n in wl.seq_len]
+        total = sum(nblk) + spare_blocks
+        perm = np.random.default_rng(seed).permutation(total).astype(np.int32)
+        table = np.full((wl.B, max(nblk)), perm[-1], dtype=np.int32)      # unused entries: a spare block
+        off = 0
+        for b, n in enumerate(nblk):
+            table[b, :n] = perm[off:off + n]
+            off += n
+        self.table_np = table
+        self.seqs = dsa.PagedSeqs(first_valid=torch.tensor(wl.first_valid, dtype=torch.int32, device=dev),
+                                  block_table=torch.from_numpy(table).to(dev))
+        self.q_seq = torch.tensor(wl.q_seq, dtype=torch.int32, device=dev)
+        self.q_pos = torch.tensor(wl.q_pos, dtype=torch.int32, device=dev)
+        T = wl.T
+        self.cache = torch.full((total * 256, d.row_bytes), 0x11, dtype=torch.int8, device=dev)
+        self.k = torch.zeros((total * 256, d.idx_dim), dtype=torch.bfloat16, device=dev)
+        self.gate = torch.zeros((total * 256, d.idx_dim), dtype=torch.bfloat16, device=dev)
+        self.pools = torch.zeros((total * 64, d.idx_dim), dtype=torch.bfloat16, device=dev)
+        lw, lb = syn.gen_ln(wl)
+        self.ln_w, self.ln_b = _f32(lw, dev), _f32(lb, dev)
+        self.q_idx = _bits_to_bf16(syn.gen_qidx(wl, 0, T), dev)
+        self.w = _f32(syn.gen_w(wl, 0, T), dev)
+        self.q = _bits_to_bf16(syn.gen_q(wl, 0, T), dev)
+        lat = np.concatenate([syn.gen_latent(wl, int(b), int(x), int(x) + 1) for b, x in zip(wl.q_seq, wl.q_pos)])
+        self.latent_q = _bits_to_bf16(lat, dev)
+        self.slots_q = torch.tensor([self.row(int(b), int(x)) for b, x in zip(wl.q_seq, wl.q_pos)], dtype=torch.int64,
+                                    device=dev)
+        pb, pe = [], []
+        for b in range(wl.B):
+            f = int(wl.first_valid[b])
+            ends = [(int(x) - f + 1) // d.kpool for x in wl.q_pos[wl.q_seq == b]
+                    if int(x) >= f and (int(x) - f + 1) % d.kpool == 0]
+            pb.append(min(ends) - 1 if ends else 0)
+            pe.append(max(ends) if ends else 0)
+        self.step_pool_begin = torch.tensor(pb, dtype=torch.int32, device=dev)
+        self.step_pool_end = torch.tensor(pe, dtype=torch.int32, device=dev)
+        self.step_max_pools = max([e - s for s, e in zip(pb, pe)] + [0])
+        self.stride = max(256, -(-max(wl.max_n_vis, 1) // 256) * 256)
+        self.scores = torch.empty((T, self.stride), dtype=torch.float32, device=dev)
+        self.pool_ids = torch.empty((T, d.select_k), dtype=torch.int32, device=dev)
+        self.indices = torch.empty((T, d.out_width), dtype=torch.int32, device=dev)
+        self.out = torch.empty((T, d.mla_heads, d.latent_dim), dtype=out_dtype, device=dev)
+        self.lse = torch.empty((T, d.mla_heads), dtype=torch.float32, device=dev)
+        self.ws = dsa.index_scores_select_workspace(self.dims, T, self.stride, device=dev)
+        n = dsa.sparse_mla_workspace_bytes(self.dims, T, num_splits)
+        self.ws_mla = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
+        # caches: every position's INT8 row and indexer state at its physical row, then every pool
+        for b in range(wl.B):
+            n_b = int(wl.seq_len[b])
+            for x0, lat_b in syn.gen_sequence_blocks(syn.gen_latent, wl, b, 0, n_b, workers=gen_workers):
+                rows = torch.from_numpy(self.rows(b, np.arange(x0, x0 + lat_b.shape[0]))).to(dev)
+                dsa.store_int8(self.dims, _bits_to_bf16(lat_b, dev), rows, self.cache)
+            for x0, (kk, gg) in syn.gen_sequence_blocks(syn.gen_kgate, wl, b, 0, n_b, workers=gen_workers):
+                rows = torch.from_numpy(self.rows(b, np.arange(x0, x0 + kk.shape[0]))).to(dev)
+                self.k[rows] = _bits_to_bf16(kk, dev)
+                self.gate[rows] = _bits_to_bf16(gg, dev)
+        ends = [wl.n_pools(b) for b in range(wl.B)]
+        if max(ends) > 0:
+            dsa.index_pools_paged(self.dims, self.k, self.gate, self.ln_w, self.ln_b, self.seqs,
+                                  torch.zeros(wl.B, dtype=torch.int32, device=dev),
+                                  torch.tensor(ends, dtype=torch.int32, device=dev), max(ends), self.pools)
+        torch.cuda.synchronize()
+
+    def row(self, b: int, x: int) -> int:
+        return int(self.table_np[b, x >> 8]) * 256 + (x & 255)
+
+    def rows(self, b: int, xs: np.ndarray) -> np.ndarray:
+        xs = np.asarray(xs, dtype=np.int64)
+        return self.table_np[b, xs >> 8].astype(np.int64) * 256 + (xs & 255)
+
+    def step(self):
+        """One decode step through the paged calls."""
+        dsa.store_int8(self.dims, self.latent_q, self.slots_q, self.cache)
+        if self.step_max_pools > 0:
+            dsa.index_pools_paged(self.dims, self.k, self.gate, self.ln_w, self.ln_b, self.seqs, self.step_pool_begin,
+                                  self.step_pool_end, self.step_max_pools, self.pools)
+        dsa.index_scores_groups_paged(self.dims, self.q_idx, self.w, self.pools, self.seqs, self.q_seq, self.q_pos,
+                                      self.scores, self.ws)
+        dsa.topk_select_groups_paged(self.dims, self.scores, self.seqs, self.q_seq, self.q_pos, self.indices, self.ws,
+                                     pool_ids=self.pool_ids)
+        dsa.sparse_mla(self.dims, self.q, self.cache, self.indices, self.wl.scale, self.out, self.lse,
+                       self.num_splits, self.ws_mla)

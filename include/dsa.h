@@ -98,6 +98,26 @@ typedef struct dsa_seqs {
     const int64_t* pool_base;    /* pool row of pool 0 */
 } dsa_seqs;
 
+/*
+ * Paged caches -- [Kernels] Install (the INT8 cache allocated as [n / 256,
+ * 256, 528]: blocks of 256 rows) and [Flash] What already exists (slot
+ * mappings for the latent, the per-token indexer state and the pooled state).
+ * A sequence's block table maps its i-th block of 256 positions to a physical
+ * block id k; block k holds latent cache rows 256 k .. 256 k + 255, indexer
+ * state (k, gate) rows 256 k .. 256 k + 255 and pool rows 64 k .. 64 k + 63.
+ * Position x of sequence b is row 256 * block_table[b * table_stride + x / 256]
+ * + x % 256; pool p is row 64 * block_table[b * table_stride + p / 64] + p % 64.
+ * The table must cover every position and pool a call touches.  New INT8 rows
+ * are written with dsa_store_int8 at their physical slots (the slot mapping);
+ * dsa_sparse_mla takes the index list the paged selection writes, whose
+ * entries are physical rows.
+ */
+typedef struct dsa_paged_seqs {
+    const int32_t* first_valid;  /* device [num_seqs]: left-padding length */
+    const int32_t* block_table;  /* device [num_seqs, table_stride]: physical block ids */
+    int32_t table_stride;        /* host: entries per sequence in block_table */
+} dsa_paged_seqs;
+
 int dsa_abi_version(void);
 const char* dsa_status_string(int status);
 
@@ -281,6 +301,29 @@ int dsa_index_scores_select(const dsa_dims* dims, const uint16_t* q_idx, const f
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * index_pools_paged / index_scores_groups_paged / topk_select_groups_paged --
+ * dsa_index_pools, dsa_index_scores_groups and dsa_topk_select_groups over
+ * paged caches: the same pools, scores, group lists and selection, bit for
+ * bit, with every k / gate row, pool row and index-list entry taken through
+ * the block table.  Arguments as the flat calls, with dsa_paged_seqs in place
+ * of dsa_seqs; the scoring workspace is the flat one
+ * (dsa_index_scores_select_workspace_bytes).  Supported: what the flat calls
+ * support.
+ */
+int dsa_index_pools_paged(const dsa_dims* dims, const void* k, const void* gate, int kg_dtype,
+                          const float* ln_w, const float* ln_b, const dsa_paged_seqs* seqs, int32_t num_seqs,
+                          const int32_t* pool_begin, const int32_t* pool_end, int32_t max_pools,
+                          uint16_t* pools, void* stream);
+int dsa_index_scores_groups_paged(const dsa_dims* dims, const uint16_t* q_idx, const float* w,
+                                  const uint16_t* pools, const dsa_paged_seqs* seqs, int32_t num_seqs,
+                                  const int32_t* q_seq, const int32_t* q_pos, int32_t T, int32_t score_stride,
+                                  float* scores, void* workspace, size_t workspace_bytes, void* stream);
+int dsa_topk_select_groups_paged(const dsa_dims* dims, const float* scores, int32_t score_stride,
+                                 const dsa_paged_seqs* seqs, int32_t num_seqs, const int32_t* q_seq,
+                                 const int32_t* q_pos, int32_t T, int32_t* pool_ids, int32_t* indices,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * INT8 pool cache -- [Flash] What is quantized (the indexer state cache row:
  * the sibling port stores its indexer cache as INT8 with one FP32 scale per
  * row).  A pool is kept as idx_dim INT8 codes (one row of idx_dim bytes) and
@@ -368,7 +411,10 @@ int dsa_append_scores_groups_shared(const dsa_dims* dims, int dtype, const void*
  * next group (the pages' integration keeps the indexer's workspaces bounded:
  * [Kernels] Included).  pool_ids and indices are those dsa_index_scores +
  * dsa_topk_select_expand give for all T queries at once; the scores are not
- * kept.
+ * kept.  For 32 x 128 indexer heads, select_k <= 512 and score_stride <=
+ * 65,536 the scoring pass also keeps each 64-pool group's best pools and the
+ * selection reads those lists (as dsa_index_scores_select does for decode);
+ * other geometries sort 256-pool tiles of the scores.
  *   q_idx .. score_stride   as dsa_index_scores
  *   chunk      host: queries per group (1 .. 65,535); the workspace holds
  *              chunk x score_stride scores, e.g. 512 x 33,792 x 4 B = 69 MB

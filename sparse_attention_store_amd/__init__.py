@@ -79,6 +79,29 @@ class Seqs:
                      self.tok_base.data_ptr(), self.pool_base.data_ptr())
 
 
+class _PagedSeqs(ctypes.Structure):
+    _fields_ = [("first_valid", ctypes.c_void_p), ("block_table", ctypes.c_void_p), ("table_stride", ctypes.c_int32)]
+
+
+@dataclass
+class PagedSeqs:
+    """Per-sequence layout of paged caches: int32 first_valid [B] and the int32
+    block table [B, stride] (physical block of each 256-position block)."""
+    first_valid: torch.Tensor
+    block_table: torch.Tensor
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.first_valid.shape[0])
+
+    def _c(self) -> _PagedSeqs:
+        _check(self.first_valid, torch.int32, "first_valid")
+        _check(self.block_table, torch.int32, "block_table")
+        if self.block_table.dim() != 2 or self.block_table.shape[0] != self.num_seqs:
+            raise ValueError("block_table must be [num_seqs, stride]")
+        return _PagedSeqs(self.first_valid.data_ptr(), self.block_table.data_ptr(), int(self.block_table.shape[1]))
+
+
 _lib = None
 
 
@@ -91,7 +114,7 @@ def lib() -> ctypes.CDLL:
                               "`python -m sparse_attention_store_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
-        DP, SP = ctypes.POINTER(Dims), ctypes.POINTER(_Seqs)
+        DP, SP, PP = ctypes.POINTER(Dims), ctypes.POINTER(_Seqs), ctypes.POINTER(_PagedSeqs)
         sig = {
             "dsa_abi_version": (ctypes.c_int, []),
             "dsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -127,6 +150,9 @@ def lib() -> ctypes.CDLL:
             "dsa_append_scores_groups_shared": (ctypes.c_int, [DP, ctypes.c_int, P, I64, I64, P, P, I64, P, P, P, P, P,
                                                                P, I32, P, P, P, P, SP, I32, P, P, I32, I32, P, P, SZ,
                                                                I32, P]),
+            "dsa_index_pools_paged": (ctypes.c_int, [DP, P, P, ctypes.c_int, P, P, PP, I32, P, P, I32, P, P]),
+            "dsa_index_scores_groups_paged": (ctypes.c_int, [DP, P, P, P, PP, I32, P, P, I32, I32, P, P, SZ, P]),
+            "dsa_topk_select_groups_paged": (ctypes.c_int, [DP, P, I32, PP, I32, P, P, I32, P, P, P, SZ, P]),
             "dsa_index_select_chunked_workspace_bytes": (SZ, [DP, I32, I32]),
             "dsa_index_select_chunked": (ctypes.c_int, [DP, P, P, P, SP, I32, P, P, I32, I32, I32, P, P, P, SZ, P]),
             "dsa_sparse_mla_noalloc_scratch_bytes": (SZ, []),
@@ -511,6 +537,53 @@ def append_scores_groups_shared(dims: Dims, latent: torch.Tensor | None, slots: 
                  workspace.numel() * workspace.element_size(), int(share), _stream(stream))
 
 
+def index_pools_paged(dims: Dims, k: torch.Tensor, gate: torch.Tensor, ln_w: torch.Tensor, ln_b: torch.Tensor,
+                      seqs: PagedSeqs, pool_begin: torch.Tensor, pool_end: torch.Tensor, max_pools: int,
+                      pools: torch.Tensor, stream=None, prepare: bool = False):
+    """index_pools over paged caches (k, gate and pools rows through the block table)."""
+    if k.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("k must be bf16 or fp32")
+    _check(k, k.dtype, "k")
+    _check(gate, k.dtype, "gate")
+    for t, dt, nm in ((ln_w, torch.float32, "ln_w"), (ln_b, torch.float32, "ln_b"),
+                      (pool_begin, torch.int32, "pool_begin"), (pool_end, torch.int32, "pool_end"),
+                      (pools, torch.bfloat16, "pools")):
+        _check(t, dt, nm)
+    return _call("dsa_index_pools_paged", prepare, ctypes.byref(dims), k.data_ptr(), gate.data_ptr(), _dt(k),
+                 ln_w.data_ptr(), ln_b.data_ptr(), ctypes.byref(seqs._c()), seqs.num_seqs, pool_begin.data_ptr(),
+                 pool_end.data_ptr(), int(max_pools), pools.data_ptr(), _stream(stream))
+
+
+def index_scores_groups_paged(dims: Dims, q_idx: torch.Tensor, w: torch.Tensor, pools: torch.Tensor,
+                              seqs: PagedSeqs, q_seq: torch.Tensor, q_pos: torch.Tensor, scores: torch.Tensor,
+                              workspace: torch.Tensor, stream=None, prepare: bool = False):
+    """index_scores_groups over paged pools."""
+    for t, dt, nm in ((q_idx, torch.bfloat16, "q_idx"), (w, torch.float32, "w"), (pools, torch.bfloat16, "pools"),
+                      (q_seq, torch.int32, "q_seq"), (q_pos, torch.int32, "q_pos"), (scores, torch.float32, "scores")):
+        _check(t, dt, nm)
+    _check(workspace, workspace.dtype, "workspace")
+    return _call("dsa_index_scores_groups_paged", prepare, ctypes.byref(dims), q_idx.data_ptr(), w.data_ptr(),
+                 pools.data_ptr(), ctypes.byref(seqs._c()), seqs.num_seqs, q_seq.data_ptr(), q_pos.data_ptr(),
+                 q_seq.shape[0], scores.shape[1], scores.data_ptr(), workspace.data_ptr(),
+                 workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def topk_select_groups_paged(dims: Dims, scores: torch.Tensor, seqs: PagedSeqs, q_seq: torch.Tensor,
+                             q_pos: torch.Tensor, indices: torch.Tensor, workspace: torch.Tensor,
+                             pool_ids: torch.Tensor | None = None, stream=None, prepare: bool = False):
+    """topk_select_groups writing the index list as physical rows of paged caches."""
+    for t, dt, nm in ((scores, torch.float32, "scores"), (q_seq, torch.int32, "q_seq"), (q_pos, torch.int32, "q_pos"),
+                      (indices, torch.int32, "indices")):
+        _check(t, dt, nm)
+    _check(workspace, workspace.dtype, "workspace")
+    if pool_ids is not None:
+        _check(pool_ids, torch.int32, "pool_ids")
+    return _call("dsa_topk_select_groups_paged", prepare, ctypes.byref(dims), scores.data_ptr(), scores.shape[1],
+                 ctypes.byref(seqs._c()), seqs.num_seqs, q_seq.data_ptr(), q_pos.data_ptr(), q_seq.shape[0],
+                 _ptr(pool_ids), indices.data_ptr(), workspace.data_ptr(),
+                 workspace.numel() * workspace.element_size(), _stream(stream))
+
+
 def index_select_chunked_workspace(dims: Dims, chunk: int, score_stride: int, device="cuda") -> torch.Tensor:
     n = int(lib().dsa_index_select_chunked_workspace_bytes(ctypes.byref(dims), int(chunk), int(score_stride)))
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
@@ -727,5 +800,6 @@ __all__ = [
     "decode_step_workspace_bytes", "decode_step_workspace", "decode_step_error", "decode_step",
     "sparse_mla_noalloc_scratch_bytes", "sparse_mla_noalloc", "index_select_chunked_workspace",
     "index_select_chunked", "index_pools_int8", "index_scores_int8", "index_scores_groups_int8",
-    "append_scores_groups_int8", "append_scores_groups_shared",
+    "append_scores_groups_int8", "append_scores_groups_shared", "PagedSeqs", "index_pools_paged",
+    "index_scores_groups_paged", "topk_select_groups_paged",
 ]

@@ -477,6 +477,74 @@ int dsa_append_scores_groups_shared(const dsa_dims* dims, int dtype, const void*
         scoring ? score_stride : 0, scores, workspace, share, as_stream(stream)));
 }
 
+// ------------------------------------------------------------------ paged caches
+
+static int check_paged(const dsa_paged_seqs* s, int32_t num_seqs) {
+    if (!s) return DSA_ERR_NULL;
+    if (num_seqs <= 0 || s->table_stride <= 0) return DSA_ERR_SIZE;
+    if (!s->first_valid || !s->block_table) return DSA_ERR_NULL;
+    return DSA_OK;
+}
+
+int dsa_index_pools_paged(const dsa_dims* dims, const void* k, const void* gate, int kg_dtype, const float* ln_w,
+                          const float* ln_b, const dsa_paged_seqs* seqs, int32_t num_seqs, const int32_t* pool_begin,
+                          const int32_t* pool_end, int32_t max_pools, uint16_t* pools, void* stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (kg_dtype != DSA_F32 && kg_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    if (dims->kpool != 4 || (dims->idx_dim != 128 && dims->idx_dim != 32)) return DSA_ERR_UNSUPPORTED;
+    st = check_paged(seqs, num_seqs);
+    if (st) return st;
+    if (max_pools < 0) return DSA_ERR_SIZE;
+    if (max_pools == 0) return DSA_OK;
+    if (num_seqs > 65535) return DSA_ERR_SIZE;
+    if (!k || !gate || !ln_w || !ln_b || !pool_begin || !pool_end || !pools) return DSA_ERR_NULL;
+    if (!aligned(pools, 4)) return DSA_ERR_ALIGN;
+    return hip_status(dsa_host::launch_index_pools_paged(*dims, k, gate, kg_dtype, ln_w, ln_b, seqs->first_valid,
+                                                         seqs->block_table, seqs->table_stride, num_seqs, pool_begin,
+                                                         pool_end, max_pools, pools, as_stream(stream)));
+}
+
+static int paged_groups_common(const dsa_dims* dims, const dsa_paged_seqs* seqs, int32_t num_seqs, int32_t T,
+                               int32_t score_stride, void* workspace, size_t workspace_bytes) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (T < 0 || score_stride < 0) return DSA_ERR_SIZE;
+    st = check_paged(seqs, num_seqs);
+    if (st) return st;
+    if (T > 0 && !dsa_host::scores_select_grouped(*dims, T, score_stride)) return DSA_ERR_UNSUPPORTED;
+    if (T == 0 || score_stride == 0) return DSA_OK;
+    if (!workspace || workspace_bytes < dsa_host::scores_select_group_bytes(T)) return DSA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return DSA_ERR_ALIGN;
+    return DSA_OK;
+}
+
+int dsa_index_scores_groups_paged(const dsa_dims* dims, const uint16_t* q_idx, const float* w, const uint16_t* pools,
+                                  const dsa_paged_seqs* seqs, int32_t num_seqs, const int32_t* q_seq,
+                                  const int32_t* q_pos, int32_t T, int32_t score_stride, float* scores,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    int st = paged_groups_common(dims, seqs, num_seqs, T, score_stride, workspace, workspace_bytes);
+    if (st || T == 0 || score_stride == 0) return st;
+    if (!q_idx || !w || !pools || !q_seq || !q_pos || !scores) return DSA_ERR_NULL;
+    if (!aligned(q_idx, 16) || !aligned(pools, 16) || !aligned(w, 16)) return DSA_ERR_ALIGN;
+    return hip_status(dsa_host::launch_scores_with_groups_paged(*dims, q_idx, w, pools, seqs->first_valid,
+                                                                seqs->block_table, seqs->table_stride, num_seqs,
+                                                                q_seq, q_pos, T, score_stride, scores, workspace,
+                                                                as_stream(stream)));
+}
+
+int dsa_topk_select_groups_paged(const dsa_dims* dims, const float* scores, int32_t score_stride,
+                                 const dsa_paged_seqs* seqs, int32_t num_seqs, const int32_t* q_seq,
+                                 const int32_t* q_pos, int32_t T, int32_t* pool_ids, int32_t* indices,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    int st = paged_groups_common(dims, seqs, num_seqs, T, score_stride, workspace, workspace_bytes);
+    if (st || T == 0 || score_stride == 0) return st;
+    if (!scores || !q_seq || !q_pos || !indices) return DSA_ERR_NULL;
+    return hip_status(dsa_host::launch_topk_groups_paged(*dims, scores, score_stride, seqs->first_valid,
+                                                         seqs->block_table, seqs->table_stride, q_seq, q_pos, T,
+                                                         pool_ids, indices, workspace, as_stream(stream)));
+}
+
 int dsa_time_next_scoring_launch(void* start_event, void* stop_event) {
     if ((start_event == nullptr) != (stop_event == nullptr)) return DSA_ERR_NULL;
     dsa_host::time_next_scoring_launch(reinterpret_cast<hipEvent_t>(start_event),
@@ -533,8 +601,16 @@ static size_t chunk_scores_bytes(int32_t chunk, int32_t score_stride) {
     return ((size_t)chunk * (size_t)score_stride * 4 + 255) / 256 * 256;
 }
 
+// The chunked selection keeps 64-pool group lists in the scoring pass (then
+// selects from them) when the geometry allows it, else sorts score tiles.
+static bool chunked_grouped(const dsa_dims* d, int32_t chunk, int32_t score_stride) {
+    return dsa_host::scores_select_grouped(*d, std::min<int32_t>(chunk, 64), score_stride);
+}
+
 size_t dsa_index_select_chunked_workspace_bytes(const dsa_dims* dims, int32_t chunk, int32_t score_stride) {
     if (check_dims(dims) != DSA_OK || chunk <= 0 || score_stride <= 0) return 0;
+    if (chunked_grouped(dims, chunk, score_stride))
+        return chunk_scores_bytes(chunk, score_stride) + dsa_host::scores_select_group_bytes(chunk);
     return chunk_scores_bytes(chunk, score_stride) + dsa_host::topk_workspace_bytes(*dims, chunk, score_stride);
 }
 
@@ -559,15 +635,27 @@ int dsa_index_select_chunked(const dsa_dims* dims, const uint16_t* q_idx, const 
     float* scores = reinterpret_cast<float*>(workspace);
     void* tws = reinterpret_cast<char*>(workspace) + chunk_scores_bytes(chunk, score_stride);
     const int HI = dims->idx_heads, DI = dims->idx_dim, K = dims->index_topk / dims->kpool, W = dims->out_width;
+    const bool grouped = chunked_grouped(dims, chunk, score_stride);
     hipStream_t s = as_stream(stream);
     for (int32_t t0 = 0; t0 < T; t0 += chunk) {
         const int32_t n = std::min(chunk, T - t0);
-        hipError_t e = dsa_host::launch_index_scores(*dims, q_idx + (int64_t)t0 * HI * DI, w + (int64_t)t0 * HI,
-                                                     pools, *seqs, num_seqs, q_seq + t0, q_pos + t0, n, score_stride,
-                                                     scores, s);
-        if (e != hipSuccess) return DSA_ERR_HIP;
-        e = dsa_host::launch_topk(*dims, scores, score_stride, *seqs, q_seq + t0, q_pos + t0, n,
-                                  pool_ids ? pool_ids + (int64_t)t0 * K : nullptr, indices + (int64_t)t0 * W, tws, s);
+        const uint16_t* qi = q_idx + (int64_t)t0 * HI * DI;
+        const float* wt = w + (int64_t)t0 * HI;
+        int32_t* pid = pool_ids ? pool_ids + (int64_t)t0 * K : nullptr;
+        int32_t* idx = indices + (int64_t)t0 * W;
+        hipError_t e;
+        if (grouped) {
+            e = dsa_host::launch_scores_lists(*dims, qi, wt, pools, *seqs, num_seqs, q_seq + t0, q_pos + t0, n,
+                                              score_stride, scores, tws, s);
+            if (e != hipSuccess) return DSA_ERR_HIP;
+            e = dsa_host::launch_topk_groups(*dims, scores, score_stride, *seqs, q_seq + t0, q_pos + t0, n, pid, idx,
+                                             tws, s);
+        } else {
+            e = dsa_host::launch_index_scores(*dims, qi, wt, pools, *seqs, num_seqs, q_seq + t0, q_pos + t0, n,
+                                              score_stride, scores, s);
+            if (e != hipSuccess) return DSA_ERR_HIP;
+            e = dsa_host::launch_topk(*dims, scores, score_stride, *seqs, q_seq + t0, q_pos + t0, n, pid, idx, tws, s);
+        }
         if (e != hipSuccess) return DSA_ERR_HIP;
     }
     return DSA_OK;

@@ -31,6 +31,12 @@ hipError_t launch_index_scores(const dsa_dims& d, const uint16_t* q_idx, const f
                                hipStream_t s);
 
 bool scores_select_grouped(const dsa_dims& d, int32_t T, int32_t stride);
+// Scores plus each 64-pool group's best pools, for any T (group-list geometry:
+// scores_select_grouped(d, min(T, 64), stride)); the lists are laid out as
+// launch_scores_with_groups lays them out for T queries.
+hipError_t launch_scores_lists(const dsa_dims& d, const uint16_t* q_idx, const float* w, const uint16_t* pools,
+                               const dsa_seqs& seqs, int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos,
+                               int32_t T, int32_t stride, float* scores, void* ws, hipStream_t s);
 size_t scores_select_group_bytes(int32_t T);
 hipError_t launch_scores_with_groups(const dsa_dims& d, const uint16_t* q_idx, const float* w,
                                      const uint16_t* pools, const dsa_seqs& seqs, int32_t num_seqs,
@@ -62,6 +68,21 @@ hipError_t launch_append_scores_groups_runs(const dsa_dims& d, const void* laten
                                             int32_t max_pools, void* pools, float* scales, const uint16_t* q_idx,
                                             const float* w, const int32_t* q_seq, const int32_t* q_pos, int32_t T,
                                             int32_t stride, float* scores, void* ws, int share, hipStream_t s);
+
+// Paged caches (paged.h): every position / pool row through a block table.
+hipError_t launch_index_pools_paged(const dsa_dims& d, const void* k, const void* gate, int dtype, const float* ln_w,
+                                    const float* ln_b, const int32_t* first_valid, const int32_t* table,
+                                    int32_t table_stride, int32_t num_seqs, const int32_t* pool_begin,
+                                    const int32_t* pool_end, int32_t max_pools, uint16_t* pools, hipStream_t s);
+hipError_t launch_scores_with_groups_paged(const dsa_dims& d, const uint16_t* q_idx, const float* w,
+                                           const uint16_t* pools, const int32_t* first_valid, const int32_t* table,
+                                           int32_t table_stride, int32_t num_seqs, const int32_t* q_seq,
+                                           const int32_t* q_pos, int32_t T, int32_t stride, float* scores, void* ws,
+                                           hipStream_t s);
+hipError_t launch_topk_groups_paged(const dsa_dims& d, const float* scores, int32_t stride, const int32_t* first_valid,
+                                    const int32_t* table, int32_t table_stride, const int32_t* q_seq,
+                                    const int32_t* q_pos, int32_t T, int32_t* pool_ids, int32_t* indices,
+                                    const void* ws, hipStream_t s);
 
 // INT8 pools (code rows of idx_dim bytes and one fp32 scale per pool).
 hipError_t launch_index_pools_int8(const dsa_dims& d, const void* k, const void* gate, int dtype,

@@ -20,19 +20,25 @@
 #include "topk_core.h"
 #include "new_tokens.h"
 #include "scores_decode.h"
+#include "paged.h"
 
 namespace dsa {
 
 constexpr int kQROW = kDI + 8;                        // padded LDS row (bf16 elements)
 constexpr int kQBYTES = kHI * kDI * 2;                // 8 KB per query
 
-template <int WAVES, int QB>
+//
+// With CANDS each wave also keeps, per query, the best pools of its 64-pool
+// group (keep_group_best, as the decode kernel does): lane l of a wave holds
+// pool p0 + l, so the wave is one group.  The selection then reads the group
+// lists (k_topk_groups) instead of sorting 256-pool tiles of the scores.
+template <int WAVES, int QB, bool CANDS = false>
 __global__ __launch_bounds__(WAVES * 64) void k_scores_mfma(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint16_t* __restrict__ pools, const int32_t* __restrict__ first_valid,
     const int64_t* __restrict__ pool_base, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_pos, int T, int q_per_block, int stride,
-    float* __restrict__ scores) {
+    float* __restrict__ scores, int select_k, uint64_t* __restrict__ cand, int32_t* __restrict__ cand_n) {
     constexpr int NT = WAVES * 64;
     constexpr int CHUNKS = QB * kQBYTES / 16;              // 16-byte pieces per batch
     constexpr int PER_T = (CHUNKS + NT - 1) / NT;
@@ -140,6 +146,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_scores_mfma(
             const float sv = g == 0 ? s0 : s1;
             const int p = p0 + g * 32 + n;                 // lanes 0-31: tile 0, 32-63: tile 1
             if (p < stride) out[p] = p < n_vis ? sv : -INFINITY;
+            if constexpr (CANDS) {
+                if (n_vis > select_k)
+                    keep_group_best(sv, p < n_vis, p, p0 / kGroupPools, group_quota(select_k, n_vis),
+                                    cand + (int64_t)t * kGroupCandCap, cand_n + (int64_t)t * kMaxGroups,
+                                    [](uint64_t* q, uint64_t x) { *q = x; },
+                                    [](int32_t* q, uint32_t x) { *q = (int32_t)x; });
+            }
         }
     }
 }
@@ -180,14 +193,18 @@ struct QueryGeom {
 // With I8 the pools are INT8 code rows with one fp32 scale each
 // (score_pool_group_i8): each wave loads 8 KB of codes and its pools' scales,
 // and a rebuilt pool is quantised the way the pool tasks store it.
-template <bool CANDS, int AD, bool I8 = false>
+//
+// With PAGED the pools are paged (paged.h): a query's sequence index is kept in
+// place of its pool base, and a group's 64 rows are one pool block, found in
+// the block table.
+template <bool CANDS, int AD, bool I8 = false, bool PAGED = false>
 __global__ __launch_bounds__(256, 4) void k_scores_groups(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const void* pools_v, const int32_t* __restrict__ first_valid,
     const int64_t* __restrict__ pool_base, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_pos, int T, int nseq, int stride, float* __restrict__ scores,
     int select_k, uint64_t* __restrict__ cand, int32_t* __restrict__ cand_n, AppendArgs ap,
-    float* pool_scales) {
+    float* pool_scales, PagedMap pm) {
     __shared__ QueryGeom geom[kDecMaxT];
     __shared__ __attribute__((aligned(16))) uint16_t s_q[kHI * kQStride];
     __shared__ __attribute__((aligned(16))) float s_w[kHI];
@@ -211,7 +228,8 @@ __global__ __launch_bounds__(256, 4) void k_scores_groups(
         u32x2 bs, ts;
         auto fields = [&](uint32_t s4) {
             f = (int)__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(first_valid, sb), s4, 0, 0);
-            bs = __builtin_amdgcn_raw_buffer_load_b64(buffer_rsrc(pool_base, 2u * sb), 2u * s4, 0, 0);
+            // (PAGED: no pool bases; the descriptor's range is empty, so nothing is read)
+            bs = __builtin_amdgcn_raw_buffer_load_b64(buffer_rsrc(pool_base, PAGED ? 0u : 2u * sb), 2u * s4, 0, 0);
             pb_s = (int)__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(ap.pool_begin, pbb), s4, 0, 0);
             pe_s = (int)__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(ap.pool_end, pbb), s4, 0, 0);
             ts = __builtin_amdgcn_raw_buffer_load_b64(buffer_rsrc(ap.tok_base, 2u * pbb), 2u * s4, 0, 0);
@@ -232,7 +250,7 @@ __global__ __launch_bounds__(256, 4) void k_scores_groups(
         int64_t base = 0, tok0 = 0;
         if (lane < T) {
             nn = min(qp >= f ? (qp - f + 1) >> 2 : 0, stride);
-            base = (int64_t)(((uint64_t)bs[1] << 32) | bs[0]);
+            base = PAGED ? (int64_t)b : (int64_t)(((uint64_t)bs[1] << 32) | bs[0]);
             if (pools_ad) {
                 pb = pb_s;
                 pe = min(pe_s, pb + 4 * ap.pool_bx);          // what the pool tasks build
@@ -291,7 +309,8 @@ __global__ __launch_bounds__(256, 4) void k_scores_groups(
         float psc = 0.f;                               // INT8: the scale of pool p0 + lane
         const int lp0 = has ? p0 : p0 - kGroupPools * wave;
         {
-            const int64_t row0 = (int64_t)uniform64((uint64_t)geom[t].base) + lp0;
+            const int64_t gb = (int64_t)uniform64((uint64_t)geom[t].base);
+            const int64_t row0 = PAGED ? pm.block((int)gb, lp0 / kPagePools) * kPagePools : gb + lp0;
             const int lim = has ? n_vis - p0 : 1;
             if constexpr (I8) {
                 load_pool_group_i8(codes + row0 * kDI, lim, v);
@@ -503,7 +522,7 @@ hipError_t launch_index_scores(const dsa_dims& d, const uint16_t* q_idx, const f
             take_events(ev0, ev1);
             hipExtLaunchKernelGGL((dsa::k_scores_groups<false, 0>), dim3(scores_groups_grid(T, stride)), dim3(256), 0,
                                   s, ev0, ev1, 0, q_idx, w, pools, seqs.first_valid, seqs.pool_base, q_seq,
-                                  q_pos, T, num_seqs, stride, scores, 0, nullptr, nullptr, dsa::AppendArgs{}, nullptr);
+                                  q_pos, T, num_seqs, stride, scores, 0, nullptr, nullptr, dsa::AppendArgs{}, nullptr, dsa::PagedMap{});
         } else {
             // Prefill: 512 resident pools per workgroup, 64 queries per workgroup.
             const int qpb = 64;
@@ -511,7 +530,8 @@ hipError_t launch_index_scores(const dsa_dims& d, const uint16_t* q_idx, const f
             hipEvent_t ev0, ev1;
             take_events(ev0, ev1);
             hipExtLaunchKernelGGL((dsa::k_scores_mfma<8, 4>), grid, block, 0, s, ev0, ev1, 0, q_idx, w, pools,
-                                  seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, qpb, stride, scores);
+                                  seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, qpb, stride, scores, 0,
+                                  nullptr, nullptr);
         }
     } else {
         dim3 grid((unsigned)cdiv(stride, 256), (unsigned)T), block(256);
@@ -519,6 +539,27 @@ hipError_t launch_index_scores(const dsa_dims& d, const uint16_t* q_idx, const f
                            seqs.first_valid, seqs.pool_base, q_seq, q_pos, d.idx_heads, d.idx_dim,
                            stride, scores);
     }
+    return hipGetLastError();
+}
+
+// Scores and group lists for any number of queries: the decode kernel for
+// at most 64, the prefill kernel (with its group lists) for more.
+hipError_t launch_scores_lists(const dsa_dims& d, const uint16_t* q_idx, const float* w, const uint16_t* pools,
+                               const dsa_seqs& seqs, int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos,
+                               int32_t T, int32_t stride, float* scores, void* ws, hipStream_t s) {
+    if (T == 0 || stride == 0) return hipSuccess;
+    if (T <= dsa::kDecMaxT)
+        return launch_scores_with_groups(d, q_idx, w, pools, seqs, num_seqs, q_seq, q_pos, T, stride, scores, ws, s);
+    uint64_t* cand;
+    int32_t* cand_n;
+    group_lists(ws, T, cand, cand_n);
+    const int qpb = 64;
+    dim3 grid((unsigned)cdiv(stride, 512), (unsigned)cdiv(T, qpb)), block(512);
+    hipEvent_t ev0, ev1;
+    take_events(ev0, ev1);
+    hipExtLaunchKernelGGL((dsa::k_scores_mfma<8, 4, true>), grid, block, 0, s, ev0, ev1, 0, q_idx, w, pools,
+                          seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, qpb, stride, scores,
+                          d.index_topk / d.kpool, cand, cand_n);
     return hipGetLastError();
 }
 
@@ -544,7 +585,7 @@ hipError_t launch_scores_with_groups(const dsa_dims& d, const uint16_t* q_idx, c
     take_events(ev0, ev1);
     hipExtLaunchKernelGGL((dsa::k_scores_groups<true, 0>), dim3(scores_groups_grid(T, stride)), dim3(256), 0, s,
                           ev0, ev1, 0, q_idx, w, pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T,
-                          num_seqs, stride, scores, d.index_topk / d.kpool, cand, cand_n, dsa::AppendArgs{}, nullptr);
+                          num_seqs, stride, scores, d.index_topk / d.kpool, cand, cand_n, dsa::AppendArgs{}, nullptr, dsa::PagedMap{});
     return hipGetLastError();
 }
 
@@ -575,7 +616,7 @@ hipError_t launch_append_scores_groups(const dsa_dims& d, const void* latent, in
 #define DSA_APPEND_SCORES(D)                                                                                        \
     hipExtLaunchKernelGGL((dsa::k_scores_groups<true, D>), dim3(grid), dim3(256), 0, s, ev0, ev1, 0, q_idx, w,    \
                           pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, num_seqs, stride,  \
-                          scores, d.index_topk / d.kpool, cand, cand_n, ap, nullptr)
+                          scores, d.index_topk / d.kpool, cand, cand_n, ap, nullptr, dsa::PagedMap{})
     switch (d.latent_dim) {
         case 512: DSA_APPEND_SCORES(512); break;
         case 256: DSA_APPEND_SCORES(256); break;
@@ -583,6 +624,26 @@ hipError_t launch_append_scores_groups(const dsa_dims& d, const void* latent, in
         default: DSA_APPEND_SCORES(64); break;
     }
 #undef DSA_APPEND_SCORES
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ paged pools
+
+hipError_t launch_scores_with_groups_paged(const dsa_dims& d, const uint16_t* q_idx, const float* w,
+                                           const uint16_t* pools, const int32_t* first_valid, const int32_t* table,
+                                           int32_t table_stride, int32_t num_seqs, const int32_t* q_seq,
+                                           const int32_t* q_pos, int32_t T, int32_t stride, float* scores, void* ws,
+                                           hipStream_t s) {
+    if (T == 0 || stride == 0) return hipSuccess;
+    uint64_t* cand;
+    int32_t* cand_n;
+    group_lists(ws, T, cand, cand_n);
+    hipEvent_t ev0, ev1;
+    take_events(ev0, ev1);
+    hipExtLaunchKernelGGL((dsa::k_scores_groups<true, 0, false, true>), dim3(scores_groups_grid(T, stride)), dim3(256),
+                          0, s, ev0, ev1, 0, q_idx, w, pools, first_valid, nullptr, q_seq, q_pos, T, num_seqs, stride,
+                          scores, d.index_topk / d.kpool, cand, cand_n, dsa::AppendArgs{}, nullptr,
+                          dsa::PagedMap{table, table_stride});
     return hipGetLastError();
 }
 
@@ -597,7 +658,7 @@ hipError_t launch_index_scores_int8(const dsa_dims& d, const uint16_t* q_idx, co
     hipExtLaunchKernelGGL((dsa::k_scores_groups<false, 0, true>), dim3(scores_groups_grid(T, stride)), dim3(256), 0, s,
                           ev0, ev1, 0, q_idx, w, codes, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T,
                           num_seqs, stride, scores, 0, nullptr, nullptr, dsa::AppendArgs{},
-                          const_cast<float*>(scales));
+                          const_cast<float*>(scales), dsa::PagedMap{});
     return hipGetLastError();
 }
 
@@ -614,7 +675,7 @@ hipError_t launch_scores_with_groups_int8(const dsa_dims& d, const uint16_t* q_i
     hipExtLaunchKernelGGL((dsa::k_scores_groups<true, 0, true>), dim3(scores_groups_grid(T, stride)), dim3(256), 0, s,
                           ev0, ev1, 0, q_idx, w, codes, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T,
                           num_seqs, stride, scores, d.index_topk / d.kpool, cand, cand_n, dsa::AppendArgs{},
-                          const_cast<float*>(scales));
+                          const_cast<float*>(scales), dsa::PagedMap{});
     return hipGetLastError();
 }
 
@@ -638,7 +699,7 @@ hipError_t launch_append_scores_groups_int8(const dsa_dims& d, const void* laten
 #define DSA_APPEND_SCORES8(D)                                                                                       \
     hipExtLaunchKernelGGL((dsa::k_scores_groups<true, D, true>), dim3(grid), dim3(256), 0, s, ev0, ev1, 0, q_idx, \
                           w, codes, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, num_seqs, stride, \
-                          scores, d.index_topk / d.kpool, cand, cand_n, ap, scales)
+                          scores, d.index_topk / d.kpool, cand, cand_n, ap, scales, dsa::PagedMap{})
     switch (d.latent_dim) {
         case 512: DSA_APPEND_SCORES8(512); break;
         case 256: DSA_APPEND_SCORES8(256); break;
