@@ -291,8 +291,10 @@ class DeviceWorkload:
     TIMED_STAGES = ("append_scores", "select_attention")
 
     def fast_supported(self) -> bool:
-        """Group lists are kept for at most 64 queries of at most 65,536 pools."""
-        return self.wl.T <= 64 and self.stride <= 65536 and self.wl.dims.idx_heads == 32 and \
+        """Group lists are kept for at most 64 queries of at most 262,144 pools
+        (65,536 for shared runs)."""
+        limit = 65536 if self.share > 1 else 262144
+        return self.wl.T <= 64 and self.stride <= limit and self.wl.dims.idx_heads == 32 and \
             self.wl.dims.idx_dim == 128 and (not self.int8 or self.latent_q.dtype == torch.bfloat16)
 
     def step_fast(self, r: int = 0):

@@ -401,6 +401,20 @@ def mini_heavy(seed: int = 13) -> Workload:
                np.arange(3), np.array(sl) - 1, latent_dist="t3")
 
 
+def mini_long(seed: int = 16) -> Workload:
+    """Rows past 65,536 pools (256-pool groups in the scoring lists) at the
+    fewest tokens that reach them: two sequences of 65,537 and 70,000 pools,
+    queried at 65,537 pools (a last group of one pool), 65,536 (the last row
+    of 64-pool groups), 65,792 (a full last 256-pool group), 70,000 and
+    20,000 pools, with tails of 0 to 3 tokens."""
+    fv = [1, 3]
+    v = [4 * 65537 + 2, 4 * 70000 + 1]
+    sl = [a + b for a, b in zip(fv, v)]
+    qs = [0, 0, 1, 1, 1]
+    qp = [sl[0] - 1, fv[0] + 4 * 65536 + 1, fv[1] + 4 * 65792 - 1, sl[1] - 1, fv[1] + 4 * 20000]
+    return _mk("mini_long", seed, production_dims(16), fv, sl, 280004, 70001, qs, qp)
+
+
 def _with_drafts(wl: Workload, name: str, k: int = 4, note: str = "") -> Workload:
     """The same sequences, each issuing k queries at its last k positions (a
     speculative decode step: the accepted token and k - 1 drafts, scored
@@ -437,6 +451,7 @@ WORKLOADS = {
     "prefill_4k_on_131k": prefill_4k_on_131k, "decode_1m_b4": decode_1m_b4,
     "mini_decode": mini_decode, "mini_decode_64": mini_decode_64, "mini_prefill": mini_prefill,
     "mini_heavy": mini_heavy, "mini_mtp": mini_mtp, "decode_262k_b8_mtp": decode_262k_b8_mtp,
+    "mini_long": mini_long,
 }
 
 

@@ -240,7 +240,7 @@ __device__ void step_select(const StepArgs& a, StepSelSmem& sm, StepPlan& plan, 
     const int tid = threadIdx.x;
     const int n = plan.nvis[t], K = a.select_k;
     const int groups = (n + kSGroup - 1) / kSGroup;
-    const int m = group_quota(K, n);
+    const int m = group_quota<true>(K, n);
     const int msh = __ffs(m) - 1;
     const int M = groups * m;
     const int32_t* cn = a.cand_n + (int64_t)t * kStepMaxGroups;
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(kStepNT, 1) void k_decode_step(StepArgs a) {
             // ============================ scoring tile
             const int p0 = jj * kSTile;
             const int nvis = plan.nvis[t];
-            const int m = nvis > a.select_k ? group_quota(a.select_k, nvis) : 0;
+            const int m = nvis > a.select_k ? group_quota<true>(a.select_k, nvis) : 0;
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const float s = score_pool_group(Q, v[half]);

@@ -236,13 +236,15 @@ size_t dsa_index_scores_select_workspace_bytes(const dsa_dims* dims, int32_t T, 
 }
 
 static int groups_common(const dsa_dims* dims, const dsa_seqs* seqs, int32_t num_seqs, int32_t T,
-                         int32_t score_stride, void* workspace, size_t workspace_bytes) {
+                         int32_t score_stride, void* workspace, size_t workspace_bytes, bool long_rows = true) {
     int st = check_dims(dims);
     if (st) return st;
     if (T < 0 || score_stride < 0) return DSA_ERR_SIZE;
     st = check_seqs(seqs, num_seqs, true, false, true);
     if (st) return st;
-    if (T > 0 && !dsa_host::scores_select_grouped(*dims, T, score_stride)) return DSA_ERR_UNSUPPORTED;
+    if (T > 0 && !(long_rows ? dsa_host::scores_select_grouped(*dims, T, score_stride)
+                             : dsa_host::scores_lists_short(*dims, T, score_stride)))
+        return DSA_ERR_UNSUPPORTED;
     if (T == 0 || score_stride == 0) return DSA_OK;
     if (!workspace || workspace_bytes < dsa_host::scores_select_group_bytes(T)) return DSA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return DSA_ERR_ALIGN;
@@ -452,7 +454,7 @@ int dsa_append_scores_groups_shared(const dsa_dims* dims, int dtype, const void*
         if (ld < D) return DSA_ERR_SIZE;
         if (!aligned(latent, 16) || (ld * 2) % 16 != 0 || !aligned(cache, 16)) return DSA_ERR_ALIGN;
     }
-    st = groups_common(dims, seqs, num_seqs, T, score_stride, workspace, workspace_bytes);
+    st = groups_common(dims, seqs, num_seqs, T, score_stride, workspace, workspace_bytes, false);   // runs: 64-pool groups
     if (st) return st;
     if (!int8_scoring_supported(dims, T)) return DSA_ERR_UNSUPPORTED;
     if (max_pools > 0) {
@@ -512,7 +514,7 @@ static int paged_groups_common(const dsa_dims* dims, const dsa_paged_seqs* seqs,
     if (T < 0 || score_stride < 0) return DSA_ERR_SIZE;
     st = check_paged(seqs, num_seqs);
     if (st) return st;
-    if (T > 0 && !dsa_host::scores_select_grouped(*dims, T, score_stride)) return DSA_ERR_UNSUPPORTED;
+    if (T > 0 && !dsa_host::scores_lists_short(*dims, T, score_stride)) return DSA_ERR_UNSUPPORTED;
     if (T == 0 || score_stride == 0) return DSA_OK;
     if (!workspace || workspace_bytes < dsa_host::scores_select_group_bytes(T)) return DSA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return DSA_ERR_ALIGN;
@@ -604,7 +606,7 @@ static size_t chunk_scores_bytes(int32_t chunk, int32_t score_stride) {
 // The chunked selection keeps 64-pool group lists in the scoring pass (then
 // selects from them) when the geometry allows it, else sorts score tiles.
 static bool chunked_grouped(const dsa_dims* d, int32_t chunk, int32_t score_stride) {
-    return dsa_host::scores_select_grouped(*d, std::min<int32_t>(chunk, 64), score_stride);
+    return dsa_host::scores_lists_short(*d, std::min<int32_t>(chunk, 64), score_stride);
 }
 
 size_t dsa_index_select_chunked_workspace_bytes(const dsa_dims* dims, int32_t chunk, int32_t score_stride) {

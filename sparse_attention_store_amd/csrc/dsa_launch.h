@@ -30,9 +30,15 @@ hipError_t launch_index_scores(const dsa_dims& d, const uint16_t* q_idx, const f
                                const int32_t* q_pos, int32_t T, int32_t stride, float* scores,
                                hipStream_t s);
 
+// Group lists for at most 64 queries of rows up to 262,144 pools (64-pool
+// groups up to 65,536 pools, 256-pool groups past that): the flat decode
+// scoring launches and the selections from their lists.
 bool scores_select_grouped(const dsa_dims& d, int32_t T, int32_t stride);
+// The same up to 65,536 pools (64-pool groups only): the paged and shared-run
+// scoring kernels and the prefill kernel's lists.
+bool scores_lists_short(const dsa_dims& d, int32_t T, int32_t stride);
 // Scores plus each 64-pool group's best pools, for any T (group-list geometry:
-// scores_select_grouped(d, min(T, 64), stride)); the lists are laid out as
+// scores_lists_short(d, min(T, 64), stride)); the lists are laid out as
 // launch_scores_with_groups lays them out for T queries.
 hipError_t launch_scores_lists(const dsa_dims& d, const uint16_t* q_idx, const float* w, const uint16_t* pools,
                                const dsa_seqs& seqs, int32_t num_seqs, const int32_t* q_seq, const int32_t* q_pos,

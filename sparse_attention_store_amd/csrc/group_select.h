@@ -1,5 +1,5 @@
-// The best K pools of a row from the 64-pool group lists the scoring pass
-// keeps ([Ref] Functions: topk_pools; [Flash] Stream C: indexer_topk512),
+// The best K pools of a row from the group lists (64 pools a group, 256 in
+// rows past 65,536 pools) the scoring pass keeps ([Ref] Functions: topk_pools; [Flash] Stream C: indexer_topk512),
 // as a workgroup-wide device function: k_topk_groups runs it on 1024
 // threads, the selection + attention launch on the 512 threads of its
 // attention workgroups.  Both make the same selection: the K best by
@@ -144,7 +144,8 @@ __device__ __forceinline__ GroupQuery select_from_groups(
     }
     g.K = select_k;
     g.listed = true;
-    const int groups = (n + kGroupPools - 1) / kGroupPools;
+    const int gp = group_pools(n);
+    const int groups = (n + gp - 1) / gp;
     const int m = group_quota(select_k, n);
     const int msh = __ffs(m) - 1;
     const int M = groups * m;

@@ -148,7 +148,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scores_mfma(
             if (p < stride) out[p] = p < n_vis ? sv : -INFINITY;
             if constexpr (CANDS) {
                 if (n_vis > select_k)
-                    keep_group_best(sv, p < n_vis, p, p0 / kGroupPools, group_quota(select_k, n_vis),
+                    keep_group_best(sv, p < n_vis, p, p0 / kGroupPools, group_quota<true>(select_k, n_vis),
                                     cand + (int64_t)t * kGroupCandCap, cand_n + (int64_t)t * kMaxGroups,
                                     [](uint64_t* q, uint64_t x) { *q = x; },
                                     [](int32_t* q, uint32_t x) { *q = (int32_t)x; });
@@ -197,7 +197,12 @@ struct QueryGeom {
 // With PAGED the pools are paged (paged.h): a query's sequence index is kept in
 // place of its pool base, and a group's 64 rows are one pool block, found in
 // the block table.
-template <bool CANDS, int AD, bool I8 = false, bool PAGED = false>
+//
+// With LONG (rows past 65,536 pools), a query of more than 65,536 visible
+// pools keeps one list per 256-pool tile: each wave keeps its 64 pools' best
+// m in LDS, then wave 0 keeps the best m of those (the best m of the tile are
+// among its waves' best m).
+template <bool CANDS, int AD, bool I8 = false, bool PAGED = false, bool LONG = false>
 __global__ __launch_bounds__(256, 4) void k_scores_groups(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const void* pools_v, const int32_t* __restrict__ first_valid,
@@ -209,6 +214,8 @@ __global__ __launch_bounds__(256, 4) void k_scores_groups(
     __shared__ __attribute__((aligned(16))) uint16_t s_q[kHI * kQStride];
     __shared__ __attribute__((aligned(16))) float s_w[kHI];
     __shared__ __attribute__((aligned(16))) uint32_t s_new[AD ? 4 : 1][kDI / 2];
+    __shared__ uint64_t s_long[LONG ? 64 : 1];         // the waves' lists of a 256-pool group
+    __shared__ int32_t s_long_n[LONG ? 4 : 1];
     const uint16_t* pools = reinterpret_cast<const uint16_t*>(pools_v);
     const int8_t* codes = reinterpret_cast<const int8_t*>(pools_v);
     const int lane = threadIdx.x & 63;
@@ -323,7 +330,7 @@ __global__ __launch_bounds__(256, 4) void k_scores_groups(
         }
         __builtin_amdgcn_sched_barrier(0);             // every load in flight before the A operand is shared
         // the group list length, while the rows are in flight
-        const int gm = CANDS && n_vis > select_k ? group_quota(select_k, n_vis) : 0;
+        const int gm = CANDS && n_vis > select_k ? group_quota<!LONG>(select_k, n_vis) : 0;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int k = lane + 64 * i;
@@ -408,11 +415,34 @@ __global__ __launch_bounds__(256, 4) void k_scores_groups(
                                                       (uint32_t)lane * 4u, 0, 0);
             }
             if constexpr (CANDS) {
-                if (n_vis > select_k)
-                    keep_group_best(s, p < n_vis, p, grp, gm,
-                                    cand + (int64_t)t * kGroupCandCap, cand_n + (int64_t)t * kMaxGroups,
-                                    [](uint64_t* q, uint64_t x) { *q = x; },
-                                    [](int32_t* q, uint32_t x) { *q = (int32_t)x; });
+                if (n_vis > select_k) {
+                    if (LONG && n_vis > kShortListPools)
+                        keep_group_best(s, p < n_vis, p, 0, gm, s_long + wave * gm, s_long_n + wave,
+                                        [](uint64_t* q, uint64_t x) { *q = x; },
+                                        [](int32_t* q, uint32_t x) { *q = (int32_t)x; });
+                    else
+                        keep_group_best(s, p < n_vis, p, grp, gm,
+                                        cand + (int64_t)t * kGroupCandCap, cand_n + (int64_t)t * kMaxGroups,
+                                        [](uint64_t* q, uint64_t x) { *q = x; },
+                                        [](int32_t* q, uint32_t x) { *q = (int32_t)x; });
+                }
+            }
+        }
+        if constexpr (CANDS && LONG) {
+            if (n_vis > kShortListPools && n_vis > select_k) {   // the same for the whole workgroup
+                lds_barrier();
+                if (wave == 0) {
+                    // lane l: entry l % gm of wave l / gm's list (lane order is id
+                    // order); a wave past the query's last group kept nothing
+                    const int wv = lane / gm;
+                    const uint64_t e = lane < 4 * gm ? s_long[lane] : 0ull;
+                    const bool ok = lane < 4 * gm && 4 * j + wv < uniform32(geom[t].ng);
+                    keep_best_keys(ok ? (uint32_t)(e >> 32) : 0u, ok && (e >> 32) != 0ull, 0xFFFFFFFFu - (uint32_t)e,
+                                   min(max(n_vis - kLongGroupPools * j, 0), kLongGroupPools), j, gm,
+                                   cand + (int64_t)t * kGroupCandCap, cand_n + (int64_t)t * kMaxGroups,
+                                   [](uint64_t* q, uint64_t x) { *q = x; },
+                                   [](int32_t* q, uint32_t x) { *q = (int32_t)x; });
+                }
             }
         }
         if (tile + (int)gridDim.x < total) lds_barrier();   // s_q is rewritten by the next tile
@@ -565,7 +595,11 @@ hipError_t launch_scores_lists(const dsa_dims& d, const uint16_t* q_idx, const f
 
 bool scores_select_grouped(const dsa_dims& d, int32_t T, int32_t stride) {
     return d.idx_heads == dsa::kHI && d.idx_dim == dsa::kDI && T <= dsa::kDecMaxT && d.kpool == 4 &&
-           stride <= dsa::kMaxGroups * dsa::kGroupPools && d.index_topk / d.kpool <= dsa::kGroupMaxK;
+           stride <= dsa::kListMaxPools && d.index_topk / d.kpool <= dsa::kGroupMaxK;
+}
+
+bool scores_lists_short(const dsa_dims& d, int32_t T, int32_t stride) {
+    return scores_select_grouped(d, T, stride) && stride <= dsa::kShortListPools;
 }
 
 size_t scores_select_group_bytes(int32_t T) {
@@ -583,9 +617,14 @@ hipError_t launch_scores_with_groups(const dsa_dims& d, const uint16_t* q_idx, c
     group_lists(ws, T, cand, cand_n);
     hipEvent_t ev0, ev1;
     take_events(ev0, ev1);
-    hipExtLaunchKernelGGL((dsa::k_scores_groups<true, 0>), dim3(scores_groups_grid(T, stride)), dim3(256), 0, s,
-                          ev0, ev1, 0, q_idx, w, pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T,
-                          num_seqs, stride, scores, d.index_topk / d.kpool, cand, cand_n, dsa::AppendArgs{}, nullptr, dsa::PagedMap{});
+#define DSA_SCORES_GROUPS(LONG)                                                                                    \
+    hipExtLaunchKernelGGL((dsa::k_scores_groups<true, 0, false, false, LONG>), dim3(scores_groups_grid(T, stride)),  \
+                          dim3(256), 0, s, ev0, ev1, 0, q_idx, w, pools, seqs.first_valid, seqs.pool_base, q_seq,    \
+                          q_pos, T, num_seqs, stride, scores, d.index_topk / d.kpool, cand, cand_n,                  \
+                          dsa::AppendArgs{}, nullptr, dsa::PagedMap{})
+    if (stride > dsa::kShortListPools) DSA_SCORES_GROUPS(true);
+    else DSA_SCORES_GROUPS(false);
+#undef DSA_SCORES_GROUPS
     return hipGetLastError();
 }
 
@@ -613,15 +652,24 @@ hipError_t launch_append_scores_groups(const dsa_dims& d, const void* latent, in
     const unsigned grid = fused_grid(T, stride, ap.tasks);
     hipEvent_t ev0, ev1;
     take_events(ev0, ev1);
-#define DSA_APPEND_SCORES(D)                                                                                        \
-    hipExtLaunchKernelGGL((dsa::k_scores_groups<true, D>), dim3(grid), dim3(256), 0, s, ev0, ev1, 0, q_idx, w,    \
-                          pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, num_seqs, stride,  \
+#define DSA_APPEND_SCORES(D, LONG)                                                                                  \
+    hipExtLaunchKernelGGL((dsa::k_scores_groups<true, D, false, false, LONG>), dim3(grid), dim3(256), 0, s, ev0, ev1, \
+                          0, q_idx, w, pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, num_seqs, stride,  \
                           scores, d.index_topk / d.kpool, cand, cand_n, ap, nullptr, dsa::PagedMap{})
-    switch (d.latent_dim) {
-        case 512: DSA_APPEND_SCORES(512); break;
-        case 256: DSA_APPEND_SCORES(256); break;
-        case 128: DSA_APPEND_SCORES(128); break;
-        default: DSA_APPEND_SCORES(64); break;
+    if (stride > dsa::kShortListPools) {
+        switch (d.latent_dim) {
+            case 512: DSA_APPEND_SCORES(512, true); break;
+            case 256: DSA_APPEND_SCORES(256, true); break;
+            case 128: DSA_APPEND_SCORES(128, true); break;
+            default: DSA_APPEND_SCORES(64, true); break;
+        }
+    } else {
+        switch (d.latent_dim) {
+            case 512: DSA_APPEND_SCORES(512, false); break;
+            case 256: DSA_APPEND_SCORES(256, false); break;
+            case 128: DSA_APPEND_SCORES(128, false); break;
+            default: DSA_APPEND_SCORES(64, false); break;
+        }
     }
 #undef DSA_APPEND_SCORES
     return hipGetLastError();
@@ -672,10 +720,14 @@ hipError_t launch_scores_with_groups_int8(const dsa_dims& d, const uint16_t* q_i
     group_lists(ws, T, cand, cand_n);
     hipEvent_t ev0, ev1;
     take_events(ev0, ev1);
-    hipExtLaunchKernelGGL((dsa::k_scores_groups<true, 0, true>), dim3(scores_groups_grid(T, stride)), dim3(256), 0, s,
-                          ev0, ev1, 0, q_idx, w, codes, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T,
-                          num_seqs, stride, scores, d.index_topk / d.kpool, cand, cand_n, dsa::AppendArgs{},
-                          const_cast<float*>(scales), dsa::PagedMap{});
+#define DSA_SCORES_GROUPS8(LONG)                                                                                   \
+    hipExtLaunchKernelGGL((dsa::k_scores_groups<true, 0, true, false, LONG>), dim3(scores_groups_grid(T, stride)),   \
+                          dim3(256), 0, s, ev0, ev1, 0, q_idx, w, codes, seqs.first_valid, seqs.pool_base, q_seq,    \
+                          q_pos, T, num_seqs, stride, scores, d.index_topk / d.kpool, cand, cand_n,                  \
+                          dsa::AppendArgs{}, const_cast<float*>(scales), dsa::PagedMap{})
+    if (stride > dsa::kShortListPools) DSA_SCORES_GROUPS8(true);
+    else DSA_SCORES_GROUPS8(false);
+#undef DSA_SCORES_GROUPS8
     return hipGetLastError();
 }
 
@@ -696,15 +748,24 @@ hipError_t launch_append_scores_groups_int8(const dsa_dims& d, const void* laten
     const unsigned grid = fused_grid(T, stride, ap.tasks);
     hipEvent_t ev0, ev1;
     take_events(ev0, ev1);
-#define DSA_APPEND_SCORES8(D)                                                                                       \
-    hipExtLaunchKernelGGL((dsa::k_scores_groups<true, D, true>), dim3(grid), dim3(256), 0, s, ev0, ev1, 0, q_idx, \
-                          w, codes, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, num_seqs, stride, \
+#define DSA_APPEND_SCORES8(D, LONG)                                                                                 \
+    hipExtLaunchKernelGGL((dsa::k_scores_groups<true, D, true, false, LONG>), dim3(grid), dim3(256), 0, s, ev0, ev1,  \
+                          0, q_idx, w, codes, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, num_seqs, stride,  \
                           scores, d.index_topk / d.kpool, cand, cand_n, ap, scales, dsa::PagedMap{})
-    switch (d.latent_dim) {
-        case 512: DSA_APPEND_SCORES8(512); break;
-        case 256: DSA_APPEND_SCORES8(256); break;
-        case 128: DSA_APPEND_SCORES8(128); break;
-        default: DSA_APPEND_SCORES8(64); break;
+    if (stride > dsa::kShortListPools) {
+        switch (d.latent_dim) {
+            case 512: DSA_APPEND_SCORES8(512, true); break;
+            case 256: DSA_APPEND_SCORES8(256, true); break;
+            case 128: DSA_APPEND_SCORES8(128, true); break;
+            default: DSA_APPEND_SCORES8(64, true); break;
+        }
+    } else {
+        switch (d.latent_dim) {
+            case 512: DSA_APPEND_SCORES8(512, false); break;
+            case 256: DSA_APPEND_SCORES8(256, false); break;
+            case 128: DSA_APPEND_SCORES8(128, false); break;
+            default: DSA_APPEND_SCORES8(64, false); break;
+        }
     }
 #undef DSA_APPEND_SCORES8
     return hipGetLastError();

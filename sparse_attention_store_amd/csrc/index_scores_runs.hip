@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256, 2) void k_scores_runs(
 #pragma unroll
         for (int m = 0; m < R; ++m) {
             const int nv = R > 1 ? uniform32(geom[t + (m < nq ? m : 0)].nnq) : n_vis;
-            gm[m] = CANDS && nv > select_k ? group_quota(select_k, nv) : 0;
+            gm[m] = CANDS && nv > select_k ? group_quota<true>(select_k, nv) : 0;
         }
 #pragma unroll
         for (int m = 0; m < R; ++m) {

@@ -24,6 +24,8 @@
 // 2^sh (the key offset shifted right), keeps the bucket that holds rank K and
 // narrows [lo, hi] to it, until that bucket is taken whole or one key value is
 // left, whose first `need` occurrences in id order are taken.
+#include <algorithm>
+
 #include "dsa_common.h"
 #include "dsa_launch.h"
 #include "topk_core.h"
@@ -35,7 +37,7 @@ constexpr int kTile = 256;                  // pools per stage-A workgroup
 constexpr int kBNT = 1024;
 constexpr int kMaxK = 1024;                 // select_k limit
 constexpr int kMaxTiles = 1024;             // 262,144 pools per row
-constexpr int kMaxCand = 32 * kBNT;         // stage-B capacity
+constexpr int kMaxKpt = 16;                 // stage-B slots per thread
 constexpr int kIncomplete = 1 << 30;        // tile count flag: the tile dropped pools
 
 // Kept per tile for a row of `ntiles` tiles.
@@ -48,9 +50,19 @@ __host__ __device__ inline int tile_quota(int select_k, int ntiles) {
 
 // Candidate slots per row: ntiles * tile_quota(ntiles) <= 16 ntiles + 5 K + 256
 // for every ntiles (m = 16; or m < 2 ceil(2.5 K / ntiles); or m = 256 only
-// when ntiles < 5 K / 256).
+// when ntiles < 5 K / 256), rounded up to even so that every row starts on
+// 16 bytes for stage B's paired-slot loads.
 __host__ __device__ inline int64_t cand_row_cap(int select_k, int ntiles_max) {
-    return 16LL * ntiles_max + 5LL * select_k + 256;
+    return (16LL * ntiles_max + 5LL * select_k + 257) & ~1LL;
+}
+
+// Slots stage B reads for the longest row: max over ntiles <= ntiles_max of
+// ntiles * tile_quota(ntiles), at most max(16 ntiles_max, 5 K + 2 ntiles_max),
+// which is 16,384 = kMaxKpt * kBNT at kMaxK and kMaxTiles.
+inline int64_t max_row_slots(int select_k, int ntiles_max) {
+    int64_t slots = 0;
+    for (int n = 1; n <= ntiles_max; ++n) slots = std::max<int64_t>(slots, (int64_t)n * tile_quota(select_k, n));
+    return slots;
 }
 
 
@@ -147,17 +159,35 @@ __global__ __launch_bounds__(kBNT) void k_topk_rows(
     if (tid < kMaxTiles) tpicked[tid] = 0u;
     if (tid == 0) fail = 0;
     const int s0 = tid * KPT;
-    uint32_t key[KPT];
-    int32_t id[KPT];
+    uint32_t key[KPT];                                       // a pool's id is re-read once it is picked
+    {
+        // Every load at once: this thread's slots (two per 16-byte load) and
+        // the counts of the (at most two, m >= 16) tiles they lie in, through
+        // descriptors bounded to the row's M slots and ntiles counts (reads
+        // past them give 0), so no load waits on another and none branches.
+        const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(cr, (uint32_t)M * 8u);
+        const __amdgpu_buffer_rsrc_t rn = buffer_rsrc(cn, (uint32_t)ntiles * 4u);
+        const int tile0 = s0 >> msh;
+        const uint32_t cnt0 = __builtin_amdgcn_raw_buffer_load_b32(rn, (uint32_t)tile0 * 4u, 0, 0);
+        const uint32_t cnt1 = __builtin_amdgcn_raw_buffer_load_b32(rn, (uint32_t)((s0 + KPT - 1) >> msh) * 4u, 0, 0);
+        uint64_t v[KPT];
+        if constexpr (KPT == 1) {
+            const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rc, (uint32_t)s0 * 8u, 0, 0);
+            v[0] = ((uint64_t)x[1] << 32) | x[0];
+        } else {
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-        const int s = s0 + j;
-        key[j] = 0u;
-        id[j] = 0;
-        if (s < M && (s & (m - 1)) < (cn[s >> msh] & (kIncomplete - 1))) {
-            const uint64_t v = cr[s];
-            key[j] = (uint32_t)(v >> 32);
-            id[j] = (int32_t)(0xFFFFFFFFu - (uint32_t)v);
+            for (int j = 0; j < KPT; j += 2) {
+                const u32x4 x = ld_buf128(rc, (uint32_t)(s0 + j) * 8u);
+                v[j] = ((uint64_t)x[1] << 32) | x[0];
+                v[j + 1] = ((uint64_t)x[3] << 32) | x[2];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const int s = s0 + j;
+            const uint32_t cnt = ((s >> msh) == tile0 ? cnt0 : cnt1) & (uint32_t)(kIncomplete - 1);
+            const bool ok = s < M && (uint32_t)(s & (m - 1)) < cnt;
+            key[j] = ok ? (uint32_t)(v[j] >> 32) : 0u;
         }
     }
     const uint32_t picks = select_top_slots<kBNT, KPT>(key, (uint32_t)select_k, T);
@@ -178,7 +208,7 @@ __global__ __launch_bounds__(kBNT) void k_topk_rows(
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
             const bool pk = (picks >> j) & 1u;
-            if (pk && pos < (uint32_t)kMaxK) sel[pos] = id[j];
+            if (pk && pos < (uint32_t)kMaxK) sel[pos] = (int32_t)(0xFFFFFFFFu - (uint32_t)cr[s0 + j]);
             pos += pk;
         }
     }
@@ -228,7 +258,7 @@ static size_t r256(size_t x) { return (x + 255) & ~(size_t)255; }
 bool topk_supported(const dsa_dims& d, int32_t stride) {
     const int sk = d.index_topk / d.kpool;
     return sk <= dsa::kMaxK && topk_tiles(stride) <= dsa::kMaxTiles &&
-           dsa::cand_row_cap(sk, topk_tiles(stride)) <= dsa::kMaxCand;
+           dsa::max_row_slots(sk, topk_tiles(stride)) <= (int64_t)dsa::kMaxKpt * dsa::kBNT;
 }
 
 size_t topk_workspace_bytes(const dsa_dims& d, int32_t T, int32_t stride) {
@@ -252,8 +282,7 @@ hipError_t launch_topk(const dsa_dims& d, const float* scores, int32_t stride, c
                        stride, seqs.first_valid, q_seq, q_pos, sk, cap, nt, cand, cand_n);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    // Slots per row are at most ntiles * tile_quota(ntiles) <= cap.
-    const int kpt = (int)cdiv(cap, dsa::kBNT);
+    const int kpt = (int)cdiv(dsa::max_row_slots(sk, nt), dsa::kBNT);     // <= kMaxKpt (topk_supported)
 #define DSA_ROWS(KPT)                                                                                     \
     hipLaunchKernelGGL((dsa::k_topk_rows<KPT>), dim3((unsigned)T), dim3(dsa::kBNT), 0, s, scores,          \
                        seqs.first_valid, q_seq, q_pos, stride, sk, cap, nt, cand, cand_n, e)
@@ -261,8 +290,8 @@ hipError_t launch_topk(const dsa_dims& d, const float* scores, int32_t stride, c
     else if (kpt <= 2) DSA_ROWS(2);
     else if (kpt <= 4) DSA_ROWS(4);
     else if (kpt <= 8) DSA_ROWS(8);
-    else if (kpt <= 16) DSA_ROWS(16);
-    else DSA_ROWS(32);
+    else if (kpt <= dsa::kMaxKpt) DSA_ROWS(16);
+    else return hipErrorInvalidValue;
 #undef DSA_ROWS
     return hipGetLastError();
 }

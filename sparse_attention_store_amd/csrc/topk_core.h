@@ -175,24 +175,35 @@ __device__ __forceinline__ uint32_t compaction_slot(const KT (&key)[KPT], KT lo,
     return block_exclusive_scan<NT>(gt + take, S.scan, &total);
 }
 
-// ---------------------------------------------------------------- 64-pool group candidates
-// A scoring pass can keep, for each 64-pool group (one wave), its best m
+// ---------------------------------------------------------------- pool group candidates
+// A scoring pass can keep, for each group of consecutive pools, its best m
 // pools by (score desc, id asc); the union of the group lists holds the top-K
 // unless a group that dropped pools has all m kept ones selected, which the
-// selection checks (falling back to an exact select over the scores).
+// selection checks (falling back to an exact select over the scores).  A
+// group is 64 pools (one wave) in rows of at most 65,536 pools, 256 pools
+// (one scoring workgroup's tile) in longer rows, so that a row never has
+// more than kMaxGroups groups.
 constexpr int kGroupPools = 64;
-constexpr int kMaxGroups = 1024;          // 65,536 pools per row
+constexpr int kLongGroupPools = 256;
+constexpr int kMaxGroups = 1024;
+constexpr int kShortListPools = kMaxGroups * kGroupPools;       // 65,536
+constexpr int kListMaxPools = kMaxGroups * kLongGroupPools;     // 262,144
 constexpr int kGroupCandCap = 8192;       // kept entries per row
 constexpr int kGroupMaxK = 512;
 constexpr int kGroupDropped = 1 << 30;    // group count flag: the group dropped pools
 
+__host__ __device__ __forceinline__ int group_pools(int n) { return n > kShortListPools ? kLongGroupPools : kGroupPools; }
+
 // Kept entries per group for a row of n visible pools (n > K): a power of two
-// >= lambda + 5 sqrt(lambda) + 4, lambda = 64 K / n being a group's mean share
-// of the K (so a group needing more than m is a > 5-sigma event); at least 8,
-// at most 64 and at most kGroupCandCap / groups.
+// >= lambda + 5 sqrt(lambda) + 4, lambda = G K / n being a group's mean share
+// of the K (G pools a group; a group needing more than m is a > 5-sigma
+// event); at least 8, at most 64 and at most kGroupCandCap / groups.
+// SHORT: the caller's rows are known to be at most 65,536 pools.
+template <bool SHORT = false>
 __device__ __forceinline__ int group_quota(int K, int n) {
-    const int groups = (n + kGroupPools - 1) / kGroupPools;
-    const float lam = 64.0f * (float)K / (float)n;
+    const int gp = SHORT ? kGroupPools : group_pools(n);
+    const int groups = (n + gp - 1) / gp;
+    const float lam = (float)gp * (float)K / (float)n;
     const float want = lam + 5.0f * sqrtf(lam) + 4.0f;
     int m = 8;
     while ((float)m < want && m < kGroupPools) m <<= 1;
@@ -200,22 +211,21 @@ __device__ __forceinline__ int group_quota(int K, int n) {
     return m;
 }
 
-// One wave's group: lanes hold consecutive pools p (lane order = id order),
-// `valid` for visible ones.  Writes the group's best m (key << 32 | ~p) in id
-// order to cand[group * m ..], zeros in the list's remaining slots (key 0
-// marks an empty slot), and the count (| kGroupDropped when more than m were
-// valid) to cand_n[group].  The best m are taken by repeated wave maxima for
-// m <= 16, else through the m-th largest key (32 ballot-and-popcount steps);
-// either way ties go to the lowest ids.  Store is the memory policy for the
-// two writes.
+// The best m of a wave's `valid` keys, lane order being id order: writes
+// them (key << 32 | ~id) in id order to cand[group * m ..], zeros in the
+// list's remaining slots (key 0 marks an empty slot), and the count
+// (| kGroupDropped when the group held more than m pools, nvalid being how
+// many it held) to cand_n[group].  The best m are taken by repeated wave
+// maxima for m = 8, else through the m-th largest key (32
+// ballot-and-popcount steps); either way ties go to the lowest ids.  Store is
+// the memory policy for the two writes.
 template <class Store64, class Store32>
-__device__ __forceinline__ void keep_group_best(float s, bool valid, int p, int group, int m, uint64_t* cand,
-                                                int32_t* cand_n, Store64 st64, Store32 st32) {
+__device__ __forceinline__ void keep_best_keys(uint32_t key, bool valid, uint32_t id, int nvalid, int group, int m,
+                                               uint64_t* cand, int32_t* cand_n, Store64 st64, Store32 st32) {
     const int lane = threadIdx.x & 63;
-    const uint32_t key = valid ? f32_key(s) : 0u;
-    const int nvalid = __popcll(__ballot(valid));
+    const int nkeys = __popcll(__ballot(valid));
     bool pick = valid;
-    if (nvalid > m && m <= 8) {
+    if (nkeys > m && m <= 8) {
         // m = 8: take the largest remaining key 8 times (a DPP wave max, then
         // the lowest lane holding it, which drops out) -- a dozen mostly
         // vector instructions a round, where the 32-step threshold search
@@ -232,7 +242,7 @@ __device__ __forceinline__ void keep_group_best(float s, bool valid, int p, int 
             cur = lane == first ? 0u : cur;
         }
         pick = (taken >> lane) & 1ull;
-    } else if (nvalid > m) {
+    } else if (nkeys > m) {
         // x = the m-th largest key: the largest x with at least m keys >= x
         uint32_t x = 0u;
 #pragma unroll
@@ -248,9 +258,18 @@ __device__ __forceinline__ void keep_group_best(float s, bool valid, int p, int 
     const unsigned long long pm = __ballot(pick);
     const int slot = popc_below(pm);
     const int npk = __popcll(pm);
-    if (pick) st64(cand + (int64_t)group * m + slot, ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)p));
+    if (pick) st64(cand + (int64_t)group * m + slot, ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - id));
     if (lane >= npk && lane < m) st64(cand + (int64_t)group * m + lane, 0ull);
     if (lane == 0) st32(cand_n + group, (uint32_t)(npk | (nvalid > m ? kGroupDropped : 0)));
+}
+
+// One wave's 64-pool group: lanes hold consecutive pools p, `valid` for
+// visible ones; keep_best_keys over their scores.
+template <class Store64, class Store32>
+__device__ __forceinline__ void keep_group_best(float s, bool valid, int p, int group, int m, uint64_t* cand,
+                                                int32_t* cand_n, Store64 st64, Store32 st32) {
+    keep_best_keys(valid ? f32_key(s) : 0u, valid, (uint32_t)p, __popcll(__ballot(valid)), group, m, cand, cand_n,
+                   st64, st32);
 }
 
 // ---------------------------------------------------------------- exact top-K of register keys

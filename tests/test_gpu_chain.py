@@ -75,7 +75,7 @@ def _run_and_check(dw, queries):
 
 
 @pytest.mark.parametrize("name", ["tiny", "tiny_seven", "tiny_padded_six", "tiny_batch", "mini_decode", "mini_decode_64",
-                                  "mini_prefill", "mini_heavy"])
+                                  "mini_prefill", "mini_heavy", "mini_long"])
 def test_chain_reduced(harness, name):
     wl = syn.get(name)
     say(f"chain {name} T={wl.T}")
@@ -156,7 +156,7 @@ def test_prepared_calls_match_the_calls(harness):
 
 
 @pytest.mark.parametrize("name,span", [("mini_decode", 3), ("mini_decode", 70), ("mini_decode_64", 5), ("mini_heavy", 5),
-                                       ("mini_heavy", 130), ("decode_32k", 4)])
+                                       ("mini_heavy", 130), ("decode_32k", 4), ("mini_long", 6)])
 def test_append_scores_groups_matches_separate_calls(harness, name, span):
     """append_scores_groups gives the bytes of append_tokens then
     index_scores_groups (cache rows, pools, scores, group lists, and the
@@ -213,7 +213,8 @@ def test_append_scores_groups_matches_separate_calls(harness, name, span):
                                               ("mini_decode", 1, "lists"), ("mini_heavy", 17, "lists"),
                                               ("mini_heavy", 3, "lists"), ("decode_32k", 17, "lists"),
                                               ("decode_32k", 17, "equal_scores"), ("mini_decode", 17, "fp32_q"),
-                                              ("mini_decode_64", 17, "lists"),
+                                              ("mini_decode_64", 17, "lists"), ("mini_long", 0, "lists"),
+                                              ("mini_long", 17, "equal_scores"),
                                               pytest.param("decode_262k_b8", 0, "lists", marks=pytest.mark.slow),
                                               pytest.param("decode_262k_b8", 0, "equal_scores",
                                                            marks=pytest.mark.slow)])

@@ -80,7 +80,7 @@ def test_index_pools_int8(harness, name):
             assert ok, ("fp32 pool state", b, p, worst)
 
 
-@pytest.mark.parametrize("name", ["mini_decode", "mini_decode_64", "mini_heavy", "decode_32k"])
+@pytest.mark.parametrize("name", ["mini_decode", "mini_decode_64", "mini_heavy", "decode_32k", "mini_long"])
 def test_index_scores_int8(harness, name):
     import sparse_attention_store_amd as dsa
     wl = syn.get(name)
@@ -110,7 +110,7 @@ def test_index_scores_int8(harness, name):
 
 
 @pytest.mark.parametrize("name,span", [("mini_decode", 3), ("mini_decode", 70), ("mini_decode_64", 5),
-                                       ("mini_heavy", 130), ("decode_32k", 4)])
+                                       ("mini_heavy", 130), ("decode_32k", 4), ("mini_long", 6)])
 def test_append_scores_groups_int8_matches_separate_calls(harness, name, span):
     """The single launch gives the bytes of store_int8 + index_pools_int8 +
     index_scores_groups_int8 (rows, codes, scales, scores, group lists, and
@@ -165,7 +165,7 @@ def test_append_scores_groups_int8_matches_separate_calls(harness, name, span):
         assert torch.equal(a, b), what
 
 
-@pytest.mark.parametrize("name", ["mini_decode", "mini_decode_64", "mini_heavy",
+@pytest.mark.parametrize("name", ["mini_decode", "mini_decode_64", "mini_heavy", "mini_long",
                                   pytest.param("decode_32k", marks=pytest.mark.slow),
                                   pytest.param("decode_262k_b8", marks=pytest.mark.slow)])
 def test_chain_int8(harness, name):

@@ -447,12 +447,15 @@ def _scores_select_case(name, zero_q=False):
         assert torch.equal(a, b), nm
 
 
-@pytest.mark.parametrize("name", ["mini_decode", "mini_heavy", "decode_32k"])
+@pytest.mark.parametrize("name", ["mini_decode", "mini_heavy", "decode_32k", "mini_long"])
 def test_index_scores_select_matches_separate_calls(dsa, name):
+    """The group-list selection (64- or 256-pool groups) against the tile
+    selection over the full score rows: the same bits."""
     say(f"index_scores_select {name}")
     _scores_select_case(name)
 
 
-def test_index_scores_select_forced_fallback(dsa):
-    say("index_scores_select with all-equal scores")
-    _scores_select_case("decode_32k", zero_q=True)
+@pytest.mark.parametrize("name", ["decode_32k", "mini_long"])
+def test_index_scores_select_forced_fallback(dsa, name):
+    say(f"index_scores_select with all-equal scores {name}")
+    _scores_select_case(name, zero_q=True)
