@@ -55,7 +55,14 @@ KERNEL_SRC = {
     "k_decode_step": [os.path.join(_CSRC, f) for f in ("decode_step.hip", "mla_core.h", "scores_core.h",
                                                        "topk_core.h", "dsa_common.h")],
 }
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "index_scores_decode_262k_b8_traffic.md")
+# committed counter summaries of the timed scoring launch: (workload, INT8 pools, share) -> (file, block)
+TRAFFIC_PROFILES = {
+    ("decode_262k_b8", False, 1): ("index_scores_decode_262k_b8_traffic.md", 0),
+    ("decode_262k_b8", True, 1): ("index_scores_int8_decode_262k_b8_traffic.md", 0),
+    ("decode_1m_b4", False, 1): ("index_scores_decode_1m_b4_traffic.md", 0),
+    ("decode_262k_b8_mtp", False, 4): ("index_scores_shared_decode_262k_b8_mtp_traffic.md", 0),
+    ("decode_262k_b8_mtp", False, 1): ("index_scores_shared_decode_262k_b8_mtp_traffic.md", 1),
+}
 COPY_BYTES = 256 << 20          # calibration copy: bytes read (and written) per launch
 
 
@@ -104,18 +111,24 @@ def _source_hash(srcs) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(summary: str, srcs):
+def traffic_from_profile(summary: str, srcs, block: int = 0):
     """HBM bytes per launch of the dominant kernel from a committed rocprofv3
-    counter summary, or None when the summary is absent or was taken on
-    different kernel sources."""
+    counter summary (its block-th kernel summary), or None when the summary is
+    absent or was taken on different kernel sources."""
     if not os.path.exists(summary):
         return None
     src_hash = _source_hash(srcs)
-    vals = {}
+    blocks = []
     for ln in open(summary):
         if ":" in ln and ln.strip().startswith("- "):
             k, v = ln.strip()[2:].split(":", 1)
-            vals[k.strip()] = v.strip()
+            if k.strip() == "kernel":
+                blocks.append({})
+            if blocks:
+                blocks[-1][k.strip()] = v.strip()
+    if block >= len(blocks):
+        return None
+    vals = blocks[block]
     if vals.get("kernel_source_sha256_16") != src_hash:
         return None
     try:
@@ -538,7 +551,7 @@ def main():
                 "avg_launch_us": round(score_us, 1), "flops_per_launch": chunk_flops,
                 "achieved_tflops": round(s_tf, 1), "frac": round(s_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                 "launches_per_step": n_chunks},
-            "sparse_mla (k_mla_mfma<4>)": {
+            "sparse_mla (k_mla_mfma<4, 8>)": {
                 "avg_launch_us": round(attn_us, 1), "flops_per_launch": pw["attn_flops"],
                 "achieved_tflops": round(a_tf, 1), "frac": round(a_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                 "launches_per_step": 1},
@@ -548,7 +561,7 @@ def main():
                                       / MFMA_BF16_PEAK_TFLOPS, 2)
         line["flops_per_step"] = pw["score_flops"] + pw["attn_flops"]
         line["roofline"] = {
-            "kernel": "sparse_mla (k_mla_mfma<4>)" if dom_attn else "index_scores (k_scores_mfma<8,4>)",
+            "kernel": "sparse_mla (k_mla_mfma<4, 8>)" if dom_attn else "index_scores (k_scores_mfma<8,4>)",
             "bound": "mfma", "achieved": round(a_tf if dom_attn else s_tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round((a_tf if dom_attn else s_tf) / MFMA_BF16_PEAK_TFLOPS, 4),
             "traffic": None, "flops_per_launch": pw["attn_flops"] if dom_attn else chunk_flops,
@@ -558,6 +571,7 @@ def main():
         ab = algorithmic_bytes(wl, 132 if int8 else 256, share)
         fast = dw.fast_supported()
         kern_bytes = ab["scores_kernel"] if fast else ab["scores_kernel"] - (ab["step"] - ab["decode_kernel"])
+        prof = TRAFFIC_PROFILES.get((wl.name, bool(int8), share))
         own_mean, own_median, burst = scoring_launch_us(dw, R, 4 * R)
         achieved = kern_bytes / (own_mean * 1e-6) / 1e9
         line["pct_hbm_peak"] = round(100.0 * ab["step"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)
@@ -566,12 +580,14 @@ def main():
             "kernel": ("append_scores_groups_shared (k_scores_runs<true, 512, %s>)" % ("true" if int8 else "false")
                        if share > 1 else
                        "append_scores_groups_int8 (k_scores_groups<true, 512, true>)" if int8 else
-                       "append_scores_groups (k_scores_groups<true, 512, false>)" if fast else
+                       "append_scores_groups (k_scores_groups<true, 512, false, false, %s>)"
+                       % ("true" if dw.stride > 65536 else "false") if fast else
                        "index_scores_select (k_scores_groups<false, 0, false>)"),
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": (traffic_from_profile(PMC_SUMMARY, SCORES_SRC)
-                        if wl.name == WORKLOAD and fast and not int8 and share == 1 else None),
+            "traffic": (traffic_from_profile(os.path.join(ROOT, "profiles", prof[0]),
+                                             KERNEL_SRC["k_scores_runs" if share > 1 else "k_scores_groups"], prof[1])
+                        if fast and prof else None),
             "algorithmic_bytes_per_launch": kern_bytes, "avg_launch_us": round(own_mean, 2),
             "median_launch_us": round(own_median, 2), "avg_launch_us_burst": round(burst, 2),
             "frac_of_copy": round(achieved / copy_gbs, 4)}

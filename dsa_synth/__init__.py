@@ -392,6 +392,16 @@ def mini_prefill(seed: int = 12) -> Workload:
                np.zeros(n_q), np.arange(n_ctx, sl))
 
 
+def mini_prefill_wide(seed: int = 17) -> Workload:
+    """96 causal queries appended to a 180,000-token context (45,024 pools at
+    the last query): rows past the single-pass selection's 40,960 pools, so a
+    chunked selection keeps 64-pool group lists, 64 heads."""
+    n_ctx, n_q = 180000, 96
+    sl = n_ctx + n_q
+    return _mk("mini_prefill_wide", seed, production_dims(64), [0], [sl], sl, sl // 4,
+               np.zeros(n_q), np.arange(n_ctx, sl))
+
+
 def mini_heavy(seed: int = 13) -> Workload:
     """64 heads, Student-t(3) latent, a mix of sparse, dense and nearly empty lists."""
     fv = [0, 3, 1]
@@ -451,7 +461,7 @@ WORKLOADS = {
     "prefill_4k_on_131k": prefill_4k_on_131k, "decode_1m_b4": decode_1m_b4,
     "mini_decode": mini_decode, "mini_decode_64": mini_decode_64, "mini_prefill": mini_prefill,
     "mini_heavy": mini_heavy, "mini_mtp": mini_mtp, "decode_262k_b8_mtp": decode_262k_b8_mtp,
-    "mini_long": mini_long,
+    "mini_long": mini_long, "mini_prefill_wide": mini_prefill_wide,
 }
 
 

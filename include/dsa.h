@@ -207,7 +207,9 @@ int dsa_index_scores(const dsa_dims* dims, const uint16_t* q_idx, const float* w
  *   workspace device scratch, >= dsa_topk_workspace_bytes(dims, T,
  *             score_stride) bytes, 256-byte aligned; needs no initialisation
  *             and holds nothing between calls.  Calls sharing one workspace
- *             must not overlap.
+ *             must not overlap.  Rows of at most 40,960 pools are selected
+ *             in one pass and need none (the size is then 0 and workspace
+ *             may be NULL).
  */
 size_t dsa_topk_workspace_bytes(const dsa_dims* dims, int32_t T, int32_t score_stride);
 int dsa_topk_select(const dsa_dims* dims, const float* scores, int32_t score_stride,
@@ -411,10 +413,12 @@ int dsa_append_scores_groups_shared(const dsa_dims* dims, int dtype, const void*
  * next group (the pages' integration keeps the indexer's workspaces bounded:
  * [Kernels] Included).  pool_ids and indices are those dsa_index_scores +
  * dsa_topk_select_expand give for all T queries at once; the scores are not
- * kept.  For 32 x 128 indexer heads, select_k <= 512 and score_stride <=
- * 65,536 the scoring pass also keeps each 64-pool group's best pools and the
- * selection reads those lists (as dsa_index_scores_select does for decode);
- * other geometries sort 256-pool tiles of the scores.
+ * kept.  Rows of at most 40,960 pools are selected in one pass over their
+ * scores.  Past that, for 32 x 128 indexer heads, select_k <= 512 and
+ * score_stride <= 65,536 the scoring pass also keeps each 64-pool group's
+ * best pools and the selection reads those lists (as
+ * dsa_index_scores_select does for decode); other geometries sort 256-pool
+ * tiles of the scores.
  *   q_idx .. score_stride   as dsa_index_scores
  *   chunk      host: queries per group (1 .. 65,535); the workspace holds
  *              chunk x score_stride scores, e.g. 512 x 33,792 x 4 B = 69 MB

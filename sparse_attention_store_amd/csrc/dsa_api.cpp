@@ -603,10 +603,12 @@ static size_t chunk_scores_bytes(int32_t chunk, int32_t score_stride) {
     return ((size_t)chunk * (size_t)score_stride * 4 + 255) / 256 * 256;
 }
 
-// The chunked selection keeps 64-pool group lists in the scoring pass (then
+// The chunked selection selects each row in one pass when rows have at most
+// 40,960 pools; else it keeps 64-pool group lists in the scoring pass (then
 // selects from them) when the geometry allows it, else sorts score tiles.
 static bool chunked_grouped(const dsa_dims* d, int32_t chunk, int32_t score_stride) {
-    return dsa_host::scores_lists_short(*d, std::min<int32_t>(chunk, 64), score_stride);
+    return !dsa_host::topk_direct(score_stride) &&
+           dsa_host::scores_lists_short(*d, std::min<int32_t>(chunk, 64), score_stride);
 }
 
 size_t dsa_index_select_chunked_workspace_bytes(const dsa_dims* dims, int32_t chunk, int32_t score_stride) {

@@ -112,6 +112,8 @@ hipError_t launch_append_scores_groups_int8(const dsa_dims& d, const void* laten
 
 size_t topk_workspace_bytes(const dsa_dims& d, int32_t T, int32_t stride);
 bool topk_supported(const dsa_dims& d, int32_t stride);
+// Rows of at most 40,960 pools are selected in one pass (k_topk_direct, no workspace).
+bool topk_direct(int32_t stride);
 hipError_t launch_topk(const dsa_dims& d, const float* scores, int32_t stride, const dsa_seqs& seqs,
                        const int32_t* q_seq, const int32_t* q_pos, int32_t T, int32_t* pool_ids,
                        int32_t* indices, void* ws, hipStream_t s);

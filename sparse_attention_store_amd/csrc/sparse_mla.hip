@@ -71,22 +71,27 @@ __global__ __launch_bounds__(64 * NW, 1) void k_mla_rows(
 }
 
 // ------------------------------------------------------------------ k_mla_mfma
-template <int HT>
-__global__ __launch_bounds__(256) void k_mla_mfma(
+template <int HT, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void k_mla_mfma(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, int row_bytes,
     const int32_t* __restrict__ indices, int W, int H, float scale_log2, int chunks_per_split,
     int splits, float* __restrict__ part_o, MlaPartial* __restrict__ part_ml,
     void* __restrict__ out, int out_f32, float* __restrict__ lse) {
+    constexpr int NT = 64 * NW;
     constexpr int HPW = 16 * HT;
-    constexpr int WPHT = 4 / HT;          // waves per head tile
+    constexpr int WPHT = NW / HT;         // waves per head tile
+    constexpr int RPW = 4 / WPHT;         // 16-row tiles per wave (S)
     constexpr int NGRP = 8 / WPHT;        // 64-column groups per wave (PV)
+    constexpr int SEGS = NT / kChunk;     // threads per gathered row
+    constexpr int SEGB = kD / SEGS;       // bytes of a row per thread
+    static_assert(WPHT * HT == NW && RPW * WPHT == 4 && SEGB % 16 == 0, "64-row chunks, 16-row tiles");
     __shared__ __attribute__((aligned(16))) uint16_t kv[kChunk * kKVRow];
     __shared__ __attribute__((aligned(16))) uint16_t pl[2][HPW * kPRow];   // P' hi, lo
     __shared__ float rs[kChunk];
     __shared__ int rvalid[kChunk];
-    __shared__ float red_max[4][16];
-    __shared__ float red_sum[4][16];
-    __shared__ int chunk_any[4];
+    __shared__ float red_max[NW][16];
+    __shared__ float red_sum[NW][16];
+    __shared__ int chunk_any[NW];
     __shared__ int idx_lds[kMaxSplitRows];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -117,28 +122,28 @@ __global__ __launch_bounds__(256) void k_mla_mfma(
     const int c_end = min(c_begin + chunks_per_split, nchunks);
     const int32_t* idx_row = indices + (int64_t)t * W;
 
-    // Row gather: thread -> (row tid/4, 128-byte segment tid%4).  The split's
+    // Row gather: thread -> (row tid / SEGS, SEGB-byte segment).  The split's
     // slice of the index list is staged in LDS once, so the loop issues the
     // rows of chunk c+1 before chunk c computes without any dependent global
     // load (or register copy of one) in between.
-    const int r = tid >> 2, sg = tid & 3;
+    const int r = tid / SEGS, sg = tid % SEGS;
     const int split_rows = (c_end - c_begin) * kChunk;
-    for (int i = tid; i < split_rows; i += 256) {
+    for (int i = tid; i < split_rows; i += NT) {
         const int pos = c_begin * kChunk + i;
         idx_lds[i] = pos < W ? idx_row[pos] : -1;
     }
     lds_barrier();
-    u32x4 raw[8];
+    u32x4 raw[SEGB / 16];
     float rsc = 0.f;
     auto load_rows = [&](int idx) {
         if (idx >= 0) {
-            const uint8_t* src = cache + (int64_t)idx * row_bytes + sg * 128;
+            const uint8_t* src = cache + (int64_t)idx * row_bytes + sg * SEGB;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) raw[i] = *reinterpret_cast<const u32x4*>(src + 16 * i);
+            for (int i = 0; i < SEGB / 16; ++i) raw[i] = *reinterpret_cast<const u32x4*>(src + 16 * i);
             rsc = sg == 0 ? *reinterpret_cast<const float*>(cache + (int64_t)idx * row_bytes + kD) : 0.f;
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) raw[i] = u32x4{0u, 0u, 0u, 0u};
+            for (int i = 0; i < SEGB / 16; ++i) raw[i] = u32x4{0u, 0u, 0u, 0u};
             rsc = 0.f;
         }
     };
@@ -151,9 +156,9 @@ __global__ __launch_bounds__(256) void k_mla_mfma(
         if (sg == 0) { rs[r] = rsc; rvalid[r] = idx_cur >= 0; }
         const bool have = idx_cur >= 0;
         {
-            uint16_t* dst = &kv[r * kKVRow + sg * 128];
+            uint16_t* dst = &kv[r * kKVRow + sg * SEGB];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < SEGB / 16; ++i) {
                 uint32_t bq[8];
                 int8x4_to_bf16x4(raw[i][0], bq[0], bq[1]);
                 int8x4_to_bf16x4(raw[i][1], bq[2], bq[3]);
@@ -169,13 +174,16 @@ __global__ __launch_bounds__(256) void k_mla_mfma(
         const unsigned long long vote = __ballot(have);
         if ((tid & 63) == 0) chunk_any[wave] = vote != 0ull;
         lds_barrier();
-        if (!(chunk_any[0] | chunk_any[1] | chunk_any[2] | chunk_any[3])) continue;   // empty chunk
-
-        // ---- 2. S for this wave's head tile and row tiles sub*HT .. sub*HT+HT-1
-        f32x4 sacc[HT];
+        int any = 0;
 #pragma unroll
-        for (int rr = 0; rr < HT; ++rr) {
-            const int rt = sub * HT + rr;
+        for (int i = 0; i < NW; ++i) any |= chunk_any[i];
+        if (!any) continue;                              // empty chunk
+
+        // ---- 2. S for this wave's head tile and row tiles sub*RPW .. sub*RPW+RPW-1
+        f32x4 sacc[RPW];
+#pragma unroll
+        for (int rr = 0; rr < RPW; ++rr) {
+            const int rt = sub * RPW + rr;
             const uint16_t* kr = &kv[(rt * 16 + n16) * kKVRow + g4 * 8];
             f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -184,11 +192,11 @@ __global__ __launch_bounds__(256) void k_mla_mfma(
             sacc[rr] = a;
         }
         // ---- 3. online softmax (log2 domain); lane holds row rt*16+n16, heads 4*g4+i
-        float z[HT][4];
+        float z[RPW][4];
         float cmax[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-        for (int rr = 0; rr < HT; ++rr) {
-            const int row = (sub * HT + rr) * 16 + n16;
+        for (int rr = 0; rr < RPW; ++rr) {
+            const int row = (sub * RPW + rr) * 16 + n16;
             const bool ok = rvalid[row] != 0;
             const float sc = rs[row] * scale_log2;
 #pragma unroll
@@ -215,8 +223,8 @@ __global__ __launch_bounds__(256) void k_mla_mfma(
         }
         float psum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int rr = 0; rr < HT; ++rr) {
-            const int row = (sub * HT + rr) * 16 + n16;
+        for (int rr = 0; rr < RPW; ++rr) {
+            const int row = (sub * RPW + rr) * 16 + n16;
             const float rsv = rs[row];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -276,6 +284,7 @@ __global__ __launch_bounds__(256) void k_mla_mfma(
                     oacc[gi][tt] = mfma16(a_hi, as_bf16x8(bb), oacc[gi][tt]);
                     oacc[gi][tt] = mfma16(a_lo, as_bf16x8(bb), oacc[gi][tt]);
                 }
+                if constexpr (NW == 8) __builtin_amdgcn_sched_barrier(0);   // one group's V loads in flight at a time
             }
         }
     }
@@ -518,11 +527,11 @@ hipError_t launch_sparse_mla(const dsa_dims& d, const MlaPlan& plan, const void*
     const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q);
     switch (plan.head_tiles) {
         case 4:
-            hipLaunchKernelGGL((dsa::k_mla_mfma<4>), grid, dim3(256), 0, s, q16, c8, d.row_bytes, indices, W, H, sl2,
+            hipLaunchKernelGGL((dsa::k_mla_mfma<4, 8>), grid, dim3(512), 0, s, q16, c8, d.row_bytes, indices, W, H, sl2,
                                plan.chunks_per_split, plan.splits, part_o, part_ml, out, out_f32, lse);
             break;
         case 2:
-            hipLaunchKernelGGL((dsa::k_mla_mfma<2>), grid, dim3(256), 0, s, q16, c8, d.row_bytes, indices, W, H, sl2,
+            hipLaunchKernelGGL((dsa::k_mla_mfma<2, 4>), grid, dim3(256), 0, s, q16, c8, d.row_bytes, indices, W, H, sl2,
                                plan.chunks_per_split, plan.splits, part_o, part_ml, out, out_f32, lse);
             break;
         default:

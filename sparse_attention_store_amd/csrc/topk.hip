@@ -19,6 +19,10 @@
 //     belong too.  The workgroup checks exactly that and, if it happens,
 //     selects again from the row's scores with an exact streaming radix
 //     select, so the result never depends on the score distribution.
+// Rows of at most kDirectPools pools skip A and B: one 1024-thread workgroup
+// per row holds the row's keys in registers (KPT consecutive pools per thread,
+// so slot order is id order) and selects the best K of them directly
+// (k_topk_direct).
 // The K-th largest key is found by range bucketing in LDS: each pass
 // histograms the keys inside [lo, hi] into one bucket per thread, of width
 // 2^sh (the key offset shifted right), keeps the bucket that holds rank K and
@@ -38,6 +42,8 @@ constexpr int kBNT = 1024;
 constexpr int kMaxK = 1024;                 // select_k limit
 constexpr int kMaxTiles = 1024;             // 262,144 pools per row
 constexpr int kMaxKpt = 16;                 // stage-B slots per thread
+constexpr int kDirectKpt = 40;              // k_topk_direct: keys per thread
+constexpr int kDirectPools = kDirectKpt * kBNT;   // 40,960 pools per row
 constexpr int kIncomplete = 1 << 30;        // tile count flag: the tile dropped pools
 
 // Kept per tile for a row of `ntiles` tiles.
@@ -216,6 +222,62 @@ __global__ __launch_bounds__(kBNT) void k_topk_rows(
     emit_selection<kBNT>(sel, select_k, select_k, t, b, f, qp, n_vis, e);
 }
 
+// Rows of at most 1024 KPT pools: thread i holds pools i KPT .. i KPT + KPT - 1
+// as keys (0 past the row's visible pools), select_top_slots picks the best
+// K, and a block scan places them in id order.  The row's scores are read
+// through a descriptor bounded to the visible pools, in 16-byte loads when
+// the row starts on 16 bytes (VEC), else one score at a time.
+template <int KPT, bool VEC>
+__global__ __launch_bounds__(kBNT) void k_topk_direct(
+    const float* __restrict__ scores, const int32_t* __restrict__ first_valid,
+    const int32_t* __restrict__ q_seq, const int32_t* __restrict__ q_pos, int stride, int select_k, Emit e) {
+    static_assert(KPT % 4 == 0, "whole 16-byte loads");
+    __shared__ TopSelShared<kBNT, KPT> T;
+    __shared__ int32_t sel[kMaxK];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    int b, f, qp, n_vis;
+    query_geom(first_valid, q_seq, q_pos, t, b, f, qp, n_vis);
+    const int n = min(n_vis, stride);
+    if (n <= select_k) {                                     // every visible pool is selected
+        emit_selection<kBNT>(nullptr, n, select_k, t, b, f, qp, n_vis, e);
+        return;
+    }
+    const int s0 = tid * KPT;
+    uint32_t key[KPT];
+    {
+        // (VEC: the range is rounded up to whole 16-byte loads, still inside
+        // the row as the stride is a multiple of 4; slots past n are masked)
+        const uint32_t nr = VEC ? (uint32_t)((n + 3) & ~3) : (uint32_t)n;
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(scores + (int64_t)t * stride, nr * 4u);
+        float v[KPT];
+        if constexpr (VEC) {
+#pragma unroll
+            for (int j = 0; j < KPT; j += 4) {
+                const u32x4 x = ld_buf128(rs, (uint32_t)(s0 + j) * 4u);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) v[j + u] = __uint_as_float(x[u]);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < KPT; ++j)
+                v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)(s0 + j) * 4u, 0, 0));
+        }
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) key[j] = s0 + j < n ? f32_key(v[j]) : 0u;
+    }
+    const SlotMask<KPT> picks = select_top_slots<kBNT, KPT>(key, (uint32_t)select_k, T);
+    uint32_t total;
+    uint32_t pos = block_exclusive_scan<kBNT>((uint32_t)__popcll((unsigned long long)picks), T.S.scan, &total);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const bool pk = (picks >> j) & 1u;
+        if (pk && pos < (uint32_t)kMaxK) sel[pos] = s0 + j;
+        pos += pk;
+    }
+    lds_barrier();
+    emit_selection<kBNT>(sel, select_k, select_k, t, b, f, qp, n_vis, e);
+}
+
 // Stage B over 64-pool group lists written by the scoring pass: one
 // 1024-thread workgroup per row (8 list slots per thread, so a thread's slots
 // lie in one group), select_from_groups, then the outputs.
@@ -255,6 +317,8 @@ static int topk_tiles(int32_t stride) { return (int)cdiv(stride, dsa::kTile); }
 
 static size_t r256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+bool topk_direct(int32_t stride) { return stride <= dsa::kDirectPools; }
+
 bool topk_supported(const dsa_dims& d, int32_t stride) {
     const int sk = d.index_topk / d.kpool;
     return sk <= dsa::kMaxK && topk_tiles(stride) <= dsa::kMaxTiles &&
@@ -262,7 +326,7 @@ bool topk_supported(const dsa_dims& d, int32_t stride) {
 }
 
 size_t topk_workspace_bytes(const dsa_dims& d, int32_t T, int32_t stride) {
-    if (T <= 0 || stride <= 0) return 0;
+    if (T <= 0 || stride <= 0 || topk_direct(stride)) return 0;
     const int sk = d.index_topk / d.kpool;
     const int nt = topk_tiles(stride);
     return r256((size_t)T * (size_t)dsa::cand_row_cap(sk, nt) * 8) + r256((size_t)T * nt * 4);
@@ -273,6 +337,16 @@ hipError_t launch_topk(const dsa_dims& d, const float* scores, int32_t stride, c
                        int32_t* indices, void* ws, hipStream_t s) {
     if (T == 0) return hipSuccess;
     const int sk = d.index_topk / d.kpool;
+    if (topk_direct(stride)) {
+        const dsa::Emit e{pool_ids, indices, seqs.row_base, d.out_width};
+        if (stride % 4 == 0 && reinterpret_cast<uintptr_t>(scores) % 16 == 0)
+            hipLaunchKernelGGL((dsa::k_topk_direct<dsa::kDirectKpt, true>), dim3((unsigned)T), dim3(dsa::kBNT), 0, s,
+                               scores, seqs.first_valid, q_seq, q_pos, stride, sk, e);
+        else
+            hipLaunchKernelGGL((dsa::k_topk_direct<dsa::kDirectKpt, false>), dim3((unsigned)T), dim3(dsa::kBNT), 0, s,
+                               scores, seqs.first_valid, q_seq, q_pos, stride, sk, e);
+        return hipGetLastError();
+    }
     const int nt = topk_tiles(stride);
     const int64_t cap = dsa::cand_row_cap(sk, nt);
     uint64_t* cand = reinterpret_cast<uint64_t*>(ws);

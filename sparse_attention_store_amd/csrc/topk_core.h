@@ -3,6 +3,7 @@
 // and order-preserving compaction.  The design notes are at the top of
 // topk.hip.
 #pragma once
+#include <type_traits>
 
 #include "dsa_common.h"
 
@@ -281,7 +282,7 @@ __device__ __forceinline__ void keep_group_best(float s, bool valid, int p, int 
 // ranked exactly by one wave (each compares itself with all of them), so a
 // selection usually takes one or two histogram passes.  A bucket of more than
 // kBoundCap equal keys is taken in slot order by a block scan.  Returns this
-// thread's selected slots as a bitmask.
+// thread's selected slots as a bitmask (64-bit past 32 keys per thread).
 constexpr int kBoundCap = 64;
 
 template <int NT, int KPT>
@@ -294,9 +295,13 @@ struct TopSelShared {
     uint32_t flag[(NT * KPT + 31) / 32];
 };
 
+template <int KPT>
+using SlotMask = std::conditional_t<(KPT > 32), uint64_t, uint32_t>;
+
 template <int NT, int KPT>
-__device__ __forceinline__ uint32_t select_top_slots(const uint32_t (&key)[KPT], uint32_t target,
-                                                     TopSelShared<NT, KPT>& T) {
+__device__ __forceinline__ SlotMask<KPT> select_top_slots(const uint32_t (&key)[KPT], uint32_t target,
+                                                              TopSelShared<NT, KPT>& T) {
+    using Mask = SlotMask<KPT>;
     constexpr int BITS = log2_of<NT>();
     constexpr int FW = (NT * KPT + 31) / 32;
     const int tid = threadIdx.x;
@@ -347,10 +352,10 @@ __device__ __forceinline__ uint32_t select_top_slots(const uint32_t (&key)[KPT],
         cnt = tot;
         whole = tot == krem;
     }
-    uint32_t picks = 0u;
+    Mask picks = 0u;
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-        if (key[j] > hi || (whole && key[j] != 0u && key[j] >= lo && key[j] <= hi)) picks |= 1u << j;
+        if (key[j] > hi || (whole && key[j] != 0u && key[j] >= lo && key[j] <= hi)) picks |= Mask(1) << j;
     if (whole) return picks;
     if (cnt <= (uint32_t)kBoundCap) {
         // gather the boundary bucket and rank it in one wave
@@ -377,7 +382,7 @@ __device__ __forceinline__ uint32_t select_top_slots(const uint32_t (&key)[KPT],
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
             const uint32_t sl = (uint32_t)(tid * KPT + j);
-            if ((T.flag[sl >> 5] >> (sl & 31)) & 1u) picks |= 1u << j;
+            if ((T.flag[sl >> 5] >> (sl & 31)) & 1u) picks |= Mask(1) << j;
         }
     } else {
         // more than kBoundCap equal keys (lo == hi): the first krem in slot order
@@ -390,7 +395,7 @@ __device__ __forceinline__ uint32_t select_top_slots(const uint32_t (&key)[KPT],
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
             if (key[j] != 0u && key[j] == lo && take > 0u) {
-                picks |= 1u << j;
+                picks |= Mask(1) << j;
                 --take;
             }
         }

@@ -305,6 +305,17 @@ def test_topk_rows_past_65536(dsa, kind):
     _topk_case(dsa, len(n_vis), 70000, n_vis, kind, seed=22)
 
 
+@pytest.mark.parametrize("kind", ["ties", "normal", "equal", "signed_zero"])
+def test_topk_rows_single_pass(dsa, kind):
+    """Rows of up to 40,960 pools are selected in one pass over their scores
+    (no workspace); 40,964 takes the tile path."""
+    n_vis = np.array([0, 1, 511, 512, 513, 2000, 20000, 40959, 40960, 33792], dtype=np.int64)
+    say(f"topk single pass {kind}")
+    assert dsa.topk_workspace_bytes(dsa.Dims.of(syn.production_dims(16)), len(n_vis), 40960) == 0
+    _topk_case(dsa, len(n_vis), 40960, n_vis, kind, seed=25)
+    _topk_case(dsa, 3, 40964, np.array([40964, 40961, 600], dtype=np.int64), kind, seed=26)
+
+
 def test_topk_rows_of_262144(dsa):
     n_vis = np.array([262144, 262143, 384, 1], dtype=np.int64)
     say("topk long 262144")
@@ -407,12 +418,15 @@ def test_sparse_mla_h64_small_batch(dsa):
     _mla_case(dsa, wl, 4, valid, 0)
 
 
-def test_sparse_mla_h64_prefill_tiles(dsa):
+@pytest.mark.parametrize("splits", [1, 3])
+def test_sparse_mla_h64_prefill_tiles(dsa, splits):
+    """The many-query kernel (64 heads a workgroup, 8 waves), whole lists per
+    workgroup or split with partials and the merge."""
     wl = syn.mini_heavy()
     g = np.random.default_rng(3)
     valid = g.integers(0, 2177, size=160)
     valid[:3] = [0, 2176, 2051]
-    _mla_case(dsa, wl, 160, valid, 1)
+    _mla_case(dsa, wl, 160, valid, splits)
 
 
 def test_sparse_mla_bf16_output(dsa):

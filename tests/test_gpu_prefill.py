@@ -1,7 +1,11 @@
 """The bounded-workspace selection for many queries (dsa_index_select_chunked)
 against the unbounded calls (dsa_index_scores over all queries, then
 dsa_topk_select_expand): the same pool ids and index lists, bit for bit,
-whatever the chunk size (ragged last chunks included)."""
+whatever the chunk size (ragged last chunks included).  The chunks select
+rows of up to 40,960 pools in one pass (mini_prefill), wider rows from the
+scoring pass's 64-pool group lists (mini_prefill_wide, 45,024 pools) or, past
+65,536 pools, from sorted score tiles (mini_long); the unbounded calls use
+the one-pass or tile selection."""
 import pytest
 import torch
 
@@ -24,6 +28,8 @@ def harness():
 
 @pytest.mark.parametrize("name,chunk", [("mini_prefill", 64), ("mini_prefill", 50), ("mini_prefill", 200),
                                         ("mini_prefill", 1), ("mini_decode", 3), ("tiny", 10),
+                                        ("mini_prefill_wide", 80), ("mini_prefill_wide", 40),
+                                        ("mini_long", 2),
                                         pytest.param("prefill_4k_on_131k", 512, marks=pytest.mark.slow)])
 def test_chunked_selection_matches_unbounded(harness, name, chunk):
     wl = syn.get(name)
