@@ -547,7 +547,7 @@ def main():
         s_tf = chunk_flops / (score_us * 1e-6) / 1e12
         a_tf = pw["attn_flops"] / (attn_us * 1e-6) / 1e12
         kernels = {
-            "index_scores (k_scores_mfma<8,4>), one 512-query chunk": {
+            "index_scores (k_scores_mfma<4,2>), one 512-query chunk": {
                 "avg_launch_us": round(score_us, 1), "flops_per_launch": chunk_flops,
                 "achieved_tflops": round(s_tf, 1), "frac": round(s_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                 "launches_per_step": n_chunks},
@@ -561,7 +561,7 @@ def main():
                                       / MFMA_BF16_PEAK_TFLOPS, 2)
         line["flops_per_step"] = pw["score_flops"] + pw["attn_flops"]
         line["roofline"] = {
-            "kernel": "sparse_mla (k_mla_mfma<4, 8>)" if dom_attn else "index_scores (k_scores_mfma<8,4>)",
+            "kernel": "sparse_mla (k_mla_mfma<4, 8>)" if dom_attn else "index_scores (k_scores_mfma<4,2>)",
             "bound": "mfma", "achieved": round(a_tf if dom_attn else s_tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round((a_tf if dom_attn else s_tf) / MFMA_BF16_PEAK_TFLOPS, 4),
             "traffic": None, "flops_per_launch": pw["attn_flops"] if dom_attn else chunk_flops,

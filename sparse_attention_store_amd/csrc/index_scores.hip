@@ -33,7 +33,7 @@ constexpr int kQBYTES = kHI * kDI * 2;                // 8 KB per query
 // pool p0 + l, so the wave is one group.  The selection then reads the group
 // lists (k_topk_groups) instead of sorting 256-pool tiles of the scores.
 template <int WAVES, int QB, bool CANDS = false>
-__global__ __launch_bounds__(WAVES * 64) void k_scores_mfma(
+__global__ __launch_bounds__(WAVES * 64, CANDS ? 2 : 3) void k_scores_mfma(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint16_t* __restrict__ pools, const int32_t* __restrict__ first_valid,
     const int64_t* __restrict__ pool_base, const int32_t* __restrict__ q_seq,
@@ -532,6 +532,10 @@ void time_next_scoring_launch(hipEvent_t start, hipEvent_t stop) {
     t_ev_stop = stop;
 }
 
+// Prefill scoring geometry (k_scores_mfma): waves per workgroup, queries per workgroup.
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillQPB = 32;
+
 // Workgroups (one 256-pool tile each) for k_scores_groups: every tile of
 // every query if that fits, else 4 per CU, which stay resident.
 static unsigned scores_groups_grid(int32_t T, int32_t stride) {
@@ -554,14 +558,18 @@ hipError_t launch_index_scores(const dsa_dims& d, const uint16_t* q_idx, const f
                                   s, ev0, ev1, 0, q_idx, w, pools, seqs.first_valid, seqs.pool_base, q_seq,
                                   q_pos, T, num_seqs, stride, scores, 0, nullptr, nullptr, dsa::AppendArgs{}, nullptr, dsa::PagedMap{});
         } else {
-            // Prefill: 512 resident pools per workgroup, 64 queries per workgroup.
-            const int qpb = 64;
-            dim3 grid((unsigned)cdiv(stride, 512), (unsigned)cdiv(T, qpb)), block(512);
+            // Prefill: 256 resident pools per workgroup (4 waves), 32 queries
+            // per workgroup: three workgroups per CU (168 VGPRs) and about 2,100
+            // workgroups per 512-query chunk of the prefill config, where 8-wave
+            // workgroups of 64 queries ran one per CU in 2.06 rounds (242 vs
+            // 218 us a chunk).
+            dim3 grid((unsigned)cdiv(stride, kPrefillWaves * 64), (unsigned)cdiv(T, kPrefillQPB)),
+                block(kPrefillWaves * 64);
             hipEvent_t ev0, ev1;
             take_events(ev0, ev1);
-            hipExtLaunchKernelGGL((dsa::k_scores_mfma<8, 4>), grid, block, 0, s, ev0, ev1, 0, q_idx, w, pools,
-                                  seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, qpb, stride, scores, 0,
-                                  nullptr, nullptr);
+            hipExtLaunchKernelGGL((dsa::k_scores_mfma<kPrefillWaves, 2>), grid, block, 0, s, ev0, ev1, 0, q_idx, w,
+                                  pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, kPrefillQPB, stride,
+                                  scores, 0, nullptr, nullptr);
         }
     } else {
         dim3 grid((unsigned)cdiv(stride, 256), (unsigned)T), block(256);
@@ -583,12 +591,11 @@ hipError_t launch_scores_lists(const dsa_dims& d, const uint16_t* q_idx, const f
     uint64_t* cand;
     int32_t* cand_n;
     group_lists(ws, T, cand, cand_n);
-    const int qpb = 64;
-    dim3 grid((unsigned)cdiv(stride, 512), (unsigned)cdiv(T, qpb)), block(512);
+    dim3 grid((unsigned)cdiv(stride, kPrefillWaves * 64), (unsigned)cdiv(T, kPrefillQPB)), block(kPrefillWaves * 64);
     hipEvent_t ev0, ev1;
     take_events(ev0, ev1);
-    hipExtLaunchKernelGGL((dsa::k_scores_mfma<8, 4, true>), grid, block, 0, s, ev0, ev1, 0, q_idx, w, pools,
-                          seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, qpb, stride, scores,
+    hipExtLaunchKernelGGL((dsa::k_scores_mfma<kPrefillWaves, 2, true>), grid, block, 0, s, ev0, ev1, 0, q_idx, w,
+                          pools, seqs.first_valid, seqs.pool_base, q_seq, q_pos, T, kPrefillQPB, stride, scores,
                           d.index_topk / d.kpool, cand, cand_n);
     return hipGetLastError();
 }

@@ -310,12 +310,12 @@ __device__ __forceinline__ void mla_rows_split(
                     l_run += p;
                     x[h] = p * fmaxf(sc[rt][i], 0.f);
                 }
-                const uint32_t h0 = f32_to_bf16_rne(x[0]), h1 = f32_to_bf16_rne(x[1]);
-                const uint32_t l0 = f32_to_bf16_rne(x[0] - bf16_to_f32(h0));
-                const uint32_t l1 = f32_to_bf16_rne(x[1] - bf16_to_f32(h1));
-                bh[rt][i2] = h0 | (h1 << 16);
-                bl[rt][i2] = l0 | (l1 << 16);
-                p_run += (bf16_to_f32(h0) + bf16_to_f32(l0)) + (bf16_to_f32(h1) + bf16_to_f32(l1));
+                uint32_t hp, lp;
+                split_bf16x2(x[0], x[1], hp, lp);
+                bh[rt][i2] = hp;
+                bl[rt][i2] = lp;
+                p_run += (__uint_as_float(hp << 16) + __uint_as_float(lp << 16)) +
+                         (__uint_as_float(hp & 0xFFFF0000u) + __uint_as_float(lp & 0xFFFF0000u));
             }
         if (live) {
 #pragma unroll

@@ -226,15 +226,22 @@ __global__ __launch_bounds__(64 * NW, 1) void k_mla_mfma(
         for (int rr = 0; rr < RPW; ++rr) {
             const int row = (sub * RPW + rr) * 16 + n16;
             const float rsv = rs[row];
+            float x[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float p = m_new[i] == -INFINITY ? 0.f : exp2f(z[rr][i] - m_new[i]);
                 psum[i] += p;
-                const float x = p * rsv;
-                const uint32_t hi = f32_to_bf16_rne(x);
-                const int o = (ht * 16 + 4 * g4 + i) * kPRow + row;
-                pl[0][o] = (uint16_t)hi;
-                pl[1][o] = (uint16_t)f32_to_bf16_rne(x - bf16_to_f32(hi));
+                x[i] = p * rsv;
+            }
+#pragma unroll
+            for (int i2 = 0; i2 < 2; ++i2) {
+                uint32_t hp, lp;
+                split_bf16x2(x[2 * i2], x[2 * i2 + 1], hp, lp);
+                const int o = (ht * 16 + 4 * g4 + 2 * i2) * kPRow + row;
+                pl[0][o] = (uint16_t)hp;
+                pl[0][o + kPRow] = (uint16_t)(hp >> 16);
+                pl[1][o] = (uint16_t)lp;
+                pl[1][o + kPRow] = (uint16_t)(lp >> 16);
             }
         }
 #pragma unroll
