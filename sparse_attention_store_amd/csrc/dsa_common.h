@@ -81,6 +81,22 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// Cross-half sums by gfx950's lane swaps (v_permlane32_swap_b32 trades the
+// upper 32 lanes of one register with the lower 32 of another, 16-swap the
+// odd and even 16-lane rows), no trip through the LDS pipe.  add_swap32(a, b):
+// lanes 0..31 get a + a of lane l + 32, lanes 32..63 b + b of lane l - 32;
+// add_swap16 the same across rows (lane l ^ 16).  Each sum adds the same two
+// values in both lanes, so the results are those of the xor shuffles.
+__device__ __forceinline__ float add_swap32(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float add_swap16(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ---------------------------------------------------------------- DPP wave scans (integers)
 // Inclusive scans over the 64 lanes with row shifts and row broadcasts: a
 // handful of VALU operations instead of cross-lane shuffles through the LDS
@@ -100,6 +116,31 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x, uint32_t iden
     x = op(x, dpp_u32<0x142, 0xA>(x, identity));      // row_bcast:15 into rows 1 and 3
     x = op(x, dpp_u32<0x143, 0xC>(x, identity));      // row_bcast:31 into rows 2 and 3
     return x;
+}
+
+// Max and sum over each row of 16 lanes, every lane of the row getting the
+// result: a butterfly of DPP moves (lane ^ 1 and lane ^ 2 within quads, then
+// the row's half mirror and mirror, which pair quads and halves) instead of
+// cross-lane shuffles through the LDS pipe.  Each step adds a pair of lanes in
+// both of them (the same two values), so every lane gets the same bits, the
+// bits the xor-1, 2, 4, 8 shuffle butterfly gives.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_f32<0xB1>(x));                   // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp_f32<0x4E>(x));                   // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp_f32<0x141>(x));                  // row_half_mirror
+    return fmaxf(x, dpp_f32<0x140>(x));               // row_mirror
+}
+
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_f32<0xB1>(x);
+    x += dpp_f32<0x4E>(x);
+    x += dpp_f32<0x141>(x);
+    return x + dpp_f32<0x140>(x);
 }
 
 // Inclusive sum within each row of 16 lanes (the first four steps above).

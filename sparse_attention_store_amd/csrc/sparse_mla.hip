@@ -85,13 +85,15 @@ __global__ __launch_bounds__(64 * NW, 1) void k_mla_mfma(
     constexpr int SEGS = NT / kChunk;     // threads per gathered row
     constexpr int SEGB = kD / SEGS;       // bytes of a row per thread
     static_assert(WPHT * HT == NW && RPW * WPHT == 4 && SEGB % 16 == 0, "64-row chunks, 16-row tiles");
-    __shared__ __attribute__((aligned(16))) uint16_t kv[kChunk * kKVRow];
+    // The rows of two chunks (the one computed, the next being converted), so
+    // that converting chunk c + 1 needs no barrier after chunk c's P'V.
+    __shared__ __attribute__((aligned(16))) uint16_t kv[2][kChunk * kKVRow];
     __shared__ __attribute__((aligned(16))) uint16_t pl[2][HPW * kPRow];   // P' hi, lo
     __shared__ float rs[kChunk];
     __shared__ int rvalid[kChunk];
     __shared__ float red_max[NW][16];
     __shared__ float red_sum[NW][16];
-    __shared__ int chunk_any[NW];
+    __shared__ int chunk_any[2][NW];
     __shared__ int idx_lds[kMaxSplitRows];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -124,7 +126,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_mla_mfma(
 
     // Row gather: thread -> (row tid / SEGS, SEGB-byte segment).  The split's
     // slice of the index list is staged in LDS once, so the loop issues the
-    // rows of chunk c+1 before chunk c computes without any dependent global
+    // rows of chunk c+2 before chunk c computes without any dependent global
     // load (or register copy of one) in between.
     const int r = tid / SEGS, sg = tid % SEGS;
     const int split_rows = (c_end - c_begin) * kChunk;
@@ -147,44 +149,55 @@ __global__ __launch_bounds__(64 * NW, 1) void k_mla_mfma(
             rsc = 0.f;
         }
     };
-    if (c_begin < c_end) load_rows(idx_lds[r]);
-
-    for (int c = c_begin; c < c_end; ++c) {
-        // ---- 1. dequant the gathered rows to bf16 in LDS, then request the next chunk
-        lds_barrier();                                   // previous chunk's readers are done
+    // Chunk c's rows to bf16 in kv[buf], its row scales and validity, then
+    // the request for chunk c + 2's rows.  The writes are safe without a
+    // barrier of their own: kv[buf] was last read by chunk c - 2's P'V, and
+    // rs / rvalid by chunk c - 1's softmax, both before chunk c - 1's last
+    // barrier; chunk_any alternates too, as a wave may write chunk c's while
+    // another still reads chunk c - 1's.
+    auto convert = [&](int c, int buf) {
         const int idx_cur = idx_lds[(c - c_begin) * kChunk + r];
         if (sg == 0) { rs[r] = rsc; rvalid[r] = idx_cur >= 0; }
-        const bool have = idx_cur >= 0;
-        {
-            uint16_t* dst = &kv[r * kKVRow + sg * SEGB];
+        uint16_t* dst = &kv[buf][r * kKVRow + sg * SEGB];
 #pragma unroll
-            for (int i = 0; i < SEGB / 16; ++i) {
-                uint32_t bq[8];
-                int8x4_to_bf16x4(raw[i][0], bq[0], bq[1]);
-                int8x4_to_bf16x4(raw[i][1], bq[2], bq[3]);
-                int8x4_to_bf16x4(raw[i][2], bq[4], bq[5]);
-                int8x4_to_bf16x4(raw[i][3], bq[6], bq[7]);
-                const u32x4 o0 = {bq[0], bq[1], bq[2], bq[3]};
-                const u32x4 o1 = {bq[4], bq[5], bq[6], bq[7]};
-                *reinterpret_cast<u32x4*>(dst + 16 * i) = o0;
-                *reinterpret_cast<u32x4*>(dst + 16 * i + 8) = o1;
-            }
+        for (int i = 0; i < SEGB / 16; ++i) {
+            uint32_t bq[8];
+            int8x4_to_bf16x4(raw[i][0], bq[0], bq[1]);
+            int8x4_to_bf16x4(raw[i][1], bq[2], bq[3]);
+            int8x4_to_bf16x4(raw[i][2], bq[4], bq[5]);
+            int8x4_to_bf16x4(raw[i][3], bq[6], bq[7]);
+            const u32x4 o0 = {bq[0], bq[1], bq[2], bq[3]};
+            const u32x4 o1 = {bq[4], bq[5], bq[6], bq[7]};
+            *reinterpret_cast<u32x4*>(dst + 16 * i) = o0;
+            *reinterpret_cast<u32x4*>(dst + 16 * i + 8) = o1;
         }
         if (c + 1 < c_end) load_rows(idx_lds[(c + 1 - c_begin) * kChunk + r]);
-        const unsigned long long vote = __ballot(have);
-        if ((tid & 63) == 0) chunk_any[wave] = vote != 0ull;
-        lds_barrier();
+        const unsigned long long vote = __ballot(idx_cur >= 0);
+        if ((tid & 63) == 0) chunk_any[buf][wave] = vote != 0ull;
+    };
+    if (c_begin < c_end) {
+        load_rows(idx_lds[r]);
+        convert(c_begin, 0);
+    }
+
+    for (int c = c_begin; c < c_end; ++c) {
+        const int buf = (c - c_begin) & 1;
+        const uint16_t* kvb = kv[buf];
+        lds_barrier();                                   // chunk c converted; chunk c - 1's P'V done
         int any = 0;
 #pragma unroll
-        for (int i = 0; i < NW; ++i) any |= chunk_any[i];
-        if (!any) continue;                              // empty chunk
+        for (int i = 0; i < NW; ++i) any |= chunk_any[buf][i];
+        if (!any) {                                      // empty chunk
+            if (c + 1 < c_end) convert(c + 1, buf ^ 1);
+            continue;
+        }
 
         // ---- 2. S for this wave's head tile and row tiles sub*RPW .. sub*RPW+RPW-1
         f32x4 sacc[RPW];
 #pragma unroll
         for (int rr = 0; rr < RPW; ++rr) {
             const int rt = sub * RPW + rr;
-            const uint16_t* kr = &kv[(rt * 16 + n16) * kKVRow + g4 * 8];
+            const uint16_t* kr = &kvb[(rt * 16 + n16) * kKVRow + g4 * 8];
             f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < 16; ++j)
@@ -206,9 +219,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_mla_mfma(
             }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) cmax[i] = fmaxf(cmax[i], __shfl_xor(cmax[i], o, 64));
+        for (int i = 0; i < 4; ++i) cmax[i] = row16_max(cmax[i]);
         if (n16 == 0)
 #pragma unroll
             for (int i = 0; i < 4; ++i) red_max[wave][4 * g4 + i] = cmax[i];
@@ -245,9 +256,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_mla_mfma(
             }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) psum[i] += __shfl_xor(psum[i], o, 64);
+        for (int i = 0; i < 4; ++i) psum[i] = row16_sum(psum[i]);
         if (n16 == 0)
 #pragma unroll
             for (int i = 0; i < 4; ++i) red_sum[wave][4 * g4 + i] = psum[i];
@@ -278,22 +287,27 @@ __global__ __launch_bounds__(64 * NW, 1) void k_mla_mfma(
                 const int col0 = 64 * (sub * NGRP + gi) + 4 * n16;
                 u32x2 v[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = *reinterpret_cast<const u32x2*>(&kv[(row0 + e) * kKVRow + col0]);
+                for (int e = 0; e < 8; ++e) v[e] = *reinterpret_cast<const u32x2*>(&kvb[(row0 + e) * kKVRow + col0]);
+                u32x4 bb[4];
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
                     const int wd = tt >> 1;
                     const uint32_t sel = (tt & 1) ? 0x07060302u : 0x05040100u;
-                    u32x4 bb;
-                    bb[0] = __builtin_amdgcn_perm(v[1][wd], v[0][wd], sel);
-                    bb[1] = __builtin_amdgcn_perm(v[3][wd], v[2][wd], sel);
-                    bb[2] = __builtin_amdgcn_perm(v[5][wd], v[4][wd], sel);
-                    bb[3] = __builtin_amdgcn_perm(v[7][wd], v[6][wd], sel);
-                    oacc[gi][tt] = mfma16(a_hi, as_bf16x8(bb), oacc[gi][tt]);
-                    oacc[gi][tt] = mfma16(a_lo, as_bf16x8(bb), oacc[gi][tt]);
+                    bb[tt][0] = __builtin_amdgcn_perm(v[1][wd], v[0][wd], sel);
+                    bb[tt][1] = __builtin_amdgcn_perm(v[3][wd], v[2][wd], sel);
+                    bb[tt][2] = __builtin_amdgcn_perm(v[5][wd], v[4][wd], sel);
+                    bb[tt][3] = __builtin_amdgcn_perm(v[7][wd], v[6][wd], sel);
                 }
+                // the four hi products, then the four lo ones: no MFMA waits on
+                // the one just issued
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) oacc[gi][tt] = mfma16(a_hi, as_bf16x8(bb[tt]), oacc[gi][tt]);
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) oacc[gi][tt] = mfma16(a_lo, as_bf16x8(bb[tt]), oacc[gi][tt]);
                 if constexpr (NW == 8) __builtin_amdgcn_sched_barrier(0);   // one group's V loads in flight at a time
             }
         }
+        if (c + 1 < c_end) convert(c + 1, buf ^ 1);
     }
 
     // ---- epilogue: lane holds heads head0 + 4*g4 + i, columns 64*grp + 4*n16 + tt
