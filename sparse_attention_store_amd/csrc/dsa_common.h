@@ -97,6 +97,16 @@ __device__ __forceinline__ float add_swap16(float a, float b) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+__device__ __forceinline__ float max_swap32(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float max_swap16(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // ---------------------------------------------------------------- DPP wave scans (integers)
 // Inclusive scans over the 64 lanes with row shifts and row broadcasts: a
 // handful of VALU operations instead of cross-lane shuffles through the LDS
@@ -141,6 +151,20 @@ __device__ __forceinline__ float row16_sum(float x) {
     x += dpp_f32<0x4E>(x);
     x += dpp_f32<0x141>(x);
     return x + dpp_f32<0x140>(x);
+}
+
+// Max and sum over all 64 lanes, every lane getting the result: the row
+// butterflies above, then the lane swaps across rows and halves.
+__device__ __forceinline__ float wave_allmax(float x) {
+    x = row16_max(x);
+    x = max_swap16(x, x);
+    return max_swap32(x, x);
+}
+
+__device__ __forceinline__ float wave_allsum(float x) {
+    x = row16_sum(x);
+    x = add_swap16(x, x);
+    return add_swap32(x, x);
 }
 
 // Inclusive sum within each row of 16 lanes (the first four steps above).

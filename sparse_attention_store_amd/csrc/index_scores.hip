@@ -141,9 +141,7 @@ __global__ __launch_bounds__(WAVES * 64, CANDS ? 2 : 3) void k_scores_mfma(
                 s0 += wh * fmaxf(acc0[r], 0.f);
                 s1 += wh * fmaxf(acc1[r], 0.f);
             }
-            s0 += __shfl_xor(s0, 32, 64);
-            s1 += __shfl_xor(s1, 32, 64);
-            const float sv = g == 0 ? s0 : s1;
+            const float sv = add_swap32(s0, s1);           // lanes 0-31: tile 0's sum, 32-63: tile 1's
             const int p = p0 + g * 32 + n;                 // lanes 0-31: tile 0, 32-63: tile 1
             if (p < stride) out[p] = p < n_vis ? sv : -INFINITY;
             if constexpr (CANDS) {

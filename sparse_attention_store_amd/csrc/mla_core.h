@@ -194,8 +194,8 @@ __device__ __forceinline__ void mla_rows_split(
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             qsum += bf16_to_f32(qb[j][k] & 0xFFFFu) + bf16_to_f32(qb[j][k] >> 16);
-    qsum += __shfl_xor(qsum, 16, 64);
-    qsum += __shfl_xor(qsum, 32, 64);
+    qsum = add_swap16(qsum, qsum);
+    qsum = add_swap32(qsum, qsum);
     const float sbias = 128.0f * qsum;
 
     // Running softmax state of head n16 (the same in every wave); l and the
@@ -261,8 +261,8 @@ __device__ __forceinline__ void mla_rows_split(
                 z[rt][i] = sc[rt][i] > 0.f ? (s[rt][i] - sbias) * (sc[rt][i] * scale_log2) : -INFINITY;
                 cmax = fmaxf(cmax, z[rt][i]);
             }
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+        cmax = max_swap16(cmax, cmax);
+        cmax = max_swap32(cmax, cmax);
         if (g4 == 0) sm.red_max[w][n16] = cmax;
         lds_barrier();
         float wmax[NW];
@@ -360,14 +360,12 @@ __device__ __forceinline__ void mla_rows_split(
     }
 
     // ---- totals over the NW waves' rows, then this wave's CW columns out
-    l_run += __shfl_xor(l_run, 16, 64);
-    l_run += __shfl_xor(l_run, 32, 64);
-    p_run += __shfl_xor(p_run, 16, 64);
-    p_run += __shfl_xor(p_run, 32, 64);
-    if (g4 == 0) {
-        sm.red_l[w][n16] = l_run;
-        sm.red_p[w][n16] = p_run;
-    }
+    // rows 0 and 2 carry l, rows 1 and 3 p: after the two swaps lanes 0..15
+    // hold the wave's l totals and lanes 16..31 its p totals (the sums of the
+    // xor-16, then xor-32 butterfly, bit for bit)
+    const float lp = add_swap32(add_swap16(l_run, p_run), add_swap16(l_run, p_run));
+    if (g4 == 0) sm.red_l[w][n16] = lp;
+    if (g4 == 1) sm.red_p[w][n16] = lp;
     lds_barrier();
     float L = 0.f, PS = 0.f;
 #pragma unroll

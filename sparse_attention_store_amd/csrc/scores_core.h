@@ -80,12 +80,10 @@ __device__ __forceinline__ void load_pool_group(const uint16_t* __restrict__ row
 // partial of pools 16 r + c for every r; lane group g ends with the full sum
 // of N-tile r = g, so lane l holds pool l.
 __device__ __forceinline__ float reduce_group_parts(const float (&part)[4]) {
-    const int lane = threadIdx.x & 63;
-    const bool h = (lane & 32) != 0;     // keeps N-tiles 2h, 2h + 1
-    const float k0 = (h ? part[2] : part[0]) + __shfl_xor(h ? part[0] : part[2], 32, 64);
-    const float k1 = (h ? part[3] : part[1]) + __shfl_xor(h ? part[1] : part[3], 32, 64);
-    const bool j = (lane & 16) != 0;     // keeps N-tile 2h + j
-    return (j ? k1 : k0) + __shfl_xor(j ? k0 : k1, 16, 64);
+    // lane half h keeps N-tiles 2h, 2h + 1, then row j of it N-tile 2h + j
+    const float k0 = add_swap32(part[0], part[2]);
+    const float k1 = add_swap32(part[1], part[3]);
+    return add_swap16(k0, k1);
 }
 
 // Returns the score of pool (lane) of the group.
@@ -126,8 +124,8 @@ __device__ __forceinline__ float score_pool_column(const IdxQuery& Q, const u32x
     for (int i = 0; i < 4; ++i) sum += Q.w[0][i] * fmaxf(acc0[i], 0.f);
 #pragma unroll
     for (int i = 0; i < 4; ++i) sum += Q.w[1][i] * fmaxf(acc1[i], 0.f);
-    const float k = sum + __shfl_xor(sum, 32, 64);
-    return k + __shfl_xor(k, 16, 64);
+    const float k = add_swap32(sum, sum);
+    return add_swap16(k, k);
 }
 
 // ------------------------------------------------------------------ INT8 pools
@@ -163,8 +161,8 @@ __device__ __forceinline__ void load_idx_query_lds_i8(const uint16_t* q_lds, int
             for (int e = 0; e < 4; ++e)
                 acc += bf16_to_f32(Q.q.a[mt][s][e] & 0xFFFFu) + bf16_to_f32(Q.q.a[mt][s][e] >> 16);
         }
-        acc += __shfl_xor(acc, 16, 64);
-        qsum[mt] = acc + __shfl_xor(acc, 32, 64);          // head 16 mt + c, in every lane group
+        acc = add_swap16(acc, acc);
+        qsum[mt] = add_swap32(acc, acc);                   // head 16 mt + c, in every lane group
     }
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -233,8 +231,8 @@ __device__ __forceinline__ float score_pool_column_i8(const IdxQueryI8& Q, const
         acc1 = mfma16(as_bf16x8(Q.q.a[1][s]), as_bf16x8(b), acc1);
     }
     const float sum = i8_head_sum(Q, acc0, acc1);
-    const float k = sum + __shfl_xor(sum, 32, 64);
-    return (k + __shfl_xor(k, 16, 64)) * scale;
+    const float k = add_swap32(sum, sum);
+    return add_swap16(k, k) * scale;
 }
 
 }  // namespace dsa

@@ -385,14 +385,10 @@ __global__ __launch_bounds__(64) void k_mla_combine(
     MlaPartial p = {-INFINITY, 0.f};
     if (lane < splits) p = part_ml[((int64_t)t * splits + lane) * H + h];
     const bool live = p.l > 0.f;
-    float M = live ? p.m : -INFINITY;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    const float M = wave_allmax(live ? p.m : -INFINITY);
     const float w = live ? exp2f(p.m - M) : 0.f;
-    float L = p.l * w;
-    // Sum in split order (a fixed tree over lanes 0..63) for determinism.
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
+    // a fixed tree over lanes 0..63 (every lane the same bits): deterministic
+    const float L = wave_allsum(p.l * w);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < kPre; ++u) {
