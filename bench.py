@@ -111,6 +111,15 @@ def _source_hash(srcs) -> str:
     return h.hexdigest()[:16]
 
 
+def device_info() -> dict:
+    """What the runtime reports of the GPU the line was measured on (the peaks
+    above are the spec sheet's; this confirms the part and its unit counts)."""
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2**30, 1), "l2_bytes": getattr(p, "L2_cache_size", None)}
+
+
 def traffic_from_profile(summary: str, srcs, block: int = 0):
     """HBM bytes per launch of the dominant kernel from a committed rocprofv3
     counter summary (its block-th kernel summary), or None when the summary is
@@ -538,6 +547,7 @@ def main():
                     "samples": len(per_step_us), "steps_per_sample": R if not prefill else 1},
         "copy_gbs": round(copy_gbs, 1),
         "stages_us_median": stages,
+        "device": device_info(),
     }
     if prefill:
         pw = prefill_work(wl)

@@ -429,6 +429,19 @@ def test_sparse_mla_h64_prefill_tiles(dsa, splits):
     _mla_case(dsa, wl, 160, valid, splits)
 
 
+@pytest.mark.parametrize("splits", [1, 2])
+def test_sparse_mla_h32_prefill_tiles(dsa, splits):
+    """32 heads over many queries: the many-query kernel with two 16-head
+    tiles a workgroup (k_mla_mfma<2, 4>)."""
+    import dataclasses
+    wl = syn.mini_heavy()
+    wl = dataclasses.replace(wl, dims=syn.production_dims(32), name="mini_heavy_h32")
+    g = np.random.default_rng(5)
+    valid = g.integers(0, 2177, size=300)
+    valid[:3] = [0, 2176, 1]
+    _mla_case(dsa, wl, 300, valid, splits)
+
+
 def test_sparse_mla_bf16_output(dsa):
     wl = syn.mini_decode()
     valid = np.array([2051, 100, 0, 2176], dtype=np.int64)
