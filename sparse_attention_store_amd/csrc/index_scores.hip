@@ -532,7 +532,7 @@ void time_next_scoring_launch(hipEvent_t start, hipEvent_t stop) {
 
 // Prefill scoring geometry (k_scores_mfma): waves per workgroup, queries per workgroup.
 constexpr int kPrefillWaves = 4;
-constexpr int kPrefillQPB = 32;
+constexpr int kPrefillQPB = 24;
 
 // Workgroups (one 256-pool tile each) for k_scores_groups: every tile of
 // every query if that fits, else 4 per CU, which stay resident.
@@ -556,11 +556,11 @@ hipError_t launch_index_scores(const dsa_dims& d, const uint16_t* q_idx, const f
                                   s, ev0, ev1, 0, q_idx, w, pools, seqs.first_valid, seqs.pool_base, q_seq,
                                   q_pos, T, num_seqs, stride, scores, 0, nullptr, nullptr, dsa::AppendArgs{}, nullptr, dsa::PagedMap{});
         } else {
-            // Prefill: 256 resident pools per workgroup (4 waves), 32 queries
-            // per workgroup: three workgroups per CU (168 VGPRs) and about 2,100
-            // workgroups per 512-query chunk of the prefill config, where 8-wave
-            // workgroups of 64 queries ran one per CU in 2.06 rounds (242 vs
-            // 218 us a chunk).
+            // Prefill: 256 resident pools per workgroup (4 waves), 24 queries
+            // per workgroup: three workgroups per CU (168 VGPRs) and about 2,900
+            // workgroups per 512-query chunk of the prefill config (3.8 rounds of
+            // 768), where 8-wave workgroups of 64 queries ran one per CU in 2.06
+            // rounds (242 us a chunk against 169 us; 32 or 48 queries: 173, 171).
             dim3 grid((unsigned)cdiv(stride, kPrefillWaves * 64), (unsigned)cdiv(T, kPrefillQPB)),
                 block(kPrefillWaves * 64);
             hipEvent_t ev0, ev1;
