@@ -21,12 +21,14 @@ struct alignas(8) MlaPartial {
     float l;   // running sum
 };
 
+// 4 INT8 codes -> 4 bf16 of the signed codes.  Each code is sign-extended
+// from its byte inside the conversion (hipcc selects v_cvt_f32_i32 with an
+// SDWA sext byte operand: one instruction a code, no extract or bias).
 __device__ __forceinline__ void int8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
-    const uint32_t u = w ^ 0x80808080u;            // biased to unsigned: code + 128
-    const float f0 = (float)(u & 0xFFu) - 128.0f;
-    const float f1 = (float)((u >> 8) & 0xFFu) - 128.0f;
-    const float f2 = (float)((u >> 16) & 0xFFu) - 128.0f;
-    const float f3 = (float)(u >> 24) - 128.0f;
+    const float f0 = (float)(int32_t)(int8_t)(w & 0xFFu);
+    const float f1 = (float)(int32_t)(int8_t)((w >> 8) & 0xFFu);
+    const float f2 = (float)(int32_t)(int8_t)((w >> 16) & 0xFFu);
+    const float f3 = (float)((int32_t)w >> 24);
     // Small integers are exact in bf16: keep the upper halves.
     lo = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
     hi = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);

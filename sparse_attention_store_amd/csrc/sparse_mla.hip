@@ -82,9 +82,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_mla_mfma(
     constexpr int WPHT = NW / HT;         // waves per head tile
     constexpr int RPW = 4 / WPHT;         // 16-row tiles per wave (S)
     constexpr int NGRP = 8 / WPHT;        // 64-column groups per wave (PV)
-    constexpr int SEGS = NT / kChunk;     // threads per gathered row
-    constexpr int SEGB = kD / SEGS;       // bytes of a row per thread
-    static_assert(WPHT * HT == NW && RPW * WPHT == 4 && SEGB % 16 == 0, "64-row chunks, 16-row tiles");
+    constexpr int RW = kChunk / NW;       // gathered rows per wave
+    static_assert(WPHT * HT == NW && RPW * WPHT == 4 && RW * NW == kChunk && RW <= 64, "64-row chunks, 16-row tiles");
     // The rows of two chunks (the one computed, the next being converted), so
     // that converting chunk c + 1 needs no barrier after chunk c's P'V.
     __shared__ __attribute__((aligned(16))) uint16_t kv[2][kChunk * kKVRow];
@@ -124,30 +123,36 @@ __global__ __launch_bounds__(64 * NW, 1) void k_mla_mfma(
     const int c_end = min(c_begin + chunks_per_split, nchunks);
     const int32_t* idx_row = indices + (int64_t)t * W;
 
-    // Row gather: thread -> (row tid / SEGS, SEGB-byte segment).  The split's
-    // slice of the index list is staged in LDS once, so the loop issues the
-    // rows of chunk c+2 before chunk c computes without any dependent global
-    // load (or register copy of one) in between.
-    const int r = tid / SEGS, sg = tid % SEGS;
+    // Row gather: wave w takes the chunk's rows RW w .. RW w + RW - 1, lane l
+    // the 8 codes 8 l .. 8 l + 7 of each (one 8-byte load a row: 512
+    // contiguous bytes a wave).  Its bf16 stores to LDS are then 16
+    // consecutive bytes a lane, so the 8 lanes of a store phase fill 128
+    // consecutive bytes, one per bank; lanes that each held a 64-code segment
+    // of one row stored 128 bytes apart, all 8 into the same 4 banks.  The
+    // split's slice of the index list is staged in LDS once, so the loop
+    // issues the rows of chunk c+2 before chunk c computes without any
+    // dependent global load in between.
     const int split_rows = (c_end - c_begin) * kChunk;
     for (int i = tid; i < split_rows; i += NT) {
         const int pos = c_begin * kChunk + i;
         idx_lds[i] = pos < W ? idx_row[pos] : -1;
     }
     lds_barrier();
-    u32x4 raw[SEGB / 16];
-    float rsc = 0.f;
-    auto load_rows = [&](int idx) {
-        if (idx >= 0) {
-            const uint8_t* src = cache + (int64_t)idx * row_bytes + sg * SEGB;
+    u32x2 raw[RW];
+    float rsc = 0.f;                                 // lane k < RW: the scale of the wave's row k
+    // lane k < RW: the id of the wave's row k in chunk c (-1: empty slot)
+    auto row_ids = [&](int c) { return idx_lds[(c - c_begin) * kChunk + RW * wave + min(lane, RW - 1)]; };
+    auto load_rows = [&](int c) {
+        const int mine = row_ids(c);
 #pragma unroll
-            for (int i = 0; i < SEGB / 16; ++i) raw[i] = *reinterpret_cast<const u32x4*>(src + 16 * i);
-            rsc = sg == 0 ? *reinterpret_cast<const float*>(cache + (int64_t)idx * row_bytes + kD) : 0.f;
-        } else {
-#pragma unroll
-            for (int i = 0; i < SEGB / 16; ++i) raw[i] = u32x4{0u, 0u, 0u, 0u};
-            rsc = 0.f;
+        for (int k = 0; k < RW; ++k) {
+            const int idx = __builtin_amdgcn_readlane(mine, k);
+            // an empty slot reads through an empty range: zeros
+            const __amdgpu_buffer_rsrc_t rr =
+                buffer_rsrc(cache + (int64_t)max(idx, 0) * row_bytes, idx >= 0 ? (uint32_t)kD : 0u);
+            raw[k] = __builtin_amdgcn_raw_buffer_load_b64(rr, (uint32_t)lane * 8u, 0, 0);
         }
+        rsc = (lane < RW && mine >= 0) ? *reinterpret_cast<const float*>(cache + (int64_t)mine * row_bytes + kD) : 0.f;
     };
     // Chunk c's rows to bf16 in kv[buf], its row scales and validity, then
     // the request for chunk c + 2's rows.  The writes are safe without a
@@ -156,27 +161,21 @@ __global__ __launch_bounds__(64 * NW, 1) void k_mla_mfma(
     // barrier; chunk_any alternates too, as a wave may write chunk c's while
     // another still reads chunk c - 1's.
     auto convert = [&](int c, int buf) {
-        const int idx_cur = idx_lds[(c - c_begin) * kChunk + r];
-        if (sg == 0) { rs[r] = rsc; rvalid[r] = idx_cur >= 0; }
-        uint16_t* dst = &kv[buf][r * kKVRow + sg * SEGB];
+        const int mine = row_ids(c);
+        if (lane < RW) { rs[RW * wave + lane] = rsc; rvalid[RW * wave + lane] = mine >= 0; }
 #pragma unroll
-        for (int i = 0; i < SEGB / 16; ++i) {
-            uint32_t bq[8];
-            int8x4_to_bf16x4(raw[i][0], bq[0], bq[1]);
-            int8x4_to_bf16x4(raw[i][1], bq[2], bq[3]);
-            int8x4_to_bf16x4(raw[i][2], bq[4], bq[5]);
-            int8x4_to_bf16x4(raw[i][3], bq[6], bq[7]);
-            const u32x4 o0 = {bq[0], bq[1], bq[2], bq[3]};
-            const u32x4 o1 = {bq[4], bq[5], bq[6], bq[7]};
-            *reinterpret_cast<u32x4*>(dst + 16 * i) = o0;
-            *reinterpret_cast<u32x4*>(dst + 16 * i + 8) = o1;
+        for (int k = 0; k < RW; ++k) {
+            uint32_t b0, b1, b2, b3;
+            int8x4_to_bf16x4(raw[k][0], b0, b1);
+            int8x4_to_bf16x4(raw[k][1], b2, b3);
+            *reinterpret_cast<u32x4*>(&kv[buf][(RW * wave + k) * kKVRow + 8 * lane]) = u32x4{b0, b1, b2, b3};
         }
-        if (c + 1 < c_end) load_rows(idx_lds[(c + 1 - c_begin) * kChunk + r]);
-        const unsigned long long vote = __ballot(idx_cur >= 0);
-        if ((tid & 63) == 0) chunk_any[buf][wave] = vote != 0ull;
+        if (c + 1 < c_end) load_rows(c + 1);
+        const unsigned long long vote = __ballot(lane < RW && mine >= 0);
+        if (lane == 0) chunk_any[buf][wave] = vote != 0ull;
     };
     if (c_begin < c_end) {
-        load_rows(idx_lds[r]);
+        load_rows(c_begin);
         convert(c_begin, 0);
     }
 
