@@ -243,15 +243,22 @@ __global__ __launch_bounds__(64 * NW, 1) void k_mla_mfma(
                 psum[i] += p;
                 x[i] = p * rsv;
             }
+            // Lanes 2k and 2k + 1 (rows 2k, 2k + 1) swap one pair of heads
+            // each, so that lane 2k + e holds heads 2e, 2e + 1 of both rows
+            // and stores them as two 4-byte words (two rows of one head).
+            uint32_t hp[2], lp[2];
+            split_bf16x2(x[0], x[1], hp[0], lp[0]);
+            split_bf16x2(x[2], x[3], hp[1], lp[1]);
+            const int e = n16 & 1;
+            const int o = (ht * 16 + 4 * g4 + 2 * e) * kPRow + (row & ~1);
 #pragma unroll
-            for (int i2 = 0; i2 < 2; ++i2) {
-                uint32_t hp, lp;
-                split_bf16x2(x[2 * i2], x[2 * i2 + 1], hp, lp);
-                const int o = (ht * 16 + 4 * g4 + 2 * i2) * kPRow + row;
-                pl[0][o] = (uint16_t)hp;
-                pl[0][o + kPRow] = (uint16_t)(hp >> 16);
-                pl[1][o] = (uint16_t)lp;
-                pl[1][o + kPRow] = (uint16_t)(lp >> 16);
+            for (int hl = 0; hl < 2; ++hl) {
+                const uint32_t* v = hl ? lp : hp;
+                const uint32_t mine = e ? v[1] : v[0];
+                const uint32_t other = dpp_u32<0xB1, 0xF>(e ? v[0] : v[1], 0u);   // quad_perm [1,0,3,2]
+                const uint32_t r_even = e ? other : mine, r_odd = e ? mine : other;
+                *reinterpret_cast<uint32_t*>(&pl[hl][o]) = __builtin_amdgcn_perm(r_odd, r_even, 0x05040100u);
+                *reinterpret_cast<uint32_t*>(&pl[hl][o + kPRow]) = __builtin_amdgcn_perm(r_odd, r_even, 0x07060302u);
             }
         }
 #pragma unroll
