@@ -81,9 +81,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_mla_mfma(
     constexpr int HPW = 16 * HT;
     constexpr int WPHT = NW / HT;         // waves per head tile
     constexpr int RPW = 4 / WPHT;         // 16-row tiles per wave (S)
-    constexpr int NGRP = 8 / WPHT;        // 64-column groups per wave (PV)
+    constexpr int NGP = 8 / NW;           // 64-column groups per wave (PV, all HT head tiles)
     constexpr int RW = kChunk / NW;       // gathered rows per wave
-    static_assert(WPHT * HT == NW && RPW * WPHT == 4 && RW * NW == kChunk && RW <= 64, "64-row chunks, 16-row tiles");
+    static_assert(WPHT * HT == NW && RPW * WPHT == 4 && NGP * NW == 8 && RW * NW == kChunk && RW <= 64,
+                  "64-row chunks, 16-row tiles, 64-column groups");
     // The rows of two chunks (the one computed, the next being converted), so
     // that converting chunk c + 1 needs no barrier after chunk c's P'V.
     __shared__ __attribute__((aligned(16))) uint16_t kv[2][kChunk * kKVRow];
@@ -92,6 +93,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_mla_mfma(
     __shared__ int rvalid[kChunk];
     __shared__ float red_max[NW][16];
     __shared__ float red_sum[NW][16];
+    __shared__ __attribute__((aligned(16))) float alpha_lds[HPW];   // per head: the chunk's rescale of O
+    __shared__ __attribute__((aligned(16))) float lsum_lds[HPW];    // per head: the final softmax sum
     __shared__ int chunk_any[2][NW];
     __shared__ int idx_lds[kMaxSplitRows];
 
@@ -112,11 +115,15 @@ __global__ __launch_bounds__(64 * NW, 1) void k_mla_mfma(
     float m_run[4], l_run[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.f; }
-    f32x4 oacc[NGRP][4];
+    // O: column groups NGP w .. NGP w + NGP - 1 of every head tile; lane holds
+    // heads 16 ht' + 4 g4 + i, columns 64 grp + 4 n16 + tt
+    f32x4 oacc[NGP][HT][4];
 #pragma unroll
-    for (int gi = 0; gi < NGRP; ++gi)
+    for (int gi = 0; gi < NGP; ++gi)
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) oacc[gi][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < HT; ++h)
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) oacc[gi][h][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nchunks = (W + kChunk - 1) / kChunk;
     const int c_begin = split * chunks_per_split;
@@ -231,6 +238,14 @@ __global__ __launch_bounds__(64 * NW, 1) void k_mla_mfma(
             for (int s2 = 1; s2 < WPHT; ++s2) mc = fmaxf(mc, red_max[ht * WPHT + s2][4 * g4 + i]);
             m_new[i] = fmaxf(m_run[i], mc);
         }
+        // the rescale of O for this tile's heads, published for the P'V waves
+        // (read after the next barrier; rewritten only after the next chunk's
+        // first two barriers, when every wave is done with it)
+        float alpha[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) alpha[i] = m_run[i] == -INFINITY ? 0.f : exp2f(m_run[i] - m_new[i]);
+        if (sub == 0 && n16 == 0)
+            *reinterpret_cast<f32x4*>(&alpha_lds[ht * 16 + 4 * g4]) = f32x4{alpha[0], alpha[1], alpha[2], alpha[3]};
         float psum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int rr = 0; rr < RPW; ++rr) {
@@ -272,25 +287,26 @@ __global__ __launch_bounds__(64 * NW, 1) void k_mla_mfma(
             float ls = 0.f;
 #pragma unroll
             for (int s2 = 0; s2 < WPHT; ++s2) ls += red_sum[ht * WPHT + s2][4 * g4 + i];
-            const float alpha = m_run[i] == -INFINITY ? 0.f : exp2f(m_run[i] - m_new[i]);
-            l_run[i] = l_run[i] * alpha + ls;
+            l_run[i] = l_run[i] * alpha[i] + ls;
             m_run[i] = m_new[i];
-#pragma unroll
-            for (int gi = 0; gi < NGRP; ++gi)
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt) oacc[gi][tt][i] *= alpha;
         }
 
-        // ---- 4. O += P' V
+        // ---- 4. O += P' V over this wave's column groups and every head
+        //      tile: each V operand is read once and used HT times
+#pragma unroll
+        for (int h = 0; h < HT; ++h) {
+            const f32x4 al = *reinterpret_cast<const f32x4*>(&alpha_lds[16 * h + 4 * g4]);
+#pragma unroll
+            for (int gi = 0; gi < NGP; ++gi)
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) oacc[gi][h][tt] *= al;
+        }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const int po = (ht * 16 + n16) * kPRow + ks * 32 + g4 * 8;
-            const bf16x8 a_hi = as_bf16x8(*reinterpret_cast<const u32x4*>(&pl[0][po]));
-            const bf16x8 a_lo = as_bf16x8(*reinterpret_cast<const u32x4*>(&pl[1][po]));
             const int row0 = ks * 32 + g4 * 8;
 #pragma unroll
-            for (int gi = 0; gi < NGRP; ++gi) {
-                const int col0 = 64 * (sub * NGRP + gi) + 4 * n16;
+            for (int gi = 0; gi < NGP; ++gi) {
+                const int col0 = 64 * (NGP * wave + gi) + 4 * n16;
                 u32x2 v[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] = *reinterpret_cast<const u32x2*>(&kvb[(row0 + e) * kKVRow + col0]);
@@ -304,56 +320,72 @@ __global__ __launch_bounds__(64 * NW, 1) void k_mla_mfma(
                     bb[tt][2] = __builtin_amdgcn_perm(v[5][wd], v[4][wd], sel);
                     bb[tt][3] = __builtin_amdgcn_perm(v[7][wd], v[6][wd], sel);
                 }
-                // the four hi products, then the four lo ones: no MFMA waits on
-                // the one just issued
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt) oacc[gi][tt] = mfma16(a_hi, as_bf16x8(bb[tt]), oacc[gi][tt]);
+                for (int h = 0; h < HT; ++h) {
+                    const int po = (h * 16 + n16) * kPRow + ks * 32 + g4 * 8;
+                    const bf16x8 a_hi = as_bf16x8(*reinterpret_cast<const u32x4*>(&pl[0][po]));
+                    const bf16x8 a_lo = as_bf16x8(*reinterpret_cast<const u32x4*>(&pl[1][po]));
+                    // the four hi products, then the four lo ones: no MFMA waits
+                    // on the one just issued
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt) oacc[gi][tt] = mfma16(a_lo, as_bf16x8(bb[tt]), oacc[gi][tt]);
-                if constexpr (NW == 8) __builtin_amdgcn_sched_barrier(0);   // one group's V loads in flight at a time
+                    for (int tt = 0; tt < 4; ++tt) oacc[gi][h][tt] = mfma16(a_hi, as_bf16x8(bb[tt]), oacc[gi][h][tt]);
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) oacc[gi][h][tt] = mfma16(a_lo, as_bf16x8(bb[tt]), oacc[gi][h][tt]);
+                }
             }
         }
         if (c + 1 < c_end) convert(c + 1, buf ^ 1);
     }
 
-    // ---- epilogue: lane holds heads head0 + 4*g4 + i, columns 64*grp + 4*n16 + tt
-    if (splits == 1) {
+    // ---- epilogue.  The softmax totals are the head tiles' (lanes n16 = 0 of
+    // their first wave); the output is written by the P'V waves: lane holds
+    // heads 16 h + 4 g4 + i, columns 64 grp + 4 n16 + tt.
+    if (sub == 0 && n16 == 0) {
+        *reinterpret_cast<f32x4*>(&lsum_lds[ht * 16 + 4 * g4]) = f32x4{l_run[0], l_run[1], l_run[2], l_run[3]};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int head = head0 + 4 * g4 + i;
-            const float inv = l_run[i] > 0.f ? 1.0f / l_run[i] : 0.f;
-            const int64_t orow = ((int64_t)t * H + head) * kD;
-#pragma unroll
-            for (int gi = 0; gi < NGRP; ++gi) {
-                const int col = 64 * (sub * NGRP + gi) + 4 * n16;
-                f32x4 v = {oacc[gi][0][i] * inv, oacc[gi][1][i] * inv, oacc[gi][2][i] * inv, oacc[gi][3][i] * inv};
-                if (out_f32) {
-                    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + orow + col) = v;
-                } else {
-                    u32x2 pk;
-                    pk[0] = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-                    pk[1] = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-                    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + orow + col) = pk;
-                }
+            if (splits == 1) {
+                if (lse)
+                    lse[(int64_t)t * H + head] = l_run[i] > 0.f ? (m_run[i] + log2f(l_run[i])) * kLn2 : -INFINITY;
+            } else {
+                part_ml[((int64_t)t * splits + split) * H + head] = MlaPartial{m_run[i], l_run[i]};
             }
-            if (lse && sub == 0 && n16 == 0)
-                lse[(int64_t)t * H + head] = l_run[i] > 0.f ? (m_run[i] + log2f(l_run[i])) * kLn2 : -INFINITY;
         }
-    } else {
+    }
+    lds_barrier();
+#pragma unroll
+    for (int h = 0; h < HT; ++h) {
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(&lsum_lds[16 * h + 4 * g4]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int head = head0 + 4 * g4 + i;
-            const int64_t slot = ((int64_t)t * splits + split) * H + head;
-            float* po = part_o + slot * kD;
-            if (l_run[i] > 0.f) {
+            const int head = hg * HPW + 16 * h + 4 * g4 + i;
+            if (splits == 1) {
+                const float inv = lv[i] > 0.f ? 1.0f / lv[i] : 0.f;
+                const int64_t orow = ((int64_t)t * H + head) * kD;
 #pragma unroll
-                for (int gi = 0; gi < NGRP; ++gi) {
-                    const int col = 64 * (sub * NGRP + gi) + 4 * n16;
+                for (int gi = 0; gi < NGP; ++gi) {
+                    const int col = 64 * (NGP * wave + gi) + 4 * n16;
+                    f32x4 v = {oacc[gi][h][0][i] * inv, oacc[gi][h][1][i] * inv, oacc[gi][h][2][i] * inv,
+                               oacc[gi][h][3][i] * inv};
+                    if (out_f32) {
+                        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + orow + col) = v;
+                    } else {
+                        u32x2 pk;
+                        pk[0] = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+                        pk[1] = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+                        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + orow + col) = pk;
+                    }
+                }
+            } else if (lv[i] > 0.f) {
+                float* po = part_o + (((int64_t)t * splits + split) * H + head) * kD;
+#pragma unroll
+                for (int gi = 0; gi < NGP; ++gi) {
+                    const int col = 64 * (NGP * wave + gi) + 4 * n16;
                     *reinterpret_cast<f32x4*>(po + col) =
-                        f32x4{oacc[gi][0][i], oacc[gi][1][i], oacc[gi][2][i], oacc[gi][3][i]};
+                        f32x4{oacc[gi][h][0][i], oacc[gi][h][1][i], oacc[gi][h][2][i], oacc[gi][h][3][i]};
                 }
             }
-            if (sub == 0 && n16 == 0) part_ml[slot] = MlaPartial{m_run[i], l_run[i]};
         }
     }
 }
