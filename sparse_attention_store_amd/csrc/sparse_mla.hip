@@ -38,8 +38,13 @@
 //    split); at the end the waves add up l and the P' sums through LDS.
 //
 // k_mla_mfma<HT> (16*HT heads per workgroup, HT = 2 or 4; prefill and
-// many-query batches).  Waves own head tiles instead and walk 64-row chunks
-// staged in LDS; waves sharing a head tile exchange their partial max and sum.
+// many-query batches).  The workgroup walks 64-row chunks staged in LDS as
+// bf16, a wave gathering whole rows (lanes over a row's codes, so its 16-byte
+// LDS stores are consecutive).  For S and the softmax the waves own head
+// tiles (waves sharing a tile split the rows and exchange their partial max
+// and sum); for P'V they own column groups of every head tile, so each V
+// operand is read from LDS once, with the per-head rescale and final sums
+// handed over through LDS.
 //
 // One split writes the normalised output directly; several splits write
 // (m, l, unnormalised O) partials that k_mla_combine merges in split order,
