@@ -57,6 +57,12 @@ __device__ __forceinline__ void biased4_to_bf16(uint32_t w, uint32_t& lo, uint32
     hi = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
 }
 
+// max(x, 0) as one integer max on the bits: a value with the sign bit set
+// (-0 included) gives +0, any other passes.  For a number this is the ReLU;
+// fmaxf would first canonicalise an operand the compiler cannot prove
+// canonical (an MFMA result), one more instruction per value.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // 8 INT8 codes (two words) -> 8 bf16 of (code + 128).
 __device__ __forceinline__ u32x4 codes8_to_biased_bf16(uint32_t a, uint32_t b) {
     uint32_t r0, r1, r2, r3;

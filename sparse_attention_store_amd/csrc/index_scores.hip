@@ -138,8 +138,8 @@ __global__ __launch_bounds__(WAVES * 64, CANDS ? 2 : 3) void k_scores_mfma(
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float wh = wq[8 * (r >> 2) + (r & 3)];
-                s0 += wh * fmaxf(acc0[r], 0.f);
-                s1 += wh * fmaxf(acc1[r], 0.f);
+                s0 += wh * relu_bits(acc0[r]);
+                s1 += wh * relu_bits(acc1[r]);
             }
             const float sv = add_swap32(s0, s1);           // lanes 0-31: tile 0's sum, 32-63: tile 1's
             const int p = p0 + g * 32 + n;                 // lanes 0-31: tile 0, 32-63: tile 1

@@ -99,9 +99,9 @@ __device__ __forceinline__ float score_pool_group(const IdxQuery& Q, const u32x4
         }
         float sum = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sum += Q.w[0][i] * fmaxf(acc0[i], 0.f);
+        for (int i = 0; i < 4; ++i) sum += Q.w[0][i] * relu_bits(acc0[i]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sum += Q.w[1][i] * fmaxf(acc1[i], 0.f);
+        for (int i = 0; i < 4; ++i) sum += Q.w[1][i] * relu_bits(acc1[i]);
         part[r] = sum;
     }
     return reduce_group_parts(part);
@@ -121,9 +121,9 @@ __device__ __forceinline__ float score_pool_column(const IdxQuery& Q, const u32x
     }
     float sum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sum += Q.w[0][i] * fmaxf(acc0[i], 0.f);
+    for (int i = 0; i < 4; ++i) sum += Q.w[0][i] * relu_bits(acc0[i]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sum += Q.w[1][i] * fmaxf(acc1[i], 0.f);
+    for (int i = 0; i < 4; ++i) sum += Q.w[1][i] * relu_bits(acc1[i]);
     const float k = add_swap32(sum, sum);
     return add_swap16(k, k);
 }
@@ -195,9 +195,9 @@ __device__ __forceinline__ u32x4 i8_kstep(const u32x4& w0, const u32x4& w1, int 
 __device__ __forceinline__ float i8_head_sum(const IdxQueryI8& Q, const f32x4& acc0, const f32x4& acc1) {
     float sum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sum += Q.q.w[0][i] * fmaxf(acc0[i] - Q.bias[0][i], 0.f);
+    for (int i = 0; i < 4; ++i) sum += Q.q.w[0][i] * relu_bits(acc0[i] - Q.bias[0][i]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sum += Q.q.w[1][i] * fmaxf(acc1[i] - Q.bias[1][i], 0.f);
+    for (int i = 0; i < 4; ++i) sum += Q.q.w[1][i] * relu_bits(acc1[i] - Q.bias[1][i]);
     return sum;
 }
 
