@@ -126,11 +126,23 @@ __global__ __launch_bounds__(WAVES * 64, CANDS ? 2 : 3) void k_scores_mfma(
             }
             f32x16 acc0 = {}, acc1 = {};
             const uint16_t* qrow = &q_lds[qi][n * kQROW + g * 64];
+// The 8 A pieces with three reads in flight ahead of the MFMA pairs (the
+            // scheduler, short of registers, would otherwise wait on each read
+            // right before its pair).
+            u32x4 ar[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ar[j] = *reinterpret_cast<const u32x4*>(qrow + j * 8);
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);     // 3 LDS reads
+#pragma unroll
+            for (int j = 0; j < 5; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0); // 2 MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // 1 LDS read
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);     // the last 6 MFMAs
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + j * 8));
-                acc0 = mfma32(a, as_bf16x8(breg[0][j]), acc0);
-                acc1 = mfma32(a, as_bf16x8(breg[1][j]), acc1);
+                acc0 = mfma32(as_bf16x8(ar[j]), as_bf16x8(breg[0][j]), acc0);
+                acc1 = mfma32(as_bf16x8(ar[j]), as_bf16x8(breg[1][j]), acc1);
             }
             // Heads held by this lane: 8*(r/4) + 4*g + (r%4).
             const float* wq = &w_lds[qi][4 * g];
