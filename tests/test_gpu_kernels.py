@@ -442,6 +442,20 @@ def test_sparse_mla_h32_prefill_tiles(dsa, splits):
     _mla_case(dsa, wl, 300, valid, splits)
 
 
+@pytest.mark.parametrize("heads,T,splits", [(64, 160, 1), (64, 160, 3), (16, 6, 0)])
+def test_sparse_mla_ragged_width(dsa, heads, T, splits):
+    """Lists 2,100 wide: a 52-row last chunk for both the many-query kernel
+    (64-row chunks, k_mla_mfma at 64 heads and 160 queries) and the decode
+    kernel (128-row chunks, 16 heads), empty slots past the width included."""
+    import dataclasses
+    wl = syn.mini_heavy() if heads == 64 else syn.mini_decode()
+    wl = dataclasses.replace(wl, dims=dataclasses.replace(wl.dims, out_width=2100), name=wl.name + "_w2100")
+    g = np.random.default_rng(11)
+    valid = g.integers(0, 2101, size=T)
+    valid[:3] = [2100, 0, 2099]
+    _mla_case(dsa, wl, T, valid, splits)
+
+
 def test_sparse_mla_bf16_output(dsa):
     wl = syn.mini_decode()
     valid = np.array([2051, 100, 0, 2176], dtype=np.int64)
